@@ -1,0 +1,80 @@
+"""Seeded synthetic input generators shared by the tests, the oracle checks and the bench.
+
+This module holds only random-number draws; none of the emulation arithmetic lives
+here.  Every generator takes an explicit seed and draws with
+``numpy.random.default_rng(seed)`` (PCG64) in a fixed order (A, then B or X), so the
+oracle and the GPU path always see bit-identical operands.
+
+Distributions (all from the workload descriptions of the emulated-fp64 GEMM/GEMV and
+the exact INT8 product):
+
+* ``uniform``:   entries U(-1, 1).
+* ``phi``:       entries (U(0,1) - 0.5) * exp(phi * N(0,1)); phi = 0.5 (moderate range)
+                 or phi = 4 (wide dynamic range).
+* ``int8``:      integers uniform in [-128, 127].
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "uniform_matrix",
+    "phi_matrix",
+    "int8_matrix",
+    "gemm_operands",
+    "gemv_operands",
+    "int8_operands",
+    "small_int_matrix",
+]
+
+
+def uniform_matrix(rng: np.random.Generator, shape) -> np.ndarray:
+    """Entries drawn from U(-1, 1), float64, C-contiguous."""
+    return rng.uniform(-1.0, 1.0, size=shape)
+
+
+def phi_matrix(rng: np.random.Generator, shape, phi: float) -> np.ndarray:
+    """Entries (U(0,1) - 0.5) * exp(phi * N(0,1)): U is drawn first, then N."""
+    u = rng.random(shape)
+    g = rng.standard_normal(shape)
+    return (u - 0.5) * np.exp(phi * g)
+
+
+def int8_matrix(rng: np.random.Generator, shape) -> np.ndarray:
+    """Integers uniform in [-128, 127], int8."""
+    return rng.integers(-128, 128, size=shape, dtype=np.int8)
+
+
+def small_int_matrix(rng: np.random.Generator, shape, bound: int) -> np.ndarray:
+    """Integer-valued float64 entries uniform in [-bound, bound]."""
+    return rng.integers(-bound, bound + 1, size=shape).astype(np.float64)
+
+
+def gemm_operands(m: int, n: int, k: int, seed: int, dist: str = "uniform", phi: float = 0.5):
+    """A (m x k) and B (k x n), float64 row-major, drawn A first then B."""
+    rng = np.random.default_rng(seed)
+    if dist == "uniform":
+        a = uniform_matrix(rng, (m, k))
+        b = uniform_matrix(rng, (k, n))
+    elif dist == "phi":
+        a = phi_matrix(rng, (m, k), phi)
+        b = phi_matrix(rng, (k, n), phi)
+    else:
+        raise ValueError(f"unknown distribution {dist!r}")
+    return a, b
+
+
+def gemv_operands(m: int, k: int, nrhs: int, seed: int):
+    """A (m x k) and X (k x nrhs), both U(-1, 1), drawn A first then X."""
+    rng = np.random.default_rng(seed)
+    a = uniform_matrix(rng, (m, k))
+    x = uniform_matrix(rng, (k, nrhs))
+    return a, x
+
+
+def int8_operands(m: int, n: int, k: int, seed: int):
+    """A (m x k) and B (k x n), int8 uniform in [-128, 127], drawn A first then B."""
+    rng = np.random.default_rng(seed)
+    a = int8_matrix(rng, (m, k))
+    b = int8_matrix(rng, (k, n))
+    return a, b
