@@ -1,0 +1,225 @@
+// extern "C" entry points of libozk.so: argument validation (before any HIP call),
+// workspace carving, and the stream-ordered launch sequence of each operation.
+#include <hip/hip_runtime.h>
+
+#include "ozk_internal.h"
+
+using namespace ozk;
+
+namespace {
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Workspace carving: consecutive 256-byte aligned regions.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  }
+};
+
+struct DgemmLayout {
+  int64_t kp;
+  size_t planes_a, planes_b, residues, exps_a, exps_b, max_a, max_b;
+  size_t total() const {
+    return align256(planes_a) + align256(planes_b) + align256(residues) + align256(exps_a) +
+           align256(exps_b) + align256(max_a) + align256(max_b);
+  }
+};
+
+DgemmLayout dgemm_layout(int64_t m, int64_t n, int64_t k, int r) {
+  DgemmLayout L;
+  L.kp = round_up(k, kPlaneK);
+  L.planes_a = (size_t)r * m * L.kp;
+  L.planes_b = (size_t)r * n * L.kp;
+  L.residues = (size_t)r * m * n;
+  L.exps_a = (size_t)m * 4;
+  L.exps_b = (size_t)n * 4;
+  L.max_a = rows_fused_supported(k) ? 0 : (size_t)m * 8;
+  L.max_b = (size_t)n * 8;
+  return L;
+}
+
+int check_r(int r) { return (r >= 1 && r <= kMaxModuli) ? OZK_OK : OZK_EINVAL; }
+
+// Deconstruct one operand (axis 0: per-row, axis 1: per-column) into planes.
+int deconstruct_impl(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis, int r,
+                     int p_bits, int8_t* planes, int64_t ldp, int64_t plane_stride,
+                     int32_t* exps, uint64_t* maxbits, hipStream_t s) {
+  int st;
+  if (axis == 0 && rows_fused_supported(cols))
+    return launch_residues_rows_fused(x, rows, cols, ldx, r, p_bits, planes, ldp, plane_stride,
+                                      exps, s);
+  const int64_t lines = axis == 0 ? rows : cols;
+  if ((st = launch_fill_u64(maxbits, lines, 0, s)) != OZK_OK) return st;
+  if ((st = launch_absmax(x, rows, cols, ldx, axis, maxbits, s)) != OZK_OK) return st;
+  return launch_residues(x, rows, cols, ldx, axis, r, p_bits, maxbits, planes, ldp, plane_stride,
+                         exps, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ozk_version(void) { return 100; }
+
+const char* ozk_status_string(int status) {
+  switch (status) {
+    case OZK_OK: return "success";
+    case OZK_EINVAL: return "invalid argument";
+    case OZK_EWORKSPACE: return "workspace missing or too small";
+    case OZK_ERANGE: return "inner dimension out of range for exact products or the bit budget";
+    case OZK_EHIP: return "HIP launch failed";
+    case OZK_EUNSUPPORTED: return "unsupported request";
+    default: return "unknown status";
+  }
+}
+
+int ozk_moduli(int r, int32_t* out) { return moduli_list(r, out); }
+
+int ozk_scaling_bits(int r, int64_t k, int32_t* pa, int32_t* pb) {
+  int a = 0, b = 0;
+  int st = scaling_bits(r, k, &a, &b);
+  if (st != OZK_OK) return st;
+  if (pa) *pa = a;
+  if (pb) *pb = b;
+  return OZK_OK;
+}
+
+int64_t ozk_planes_ld(int64_t k) { return k <= 0 ? 0 : round_up(k, kPlaneK); }
+
+int ozk_deconstruct_workspace_size(int64_t rows, int64_t cols, int axis, size_t* bytes) {
+  if (!bytes || rows < 0 || cols < 0 || (axis != 0 && axis != 1)) return OZK_EINVAL;
+  if (axis == 0)
+    *bytes = rows_fused_supported(cols) ? 0 : align256((size_t)rows * 8);
+  else
+    *bytes = align256((size_t)cols * 8);
+  return OZK_OK;
+}
+
+int ozk_deconstruct(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis, int r,
+                    int64_t k_budget, int8_t* planes, int64_t ldp, int64_t plane_stride,
+                    int32_t* exps, void* workspace, size_t workspace_bytes, void* stream) {
+  if (axis != 0 && axis != 1) return OZK_EINVAL;
+  if (check_r(r) != OZK_OK) return OZK_EINVAL;
+  if (rows < 0 || cols < 0 || ldx < (cols > 0 ? cols : 1)) return OZK_EINVAL;
+  const int64_t K = axis == 0 ? cols : rows;
+  const int64_t lines = axis == 0 ? rows : cols;
+  if (ldp < K || ldp % kPlaneK != 0 || ldp <= 0) return OZK_EINVAL;
+  if (plane_stride < lines * ldp || plane_stride % kPlaneK != 0) return OZK_EINVAL;
+  int pa = 0, pb = 0;
+  int st = scaling_bits(r, k_budget, &pa, &pb);
+  if (st != OZK_OK) return st;
+  if (lines == 0) return OZK_OK;
+  if (!planes || !exps || (K > 0 && !x)) return OZK_EINVAL;
+  if (!aligned(planes, 16)) return OZK_EINVAL;
+  size_t need = 0;
+  ozk_deconstruct_workspace_size(rows, cols, axis, &need);
+  if (need > workspace_bytes || (need > 0 && !workspace)) return OZK_EWORKSPACE;
+  return deconstruct_impl(x, rows, cols, ldx, axis, r, axis == 0 ? pa : pb, planes, ldp,
+                          plane_stride, exps, static_cast<uint64_t*>(workspace),
+                          as_stream(stream));
+}
+
+int ozk_modular_products(int64_t m, int64_t n, int64_t kp, int r, const int8_t* pa,
+                         int64_t stride_a, const int8_t* pb, int64_t stride_b,
+                         int32_t* products, int64_t ldp_out, int64_t stride_p, void* stream) {
+  if (check_r(r) != OZK_OK) return OZK_EINVAL;
+  if (m < 0 || n < 0 || kp <= 0 || kp % kPlaneK != 0) return OZK_EINVAL;
+  if (kp > round_up(OZK_MAX_K, kPlaneK)) return OZK_ERANGE;
+  if (ldp_out < (n > 0 ? n : 1) || stride_p < m * ldp_out) return OZK_EINVAL;
+  if (stride_a < m * kp || stride_b < n * kp) return OZK_EINVAL;
+  if (stride_a % 16 || stride_b % 16) return OZK_EINVAL;
+  if (m == 0 || n == 0) return OZK_OK;
+  if (!pa || !pb || !products || !aligned(pa, 16) || !aligned(pb, 16)) return OZK_EINVAL;
+  return launch_gemm_i8(m, n, kp, r, pa, stride_a, pb, stride_b, products, ldp_out, stride_p,
+                        kEpiProducts, as_stream(stream));
+}
+
+int ozk_reconstruct(int64_t m, int64_t n, int r, const int32_t* products, int64_t ldp_in,
+                    int64_t stride_p, const int32_t* exps_a, const int32_t* exps_b, double* C,
+                    int64_t ldc, void* stream) {
+  if (check_r(r) != OZK_OK) return OZK_EINVAL;
+  if (m < 0 || n < 0) return OZK_EINVAL;
+  if (ldp_in < (n > 0 ? n : 1) || stride_p < m * ldp_in || ldc < (n > 0 ? n : 1))
+    return OZK_EINVAL;
+  if (m == 0 || n == 0) return OZK_OK;
+  if (!products || !exps_a || !exps_b || !C) return OZK_EINVAL;
+  return launch_crt(m, n, r, products, 1, ldp_in, stride_p, exps_a, exps_b, C, ldc,
+                    as_stream(stream));
+}
+
+int ozk_dgemm_workspace_size(int64_t m, int64_t n, int64_t k, int r, size_t* bytes) {
+  if (!bytes || m < 0 || n < 0 || k < 1 || check_r(r) != OZK_OK) return OZK_EINVAL;
+  if (k > OZK_MAX_K) return OZK_ERANGE;
+  *bytes = dgemm_layout(m, n, k, r).total();
+  return OZK_OK;
+}
+
+int ozk_dgemm(int64_t m, int64_t n, int64_t k, const double* A, int64_t lda, const double* B,
+              int64_t ldb, double* C, int64_t ldc, int r, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  if (check_r(r) != OZK_OK) return OZK_EINVAL;
+  if (m < 0 || n < 0 || k < 1) return OZK_EINVAL;
+  if (k > OZK_MAX_K) return OZK_ERANGE;
+  if (lda < k || ldb < (n > 0 ? n : 1) || ldc < (n > 0 ? n : 1)) return OZK_EINVAL;
+  int pa = 0, pb = 0;
+  int st = scaling_bits(r, k, &pa, &pb);
+  if (st != OZK_OK) return st;
+  if (m == 0 || n == 0) return OZK_OK;
+  if (!A || !B || !C) return OZK_EINVAL;
+  const DgemmLayout L = dgemm_layout(m, n, k, r);
+  if (!workspace || workspace_bytes < L.total()) return OZK_EWORKSPACE;
+  if (!aligned(workspace, 256)) return OZK_EINVAL;
+  if ((size_t)m * n > (size_t)0x7fffffffffffull) return OZK_EUNSUPPORTED;
+  Carver cv(workspace);
+  int8_t* planes_a = static_cast<int8_t*>(cv.take(L.planes_a));
+  int8_t* planes_b = static_cast<int8_t*>(cv.take(L.planes_b));
+  int8_t* residues = static_cast<int8_t*>(cv.take(L.residues));
+  int32_t* exps_a = static_cast<int32_t*>(cv.take(L.exps_a));
+  int32_t* exps_b = static_cast<int32_t*>(cv.take(L.exps_b));
+  uint64_t* max_a = static_cast<uint64_t*>(cv.take(L.max_a));
+  uint64_t* max_b = static_cast<uint64_t*>(cv.take(L.max_b));
+  hipStream_t s = as_stream(stream);
+  const int64_t kp = L.kp;
+  if ((st = deconstruct_impl(A, m, k, lda, 0, r, pa, planes_a, kp, m * kp, exps_a, max_a, s)))
+    return st;
+  if ((st = deconstruct_impl(B, k, n, ldb, 1, r, pb, planes_b, kp, n * kp, exps_b, max_b, s)))
+    return st;
+  if ((st = launch_gemm_i8(m, n, kp, r, planes_a, m * kp, planes_b, n * kp, residues, n, m * n,
+                           kEpiResidues, s)))
+    return st;
+  return launch_crt(m, n, r, residues, 0, n, m * n, exps_a, exps_b, C, ldc, s);
+}
+
+// GEMV and FP4-limb entry points: kernels not yet in this build.
+int ozk_dgemv_workspace_size(int64_t, int64_t, int64_t, int, int, size_t*) {
+  return OZK_EUNSUPPORTED;
+}
+int ozk_dgemv(int64_t, int64_t, int64_t, const double*, int64_t, const int8_t*, int64_t, int64_t,
+              const int32_t*, const double*, int64_t, double*, int64_t, int, int, void*, size_t,
+              void*) {
+  return OZK_EUNSUPPORTED;
+}
+int ozk_fp4limb_pack(const int8_t*, int64_t, int64_t, int64_t, int, uint8_t*, int64_t, int64_t,
+                     void*) {
+  return OZK_EUNSUPPORTED;
+}
+int ozk_fp4limb_products(int64_t, int64_t, int64_t, const uint8_t*, int64_t, const uint8_t*,
+                         int64_t, int32_t*, int64_t, int64_t, void*) {
+  return OZK_EUNSUPPORTED;
+}
+int ozk_int8gemm_fp4limb_workspace_size(int64_t, int64_t, int64_t, size_t*) {
+  return OZK_EUNSUPPORTED;
+}
+int ozk_int8gemm_fp4limb(int64_t, int64_t, int64_t, const int8_t*, int64_t, const int8_t*,
+                         int64_t, int32_t*, int64_t, void*, size_t, void*) {
+  return OZK_EUNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,281 @@
+// Deconstruction kernels: per-line exponents by the max rule and the r int8 residue
+// planes, written K-contiguous.  [TME4] abstract (the per-input deconstruction term).
+//
+// Kernels
+//   fill_u64            clears the column-maximum scratch before atomics
+//   absmax_rows/cols    bit pattern of max |x| per row / column (atomicMax on u64;
+//                       the order of non-negative doubles equals that of their bits,
+//                       and Inf/NaN patterns sort above every finite value)
+//   residues_rows       8 consecutive K elements per thread -> 8 bytes per plane
+//   residues_cols       16 consecutive K elements of one column per thread -> 16 bytes
+//                       per plane (the transpose happens in the store address)
+//   residues_rows_fused one workgroup per row: the row is held in registers, reduced
+//                       for its maximum, then turned into residues (one HBM read)
+#include "ozk_internal.h"
+#include "residue_math.h"
+
+namespace ozk {
+namespace {
+
+__global__ void fill_u64_kernel(uint64_t* __restrict__ p, int64_t n, uint64_t v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint64_t o = __shfl_xor(v, off, 64);
+    v = umax64(v, o);
+  }
+  return v;
+}
+
+// Row maxima: grid (chunks of 2048 columns, rows); 256 threads x 8 elements.
+__global__ __launch_bounds__(256) void absmax_rows_kernel(const double* __restrict__ x,
+                                                          int64_t cols, int64_t ldx,
+                                                          uint64_t* __restrict__ maxbits) {
+  const int64_t row = blockIdx.y;
+  const int64_t base = (int64_t)blockIdx.x * 2048;
+  const double* xr = x + row * ldx;
+  uint64_t v = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    int64_t h = base + u * 256 + threadIdx.x;
+    if (h < cols) v = umax64(v, abs_bits(xr[h]));
+  }
+  v = wave_max_u64(v);
+  __shared__ uint64_t part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t m = umax64(umax64(part[0], part[1]), umax64(part[2], part[3]));
+    atomicMax((unsigned long long*)&maxbits[row], (unsigned long long)m);
+  }
+}
+
+// Column maxima: grid (column blocks of 256, row chunks of 64).
+__global__ __launch_bounds__(256) void absmax_cols_kernel(const double* __restrict__ x,
+                                                          int64_t rows, int64_t cols,
+                                                          int64_t ldx,
+                                                          uint64_t* __restrict__ maxbits) {
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (col >= cols) return;
+  const int64_t r0 = (int64_t)blockIdx.y * 64;
+  const int64_t r1 = r0 + 64 < rows ? r0 + 64 : rows;
+  uint64_t v = 0;
+  for (int64_t h = r0; h < r1; ++h) v = umax64(v, abs_bits(x[h * ldx + col]));
+  atomicMax((unsigned long long*)&maxbits[col], (unsigned long long)v);
+}
+
+// Residues of 8 prepared elements for every modulus, stored as 8 bytes per plane.
+template <bool kWide>
+__device__ __forceinline__ void store_residues8(const double (&a)[8], int e,
+                                                const ResidueConsts& K, int8_t* dst,
+                                                int64_t plane_stride) {
+  Prepared p[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) p[u] = prepare_element<kWide>(a[u], e);
+  {
+    uint2 w;
+    w.x = pack4(residue_byte_256(p[0]), residue_byte_256(p[1]), residue_byte_256(p[2]),
+                residue_byte_256(p[3]));
+    w.y = pack4(residue_byte_256(p[4]), residue_byte_256(p[5]), residue_byte_256(p[6]),
+                residue_byte_256(p[7]));
+    *reinterpret_cast<uint2*>(dst) = w;
+  }
+  for (int l = 1; l < K.r; ++l) {
+    const double m = K.m[l], inv = K.inv[l], c = K.c32[l];
+    uint32_t b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) b[u] = residue_byte<kWide>(p[u], m, inv, c);
+    uint2 w;
+    w.x = pack4(b[0], b[1], b[2], b[3]);
+    w.y = pack4(b[4], b[5], b[6], b[7]);
+    *reinterpret_cast<uint2*>(dst + l * plane_stride) = w;
+  }
+}
+
+// Row residues with exponents from maxbits: grid (ldp / 2048 chunks, rows).
+template <bool kWide>
+__global__ __launch_bounds__(256) void residues_rows_kernel(
+    const double* __restrict__ x, int64_t cols, int64_t ldx, ResidueConsts K, int p_bits,
+    const uint64_t* __restrict__ maxbits, int8_t* __restrict__ planes, int64_t ldp,
+    int64_t plane_stride, int32_t* __restrict__ exps) {
+  const int64_t row = blockIdx.y;
+  const int e = line_exponent(maxbits[row], p_bits);
+  if (blockIdx.x == 0 && threadIdx.x == 0) exps[row] = e;
+  const int64_t h0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (h0 >= ldp) return;
+  const double* xr = x + row * ldx;
+  double a[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    int64_t h = h0 + u;
+    a[u] = (h < cols && e != INT32_MIN) ? xr[h] : 0.0;
+  }
+  int8_t* dst = planes + row * ldp + h0;
+  store_residues8<kWide>(a, e == INT32_MIN ? 0 : e, K, dst, plane_stride);
+}
+
+// Column residues: grid (ceil(cols/64), ldp/64); thread t owns column j0 + (t & 63)
+// and K rows h0 + 16*(t >> 6) .. +15, stored as 16 contiguous bytes per plane.
+template <bool kWide>
+__global__ __launch_bounds__(256) void residues_cols_kernel(
+    const double* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, ResidueConsts K,
+    int p_bits, const uint64_t* __restrict__ maxbits, int8_t* __restrict__ planes,
+    int64_t ldp, int64_t plane_stride, int32_t* __restrict__ exps) {
+  const int64_t col = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+  if (col >= cols) return;
+  const int e = line_exponent(maxbits[col], p_bits);
+  const int64_t h0 = (int64_t)blockIdx.y * 64 + (threadIdx.x >> 6) * 16;
+  if (blockIdx.y == 0 && threadIdx.x < 64) exps[col] = e;
+  int8_t* dst = planes + col * ldp + h0;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    double a[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      int64_t h = h0 + half * 8 + u;
+      a[u] = (h < rows && e != INT32_MIN) ? x[h * ldx + col] : 0.0;
+    }
+    store_residues8<kWide>(a, e == INT32_MIN ? 0 : e, K, dst + half * 8, plane_stride);
+  }
+}
+
+// One workgroup per row, the row in registers: kNT threads x kG groups of 8 elements.
+template <bool kWide, int kNT, int kG>
+__global__ __launch_bounds__(kNT) void residues_rows_fused_kernel(
+    const double* __restrict__ x, int64_t cols, int64_t ldx, ResidueConsts K, int p_bits,
+    int8_t* __restrict__ planes, int64_t ldp, int64_t plane_stride,
+    int32_t* __restrict__ exps) {
+  const int64_t row = blockIdx.x;
+  const double* xr = x + row * ldx;
+  double a[kG][8];
+  uint64_t v = 0;
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    const int64_t h0 = ((int64_t)g * kNT + threadIdx.x) * 8;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      int64_t h = h0 + u;
+      a[g][u] = h < cols ? xr[h] : 0.0;
+      v = umax64(v, abs_bits(a[g][u]));
+    }
+  }
+  v = wave_max_u64(v);
+  __shared__ uint64_t part[kNT / 64];
+  __shared__ int exp_shared;
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t mx = 0;
+    for (int w = 0; w < kNT / 64; ++w) mx = umax64(mx, part[w]);
+    int e = line_exponent(mx, p_bits);
+    exp_shared = e;
+    exps[row] = e;
+  }
+  __syncthreads();
+  int e = exp_shared;
+  const bool bad = e == INT32_MIN;
+  if (bad) e = 0;
+  int8_t* prow = planes + row * ldp;
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    const int64_t h0 = ((int64_t)g * kNT + threadIdx.x) * 8;
+    if (h0 >= ldp) continue;
+    if (bad) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[g][u] = 0.0;
+    }
+    store_residues8<kWide>(a[g], e, K, prow + h0, plane_stride);
+  }
+  // Padding beyond the register-resident part (only when ldp exceeds kNT * kG * 8).
+  for (int64_t h0 = ((int64_t)kG * kNT + threadIdx.x) * 8; h0 < ldp; h0 += (int64_t)kNT * 8) {
+    for (int l = 0; l < K.r; ++l)
+      *reinterpret_cast<uint2*>(prow + l * plane_stride + h0) = make_uint2(0u, 0u);
+  }
+}
+
+template <bool kWide, int kNT, int kG>
+int launch_fused(const double* x, int64_t rows, int64_t cols, int64_t ldx,
+                 const ResidueConsts& K, int p_bits, int8_t* planes, int64_t ldp,
+                 int64_t plane_stride, int32_t* exps, hipStream_t s) {
+  hipLaunchKernelGGL((residues_rows_fused_kernel<kWide, kNT, kG>), dim3((unsigned)rows),
+                     dim3(kNT), 0, s, x, cols, ldx, K, p_bits, planes, ldp, plane_stride, exps);
+  return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
+}
+
+}  // namespace
+
+int launch_fill_u64(uint64_t* p, int64_t n, uint64_t v, hipStream_t s) {
+  if (n <= 0) return OZK_OK;
+  hipLaunchKernelGGL(fill_u64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p,
+                     n, v);
+  return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
+}
+
+int launch_absmax(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                  uint64_t* maxbits, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return OZK_OK;
+  if (axis == 0) {
+    dim3 grid((unsigned)((cols + 2047) / 2048), (unsigned)rows);
+    hipLaunchKernelGGL(absmax_rows_kernel, grid, dim3(256), 0, s, x, cols, ldx, maxbits);
+  } else {
+    dim3 grid((unsigned)((cols + 255) / 256), (unsigned)((rows + 63) / 64));
+    hipLaunchKernelGGL(absmax_cols_kernel, grid, dim3(256), 0, s, x, rows, cols, ldx, maxbits);
+  }
+  return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
+}
+
+int launch_residues(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis, int r,
+                    int p_bits, const uint64_t* maxbits, int8_t* planes, int64_t ldp,
+                    int64_t plane_stride, int32_t* exps, hipStream_t s) {
+  const ResidueConsts& K = *residue_consts(r, p_bits);
+  const bool wide = K.wide != 0;
+  if (axis == 0) {
+    if (rows <= 0) return OZK_OK;
+    dim3 grid((unsigned)((ldp + 2047) / 2048), (unsigned)rows);
+    if (wide)
+      hipLaunchKernelGGL(residues_rows_kernel<true>, grid, dim3(256), 0, s, x, cols, ldx, K,
+                         p_bits, maxbits, planes, ldp, plane_stride, exps);
+    else
+      hipLaunchKernelGGL(residues_rows_kernel<false>, grid, dim3(256), 0, s, x, cols, ldx, K,
+                         p_bits, maxbits, planes, ldp, plane_stride, exps);
+  } else {
+    if (cols <= 0) return OZK_OK;
+    dim3 grid((unsigned)((cols + 63) / 64), (unsigned)(ldp / 64));
+    if (wide)
+      hipLaunchKernelGGL(residues_cols_kernel<true>, grid, dim3(256), 0, s, x, rows, cols, ldx,
+                         K, p_bits, maxbits, planes, ldp, plane_stride, exps);
+    else
+      hipLaunchKernelGGL(residues_cols_kernel<false>, grid, dim3(256), 0, s, x, rows, cols, ldx,
+                         K, p_bits, maxbits, planes, ldp, plane_stride, exps);
+  }
+  return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
+}
+
+bool rows_fused_supported(int64_t cols) { return cols <= 32768; }
+
+int launch_residues_rows_fused(const double* x, int64_t rows, int64_t cols, int64_t ldx, int r,
+                               int p_bits, int8_t* planes, int64_t ldp, int64_t plane_stride,
+                               int32_t* exps, hipStream_t s) {
+  if (rows <= 0) return OZK_OK;
+  const ResidueConsts& K = *residue_consts(r, p_bits);
+  const bool wide = K.wide != 0;
+#define OZK_FUSED(NT, G)                                                                     \
+  return wide ? launch_fused<true, NT, G>(x, rows, cols, ldx, K, p_bits, planes, ldp,        \
+                                          plane_stride, exps, s)                             \
+              : launch_fused<false, NT, G>(x, rows, cols, ldx, K, p_bits, planes, ldp,       \
+                                           plane_stride, exps, s)
+  if (cols <= 2048) { OZK_FUSED(256, 1); }
+  if (cols <= 4096) { OZK_FUSED(256, 2); }
+  if (cols <= 8192) { OZK_FUSED(256, 4); }
+  if (cols <= 16384) { OZK_FUSED(512, 4); }
+  OZK_FUSED(1024, 4);
+#undef OZK_FUSED
+}
+
+}  // namespace ozk

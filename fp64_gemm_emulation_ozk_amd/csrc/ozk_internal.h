@@ -1,0 +1,75 @@
+// Internal declarations of the ozk library: constant tables, launch helpers and the
+// per-element arithmetic shared by the kernels.  Nothing here is part of the C ABI.
+//
+// Method: Ozaki scheme II emulation of fp64 matrix products, as summarised in "The
+// Missing Fourth Term for the Emulation Tensor Memory Equilibrium (TME) Model: The
+// Residue Deconstruction Cost" (arXiv 2610.10924), abstract: operands are scaled,
+// rounded and reduced modulo r moduli; one integer matrix product per modulus; a
+// per-output reconstruction returns fp64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ozk.h"
+
+namespace ozk {
+
+constexpr int kMaxModuli = 20;
+constexpr int kPlaneK = 64;          // residue planes: K padded to a multiple of this
+constexpr int kExpNonfinite = INT32_MIN;
+constexpr int kMaxLimbs = 4;         // CRT limbs of 2^40
+constexpr double kMagic = 6755399441055744.0;  // 1.5 * 2^52: x + kMagic rounds x to an integer
+
+// Per-modulus constants for the residue kernels (passed by value as kernel arguments).
+struct ResidueConsts {
+  int r;
+  int wide;                     // 1 when scaled integers may exceed 2^51 (split path)
+  double m[kMaxModuli];         // moduli as doubles
+  double inv[kMaxModuli];       // RN(1/m)
+  double c32[kMaxModuli];       // smod(2^32, m)
+};
+
+// Constants of the CRT reconstruction.
+struct CrtConsts {
+  int r;
+  int limbs;                          // 3 or 4 limbs of 2^40
+  int32_t mod[kMaxModuli];            // moduli
+  double inv[kMaxModuli];             // RN(1/m)
+  double frac[kMaxModuli];            // RN(E_l / M) = RN(w_l / m_l)
+  double e_limb[kMaxModuli][kMaxLimbs];  // E_l in base 2^40, least significant first
+  double m_limb[kMaxLimbs];           // M in base 2^40
+};
+
+// Host side (rns_host.cpp)
+int moduli_list(int r, int32_t* out);
+int scaling_bits(int r, int64_t k, int* pa, int* pb);
+const ResidueConsts* residue_consts(int r, int p_bits);
+const CrtConsts* crt_consts(int r);
+
+inline int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Launchers (each defined next to its kernels).  All return OZK_OK or OZK_EHIP.
+int launch_fill_u64(uint64_t* p, int64_t n, uint64_t v, hipStream_t s);
+int launch_absmax(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                  uint64_t* maxbits, hipStream_t s);
+int launch_residues(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                    int r, int p_bits, const uint64_t* maxbits, int8_t* planes, int64_t ldp,
+                    int64_t plane_stride, int32_t* exps, hipStream_t s);
+int launch_residues_rows_fused(const double* x, int64_t rows, int64_t cols, int64_t ldx,
+                               int r, int p_bits, int8_t* planes, int64_t ldp,
+                               int64_t plane_stride, int32_t* exps, hipStream_t s);
+bool rows_fused_supported(int64_t cols);
+
+enum GemmEpilogue { kEpiProducts = 0, kEpiResidues = 1 };
+int launch_gemm_i8(int64_t m, int64_t n, int64_t kp, int r, const int8_t* pa, int64_t stride_a,
+                   const int8_t* pb, int64_t stride_b, void* out, int64_t ldo, int64_t stride_o,
+                   int epilogue, hipStream_t s);
+
+int launch_crt(int64_t m, int64_t n, int r, const void* res, int res_is_i32, int64_t ldr,
+               int64_t stride_r, const int32_t* ea, const int32_t* eb, double* c, int64_t ldc,
+               hipStream_t s);
+
+}  // namespace ozk

@@ -1,0 +1,177 @@
+/*
+ * ozk — Ozaki scheme II fp64 GEMM/GEMV emulation and exact INT8 products through FP4
+ * limbs, for AMD Instinct MI355X (gfx950).  C ABI of libozk.so.
+ *
+ * Sources (cited by page title and part):
+ *  [TME4] "The Missing Fourth Term for the Emulation Tensor Memory Equilibrium (TME)
+ *         Model: The Residue Deconstruction Cost", arXiv 2610.10924v1, abstract.
+ *         Ozaki scheme II emulates an fp64 matrix product with integer matrix
+ *         products: every fp64 operand is scaled, rounded and reduced modulo each of r
+ *         moduli (the deconstruction), one integer product runs per modulus (the
+ *         tensor term), and a per-output reconstruction returns fp64.  GEMV and
+ *         low-batch GEMV are memory bound; precomputed, stored residues move the
+ *         deconstruction cost into HBM traffic.
+ *  [AWE]  arXiv 2609.24519 listing (Nagoya University), English abstract.  Every
+ *         product of the scheme is an exact integer product times a scale; 2 x FP4
+ *         covers every residue mod 13, so an INT8 operand splits into three base-13
+ *         digits (weights 1, 13, 169) stored as FP4, and INT8 x INT8 takes 9 FP4 GEMMs.
+ *
+ * Conventions for every entry point:
+ *  - Matrices are row-major with a leading dimension (elements), as in PyTorch.
+ *  - Pointers named A, B, C, X, Y, planes, exps, products, workspace are DEVICE
+ *    pointers; pointers documented as "host" are host memory.  The caller owns all
+ *    memory; the library never allocates device memory.  Scratch memory comes from a
+ *    caller-provided workspace sized by the matching *_workspace_size query.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously; device faults surface at the caller's next synchronisation.
+ *  - Arguments are validated before any HIP call; a failing check returns a negative
+ *    status and enqueues nothing.  No C++ exception crosses the ABI.
+ *  - Moduli: the first r of the pairwise-coprime integers <= 256 taken greedily from
+ *    256 downwards (256, 255, 253, 251, 247, 241, 239, 233, 229, 227, 223, 217, 211,
+ *    199, 197, 193, 191, 181, 179, 173); 1 <= r <= 20.
+ *  - Scaling: a power of two per row of A and per column of B/X by the max rule
+ *    e = P - 1 - ilogb(max |x|) (0 for an all-zero line), with bit budgets
+ *    P_A = floor(beta/2), P_B = beta - P_A, beta = floor(log2((M-1)/2)) - ceil(log2 k),
+ *    M the product of the moduli.  Scaled integers are rounded half to even.
+ *  - Residues are symmetric: smod(x, m) in [-floor(m/2), ceil(m/2) - 1] (int8).
+ *  - A line (row or column) holding Inf or NaN gets the exponent INT32_MIN, all-zero
+ *    residues, and NaN in every output it touches.
+ */
+#ifndef OZK_H
+#define OZK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OZK_OK 0
+#define OZK_EINVAL (-1)       /* bad argument (null pointer, size, leading dimension, r) */
+#define OZK_EWORKSPACE (-2)   /* workspace missing or smaller than the query returned */
+#define OZK_ERANGE (-3)       /* k too large: int32 products or the bit budget would fail */
+#define OZK_EHIP (-4)         /* a HIP launch failed */
+#define OZK_EUNSUPPORTED (-5) /* valid request this build does not handle */
+
+#define OZK_MAX_MODULI 20
+#define OZK_MAX_K 131071      /* |residue product| <= 2^14: int32 sums stay exact */
+#define OZK_PLANE_K 64        /* residue and limb planes pad K to a multiple of this */
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int ozk_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* ozk_status_string(int status);
+
+/* Moduli of an r-modulus system: writes r int32 to `out` (host).  [TME4] abstract
+ * ("each of the r moduli").  Returns OZK_EINVAL for r outside [1, 20] or out NULL. */
+int ozk_moduli(int r, int32_t* out);
+
+/* Bit budgets (P_A, P_B) of the scaling for r moduli and inner dimension k (host
+ * outputs).  OZK_ERANGE when beta < 2 or k > OZK_MAX_K. */
+int ozk_scaling_bits(int r, int64_t k, int32_t* pa, int32_t* pb);
+
+/* Leading dimension used for planes over an inner dimension k: round_up(k, 64). */
+int64_t ozk_planes_ld(int64_t k);
+
+/* ---------------------------------------------------------------- deconstruction
+ * [TME4] abstract, the per-input deconstruction term: scale each line of x by a
+ * power of two, round to an integer, reduce modulo each of the r moduli.
+ *
+ * axis 0 (A-side, per-row scaling with P_A):  x is rows x cols; K = cols.
+ *     planes[l*plane_stride + i*ldp + h] = smod(RNE(x[i][h] 2^exps[i]), m_l)
+ * axis 1 (B-side, per-column scaling with P_B): x is rows x cols with K = rows;
+ *     planes[l*plane_stride + j*ldp + h] = smod(RNE(x[h][j] 2^exps[j]), m_l)
+ *     (transposed, so K is contiguous as the products consume it).
+ * In both cases entries with h in [K, ldp) are written as 0, exps has one int32 per
+ * line (rows for axis 0, cols for axis 1), and the budget is that of inner dimension
+ * k_budget (normally K).  ldp must be a multiple of 64 with ldp >= K; plane_stride >=
+ * lines * ldp.  Reads x once for axis 0 when K <= 32768 (else twice); axis 1 reads x
+ * twice (column maxima, then residues).
+ */
+int ozk_deconstruct_workspace_size(int64_t rows, int64_t cols, int axis, size_t* bytes);
+int ozk_deconstruct(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                    int r, int64_t k_budget, int8_t* planes, int64_t ldp,
+                    int64_t plane_stride, int32_t* exps, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- modular products
+ * [TME4] abstract, the tensor term; [AWE] abstract, each product is an error-free
+ * integer matrix product.  For l < r:
+ *     products[l*stride_p + i*ldp_out + j] = sum_{h < kp} pa[l*stride_a + i*kp + h]
+ *                                                       * pb[l*stride_b + j*kp + h]
+ * exactly in int32 (int8 planes as written by ozk_deconstruct; kp a multiple of 64,
+ * kp <= OZK_MAX_K rounded up).  m x n outputs per modulus; ldp_out >= n. */
+int ozk_modular_products(int64_t m, int64_t n, int64_t kp, int r, const int8_t* pa,
+                         int64_t stride_a, const int8_t* pb, int64_t stride_b,
+                         int32_t* products, int64_t ldp_out, int64_t stride_p, void* stream);
+
+/* ---------------------------------------------------------------- reconstruction
+ * [TME4] abstract, the per-output reconstruction term.  For each output, the r
+ * int32 products are reduced modulo their moduli, lifted exactly by the Chinese
+ * Remainder Theorem to the integer X in [-M/2, M/2), and
+ *     C[i][j] = RN(X * 2^-(exps_a[i] + exps_b[j]))
+ * rounded once to nearest even (subnormal results included; overflow gives +-Inf).
+ * A NONFINITE (INT32_MIN) exponent gives NaN.  ldp_in >= n, ldc >= n. */
+int ozk_reconstruct(int64_t m, int64_t n, int r, const int32_t* products, int64_t ldp_in,
+                    int64_t stride_p, const int32_t* exps_a, const int32_t* exps_b,
+                    double* C, int64_t ldc, void* stream);
+
+/* ---------------------------------------------------------------- emulated DGEMM
+ * C = A B (m x n, A m x k, B k x n, no alpha/beta) through r moduli: deconstruction
+ * of A (rows) and B (columns), r int8 MFMA products with the residue epilogue, CRT
+ * reconstruction.  The result equals RN(2^-(e_i+f_j) sum_h a'_ih b'_hj) with the
+ * sum exact.  m, n >= 0; 1 <= k <= OZK_MAX_K; lda >= k, ldb >= n, ldc >= n. */
+int ozk_dgemm_workspace_size(int64_t m, int64_t n, int64_t k, int r, size_t* bytes);
+int ozk_dgemm(int64_t m, int64_t n, int64_t k, const double* A, int64_t lda,
+              const double* B, int64_t ldb, double* C, int64_t ldc, int r,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- emulated DGEMV
+ * Y = A X for A m x k and X k x nrhs (1 <= nrhs <= 32): the memory-bound GEMV and
+ * low-batch GEMV of [TME4] abstract.  Same arithmetic and result as ozk_dgemm.
+ * mode 0 (on the fly): A is streamed as fp64 and deconstructed in registers; A_exps
+ *        may be NULL (row exponents are then computed first, one extra pass over A)
+ *        or hold exponents from ozk_deconstruct(axis 0, k_budget = k).
+ * mode 1 (stored):     A_planes/A_exps come from ozk_deconstruct(A, axis 0,
+ *        k_budget = k) with leading dimension ldp and plane stride plane_stride; A
+ *        may be NULL.  r bytes per element of A are streamed.  [TME4] abstract: the
+ *        stored residues move the deconstruction cost into the bandwidth term. */
+int ozk_dgemv_workspace_size(int64_t m, int64_t k, int64_t nrhs, int r, int mode,
+                             size_t* bytes);
+int ozk_dgemv(int64_t m, int64_t k, int64_t nrhs, const double* A, int64_t lda,
+              const int8_t* A_planes, int64_t ldp, int64_t plane_stride,
+              const int32_t* A_exps, const double* X, int64_t ldx, double* Y, int64_t ldy,
+              int r, int mode, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- FP4-limb INT8 GEMM
+ * [AWE] abstract: x = d0 + 13 d1 + 169 d2 with every digit in
+ * S = {0, +-1, +-2, +-3, +-4, +-6, +-8, +-12}; the digit of residue rho (mod 13) is
+ * the element of S of least magnitude congruent to rho; digit d is stored as the
+ * e2m1 code of d/2, two codes per byte, the even K index in the low nibble.
+ *
+ * ozk_fp4limb_pack:  axis 0: x rows x cols (K = cols) ->
+ *        planes[d*plane_stride + i*ldp_bytes + h/2], nibble h&1, for digit d in 0..2;
+ *   axis 1: x rows x cols (K = rows) -> planes[d*plane_stride + j*ldp_bytes + h/2].
+ *   Codes for h in [K, 2*ldp_bytes) are 0.  ldp_bytes multiple of 32, >= round_up(K,64)/2.
+ * ozk_fp4limb_products: the 9 digit products, exact:
+ *   products[(3*da+db)*stride_p + i*ldp_out + j] = sum_h D_da(A)[i][h] D_db(B)[h][j]
+ *   from packed planes with K extent kp = 2*ldp_bytes (a multiple of 64).
+ * ozk_int8gemm_fp4limb: C = A B exactly in int32 (A m x k, B k x n int8), as the sum
+ *   of the 9 FP4 products weighted by 13^(da+db).  k <= OZK_MAX_K. */
+int ozk_fp4limb_pack(const int8_t* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                     uint8_t* planes, int64_t ldp_bytes, int64_t plane_stride, void* stream);
+int ozk_fp4limb_products(int64_t m, int64_t n, int64_t ldp_bytes, const uint8_t* planes_a,
+                         int64_t stride_a, const uint8_t* planes_b, int64_t stride_b,
+                         int32_t* products, int64_t ldp_out, int64_t stride_p, void* stream);
+int ozk_int8gemm_fp4limb_workspace_size(int64_t m, int64_t n, int64_t k, size_t* bytes);
+int ozk_int8gemm_fp4limb(int64_t m, int64_t n, int64_t k, const int8_t* A, int64_t lda,
+                         const int8_t* B, int64_t ldb, int32_t* C, int64_t ldc,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OZK_H */

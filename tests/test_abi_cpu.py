@@ -1,0 +1,126 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the header
+declares, reports the documented constants, and rejects bad arguments before any HIP
+call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp64_gemm_emulation_ozk_amd as ozk
+from oracle import rns
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ozk.h")
+
+OK, EINVAL, EWORKSPACE, ERANGE, EHIP, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ozk.LIB_PATH):
+        from fp64_gemm_emulation_ozk_amd.build import build_library
+        build_library(verbose=False)
+    return ozk.library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ozk_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_functions_exported(lib):
+    names = _declared_functions()
+    assert len(names) >= 17
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(ozk._SIGNATURES), "binding and header declare different functions"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ozk_version() >= 100
+    for st in (OK, EINVAL, EWORKSPACE, ERANGE, EHIP, EUNSUPPORTED, 12345):
+        assert isinstance(lib.ozk_status_string(st), bytes)
+
+
+@pytest.mark.parametrize("r", [1, 7, 14, 20])
+def test_moduli_match_oracle(lib, r):
+    assert ozk.ozk_moduli(r) == rns.moduli(r)
+
+
+def test_moduli_rejects_bad_r(lib):
+    buf = (ctypes.c_int32 * 21)()
+    assert lib.ozk_moduli(0, ctypes.cast(buf, ctypes.c_void_p)) == EINVAL
+    assert lib.ozk_moduli(21, ctypes.cast(buf, ctypes.c_void_p)) == EINVAL
+    assert lib.ozk_moduli(3, None) == EINVAL
+
+
+@pytest.mark.parametrize("r,k", [(14, 64), (12, 4096), (16, 4096), (18, 4096), (20, 8192),
+                                 (14, 32768), (5, 100), (16, 131071)])
+def test_scaling_bits_match_oracle(lib, r, k):
+    assert ozk.ozk_scaling_bits(r, k) == rns.scaling_bits(r, k)
+
+
+def test_scaling_bits_errors(lib):
+    pa, pb = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.ozk_scaling_bits(16, 131072, ctypes.byref(pa), ctypes.byref(pb)) == ERANGE
+    assert lib.ozk_scaling_bits(1, 64, ctypes.byref(pa), ctypes.byref(pb)) == ERANGE
+    assert lib.ozk_scaling_bits(0, 64, ctypes.byref(pa), ctypes.byref(pb)) == EINVAL
+    assert lib.ozk_scaling_bits(5, 0, ctypes.byref(pa), ctypes.byref(pb)) == EINVAL
+
+
+def test_planes_ld(lib):
+    assert [lib.ozk_planes_ld(k) for k in (1, 63, 64, 65, 4096, 4097)] == [64, 64, 64, 128, 4096,
+                                                                          4160]
+
+
+def test_workspace_sizes(lib):
+    ws = ozk.ozk_dgemm_workspace_size(4096, 4096, 4096, 16)
+    assert ws >= 16 * 4096 * 4096 * 3           # two operand plane sets + residues
+    out = ctypes.c_size_t()
+    assert lib.ozk_dgemm_workspace_size(4, 4, 200000, 16, ctypes.byref(out)) == ERANGE
+    assert lib.ozk_dgemm_workspace_size(4, 4, 4, 0, ctypes.byref(out)) == EINVAL
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+def test_dgemm_validation_before_any_hip_call(lib):
+    f = lib.ozk_dgemm
+    assert f(4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 0, FAKE, 1 << 20, None) == EINVAL   # r
+    assert f(4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 21, FAKE, 1 << 20, None) == EINVAL  # r
+    assert f(4, 4, 200000, FAKE, 200000, FAKE, 4, FAKE, 4, 16, FAKE, 1 << 20, None) == ERANGE
+    assert f(4, 4, 4, FAKE, 3, FAKE, 4, FAKE, 4, 14, FAKE, 1 << 20, None) == EINVAL  # lda < k
+    assert f(4, 4, 4, FAKE, 4, FAKE, 3, FAKE, 4, 14, FAKE, 1 << 20, None) == EINVAL  # ldb < n
+    assert f(4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 3, 14, FAKE, 1 << 20, None) == EINVAL  # ldc < n
+    assert f(-1, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 14, FAKE, 1 << 20, None) == EINVAL
+    assert f(4, 4, 4, None, 4, FAKE, 4, FAKE, 4, 14, FAKE, 1 << 20, None) == EINVAL  # null A
+    assert f(4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 14, None, 0, None) == EWORKSPACE
+    assert f(4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 14, FAKE, 16, None) == EWORKSPACE
+    assert f(4, 4, 1 << 16, FAKE, 1 << 16, FAKE, 4, FAKE, 4, 2, FAKE, 1 << 30, None) == ERANGE
+    assert f(0, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 14, None, 0, None) == OK           # empty
+
+
+def test_deconstruct_validation(lib):
+    f = lib.ozk_deconstruct
+    # ldp not a multiple of 64, ldp < K, bad axis, bad r, short plane stride, null planes
+    assert f(FAKE, 4, 100, 100, 0, 14, 100, FAKE, 100, 400, FAKE, FAKE, 0, None) == EINVAL
+    assert f(FAKE, 4, 100, 100, 0, 14, 100, FAKE, 64, 256, FAKE, FAKE, 0, None) == EINVAL
+    assert f(FAKE, 4, 100, 100, 2, 14, 100, FAKE, 128, 512, FAKE, FAKE, 0, None) == EINVAL
+    assert f(FAKE, 4, 100, 100, 0, 0, 100, FAKE, 128, 512, FAKE, FAKE, 0, None) == EINVAL
+    assert f(FAKE, 4, 100, 100, 0, 14, 100, FAKE, 128, 256, FAKE, FAKE, 0, None) == EINVAL
+    assert f(FAKE, 4, 100, 100, 0, 14, 100, None, 128, 512, FAKE, FAKE, 0, None) == EINVAL
+    # axis 1 needs a column-maximum workspace
+    assert f(FAKE, 100, 4, 4, 1, 14, 100, FAKE, 128, 512, FAKE, None, 0, None) == EWORKSPACE
+
+
+def test_products_and_reconstruct_validation(lib):
+    f = lib.ozk_modular_products
+    assert f(4, 4, 100, 3, FAKE, 400, FAKE, 400, FAKE, 4, 16, None) == EINVAL       # kp % 64
+    assert f(4, 4, 64, 3, FAKE, 128, FAKE, 256, FAKE, 4, 16, None) == EINVAL        # stride_a
+    assert f(4, 4, 131136, 3, FAKE, 1 << 20, FAKE, 1 << 20, FAKE, 4, 16, None) == ERANGE
+    g = lib.ozk_reconstruct
+    assert g(4, 4, 0, FAKE, 4, 16, FAKE, FAKE, FAKE, 4, None) == EINVAL
+    assert g(4, 4, 3, FAKE, 3, 16, FAKE, FAKE, FAKE, 4, None) == EINVAL             # ld < n
+    assert g(4, 4, 3, None, 4, 16, FAKE, FAKE, FAKE, 4, None) == EINVAL
