@@ -1,0 +1,228 @@
+#!/usr/bin/env python
+"""Benchmark of the emulated fp64 GEMM (Ozaki scheme II through int8 MFMA) on one MI355X.
+
+One step = one ozk_dgemm call on the 4096 x 4096 x 4096 workload with entries
+(U(0,1) - 0.5) exp(0.5 N(0,1)) (seed 2) at r = 16 moduli: deconstruction of A and B,
+16 int8 MFMA products with the residue epilogue, CRT reconstruction.  Inputs are
+resident in HBM before timing starts.  `value` is emulated fp64 TFLOP/s = 2 m n k / t.
+
+Also reported on the same JSON line:
+  roofline      the dominant kernel (batched int8 MFMA products, residue epilogue) timed
+                alone with HIP events on its stream: r * 2 * m * n * kp int8 ops per launch
+                against the 5.0 POP/s dense int8 MFMA peak; HBM traffic per launch from
+                the committed rocprofv3 counter summary when it matches the kernel source.
+  cpu_baseline  the CPU oracle (numpy, one BLAS thread) on 8 full output rows.
+  extras        native fp64 DGEMM (torch.matmul), the r sweep 12..18, deconstruction HBM
+                GB/s, the GEMV and FP4-limb engines when built.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--r 16] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("emulated FP64 GEMM TFLOP/s and % int8-MFMA peak; deconstruction/GEMV HBM GB/s")
+PEAK_INT8_TOPS = 5000.0     # dense int8 MFMA, TOP/s
+PEAK_FP4_TFLOPS = 10100.0   # dense FP4 MFMA
+PEAK_HBM_GBS = 8000.0
+M = N = K = 4096
+SEED = 2
+PHI = 0.5
+
+
+def _source_digest(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "fp64_gemm_emulation_ozk_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _time_events(fn, reps: int, stream) -> float:
+    """Average milliseconds per call of fn over reps calls, HIP events on `stream`."""
+    import torch
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def _traffic(kernel: str, digest: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on this
+    exact kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel)
+    if not ent or ent.get("source_digest") != digest:
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(a, b, r: int) -> dict:
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import ozaki2
+
+    rows = np.arange(8)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        ozaki2.dgemm(a, b, r, rows=rows)
+        dt = time.perf_counter() - t0
+    flops = 2.0 * len(rows) * N * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"8 full rows of C (8 x {N} outputs; all of A's 8 rows and all of B "
+                      f"deconstructed), r={r}, numpy with 1 BLAS thread"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--r", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the emulation "
+              "path is built and measured on a single MI355X; multi-GPU runs are not "
+              "supported.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import fp64_gemm_emulation_ozk_amd as ozk
+    import ozk_inputs
+
+    if not os.path.exists(ozk.LIB_PATH):
+        from fp64_gemm_emulation_ozk_amd.build import build_library
+        build_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    r = args.r
+
+    a, b = ozk_inputs.gemm_operands(M, N, K, seed=SEED, dist="phi", phi=PHI)
+    da = torch.from_numpy(a).to(dev)
+    db = torch.from_numpy(b).to(dev)
+    out = torch.empty((M, N), dtype=torch.float64, device=dev)
+    ws = torch.empty(ozk.ozk_dgemm_workspace_size(M, N, K, r), dtype=torch.uint8, device=dev)
+    step = lambda: ozk.ozk_dgemm(da, db, r, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_events = _time_events(step, args.steps, stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_per_step = max(ms_events, 1e-9)
+    value = 2.0 * M * N * K / (ms_per_step * 1e-3) / 1e12
+
+    # Sanity: normwise distance to native fp64 (not a parity check; tests do that).
+    ref = torch.matmul(da, db)
+    rel = float(torch.linalg.norm(out - ref) / torch.linalg.norm(ref))
+
+    # Dominant kernel alone: batched int8 MFMA products with the residue epilogue.
+    planes_a, exps_a = ozk.ozk_deconstruct(da, 0, r)
+    planes_b, exps_b = ozk.ozk_deconstruct(db, 1, r, k_budget=K)
+    res = torch.empty((r, M, N), dtype=torch.int8, device=dev)
+    gemm = lambda: ozk.ozk_modular_residues(planes_a, planes_b, out=res)
+    for _ in range(2):
+        gemm()
+    gemm_ms = _time_events(gemm, args.steps, stream)
+    kp = planes_a.shape[-1]
+    ops = r * 2.0 * M * N * kp
+    achieved = ops / (gemm_ms * 1e-3) / 1e12
+    digest = _source_digest(["gemm_i8.hip"])
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                "traffic": _traffic("gemm_i8_residues", digest),
+                "kernel": "gemm_i8_kernel<residues> (v_mfma_i32_32x32x32_i8)",
+                "kernel_ms": round(gemm_ms, 4), "ops_per_launch": ops,
+                "source_digest": digest}
+
+    extras = {"wall_ms_per_step": round(wall_ms, 4), "normwise_vs_native_fp64": rel,
+              "emulated_pct_int8_peak": round(r * value / PEAK_INT8_TOPS * 100, 2)}
+    if not args.no_extras:
+        reps = max(args.steps // 2, 5)
+        nat_ms = _time_events(lambda: torch.matmul(da, db, out=ref), reps, stream)
+        extras["native_fp64_dgemm"] = {"ms": round(nat_ms, 4),
+                                       "tflops": round(2.0 * M * N * K / nat_ms / 1e9, 2)}
+        try:
+            ia = torch.randint(-128, 128, (M, K), dtype=torch.int8, device=dev)
+            ib = torch.randint(-128, 128, (K, N), dtype=torch.int8, device=dev)
+            torch._int_mm(ia, ib)
+            i8_ms = _time_events(lambda: torch._int_mm(ia, ib), reps, stream)
+            extras["library_int8_gemm"] = {
+                "what": "torch._int_mm (vendor int8 GEMM) on one 4096^3 int8 product",
+                "ms": round(i8_ms, 4), "tops": round(2.0 * M * N * K / i8_ms / 1e9, 1),
+                "ours_per_modulus_ms": round(gemm_ms / r, 4)}
+            del ia, ib
+        except RuntimeError as exc:  # not every build ships the int8 path
+            extras["library_int8_gemm"] = {"error": str(exc)[:200]}
+        sweep = []
+        for rr in range(12, 19):
+            wsr = torch.empty(ozk.ozk_dgemm_workspace_size(M, N, K, rr), dtype=torch.uint8,
+                              device=dev)
+            f = lambda: ozk.ozk_dgemm(da, db, rr, out=out, workspace=wsr)
+            f()
+            ms = _time_events(f, reps, stream)
+            sweep.append({"r": rr, "ms": round(ms, 4),
+                          "tflops": round(2.0 * M * N * K / ms / 1e9, 2)})
+            del wsr
+        extras["r_sweep"] = sweep
+        dec = lambda: ozk.ozk_deconstruct(da, 0, r, planes=planes_a, exps=exps_a)
+        dec()
+        dec_ms = _time_events(dec, reps, stream)
+        extras["deconstruct_rows"] = {
+            "ms": round(dec_ms, 4), "bytes": (8 + r) * M * K,
+            "gbs": round((8 + r) * M * K / dec_ms / 1e6, 1),
+            "frac_hbm": round((8 + r) * M * K / dec_ms / 1e6 / PEAK_HBM_GBS, 4)}
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": f"emulated DGEMM {M}x{N}x{K}, entries (U-0.5)*exp({PHI}*N(0,1)), "
+                               f"seed {SEED}, r={r} moduli",
+                   "m": M, "n": N, "k": K, "r": r, "compute": "int8 MFMA + fp64 VALU"},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(a, b, r)
+    line["extras"] = extras
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "LIB_PATH", "OzkError", "library",
     "ozk_version", "ozk_moduli", "ozk_scaling_bits", "ozk_planes_ld",
-    "ozk_deconstruct", "ozk_modular_products", "ozk_reconstruct", "ozk_dgemm", "ozk_dgemv",
+    "ozk_deconstruct", "ozk_modular_products", "ozk_modular_residues", "ozk_reconstruct", "ozk_dgemm", "ozk_dgemv",
     "ozk_fp4limb_pack", "ozk_fp4limb_products", "ozk_int8gemm_fp4limb",
     "ozk_dgemm_workspace_size", "ozk_dgemv_workspace_size",
     "ozk_int8gemm_fp4limb_workspace_size", "ozk_deconstruct_workspace_size",
@@ -42,6 +42,8 @@ _SIGNATURES = {
     "ozk_deconstruct": (_int, [_ptr, _i64, _i64, _i64, _int, _int, _i64, _ptr, _i64, _i64, _ptr,
                                _ptr, _size, _ptr]),
     "ozk_modular_products": (_int, [_i64, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64,
+                                    _i64, _ptr]),
+    "ozk_modular_residues": (_int, [_i64, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64,
                                     _i64, _ptr]),
     "ozk_reconstruct": (_int, [_i64, _i64, _int, _ptr, _i64, _i64, _ptr, _ptr, _ptr, _i64, _ptr]),
     "ozk_dgemm_workspace_size": (_int, [_i64, _i64, _i64, _int, _ptr]),
@@ -198,6 +200,22 @@ def ozk_modular_products(planes_a: torch.Tensor, planes_b: torch.Tensor, r: int 
     if out is None:
         out = torch.empty((r, m, n), dtype=torch.int32, device=planes_a.device)
     _call("ozk_modular_products", m, n, kp, r, _dev_ptr(planes_a), planes_a.stride(0),
+          _dev_ptr(planes_b), planes_b.stride(0), _dev_ptr(out), out.stride(1), out.stride(0),
+          _stream(stream))
+    return out
+
+
+def ozk_modular_residues(planes_a: torch.Tensor, planes_b: torch.Tensor, r: int | None = None,
+                         out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """int8 [r][m][n]: symmetric residues of the exact plane products modulo m_l."""
+    _check(planes_a, torch.int8, "planes_a", 3)
+    _check(planes_b, torch.int8, "planes_b", 3)
+    r = planes_a.shape[0] if r is None else r
+    _, m, kp = planes_a.shape
+    n = planes_b.shape[1]
+    if out is None:
+        out = torch.empty((r, m, n), dtype=torch.int8, device=planes_a.device)
+    _call("ozk_modular_residues", m, n, kp, r, _dev_ptr(planes_a), planes_a.stride(0),
           _dev_ptr(planes_b), planes_b.stride(0), _dev_ptr(out), out.stride(1), out.stride(0),
           _stream(stream))
     return out

@@ -141,6 +141,21 @@ int ozk_modular_products(int64_t m, int64_t n, int64_t kp, int r, const int8_t* 
                         kEpiProducts, as_stream(stream));
 }
 
+int ozk_modular_residues(int64_t m, int64_t n, int64_t kp, int r, const int8_t* pa,
+                         int64_t stride_a, const int8_t* pb, int64_t stride_b, int8_t* residues,
+                         int64_t ldr, int64_t stride_r, void* stream) {
+  if (check_r(r) != OZK_OK) return OZK_EINVAL;
+  if (m < 0 || n < 0 || kp <= 0 || kp % kPlaneK != 0) return OZK_EINVAL;
+  if (kp > round_up(OZK_MAX_K, kPlaneK)) return OZK_ERANGE;
+  if (ldr < (n > 0 ? n : 1) || stride_r < m * ldr) return OZK_EINVAL;
+  if (stride_a < m * kp || stride_b < n * kp) return OZK_EINVAL;
+  if (stride_a % 16 || stride_b % 16) return OZK_EINVAL;
+  if (m == 0 || n == 0) return OZK_OK;
+  if (!pa || !pb || !residues || !aligned(pa, 16) || !aligned(pb, 16)) return OZK_EINVAL;
+  return launch_gemm_i8(m, n, kp, r, pa, stride_a, pb, stride_b, residues, ldr, stride_r,
+                        kEpiResidues, as_stream(stream));
+}
+
 int ozk_reconstruct(int64_t m, int64_t n, int r, const int32_t* products, int64_t ldp_in,
                     int64_t stride_p, const int32_t* exps_a, const int32_t* exps_b, double* C,
                     int64_t ldc, void* stream) {

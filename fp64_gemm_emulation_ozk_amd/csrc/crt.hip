@@ -1,5 +1,5 @@
 // CRT reconstruction and inverse scaling: the per-output reconstruction term of Ozaki
-// scheme II ([TME4] abstract).  One thread per output.
+// scheme II ([TME4] abstract).  Each thread reconstructs 4 consecutive outputs of a row.
 //
 // Given symmetric residues c_l (|c_l| <= 128) of the exact integer X modulo m_l:
 //   1. q = round(sum_l c_l * RN(E_l / M)).  The exact value of the sum is q + X/M with
@@ -11,38 +11,49 @@
 //      packed into three 64-bit words, and RN(|X| 2^-s) is formed by integer rounding
 //      (half to even) at the precision of the result's binade: 53 bits for a normal
 //      result, fewer for a subnormal one, so the output is rounded exactly once.
+// The constants come from the compile-time table in __constant__ memory; each block
+// stages the r(L+1)+L values it needs in LDS (compile-time r), and every constant is
+// read once per 4 outputs, so none of them has to live in scalar registers.
 #include "ozk_internal.h"
+#include "rns_table.h"
 
 namespace ozk {
+
+__constant__ RnsTable d_rns = make_rns_table();
+
 namespace {
 
-__device__ __forceinline__ int clz64(uint64_t x) { return __builtin_clzll(x); }
+__device__ __forceinline__ uint64_t u64_of(double d) {  // d integer in [0, 2^53)
+  const double hi = __builtin_floor(d * 0x1p-32);
+  const double lo = __builtin_fma(-hi, 0x1p32, d);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo;
+}
 
 // RN(mag * 2^-s) for mag = w2:w1:w0 (little-endian 64-bit words), mag != 0.
-__device__ double round_scaled_words(uint64_t w0, uint64_t w1, uint64_t w2, int s) {
+__device__ __forceinline__ double round_scaled_words(uint64_t w0, uint64_t w1, uint64_t w2,
+                                                     int s) {
   uint64_t top;
   bool sticky;
   int lead;  // bit index of the leading 1 of mag
   if (w2) {
-    int sh = clz64(w2);
+    const int sh = __builtin_clzll(w2);
     top = sh ? (w2 << sh) | (w1 >> (64 - sh)) : w2;
     sticky = (sh ? (w1 << sh) : w1) != 0 || w0 != 0;
     lead = 191 - sh;
   } else if (w1) {
-    int sh = clz64(w1);
+    const int sh = __builtin_clzll(w1);
     top = sh ? (w1 << sh) | (w0 >> (64 - sh)) : w1;
     sticky = (sh ? (w0 << sh) : w0) != 0;
     lead = 127 - sh;
   } else {
-    int sh = clz64(w0);
+    const int sh = __builtin_clzll(w0);
     top = w0 << sh;
     sticky = false;
     lead = 63 - sh;
   }
-  // Result exponent: mag * 2^-s lies in [2^E, 2^(E+1)).
-  const int E = lead - s;
+  const int E = lead - s;  // mag * 2^-s lies in [2^E, 2^(E+1))
   if (E > 1023) return __builtin_huge_val();
-  int keep = E >= -1022 ? 53 : E + 1075;  // significant bits the result can hold
+  const int keep = E >= -1022 ? 53 : E + 1075;  // significant bits the result holds
   if (keep < 0) return 0.0;
   uint64_t mant;
   bool up;
@@ -57,93 +68,188 @@ __device__ double round_scaled_words(uint64_t w0, uint64_t w1, uint64_t w2, int 
     up = rem > half || (rem == half && (sticky || (mant & 1)));
   }
   mant += up ? 1 : 0;
-  if (E >= -1022) return __builtin_ldexp((double)mant, E - 52);
-  return __builtin_ldexp((double)mant, -1074);
+  // mant <= 2^53: the conversion is exact; ldexp scales exactly (or overflows to Inf).
+  return __builtin_ldexp((double)mant, E >= -1022 ? E - 52 : -1074);
+}
+
+// Exact integer X of 4 outputs from their residues and the RNS constants in LDS,
+// rounded to fp64 with the shift s[u].
+template <int R>
+__device__ __forceinline__ void reconstruct4(const int32_t (&word)[R], const double* __restrict__ sc,
+                                             const int (&s)[4], const bool (&nan)[4],
+                                             double (&out)[4]) {
+  constexpr int L = R <= 15 ? 3 : 4;
+  // sc layout: frac[R], e[R][L], m[L]
+  double qf[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int l = 0; l < R; ++l) {
+    const double fr = sc[l];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      qf[u] = __builtin_fma((double)(int)(int8_t)(word[l] >> (8 * u)), fr, qf[u]);
+  }
+  double x[4][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const double q = __builtin_rint(qf[u]);
+#pragma unroll
+    for (int p = 0; p < L; ++p) x[u][p] = -q * sc[R + R * L + p];  // |q| < 2^11.4: exact
+#pragma unroll
+    for (int p = L; p < 4; ++p) x[u][p] = 0.0;
+  }
+#pragma unroll
+  for (int l = 0; l < R; ++l) {
+    double cd[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cd[u] = (double)(int)(int8_t)(word[l] >> (8 * u));
+#pragma unroll
+    for (int p = 0; p < L; ++p) {
+      const double e = sc[R + l * L + p];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u][p] = __builtin_fma(cd[u], e, x[u][p]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    double* xu = x[u];
+#pragma unroll
+    for (int p = 0; p < L - 1; ++p) {  // digits 0..L-2 in [0, 2^40); sign in digit L-1
+      const double carry = __builtin_floor(xu[p] * 0x1p-40);
+      xu[p] = __builtin_fma(-carry, 0x1p40, xu[p]);
+      xu[p + 1] += carry;
+    }
+    const bool neg = xu[L - 1] < 0.0;
+    if (neg) {
+#pragma unroll
+      for (int p = 0; p < L; ++p) xu[p] = -xu[p];
+#pragma unroll
+      for (int p = 0; p < L - 1; ++p) {
+        const double carry = __builtin_floor(xu[p] * 0x1p-40);
+        xu[p] = __builtin_fma(-carry, 0x1p40, xu[p]);
+        xu[p + 1] += carry;
+      }
+    }
+    const uint64_t d0 = u64_of(xu[0]), d1 = u64_of(xu[1]), d2 = u64_of(xu[2]);
+    const uint64_t d3 = L > 3 ? u64_of(xu[3]) : 0;
+    const uint64_t w0 = d0 | (d1 << 40);
+    const uint64_t w1 = (d1 >> 24) | (d2 << 16) | (d3 << 56);
+    const uint64_t w2 = d3 >> 8;
+    double o = 0.0;
+    if ((w0 | w1 | w2) != 0) {
+      o = round_scaled_words(w0, w1, w2, s[u]);
+      o = neg ? -o : o;
+    }
+    out[u] = nan[u] ? __builtin_nan("") : o;
+  }
 }
 
 template <typename T>
+__device__ __forceinline__ int symmetric(T v, int l, int mod) {
+  if (sizeof(T) == 1) return (int)v;
+  // raw int32 products: reduce to the symmetric residue first
+  if (mod == 256) return (int)(int8_t)(v & 0xff);
+  constexpr double kMagicD = 6755399441055744.0;
+  const double d = (double)v;
+  const double q = __builtin_fma(d, d_rns.inv[l], kMagicD) - kMagicD;
+  return (int)__builtin_fma(-q, (double)mod, d);
+}
+
+template <int R, typename T>
 __global__ __launch_bounds__(256) void crt_kernel(int64_t m, int64_t n, const T* __restrict__ res,
                                                   int64_t ldr, int64_t stride_r,
                                                   const int32_t* __restrict__ ea,
                                                   const int32_t* __restrict__ eb,
-                                                  double* __restrict__ c, int64_t ldc,
-                                                  CrtConsts K) {
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (j >= n) return;
-  const int32_t f_j = eb[j];
+                                                  double* __restrict__ c, int64_t ldc) {
+  constexpr int L = R <= 15 ? 3 : 4;
+  constexpr int kConsts = R + R * L + L;
+  __shared__ double sc[kConsts];
+  for (int t = threadIdx.x; t < kConsts; t += blockDim.x) {
+    double v;
+    if (t < R)
+      v = d_rns.frac[R][t];
+    else if (t < R + R * L)
+      v = d_rns.e_limb[R][(t - R) / L][(t - R) % L];
+    else
+      v = d_rns.m_limb[R][t - R - R * L];
+    sc[t] = v;
+  }
+  __syncthreads();
+  const int64_t j0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (j0 >= n) return;
+  const int cnt = n - j0 >= 4 ? 4 : (int)(n - j0);
+  int f[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) f[u] = u < cnt ? eb[j0 + u] : 0;
+  const bool vec = cnt == 4 && sizeof(T) == 1 && ((ldr | stride_r | j0) & 3) == 0;
   for (int64_t i = blockIdx.y; i < m; i += gridDim.y) {
-  const int32_t e_i = ea[i];
-  double* dst = c + i * ldc + j;
-  if (e_i == INT32_MIN || f_j == INT32_MIN) {
-    *dst = __builtin_nan("");
-    continue;
-  }
-  constexpr double kMagicD = 6755399441055744.0;
-  const int r = K.r;
-  double cd[kMaxModuli];
-  double qf = 0.0;
-  const T* src = res + i * ldr + j;
+    const int32_t e_i = ea[i];
+    const T* src = res + i * ldr + j0;
+    // Symmetric residues of the 4 outputs, one byte each, packed per modulus.
+    int32_t word[R];
+    if (vec) {
 #pragma unroll
-  for (int l = 0; l < kMaxModuli; ++l) {
-    if (l < r) {
-      int v = (int)src[l * stride_r];
-      if (sizeof(T) == 4) {  // raw products: reduce to the symmetric residue first
-        const int mod = K.mod[l];
-        if (mod == 256) {
-          v = (int)(int8_t)(v & 0xff);
-        } else {
-          double d = (double)v;
-          double q = __builtin_fma(d, K.inv[l], kMagicD) - kMagicD;
-          v = (int)__builtin_fma(-q, (double)mod, d);
-        }
-      }
-      cd[l] = (double)v;
-      qf = __builtin_fma(cd[l], K.frac[l], qf);
+      for (int l = 0; l < R; ++l) word[l] = *reinterpret_cast<const int32_t*>(src + l * stride_r);
     } else {
-      cd[l] = 0.0;
+#pragma unroll
+      for (int l = 0; l < R; ++l) {
+        uint32_t w = 0;
+        for (int u = 0; u < cnt; ++u)
+          w |= ((uint32_t)symmetric<T>(src[l * stride_r + u], l, d_rns.moduli[l]) & 0xffu)
+               << (8 * u);
+        word[l] = (int32_t)w;
+      }
     }
-  }
-  const double q = __builtin_rint(qf);
-  double x[kMaxLimbs];
+    int s[4];
+    bool nan[4];
 #pragma unroll
-  for (int p = 0; p < kMaxLimbs; ++p) {
-    double t = -q * K.m_limb[p];  // |q| < 2^11.4, limb < 2^40: exact
-#pragma unroll
-    for (int l = 0; l < kMaxModuli; ++l)
-      if (l < r) t = __builtin_fma(cd[l], K.e_limb[l][p], t);
-    x[p] = t;
-  }
-  // Normalise: digits 0..2 in [0, 2^40), the sign in digit 3.
-#pragma unroll
-  for (int p = 0; p < kMaxLimbs - 1; ++p) {
-    double carry = __builtin_floor(x[p] * 0x1p-40);
-    x[p] = __builtin_fma(-carry, 0x1p40, x[p]);
-    x[p + 1] += carry;
-  }
-  const bool neg = x[kMaxLimbs - 1] < 0.0;
-  if (neg) {
-#pragma unroll
-    for (int p = 0; p < kMaxLimbs; ++p) x[p] = -x[p];
-#pragma unroll
-    for (int p = 0; p < kMaxLimbs - 1; ++p) {
-      double carry = __builtin_floor(x[p] * 0x1p-40);
-      x[p] = __builtin_fma(-carry, 0x1p40, x[p]);
-      x[p + 1] += carry;
+    for (int u = 0; u < 4; ++u) {
+      s[u] = e_i + f[u];
+      nan[u] = e_i == INT32_MIN || f[u] == INT32_MIN;
     }
-  }
-  const uint64_t d0 = (uint64_t)x[0], d1 = (uint64_t)x[1], d2 = (uint64_t)x[2],
-                 d3 = (uint64_t)x[3];
-  const uint64_t w0 = d0 | (d1 << 40);
-  const uint64_t w1 = (d1 >> 24) | (d2 << 16) | (d3 << 56);
-  const uint64_t w2 = d3 >> 8;
-  double out = 0.0;
-  if (w0 | w1 | w2) {
-    out = round_scaled_words(w0, w1, w2, e_i + f_j);
-    if (neg) out = -out;
-  }
-  *dst = out;
+    double out[4];
+    reconstruct4<R>(word, sc, s, nan, out);
+    double* dst = c + i * ldc + j0;
+    if (cnt == 4 && ((ldc | j0) & 1) == 0) {
+      *reinterpret_cast<double2*>(dst) = make_double2(out[0], out[1]);
+      *reinterpret_cast<double2*>(dst + 2) = make_double2(out[2], out[3]);
+    } else {
+      for (int u = 0; u < cnt; ++u) dst[u] = out[u];
+    }
   }
 }
+
+template <int R>
+void launch_r(dim3 grid, hipStream_t s, int64_t m, int64_t n, const void* res, int is_i32,
+              int64_t ldr, int64_t stride_r, const int32_t* ea, const int32_t* eb, double* c,
+              int64_t ldc) {
+  if (is_i32)
+    hipLaunchKernelGGL((crt_kernel<R, int32_t>), grid, dim3(256), 0, s, m, n,
+                       (const int32_t*)res, ldr, stride_r, ea, eb, c, ldc);
+  else
+    hipLaunchKernelGGL((crt_kernel<R, int8_t>), grid, dim3(256), 0, s, m, n, (const int8_t*)res,
+                       ldr, stride_r, ea, eb, c, ldc);
+}
+
+template <int... Rs>
+struct Dispatch;
+
+template <>
+struct Dispatch<> {
+  static void go(int, dim3, hipStream_t, int64_t, int64_t, const void*, int, int64_t, int64_t,
+                 const int32_t*, const int32_t*, double*, int64_t) {}
+};
+
+template <int R0, int... Rs>
+struct Dispatch<R0, Rs...> {
+  static void go(int r, dim3 g, hipStream_t s, int64_t m, int64_t n, const void* res, int i32,
+                 int64_t ldr, int64_t sr, const int32_t* ea, const int32_t* eb, double* c,
+                 int64_t ldc) {
+    if (r == R0)
+      launch_r<R0>(g, s, m, n, res, i32, ldr, sr, ea, eb, c, ldc);
+    else
+      Dispatch<Rs...>::go(r, g, s, m, n, res, i32, ldr, sr, ea, eb, c, ldc);
+  }
+};
 
 }  // namespace
 
@@ -151,14 +257,10 @@ int launch_crt(int64_t m, int64_t n, int r, const void* res, int res_is_i32, int
                int64_t stride_r, const int32_t* ea, const int32_t* eb, double* c, int64_t ldc,
                hipStream_t s) {
   if (m <= 0 || n <= 0) return OZK_OK;
-  const CrtConsts& K = *crt_consts(r);
-  dim3 grid((unsigned)((n + 255) / 256), (unsigned)(m < 65535 ? m : 65535));
-  if (res_is_i32)
-    hipLaunchKernelGGL(crt_kernel<int32_t>, grid, dim3(256), 0, s, m, n,
-                       (const int32_t*)res, ldr, stride_r, ea, eb, c, ldc, K);
-  else
-    hipLaunchKernelGGL(crt_kernel<int8_t>, grid, dim3(256), 0, s, m, n, (const int8_t*)res, ldr,
-                       stride_r, ea, eb, c, ldc, K);
+  if (r < 1 || r > kMaxModuli) return OZK_EINVAL;
+  dim3 grid((unsigned)((n + 1023) / 1024), (unsigned)(m < 65535 ? m : 65535));
+  Dispatch<1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20>::go(
+      r, grid, s, m, n, res, res_is_i32, ldr, stride_r, ea, eb, c, ldc);
   return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
 }
 

@@ -66,40 +66,71 @@ __global__ __launch_bounds__(256) void absmax_cols_kernel(const double* __restri
   const int64_t r0 = (int64_t)blockIdx.y * 64;
   const int64_t r1 = r0 + 64 < rows ? r0 + 64 : rows;
   uint64_t v = 0;
+#pragma unroll 16
   for (int64_t h = r0; h < r1; ++h) v = umax64(v, abs_bits(x[h * ldx + col]));
   atomicMax((unsigned long long*)&maxbits[col], (unsigned long long)v);
 }
 
-// Residues of 8 prepared elements for every modulus, stored as 8 bytes per plane.
-template <bool kWide>
-__device__ __forceinline__ void store_residues8(const double (&a)[8], int e,
-                                                const ResidueConsts& K, int8_t* dst,
-                                                int64_t plane_stride) {
-  Prepared p[8];
+// Residues of kN (8 or 16) consecutive prepared elements for every modulus, stored as
+// kN bytes per plane.
+template <int kN>
+struct Bytes;
+template <>
+struct Bytes<8> {
+  typedef uint2 type;
+};
+template <>
+struct Bytes<16> {
+  typedef uint4 type;
+};
+
+template <bool kWide, int kN>
+__device__ __forceinline__ void store_residues(const double (&a)[kN], int e,
+                                               const ResidueConsts& K, int8_t* dst,
+                                               int64_t plane_stride) {
+  typedef typename Bytes<kN>::type V;
+  Prepared p[kN];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) p[u] = prepare_element<kWide>(a[u], e);
+  for (int u = 0; u < kN; ++u) p[u] = prepare_element<kWide>(a[u], e);
   {
-    uint2 w;
-    w.x = pack4(residue_byte_256(p[0]), residue_byte_256(p[1]), residue_byte_256(p[2]),
-                residue_byte_256(p[3]));
-    w.y = pack4(residue_byte_256(p[4]), residue_byte_256(p[5]), residue_byte_256(p[6]),
-                residue_byte_256(p[7]));
-    *reinterpret_cast<uint2*>(dst) = w;
+    uint32_t w[kN / 4];
+#pragma unroll
+    for (int q = 0; q < kN / 4; ++q)
+      w[q] = pack4(residue_byte_256(p[4 * q]), residue_byte_256(p[4 * q + 1]),
+                   residue_byte_256(p[4 * q + 2]), residue_byte_256(p[4 * q + 3]));
+    *reinterpret_cast<V*>(dst) = *reinterpret_cast<const V*>(w);
   }
   for (int l = 1; l < K.r; ++l) {
     const double m = K.m[l], inv = K.inv[l], c = K.c32[l];
-    uint32_t b[8];
+    uint32_t b[kN];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) b[u] = residue_byte<kWide>(p[u], m, inv, c);
-    uint2 w;
-    w.x = pack4(b[0], b[1], b[2], b[3]);
-    w.y = pack4(b[4], b[5], b[6], b[7]);
-    *reinterpret_cast<uint2*>(dst + l * plane_stride) = w;
+    for (int u = 0; u < kN; ++u) b[u] = residue_byte<kWide>(p[u], m, inv, c);
+    uint32_t w[kN / 4];
+#pragma unroll
+    for (int q = 0; q < kN / 4; ++q) w[q] = pack4(b[4 * q], b[4 * q + 1], b[4 * q + 2], b[4 * q + 3]);
+    *reinterpret_cast<V*>(dst + l * plane_stride) = *reinterpret_cast<const V*>(w);
+  }
+}
+
+// 8 consecutive elements x[h0 .. h0+7] (0 beyond cols), 16-byte loads when aligned.
+template <bool kVec>
+__device__ __forceinline__ void load8(const double* __restrict__ xr, int64_t h0, int64_t cols,
+                                      double (&a)[8]) {
+  if (kVec && h0 + 8 <= cols) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const double2 v = *reinterpret_cast<const double2*>(xr + h0 + 2 * u);
+      a[2 * u] = v.x;
+      a[2 * u + 1] = v.y;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] = h0 + u < cols ? xr[h0 + u] : 0.0;
   }
 }
 
 // Row residues with exponents from maxbits: grid (ldp / 2048 chunks, rows).
-template <bool kWide>
+template <bool kWide, bool kVec>
 __global__ __launch_bounds__(256) void residues_rows_kernel(
     const double* __restrict__ x, int64_t cols, int64_t ldx, ResidueConsts K, int p_bits,
     const uint64_t* __restrict__ maxbits, int8_t* __restrict__ planes, int64_t ldp,
@@ -111,42 +142,35 @@ __global__ __launch_bounds__(256) void residues_rows_kernel(
   if (h0 >= ldp) return;
   const double* xr = x + row * ldx;
   double a[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    int64_t h = h0 + u;
-    a[u] = (h < cols && e != INT32_MIN) ? xr[h] : 0.0;
-  }
+  load8<kVec>(xr, h0, e == INT32_MIN ? 0 : cols, a);
   int8_t* dst = planes + row * ldp + h0;
-  store_residues8<kWide>(a, e == INT32_MIN ? 0 : e, K, dst, plane_stride);
+  store_residues<kWide, 8>(a, e == INT32_MIN ? 0 : e, K, dst, plane_stride);
 }
 
-// Column residues: grid (ceil(cols/64), ldp/64); thread t owns column j0 + (t & 63)
-// and K rows h0 + 16*(t >> 6) .. +15, stored as 16 contiguous bytes per plane.
+// Column residues: grid (ceil(cols/64), ldp/64).  Lane t owns column j0 + (t >> 2) and
+// K rows h0 + 16*(t & 3) .. +15; four consecutive lanes store 64 contiguous bytes of
+// one plane row (16 bytes each), and each load instruction reads 4 rows x 16 columns.
 template <bool kWide>
 __global__ __launch_bounds__(256) void residues_cols_kernel(
     const double* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, ResidueConsts K,
     int p_bits, const uint64_t* __restrict__ maxbits, int8_t* __restrict__ planes,
     int64_t ldp, int64_t plane_stride, int32_t* __restrict__ exps) {
-  const int64_t col = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+  const int64_t col = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
   if (col >= cols) return;
   const int e = line_exponent(maxbits[col], p_bits);
-  const int64_t h0 = (int64_t)blockIdx.y * 64 + (threadIdx.x >> 6) * 16;
-  if (blockIdx.y == 0 && threadIdx.x < 64) exps[col] = e;
-  int8_t* dst = planes + col * ldp + h0;
+  const int64_t h0 = (int64_t)blockIdx.y * 64 + (threadIdx.x & 3) * 16;
+  if (blockIdx.y == 0 && (threadIdx.x & 3) == 0) exps[col] = e;
+  double a[16];
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    double a[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      int64_t h = h0 + half * 8 + u;
-      a[u] = (h < rows && e != INT32_MIN) ? x[h * ldx + col] : 0.0;
-    }
-    store_residues8<kWide>(a, e == INT32_MIN ? 0 : e, K, dst + half * 8, plane_stride);
+  for (int u = 0; u < 16; ++u) {
+    const int64_t h = h0 + u;
+    a[u] = (h < rows && e != INT32_MIN) ? x[h * ldx + col] : 0.0;
   }
+  store_residues<kWide, 16>(a, e == INT32_MIN ? 0 : e, K, planes + col * ldp + h0, plane_stride);
 }
 
 // One workgroup per row, the row in registers: kNT threads x kG groups of 8 elements.
-template <bool kWide, int kNT, int kG>
+template <bool kWide, bool kVec, int kNT, int kG>
 __global__ __launch_bounds__(kNT) void residues_rows_fused_kernel(
     const double* __restrict__ x, int64_t cols, int64_t ldx, ResidueConsts K, int p_bits,
     int8_t* __restrict__ planes, int64_t ldp, int64_t plane_stride,
@@ -158,12 +182,9 @@ __global__ __launch_bounds__(kNT) void residues_rows_fused_kernel(
 #pragma unroll
   for (int g = 0; g < kG; ++g) {
     const int64_t h0 = ((int64_t)g * kNT + threadIdx.x) * 8;
+    load8<kVec>(xr, h0, cols, a[g]);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      int64_t h = h0 + u;
-      a[g][u] = h < cols ? xr[h] : 0.0;
-      v = umax64(v, abs_bits(a[g][u]));
-    }
+    for (int u = 0; u < 8; ++u) v = umax64(v, abs_bits(a[g][u]));
   }
   v = wave_max_u64(v);
   __shared__ uint64_t part[kNT / 64];
@@ -190,7 +211,7 @@ __global__ __launch_bounds__(kNT) void residues_rows_fused_kernel(
 #pragma unroll
       for (int u = 0; u < 8; ++u) a[g][u] = 0.0;
     }
-    store_residues8<kWide>(a[g], e, K, prow + h0, plane_stride);
+    store_residues<kWide, 8>(a[g], e, K, prow + h0, plane_stride);
   }
   // Padding beyond the register-resident part (only when ldp exceeds kNT * kG * 8).
   for (int64_t h0 = ((int64_t)kG * kNT + threadIdx.x) * 8; h0 < ldp; h0 += (int64_t)kNT * 8) {
@@ -203,8 +224,14 @@ template <bool kWide, int kNT, int kG>
 int launch_fused(const double* x, int64_t rows, int64_t cols, int64_t ldx,
                  const ResidueConsts& K, int p_bits, int8_t* planes, int64_t ldp,
                  int64_t plane_stride, int32_t* exps, hipStream_t s) {
-  hipLaunchKernelGGL((residues_rows_fused_kernel<kWide, kNT, kG>), dim3((unsigned)rows),
-                     dim3(kNT), 0, s, x, cols, ldx, K, p_bits, planes, ldp, plane_stride, exps);
+  const bool vec = (reinterpret_cast<uintptr_t>(x) & 15) == 0 && (ldx & 1) == 0;
+  if (vec)
+    hipLaunchKernelGGL((residues_rows_fused_kernel<kWide, true, kNT, kG>), dim3((unsigned)rows),
+                       dim3(kNT), 0, s, x, cols, ldx, K, p_bits, planes, ldp, plane_stride, exps);
+  else
+    hipLaunchKernelGGL((residues_rows_fused_kernel<kWide, false, kNT, kG>),
+                       dim3((unsigned)rows), dim3(kNT), 0, s, x, cols, ldx, K, p_bits, planes,
+                       ldp, plane_stride, exps);
   return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
 }
 
@@ -221,6 +248,7 @@ int launch_absmax(const double* x, int64_t rows, int64_t cols, int64_t ldx, int 
                   uint64_t* maxbits, hipStream_t s) {
   if (rows <= 0 || cols <= 0) return OZK_OK;
   if (axis == 0) {
+    if (rows > 65535) return OZK_EUNSUPPORTED;
     dim3 grid((unsigned)((cols + 2047) / 2048), (unsigned)rows);
     hipLaunchKernelGGL(absmax_rows_kernel, grid, dim3(256), 0, s, x, cols, ldx, maxbits);
   } else {
@@ -237,13 +265,17 @@ int launch_residues(const double* x, int64_t rows, int64_t cols, int64_t ldx, in
   const bool wide = K.wide != 0;
   if (axis == 0) {
     if (rows <= 0) return OZK_OK;
+    if (rows > 65535) return OZK_EUNSUPPORTED;
     dim3 grid((unsigned)((ldp + 2047) / 2048), (unsigned)rows);
-    if (wide)
-      hipLaunchKernelGGL(residues_rows_kernel<true>, grid, dim3(256), 0, s, x, cols, ldx, K,
-                         p_bits, maxbits, planes, ldp, plane_stride, exps);
-    else
-      hipLaunchKernelGGL(residues_rows_kernel<false>, grid, dim3(256), 0, s, x, cols, ldx, K,
-                         p_bits, maxbits, planes, ldp, plane_stride, exps);
+    const bool vec = (reinterpret_cast<uintptr_t>(x) & 15) == 0 && (ldx & 1) == 0;
+#define OZK_ROWS(W, V)                                                                     \
+  hipLaunchKernelGGL((residues_rows_kernel<W, V>), grid, dim3(256), 0, s, x, cols, ldx, K, \
+                     p_bits, maxbits, planes, ldp, plane_stride, exps)
+    if (wide && vec) OZK_ROWS(true, true);
+    else if (wide) OZK_ROWS(true, false);
+    else if (vec) OZK_ROWS(false, true);
+    else OZK_ROWS(false, false);
+#undef OZK_ROWS
   } else {
     if (cols <= 0) return OZK_OK;
     dim3 grid((unsigned)((cols + 63) / 64), (unsigned)(ldp / 64));

@@ -6,14 +6,20 @@
 // transposed by the deconstruction), kp a multiple of 64 and zero-padded, so the K loop
 // has no tail.  |residue| <= 128 and kp <= 131072 keep every int32 sum exact.
 //
-// Tiling: workgroup tile 256 x 128 x 64, 256 threads = 4 waves, each wave a 128 x 64
-// block of 4 x 2 MFMA tiles of 32 x 32 (128 accumulator registers).  Global tiles go
-// through registers into double-buffered LDS (48 KiB); LDS rows are 64 bytes with the
-// four 16-byte chunks XOR-swizzled by (row >> 1) & 3 so that the 16-byte fragment reads
-// of 8 consecutive rows hit 8 distinct bank groups.
+// Tiling: workgroup tile 256 x 256 x 64, 256 threads = 4 waves, each wave a 128 x 128
+// block of 4 x 4 MFMA tiles of 32 x 32 (256 accumulator registers, held in AGPRs), so
+// every 16-byte LDS fragment read feeds two MFMAs.  Global tiles go through two sets of
+// registers into double-buffered LDS (64 KiB), with the MFMA, LDS and global-memory
+// instructions of each K sub-step interleaved explicitly (see the pipeline below); LDS rows are 64 bytes with the four 16-byte chunks
+// XOR-swizzled by (row >> 1) & 3 so that the fragment reads of 8 consecutive rows hit 8
+// distinct bank groups.  Workgroups are mapped XCD by XCD (the hardware deals them out
+// round-robin over the 8 XCDs) onto contiguous runs of tiles, ordered in groups of 4
+// tile rows, so the tiles in flight on one XCD share A rows and B columns in its L2.
 //
 // Epilogues: the int32 products themselves, or their symmetric residues modulo m_l as
 // int8 (what the CRT reconstruction consumes: 1 byte instead of 4 per output).
+#include <type_traits>
+
 #include "ozk_internal.h"
 
 namespace ozk {
@@ -22,7 +28,9 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 256, BN = 128, BK = 64;
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kGroupM = 4;
+constexpr int kXcds = 8;
 constexpr int kThreads = 256;
 constexpr int kLdsA = BM * BK;   // bytes per stage
 constexpr int kLdsB = BN * BK;
@@ -46,19 +54,25 @@ __device__ __forceinline__ int sym_residue(int v, int m, double inv) {
 }
 
 template <int kEpi>
-__global__ __launch_bounds__(kThreads, 2) void gemm_i8_kernel(
+__global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     int64_t m, int64_t n, int64_t kp, const int8_t* __restrict__ pa, int64_t stride_a,
     const int8_t* __restrict__ pb, int64_t stride_b, void* __restrict__ out, int64_t ldo,
     int64_t stride_o, int tiles_m, int tiles_n, EpiModuli E) {
   __shared__ __attribute__((aligned(16))) int8_t lds[2 * (kLdsA + kLdsB)];
 
-  // Block -> (modulus, tile row, tile column), tile columns fastest.
-  const int bid = blockIdx.x;
+  // Block -> (modulus, tile row, tile column): XCD-contiguous, then grouped by kGroupM.
+  const int total = gridDim.x;
+  int bid = blockIdx.x;
+  if (total % kXcds == 0) bid = (bid % kXcds) * (total / kXcds) + bid / kXcds;
   const int per_mod = tiles_m * tiles_n;
   const int l = bid / per_mod;
   const int rem = bid - l * per_mod;
-  const int tm = rem / tiles_n;
-  const int tn = rem - tm * tiles_n;
+  const int per_group = kGroupM * tiles_n;
+  const int first_m = (rem / per_group) * kGroupM;
+  const int gsize = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+  const int in_group = rem % per_group;
+  const int tm = first_m + in_group % gsize;
+  const int tn = in_group / gsize;
 
   const int8_t* A = pa + l * stride_a;
   const int8_t* B = pb + l * stride_b;
@@ -69,7 +83,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_i8_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wr = wave >> 1;   // 0..1: rows wr*128
-  const int wc = wave & 1;    // 0..1: cols wc*64
+  const int wc = wave & 1;    // 0..1: cols wc*128
 
   // Global load assignment: 16-byte chunk q = tid + 256*s, row q >> 2, chunk q & 3.
   const int64_t last_a = m - 1, last_b = n - 1;
@@ -84,10 +98,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_i8_kernel(
     ga[s] = A + gr * kp + c * 16;
     sa[s] = swz(r, c);
   }
-  const int8_t* gb[2];
-  int sb[2];
+  const int8_t* gb[4];
+  int sb[4];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < 4; ++s) {
     int q = tid + kThreads * s;
     int r = q >> 2, c = q & 3;
     int64_t gr = col0 + r;
@@ -96,67 +110,104 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_i8_kernel(
     sb[s] = swz(r, c);
   }
 
-  v16i acc[4][2];
+  v16i acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
 
-  v4i ra[4], rb[2];
-  auto load_global = [&](int64_t k0) {
+  // Software pipeline over K tiles of 64 (two MFMA sub-steps of K = 32 each):
+  //   sub-step 0 of tile t: 16 MFMAs on fragments (t, 0), interleaved with the global
+  //     loads of tile t+2 into register set t%2, the LDS writes of tile t+1 (register
+  //     set (t+1)%2, loaded one tile earlier) and the fragment reads of (t, 1);
+  //   sub-step 1 of tile t: barrier (tile t+1 visible), then 16 MFMAs on (t, 1)
+  //     interleaved with the fragment reads of (t+1, 0).
+  // Loads past the last tile are clamped to it (in bounds, results unused), so each
+  // sub-step is a single basic block that the scheduling groups below can interleave.
+  v4i ra[2][4], rb[2][4];   // global tiles in flight
+  v4i fa[2][4], fb[2][4];   // MFMA fragments of the current and next sub-step
+  const int64_t nk = kp / BK;
+  auto load_global = [&](v4i (&xa)[4], v4i (&xb)[4], int64_t t) {
+    const int64_t k0 = (t < nk ? t : nk - 1) * BK;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) ra[s] = *reinterpret_cast<const v4i*>(ga[s] + k0);
+    for (int s = 0; s < 4; ++s) xa[s] = *reinterpret_cast<const v4i*>(ga[s] + k0);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) rb[s] = *reinterpret_cast<const v4i*>(gb[s] + k0);
+    for (int s = 0; s < 4; ++s) xb[s] = *reinterpret_cast<const v4i*>(gb[s] + k0);
   };
-  auto store_lds = [&](int buf) {
+  auto store_lds = [&](int buf, const v4i (&xa)[4], const v4i (&xb)[4]) {
     int8_t* la = lds + buf * (kLdsA + kLdsB);
     int8_t* lb = la + kLdsA;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) *reinterpret_cast<v4i*>(la + sa[s]) = ra[s];
+    for (int s = 0; s < 4; ++s) *reinterpret_cast<v4i*>(la + sa[s]) = xa[s];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) *reinterpret_cast<v4i*>(lb + sb[s]) = rb[s];
+    for (int s = 0; s < 4; ++s) *reinterpret_cast<v4i*>(lb + sb[s]) = xb[s];
   };
-
   // Fragment reads: lane holds row (lane & 31) of a 32-row block and 16 bytes at
   // K offset 32*kk + 16*(lane >> 5); A and B use the same K map, so the product is
   // independent of how the instruction orders K internally.
   const int frow = lane & 31;
   const int fchunk = lane >> 5;
-
-  const int64_t nk = kp / BK;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int cur = (int)(kt & 1);
-    if (kt + 1 < nk) load_global((kt + 1) * BK);
-    const int8_t* la = lds + cur * (kLdsA + kLdsB);
+  auto read_frags = [&](v4i (&xa)[4], v4i (&xb)[4], int buf, int kk) {
+    const int8_t* la = lds + buf * (kLdsA + kLdsB);
     const int8_t* lb = la + kLdsA;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      v4i fa[4], fb[2];
+    for (int i = 0; i < 4; ++i)
+      xa[i] = *reinterpret_cast<const v4i*>(la + swz(wr * 128 + i * 32 + frow, kk * 2 + fchunk));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int r = wr * 128 + i * 32 + frow;
-        fa[i] = *reinterpret_cast<const v4i*>(la + swz(r, kk * 2 + fchunk));
-      }
+    for (int j = 0; j < 4; ++j)
+      xb[j] = *reinterpret_cast<const v4i*>(lb + swz(wc * 128 + j * 32 + frow, kk * 2 + fchunk));
+  };
+  auto mfma16 = [&](const v4i (&xa)[4], const v4i (&xb)[4]) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        int r = wc * 64 + j * 32 + frow;
-        fb[j] = *reinterpret_cast<const v4i*>(lb + swz(r, kk * 2 + fchunk));
-      }
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa[i], xb[j], acc[i][j], 0, 0, 0);
+  };
+
+  load_global(ra[0], rb[0], 0);
+  load_global(ra[1], rb[1], 1);
+  store_lds(0, ra[0], rb[0]);
+  __syncthreads();
+  read_frags(fa[0], fb[0], 0, 0);
+
+  auto tile_step = [&](auto parity, int64_t t) {
+    constexpr int p = decltype(parity)::value;
+    // sub-step 0
+    __builtin_amdgcn_sched_barrier(0);
+    load_global(ra[p], rb[p], t + 2);
+    store_lds(p ^ 1, ra[p ^ 1], rb[p ^ 1]);
+    read_frags(fa[1], fb[1], p, 1);
+    mfma16(fa[0], fb[0]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
     }
-    if (kt + 1 < nk) store_lds(cur ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // sub-step 1
     __syncthreads();
+    read_frags(fa[0], fb[0], p ^ 1, 0);
+    mfma16(fa[1], fb[1]);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int64_t t = 0;
+  for (; t + 2 <= nk; t += 2) {
+    tile_step(std::integral_constant<int, 0>(), t);
+    tile_step(std::integral_constant<int, 1>(), t + 1);
   }
+  if (t < nk) tile_step(std::integral_constant<int, 0>(), t);
 
   // Output layout of a 32x32 MFMA tile: lane -> column (lane & 31); register v ->
   // row 8*(v/4) + 4*(lane/32) + (v%4).
@@ -165,8 +216,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_i8_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = col0 + wc * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = col0 + wc * 128 + j * 32 + (lane & 31);
       if (col >= n) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {

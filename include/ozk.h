@@ -107,6 +107,13 @@ int ozk_modular_products(int64_t m, int64_t n, int64_t kp, int r, const int8_t* 
                          int64_t stride_a, const int8_t* pb, int64_t stride_b,
                          int32_t* products, int64_t ldp_out, int64_t stride_p, void* stream);
 
+/* Same products reduced to their symmetric residues modulo m_l, as int8 (what the
+ * reconstruction consumes; the kernel ozk_dgemm runs):
+ *     residues[l*stride_r + i*ldr + j] = smod(sum_h pa[..] * pb[..], m_l)          */
+int ozk_modular_residues(int64_t m, int64_t n, int64_t kp, int r, const int8_t* pa,
+                         int64_t stride_a, const int8_t* pb, int64_t stride_b,
+                         int8_t* residues, int64_t ldr, int64_t stride_r, void* stream);
+
 /* ---------------------------------------------------------------- reconstruction
  * [TME4] abstract, the per-output reconstruction term.  For each output, the r
  * int32 products are reduced modulo their moduli, lifted exactly by the Chinese

@@ -98,6 +98,20 @@ def test_modular_products_bit_exact(m, n, kp, r):
     assert want[0, 0, 0] == kp * 2**14
 
 
+@pytest.mark.parametrize("m,n,kp,r", [(300, 200, 256, 20), (1, 1, 64, 1), (257, 130, 128, 16)])
+def test_modular_residues_bit_exact(m, n, kp, r):
+    announce(f"modular_residues m={m} n={n} kp={kp} r={r}")
+    rng = np.random.default_rng(m * n + kp)
+    pa = rng.integers(-128, 128, size=(r, m, kp), dtype=np.int8)
+    pb = rng.integers(-128, 128, size=(r, n, kp), dtype=np.int8)
+    got = ozk.ozk_modular_residues(to_dev(pa), to_dev(pb))
+    torch.cuda.synchronize()
+    prods = ozaki2.modular_products(pa, pb)
+    want = np.stack([(prods[l] + m_l // 2) % m_l - m_l // 2
+                     for l, m_l in enumerate(rns.moduli(r))])
+    np.testing.assert_array_equal(got.cpu().numpy().astype(np.int64), want)
+
+
 @pytest.mark.parametrize("m,n,k,r,dist", [(40, 33, 100, 14, "uniform"), (64, 70, 300, 20, "phi"),
                                           (17, 5, 9, 8, "phi")])
 def test_reconstruct_bit_exact(m, n, k, r, dist):
