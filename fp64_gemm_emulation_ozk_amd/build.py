@@ -39,8 +39,7 @@ def _hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     cmd = [_hipcc(), *COMMON_FLAGS]
-    if src.endswith(".hip"):
-        cmd += DEVICE_FLAGS
+    cmd += DEVICE_FLAGS
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:

@@ -212,15 +212,96 @@ int ozk_dgemm(int64_t m, int64_t n, int64_t k, const double* A, int64_t lda, con
   return launch_crt(m, n, r, residues, 0, n, m * n, exps_a, exps_b, C, ldc, s);
 }
 
-// GEMV and FP4-limb entry points: kernels not yet in this build.
-int ozk_dgemv_workspace_size(int64_t, int64_t, int64_t, int, int, size_t*) {
-  return OZK_EUNSUPPORTED;
+}  // extern "C"
+
+// ---------------------------------------------------------------- emulated DGEMV
+namespace {
+
+struct GemvLayout {
+  int64_t kp;
+  size_t x_planes, x_exps, x_max, res, a_exps, a_max;
+  size_t total() const {
+    return align256(x_planes) + align256(x_exps) + align256(x_max) + align256(res) +
+           align256(a_exps) + align256(a_max);
+  }
+};
+
+GemvLayout gemv_layout(int64_t m, int64_t k, int64_t nrhs, int r, int mode) {
+  GemvLayout L;
+  L.kp = round_up(k, kPlaneK);
+  L.x_planes = (size_t)r * nrhs * L.kp;
+  L.x_exps = (size_t)nrhs * 4;
+  L.x_max = (size_t)nrhs * 8;
+  L.res = (size_t)r * m * nrhs;
+  L.a_exps = mode == 0 ? (size_t)m * 4 : 0;
+  L.a_max = mode == 0 ? (size_t)m * 8 : 0;
+  return L;
 }
-int ozk_dgemv(int64_t, int64_t, int64_t, const double*, int64_t, const int8_t*, int64_t, int64_t,
-              const int32_t*, const double*, int64_t, double*, int64_t, int, int, void*, size_t,
-              void*) {
-  return OZK_EUNSUPPORTED;
+
+}  // namespace
+
+extern "C" {
+
+int ozk_dgemv_workspace_size(int64_t m, int64_t k, int64_t nrhs, int r, int mode,
+                             size_t* bytes) {
+  if (!bytes || m < 0 || k < 1 || nrhs < 1 || nrhs > 32 || check_r(r) != OZK_OK) return OZK_EINVAL;
+  if (mode != 0 && mode != 1) return OZK_EINVAL;
+  if (k > OZK_MAX_K) return OZK_ERANGE;
+  *bytes = gemv_layout(m, k, nrhs, r, mode).total();
+  return OZK_OK;
 }
+
+int ozk_dgemv(int64_t m, int64_t k, int64_t nrhs, const double* A, int64_t lda,
+              const int8_t* A_planes, int64_t ldp, int64_t plane_stride, const int32_t* A_exps,
+              const double* X, int64_t ldx, double* Y, int64_t ldy, int r, int mode,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  if (check_r(r) != OZK_OK || (mode != 0 && mode != 1)) return OZK_EINVAL;
+  if (m < 0 || k < 1 || nrhs < 1 || nrhs > 32) return OZK_EINVAL;
+  if (k > OZK_MAX_K) return OZK_ERANGE;
+  if (ldx < nrhs || ldy < nrhs) return OZK_EINVAL;
+  int pa = 0, pb = 0;
+  int st = scaling_bits(r, k, &pa, &pb);
+  if (st != OZK_OK) return st;
+  const GemvLayout L = gemv_layout(m, k, nrhs, r, mode);
+  if (mode == 0) {
+    if (lda < k) return OZK_EINVAL;
+  } else {
+    if (ldp < L.kp || ldp % kPlaneK != 0 || plane_stride < m * ldp || plane_stride % 16 != 0)
+      return OZK_EINVAL;
+  }
+  if (m == 0) return OZK_OK;
+  if (!X || !Y) return OZK_EINVAL;
+  if (mode == 0 && !A) return OZK_EINVAL;
+  if (mode == 1 && (!A_planes || !A_exps || !aligned(A_planes, 16))) return OZK_EINVAL;
+  if (!workspace || workspace_bytes < L.total()) return OZK_EWORKSPACE;
+  if (!aligned(workspace, 256)) return OZK_EINVAL;
+  Carver cv(workspace);
+  int8_t* x_planes = static_cast<int8_t*>(cv.take(L.x_planes));
+  int32_t* x_exps = static_cast<int32_t*>(cv.take(L.x_exps));
+  uint64_t* x_max = static_cast<uint64_t*>(cv.take(L.x_max));
+  int8_t* res = static_cast<int8_t*>(cv.take(L.res));
+  int32_t* a_exps = static_cast<int32_t*>(cv.take(L.a_exps));
+  uint64_t* a_max = static_cast<uint64_t*>(cv.take(L.a_max));
+  hipStream_t s = as_stream(stream);
+  const int64_t kp = L.kp;
+  if ((st = deconstruct_impl(X, k, nrhs, ldx, 1, r, pb, x_planes, kp, nrhs * kp, x_exps, x_max,
+                             s)))
+    return st;
+  const int32_t* ea = A_exps;
+  if (mode == 0) {
+    if (!ea) {
+      if ((st = launch_line_exps(A, m, k, lda, 0, pa, a_max, a_exps, s))) return st;
+      ea = a_exps;
+    }
+    st = launch_gemv_fly(A, m, k, lda, ea, r, pa, x_planes, kp, nrhs * kp, (int)nrhs, res, s);
+  } else {
+    st = launch_gemv_stored(m, kp, r, A_planes, ldp, plane_stride, x_planes, nrhs * kp,
+                            (int)nrhs, res, s);
+  }
+  if (st) return st;
+  return launch_crt(m, nrhs, r, res, 0, nrhs, m * nrhs, ea, x_exps, Y, ldy, s);
+}
+
 int ozk_fp4limb_pack(const int8_t*, int64_t, int64_t, int64_t, int, uint8_t*, int64_t, int64_t,
                      void*) {
   return OZK_EUNSUPPORTED;

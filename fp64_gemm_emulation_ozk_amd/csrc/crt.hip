@@ -174,14 +174,18 @@ __global__ __launch_bounds__(256) void crt_kernel(int64_t m, int64_t n, const T*
     sc[t] = v;
   }
   __syncthreads();
-  const int64_t j0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (j0 >= n) return;
+  // Flat index over (row, quad of 4 columns).
+  const int64_t nq = (n + 3) / 4;
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= m * nq) return;
+  const int64_t i = g / nq;
+  const int64_t j0 = (g - i * nq) * 4;
   const int cnt = n - j0 >= 4 ? 4 : (int)(n - j0);
   int f[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) f[u] = u < cnt ? eb[j0 + u] : 0;
   const bool vec = cnt == 4 && sizeof(T) == 1 && ((ldr | stride_r | j0) & 3) == 0;
-  for (int64_t i = blockIdx.y; i < m; i += gridDim.y) {
+  {
     const int32_t e_i = ea[i];
     const T* src = res + i * ldr + j0;
     // Symmetric residues of the 4 outputs, one byte each, packed per modulus.
@@ -258,7 +262,9 @@ int launch_crt(int64_t m, int64_t n, int r, const void* res, int res_is_i32, int
                hipStream_t s) {
   if (m <= 0 || n <= 0) return OZK_OK;
   if (r < 1 || r > kMaxModuli) return OZK_EINVAL;
-  dim3 grid((unsigned)((n + 1023) / 1024), (unsigned)(m < 65535 ? m : 65535));
+  const int64_t blocks = (m * ((n + 3) / 4) + 255) / 256;
+  if (blocks > 0x7fffffff) return OZK_EUNSUPPORTED;
+  dim3 grid((unsigned)blocks);
   Dispatch<1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20>::go(
       r, grid, s, m, n, res, res_is_i32, ldr, stride_r, ea, eb, c, ldc);
   return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;

@@ -220,6 +220,12 @@ __global__ __launch_bounds__(kNT) void residues_rows_fused_kernel(
   }
 }
 
+__global__ void exps_from_maxbits_kernel(const uint64_t* __restrict__ maxbits, int64_t n,
+                                         int p_bits, int32_t* __restrict__ exps) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) exps[i] = line_exponent(maxbits[i], p_bits);
+}
+
 template <bool kWide, int kNT, int kG>
 int launch_fused(const double* x, int64_t rows, int64_t cols, int64_t ldx,
                  const ResidueConsts& K, int p_bits, int8_t* planes, int64_t ldp,
@@ -290,6 +296,18 @@ int launch_residues(const double* x, int64_t rows, int64_t cols, int64_t ldx, in
 }
 
 bool rows_fused_supported(int64_t cols) { return cols <= 32768; }
+
+int launch_line_exps(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                     int p_bits, uint64_t* maxbits, int32_t* exps, hipStream_t s) {
+  const int64_t lines = axis == 0 ? rows : cols;
+  if (lines <= 0) return OZK_OK;
+  int st;
+  if ((st = launch_fill_u64(maxbits, lines, 0, s)) != OZK_OK) return st;
+  if ((st = launch_absmax(x, rows, cols, ldx, axis, maxbits, s)) != OZK_OK) return st;
+  hipLaunchKernelGGL(exps_from_maxbits_kernel, dim3((unsigned)((lines + 255) / 256)), dim3(256), 0,
+                     s, maxbits, lines, p_bits, exps);
+  return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
+}
 
 int launch_residues_rows_fused(const double* x, int64_t rows, int64_t cols, int64_t ldx, int r,
                                int p_bits, int8_t* planes, int64_t ldp, int64_t plane_stride,

@@ -1,0 +1,264 @@
+// Emulated fp64 GEMV and low-batch GEMV (Y = A X, X with 1..32 columns): the memory-bound
+// case of [TME4] abstract, in its two forms:
+//   stored      A arrives as precomputed int8 residue planes (r bytes per element): the
+//               deconstruction cost has moved into HBM traffic.
+//   on the fly  A arrives as fp64 (8 bytes per element) and every element is scaled,
+//               rounded and reduced modulo each modulus in registers before the products:
+//               the per-input deconstruction term sits on the VALU.
+// Both feed v_mfma_i32_32x32x32_i8 with the 1..32 right-hand sides padded to 32 columns
+// (the MFMA time stays far below the HBM time) and write the symmetric residues of the
+// exact int32 products; the CRT kernel then reconstructs Y.
+//
+// MFMA operand layout used here: for K chunk k0 of 32, lane (row or column = lane & 31,
+// half = lane >> 5) supplies the 16 bytes at K = k0 + 16*half .. +15, identically for A
+// (rows) and X (columns), so the K order inside the instruction does not matter.
+#include "ozk_internal.h"
+#include "residue_math.h"
+
+namespace ozk {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+struct GemvModuli {
+  int32_t mod[kMaxModuli];
+  double inv[kMaxModuli];
+};
+
+__device__ __forceinline__ int sym_residue32(int v, int m, double inv) {
+  if (m == 256) return (int)(int8_t)(v & 0xff);
+  constexpr double kMagicD = 6755399441055744.0;
+  const double d = (double)v;
+  const double q = __builtin_fma(d, inv, kMagicD) - kMagicD;
+  return (int)__builtin_fma(-q, (double)m, d);
+}
+
+// Residues of one 32 x 32 accumulator tile (rows row0.., columns 0..31) to res.
+__device__ __forceinline__ void store_tile(const v16i& acc, int lane, int64_t row0, int64_t m,
+                                           int nrhs, int mod, double inv, int8_t* res) {
+  const int col = lane & 31;
+  if (col >= nrhs) return;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int64_t row = row0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    if (row < m) res[row * nrhs + col] = (int8_t)sym_residue32(acc[v], mod, inv);
+  }
+}
+
+// ------------------------------------------------------------------ stored planes
+// grid (ceil(m / 128), r); 4 waves, each 32 rows of one modulus over all of K.
+__global__ __launch_bounds__(256) void gemv_stored_kernel(
+    const int8_t* __restrict__ ap, int64_t lda_p, int64_t a_stride, int64_t m,
+    const int8_t* __restrict__ xp, int64_t kp, int64_t x_stride, int nrhs,
+    int8_t* __restrict__ res, int64_t res_stride, GemvModuli E) {
+  const int l = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 32;
+  if (row0 >= m) return;
+  int64_t row = row0 + (lane & 31);
+  row = row < m ? row : m - 1;
+  int col = lane & 31;
+  col = col < nrhs ? col : nrhs - 1;
+  const int half = lane >> 5;
+  const int8_t* pa = ap + l * a_stride + row * lda_p + 16 * half;
+  const int8_t* px = xp + l * x_stride + col * kp + 16 * half;
+  v16i acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0;
+  const int64_t nc = kp / 32;
+  int64_t c = 0;
+  for (; c + 4 <= nc; c += 4) {
+    v4i a[4], x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a[u] = *reinterpret_cast<const v4i*>(pa + (c + u) * 32);
+      x[u] = *reinterpret_cast<const v4i*>(px + (c + u) * 32);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[u], x[u], acc, 0, 0, 0);
+  }
+  for (; c < nc; ++c) {
+    const v4i a = *reinterpret_cast<const v4i*>(pa + c * 32);
+    const v4i x = *reinterpret_cast<const v4i*>(px + c * 32);
+    acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, x, acc, 0, 0, 0);
+  }
+  store_tile(acc, lane, row0, m, nrhs, E.mod[l], E.inv[l], res + l * res_stride);
+}
+
+// ------------------------------------------------------------------ on the fly
+// grid ceil(m / 128); 4 waves, each 32 rows and the moduli l0 .. l0+NR-1 (NR accumulator
+// tiles in AGPRs).  Per K chunk of 32: each lane loads its row's 16 fp64 values, scales
+// and rounds them (row exponent from exps), turns them into 16 residue bytes per modulus
+// and issues one MFMA per modulus against the X residues staged in LDS.
+template <bool kWide, int NR>
+__global__ __launch_bounds__(256, 1) void gemv_fly_kernel(
+    const double* __restrict__ a, int64_t m, int64_t k, int64_t lda,
+    const int32_t* __restrict__ exps, ResidueConsts K, int l0, const int8_t* __restrict__ xp,
+    int64_t ldp, int64_t x_stride, int nrhs, int8_t* __restrict__ res, int64_t res_stride,
+    GemvModuli E, int vec) {
+  __shared__ __attribute__((aligned(16))) int8_t xs[2][NR][32][32];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (tid >> 6)) * 32;
+  int64_t row = row0 + (lane & 31);
+  row = row < m ? row : m - 1;
+  const int half = lane >> 5;
+  int e = exps[row];
+  const bool bad = e == INT32_MIN;
+  if (bad) e = 0;
+  const int64_t klim = bad ? 0 : k;  // a row with Inf/NaN contributes residues 0
+  const double* pa = a + row * lda;
+
+  v16i acc[NR];
+#pragma unroll
+  for (int q = 0; q < NR; ++q)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[q][v] = 0;
+
+  const int64_t nc = ldp / 32;
+  // X staging: NR moduli x 32 columns x 32 bytes = NR * 64 chunks of 16 bytes.
+  auto stage_x = [&](int buf, int64_t c) {
+    for (int idx = tid; idx < NR * 64; idx += 256) {
+      const int q = idx >> 6;
+      int col = (idx >> 1) & 31;
+      const int hh = idx & 1;
+      col = col < nrhs ? col : nrhs - 1;
+      const v4i v = *reinterpret_cast<const v4i*>(xp + (int64_t)(l0 + q) * x_stride + col * ldp +
+                                                  c * 32 + 16 * hh);
+      *reinterpret_cast<v4i*>(&xs[buf][q][(idx >> 1) & 31][16 * hh]) = v;
+    }
+  };
+  auto load_a = [&](double (&v)[16], int64_t c) {
+    const int64_t h0 = c * 32 + 16 * half;
+    if (vec && h0 + 16 <= klim) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const double2 d = *reinterpret_cast<const double2*>(pa + h0 + 2 * u);
+        v[2 * u] = d.x;
+        v[2 * u + 1] = d.y;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = h0 + u < klim ? pa[h0 + u] : 0.0;
+    }
+  };
+
+  double cur[16], nxt[16];
+  load_a(cur, 0);
+  stage_x(0, 0);
+  __syncthreads();
+  for (int64_t c = 0; c < nc; ++c) {
+    const int buf = (int)(c & 1);
+    if (c + 1 < nc) {
+      load_a(nxt, c + 1);
+      stage_x(buf ^ 1, c + 1);
+    }
+    Prepared p[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) p[u] = prepare_element<kWide>(cur[u], e);
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      const int l = l0 + q;
+      v4i frag;
+      if (l == 0) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          frag[w] = (int)pack4(residue_byte_256(p[4 * w]), residue_byte_256(p[4 * w + 1]),
+                               residue_byte_256(p[4 * w + 2]), residue_byte_256(p[4 * w + 3]));
+      } else {
+        const double md = K.m[l], inv = K.inv[l], c32 = K.c32[l];
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          frag[w] = (int)pack4(residue_byte<kWide>(p[4 * w], md, inv, c32),
+                               residue_byte<kWide>(p[4 * w + 1], md, inv, c32),
+                               residue_byte<kWide>(p[4 * w + 2], md, inv, c32),
+                               residue_byte<kWide>(p[4 * w + 3], md, inv, c32));
+      }
+      const v4i xf = *reinterpret_cast<const v4i*>(&xs[buf][q][lane & 31][16 * half]);
+      acc[q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(frag, xf, acc[q], 0, 0, 0);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 16; ++u) cur[u] = nxt[u];
+  }
+  if (row0 >= m) return;
+#pragma unroll
+  for (int q = 0; q < NR; ++q)
+    store_tile(acc[q], lane, row0, m, nrhs, E.mod[l0 + q], E.inv[l0 + q],
+               res + (int64_t)(l0 + q) * res_stride);
+}
+
+GemvModuli gemv_moduli(int r) {
+  GemvModuli E;
+  const CrtConsts* C = crt_consts(r);
+  for (int i = 0; i < kMaxModuli; ++i) {
+    E.mod[i] = i < r ? C->mod[i] : 1;
+    E.inv[i] = i < r ? C->inv[i] : 1.0;
+  }
+  return E;
+}
+
+template <bool kWide, int NR>
+void launch_fly(dim3 grid, hipStream_t s, const double* a, int64_t m, int64_t k, int64_t lda,
+                const int32_t* exps, const ResidueConsts& K, int l0, const int8_t* xp,
+                int64_t ldp, int64_t x_stride, int nrhs, int8_t* res, int64_t res_stride,
+                const GemvModuli& E) {
+  const int vec = (reinterpret_cast<uintptr_t>(a) & 15) == 0 && (lda & 1) == 0;
+  hipLaunchKernelGGL((gemv_fly_kernel<kWide, NR>), grid, dim3(256), 0, s, a, m, k, lda, exps, K,
+                     l0, xp, ldp, x_stride, nrhs, res, res_stride, E, vec);
+}
+
+template <bool kWide>
+void dispatch_fly(int nr, dim3 grid, hipStream_t s, const double* a, int64_t m, int64_t k,
+                  int64_t lda, const int32_t* exps, const ResidueConsts& K, int l0,
+                  const int8_t* xp, int64_t ldp, int64_t x_stride, int nrhs, int8_t* res,
+                  int64_t res_stride, const GemvModuli& E) {
+#define OZK_FLY(N)                                                                            \
+  case N:                                                                                     \
+    launch_fly<kWide, N>(grid, s, a, m, k, lda, exps, K, l0, xp, ldp, x_stride, nrhs, res,    \
+                         res_stride, E);                                                      \
+    break
+  switch (nr) {
+    OZK_FLY(1); OZK_FLY(2); OZK_FLY(3); OZK_FLY(4); OZK_FLY(5); OZK_FLY(6); OZK_FLY(7);
+    OZK_FLY(8); OZK_FLY(9); OZK_FLY(10); OZK_FLY(11); OZK_FLY(12); OZK_FLY(13); OZK_FLY(14);
+    OZK_FLY(15); OZK_FLY(16);
+    default: break;
+  }
+#undef OZK_FLY
+}
+
+}  // namespace
+
+int launch_gemv_stored(int64_t m, int64_t kp, int r, const int8_t* ap, int64_t lda_p,
+                       int64_t a_stride, const int8_t* xp, int64_t x_stride, int nrhs,
+                       int8_t* res, hipStream_t s) {
+  if (m <= 0) return OZK_OK;
+  dim3 grid((unsigned)((m + 127) / 128), (unsigned)r);
+  hipLaunchKernelGGL(gemv_stored_kernel, grid, dim3(256), 0, s, ap, lda_p, a_stride, m, xp, kp,
+                     x_stride, nrhs, res, m * nrhs, gemv_moduli(r));
+  return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
+}
+
+int launch_gemv_fly(const double* a, int64_t m, int64_t k, int64_t lda, const int32_t* exps,
+                    int r, int p_bits, const int8_t* xp, int64_t ldp, int64_t x_stride, int nrhs,
+                    int8_t* res, hipStream_t s) {
+  if (m <= 0) return OZK_OK;
+  const ResidueConsts& K = *residue_consts(r, p_bits);
+  const GemvModuli E = gemv_moduli(r);
+  dim3 grid((unsigned)((m + 127) / 128));
+  // At most 16 moduli per pass (16 accumulator tiles = 256 AGPRs); r > 16 takes two.
+  for (int l0 = 0; l0 < r; l0 += 16) {
+    const int nr = r - l0 < 16 ? r - l0 : 16;
+    if (K.wide)
+      dispatch_fly<true>(nr, grid, s, a, m, k, lda, exps, K, l0, xp, ldp, x_stride, nrhs, res,
+                         m * nrhs, E);
+    else
+      dispatch_fly<false>(nr, grid, s, a, m, k, lda, exps, K, l0, xp, ldp, x_stride, nrhs, res,
+                          m * nrhs, E);
+    if (hipGetLastError() != hipSuccess) return OZK_EHIP;
+  }
+  return OZK_OK;
+}
+
+}  // namespace ozk

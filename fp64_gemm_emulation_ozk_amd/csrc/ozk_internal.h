@@ -62,6 +62,16 @@ int launch_residues_rows_fused(const double* x, int64_t rows, int64_t cols, int6
                                int r, int p_bits, int8_t* planes, int64_t ldp,
                                int64_t plane_stride, int32_t* exps, hipStream_t s);
 bool rows_fused_supported(int64_t cols);
+// Row (axis 0) or column (axis 1) exponents only, through maxbits scratch.
+int launch_line_exps(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                     int p_bits, uint64_t* maxbits, int32_t* exps, hipStream_t s);
+
+int launch_gemv_stored(int64_t m, int64_t kp, int r, const int8_t* ap, int64_t lda_p,
+                       int64_t a_stride, const int8_t* xp, int64_t x_stride, int nrhs,
+                       int8_t* res, hipStream_t s);
+int launch_gemv_fly(const double* a, int64_t m, int64_t k, int64_t lda, const int32_t* exps,
+                    int r, int p_bits, const int8_t* xp, int64_t ldp, int64_t x_stride, int nrhs,
+                    int8_t* res, hipStream_t s);
 
 enum GemmEpilogue { kEpiProducts = 0, kEpiResidues = 1 };
 int launch_gemm_i8(int64_t m, int64_t n, int64_t kp, int r, const int8_t* pa, int64_t stride_a,

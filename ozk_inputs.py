@@ -78,3 +78,13 @@ def int8_operands(m: int, n: int, k: int, seed: int):
     a = int8_matrix(rng, (m, k))
     b = int8_matrix(rng, (k, n))
     return a, b
+
+
+def uniform_matrix_device(shape, seed: int, device):
+    """Entries U(-1, 1) as float64 drawn on a GPU by torch's seeded generator (for
+    operands too large to draw on the host); the same seed gives the same matrix."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return torch.rand(shape, generator=gen, dtype=torch.float64, device=device) * 2.0 - 1.0

@@ -1,0 +1,138 @@
+"""GPU parity of the emulated GEMV / low-batch GEMV (both modes) against the CPU oracle.
+
+On the fly (A streamed as fp64, residues formed in registers) and stored (A's residue
+planes from ozk_deconstruct) must both equal the oracle's emulated product element by
+element (<= 2 ulp, expected bit-exact), for 1..32 right-hand sides, ragged sizes, r up to
+20 (more than 16 moduli takes two on-the-fly passes), special rows, and the full
+32768 x 32768 configuration on sampled rows."""
+import numpy as np
+import pytest
+import torch
+
+import fp64_gemm_emulation_ozk_amd as ozk
+import ozk_inputs
+from oracle import ozaki2, reference
+
+from gpu_common import announce, assert_within_ulps, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(a, x, r, mode, cached_exps=False):
+    da, dx = to_dev(a), to_dev(x)
+    if mode == 1:
+        planes, exps = ozk.ozk_deconstruct(da, 0, r, k_budget=a.shape[1])
+        return ozk.ozk_dgemv(None, dx, r, mode=1, a_planes=planes, a_exps=exps)
+    exps = None
+    if cached_exps:
+        _, exps = ozk.ozk_deconstruct(da, 0, r, k_budget=a.shape[1])
+    return ozk.ozk_dgemv(da, dx, r, mode=0, a_exps=exps)
+
+
+CASES = [
+    # m, k, nrhs, r
+    (300, 257, 1, 14),
+    (300, 257, 8, 16),
+    (129, 1000, 32, 14),
+    (65, 64, 3, 8),
+    (1, 1, 1, 5),
+    (200, 300, 5, 20),
+    (257, 4100, 32, 18),
+]
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("m,k,nrhs,r", CASES)
+def test_dgemv_matches_oracle(m, k, nrhs, r, mode):
+    announce(f"dgemv m={m} k={k} nrhs={nrhs} r={r} mode={mode}")
+    a, x = ozk_inputs.gemv_operands(m, k, nrhs, seed=m + k + nrhs)
+    got = _run(a, x, r, mode)
+    torch.cuda.synchronize()
+    want = ozaki2.dgemv(a, x, r)
+    assert assert_within_ulps(got.cpu().numpy(), want, 2) == 0
+
+
+def test_dgemv_cached_exponents_equal_computed():
+    announce("dgemv cached exps")
+    a, x = ozk_inputs.gemv_operands(190, 513, 4, seed=3)
+    g1 = _run(a, x, 14, 0, cached_exps=True)
+    g2 = _run(a, x, 14, 0, cached_exps=False)
+    torch.cuda.synchronize()
+    assert torch.equal(g1.view(torch.int64), g2.view(torch.int64))
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_dgemv_special_rows(mode):
+    announce(f"dgemv special rows mode={mode}")
+    a, x = ozk_inputs.gemv_operands(100, 300, 4, seed=8)
+    a = ozk_inputs.phi_matrix(np.random.default_rng(8), (100, 300), 4.0)
+    a[3] = 0.0
+    a[7, 11] = np.nan
+    a[9] *= 1e-305
+    x[5, 2] = np.inf
+    got = _run(a, x, 16, mode)
+    torch.cuda.synchronize()
+    want = ozaki2.dgemv(a, x, 16)
+    assert assert_within_ulps(got.cpu().numpy(), want, 2) == 0
+
+
+def test_dgemv_strided():
+    announce("dgemv strided")
+    a, x = ozk_inputs.gemv_operands(70, 90, 3, seed=2)
+    abig = np.zeros((70, 96))
+    abig[:, :90] = a
+    xbig = np.zeros((90, 5))
+    xbig[:, :3] = x
+    da, dx = to_dev(abig)[:, :90], to_dev(xbig)[:, :3]
+    out = torch.full((70, 4), 5.0, dtype=torch.float64, device=da.device)
+    ozk.ozk_dgemv(da, dx, 14, mode=0, out=out[:, :3])
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(got[:, 3] == 5.0)
+    assert assert_within_ulps(got[:, :3], ozaki2.dgemv(a, x, 14), 2) == 0
+
+
+@pytest.fixture(scope="module")
+def big_gemv():
+    """A 32768 x 32768, U(-1,1) (seed 4, drawn on the GPU) and X 32768 x 32 (seed 4,
+    host); the 1- and 8-column cases use X's leading columns."""
+    dev = torch.device("cuda:0")
+    da = ozk_inputs.uniform_matrix_device((32768, 32768), 4, dev)
+    x = ozk_inputs.uniform_matrix(np.random.default_rng(4), (32768, 32))
+    return da, x
+
+
+@pytest.mark.parametrize("nrhs", [1, 8, 32])
+def test_dgemv_32768_sampled(big_gemv, nrhs):
+    da, x = big_gemv
+    r = 14
+    announce(f"dgemv 32768^2 nrhs={nrhs} r={r} both modes, sampled rows")
+    xs = np.ascontiguousarray(x[:, :nrhs])
+    dx = to_dev(xs)
+    y_fly = ozk.ozk_dgemv(da, dx, r, mode=0)
+    planes, exps = ozk.ozk_deconstruct(da, 0, r, k_budget=32768)
+    y_st = ozk.ozk_dgemv(None, dx, r, mode=1, a_planes=planes, a_exps=exps)
+    torch.cuda.synchronize()
+    del planes
+    assert torch.equal(y_fly.view(torch.int64), y_st.view(torch.int64))
+    rows = np.array([0, 1, 12345, 20000, 32767])
+    a_rows = da[torch.as_tensor(rows, device=da.device)].cpu().numpy()
+    want = ozaki2.dgemv(a_rows, xs, r)
+    assert assert_within_ulps(y_fly.cpu().numpy()[rows], want, 2) == 0
+
+
+def test_dgemv_32768_accuracy_r14_r16(big_gemv):
+    """Normwise error against Dot2 on sampled rows: r = 14 is the configured size;
+    r = 16 is the accuracy run (1e-15 needs 16 moduli at k = 32768 under the max rule)."""
+    da, x = big_gemv
+    rows = np.array([5, 777, 31000])
+    a_rows = da[torch.as_tensor(rows, device=da.device)].cpu().numpy()
+    xs = np.ascontiguousarray(x[:, :1])
+    dd = reference.dot2_matmul(a_rows, xs)
+    errs = {}
+    for r in (14, 16):
+        announce(f"dgemv 32768 accuracy r={r}")
+        y = ozk.ozk_dgemv(da, to_dev(xs), r, mode=0).cpu().numpy()[rows]
+        errs[r] = np.linalg.norm(y - dd) / np.linalg.norm(dd)
+    assert errs[16] <= 1e-15
+    assert errs[14] <= 1e-13
