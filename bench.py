@@ -75,6 +75,63 @@ def _traffic(kernel: str, digest: str):
     return ent.get("hbm_bytes_per_launch")
 
 
+def measure_gemv(reps: int, stream) -> dict:
+    """The 32768 x 32768 GEMV / low-batch GEMV workload at r = 14: A U(-1,1) (seed 4, drawn
+    on the GPU), X U(-1,1) with 1, 8 and 32 columns.  GB/s counts the algorithmic bytes of
+    A streamed per call (8 per element on the fly, r per element from stored planes)."""
+    import numpy as np
+    import torch
+
+    import fp64_gemm_emulation_ozk_amd as ozk
+    import ozk_inputs
+
+    mg, kg, r = 32768, 32768, 14
+    dev = torch.device("cuda:0")
+    da = ozk_inputs.uniform_matrix_device((mg, kg), 4, dev)
+    x_all = torch.from_numpy(ozk_inputs.uniform_matrix(np.random.default_rng(4), (kg, 32))).to(dev)
+    elems = float(mg) * kg
+    out = {"workload": f"A {mg}x{kg} U(-1,1), X {kg}x{{1,8,32}} U(-1,1), r={r}"}
+    planes, exps = ozk.ozk_deconstruct(da, 0, r, k_budget=kg)
+    dec = lambda: ozk.ozk_deconstruct(da, 0, r, k_budget=kg, planes=planes, exps=exps)
+    dec()
+    ms = _time_events(dec, reps, stream)
+    out["deconstruct_A"] = {"ms": round(ms, 4), "gbs": round((8 + r) * elems / ms / 1e6, 1),
+                            "bytes_per_elem": 8 + r}
+    rows = []
+    for nrhs in (1, 8, 32):
+        dx = x_all[:, :nrhs].contiguous()
+        y = torch.empty((mg, nrhs), dtype=torch.float64, device=dev)
+        res = {"nrhs": nrhs}
+        nat = lambda: torch.matmul(da, dx, out=y)
+        nat()
+        t = _time_events(nat, reps, stream)
+        res["native_fp64"] = {"ms": round(t, 4), "gbs": round(8 * elems / t / 1e6, 1)}
+        ws0 = torch.empty(ozk.ozk_dgemv_workspace_size(mg, kg, nrhs, r, 0), dtype=torch.uint8,
+                          device=dev)
+        fly = lambda: ozk.ozk_dgemv(da, dx, r, mode=0, a_exps=exps, out=y, workspace=ws0)
+        fly()
+        t = _time_events(fly, reps, stream)
+        res["on_the_fly_cached_exps"] = {"ms": round(t, 4), "gbs": round(8 * elems / t / 1e6, 1),
+                                         "frac_hbm": round(8 * elems / t / 1e6 / PEAK_HBM_GBS, 4)}
+        fly2 = lambda: ozk.ozk_dgemv(da, dx, r, mode=0, out=y, workspace=ws0)
+        fly2()
+        t = _time_events(fly2, reps, stream)
+        res["on_the_fly_with_exps_pass"] = {"ms": round(t, 4)}
+        ws1 = torch.empty(ozk.ozk_dgemv_workspace_size(mg, kg, nrhs, r, 1), dtype=torch.uint8,
+                          device=dev)
+        st = lambda: ozk.ozk_dgemv(None, dx, r, mode=1, a_planes=planes, a_exps=exps, out=y,
+                                   workspace=ws1)
+        st()
+        t = _time_events(st, reps, stream)
+        res["stored_planes"] = {"ms": round(t, 4), "gbs": round(r * elems / t / 1e6, 1),
+                                "frac_hbm": round(r * elems / t / 1e6 / PEAK_HBM_GBS, 4)}
+        rows.append(res)
+    out["runs"] = rows
+    del da, planes
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(a, b, r: int) -> dict:
     import numpy as np
     from threadpoolctl import threadpool_limits
@@ -101,6 +158,7 @@ def main() -> int:
     ap.add_argument("--r", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-gemv", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the emulation "
@@ -198,6 +256,10 @@ def main() -> int:
             "ms": round(dec_ms, 4), "bytes": (8 + r) * M * K,
             "gbs": round((8 + r) * M * K / dec_ms / 1e6, 1),
             "frac_hbm": round((8 + r) * M * K / dec_ms / 1e6 / PEAK_HBM_GBS, 4)}
+        if not args.no_gemv:
+            del planes_a, planes_b, res, ws
+            torch.cuda.empty_cache()
+            extras["gemv_32768"] = measure_gemv(reps, stream)
 
     line = {
         "metric": METRIC,

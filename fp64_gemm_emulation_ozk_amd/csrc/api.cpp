@@ -302,20 +302,65 @@ int ozk_dgemv(int64_t m, int64_t k, int64_t nrhs, const double* A, int64_t lda,
   return launch_crt(m, nrhs, r, res, 0, nrhs, m * nrhs, ea, x_exps, Y, ldy, s);
 }
 
-int ozk_fp4limb_pack(const int8_t*, int64_t, int64_t, int64_t, int, uint8_t*, int64_t, int64_t,
-                     void*) {
-  return OZK_EUNSUPPORTED;
+// ---------------------------------------------------------------- FP4-limb INT8 GEMM
+int ozk_fp4limb_pack(const int8_t* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                     uint8_t* planes, int64_t ldp_bytes, int64_t plane_stride, void* stream) {
+  if (axis != 0 && axis != 1) return OZK_EINVAL;
+  if (rows < 0 || cols < 0 || ldx < (cols > 0 ? cols : 1)) return OZK_EINVAL;
+  const int64_t K = axis == 0 ? cols : rows;
+  const int64_t lines = axis == 0 ? rows : cols;
+  if (ldp_bytes <= 0 || ldp_bytes % 32 != 0 || 2 * ldp_bytes < K) return OZK_EINVAL;
+  if (plane_stride < lines * ldp_bytes || plane_stride % 16 != 0) return OZK_EINVAL;
+  if (lines == 0) return OZK_OK;
+  if (!planes || (K > 0 && !x) || !aligned(planes, 16)) return OZK_EINVAL;
+  return launch_fp4_pack(x, rows, cols, ldx, axis, planes, ldp_bytes, plane_stride,
+                         as_stream(stream));
 }
-int ozk_fp4limb_products(int64_t, int64_t, int64_t, const uint8_t*, int64_t, const uint8_t*,
-                         int64_t, int32_t*, int64_t, int64_t, void*) {
-  return OZK_EUNSUPPORTED;
+
+int ozk_fp4limb_products(int64_t m, int64_t n, int64_t ldp_bytes, const uint8_t* planes_a,
+                         int64_t stride_a, const uint8_t* planes_b, int64_t stride_b,
+                         int32_t* products, int64_t ldp_out, int64_t stride_p, void* stream) {
+  if (m < 0 || n < 0 || ldp_bytes <= 0 || ldp_bytes % 32 != 0) return OZK_EINVAL;
+  if (2 * ldp_bytes > round_up(OZK_MAX_K, kPlaneK)) return OZK_ERANGE;
+  if (stride_a < m * ldp_bytes || stride_b < n * ldp_bytes || stride_a % 16 || stride_b % 16)
+    return OZK_EINVAL;
+  if (ldp_out < (n > 0 ? n : 1) || stride_p < m * ldp_out) return OZK_EINVAL;
+  if (m == 0 || n == 0) return OZK_OK;
+  if (!planes_a || !planes_b || !products || !aligned(planes_a, 16) || !aligned(planes_b, 16))
+    return OZK_EINVAL;
+  return launch_fp4_products(m, n, ldp_bytes, planes_a, stride_a, planes_b, stride_b, products,
+                             ldp_out, stride_p, as_stream(stream));
 }
-int ozk_int8gemm_fp4limb_workspace_size(int64_t, int64_t, int64_t, size_t*) {
-  return OZK_EUNSUPPORTED;
+
+int ozk_int8gemm_fp4limb_workspace_size(int64_t m, int64_t n, int64_t k, size_t* bytes) {
+  if (!bytes || m < 0 || n < 0 || k < 1) return OZK_EINVAL;
+  if (k > OZK_MAX_K) return OZK_ERANGE;
+  const int64_t ldpb = round_up(k, kPlaneK) / 2;
+  *bytes = align256((size_t)3 * m * ldpb) + align256((size_t)3 * n * ldpb);
+  return OZK_OK;
 }
-int ozk_int8gemm_fp4limb(int64_t, int64_t, int64_t, const int8_t*, int64_t, const int8_t*,
-                         int64_t, int32_t*, int64_t, void*, size_t, void*) {
-  return OZK_EUNSUPPORTED;
+
+int ozk_int8gemm_fp4limb(int64_t m, int64_t n, int64_t k, const int8_t* A, int64_t lda,
+                         const int8_t* B, int64_t ldb, int32_t* C, int64_t ldc, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (m < 0 || n < 0 || k < 1) return OZK_EINVAL;
+  if (k > OZK_MAX_K) return OZK_ERANGE;
+  if (lda < k || ldb < (n > 0 ? n : 1) || ldc < (n > 0 ? n : 1)) return OZK_EINVAL;
+  if (m == 0 || n == 0) return OZK_OK;
+  if (!A || !B || !C) return OZK_EINVAL;
+  size_t need = 0;
+  ozk_int8gemm_fp4limb_workspace_size(m, n, k, &need);
+  if (!workspace || workspace_bytes < need) return OZK_EWORKSPACE;
+  if (!aligned(workspace, 256)) return OZK_EINVAL;
+  const int64_t ldpb = round_up(k, kPlaneK) / 2;
+  Carver cv(workspace);
+  uint8_t* pa = static_cast<uint8_t*>(cv.take((size_t)3 * m * ldpb));
+  uint8_t* pb = static_cast<uint8_t*>(cv.take((size_t)3 * n * ldpb));
+  hipStream_t s = as_stream(stream);
+  int st;
+  if ((st = launch_fp4_pack(A, m, k, lda, 0, pa, ldpb, m * ldpb, s))) return st;
+  if ((st = launch_fp4_pack(B, k, n, ldb, 1, pb, ldpb, n * ldpb, s))) return st;
+  return launch_fp4_gemm(m, n, ldpb, pa, m * ldpb, pb, n * ldpb, C, ldc, s);
 }
 
 }  // extern "C"

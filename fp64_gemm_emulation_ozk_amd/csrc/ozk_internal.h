@@ -73,6 +73,14 @@ int launch_gemv_fly(const double* a, int64_t m, int64_t k, int64_t lda, const in
                     int r, int p_bits, const int8_t* xp, int64_t ldp, int64_t x_stride, int nrhs,
                     int8_t* res, hipStream_t s);
 
+int launch_fp4_pack(const int8_t* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                    uint8_t* planes, int64_t ldpb, int64_t plane_stride, hipStream_t s);
+int launch_fp4_products(int64_t m, int64_t n, int64_t ldpb, const uint8_t* pa, int64_t stride_a,
+                        const uint8_t* pb, int64_t stride_b, int32_t* out, int64_t ldo,
+                        int64_t stride_o, hipStream_t s);
+int launch_fp4_gemm(int64_t m, int64_t n, int64_t ldpb, const uint8_t* pa, int64_t stride_a,
+                    const uint8_t* pb, int64_t stride_b, int32_t* c, int64_t ldc, hipStream_t s);
+
 enum GemmEpilogue { kEpiProducts = 0, kEpiResidues = 1 };
 int launch_gemm_i8(int64_t m, int64_t n, int64_t kp, int r, const int8_t* pa, int64_t stride_a,
                    const int8_t* pb, int64_t stride_b, void* out, int64_t ldo, int64_t stride_o,
