@@ -132,6 +132,50 @@ def measure_gemv(reps: int, stream) -> dict:
     return out
 
 
+def measure_fp4(reps: int, stream) -> dict:
+    """The exact INT8 x INT8 product of 8192^3 int8 operands (uniform in [-128, 127],
+    seed 5) through 9 FP4 GEMMs, against the 10.1 PFLOP/s dense FP4 MFMA peak."""
+    import numpy as np
+    import torch
+
+    import fp64_gemm_emulation_ozk_amd as ozk
+    import ozk_inputs
+
+    n = 8192
+    dev = torch.device("cuda:0")
+    a, b = ozk_inputs.int8_operands(n, n, n, seed=5)
+    ia, ib = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    c = torch.empty((n, n), dtype=torch.int32, device=dev)
+    ws = torch.empty(ozk.ozk_int8gemm_fp4limb_workspace_size(n, n, n), dtype=torch.uint8,
+                     device=dev)
+    f = lambda: ozk.ozk_int8gemm_fp4limb(ia, ib, out=c, workspace=ws)
+    f()
+    t = _time_events(f, reps, stream)
+    pa = ozk.ozk_fp4limb_pack(ia, 0)
+    pb = ozk.ozk_fp4limb_pack(ib, 1)
+    ldpb = pa.shape[-1]
+    pack = lambda: (ozk.ozk_fp4limb_pack(ia, 0, planes=pa), ozk.ozk_fp4limb_pack(ib, 1, planes=pb))
+    pack()
+    tp = _time_events(pack, reps, stream)
+    fp4_flops = 9 * 2.0 * n * n * (2 * ldpb)
+    out = {"workload": f"int8 {n}x{n}x{n} uniform [-128,127], seed 5",
+           "ms": round(t, 4), "pack_ms": round(tp, 4),
+           "fp4_tflops_incl_pack": round(fp4_flops / t / 1e9, 1),
+           "gemm_ms_excl_pack": round(t - tp, 4),
+           "fp4_tflops_gemm": round(fp4_flops / (t - tp) / 1e9, 1),
+           "frac_fp4_peak_gemm": round(fp4_flops / (t - tp) / 1e9 / PEAK_FP4_TFLOPS, 4),
+           "int8_equiv_tops": round(2.0 * n ** 3 / t / 1e9, 1)}
+    try:
+        torch._int_mm(ia, ib)
+        ti = _time_events(lambda: torch._int_mm(ia, ib), reps, stream)
+        out["vendor_int8_gemm"] = {"ms": round(ti, 4), "tops": round(2.0 * n ** 3 / ti / 1e9, 1)}
+    except RuntimeError as exc:
+        out["vendor_int8_gemm"] = {"error": str(exc)[:200]}
+    del ia, ib, c, ws, pa, pb
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(a, b, r: int) -> dict:
     import numpy as np
     from threadpoolctl import threadpool_limits
@@ -159,6 +203,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-gemv", action="store_true")
+    ap.add_argument("--no-fp4", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the emulation "
@@ -260,6 +305,8 @@ def main() -> int:
             del planes_a, planes_b, res, ws
             torch.cuda.empty_cache()
             extras["gemv_32768"] = measure_gemv(reps, stream)
+        if not args.no_fp4:
+            extras["fp4limb_int8gemm_8192"] = measure_fp4(reps, stream)
 
     line = {
         "metric": METRIC,
