@@ -7,10 +7,10 @@
 //      the < 2^-30 error of the fp64 sum, so q is exact.
 //   2. X = sum_l c_l E_l - q M, in 2^40 limbs held in fp64: every limb sum stays below
 //      2^53 (at most 20 * 2^47 + 2^51.4), so all fp64 operations are exact.
-//   3. Limbs are normalised to digits in [0, 2^40), the sign split off, the magnitude
-//      packed into three 64-bit words, and RN(|X| 2^-s) is formed by integer rounding
-//      (half to even) at the precision of the result's binade: 53 bits for a normal
-//      result, fewer for a subnormal one, so the output is rounded exactly once.
+//   3. Limbs are normalised to digits in [0, 2^40) and the sign split off; RN(|X| 2^-s)
+//      is formed with one fp64 rounding of the top digits plus an exact tie correction
+//      (round_digits), or, for a subnormal result, by integer rounding at the reduced
+//      precision, so the output is rounded exactly once.
 // The constants come from the compile-time table in __constant__ memory; each block
 // stages the r(L+1)+L values it needs in LDS (compile-time r), and every constant is
 // read once per 4 outputs, so none of them has to live in scalar registers.
@@ -72,6 +72,59 @@ __device__ __forceinline__ double round_scaled_words(uint64_t w0, uint64_t w1, u
   return __builtin_ldexp((double)mant, E >= -1022 ? E - 52 : -1074);
 }
 
+// RN(V * 2^-s) for V = sum_p d[p] 2^(40 p), digits d[p] integers in [0, 2^40).
+// Fast path, all in exact fp64 arithmetic: take the top nonzero digit H and the digits
+// below it so that S = H*2^40 + next (or (H*2^40 + next)*2^40 + next2 when H < 2^13) has
+// at least 54 bits; fma rounds S once (RNE), and its error err = S - RN(S) is exact.
+// Digits further down add a fraction 0 <= eps < 1 (in units of S); S is an integer and
+// every rounding midpoint at >= 54 bits is an integer, so eps can only matter when S sits
+// exactly on a midpoint below it (err = +ulp/2): then the true value lies above the
+// midpoint and RN rounds up.  Scaling by 2^(base - s) is exact for a normal result; a
+// subnormal (or zero) result takes the integer path below.
+template <int L>
+__device__ __forceinline__ double round_digits(const double (&d)[4], int s) {
+  double h, lo, lo2;
+  bool rest;  // any nonzero digit below lo2
+  int top;
+  if (L > 3 && d[3] != 0.0) {
+    top = 3; h = d[3]; lo = d[2]; lo2 = d[1]; rest = d[0] != 0.0;
+  } else if (d[2] != 0.0) {
+    top = 2; h = d[2]; lo = d[1]; lo2 = d[0]; rest = false;
+  } else if (d[1] != 0.0) {
+    top = 1; h = d[1]; lo = d[0]; lo2 = 0.0; rest = false;
+  } else {
+    top = 0; h = d[0]; lo = 0.0; lo2 = 0.0; rest = false;
+  }
+  if (h == 0.0) return 0.0;
+  double S, err;
+  bool below;  // nonzero digits below the ones folded into S
+  int base;
+  if (h >= 8192.0) {  // H has >= 14 bits: H*2^40 + lo has >= 54
+    S = __builtin_fma(h, 0x1p40, lo);
+    err = __builtin_fma(h, 0x1p40, -S) + lo;
+    below = lo2 != 0.0 || rest;
+    base = 40 * (top - 1);
+  } else {
+    const double t = __builtin_fma(h, 0x1p40, lo);  // < 2^53: exact
+    S = __builtin_fma(t, 0x1p40, lo2);
+    err = __builtin_fma(t, 0x1p40, -S) + lo2;
+    below = rest;
+    base = 40 * (top - 2);
+  }
+  const int e = __builtin_amdgcn_frexp_exp(S) - 1;  // ilogb(S)
+  const double half_ulp = __builtin_ldexp(1.0, e - 53);
+  if (below && err == half_ulp) S += 2.0 * half_ulp;
+  const int E = e + base - s;  // exponent of the result (before a possible carry)
+  if (E >= -1021) return __builtin_ldexp(S, base - s);
+  // Subnormal or underflowing result: exact integer rounding at the reduced precision.
+  const uint64_t d0 = u64_of(d[0]), d1 = u64_of(d[1]), d2 = u64_of(d[2]);
+  const uint64_t d3 = L > 3 ? u64_of(d[3]) : 0;
+  const uint64_t w0 = d0 | (d1 << 40);
+  const uint64_t w1 = (d1 >> 24) | (d2 << 16) | (d3 << 56);
+  const uint64_t w2 = d3 >> 8;
+  return round_scaled_words(w0, w1, w2, s);
+}
+
 // Exact integer X of 4 outputs from their residues and the RNS constants in LDS,
 // rounded to fp64 with the shift s[u].
 template <int R>
@@ -129,16 +182,8 @@ __device__ __forceinline__ void reconstruct4(const int32_t (&word)[R], const dou
         xu[p + 1] += carry;
       }
     }
-    const uint64_t d0 = u64_of(xu[0]), d1 = u64_of(xu[1]), d2 = u64_of(xu[2]);
-    const uint64_t d3 = L > 3 ? u64_of(xu[3]) : 0;
-    const uint64_t w0 = d0 | (d1 << 40);
-    const uint64_t w1 = (d1 >> 24) | (d2 << 16) | (d3 << 56);
-    const uint64_t w2 = d3 >> 8;
-    double o = 0.0;
-    if ((w0 | w1 | w2) != 0) {
-      o = round_scaled_words(w0, w1, w2, s[u]);
-      o = neg ? -o : o;
-    }
+    double o = round_digits<L>(x[u], s[u]);
+    o = neg ? -o : o;
     out[u] = nan[u] ? __builtin_nan("") : o;
   }
 }

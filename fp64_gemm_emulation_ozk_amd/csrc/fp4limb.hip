@@ -184,14 +184,16 @@ __global__ __launch_bounds__(64) void limb_products_kernel(
 // Workgroup tile 128 x 128, K step 64 (32 bytes per row per digit plane), 512 threads =
 // 8 waves in 2 x 4, each wave 64 x 32 = 2 MFMA blocks x 5 weight classes (160 AGPRs).
 // Digit planes of A and B go through registers into double-buffered LDS (2 x 24 KiB);
-// LDS rows are 32 bytes with the two 16-byte halves swapped on rows with bit 2 set.
+// LDS rows are 32 bytes with the two 16-byte halves swapped on rows with bit 3 set.
 constexpr int FBM = 128, FBN = 128, FROW = 32;  // bytes per row per plane per K step
 constexpr int kFThreads = 512;
 constexpr int kPlaneA = FBM * FROW, kPlaneB = FBN * FROW;
 constexpr int kStage = 3 * (kPlaneA + kPlaneB);  // 24 KiB
 
+// 16 lanes read rows r..r+15 at the same half; rows 8 apart share banks without the XOR
+// (gfx950 LDS: 64 four-byte banks, 16 lanes of 16 bytes per clock).
 __device__ __forceinline__ int fswz(int row, int half) {
-  return row * FROW + ((half ^ ((row >> 2) & 1)) << 4);
+  return row * FROW + ((half ^ ((row >> 3) & 1)) << 4);
 }
 
 __global__ __launch_bounds__(kFThreads, 1) void fp4_gemm_kernel(

@@ -8,16 +8,17 @@
 //
 // Tiling: workgroup tile 256 x 256 x 64, 256 threads = 4 waves, each wave a 128 x 128
 // block of 4 x 4 MFMA tiles of 32 x 32 (256 accumulator registers, held in AGPRs), so
-// every 16-byte LDS fragment read feeds two MFMAs.  Global tiles go through two sets of
-// registers into double-buffered LDS (64 KiB), with the MFMA, LDS and global-memory
-// instructions of each K sub-step interleaved explicitly (see the pipeline below); LDS rows are 64 bytes with the four 16-byte chunks
+// every 16-byte LDS fragment read feeds two MFMAs.  Global tiles are loaded straight into
+// a 4-stage LDS ring (128 KiB) by global_load_lds_dwordx4, three K tiles ahead, with one
+// barrier per K tile placed between the two MFMA sub-steps (see the pipeline below); LDS rows are 64 bytes with the four 16-byte chunks
 // XOR-swizzled by (row >> 1) & 3 so that the fragment reads of 8 consecutive rows hit 8
 // distinct bank groups.  Workgroups are mapped XCD by XCD (the hardware deals them out
 // round-robin over the 8 XCDs) onto contiguous runs of tiles, ordered in groups of 4
 // tile rows, so the tiles in flight on one XCD share A rows and B columns in its L2.
 //
 // Epilogues: the int32 products themselves, or their symmetric residues modulo m_l as
-// int8 (what the CRT reconstruction consumes: 1 byte instead of 4 per output).
+// int8 (what the CRT reconstruction consumes: 1 byte instead of 4 per output), staged
+// through LDS so that global stores are 16-byte and coalesced.
 #include <type_traits>
 
 #include "ozk_internal.h"
@@ -40,8 +41,11 @@ struct EpiModuli {
   double inv[kMaxModuli];
 };
 
+// gfx950 LDS serves a 16-byte-per-lane read 16 lanes at a time from 64 four-byte banks
+// (256 bytes per clock): lanes 0..15 of a fragment read rows r..r+15 at the same logical
+// chunk, and rows with equal (row mod 4) would hit the same banks without the XOR.
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * BK + ((chunk ^ ((row >> 1) & 3)) << 4);
+  return row * BK + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
 
 // Symmetric residue of an exact int32 product modulo m (m odd <= 255, or 256).
@@ -53,12 +57,35 @@ __device__ __forceinline__ int sym_residue(int v, int m, double inv) {
   return (int)__builtin_fma(-q, (double)m, d);
 }
 
+// Direct global -> LDS load of 16 bytes per lane (gfx950 global_load_lds_dwordx4): lane i
+// of the wave writes LDS bytes [lds_base + 16 i, +16).  Issued through inline assembly so
+// the compiler neither reorders it nor inserts conservative waits; completion is tracked
+// explicitly with s_waitcnt vmcnt and made visible to the other waves with s_barrier.
+__device__ __forceinline__ void dma16(const int8_t* g, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(g), "s"(lds_base)
+      : "memory", "m0");
+}
+
+constexpr int kStages = 4;
+constexpr int kStageBytes = kLdsA + kLdsB;  // 32 KiB: A rows 0..255 then B rows 0..255
+constexpr int kRegions = kStageBytes / 1024;  // 1 KiB regions, one per wave instruction
+constexpr int kRegionsPerWave = kRegions / 4;
+
+__device__ __forceinline__ uint32_t pack4b(int b0, int b1, int b2, int b3) {
+  return (uint32_t)(b0 & 0xff) | ((uint32_t)(b1 & 0xff) << 8) | ((uint32_t)(b2 & 0xff) << 16) |
+         ((uint32_t)b3 << 24);
+}
+
 template <int kEpi>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     int64_t m, int64_t n, int64_t kp, const int8_t* __restrict__ pa, int64_t stride_a,
     const int8_t* __restrict__ pb, int64_t stride_b, void* __restrict__ out, int64_t ldo,
-    int64_t stride_o, int tiles_m, int tiles_n, EpiModuli E) {
-  __shared__ __attribute__((aligned(16))) int8_t lds[2 * (kLdsA + kLdsB)];
+    int64_t stride_o, int tiles_m, int tiles_n, EpiModuli E, int vec_out) {
+  __shared__ __attribute__((aligned(1024))) int8_t lds[kStages * kStageBytes];
 
   // Block -> (modulus, tile row, tile column): XCD-contiguous, then grouped by kGroupM.
   const int total = gridDim.x;
@@ -85,30 +112,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
   const int wr = wave >> 1;   // 0..1: rows wr*128
   const int wc = wave & 1;    // 0..1: cols wc*128
 
-  // Global load assignment: 16-byte chunk q = tid + 256*s, row q >> 2, chunk q & 3.
-  const int64_t last_a = m - 1, last_b = n - 1;
-  const int8_t* ga[4];
-  int sa[4];
+  // Direct-load sources: wave w fills regions w, w+4, ...; region rg holds 16 rows of A
+  // (rg < 16) or B, 64 bytes each; lane i lands at row 16*(rg%16) + i/4, physical chunk
+  // i%4, which holds logical K chunk (i%4) ^ ((row >> 2) & 3) (the read-side swizzle).
+  const int8_t* src[kRegionsPerWave];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    int q = tid + kThreads * s;
-    int r = q >> 2, c = q & 3;
-    int64_t gr = row0 + r;
-    gr = gr < last_a ? gr : last_a;
-    ga[s] = A + gr * kp + c * 16;
-    sa[s] = swz(r, c);
+  for (int q = 0; q < kRegionsPerWave; ++q) {
+    const int rg = wave + 4 * q;
+    const bool is_b = rg >= 16;
+    const int row = 16 * (rg & 15) + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+    int64_t gr = (is_b ? col0 : row0) + row;
+    const int64_t last = (is_b ? n : m) - 1;
+    gr = gr < last ? gr : last;
+    src[q] = (is_b ? B : A) + gr * kp + 16 * chunk;
   }
-  const int8_t* gb[4];
-  int sb[4];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int8_t*)lds;
+  const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(lds0 + wave * 1024);
+  const int64_t nk = kp / BK;
+  auto issue_tile = [&](int64_t t) {  // tile t (clamped to the last) into stage t % kStages
+    const int64_t tc = t < nk ? t : nk - 1;
+    const uint32_t base = wave_lds + (uint32_t)(t % kStages) * kStageBytes;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    int q = tid + kThreads * s;
-    int r = q >> 2, c = q & 3;
-    int64_t gr = col0 + r;
-    gr = gr < last_b ? gr : last_b;
-    gb[s] = B + gr * kp + c * 16;
-    sb[s] = swz(r, c);
-  }
+    for (int q = 0; q < kRegionsPerWave; ++q) dma16(src[q] + tc * BK, base + q * 4096);
+  };
 
   v16i acc[4][4];
 #pragma unroll
@@ -118,39 +145,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
 
-  // Software pipeline over K tiles of 64 (two MFMA sub-steps of K = 32 each):
-  //   sub-step 0 of tile t: 16 MFMAs on fragments (t, 0), interleaved with the global
-  //     loads of tile t+2 into register set t%2, the LDS writes of tile t+1 (register
-  //     set (t+1)%2, loaded one tile earlier) and the fragment reads of (t, 1);
-  //   sub-step 1 of tile t: barrier (tile t+1 visible), then 16 MFMAs on (t, 1)
-  //     interleaved with the fragment reads of (t+1, 0).
-  // Loads past the last tile are clamped to it (in bounds, results unused), so each
-  // sub-step is a single basic block that the scheduling groups below can interleave.
-  v4i ra[2][4], rb[2][4];   // global tiles in flight
-  v4i fa[2][4], fb[2][4];   // MFMA fragments of the current and next sub-step
-  const int64_t nk = kp / BK;
-  auto load_global = [&](v4i (&xa)[4], v4i (&xb)[4], int64_t t) {
-    const int64_t k0 = (t < nk ? t : nk - 1) * BK;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) xa[s] = *reinterpret_cast<const v4i*>(ga[s] + k0);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) xb[s] = *reinterpret_cast<const v4i*>(gb[s] + k0);
-  };
-  auto store_lds = [&](int buf, const v4i (&xa)[4], const v4i (&xb)[4]) {
-    int8_t* la = lds + buf * (kLdsA + kLdsB);
-    int8_t* lb = la + kLdsA;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) *reinterpret_cast<v4i*>(la + sa[s]) = xa[s];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) *reinterpret_cast<v4i*>(lb + sb[s]) = xb[s];
-  };
   // Fragment reads: lane holds row (lane & 31) of a 32-row block and 16 bytes at
   // K offset 32*kk + 16*(lane >> 5); A and B use the same K map, so the product is
   // independent of how the instruction orders K internally.
   const int frow = lane & 31;
   const int fchunk = lane >> 5;
-  auto read_frags = [&](v4i (&xa)[4], v4i (&xb)[4], int buf, int kk) {
-    const int8_t* la = lds + buf * (kLdsA + kLdsB);
+  v4i fa[2][4], fb[2][4];
+  auto read_frags = [&](v4i (&xa)[4], v4i (&xb)[4], int64_t t, int kk) {
+    const int8_t* la = lds + (t % kStages) * kStageBytes;
     const int8_t* lb = la + kLdsA;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -159,76 +161,117 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     for (int j = 0; j < 4; ++j)
       xb[j] = *reinterpret_cast<const v4i*>(lb + swz(wc * 128 + j * 32 + frow, kk * 2 + fchunk));
   };
-  auto mfma16 = [&](const v4i (&xa)[4], const v4i (&xb)[4]) {
+
+  // Pipeline: tiles t+1 .. t+3 are in flight while tile t is multiplied.
+  //   sub-step 0 of tile t: 16 MFMAs on fragments (t, 0), reading fragments (t, 1);
+  //   wait for this wave's loads of tile t+1, barrier (tile t+1 complete from all waves;
+  //   every wave is past its reads of tile t-1);
+  //   sub-step 1 of tile t: loads of tile t+3 into the stage of tile t-1, 16 MFMAs on
+  //   (t, 1), reading fragments (t+1, 0).
+  issue_tile(0);
+  issue_tile(1);
+  issue_tile(2);
+  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  read_frags(fa[0], fb[0], 0, 0);
+  for (int64_t t = 0; t < nk; ++t) {
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(fa[1], fb[1], t, 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa[i], xb[j], acc[i][j], 0, 0, 0);
-  };
-
-  load_global(ra[0], rb[0], 0);
-  load_global(ra[1], rb[1], 1);
-  store_lds(0, ra[0], rb[0]);
-  __syncthreads();
-  read_frags(fa[0], fb[0], 0, 0);
-
-  auto tile_step = [&](auto parity, int64_t t) {
-    constexpr int p = decltype(parity)::value;
-    // sub-step 0
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[0][j], fa[0][i], acc[i][j], 0, 0, 0);
+    // All 8 reads of the next sub-step's fragments go out right after the first MFMA,
+    // so they complete long before the next sub-step needs them.
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS read x 8
+    __builtin_amdgcn_sched_group_barrier(0x008, 15, 0);  // MFMA x 15
     __builtin_amdgcn_sched_barrier(0);
-    load_global(ra[p], rb[p], t + 2);
-    store_lds(p ^ 1, ra[p ^ 1], rb[p ^ 1]);
-    read_frags(fa[1], fb[1], p, 1);
-    mfma16(fa[0], fb[0]);
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue_tile(t + 3);
+    read_frags(fa[0], fb[0], t + 1, 0);
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // sub-step 1
-    __syncthreads();
-    read_frags(fa[0], fb[0], p ^ 1, 0);
-    mfma16(fa[1], fb[1]);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-    }
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[1][j], fa[1][i], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);   // DS read x 8
+    __builtin_amdgcn_sched_group_barrier(0x008, 15, 1);  // MFMA x 15
     __builtin_amdgcn_sched_barrier(0);
-  };
-  int64_t t = 0;
-  for (; t + 2 <= nk; t += 2) {
-    tile_step(std::integral_constant<int, 0>(), t);
-    tile_step(std::integral_constant<int, 1>(), t + 1);
   }
-  if (t < nk) tile_step(std::integral_constant<int, 0>(), t);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // Output layout of a 32x32 MFMA tile: lane -> column (lane & 31); register v ->
-  // row 8*(v/4) + 4*(lane/32) + (v%4).
+  // The MFMA runs with the B fragment as its first operand, so each accumulator tile is
+  // C^T: lane -> row (lane & 31) of the 32 x 32 block of C, register v -> column
+  // 8*(v/4) + 4*(lane/32) + (v%4); registers 4q..4q+3 hold 4 consecutive columns.
   const int mod = E.mod[l];
   const double inv = E.inv[l];
+  const int64_t wrow0 = row0 + wr * 128, wcol0 = col0 + wc * 128;
+  if (kEpi == kEpiProducts) {
+    int32_t* o = reinterpret_cast<int32_t*>(out) + l * stride_o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = wrow0 + i * 32 + (lane & 31);
+      if (row >= m) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = col0 + wc * 128 + j * 32 + (lane & 31);
-      if (col >= n) continue;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = row0 + wr * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row >= m) continue;
-        const int64_t off = l * stride_o + row * ldo + col;
-        if (kEpi == kEpiProducts)
-          reinterpret_cast<int32_t*>(out)[off] = acc[i][j][v];
-        else
-          reinterpret_cast<int8_t*>(out)[off] = (int8_t)sym_residue(acc[i][j][v], mod, inv);
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = wcol0 + j * 32 + 8 * q + 4 * (lane >> 5);
+          int32_t* dst = o + row * ldo + col;
+          if (vec_out && col + 4 <= n) {
+            *reinterpret_cast<v4i*>(dst) = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                               acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (col + u < n) dst[u] = acc[i][j][4 * q + u];
+          }
+        }
+    }
+    return;
+  }
+  // Residues: stage the wave's 128 x 128 byte tile in LDS (row pitch 136: the dword writes
+  // of 64 lanes and the 8-byte reads of each 16-lane group hit distinct banks), then store
+  // rows with 16-byte coalesced writes (8 lanes per 128-byte row segment).
+  constexpr int kPitch = 136;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();  // every wave is past its last read of the LDS ring
+  int8_t* tile = lds + wave * (128 * kPitch);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w = pack4b(sym_residue(acc[i][j][4 * q], mod, inv),
+                                  sym_residue(acc[i][j][4 * q + 1], mod, inv),
+                                  sym_residue(acc[i][j][4 * q + 2], mod, inv),
+                                  sym_residue(acc[i][j][4 * q + 3], mod, inv));
+        *reinterpret_cast<uint32_t*>(tile + (i * 32 + (lane & 31)) * kPitch + j * 32 + 8 * q +
+                                     4 * (lane >> 5)) = w;
       }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave reads back only its own tile
+  int8_t* o = reinterpret_cast<int8_t*>(out) + l * stride_o;
+#pragma unroll 4
+  for (int s8 = 0; s8 < 16; ++s8) {
+    const int rl = s8 * 8 + (lane >> 3), cl = 16 * (lane & 7);
+    const int64_t row = wrow0 + rl, col = wcol0 + cl;
+    const int8_t* srcp = tile + rl * kPitch + cl;
+    const uint2 lo = *reinterpret_cast<const uint2*>(srcp);
+    const uint2 hi = *reinterpret_cast<const uint2*>(srcp + 8);
+    if (row >= m) continue;
+    int8_t* dst = o + row * ldo + col;
+    if (vec_out && col + 16 <= n) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    } else {
+      const uint32_t wv[4] = {lo.x, lo.y, hi.x, hi.y};
+      for (int u = 0; u < 16; ++u)
+        if (col + u < n) dst[u] = (int8_t)(wv[u >> 2] >> (8 * (u & 3)));
     }
   }
 }
@@ -249,14 +292,18 @@ int launch_gemm_i8(int64_t m, int64_t n, int64_t kp, int r, const int8_t* pa, in
   }
   const int64_t blocks = (int64_t)tiles_m * tiles_n * r;
   if (blocks > 0x7fffffff) return OZK_EUNSUPPORTED;
+  const int64_t elem = epilogue == kEpiProducts ? 4 : 1;
+  const int64_t vbytes = 16;
+  const int vec_out = (reinterpret_cast<uintptr_t>(out) % vbytes) == 0 &&
+                      (ldo * elem) % vbytes == 0 && (stride_o * elem) % vbytes == 0;
   if (epilogue == kEpiProducts)
     hipLaunchKernelGGL(gemm_i8_kernel<kEpiProducts>, dim3((unsigned)blocks), dim3(kThreads), 0,
                        s, m, n, kp, pa, stride_a, pb, stride_b, out, ldo, stride_o, tiles_m,
-                       tiles_n, E);
+                       tiles_n, E, vec_out);
   else
     hipLaunchKernelGGL(gemm_i8_kernel<kEpiResidues>, dim3((unsigned)blocks), dim3(kThreads), 0,
                        s, m, n, kp, pa, stride_a, pb, stride_b, out, ldo, stride_o, tiles_m,
-                       tiles_n, E);
+                       tiles_n, E, vec_out);
   return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
 }
 

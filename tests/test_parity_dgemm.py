@@ -140,8 +140,13 @@ def test_reconstruct_extremes():
     rng = np.random.default_rng(0)
     xs = [0, 1, -1, half, -half, half - 12345, 2**60 + 1, -(2**53 + 1), 2**53 + 3, 3, 5, 7]
     xs += [int(v) for v in rng.integers(-2**62, 2**62, size=20)]
+    # exact midpoints of the 53-bit rounding, with and without nonzero lower digits
+    ties = [2**93 + 2**40, 2**93 + 2**40 + 1, -(2**93 + 2**40 + 1), 2**53 + 1, 2**53 + 3,
+            (2**53 + 1) * 2**40 + 7, 2**80 + 2**27, 2**80 + 2**27 + 5, 2**101 + 2**48 + 3]
+    xs += ties
     shifts = [0, 1075, 1076, 1074, 1100, -970, -1000, 60, -10, 1075, 1075, 1075]
     shifts += [int(v) for v in rng.integers(-900, 1200, size=20)]
+    shifts += [0, 0, 0, 0, 0, 40, 0, 3, 1100]
     n = len(xs)
     prods = np.empty((r, 1, n), dtype=np.int64)
     for j, x in enumerate(xs):
