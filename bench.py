@@ -10,12 +10,16 @@ Also reported on the same JSON line:
   roofline      the dominant kernel (batched int8 MFMA products, residue epilogue) timed
                 alone with HIP events on its stream: r * 2 * m * n * kp int8 ops per launch
                 against the 5.0 POP/s dense int8 MFMA peak; HBM traffic per launch from
-                the committed rocprofv3 counter summary when it matches the kernel source.
+                the committed rocprofv3 counter summary when it matches the kernel source
+                (made by `--counters` under two `rocprofv3 --pmc` passes, then
+                `--traffic-summary FETCH_DIR WRITE_DIR`).
   cpu_baseline  the CPU oracle (numpy, one BLAS thread) on 8 full output rows.
   extras        native fp64 DGEMM (torch.matmul), the r sweep 12..18, deconstruction HBM
                 GB/s, the GEMV and FP4-limb engines when built.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--r 16] [--no-cpu-baseline]
+       python bench.py --counters            (launches only, for rocprofv3 --pmc)
+       python bench.py --traffic-summary FETCH_DIR WRITE_DIR
 """
 from __future__ import annotations
 
@@ -60,19 +64,111 @@ def _time_events(fn, reps: int, stream) -> float:
     return start.elapsed_time(end) / reps
 
 
+TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic_dgemm_4096_r16.json")
+COPY_BYTES = 1 << 30   # calibration copy (elementwise negation): 1 GiB read + 1 GiB written
+
+
 def _traffic(kernel: str, digest: str):
     """HBM bytes per launch from the committed counter summary, if it was taken on this
     exact kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
-        with open(path) as fh:
+        with open(TRAFFIC_PATH) as fh:
             data = json.load(fh)
     except (OSError, ValueError):
         return None
-    ent = data.get(kernel)
+    ent = data.get("kernels", {}).get(kernel)
     if not ent or ent.get("source_digest") != digest:
         return None
     return ent.get("hbm_bytes_per_launch")
+
+
+# Kernels summarised from the counter passes: key -> (kernel-name substring, sources).
+COUNTER_KERNELS = {
+    "gemm_i8_residues": ("gemm_i8_kernel<1>", ["gemm_i8.hip"]),
+    "residues_rows_fused": ("residues_rows_fused_kernel", ["deconstruct.hip"]),
+    "absmax_cols": ("absmax_cols_kernel", ["deconstruct.hip"]),
+    "residues_cols": ("residues_cols_kernel", ["deconstruct.hip"]),
+    "crt": ("crt_kernel<16", ["crt.hip"]),
+}
+
+
+def run_counter_workload() -> int:
+    """Launches profiled by the rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE): a
+    plain device copy of COPY_BYTES (calibration), then two default steps (their kernels:
+    deconstruction of A and B, the residue GEMM, CRT).  Nothing is timed."""
+    import torch
+
+    import fp64_gemm_emulation_ozk_amd as ozk
+    import ozk_inputs
+
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 8, dtype=torch.float64, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        torch.neg(src, out=dst)     # one plain streaming read and write of COPY_BYTES
+    torch.cuda.synchronize()
+    del src, dst
+    a, b = ozk_inputs.gemm_operands(M, N, K, seed=SEED, dist="phi", phi=PHI)
+    da, db = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    out = torch.empty((M, N), dtype=torch.float64, device=dev)
+    ws = torch.empty(ozk.ozk_dgemm_workspace_size(M, N, K, 16), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        ozk.ozk_dgemm(da, db, 16, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    print("counter workload done", flush=True)
+    return 0
+
+
+def _counter_means(run_dir: str, counter: str) -> dict:
+    """Mean per-dispatch value of `counter` for each kernel name in a rocprofv3 csv run."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    acc = {}
+    for f in files:
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != counter:
+                    continue
+                acc.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def traffic_summary(fetch_dir: str, write_dir: str) -> int:
+    """Turn the two counter passes into per-launch HBM bytes, scaled by what the same
+    counters read for the calibration copy, and write TRAFFIC_PATH."""
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+
+    def pick(table, sub):
+        hits = [v for k, v in table.items() if sub in k]
+        if not hits:
+            raise SystemExit(f"kernel {sub!r} not found among {sorted(table)[:8]}")
+        return sum(hits) / len(hits)
+
+    copy_f, copy_w = pick(fetch, "neg_kernel"), pick(write, "neg_kernel")   # KiB per dispatch
+    f_fac = COPY_BYTES / (copy_f * 1024.0)
+    w_fac = COPY_BYTES / (copy_w * 1024.0)
+    data = {"what": "L2-to-fabric bytes per launch (HBM or MALL) from rocprofv3 FETCH_SIZE and "
+                    "WRITE_SIZE (KiB per dispatch), each scaled by the factor that maps the "
+                    "same counter on a plain 1 GiB device copy to 1 GiB",
+            "calibration": {"copy_bytes": COPY_BYTES, "fetch_kib": copy_f, "write_kib": copy_w,
+                            "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},
+            "kernels": {}}
+    for key, (sub, srcs) in COUNTER_KERNELS.items():
+        fb = pick(fetch, sub) * 1024.0 * f_fac
+        wb = pick(write, sub) * 1024.0 * w_fac
+        data["kernels"][key] = {"kernel": sub, "fetch_bytes": round(fb), "write_bytes": round(wb),
+                                "hbm_bytes_per_launch": round(fb + wb),
+                                "source_digest": _source_digest(srcs)}
+    with open(TRAFFIC_PATH, "w") as fh:
+        json.dump(data, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(data, indent=1))
+    return 0
 
 
 def measure_gemv(reps: int, stream) -> dict:
@@ -204,7 +300,13 @@ def main() -> int:
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--no-fp4", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="only launch the kernels the counter passes profile")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the HBM traffic summary from two rocprofv3 --pmc csv runs")
     args = ap.parse_args()
+    if args.traffic_summary:
+        return traffic_summary(*args.traffic_summary)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the emulation "
               "path is built and measured on a single MI355X; multi-GPU runs are not "
@@ -220,6 +322,8 @@ def main() -> int:
     if not os.path.exists(ozk.LIB_PATH):
         from fp64_gemm_emulation_ozk_amd.build import build_library
         build_library()
+    if args.counters:
+        return run_counter_workload()
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     r = args.r

@@ -8,13 +8,14 @@
 //
 // Tiling: workgroup tile 256 x 256 x 64, 256 threads = 4 waves, each wave a 128 x 128
 // block of 4 x 4 MFMA tiles of 32 x 32 (256 accumulator registers, held in AGPRs), so
-// every 16-byte LDS fragment read feeds two MFMAs.  Global tiles are loaded straight into
-// a 4-stage LDS ring (128 KiB) by global_load_lds_dwordx4, three K tiles ahead, with one
-// barrier per K tile placed between the two MFMA sub-steps (see the pipeline below); LDS rows are 64 bytes with the four 16-byte chunks
-// XOR-swizzled by (row >> 1) & 3 so that the fragment reads of 8 consecutive rows hit 8
-// distinct bank groups.  Workgroups are mapped XCD by XCD (the hardware deals them out
-// round-robin over the 8 XCDs) onto contiguous runs of tiles, ordered in groups of 4
-// tile rows, so the tiles in flight on one XCD share A rows and B columns in its L2.
+// every 16-byte LDS fragment read feeds four MFMAs.  Global tiles are loaded straight
+// into a 4-stage LDS ring (128 KiB) by global_load_lds_dwordx4, three K tiles ahead, with
+// one barrier per K tile placed between the two MFMA sub-steps (see the pipeline below).
+// LDS rows are 64 bytes with the four 16-byte chunks XOR-swizzled by (row >> 2) & 3, so
+// the 16 lanes of a fragment read (16 consecutive rows, one chunk each) cover all 64
+// banks.  Workgroups are mapped XCD by XCD (the hardware deals them out round-robin over
+// the 8 XCDs) onto contiguous runs of tiles, ordered in groups of 4 tile rows, so the
+// tiles in flight on one XCD share A rows and B columns in its L2.
 //
 // Epilogues: the int32 products themselves, or their symmetric residues modulo m_l as
 // int8 (what the CRT reconstruction consumes: 1 byte instead of 4 per output), staged
@@ -48,13 +49,23 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * BK + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
 
-// Symmetric residue of an exact int32 product modulo m (m odd <= 255, or 256).
-__device__ __forceinline__ int sym_residue(int v, int m, double inv) {
-  if (m == 256) return (int)(int8_t)(v & 0xff);
+// Low byte of the symmetric residue of an exact int32 product v modulo an odd m <= 255.
+// q = round(v / m) is read from the low word of v * RN(1/m) + 1.5 * 2^52: the product is
+// within 2^-30 of v / m, whose distance to a half-integer is at least 1 / (2m), so the
+// rounding is exact.  The residue v - q m lies in [-(m-1)/2, (m-1)/2]; its low byte is
+// (v - q m) mod 2^8, for which the low 24 bits of q suffice (v_mul_u32_u24).
+__device__ __forceinline__ uint32_t residue_byte_odd(int v, uint32_t m, double inv) {
   constexpr double kMagicD = 6755399441055744.0;
-  double d = (double)v;
-  double q = __builtin_fma(d, inv, kMagicD) - kMagicD;
-  return (int)__builtin_fma(-q, (double)m, d);
+  const double t = __builtin_fma((double)v, inv, kMagicD);
+  const uint32_t q = (uint32_t)__double_as_longlong(t);
+  return (uint32_t)v - __umul24(q, m);
+}
+
+// Bytes 0 of four words into one word (b0 lowest).
+__device__ __forceinline__ uint32_t pack4b(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
 // Direct global -> LDS load of 16 bytes per lane (gfx950 global_load_lds_dwordx4): lane i
@@ -64,6 +75,7 @@ __device__ __forceinline__ int sym_residue(int v, int m, double inv) {
 __device__ __forceinline__ void dma16(const int8_t* g, uint32_t lds_base) {
   asm volatile(
       "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
       "global_load_lds_dwordx4 %0, off"
       :
       : "v"(g), "s"(lds_base)
@@ -74,11 +86,6 @@ constexpr int kStages = 4;
 constexpr int kStageBytes = kLdsA + kLdsB;  // 32 KiB: A rows 0..255 then B rows 0..255
 constexpr int kRegions = kStageBytes / 1024;  // 1 KiB regions, one per wave instruction
 constexpr int kRegionsPerWave = kRegions / 4;
-
-__device__ __forceinline__ uint32_t pack4b(int b0, int b1, int b2, int b3) {
-  return (uint32_t)(b0 & 0xff) | ((uint32_t)(b1 & 0xff) << 8) | ((uint32_t)(b2 & 0xff) << 16) |
-         ((uint32_t)b3 << 24);
-}
 
 template <int kEpi>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
@@ -162,12 +169,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
       xb[j] = *reinterpret_cast<const v4i*>(lb + swz(wc * 128 + j * 32 + frow, kk * 2 + fchunk));
   };
 
+  // One fragment read (idx 0..3: A blocks, 4..7: B blocks) of K half kk of tile t.
+  auto frag_read = [&](v4i (&xa)[4], v4i (&xb)[4], int64_t t, int kk, int idx) {
+    const int8_t* la = lds + (t % kStages) * kStageBytes;
+    if (idx < 4)
+      xa[idx] = *reinterpret_cast<const v4i*>(la + swz(wr * 128 + idx * 32 + frow, kk * 2 + fchunk));
+    else
+      xb[idx - 4] = *reinterpret_cast<const v4i*>(
+          la + kLdsA + swz(wc * 128 + (idx - 4) * 32 + frow, kk * 2 + fchunk));
+  };
+
   // Pipeline: tiles t+1 .. t+3 are in flight while tile t is multiplied.
-  //   sub-step 0 of tile t: 16 MFMAs on fragments (t, 0), reading fragments (t, 1);
+  //   sub-step 0 of tile t: 16 MFMAs on fragments (t, 0), one read of fragments (t, 1)
+  //   after every other MFMA;
   //   wait for this wave's loads of tile t+1, barrier (tile t+1 complete from all waves;
   //   every wave is past its reads of tile t-1);
-  //   sub-step 1 of tile t: loads of tile t+3 into the stage of tile t-1, 16 MFMAs on
-  //   (t, 1), reading fragments (t+1, 0).
+  //   sub-step 1 of tile t: 16 MFMAs on (t, 1), alternately followed by one load of tile
+  //   t+3 (into the stage of tile t-1) and one read of fragments (t+1, 0).
+  // Every MFMA is followed by at most one memory instruction (pinned by scheduling
+  // barriers), so the issue of loads and LDS reads hides behind the matrix pipe.
   issue_tile(0);
   issue_tile(1);
   issue_tile(2);
@@ -176,32 +196,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
   read_frags(fa[0], fb[0], 0, 0);
   for (int64_t t = 0; t < nk; ++t) {
     __builtin_amdgcn_sched_barrier(0);
-    read_frags(fa[1], fb[1], t, 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[0][j], fa[0][i], acc[i][j], 0, 0, 0);
-    // All 8 reads of the next sub-step's fragments go out right after the first MFMA,
-    // so they complete long before the next sub-step needs them.
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS read x 8
-    __builtin_amdgcn_sched_group_barrier(0x008, 15, 0);  // MFMA x 15
-    __builtin_amdgcn_sched_barrier(0);
+    for (int idx = 0; idx < 16; ++idx) {
+      const int i = idx >> 2, j = idx & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[0][j], fa[0][i], acc[i][j], 0, 0, 0);
+      if ((idx & 1) == 0) frag_read(fa[1], fb[1], t, 1, idx >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue_tile(t + 3);
-    read_frags(fa[0], fb[0], t + 1, 0);
+    const int64_t tl = t + 3 < nk ? t + 3 : nk - 1;   // past the end: reload the last tile
+    const uint32_t base = wave_lds + (uint32_t)((t + 3) % kStages) * kStageBytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[1][j], fa[1][i], acc[i][j], 0, 0, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);   // DS read x 8
-    __builtin_amdgcn_sched_group_barrier(0x008, 15, 1);  // MFMA x 15
-    __builtin_amdgcn_sched_barrier(0);
+    for (int idx = 0; idx < 16; ++idx) {
+      const int i = idx >> 2, j = idx & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[1][j], fa[1][i], acc[i][j], 0, 0, 0);
+      if ((idx & 1) == 0)
+        dma16(src[idx >> 1] + tl * BK, base + (idx >> 1) * 4096);
+      else
+        frag_read(fa[0], fb[0], t + 1, 0, idx >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -242,19 +258,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();  // every wave is past its last read of the LDS ring
   int8_t* tile = lds + wave * (128 * kPitch);
+  // m = 256 keeps the low byte of the product; odd moduli reduce (uniform branch, taken
+  // once per tile rather than per element).
+  auto stage = [&](auto byte_of) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t w = pack4b(sym_residue(acc[i][j][4 * q], mod, inv),
-                                  sym_residue(acc[i][j][4 * q + 1], mod, inv),
-                                  sym_residue(acc[i][j][4 * q + 2], mod, inv),
-                                  sym_residue(acc[i][j][4 * q + 3], mod, inv));
-        *reinterpret_cast<uint32_t*>(tile + (i * 32 + (lane & 31)) * kPitch + j * 32 + 8 * q +
-                                     4 * (lane >> 5)) = w;
-      }
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t w = pack4b(byte_of(acc[i][j][4 * q]), byte_of(acc[i][j][4 * q + 1]),
+                                    byte_of(acc[i][j][4 * q + 2]), byte_of(acc[i][j][4 * q + 3]));
+          *reinterpret_cast<uint32_t*>(tile + (i * 32 + (lane & 31)) * kPitch + j * 32 + 8 * q +
+                                       4 * (lane >> 5)) = w;
+        }
+  };
+  if (mod == 256) {
+    stage([](int v) { return (uint32_t)v; });
+  } else {
+    const uint32_t um = (uint32_t)mod;
+    stage([=](int v) { return residue_byte_odd(v, um, inv); });
+  }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave reads back only its own tile
   int8_t* o = reinterpret_cast<int8_t*>(out) + l * stride_o;
 #pragma unroll 4
