@@ -219,10 +219,12 @@ namespace {
 
 struct GemvLayout {
   int64_t kp;
-  size_t x_planes, x_exps, x_max, res, a_exps, a_max;
+  bool digits;   // on the fly through base-256 digits (scaling bits of A <= 50)
+  size_t x_planes, x_exps, x_max, res, a_exps, a_max, xd, corr, part;
   size_t total() const {
     return align256(x_planes) + align256(x_exps) + align256(x_max) + align256(res) +
-           align256(a_exps) + align256(a_max);
+           align256(a_exps) + align256(a_max) + align256(xd) + align256(corr) +
+           align256(part);
   }
 };
 
@@ -235,6 +237,11 @@ GemvLayout gemv_layout(int64_t m, int64_t k, int64_t nrhs, int r, int mode) {
   L.res = (size_t)r * m * nrhs;
   L.a_exps = mode == 0 ? (size_t)m * 4 : 0;
   L.a_max = mode == 0 ? (size_t)m * 8 : 0;
+  int pa = 0, pb = 0;
+  L.digits = mode == 0 && scaling_bits(r, k, &pa, &pb) == OZK_OK &&
+             gemv_digits_supported(pa, (int64_t)r * nrhs);
+  L.xd = L.corr = L.part = 0;
+  if (L.digits) gemv_digits_workspace(m, L.kp, r, nrhs, &L.xd, &L.corr, &L.part);
   return L;
 }
 
@@ -282,6 +289,9 @@ int ozk_dgemv(int64_t m, int64_t k, int64_t nrhs, const double* A, int64_t lda,
   int8_t* res = static_cast<int8_t*>(cv.take(L.res));
   int32_t* a_exps = static_cast<int32_t*>(cv.take(L.a_exps));
   uint64_t* a_max = static_cast<uint64_t*>(cv.take(L.a_max));
+  int8_t* xd = static_cast<int8_t*>(cv.take(L.xd));
+  int32_t* corr = static_cast<int32_t*>(cv.take(L.corr));
+  int8_t* part = static_cast<int8_t*>(cv.take(L.part));
   hipStream_t s = as_stream(stream);
   const int64_t kp = L.kp;
   if ((st = deconstruct_impl(X, k, nrhs, ldx, 1, r, pb, x_planes, kp, nrhs * kp, x_exps, x_max,
@@ -293,7 +303,11 @@ int ozk_dgemv(int64_t m, int64_t k, int64_t nrhs, const double* A, int64_t lda,
       if ((st = launch_line_exps(A, m, k, lda, 0, pa, a_max, a_exps, s))) return st;
       ea = a_exps;
     }
-    st = launch_gemv_fly(A, m, k, lda, ea, r, pa, x_planes, kp, nrhs * kp, (int)nrhs, res, s);
+    if (L.digits)
+      st = launch_gemv_digits(A, m, k, lda, ea, r, x_planes, kp, nrhs * kp, (int)nrhs, xd, corr,
+                              part, res, s);
+    else
+      st = launch_gemv_fly(A, m, k, lda, ea, r, pa, x_planes, kp, nrhs * kp, (int)nrhs, res, s);
   } else {
     st = launch_gemv_stored(m, kp, r, A_planes, ldp, plane_stride, x_planes, nrhs * kp,
                             (int)nrhs, res, s);

@@ -73,6 +73,15 @@ int launch_gemv_fly(const double* a, int64_t m, int64_t k, int64_t lda, const in
                     int r, int p_bits, const int8_t* xp, int64_t ldp, int64_t x_stride, int nrhs,
                     int8_t* res, hipStream_t s);
 
+// On-the-fly GEMV through base-256 digits of the scaled integers (scaling bits <= 50,
+// at most 256 output columns r * nrhs).
+bool gemv_digits_supported(int p_bits, int64_t ncols);
+size_t gemv_digits_workspace(int64_t m, int64_t kp, int r, int64_t nrhs, size_t* xd_bytes,
+                             size_t* corr_bytes, size_t* part_bytes);
+int launch_gemv_digits(const double* a, int64_t m, int64_t k, int64_t lda, const int32_t* exps,
+                       int r, const int8_t* xp, int64_t kp, int64_t x_stride, int nrhs,
+                       int8_t* xd, int32_t* psum, int8_t* part, int8_t* res, hipStream_t s);
+
 int launch_fp4_pack(const int8_t* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
                     uint8_t* planes, int64_t ldpb, int64_t plane_stride, hipStream_t s);
 int launch_fp4_products(int64_t m, int64_t n, int64_t ldpb, const uint8_t* pa, int64_t stride_a,
