@@ -76,6 +76,67 @@ def test_dgemv_special_rows(mode):
     assert assert_within_ulps(got.cpu().numpy(), want, 2) == 0
 
 
+# The on-the-fly mode streams A through base-256 digits of the scaled integers when the
+# row budget P_A is at most 50 bits and r * nrhs <= 256; these cases are chosen to take
+# that path (P_A from the oracle's budget), with its edge cases: rows so small that the
+# scale 2^e exceeds the fp64 range (e > 1023), zero and NaN rows, scaled integers of
+# exactly +-2^P_A at P_A = 50, several K slices of 8192 with a ragged tail, and 8 column
+# tiles.
+def _digit_path(k, r, nrhs):
+    from oracle import rns
+    pa, _ = rns.scaling_bits(r, k)
+    return pa <= 50 and r * nrhs <= 256
+
+
+def test_dgemv_digits_special_rows():
+    announce("dgemv digits special rows")
+    m, k, nrhs, r = 100, 300, 4, 14
+    assert _digit_path(k, r, nrhs)
+    rng = np.random.default_rng(18)
+    a = ozk_inputs.phi_matrix(rng, (m, k), 4.0)
+    x = ozk_inputs.uniform_matrix(rng, (k, nrhs))
+    a[3] = 0.0
+    a[7, 11] = np.nan
+    a[9] *= 1e-305          # e > 1023 for this row
+    a[10] = 1e-320 * np.sign(a[10])   # subnormal row
+    a[12, 5] = np.inf
+    got = _run(a, x, r, 0)
+    torch.cuda.synchronize()
+    want = ozaki2.dgemv(a, x, r)
+    assert assert_within_ulps(got.cpu().numpy(), want, 2) == 0
+
+
+def test_dgemv_digits_extreme_scaled_integers():
+    announce("dgemv digits |a'| = 2^P_A")
+    from oracle import rns
+    m, k, nrhs, r = 40, 257, 2, 14
+    pa, _ = rns.scaling_bits(r, k)
+    assert pa == 50 and _digit_path(k, r, nrhs)
+    rng = np.random.default_rng(19)
+    a = ozk_inputs.uniform_matrix(rng, (m, k))
+    x = ozk_inputs.uniform_matrix(rng, (k, nrhs))
+    top = np.nextafter(2.0, 0.0)        # scales to 2^50 - 1/8, rounds to 2^50
+    for i in range(m):
+        a[i, (7 * i) % k] = (top if i % 2 == 0 else -top) * 2.0 ** (i - 20)
+        a[i] = np.where(np.abs(a[i]) > abs(a[i, (7 * i) % k]), 0.0, a[i])
+    got = _run(a, x, r, 0)
+    torch.cuda.synchronize()
+    want = ozaki2.dgemv(a, x, r)
+    assert assert_within_ulps(got.cpu().numpy(), want, 2) == 0
+
+
+@pytest.mark.parametrize("m,k,nrhs,r", [(130, 2 * 8192 + 37, 2, 12), (70, 500, 18, 14),
+                                        (33, 8192, 1, 10)])
+def test_dgemv_digits_slices_and_tiles(m, k, nrhs, r):
+    announce(f"dgemv digits m={m} k={k} nrhs={nrhs} r={r}")
+    assert _digit_path(k, r, nrhs)
+    a, x = ozk_inputs.gemv_operands(m, k, nrhs, seed=m + nrhs)
+    got = _run(a, x, r, 0)
+    torch.cuda.synchronize()
+    want = ozaki2.dgemv(a, x, r)
+    assert assert_within_ulps(got.cpu().numpy(), want, 2) == 0
+
+
 def test_dgemv_strided():
     announce("dgemv strided")
     a, x = ozk_inputs.gemv_operands(70, 90, 3, seed=2)
