@@ -47,43 +47,76 @@ __device__ __forceinline__ void store_tile(const v16i& acc, int lane, int64_t ro
 }
 
 // ------------------------------------------------------------------ stored planes
-// grid (ceil(m / 128), r); 4 waves, each 32 rows of one modulus over all of K.
+// grid (ceil(m / (128 TR)), r); 4 waves, each TR tiles of 32 rows of one modulus over all
+// of K, so every X fragment (read from L2) feeds TR MFMAs.  Per step of 4 K chunks a lane
+// loads 64 contiguous bytes of each of its rows (one 128-byte line per row and lane pair);
+// the next step's loads are issued before this step's MFMAs.
+template <int TR>
 __global__ __launch_bounds__(256) void gemv_stored_kernel(
     const int8_t* __restrict__ ap, int64_t lda_p, int64_t a_stride, int64_t m,
     const int8_t* __restrict__ xp, int64_t kp, int64_t x_stride, int nrhs,
     int8_t* __restrict__ res, int64_t res_stride, GemvModuli E) {
   const int l = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 32;
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 32 * TR;
   if (row0 >= m) return;
-  int64_t row = row0 + (lane & 31);
-  row = row < m ? row : m - 1;
+  const int half = lane >> 5;
+  const int8_t* pa[TR];
+#pragma unroll
+  for (int t = 0; t < TR; ++t) {
+    int64_t row = row0 + 32 * t + (lane & 31);
+    row = row < m ? row : m - 1;
+    pa[t] = ap + l * a_stride + row * lda_p + 16 * half;
+  }
   int col = lane & 31;
   col = col < nrhs ? col : nrhs - 1;
-  const int half = lane >> 5;
-  const int8_t* pa = ap + l * a_stride + row * lda_p + 16 * half;
   const int8_t* px = xp + l * x_stride + col * kp + 16 * half;
-  v16i acc;
+  v16i acc[TR];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0;
+  for (int t = 0; t < TR; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[t][v] = 0;
+  // Register double buffering: the loads of step c + kU are in flight while the MFMAs of
+  // step c run.
+  constexpr int kU = 4;   // K chunks of 32 bytes per step
   const int64_t nc = kp / 32;
-  int64_t c = 0;
-  for (; c + 4 <= nc; c += 4) {
-    v4i a[4], x[4];
+  const int64_t nsteps = nc / kU;
+  v4i a0[TR][kU], x0[kU], a1[TR][kU], x1[kU];
+  auto load = [&](v4i (&av)[TR][kU], v4i (&xv)[kU], int64_t c) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      a[u] = *reinterpret_cast<const v4i*>(pa + (c + u) * 32);
-      x[u] = *reinterpret_cast<const v4i*>(px + (c + u) * 32);
+    for (int u = 0; u < kU; ++u) {
+#pragma unroll
+      for (int t = 0; t < TR; ++t) av[t][u] = *reinterpret_cast<const v4i*>(pa[t] + (c + u) * 32);
+      xv[u] = *reinterpret_cast<const v4i*>(px + (c + u) * 32);
     }
+  };
+  auto mma = [&](const v4i (&av)[TR][kU], const v4i (&xv)[kU]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[u], x[u], acc, 0, 0, 0);
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int t = 0; t < TR; ++t)
+        acc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[t][u], xv[u], acc[t], 0, 0, 0);
+  };
+  if (nsteps > 0) load(a0, x0, 0);
+  int64_t st = 0;
+  for (; st + 2 <= nsteps; st += 2) {
+    load(a1, x1, (st + 1) * kU);
+    mma(a0, x0);
+    if (st + 2 < nsteps) load(a0, x0, (st + 2) * kU);
+    mma(a1, x1);
   }
-  for (; c < nc; ++c) {
-    const v4i a = *reinterpret_cast<const v4i*>(pa + c * 32);
+  if (st < nsteps) mma(a0, x0);
+  for (int64_t c = nsteps * kU; c < nc; ++c) {
     const v4i x = *reinterpret_cast<const v4i*>(px + c * 32);
-    acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, x, acc, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < TR; ++t) {
+      const v4i a = *reinterpret_cast<const v4i*>(pa[t] + c * 32);
+      acc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, x, acc[t], 0, 0, 0);
+    }
   }
-  store_tile(acc, lane, row0, m, nrhs, E.mod[l], E.inv[l], res + l * res_stride);
+#pragma unroll
+  for (int t = 0; t < TR; ++t)
+    store_tile(acc[t], lane, row0 + 32 * t, m, nrhs, E.mod[l], E.inv[l], res + l * res_stride);
 }
 
 // ------------------------------------------------------------------ on the fly
@@ -234,9 +267,12 @@ int launch_gemv_stored(int64_t m, int64_t kp, int r, const int8_t* ap, int64_t l
                        int64_t a_stride, const int8_t* xp, int64_t x_stride, int nrhs,
                        int8_t* res, hipStream_t s) {
   if (m <= 0) return OZK_OK;
-  dim3 grid((unsigned)((m + 127) / 128), (unsigned)r);
-  hipLaunchKernelGGL(gemv_stored_kernel, grid, dim3(256), 0, s, ap, lda_p, a_stride, m, xp, kp,
-                     x_stride, nrhs, res, m * nrhs, gemv_moduli(r));
+  // Two row tiles per wave: every X fragment (an L2 read) feeds two MFMAs; measured
+  // faster than one or four tiles for 1, 8 and 32 right-hand sides at 32768 x 32768.
+  constexpr int kTr = 2;
+  dim3 grid((unsigned)((m + 128 * kTr - 1) / (128 * kTr)), (unsigned)r);
+  hipLaunchKernelGGL(gemv_stored_kernel<kTr>, grid, dim3(256), 0, s, ap, lda_p, a_stride, m, xp,
+                     kp, x_stride, nrhs, res, m * nrhs, gemv_moduli(r));
   return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
 }
 
