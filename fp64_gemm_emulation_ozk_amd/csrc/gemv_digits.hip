@@ -41,7 +41,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 constexpr int kSliceElems = 8192;          // elements of K per int32 accumulation
 constexpr int kSuper = 16;                 // elements per super-chunk (128 digit bytes)
 constexpr int kRowsPerBlock = 128;         // 4 waves x 32 rows
-constexpr int kMaxTiles = 16;              // 32-column MFMA tiles per pass (256 AGPRs)
+constexpr int kMaxTiles = 8;               // 32-column MFMA tiles per pass (r * nrhs <= 256)
 
 struct DigitModuli {
   int32_t m[kMaxModuli];
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void xdigits_kernel(const int8_t* __restrict__
 // next group are issued at the start of a group and written to LDS at its end.
 template <int NT>
 struct DigitsShape {
-  static constexpr int G = NT == 1 ? 4 : (NT == 2 ? 2 : 1);   // super-chunks per stage
+  static constexpr int G = NT == 1 ? 4 : (NT <= 4 ? 2 : 1);   // super-chunks per stage
   static constexpr int kStageBytes = G * NT * 32 * 128;
   static constexpr int kLoads = G * NT;                        // 16-byte loads per thread
 };
@@ -383,8 +383,7 @@ int launch_gemv_digits(const double* a, int64_t m, int64_t k, int64_t lda, const
     break
   switch (nt) {
     OZK_DIG(1); OZK_DIG(2); OZK_DIG(3); OZK_DIG(4); OZK_DIG(5); OZK_DIG(6); OZK_DIG(7);
-    OZK_DIG(8); OZK_DIG(9); OZK_DIG(10); OZK_DIG(11); OZK_DIG(12); OZK_DIG(13); OZK_DIG(14);
-    OZK_DIG(15); OZK_DIG(16);
+    OZK_DIG(8);
     default: return OZK_EINVAL;
   }
 #undef OZK_DIG
