@@ -16,6 +16,7 @@
 // for K <= 131071 every partial sum is an integer below 2^24 and fp32 holds it exactly;
 // the classes are then converted to integers and combined with weights 1, 13, 169, 2197,
 // 28561 in wrap-around 32-bit arithmetic (the exact result fits int32: |C| <= 2^14 K).
+#include "lds_dma.h"
 #include "ozk_internal.h"
 
 namespace ozk {
@@ -183,12 +184,27 @@ __global__ __launch_bounds__(64) void limb_products_kernel(
 // ------------------------------------------------------------------ fused weighted GEMM
 // Workgroup tile 128 x 128, K step 64 (32 bytes per row per digit plane), 512 threads =
 // 8 waves in 2 x 4, each wave 64 x 32 = 2 MFMA blocks x 5 weight classes (160 AGPRs).
-// Digit planes of A and B go through registers into double-buffered LDS (2 x 24 KiB);
-// LDS rows are 32 bytes with the two 16-byte halves swapped on rows with bit 3 set.
+// The three digit planes of A and of B (24 KiB per K step) are loaded straight into a
+// 4-stage LDS ring by global_load_lds_dwordx4, three K steps ahead; LDS rows are 32 bytes
+// with the two 16-byte halves swapped on rows with bit 3 set (the swap is applied on the
+// load side), so the 16 lanes of a fragment read hit distinct banks.  Each K step runs
+// in two halves around one barrier:
+//   half 0: the 9 digit products of row block 0, reading row block 1's A fragments;
+//   wait for this wave's loads of step t+1, barrier (step t+1 complete from all waves,
+//   every wave past its reads of step t-1);
+//   half 1: the 9 products of row block 1, with the loads of step t+3 (into the stage of
+//   step t-1) and the reads of step t+1's row block 0 and B fragments between the MFMAs.
+// Workgroups are dealt out XCD by XCD onto contiguous runs of tiles grouped by 4 tile
+// rows, so the tiles in flight on one XCD share A rows and B columns in its L2.
 constexpr int FBM = 128, FBN = 128, FROW = 32;  // bytes per row per plane per K step
 constexpr int kFThreads = 512;
 constexpr int kPlaneA = FBM * FROW, kPlaneB = FBN * FROW;
 constexpr int kStage = 3 * (kPlaneA + kPlaneB);  // 24 KiB
+constexpr int kFStages = 4;
+constexpr int kFRegions = kStage / 1024;         // 1 KiB per wave load instruction
+constexpr int kFRegionsPerWave = kFRegions / 8;  // 3
+constexpr int kFGroupM = 4;
+constexpr int kFXcds = 8;
 
 // 16 lanes read rows r..r+15 at the same half; rows 8 apart share banks without the XOR
 // (gfx950 LDS: 64 four-byte banks, 16 lanes of 16 bytes per clock).
@@ -199,31 +215,48 @@ __device__ __forceinline__ int fswz(int row, int half) {
 __global__ __launch_bounds__(kFThreads, 1) void fp4_gemm_kernel(
     int64_t m, int64_t n, int64_t ldpb, const uint8_t* __restrict__ pa, int64_t stride_a,
     const uint8_t* __restrict__ pb, int64_t stride_b, int32_t* __restrict__ c, int64_t ldc,
-    int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - (blockIdx.x / tiles_n) * tiles_n;
+    int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kFStages * kStage];
+
+  // Block -> tile: XCD-contiguous, then grouped by kFGroupM tile rows.
+  const int total = gridDim.x;
+  int bid = blockIdx.x;
+  if (total % kFXcds == 0) bid = (bid % kFXcds) * (total / kFXcds) + bid / kFXcds;
+  const int per_group = kFGroupM * tiles_n;
+  const int first_m = (bid / per_group) * kFGroupM;
+  const int gsize = tiles_m - first_m < kFGroupM ? tiles_m - first_m : kFGroupM;
+  const int in_group = bid % per_group;
+  const int tm = first_m + in_group % gsize;
+  const int tn = in_group / gsize;
   const int64_t row0 = (int64_t)tm * FBM, col0 = (int64_t)tn * FBN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 2;  // 0..1: rows wr*64
   const int wc = wave & 3;   // 0..3: cols wc*32
 
-  // Global -> LDS assignment: 1536 chunks of 16 bytes (A planes, then B planes), 3 each.
-  const uint8_t* gsrc[3];
-  int ldst[3];
+  // Direct-load sources: wave w fills regions w, w + 8, w + 16 of a stage; region g holds
+  // 32 rows of one plane (g < 12: A planes g / 4, else B planes (g - 12) / 4); lane i
+  // lands at row 32 (g % 4) + i / 2, physical half i % 2, which holds logical half
+  // (i % 2) ^ ((row >> 3) & 1).
+  const uint8_t* src[kFRegionsPerWave];
 #pragma unroll
-  for (int s = 0; s < 3; ++s) {
-    const int q = tid + kFThreads * s;
-    const bool is_b = q >= 3 * FBM * 2;
-    const int qq = is_b ? q - 3 * FBM * 2 : q;
-    const int d = qq / (FBM * 2);  // FBM == FBN
-    const int r = (qq >> 1) % FBM;
-    const int h = qq & 1;
-    int64_t gr = (is_b ? col0 : row0) + r;
+  for (int q = 0; q < kFRegionsPerWave; ++q) {
+    const int g = wave + 8 * q;
+    const bool is_b = g >= 12;
+    const int gg = is_b ? g - 12 : g;
+    const int d = gg >> 2;
+    const int row = 32 * (gg & 3) + (lane >> 1);
+    const int half = (lane & 1) ^ ((row >> 3) & 1);
+    int64_t gr = (is_b ? col0 : row0) + row;
     const int64_t last = (is_b ? n : m) - 1;
     gr = gr < last ? gr : last;
-    gsrc[s] = (is_b ? pb + d * stride_b : pa + d * stride_a) + gr * ldpb + 16 * h;
-    ldst[s] = (is_b ? 3 * kPlaneA + d * kPlaneB : d * kPlaneA) + fswz(r, h);
+    src[q] = (is_b ? pb + d * stride_b : pa + d * stride_a) + gr * ldpb + 16 * half;
   }
+  const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(lds_address(lds) + wave * 1024);
+  const int64_t nk = ldpb / FROW;
+  auto issue_one = [&](int q, int64_t t) {  // region q of step t (clamped to the last)
+    const int64_t tc = t < nk ? t : nk - 1;
+    dma16(src[q] + tc * FROW, wave_lds + (uint32_t)(t % kFStages) * kStage + q * 8192);
+  };
 
   v16f acc[2][5];
 #pragma unroll
@@ -233,44 +266,62 @@ __global__ __launch_bounds__(kFThreads, 1) void fp4_gemm_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][w][v] = 0.0f;
 
-  v4i reg[3];
-  const int64_t nk = ldpb / FROW;
-  auto load_global = [&](int64_t t) {
-#pragma unroll
-    for (int s = 0; s < 3; ++s) reg[s] = *reinterpret_cast<const v4i*>(gsrc[s] + t * FROW);
-  };
-  auto store_lds = [&](int buf) {
-#pragma unroll
-    for (int s = 0; s < 3; ++s) *reinterpret_cast<v4i*>(lds + buf * kStage + ldst[s]) = reg[s];
-  };
+  // Fragments: lane (row = lane & 31, half = lane >> 5) of a 32-row block; 16 bytes =
+  // 32 codes at K offset 32 * half within the step, the same map for A and B.
   const int frow = lane & 31, fhalf = lane >> 5;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-  for (int64_t t = 0; t < nk; ++t) {
-    const int buf = (int)(t & 1);
-    if (t + 1 < nk) load_global(t + 1);
-    const uint8_t* base = lds + buf * kStage;
-    v4i fa[2][3], fb[3];
+  auto read_a = [&](v4i& x, int64_t t, int i, int d) {
+    x = *reinterpret_cast<const v4i*>(lds + (t % kFStages) * kStage + d * kPlaneA +
+                                      fswz(wr * 64 + i * 32 + frow, fhalf));
+  };
+  auto read_b = [&](v4i& x, int64_t t, int d) {
+    x = *reinterpret_cast<const v4i*>(lds + (t % kFStages) * kStage + 3 * kPlaneA +
+                                      d * kPlaneB + fswz(wc * 32 + frow, fhalf));
+  };
+
+  v4i fa0[3], fa1[3], fb[2][3];
 #pragma unroll
-    for (int d = 0; d < 3; ++d) {
+  for (int q = 0; q < kFRegionsPerWave; ++q) issue_one(q, 0);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fa[i][d] = *reinterpret_cast<const v4i*>(base + d * kPlaneA +
-                                                 fswz(wr * 64 + i * 32 + frow, fhalf));
-      fb[d] = *reinterpret_cast<const v4i*>(base + 3 * kPlaneA + d * kPlaneB +
-                                            fswz(wc * 32 + frow, fhalf));
-    }
+  for (int q = 0; q < kFRegionsPerWave; ++q) issue_one(q, 1);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+  for (int q = 0; q < kFRegionsPerWave; ++q) issue_one(q, 2);
+  asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
 #pragma unroll
-      for (int da = 0; da < 3; ++da)
-#pragma unroll
-        for (int db = 0; db < 3; ++db)
-          acc[i][da + db] = mfma_fp4(fa[i][da], fb[db], acc[i][da + db]);
-    if (t + 1 < nk) store_lds(buf ^ 1);
-    __syncthreads();
+  for (int d = 0; d < 3; ++d) {
+    read_a(fa0[d], 0, 0, d);
+    read_b(fb[0][d], 0, d);
   }
+  for (int64_t t = 0; t < nk; ++t) {
+    const int cb = (int)(t & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // Half 0: row block 0; reads of row block 1's A fragments after MFMAs 0, 3, 6.
+#pragma unroll
+    for (int idx = 0; idx < 9; ++idx) {
+      const int da = idx / 3, db = idx % 3;
+      acc[0][da + db] = mfma_fp4(fa0[da], fb[cb][db], acc[0][da + db]);
+      if (idx % 3 == 0) read_a(fa1[idx / 3], t, 1, idx / 3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // Half 1: row block 1; loads of step t+3 after MFMAs 0..2, reads of step t+1's row
+    // block 0 and B fragments after MFMAs 3..8.
+#pragma unroll
+    for (int idx = 0; idx < 9; ++idx) {
+      const int da = idx / 3, db = idx % 3;
+      acc[1][da + db] = mfma_fp4(fa1[da], fb[cb][db], acc[1][da + db]);
+      if (idx < 3)
+        issue_one(idx, t + 3);
+      else if (idx < 6)
+        read_a(fa0[idx - 3], t + 1, 0, idx - 3);
+      else
+        read_b(fb[cb ^ 1][idx - 6], t + 1, idx - 6);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   const int64_t col = col0 + wc * 32 + (lane & 31);
   if (col >= n) return;
@@ -322,7 +373,7 @@ int launch_fp4_gemm(int64_t m, int64_t n, int64_t ldpb, const uint8_t* pa, int64
   const int64_t tiles_m = (m + FBM - 1) / FBM, tiles_n = (n + FBN - 1) / FBN;
   if (tiles_m * tiles_n > 0x7fffffff) return OZK_EUNSUPPORTED;
   hipLaunchKernelGGL(fp4_gemm_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kFThreads), 0, s,
-                     m, n, ldpb, pa, stride_a, pb, stride_b, c, ldc, (int)tiles_n);
+                     m, n, ldpb, pa, stride_a, pb, stride_b, c, ldc, (int)tiles_m, (int)tiles_n);
   return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
 }
 

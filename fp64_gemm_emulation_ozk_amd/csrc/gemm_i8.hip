@@ -22,6 +22,7 @@
 // through LDS so that global stores are 16-byte and coalesced.
 #include <type_traits>
 
+#include "lds_dma.h"
 #include "ozk_internal.h"
 
 namespace ozk {
@@ -66,20 +67,6 @@ __device__ __forceinline__ uint32_t pack4b(uint32_t b0, uint32_t b1, uint32_t b2
   const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
   const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-}
-
-// Direct global -> LDS load of 16 bytes per lane (gfx950 global_load_lds_dwordx4): lane i
-// of the wave writes LDS bytes [lds_base + 16 i, +16).  Issued through inline assembly so
-// the compiler neither reorders it nor inserts conservative waits; completion is tracked
-// explicitly with s_waitcnt vmcnt and made visible to the other waves with s_barrier.
-__device__ __forceinline__ void dma16(const int8_t* g, uint32_t lds_base) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(g), "s"(lds_base)
-      : "memory", "m0");
 }
 
 constexpr int kStages = 4;
@@ -134,7 +121,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     gr = gr < last ? gr : last;
     src[q] = (is_b ? B : A) + gr * kp + 16 * chunk;
   }
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int8_t*)lds;
+  const uint32_t lds0 = lds_address(lds);
   const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(lds0 + wave * 1024);
   const int64_t nk = kp / BK;
   auto issue_tile = [&](int64_t t) {  // tile t (clamped to the last) into stage t % kStages
