@@ -193,7 +193,8 @@ __global__ __launch_bounds__(64) void limb_products_kernel(
 //   wait for this wave's loads of step t+1, barrier (step t+1 complete from all waves,
 //   every wave past its reads of step t-1);
 //   half 1: the 9 products of row block 1, with the loads of step t+3 (into the stage of
-//   step t-1) and the reads of step t+1's row block 0 and B fragments between the MFMAs.
+//   step t-1) and the reads of step t+1's row block 0 and B fragments between the MFMAs
+//   (for kFStages = 4; in general the loads run kFStages - 1 steps ahead).
 // Workgroups are dealt out XCD by XCD onto contiguous runs of tiles grouped by 4 tile
 // rows, so the tiles in flight on one XCD share A rows and B columns in its L2.
 constexpr int FBM = 128, FBN = 128, FROW = 32;  // bytes per row per plane per K step
@@ -280,12 +281,11 @@ __global__ __launch_bounds__(kFThreads, 1) void fp4_gemm_kernel(
 
   v4i fa0[3], fa1[3], fb[2][3];
 #pragma unroll
-  for (int q = 0; q < kFRegionsPerWave; ++q) issue_one(q, 0);
+  for (int t = 0; t < kFStages - 1; ++t)
 #pragma unroll
-  for (int q = 0; q < kFRegionsPerWave; ++q) issue_one(q, 1);
-#pragma unroll
-  for (int q = 0; q < kFRegionsPerWave; ++q) issue_one(q, 2);
-  asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    for (int q = 0; q < kFRegionsPerWave; ++q) issue_one(q, t);
+  // Step 0 complete: the loads of steps 1 .. kFStages - 2 may still be in flight.
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kFRegionsPerWave * (kFStages - 2)) : "memory");
   __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int d = 0; d < 3; ++d) {
@@ -303,7 +303,8 @@ __global__ __launch_bounds__(kFThreads, 1) void fp4_gemm_kernel(
       if (idx % 3 == 0) read_a(fa1[idx / 3], t, 1, idx / 3);
       __builtin_amdgcn_sched_barrier(0);
     }
-    asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    // Step t+1 complete: the loads of steps t+2 .. t+kFStages-2 may still be in flight.
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kFRegionsPerWave * (kFStages - 3)) : "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     // Half 1: row block 1; loads of step t+3 after MFMAs 0..2, reads of step t+1's row
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(kFThreads, 1) void fp4_gemm_kernel(
       const int da = idx / 3, db = idx % 3;
       acc[1][da + db] = mfma_fp4(fa1[da], fb[cb][db], acc[1][da + db]);
       if (idx < 3)
-        issue_one(idx, t + 3);
+        issue_one(idx, t + kFStages - 1);
       else if (idx < 6)
         read_a(fa0[idx - 3], t + 1, 0, idx - 3);
       else
