@@ -6,11 +6,16 @@
 // transposed by the deconstruction), kp a multiple of 64 and zero-padded, so the K loop
 // has no tail.  |residue| <= 128 and kp <= 131072 keep every int32 sum exact.
 //
-// Tiling: workgroup tile 256 x 256 x 64, 256 threads = 4 waves, each wave a 128 x 128
-// block of 4 x 4 MFMA tiles of 32 x 32 (256 accumulator registers, held in AGPRs), so
-// every 16-byte LDS fragment read feeds four MFMAs.  Global tiles are loaded straight
-// into a 4-stage LDS ring (128 KiB) by global_load_lds_dwordx4, three K tiles ahead, with
-// one barrier per K tile placed between the two MFMA sub-steps (see the pipeline below).
+// Tiling: workgroup tile 256 x 256 x 64, 512 threads = 8 waves, two per SIMD.  Waves
+// 0..3 (group 0) own rows 0..127 of the tile, waves 4..7 (group 1) rows 128..255; each
+// wave a 128 x 64 block of 4 x 2 MFMA tiles of 32 x 32 (128 accumulator registers).
+// The two groups run out of phase ("ping-pong"): while one group issues its 16 MFMAs of
+// a K step (and its share of the global loads), the other reads its fragments of the next
+// K step from LDS, so each SIMD's matrix unit always has one wave that does not wait on
+// memory.  Phases are separated by workgroup barriers; group 1 starts one phase late.
+// Global tiles go straight into a 5-deep LDS ring (32 KiB per K step) by
+// global_load_lds_dwordx4, 4 K steps ahead, issued between the MFMAs of compute phases
+// from a wave-uniform SGPR base plus a fixed per-lane offset.
 // LDS rows are 64 bytes with the four 16-byte chunks XOR-swizzled by (row >> 2) & 3, so
 // the 16 lanes of a fragment read (16 consecutive rows, one chunk each) cover all 64
 // banks.  Workgroups are mapped XCD by XCD (the hardware deals them out round-robin over
@@ -19,7 +24,7 @@
 //
 // Epilogues: the int32 products themselves, or their symmetric residues modulo m_l as
 // int8 (what the CRT reconstruction consumes: 1 byte instead of 4 per output), staged
-// through LDS so that global stores are 16-byte and coalesced.
+// through LDS as one 256 x 256 byte tile so that every global store writes 256-byte rows.
 #include <type_traits>
 
 #include "lds_dma.h"
@@ -34,7 +39,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kGroupM = 4;
 constexpr int kXcds = 8;
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kLdsA = BM * BK;   // bytes per stage
 constexpr int kLdsB = BN * BK;
 
@@ -69,10 +74,26 @@ __device__ __forceinline__ uint32_t pack4b(uint32_t b0, uint32_t b1, uint32_t b2
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
-constexpr int kStages = 4;
-constexpr int kStageBytes = kLdsA + kLdsB;  // 32 KiB: A rows 0..255 then B rows 0..255
-constexpr int kRegions = kStageBytes / 1024;  // 1 KiB regions, one per wave instruction
-constexpr int kRegionsPerWave = kRegions / 4;
+// Workgroup barrier that is also a compiler barrier for memory operations, so that no
+// LDS access is moved across it.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+constexpr int kStages = 5;                    // LDS ring of K steps: 160 KiB
+constexpr int kStageBytes = kLdsA + kLdsB;    // 32 KiB: A rows 0..255 then B rows 0..255
+constexpr int kWaves = kThreads / 64;
+constexpr int kRegionsPerWave = kStageBytes / 1024 / kWaves;  // 1 KiB per load instruction
+// Loads younger than the last load of step t + 1 when a wave waits for it: group 0 waits
+// after its compute phase of step t (steps t+2 .. t+kStages-1 issued), group 1 after its
+// memory phase of step t (steps t+2 .. t+kStages-2 issued).
+constexpr int kPending0 = kRegionsPerWave * (kStages - 2);
+constexpr int kPending1 = kRegionsPerWave * (kStages - 3);
+static_assert(kRegionsPerWave == 4, "one load per wave after every fourth MFMA");
+constexpr int kOutPitch = BN + 8;  // residue staging: 2 rows apart = 1 bank apart (dwords)
+static_assert(BM * kOutPitch <= kStages * kStageBytes, "residue staging must fit the ring");
 
 template <int kEpi>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
@@ -103,39 +124,51 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wr = wave >> 1;   // 0..1: rows wr*128
-  const int wc = wave & 1;    // 0..1: cols wc*128
+  // rows grp*128 of the tile; also the phase offset (wave-uniform, held in an SGPR so that
+  // the branches around barriers are scalar branches)
+  const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
+  const int wq = __builtin_amdgcn_readfirstlane(wave & 3);  // columns wq*64 (uniform)
 
-  // Direct-load sources: wave w fills regions w, w+4, ...; region rg holds 16 rows of A
-  // (rg < 16) or B, 64 bytes each; lane i lands at row 16*(rg%16) + i/4, physical chunk
-  // i%4, which holds logical K chunk (i%4) ^ ((row >> 2) & 3) (the read-side swizzle).
-  const int8_t* src[kRegionsPerWave];
+  // Direct-load sources: wave w fills regions w, w+8, w+16, w+24 of a stage; region rg
+  // holds 16 rows of A (rg < 16) or B, 64 bytes each; lane i lands at row 16*(rg%16) + i/4,
+  // physical chunk i%4, which holds logical K chunk (i%4) ^ ((row >> 2) & 3) (the
+  // read-side swizzle).
+  // Sources are addressed as a wave-uniform base (tile origin of A or B plus the K offset,
+  // in SGPRs) plus a fixed 32-bit lane offset (row within the tile, clamped to the last
+  // row of the matrix, times kp, plus the chunk); regions 0..15 are A, 16..31 B.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint64_t sbase_a = (uint64_t)(A + row0 * kp), sbase_b = (uint64_t)(B + col0 * kp);
+  uint32_t voff[kRegionsPerWave];
 #pragma unroll
   for (int q = 0; q < kRegionsPerWave; ++q) {
-    const int rg = wave + 4 * q;
+    const int rg = wave + kWaves * q;
     const bool is_b = rg >= 16;
     const int row = 16 * (rg & 15) + (lane >> 2);
     const int chunk = (lane & 3) ^ ((row >> 2) & 3);
-    int64_t gr = (is_b ? col0 : row0) + row;
+    const int64_t origin = is_b ? col0 : row0;
     const int64_t last = (is_b ? n : m) - 1;
-    gr = gr < last ? gr : last;
-    src[q] = (is_b ? B : A) + gr * kp + 16 * chunk;
+    const int64_t gr = origin + row < last ? origin + row : last;
+    voff[q] = (uint32_t)((gr - origin) * kp + 16 * chunk);
   }
+  auto region_base = [&](int q) {  // uniform: region wave + 8q is B iff q >= 2
+    return wave_u + kWaves * q >= 16 ? sbase_b : sbase_a;
+  };
   const uint32_t lds0 = lds_address(lds);
   const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(lds0 + wave * 1024);
-  const int64_t nk = kp / BK;
-  auto issue_tile = [&](int64_t t) {  // tile t (clamped to the last) into stage t % kStages
-    const int64_t tc = t < nk ? t : nk - 1;
+  const int nk = (int)(kp / BK);
+  auto issue_step = [&](int t) {  // K step t (clamped to the last) into stage t % kStages
+    const int tc = t < nk ? t : nk - 1;
     const uint32_t base = wave_lds + (uint32_t)(t % kStages) * kStageBytes;
 #pragma unroll
-    for (int q = 0; q < kRegionsPerWave; ++q) dma16(src[q] + tc * BK, base + q * 4096);
+    for (int q = 0; q < kRegionsPerWave; ++q)
+      dma16_sbase(voff[q], region_base(q) + (uint64_t)tc * BK, base + q * (kWaves * 1024));
   };
 
-  v16i acc[4][4];
+  v16i acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
 
@@ -144,68 +177,65 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
   // independent of how the instruction orders K internally.
   const int frow = lane & 31;
   const int fchunk = lane >> 5;
-  v4i fa[2][4], fb[2][4];
-  auto read_frags = [&](v4i (&xa)[4], v4i (&xb)[4], int64_t t, int kk) {
-    const int8_t* la = lds + (t % kStages) * kStageBytes;
-    const int8_t* lb = la + kLdsA;
+  int offa[4], offb[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      xa[i] = *reinterpret_cast<const v4i*>(la + swz(wr * 128 + i * 32 + frow, kk * 2 + fchunk));
+  for (int i = 0; i < 4; ++i) offa[i] = (grp * 128 + i * 32 + frow) * BK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      xb[j] = *reinterpret_cast<const v4i*>(lb + swz(wc * 128 + j * 32 + frow, kk * 2 + fchunk));
-  };
+  for (int j = 0; j < 2; ++j) offb[j] = kLdsA + (wq * 64 + j * 32 + frow) * BK;
+  const int sw = (frow >> 2) & 3;  // row swizzle (the same for every block: 32 | block rows)
+  v4i fa[2][4], fb[2][2];
 
-  // One fragment read (idx 0..3: A blocks, 4..7: B blocks) of K half kk of tile t.
-  auto frag_read = [&](v4i (&xa)[4], v4i (&xb)[4], int64_t t, int kk, int idx) {
-    const int8_t* la = lds + (t % kStages) * kStageBytes;
-    if (idx < 4)
-      xa[idx] = *reinterpret_cast<const v4i*>(la + swz(wr * 128 + idx * 32 + frow, kk * 2 + fchunk));
-    else
-      xb[idx - 4] = *reinterpret_cast<const v4i*>(
-          la + kLdsA + swz(wc * 128 + (idx - 4) * 32 + frow, kk * 2 + fchunk));
-  };
-
-  // Pipeline: tiles t+1 .. t+3 are in flight while tile t is multiplied.
-  //   sub-step 0 of tile t: 16 MFMAs on fragments (t, 0), one read of fragments (t, 1)
-  //   after every other MFMA;
-  //   wait for this wave's loads of tile t+1, barrier (tile t+1 complete from all waves;
-  //   every wave is past its reads of tile t-1);
-  //   sub-step 1 of tile t: 16 MFMAs on (t, 1), alternately followed by one load of tile
-  //   t+3 (into the stage of tile t-1) and one read of fragments (t+1, 0).
-  // Every MFMA is followed by at most one memory instruction (pinned by scheduling
-  // barriers), so the issue of loads and LDS reads hides behind the matrix pipe.
-  issue_tile(0);
-  issue_tile(1);
-  issue_tile(2);
-  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  read_frags(fa[0], fb[0], 0, 0);
-  for (int64_t t = 0; t < nk; ++t) {
-    __builtin_amdgcn_sched_barrier(0);
+  // Phase schedule (one barrier between phases; group 1 runs one phase behind group 0):
+  //   memory phase of step t: read the 12 fragments of step t;
+  //   compute phase of step t: the 16 MFMAs of step t, and this wave's 4 loads of step
+  //   t + kStages - 1 into the stage of step t - 1 (read by both groups in earlier phases;
+  //   every wave waited for its reads before the barrier that ended them), one after each
+  //   fourth MFMA.  Issued from the memory phase instead, four waves issuing together
+  //   stall about 70 cycles per load and the memory phase becomes the critical path.
+  // Both groups wait for their own loads of step t + 1 before the barrier that ends
+  // phase 2t + 1 (group 0: end of its compute phase; group 1: end of its memory phase), so
+  // step t + 1 is complete in LDS before group 0 reads it in phase 2t + 2.
 #pragma unroll
-    for (int idx = 0; idx < 16; ++idx) {
-      const int i = idx >> 2, j = idx & 3;
-      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[0][j], fa[0][i], acc[i][j], 0, 0, 0);
-      if ((idx & 1) == 0) frag_read(fa[1], fb[1], t, 1, idx >> 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
+  for (int t = 0; t < kStages - 1; ++t) issue_step(t);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRegionsPerWave * (kStages - 2)) : "memory");
+  wg_barrier();
+  if (grp == 1) wg_barrier();
+  for (int t = 0; t < nk; ++t) {
     __builtin_amdgcn_sched_barrier(0);
-    const int64_t tl = t + 3 < nk ? t + 3 : nk - 1;   // past the end: reload the last tile
-    const uint32_t base = wave_lds + (uint32_t)((t + 3) % kStages) * kStageBytes;
+    const int8_t* st = lds + (t % kStages) * kStageBytes;
 #pragma unroll
-    for (int idx = 0; idx < 16; ++idx) {
-      const int i = idx >> 2, j = idx & 3;
-      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[1][j], fa[1][i], acc[i][j], 0, 0, 0);
-      if ((idx & 1) == 0)
-        dma16(src[idx >> 1] + tl * BK, base + (idx >> 1) * 4096);
-      else
-        frag_read(fa[0], fb[0], t + 1, 0, idx >> 1);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = ((kk * 2 + fchunk) ^ sw) << 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[kk][i] = *reinterpret_cast<const v4i*>(st + offa[i] + c);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fb[kk][j] = *reinterpret_cast<const v4i*>(st + offb[j] + c);
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (grp == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPending1) : "memory");
+    wg_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const int tl = t + kStages - 1;
+    const int64_t koff = (int64_t)(tl < nk ? tl : nk - 1) * BK;
+    const uint32_t lbase = wave_lds + (uint32_t)(tl % kStages) * kStageBytes;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[kk][j], fa[kk][i], acc[i][j], 0, 0, 0);
+          const int idx = kk * 8 + i * 2 + j;
+          if ((idx & 3) == 0)
+            dma16_sbase(voff[idx >> 2], region_base(idx >> 2) + (uint64_t)koff,
+                        lbase + (idx >> 2) * (kWaves * 1024));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    if (grp == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPending0) : "memory");
+    wg_barrier();
   }
+  if (grp == 0) wg_barrier();
+  // The clamped loads past the last K step are still landing in the ring.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // The MFMA runs with the B fragment as its first operand, so each accumulator tile is
@@ -213,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
   // 8*(v/4) + 4*(lane/32) + (v%4); registers 4q..4q+3 hold 4 consecutive columns.
   const int mod = E.mod[l];
   const double inv = E.inv[l];
-  const int64_t wrow0 = row0 + wr * 128, wcol0 = col0 + wc * 128;
+  const int64_t wrow0 = row0 + grp * 128, wcol0 = col0 + wq * 64;
   if (kEpi == kEpiProducts) {
     int32_t* o = reinterpret_cast<int32_t*>(out) + l * stride_o;
 #pragma unroll
@@ -221,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
       const int64_t row = wrow0 + i * 32 + (lane & 31);
       if (row >= m) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int64_t col = wcol0 + j * 32 + 8 * q + 4 * (lane >> 5);
@@ -238,26 +268,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     }
     return;
   }
-  // Residues: stage the wave's 128 x 128 byte tile in LDS (row pitch 136: the dword writes
-  // of 64 lanes and the 8-byte reads of each 16-lane group hit distinct banks), then store
-  // rows with 16-byte coalesced writes (8 lanes per 128-byte row segment).
-  constexpr int kPitch = 136;
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();  // every wave is past its last read of the LDS ring
-  int8_t* tile = lds + wave * (128 * kPitch);
+  // Residues: stage the 256 x 256 byte tile in LDS (row pitch 264: the dword writes of
+  // 64 lanes hit distinct banks), then each wave stores 32 rows, 16 lanes x 16 bytes per
+  // 256-byte row.
+  wg_barrier();  // every wave is past its reads and loads of the ring
+  int8_t* tile = lds;
   // m = 256 keeps the low byte of the product; odd moduli reduce (uniform branch, taken
   // once per tile rather than per element).
   auto stage = [&](auto byte_of) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t w = pack4b(byte_of(acc[i][j][4 * q]), byte_of(acc[i][j][4 * q + 1]),
                                     byte_of(acc[i][j][4 * q + 2]), byte_of(acc[i][j][4 * q + 3]));
-          *reinterpret_cast<uint32_t*>(tile + (i * 32 + (lane & 31)) * kPitch + j * 32 + 8 * q +
-                                       4 * (lane >> 5)) = w;
+          *reinterpret_cast<uint32_t*>(tile + (grp * 128 + i * 32 + (lane & 31)) * kOutPitch +
+                                       wq * 64 + j * 32 + 8 * q + 4 * (lane >> 5)) = w;
         }
   };
   if (mod == 256) {
@@ -266,13 +294,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     const uint32_t um = (uint32_t)mod;
     stage([=](int v) { return residue_byte_odd(v, um, inv); });
   }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave reads back only its own tile
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  wg_barrier();  // the whole tile is staged
   int8_t* o = reinterpret_cast<int8_t*>(out) + l * stride_o;
 #pragma unroll 4
-  for (int s8 = 0; s8 < 16; ++s8) {
-    const int rl = s8 * 8 + (lane >> 3), cl = 16 * (lane & 7);
-    const int64_t row = wrow0 + rl, col = wcol0 + cl;
-    const int8_t* srcp = tile + rl * kPitch + cl;
+  for (int s4 = 0; s4 < 8; ++s4) {
+    const int rl = wave * 32 + s4 * 4 + (lane >> 4), cl = 16 * (lane & 15);
+    const int64_t row = row0 + rl, col = col0 + cl;
+    const int8_t* srcp = tile + rl * kOutPitch + cl;
     const uint2 lo = *reinterpret_cast<const uint2*>(srcp);
     const uint2 hi = *reinterpret_cast<const uint2*>(srcp + 8);
     if (row >= m) continue;

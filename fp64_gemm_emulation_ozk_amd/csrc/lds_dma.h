@@ -21,6 +21,18 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
       : "memory", "m0");
 }
 
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset
+// (global address = base + offset): advancing the source only takes scalar adds.
+__device__ __forceinline__ void dma16_sbase(uint32_t voffset, uint64_t sbase, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voffset), "s"(sbase), "s"(lds_base)
+      : "memory", "m0");
+}
+
 // Byte address of a __shared__ object in the LDS aperture.
 template <typename T>
 __device__ __forceinline__ uint32_t lds_address(T* p) {
