@@ -349,7 +349,7 @@ int ozk_fp4limb_products(int64_t m, int64_t n, int64_t ldp_bytes, const uint8_t*
 int ozk_int8gemm_fp4limb_workspace_size(int64_t m, int64_t n, int64_t k, size_t* bytes) {
   if (!bytes || m < 0 || n < 0 || k < 1) return OZK_EINVAL;
   if (k > OZK_MAX_K) return OZK_ERANGE;
-  const int64_t ldpb = round_up(k, kPlaneK) / 2;
+  const int64_t ldpb = round_up(k, 2 * kPlaneK) / 2;  // K steps of 128 codes
   *bytes = align256((size_t)3 * m * ldpb) + align256((size_t)3 * n * ldpb);
   return OZK_OK;
 }
@@ -366,7 +366,7 @@ int ozk_int8gemm_fp4limb(int64_t m, int64_t n, int64_t k, const int8_t* A, int64
   ozk_int8gemm_fp4limb_workspace_size(m, n, k, &need);
   if (!workspace || workspace_bytes < need) return OZK_EWORKSPACE;
   if (!aligned(workspace, 256)) return OZK_EINVAL;
-  const int64_t ldpb = round_up(k, kPlaneK) / 2;
+  const int64_t ldpb = round_up(k, 2 * kPlaneK) / 2;  // K steps of 128 codes
   Carver cv(workspace);
   uint8_t* pa = static_cast<uint8_t*>(cv.take((size_t)3 * m * ldpb));
   uint8_t* pb = static_cast<uint8_t*>(cv.take((size_t)3 * n * ldpb));

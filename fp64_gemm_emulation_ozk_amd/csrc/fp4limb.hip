@@ -182,35 +182,34 @@ __global__ __launch_bounds__(64) void limb_products_kernel(
 }
 
 // ------------------------------------------------------------------ fused weighted GEMM
-// Workgroup tile 128 x 128, K step 64 (32 bytes per row per digit plane), 512 threads =
-// 8 waves in 2 x 4, each wave 64 x 32 = 2 MFMA blocks x 5 weight classes (160 AGPRs).
-// The three digit planes of A and of B (24 KiB per K step) are loaded straight into a
-// 4-stage LDS ring by global_load_lds_dwordx4, three K steps ahead; LDS rows are 32 bytes
-// with the two 16-byte halves swapped on rows with bit 3 set (the swap is applied on the
-// load side), so the 16 lanes of a fragment read hit distinct banks.  Each K step runs
-// in two halves around one barrier:
-//   half 0: the 9 digit products of row block 0, reading row block 1's A fragments;
-//   wait for this wave's loads of step t+1, barrier (step t+1 complete from all waves,
-//   every wave past its reads of step t-1);
-//   half 1: the 9 products of row block 1, with the loads of step t+3 (into the stage of
-//   step t-1) and the reads of step t+1's row block 0 and B fragments between the MFMAs
-//   (for kFStages = 4; in general the loads run kFStages - 1 steps ahead).
-// Workgroups are dealt out XCD by XCD onto contiguous runs of tiles grouped by 4 tile
-// rows, so the tiles in flight on one XCD share A rows and B columns in its L2.
-constexpr int FBM = 128, FBN = 128, FROW = 32;  // bytes per row per plane per K step
+// Workgroup tile 128 x 128, K step 128 codes (64 bytes per row per digit plane), 512
+// threads = 8 waves in 2 x 4, each wave 64 x 32 = 2 MFMA row blocks x 5 weight classes
+// (160 accumulator registers).  The three digit planes of A and of B (48 KiB per K step)
+// are loaded straight into a 3-stage LDS ring by global_load_lds_dwordx4, two K steps
+// ahead; every load instruction covers 16 rows x 64 bytes (16 lines, where 32-byte row
+// pieces would touch 32 lines for the same kilobyte).  LDS rows are 64 bytes with the
+// four 16-byte chunks XOR-swizzled by (row >> 2) & 3, so the 16 lanes of a fragment read
+// cover all 64 banks.  A K step runs as four quarters of 9 MFMAs, (kk, row block) =
+// (0,0), (0,1), (1,0), (1,1), each reading the fragments of the next quarter between its
+// MFMAs; one barrier per step sits between quarters 1 and 2 and follows a wait for all of
+// this wave's loads (those of step t+1).  After it the loads of step t+2 (into the stage
+// of step t-1, whose last reads were in quarter 2 of step t-1; past the last step the last
+// step is loaded again) are issued between the MFMAs of quarter 2, from wave-uniform SGPR
+// bases plus a fixed lane offset; quarter 3 reads step t+1's first fragments.  Workgroups are dealt out XCD by XCD onto
+// contiguous runs of tiles grouped by 4 tile rows, so the tiles in flight on one XCD share
+// A rows and B columns in its L2.
+constexpr int FBM = 128, FBN = 128, FROW = 64;  // bytes per row per plane per K step
 constexpr int kFThreads = 512;
-constexpr int kPlaneA = FBM * FROW, kPlaneB = FBN * FROW;
-constexpr int kStage = 3 * (kPlaneA + kPlaneB);  // 24 KiB
-constexpr int kFStages = 4;
-constexpr int kFRegions = kStage / 1024;         // 1 KiB per wave load instruction
-constexpr int kFRegionsPerWave = kFRegions / 8;  // 3
+constexpr int kFPlane = 128 * FROW;              // 8 KiB: one digit plane of A or B
+constexpr int kStage = 6 * kFPlane;              // 48 KiB: A planes 0..2, then B planes
+constexpr int kFStages = 3;
 constexpr int kFGroupM = 4;
 constexpr int kFXcds = 8;
 
-// 16 lanes read rows r..r+15 at the same half; rows 8 apart share banks without the XOR
-// (gfx950 LDS: 64 four-byte banks, 16 lanes of 16 bytes per clock).
-__device__ __forceinline__ int fswz(int row, int half) {
-  return row * FROW + ((half ^ ((row >> 3) & 1)) << 4);
+// 16 lanes read rows r..r+15 at one logical chunk; rows with equal (row mod 4) share
+// banks without the XOR (gfx950 LDS: 64 four-byte banks, 16 lanes of 16 bytes per clock).
+__device__ __forceinline__ int fswz(int row, int chunk) {
+  return row * FROW + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
 
 __global__ __launch_bounds__(kFThreads, 1) void fp4_gemm_kernel(
@@ -234,29 +233,28 @@ __global__ __launch_bounds__(kFThreads, 1) void fp4_gemm_kernel(
   const int wr = wave >> 2;  // 0..1: rows wr*64
   const int wc = wave & 3;   // 0..3: cols wc*32
 
-  // Direct-load sources: wave w fills regions w, w + 8, w + 16 of a stage; region g holds
-  // 32 rows of one plane (g < 12: A planes g / 4, else B planes (g - 12) / 4); lane i
-  // lands at row 32 (g % 4) + i / 2, physical half i % 2, which holds logical half
-  // (i % 2) ^ ((row >> 3) & 1).
-  const uint8_t* src[kFRegionsPerWave];
-#pragma unroll
-  for (int q = 0; q < kFRegionsPerWave; ++q) {
-    const int g = wave + 8 * q;
-    const bool is_b = g >= 12;
-    const int gg = is_b ? g - 12 : g;
-    const int d = gg >> 2;
-    const int row = 32 * (gg & 3) + (lane >> 1);
-    const int half = (lane & 1) ^ ((row >> 3) & 1);
-    int64_t gr = (is_b ? col0 : row0) + row;
-    const int64_t last = (is_b ? n : m) - 1;
-    gr = gr < last ? gr : last;
-    src[q] = (is_b ? pb + d * stride_b : pa + d * stride_a) + gr * ldpb + 16 * half;
-  }
+  // Direct loads: load q (0..5) of a wave fills rows 16*wave .. +15 of plane q (q < 3: A
+  // digit q, else B digit q - 3); lane i lands at row 16*wave + i/4, physical chunk i%4,
+  // which holds logical chunk (i%4) ^ ((row >> 2) & 3).  Rows past the matrix edge read
+  // its last row.
+  const int lrow = 16 * wave + (lane >> 2);
+  const int lchunk = (lane & 3) ^ ((lrow >> 2) & 3);
+  const int64_t ra = row0 + lrow < m - 1 ? row0 + lrow : m - 1;
+  const int64_t rb = col0 + lrow < n - 1 ? col0 + lrow : n - 1;
+  const uint32_t voff_a = (uint32_t)((ra - row0) * ldpb + 16 * lchunk);
+  const uint32_t voff_b = (uint32_t)((rb - col0) * ldpb + 16 * lchunk);
+  const uint64_t base_a = (uint64_t)(pa + row0 * ldpb), base_b = (uint64_t)(pb + col0 * ldpb);
   const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(lds_address(lds) + wave * 1024);
-  const int64_t nk = ldpb / FROW;
-  auto issue_one = [&](int q, int64_t t) {  // region q of step t (clamped to the last)
-    const int64_t tc = t < nk ? t : nk - 1;
-    dma16(src[q] + tc * FROW, wave_lds + (uint32_t)(t % kFStages) * kStage + q * 8192);
+  const int nk = (int)(ldpb / FROW);
+  // Load q of K step tk into the stage of step ts (ts = tk except past the last step, where
+  // the last step is loaded again into the stage that step ts would use).
+  auto issue_one = [&](int q, int tk, int ts) {
+    const uint64_t kb = (uint64_t)tk * FROW;
+    const uint32_t dst = wave_lds + (uint32_t)(ts % kFStages) * kStage + q * kFPlane;
+    if (q < 3)
+      dma16_sbase(voff_a, base_a + (uint64_t)(q * stride_a) + kb, dst);
+    else
+      dma16_sbase(voff_b, base_b + (uint64_t)((q - 3) * stride_b) + kb, dst);
   };
 
   v16f acc[2][5];
@@ -268,57 +266,86 @@ __global__ __launch_bounds__(kFThreads, 1) void fp4_gemm_kernel(
       for (int v = 0; v < 16; ++v) acc[i][w][v] = 0.0f;
 
   // Fragments: lane (row = lane & 31, half = lane >> 5) of a 32-row block; 16 bytes =
-  // 32 codes at K offset 32 * half within the step, the same map for A and B.
+  // 32 codes at K offset 64 kk + 32 half within the step, the same map for A and B.
   const int frow = lane & 31, fhalf = lane >> 5;
-  auto read_a = [&](v4i& x, int64_t t, int i, int d) {
-    x = *reinterpret_cast<const v4i*>(lds + (t % kFStages) * kStage + d * kPlaneA +
-                                      fswz(wr * 64 + i * 32 + frow, fhalf));
+  auto read_a = [&](v4i& x, int t, int rbk, int d, int kk) {
+    x = *reinterpret_cast<const v4i*>(lds + (t % kFStages) * kStage + d * kFPlane +
+                                      fswz(wr * 64 + rbk * 32 + frow, 2 * kk + fhalf));
   };
-  auto read_b = [&](v4i& x, int64_t t, int d) {
-    x = *reinterpret_cast<const v4i*>(lds + (t % kFStages) * kStage + 3 * kPlaneA +
-                                      d * kPlaneB + fswz(wc * 32 + frow, fhalf));
+  auto read_b = [&](v4i& x, int t, int d, int kk) {
+    x = *reinterpret_cast<const v4i*>(lds + (t % kFStages) * kStage + (3 + d) * kFPlane +
+                                      fswz(wc * 32 + frow, 2 * kk + fhalf));
   };
 
-  v4i fa0[3], fa1[3], fb[2][3];
+  v4i fa[2][3], fb[2][3];
 #pragma unroll
-  for (int t = 0; t < kFStages - 1; ++t)
+  for (int q = 0; q < 6; ++q) issue_one(q, 0, 0);
+  if (nk > 1) {
 #pragma unroll
-    for (int q = 0; q < kFRegionsPerWave; ++q) issue_one(q, t);
-  // Step 0 complete: the loads of steps 1 .. kFStages - 2 may still be in flight.
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kFRegionsPerWave * (kFStages - 2)) : "memory");
+    for (int q = 0; q < 6; ++q) issue_one(q, 1, 1);
+    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");  // step 0 complete
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int d = 0; d < 3; ++d) {
-    read_a(fa0[d], 0, 0, d);
-    read_b(fb[0][d], 0, d);
+    read_a(fa[0][d], 0, 0, d, 0);
+    read_b(fb[0][d], 0, d, 0);
   }
-  for (int64_t t = 0; t < nk; ++t) {
-    const int cb = (int)(t & 1);
+  for (int t = 0; t < nk; ++t) {
     __builtin_amdgcn_sched_barrier(0);
-    // Half 0: row block 0; reads of row block 1's A fragments after MFMAs 0, 3, 6.
+    // Quarter 0 (kk 0, row block 0); reads A (kk 0, row block 1).
 #pragma unroll
     for (int idx = 0; idx < 9; ++idx) {
       const int da = idx / 3, db = idx % 3;
-      acc[0][da + db] = mfma_fp4(fa0[da], fb[cb][db], acc[0][da + db]);
-      if (idx % 3 == 0) read_a(fa1[idx / 3], t, 1, idx / 3);
+      acc[0][da + db] = mfma_fp4(fa[0][da], fb[0][db], acc[0][da + db]);
+      if (idx % 3 == 0) read_a(fa[1][idx / 3], t, 1, idx / 3, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // Step t+1 complete: the loads of steps t+2 .. t+kFStages-2 may still be in flight.
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kFRegionsPerWave * (kFStages - 3)) : "memory");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    // Half 1: row block 1; loads of step t+3 after MFMAs 0..2, reads of step t+1's row
-    // block 0 and B fragments after MFMAs 3..8.
+    // Quarter 1 (kk 0, row block 1); reads A (kk 1, row block 0) and B (kk 1).
 #pragma unroll
     for (int idx = 0; idx < 9; ++idx) {
       const int da = idx / 3, db = idx % 3;
-      acc[1][da + db] = mfma_fp4(fa1[da], fb[cb][db], acc[1][da + db]);
+      acc[1][da + db] = mfma_fp4(fa[1][da], fb[0][db], acc[1][da + db]);
       if (idx < 3)
-        issue_one(idx, t + kFStages - 1);
+        read_a(fa[0][idx], t, 0, idx, 1);
       else if (idx < 6)
-        read_a(fa0[idx - 3], t + 1, 0, idx - 3);
-      else
-        read_b(fb[cb ^ 1][idx - 6], t + 1, idx - 6);
+        read_b(fb[1][idx - 3], t, idx - 3, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Every load of this wave (those of step t+1) complete; after the barrier step t+1
+    // is complete in LDS and every wave is past its reads of step t-1.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const int tl = t + 2 < nk ? t + 2 : nk - 1;  // past the end: reload the last step
+    // Quarter 2 (kk 1, row block 0); reads A (kk 1, row block 1); the 6 loads of step t+2,
+    // after MFMAs 0, 1, 3, 4, 6, 7 (as early as the stage is free: the latency they must
+    // hide runs to the barrier of step t+1).
+#pragma unroll
+    for (int idx = 0; idx < 9; ++idx) {
+      const int da = idx / 3, db = idx % 3;
+      acc[0][da + db] = mfma_fp4(fa[0][da], fb[1][db], acc[0][da + db]);
+      if (idx % 3 == 0) {
+        read_a(fa[1][idx / 3], t, 1, idx / 3, 1);
+        issue_one(idx / 3, tl, t + 2);
+      } else if (idx % 3 == 1) {
+        issue_one(3 + idx / 3, tl, t + 2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Quarter 3 (kk 1, row block 1); reads step t+1's A (kk 0, row block 0) and B (kk 0).
+    const int tn1 = t + 1 < nk ? t + 1 : t;  // past the last step: harmless re-read
+#pragma unroll
+    for (int idx = 0; idx < 9; ++idx) {
+      const int da = idx / 3, db = idx % 3;
+      acc[1][da + db] = mfma_fp4(fa[1][da], fb[1][db], acc[1][da + db]);
+      if (idx % 3 == 0) {
+        read_a(fa[0][idx / 3], tn1, 0, idx / 3, 0);
+      } else if (idx % 3 == 1) {
+        read_b(fb[0][idx / 3], tn1, idx / 3, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -371,6 +398,8 @@ int launch_fp4_products(int64_t m, int64_t n, int64_t ldpb, const uint8_t* pa, i
 int launch_fp4_gemm(int64_t m, int64_t n, int64_t ldpb, const uint8_t* pa, int64_t stride_a,
                     const uint8_t* pb, int64_t stride_b, int32_t* c, int64_t ldc, hipStream_t s) {
   if (m <= 0 || n <= 0) return OZK_OK;
+  // K steps of 64 bytes per row; 32-bit lane offsets within a 128-row tile.
+  if (ldpb % FROW != 0 || ldpb <= 0 || 128 * ldpb >= (int64_t)1 << 31) return OZK_EINVAL;
   const int64_t tiles_m = (m + FBM - 1) / FBM, tiles_n = (n + FBN - 1) / FBN;
   if (tiles_m * tiles_n > 0x7fffffff) return OZK_EUNSUPPORTED;
   hipLaunchKernelGGL(fp4_gemm_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kFThreads), 0, s,
