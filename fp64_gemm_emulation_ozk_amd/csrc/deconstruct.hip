@@ -8,7 +8,8 @@
 //                       and Inf/NaN patterns sort above every finite value)
 //   residues_rows       8 consecutive K elements per thread -> 8 bytes per plane
 //   residues_cols       16 consecutive K elements of one column per thread -> 16 bytes
-//                       per plane (the transpose happens in the store address)
+//                       per plane, 8 threads per 128-byte plane line (the transpose
+//                       happens in the store address)
 //   residues_rows_fused one workgroup per row: the row is held in registers, reduced
 //                       for its maximum, then turned into residues (one HBM read)
 #include "ozk_internal.h"
@@ -147,19 +148,22 @@ __global__ __launch_bounds__(256) void residues_rows_kernel(
   store_residues<kWide, 8>(a, e == INT32_MIN ? 0 : e, K, dst, plane_stride);
 }
 
-// Column residues: grid (ceil(cols/64), ldp/64).  Lane t owns column j0 + (t >> 2) and
-// K rows h0 + 16*(t & 3) .. +15; four consecutive lanes store 64 contiguous bytes of
-// one plane row (16 bytes each), and each load instruction reads 4 rows x 16 columns.
+// Column residues: grid (ceil(cols/32), ceil(ldp/128)).  Lane t of wave w owns column
+// j0 + 8w + (t >> 3) and K rows h0 + 16*(t & 7) .. +15; the eight lanes of a column store
+// one whole 128-byte line of each plane row (16 bytes each), and each load instruction
+// reads 8 rows x 8 columns (the four waves of a block read the 32 columns of a row, so
+// every line is fetched once).
 template <bool kWide>
 __global__ __launch_bounds__(256) void residues_cols_kernel(
     const double* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, ResidueConsts K,
     int p_bits, const uint64_t* __restrict__ maxbits, int8_t* __restrict__ planes,
     int64_t ldp, int64_t plane_stride, int32_t* __restrict__ exps) {
-  const int64_t col = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+  const int64_t col = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
   if (col >= cols) return;
+  const int64_t h0 = (int64_t)blockIdx.y * 128 + (threadIdx.x & 7) * 16;
+  if (h0 >= ldp) return;  // ldp is a multiple of 64: the last block row may be half full
   const int e = line_exponent(maxbits[col], p_bits);
-  const int64_t h0 = (int64_t)blockIdx.y * 64 + (threadIdx.x & 3) * 16;
-  if (blockIdx.y == 0 && (threadIdx.x & 3) == 0) exps[col] = e;
+  if (blockIdx.y == 0 && (threadIdx.x & 7) == 0) exps[col] = e;
   double a[16];
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
@@ -284,7 +288,7 @@ int launch_residues(const double* x, int64_t rows, int64_t cols, int64_t ldx, in
 #undef OZK_ROWS
   } else {
     if (cols <= 0) return OZK_OK;
-    dim3 grid((unsigned)((cols + 63) / 64), (unsigned)(ldp / 64));
+    dim3 grid((unsigned)((cols + 31) / 32), (unsigned)((ldp + 127) / 128));
     if (wide)
       hipLaunchKernelGGL(residues_cols_kernel<true>, grid, dim3(256), 0, s, x, rows, cols, ldx,
                          K, p_bits, maxbits, planes, ldp, plane_stride, exps);
