@@ -7,15 +7,13 @@
 // has no tail.  |residue| <= 128 and kp <= 131072 keep every int32 sum exact.
 //
 // Tiling: workgroup tile 256 x 256 x 64, 512 threads = 8 waves, two per SIMD.  Waves
-// 0..3 (group 0) own rows 0..127 of the tile, waves 4..7 (group 1) rows 128..255; each
-// wave a 128 x 64 block of 4 x 2 MFMA tiles of 32 x 32 (128 accumulator registers).
-// The two groups run out of phase ("ping-pong"): while one group issues its 16 MFMAs of
-// a K step (and its share of the global loads), the other reads its fragments of the next
-// K step from LDS, so each SIMD's matrix unit always has one wave that does not wait on
-// memory.  Phases are separated by workgroup barriers; group 1 starts one phase late.
-// Global tiles go straight into a 5-deep LDS ring (32 KiB per K step) by
-// global_load_lds_dwordx4, 4 K steps ahead, issued between the MFMAs of compute phases
-// from a wave-uniform SGPR base plus a fixed per-lane offset.
+// 0..3 own rows 0..127 of the tile, waves 4..7 rows 128..255; each wave a 128 x 64 block
+// of 4 x 2 MFMA tiles of 32 x 32 (128 accumulator registers).  Each K step is two halves
+// of 8 MFMAs around one workgroup barrier; the fragments of the next half are read from
+// LDS between the MFMAs of the current one, and the two waves of a SIMD cover each
+// other's waits.  Global tiles go straight into a 5-deep LDS ring (32 KiB per K step) by
+// global_load_lds_dwordx4, issued between MFMAs from a wave-uniform SGPR base plus a
+// fixed per-lane offset into the stage consumed one barrier earlier, five K steps ahead.
 // LDS rows are 64 bytes with the four 16-byte chunks XOR-swizzled by (row >> 2) & 3, so
 // the 16 lanes of a fragment read (16 consecutive rows, one chunk each) cover all 64
 // banks.  Workgroups are mapped XCD by XCD (the hardware deals them out round-robin over
@@ -86,12 +84,7 @@ constexpr int kStages = 5;                    // LDS ring of K steps: 160 KiB
 constexpr int kStageBytes = kLdsA + kLdsB;    // 32 KiB: A rows 0..255 then B rows 0..255
 constexpr int kWaves = kThreads / 64;
 constexpr int kRegionsPerWave = kStageBytes / 1024 / kWaves;  // 1 KiB per load instruction
-// Loads younger than the last load of step t + 1 when a wave waits for it: group 0 waits
-// after its compute phase of step t (steps t+2 .. t+kStages-1 issued), group 1 after its
-// memory phase of step t (steps t+2 .. t+kStages-2 issued).
-constexpr int kPending0 = kRegionsPerWave * (kStages - 2);
-constexpr int kPending1 = kRegionsPerWave * (kStages - 3);
-static_assert(kRegionsPerWave == 4, "one load per wave after every fourth MFMA");
+static_assert(kRegionsPerWave == 4, "one load per wave after every other MFMA of half 1");
 constexpr int kOutPitch = BN + 8;  // residue staging: 2 rows apart = 1 bank apart (dwords)
 static_assert(BM * kOutPitch <= kStages * kStageBytes, "residue staging must fit the ring");
 
@@ -124,9 +117,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  // rows grp*128 of the tile; also the phase offset (wave-uniform, held in an SGPR so that
-  // the branches around barriers are scalar branches)
-  const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
+  const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);  // rows grp*128 (uniform)
   const int wq = __builtin_amdgcn_readfirstlane(wave & 3);  // columns wq*64 (uniform)
 
   // Direct-load sources: wave w fills regions w, w+8, w+16, w+24 of a stage; region rg
@@ -185,56 +176,64 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
   const int sw = (frow >> 2) & 3;  // row swizzle (the same for every block: 32 | block rows)
   v4i fa[2][4], fb[2][2];
 
-  // Phase schedule (one barrier between phases; group 1 runs one phase behind group 0):
-  //   memory phase of step t: read the 12 fragments of step t;
-  //   compute phase of step t: the 16 MFMAs of step t, and this wave's 4 loads of step
-  //   t + kStages - 1 into the stage of step t - 1 (read by both groups in earlier phases;
-  //   every wave waited for its reads before the barrier that ended them), one after each
-  //   fourth MFMA.  Issued from the memory phase instead, four waves issuing together
-  //   stall about 70 cycles per load and the memory phase becomes the critical path.
-  // Both groups wait for their own loads of step t + 1 before the barrier that ends
-  // phase 2t + 1 (group 0: end of its compute phase; group 1: end of its memory phase), so
-  // step t + 1 is complete in LDS before group 0 reads it in phase 2t + 2.
+  // Schedule: every wave runs the same two halves per K step, one barrier between them:
+  //   half 0 of step t: the 8 MFMAs of K half 0, reading the K half 1 fragments of step t
+  //   between them; then wait for this wave's loads of step t+1 and for its reads;
+  //   barrier: step t+1 is complete in LDS and every wave has finished reading step t;
+  //   half 1: the 8 MFMAs of K half 1, reading step t+1's K half 0 fragments and issuing
+  //   this wave's 4 loads of step t+kStages into the stage of step t (just consumed).
+  // Loads therefore run kStages - 1 full steps ahead of their wait; younger than the last
+  // load of step t+1 at the wait are those of steps t+2 .. t+kStages-1.
 #pragma unroll
-  for (int t = 0; t < kStages - 1; ++t) issue_step(t);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRegionsPerWave * (kStages - 2)) : "memory");
+  for (int t = 0; t < kStages; ++t) issue_step(t);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRegionsPerWave * (kStages - 1)) : "memory");
   wg_barrier();
-  if (grp == 1) wg_barrier();
+  {
+    const int8_t* st = lds;
+    const int c = (fchunk ^ sw) << 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[0][i] = *reinterpret_cast<const v4i*>(st + offa[i] + c);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[0][j] = *reinterpret_cast<const v4i*>(st + offb[j] + c);
+  }
   for (int t = 0; t < nk; ++t) {
     __builtin_amdgcn_sched_barrier(0);
     const int8_t* st = lds + (t % kStages) * kStageBytes;
+    const int c1 = ((2 + fchunk) ^ sw) << 4;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int c = ((kk * 2 + fchunk) ^ sw) << 4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fa[kk][i] = *reinterpret_cast<const v4i*>(st + offa[i] + c);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) fb[kk][j] = *reinterpret_cast<const v4i*>(st + offb[j] + c);
+    for (int idx = 0; idx < 8; ++idx) {
+      const int i = idx >> 1, j = idx & 1;
+      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[0][j], fa[0][i], acc[i][j], 0, 0, 0);
+      if (idx < 4)
+        fa[1][idx] = *reinterpret_cast<const v4i*>(st + offa[idx] + c1);
+      else if (idx < 6)
+        fb[1][idx - 4] = *reinterpret_cast<const v4i*>(st + offb[idx - 4] + c1);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRegionsPerWave * (kStages - 2)) : "memory");
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (grp == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPending1) : "memory");
     wg_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    const int tl = t + kStages - 1;
+    const int tn = t + 1 < nk ? t + 1 : t;  // past the last step: a harmless re-read
+    const int8_t* sn = lds + (tn % kStages) * kStageBytes;
+    const int c0 = (fchunk ^ sw) << 4;
+    const int tl = t + kStages;
     const int64_t koff = (int64_t)(tl < nk ? tl : nk - 1) * BK;
-    const uint32_t lbase = wave_lds + (uint32_t)(tl % kStages) * kStageBytes;
+    const uint32_t lbase = wave_lds + (uint32_t)(t % kStages) * kStageBytes;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[kk][j], fa[kk][i], acc[i][j], 0, 0, 0);
-          const int idx = kk * 8 + i * 2 + j;
-          if ((idx & 3) == 0)
-            dma16_sbase(voff[idx >> 2], region_base(idx >> 2) + (uint64_t)koff,
-                        lbase + (idx >> 2) * (kWaves * 1024));
-          __builtin_amdgcn_sched_barrier(0);
-        }
-    if (grp == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPending0) : "memory");
-    wg_barrier();
+    for (int idx = 0; idx < 8; ++idx) {
+      const int i = idx >> 1, j = idx & 1;
+      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[1][j], fa[1][i], acc[i][j], 0, 0, 0);
+      if (idx < 4)
+        fa[0][idx] = *reinterpret_cast<const v4i*>(sn + offa[idx] + c0);
+      else if (idx < 6)
+        fb[0][idx - 4] = *reinterpret_cast<const v4i*>(sn + offb[idx - 4] + c0);
+      if ((idx & 1) == 1)
+        dma16_sbase(voff[idx >> 1], region_base(idx >> 1) + (uint64_t)koff,
+                    lbase + (idx >> 1) * (kWaves * 1024));
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  if (grp == 0) wg_barrier();
   // The clamped loads past the last K step are still landing in the ring.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
