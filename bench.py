@@ -272,6 +272,47 @@ def measure_fp4(reps: int, stream) -> dict:
     return out
 
 
+def measure_practical_peaks(stream) -> dict:
+    """Rates this GPU sustains on data like the products': the register-only int8 and e2m1
+    matrix-core loops of ozk_probe_mfma over random operand bytes (about 0.2 s per launch,
+    the last of three back-to-back launches timed, so the board sits at its power limit),
+    a plain device copy of 2 GiB (torch, read + write bytes) and a 2 GiB reduction (torch
+    sum, read bytes)."""
+    import torch
+
+    import fp64_gemm_emulation_ozk_amd as ozk
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    operands = torch.randint(-128, 128, (1 << 20,), dtype=torch.int8, device=dev, generator=g)
+    out = {}
+    for kind, key in ((0, "int8_mfma_random_operands_tops"), (1, "fp4_mfma_random_operands_tflops")):
+        iters = 150000 if kind == 0 else 80000
+        ops = 0.0
+        for _ in range(2):
+            ops = ozk.ozk_probe_mfma(kind, operands, iters, 256)
+        t = _time_events(lambda: ozk.ozk_probe_mfma(kind, operands, iters, 256), 1, stream)
+        out[key] = round(ops / (t * 1e-3) / 1e12, 1)
+    src = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    t = _time_events(lambda: dst.copy_(src), 5, stream)
+    out["hbm_copy_gbs"] = round(2.0 * src.numel() / t / 1e6, 1)
+    del dst
+    x = src.view(torch.float64)
+    acc = torch.empty((), dtype=torch.float64, device=dev)
+    torch.sum(x, out=acc)
+    t = _time_events(lambda: torch.sum(x, out=acc), 5, stream)
+    out["hbm_read_gbs"] = round(src.numel() / t / 1e6, 1)
+    del src, x, operands
+    torch.cuda.empty_cache()
+    out["what"] = ("sustained rates with random operands (matrix cores draw data-dependent "
+                   "power; the board holds its power limit below the datasheet clock) and "
+                   "a 2 GiB device copy and a 2 GiB read-only reduction")
+    return out
+
+
 def cpu_baseline(a, b, r: int) -> dict:
     import numpy as np
     from threadpoolctl import threadpool_limits
@@ -371,6 +412,11 @@ def main() -> int:
     extras = {"wall_ms_per_step": round(wall_ms, 4), "normwise_vs_native_fp64": rel,
               "emulated_pct_int8_peak": round(r * value / PEAK_INT8_TOPS * 100, 2)}
     if not args.no_extras:
+        peaks = measure_practical_peaks(stream)
+        extras["practical_peaks"] = peaks
+        ceil = peaks["int8_mfma_random_operands_tops"]
+        roofline["measured_ceiling"] = ceil
+        roofline["frac_of_measured_ceiling"] = round(achieved / ceil, 4)
         reps = max(args.steps // 2, 5)
         nat_ms = _time_events(lambda: torch.matmul(da, db, out=ref), reps, stream)
         extras["native_fp64_dgemm"] = {"ms": round(nat_ms, 4),

@@ -21,6 +21,7 @@ __all__ = [
     "ozk_fp4limb_pack", "ozk_fp4limb_products", "ozk_int8gemm_fp4limb",
     "ozk_dgemm_workspace_size", "ozk_dgemv_workspace_size",
     "ozk_int8gemm_fp4limb_workspace_size", "ozk_deconstruct_workspace_size",
+    "ozk_probe_mfma",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libozk.so")
@@ -58,6 +59,7 @@ _SIGNATURES = {
     "ozk_int8gemm_fp4limb_workspace_size": (_int, [_i64, _i64, _i64, _ptr]),
     "ozk_int8gemm_fp4limb": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr,
                                     _size, _ptr]),
+    "ozk_probe_mfma": (_int, [_int, _ptr, _i64, _i64, _int, _ptr, _ptr, _ptr]),
 }
 
 _LIB = None
@@ -326,3 +328,20 @@ def ozk_int8gemm_fp4limb(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | N
     _call("ozk_int8gemm_fp4limb", m, n, k, _dev_ptr(a), _ld(a), _dev_ptr(b), _ld(b),
           _dev_ptr(out), _ld(out), _dev_ptr(workspace), workspace.numel(), _stream(stream))
     return out
+
+
+# ----------------------------------------------------------------------- measurement
+def ozk_probe_mfma(kind: int, operands: torch.Tensor, iters: int, workgroups: int,
+                   sink: torch.Tensor | None = None, stream=None) -> float:
+    """Enqueue the register-only matrix-core loop (kind 0: int8 32x32x32, kind 1: e2m1
+    32x32x64) over the bytes of `operands`; returns the operation count of the launch."""
+    if not isinstance(operands, torch.Tensor) or not operands.is_cuda or not operands.is_contiguous():
+        raise TypeError("operands must be a contiguous CUDA/HIP tensor")
+    if sink is None:
+        sink = torch.empty(workgroups * 512, dtype=torch.int32, device=operands.device)
+    if sink.dtype != torch.int32 or sink.numel() < workgroups * 512:
+        raise ValueError("sink must hold workgroups * 512 int32 values")
+    ops = ctypes.c_double(0.0)
+    _call("ozk_probe_mfma", kind, _dev_ptr(operands), operands.numel() * operands.element_size(),
+          iters, workgroups, _dev_ptr(sink), ctypes.byref(ops), _stream(stream))
+    return ops.value

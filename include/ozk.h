@@ -177,6 +177,22 @@ int ozk_int8gemm_fp4limb(int64_t m, int64_t n, int64_t k, const int8_t* A, int64
                          const int8_t* B, int64_t ldb, int32_t* C, int64_t ldc,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- measurement support
+ * ozk_probe_mfma: enqueue a register-only loop of matrix-core instructions with the
+ *   caller's operand bytes, to measure the sustained rate this GPU reaches on data like
+ *   the products' (the matrix cores draw data-dependent power; random operands hold
+ *   the board at its power cap below the datasheet clock).  kind 0: int8
+ *   v_mfma_i32_32x32x32_i8 (65536 ops each); kind 1: e2m1 x e2m1
+ *   v_mfma_scale_f32_32x32x64_f8f6f4 (131072 ops each).  `operands`: device memory,
+ *   16-byte aligned, operand_bytes >= 16 (random bytes give the representative rate;
+ *   each wave reads 16 KiB of it, wrapping around).  `sink`: device int32 array of
+ *   workgroups * 512 entries, overwritten.  `ops` (host, may be NULL) receives the
+ *   operation count of the launch, to be divided by the caller's measured time.
+ *   Launches `workgroups` workgroups of 512 threads, each running `iters` iterations of
+ *   32 instructions per wave. */
+int ozk_probe_mfma(int kind, const void* operands, int64_t operand_bytes, int64_t iters,
+                   int workgroups, int32_t* sink, double* ops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -124,3 +124,16 @@ def test_products_and_reconstruct_validation(lib):
     assert g(4, 4, 0, FAKE, 4, 16, FAKE, FAKE, FAKE, 4, None) == EINVAL
     assert g(4, 4, 3, FAKE, 3, 16, FAKE, FAKE, FAKE, 4, None) == EINVAL             # ld < n
     assert g(4, 4, 3, None, 4, 16, FAKE, FAKE, FAKE, 4, None) == EINVAL
+
+
+def test_probe_validation(lib):
+    f = lib.ozk_probe_mfma
+    ops = ctypes.c_double(-1.0)
+    assert f(2, FAKE, 1024, 10, 4, FAKE, ctypes.byref(ops), None) == EINVAL        # kind
+    assert f(0, None, 1024, 10, 4, FAKE, ctypes.byref(ops), None) == EINVAL        # operands
+    assert f(0, FAKE, 8, 10, 4, FAKE, ctypes.byref(ops), None) == EINVAL           # < 16 bytes
+    assert f(0, FAKE, 1024, 0, 4, FAKE, ctypes.byref(ops), None) == EINVAL         # iters
+    assert f(1, FAKE, 1024, 10, 0, FAKE, ctypes.byref(ops), None) == EINVAL        # workgroups
+    assert f(1, FAKE, 1024, 10, 4, None, ctypes.byref(ops), None) == EINVAL        # sink
+    assert f(0, ctypes.c_void_p(0x1008), 1024, 10, 4, FAKE, ctypes.byref(ops), None) == EINVAL
+    assert ops.value == -1.0                                                       # untouched
