@@ -302,8 +302,8 @@ def measure_practical_peaks(stream) -> dict:
     del dst
     x = src.view(torch.float64)
     acc = torch.empty((), dtype=torch.float64, device=dev)
-    torch.sum(x, out=acc)
-    t = _time_events(lambda: torch.sum(x, out=acc), 5, stream)
+    torch.sum(x, dim=0, out=acc)
+    t = _time_events(lambda: torch.sum(x, dim=0, out=acc), 5, stream)
     out["hbm_read_gbs"] = round(src.numel() / t / 1e6, 1)
     del src, x, operands
     torch.cuda.empty_cache()
