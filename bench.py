@@ -8,7 +8,8 @@ resident in HBM before timing starts.  `value` is emulated fp64 TFLOP/s = 2 m n 
 
 Also reported on the same JSON line:
   roofline      the dominant kernel (batched int8 MFMA products, residue epilogue) timed
-                alone with HIP events on its stream: r * 2 * m * n * kp int8 ops per launch
+                alone, one HIP event pair per launch on its stream: r * 2 * m * n * kp int8
+                ops per launch
                 against the 5.0 POP/s dense int8 MFMA peak; HBM traffic per launch from
                 the committed rocprofv3 counter summary when it matches the kernel source
                 (made by `--counters` under two `rocprofv3 --pmc` passes, then
@@ -62,6 +63,21 @@ def _time_events(fn, reps: int, stream) -> float:
     end.record(stream)
     end.synchronize()
     return start.elapsed_time(end) / reps
+
+
+def _time_each(fn, reps: int, stream) -> float:
+    """Average milliseconds per launch of fn, one HIP event pair around each of reps
+    back-to-back launches on `stream` (launch gaps between calls are not counted)."""
+    import torch
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    ev[-1][1].synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / reps
 
 
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic_dgemm_4096_r16.json")
@@ -397,7 +413,7 @@ def main() -> int:
     gemm = lambda: ozk.ozk_modular_residues(planes_a, planes_b, out=res)
     for _ in range(2):
         gemm()
-    gemm_ms = _time_events(gemm, args.steps, stream)
+    gemm_ms = _time_each(gemm, args.steps, stream)
     kp = planes_a.shape[-1]
     ops = r * 2.0 * M * N * kp
     achieved = ops / (gemm_ms * 1e-3) / 1e12
