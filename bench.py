@@ -187,6 +187,176 @@ def traffic_summary(fetch_dir: str, write_dir: str) -> int:
     return 0
 
 
+TME_COUNTERS = ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_WAVES",
+                "GRBM_GUI_ACTIVE"]
+TME_PATH = os.path.join(ROOT, "profiles", "tme_counters.json")
+# Kernels whose instruction counts calibrate the time model: key -> (kernel-name
+# substring, unit the counts are divided by, number of units per dispatch, moduli).
+TME_KERNELS = {
+    "decon_rows_wide_4096_r16": ("residues_rows_fused_kernel<true, true, 256, 2>",
+                                 "element", 4096 * 4096, 16),
+    "decon_rows_narrow_32768_r14": ("residues_rows_fused_kernel<false, true, 1024, 4>",
+                                    "element", 32768 * 32768, 14),
+    "decon_cols_wide_4096_r16": ("residues_cols_kernel<true>", "element", 4096 * 4096, 16),
+    "gemv_fly_32768_r14_32cols": ("gemv_fly_kernel<false, 14>", "element of A",
+                                  32768 * 32768, 14),
+    "gemv_digits_32768_r14_1col": ("gemv_digits_kernel<1>", "element of A", 32768 * 32768, 14),
+    "gemv_digits_32768_r14_8cols": ("gemv_digits_kernel<4>", "element of A", 32768 * 32768, 14),
+    "gemv_stored_32768_r14_1col": ("gemv_stored_kernel", "element of A", 32768 * 32768, 14),
+    "crt_4096_r16": ("crt_kernel<16", "output", 4096 * 4096, 16),
+    "gemm_i8_4096_r16": ("gemm_i8_kernel<1>", "output x modulus", 4096 * 4096 * 16, 16),
+}
+
+
+def run_tme_workload() -> int:
+    """Launches profiled by the time-model counter pass (instruction counts only; nothing
+    is timed): two DGEMM steps of the 4096^3 r=16 workload, then the 32768^2 r=14 GEMV
+    workload's deconstruction and one on-the-fly call for 1, 8 and 32 columns and one
+    stored-plane call for 1 column."""
+    import numpy as np
+    import torch
+
+    import fp64_gemm_emulation_ozk_amd as ozk
+    import ozk_inputs
+
+    dev = torch.device("cuda:0")
+    a, b = ozk_inputs.gemm_operands(M, N, K, seed=SEED, dist="phi", phi=PHI)
+    da, db = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    out = torch.empty((M, N), dtype=torch.float64, device=dev)
+    ws = torch.empty(ozk.ozk_dgemm_workspace_size(M, N, K, 16), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        ozk.ozk_dgemm(da, db, 16, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    del da, db, out, ws
+    mg, r = 32768, 14
+    ga = ozk_inputs.uniform_matrix_device((mg, mg), 4, dev)
+    x_all = torch.from_numpy(ozk_inputs.uniform_matrix(np.random.default_rng(4), (mg, 32))).to(dev)
+    planes, exps = ozk.ozk_deconstruct(ga, 0, r, k_budget=mg)
+    for nrhs in (1, 8, 32):
+        dx = x_all[:, :nrhs].contiguous()
+        ozk.ozk_dgemv(ga, dx, r, mode=0, a_exps=exps)
+    ozk.ozk_dgemv(None, x_all[:, :1].contiguous(), r, mode=1, a_planes=planes, a_exps=exps)
+    torch.cuda.synchronize()
+    print("time-model counter workload done", flush=True)
+    return 0
+
+
+def tme_summary(run_dir: str) -> int:
+    """Per-dispatch instruction counts of the calibration kernels from one rocprofv3 --pmc
+    pass over the TME_COUNTERS, and the per-unit figures the time model uses (vector
+    instructions x 64 lanes per element per modulus = c_q)."""
+    means = {c: _counter_means(run_dir, c) for c in TME_COUNTERS}
+    data = {"what": "rocprofv3 --pmc " + " ".join(TME_COUNTERS) + " over `bench.py "
+                    "--tme-counters`; instruction counts are per wave (64 lanes)",
+            "kernels": {}}
+    for key, (sub, unit, units, r) in TME_KERNELS.items():
+        ent = {"kernel": sub, "unit": unit, "units_per_dispatch": units, "r": r}
+        for c in TME_COUNTERS:
+            hits = [v for k, v in means[c].items() if sub in k]
+            ent[c] = round(sum(hits) / len(hits), 1) if hits else None
+        valu, mfma = ent["SQ_INSTS_VALU"], ent["SQ_INSTS_MFMA"]
+        if valu is not None and mfma is not None:
+            vec = max(valu - mfma, 0.0)
+            ent["vector_lane_ops_per_unit"] = round(vec * 64 / units, 3)
+            ent["vector_lane_ops_per_unit_per_modulus"] = round(vec * 64 / units / r, 3)
+            ent["mfma_per_unit"] = round(mfma / units, 6)
+        data["kernels"][key] = ent
+    with open(TME_PATH, "w") as fh:
+        json.dump(data, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(data, indent=1))
+    return 0
+
+
+P_FP64 = 78.6e12          # fp64 FLOP/s (datasheet, vector and matrix)
+P_VALU = 256 * 4 * 16 * 2.4e9   # vector lane-operations per second: 256 CUs x 4 SIMDs x 16 lanes
+
+
+def tme_model(extras: dict, peaks: dict, dgemm_ms: float) -> dict | None:
+    """Page 1's four-term time model instantiated on this GPU: T = max(T_tensor, T_HBM) +
+    T_recon + T_decon, with T_decon = c_q r N / P_int the per-input deconstruction term.
+    Instruction counts come from the committed counter pass (profiles/tme_counters.json:
+    vector lane-operations and MFMA instructions per element, per kernel); rates are the
+    measured random-operand MFMA ceiling and read bandwidth of this run, and the datasheet
+    vector rate.  Returns the threshold OI* = c_q r P_fp64 / (8 P_int), the per-element
+    instruction budget below which an on-the-fly GEMV can stream at memory speed, and
+    model-versus-measured times of the GEMV paths and the DGEMM step."""
+    try:
+        with open(TME_PATH) as fh:
+            cal = json.load(fh)["kernels"]
+    except (OSError, ValueError, KeyError):
+        return None
+    p_i8 = peaks["int8_mfma_random_operands_tops"] * 1e12
+    bw = peaks["hbm_read_gbs"] * 1e9
+
+    def k(key, field):
+        return cal[key][field]
+
+    cq = k("decon_rows_narrow_32768_r14", "vector_lane_ops_per_unit_per_modulus")
+    r14 = 14
+    out = {"c_q_residue_path_narrow": cq,
+           "c_q_residue_path_wide": k("decon_rows_wide_4096_r16",
+                                      "vector_lane_ops_per_unit_per_modulus"),
+           "P_int_lane_ops_per_s": P_VALU, "P_fp64_flops": P_FP64,
+           "oi_star_flop_per_byte_r14": round(cq * r14 * P_FP64 / (8 * P_VALU), 2),
+           "fp64_ridge_flop_per_byte": round(P_FP64 / 8e12, 2),
+           "max_lane_ops_per_element_for_memory_speed": {
+               "at_8_TBs": round(8 * P_VALU / 8e12, 1),
+               "at_measured_read_bw": round(8 * P_VALU / bw, 1)},
+           "digits_path_lane_ops_per_element": k("gemv_digits_32768_r14_1col",
+                                                 "vector_lane_ops_per_unit")}
+    n_a = 32768.0 * 32768.0
+    rows = []
+    g = extras.get("gemv_32768")
+    if g:
+        by = {run["nrhs"]: run for run in g["runs"]}
+
+        def model(key, hbm_bytes, mfma_ops_per_inst=65536.0):
+            t_t = cal[key]["mfma_per_unit"] * n_a * mfma_ops_per_inst / p_i8
+            t_h = hbm_bytes / bw
+            t_d = cal[key]["vector_lane_ops_per_unit"] * n_a / P_VALU
+            return t_t, t_h, t_d
+
+        cases = [("on the fly, digits, 1 col", "gemv_digits_32768_r14_1col", 8 * n_a,
+                  by.get(1, {}).get("on_the_fly_cached_exps", {}).get("ms")),
+                 ("on the fly, digits, 8 cols", "gemv_digits_32768_r14_8cols", 8 * n_a,
+                  by.get(8, {}).get("on_the_fly_cached_exps", {}).get("ms")),
+                 ("on the fly, residues, 32 cols", "gemv_fly_32768_r14_32cols", 8 * n_a,
+                  by.get(32, {}).get("on_the_fly_cached_exps", {}).get("ms")),
+                 ("stored planes, 1 col", "gemv_stored_32768_r14_1col", r14 * n_a,
+                  by.get(1, {}).get("stored_planes", {}).get("ms"))]
+        for name, key, hbm, measured in cases:
+            t_t, t_h, t_d = model(key, hbm)
+            rows.append({"case": f"GEMV 32768^2 r=14, {name}", "T_tensor_ms": round(t_t * 1e3, 3),
+                         "T_hbm_ms": round(t_h * 1e3, 3), "T_decon_ms": round(t_d * 1e3, 3),
+                         "model_ms": round((max(t_t, t_h) + t_d) * 1e3, 3),
+                         "measured_ms": measured})
+        for nrhs in (1, 8, 32):
+            if nrhs in by:
+                rows.append({"case": f"GEMV 32768^2 native fp64, {nrhs} col",
+                             "T_hbm_ms": round(8 * n_a / bw * 1e3, 3),
+                             "model_ms": round(8 * n_a / bw * 1e3, 3),
+                             "measured_ms": by[nrhs]["native_fp64"]["ms"]})
+    # DGEMM step: products on the matrix cores, deconstruction of A (rows) and B
+    # (columns), CRT per output; HBM bytes are small next to the tensor term.
+    t_t = 16 * 2.0 * M * N * K / p_i8
+    t_d = (k("decon_rows_wide_4096_r16", "vector_lane_ops_per_unit") +
+           k("decon_cols_wide_4096_r16", "vector_lane_ops_per_unit")) * M * K / P_VALU
+    t_r = k("crt_4096_r16", "vector_lane_ops_per_unit") * M * N / P_VALU
+    case = {"case": "DGEMM 4096^3 r=16", "T_tensor_ms": round(t_t * 1e3, 3),
+            "T_decon_ms": round(t_d * 1e3, 3), "T_recon_ms": round(t_r * 1e3, 3),
+            "model_ms": round((t_t + t_d + t_r) * 1e3, 3), "measured_ms": round(dgemm_ms, 4)}
+    if "deconstruct_cols" in extras and "reconstruct_and_gaps" in extras:
+        case["measured_phases_ms"] = {
+            "products": extras.get("products_ms"),
+            "deconstruct_rows": extras["deconstruct_rows"]["ms"],
+            "deconstruct_cols": extras["deconstruct_cols"]["ms"],
+            "reconstruct_and_gaps": extras["reconstruct_and_gaps"]["ms"]}
+    rows.append(case)
+    out["cases"] = rows
+    return out
+
+
 def measure_gemv(reps: int, stream) -> dict:
     """The 32768 x 32768 GEMV / low-batch GEMV workload at r = 14: A U(-1,1) (seed 4, drawn
     on the GPU), X U(-1,1) with 1, 8 and 32 columns.  GB/s counts the algorithmic bytes of
@@ -361,9 +531,15 @@ def main() -> int:
                     help="only launch the kernels the counter passes profile")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the HBM traffic summary from two rocprofv3 --pmc csv runs")
+    ap.add_argument("--tme-counters", action="store_true",
+                    help="only launch the kernels the time-model counter pass profiles")
+    ap.add_argument("--tme-summary", metavar="DIR",
+                    help="write the time-model instruction counts from a rocprofv3 --pmc run")
     args = ap.parse_args()
     if args.traffic_summary:
         return traffic_summary(*args.traffic_summary)
+    if args.tme_summary:
+        return tme_summary(args.tme_summary)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the emulation "
               "path is built and measured on a single MI355X; multi-GPU runs are not "
@@ -381,6 +557,8 @@ def main() -> int:
         build_library()
     if args.counters:
         return run_counter_workload()
+    if args.tme_counters:
+        return run_tme_workload()
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     r = args.r
@@ -426,7 +604,8 @@ def main() -> int:
                 "source_digest": digest}
 
     extras = {"wall_ms_per_step": round(wall_ms, 4), "normwise_vs_native_fp64": rel,
-              "emulated_pct_int8_peak": round(r * value / PEAK_INT8_TOPS * 100, 2)}
+              "emulated_pct_int8_peak": round(r * value / PEAK_INT8_TOPS * 100, 2),
+              "products_ms": round(gemm_ms, 4)}
     if not args.no_extras:
         peaks = measure_practical_peaks(stream)
         extras["practical_peaks"] = peaks
@@ -467,12 +646,27 @@ def main() -> int:
             "ms": round(dec_ms, 4), "bytes": (8 + r) * M * K,
             "gbs": round((8 + r) * M * K / dec_ms / 1e6, 1),
             "frac_hbm": round((8 + r) * M * K / dec_ms / 1e6 / PEAK_HBM_GBS, 4)}
+        decb = lambda: ozk.ozk_deconstruct(db, 1, r, k_budget=K, planes=planes_b, exps=exps_b)
+        decb()
+        decb_ms = _time_events(decb, reps, stream)
+        extras["deconstruct_cols"] = {
+            "ms": round(decb_ms, 4), "bytes": (8 + 8 + r) * K * N,
+            "gbs": round((8 + 8 + r) * K * N / decb_ms / 1e6, 1),
+            "note": "column maxima pass (8 B per element) + residues (8 + r B per element)"}
+        # The CRT of the step runs on int8 residues inside ozk_dgemm; its share is what the
+        # step leaves after the products and both deconstructions.
+        extras["reconstruct_and_gaps"] = {
+            "ms": round(ms_per_step - gemm_ms - dec_ms - decb_ms, 4),
+            "note": "step time minus the products and both deconstructions"}
         if not args.no_gemv:
             del planes_a, planes_b, res, ws
             torch.cuda.empty_cache()
             extras["gemv_32768"] = measure_gemv(reps, stream)
         if not args.no_fp4:
             extras["fp4limb_int8gemm_8192"] = measure_fp4(reps, stream)
+        model = tme_model(extras, peaks, ms_per_step)
+        if model is not None:
+            extras["tme_model"] = model
 
     line = {
         "metric": METRIC,
