@@ -37,7 +37,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kGroupM = 4;
 constexpr int kXcds = 8;
-constexpr int kThreads = 512;
+constexpr int kWavesDefault = 8;  // waves per workgroup of the launched kernel
 constexpr int kLdsA = BM * BK;   // bytes per stage
 constexpr int kLdsB = BN * BK;
 
@@ -82,14 +82,23 @@ __device__ __forceinline__ void wg_barrier() {
 
 constexpr int kStages = 5;                    // LDS ring of K steps: 160 KiB
 constexpr int kStageBytes = kLdsA + kLdsB;    // 32 KiB: A rows 0..255 then B rows 0..255
-constexpr int kWaves = kThreads / 64;
-constexpr int kRegionsPerWave = kStageBytes / 1024 / kWaves;  // 1 KiB per load instruction
-static_assert(kRegionsPerWave == 4, "one load per wave after every other MFMA of half 1");
 constexpr int kOutPitch = BN + 8;  // residue staging: 2 rows apart = 1 bank apart (dwords)
+
+// Wave layout of a 256 x 256 tile: NW waves in 2 rows x NW/2 columns, each wave WM x WN
+// = 128 x (512 / NW) outputs as TI x TJ MFMA blocks of 32 x 32.
+template <int NW>
+struct WaveLayout {
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int WN = 2 * BN / NW;
+  static constexpr int TI = 4, TJ = WN / 32;
+  static constexpr int kLoads = kStageBytes / 1024 / NW;  // 1 KiB load instructions per step
+  static constexpr int kMfmaHalf = TI * TJ;
+  static_assert(kMfmaHalf >= TI + TJ && kMfmaHalf == 2 * kLoads, "load and read slots");
+};
 static_assert(BM * kOutPitch <= kStages * kStageBytes, "residue staging must fit the ring");
 
-template <int kEpi>
-__global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
+template <int kEpi, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_i8_kernel(
     int64_t m, int64_t n, int64_t kp, const int8_t* __restrict__ pa, int64_t stride_a,
     const int8_t* __restrict__ pb, int64_t stride_b, void* __restrict__ out, int64_t ldo,
     int64_t stride_o, int tiles_m, int tiles_n, EpiModuli E, int vec_out) {
@@ -114,11 +123,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
   const int64_t row0 = (int64_t)tm * BM;
   const int64_t col0 = (int64_t)tn * BN;
 
+  using WL = WaveLayout<NW>;
+  constexpr int TI = WL::TI, TJ = WL::TJ, kWaves = NW, kRegionsPerWave = WL::kLoads;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);  // rows grp*128 (uniform)
-  const int wq = __builtin_amdgcn_readfirstlane(wave & 3);  // columns wq*64 (uniform)
+  const int grp = __builtin_amdgcn_readfirstlane(wave / (NW / 2));  // rows grp*128 (uniform)
+  const int wq = __builtin_amdgcn_readfirstlane(wave % (NW / 2));   // columns wq*WN (uniform)
 
   // Direct-load sources: wave w fills regions w, w+8, w+16, w+24 of a stage; region rg
   // holds 16 rows of A (rg < 16) or B, 64 bytes each; lane i lands at row 16*(rg%16) + i/4,
@@ -141,7 +152,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     const int64_t gr = origin + row < last ? origin + row : last;
     voff[q] = (uint32_t)((gr - origin) * kp + 16 * chunk);
   }
-  auto region_base = [&](int q) {  // uniform: region wave + 8q is B iff q >= 2
+  auto region_base = [&](int q) {  // uniform: region wave + NW q is B iff it is >= 16
     return wave_u + kWaves * q >= 16 ? sbase_b : sbase_a;
   };
   const uint32_t lds0 = lds_address(lds);
@@ -155,11 +166,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
       dma16_sbase(voff[q], region_base(q) + (uint64_t)tc * BK, base + q * (kWaves * 1024));
   };
 
-  v16i acc[4][2];
+  v16i acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
 
@@ -168,13 +179,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
   // independent of how the instruction orders K internally.
   const int frow = lane & 31;
   const int fchunk = lane >> 5;
-  int offa[4], offb[2];
+  int offa[TI], offb[TJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) offa[i] = (grp * 128 + i * 32 + frow) * BK;
+  for (int i = 0; i < TI; ++i) offa[i] = (grp * 128 + i * 32 + frow) * BK;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) offb[j] = kLdsA + (wq * 64 + j * 32 + frow) * BK;
+  for (int j = 0; j < TJ; ++j) offb[j] = kLdsA + (wq * WL::WN + j * 32 + frow) * BK;
   const int sw = (frow >> 2) & 3;  // row swizzle (the same for every block: 32 | block rows)
-  v4i fa[2][4], fb[2][2];
+  v4i fa[2][TI], fb[2][TJ];
 
   // Schedule: every wave runs the same two halves per K step, one barrier between them:
   //   half 0 of step t: the 8 MFMAs of K half 0, reading the K half 1 fragments of step t
@@ -192,22 +203,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     const int8_t* st = lds;
     const int c = (fchunk ^ sw) << 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[0][i] = *reinterpret_cast<const v4i*>(st + offa[i] + c);
+    for (int i = 0; i < TI; ++i) fa[0][i] = *reinterpret_cast<const v4i*>(st + offa[i] + c);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) fb[0][j] = *reinterpret_cast<const v4i*>(st + offb[j] + c);
+    for (int j = 0; j < TJ; ++j) fb[0][j] = *reinterpret_cast<const v4i*>(st + offb[j] + c);
   }
   for (int t = 0; t < nk; ++t) {
     __builtin_amdgcn_sched_barrier(0);
     const int8_t* st = lds + (t % kStages) * kStageBytes;
     const int c1 = ((2 + fchunk) ^ sw) << 4;
 #pragma unroll
-    for (int idx = 0; idx < 8; ++idx) {
-      const int i = idx >> 1, j = idx & 1;
+    for (int idx = 0; idx < WL::kMfmaHalf; ++idx) {
+      const int i = idx / TJ, j = idx % TJ;
       acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[0][j], fa[0][i], acc[i][j], 0, 0, 0);
-      if (idx < 4)
+      if (idx < TI)
         fa[1][idx] = *reinterpret_cast<const v4i*>(st + offa[idx] + c1);
-      else if (idx < 6)
-        fb[1][idx - 4] = *reinterpret_cast<const v4i*>(st + offb[idx - 4] + c1);
+      else if (idx < TI + TJ)
+        fb[1][idx - TI] = *reinterpret_cast<const v4i*>(st + offb[idx - TI] + c1);
       __builtin_amdgcn_sched_barrier(0);
     }
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRegionsPerWave * (kStages - 2)) : "memory");
@@ -221,13 +232,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     const int64_t koff = (int64_t)(tl < nk ? tl : nk - 1) * BK;
     const uint32_t lbase = wave_lds + (uint32_t)(t % kStages) * kStageBytes;
 #pragma unroll
-    for (int idx = 0; idx < 8; ++idx) {
-      const int i = idx >> 1, j = idx & 1;
+    for (int idx = 0; idx < WL::kMfmaHalf; ++idx) {
+      const int i = idx / TJ, j = idx % TJ;
       acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[1][j], fa[1][i], acc[i][j], 0, 0, 0);
-      if (idx < 4)
+      if (idx < TI)
         fa[0][idx] = *reinterpret_cast<const v4i*>(sn + offa[idx] + c0);
-      else if (idx < 6)
-        fb[0][idx - 4] = *reinterpret_cast<const v4i*>(sn + offb[idx - 4] + c0);
+      else if (idx < TI + TJ)
+        fb[0][idx - TI] = *reinterpret_cast<const v4i*>(sn + offb[idx - TI] + c0);
       if ((idx & 1) == 1)
         dma16_sbase(voff[idx >> 1], region_base(idx >> 1) + (uint64_t)koff,
                     lbase + (idx >> 1) * (kWaves * 1024));
@@ -242,15 +253,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
   // 8*(v/4) + 4*(lane/32) + (v%4); registers 4q..4q+3 hold 4 consecutive columns.
   const int mod = E.mod[l];
   const double inv = E.inv[l];
-  const int64_t wrow0 = row0 + grp * 128, wcol0 = col0 + wq * 64;
+  const int64_t wrow0 = row0 + grp * 128, wcol0 = col0 + wq * WL::WN;
   if (kEpi == kEpiProducts) {
     int32_t* o = reinterpret_cast<int32_t*>(out) + l * stride_o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TI; ++i) {
       const int64_t row = wrow0 + i * 32 + (lane & 31);
       if (row >= m) continue;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < TJ; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int64_t col = wcol0 + j * 32 + 8 * q + 4 * (lane >> 5);
@@ -276,15 +287,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
   // once per tile rather than per element).
   auto stage = [&](auto byte_of) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < TJ; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t w = pack4b(byte_of(acc[i][j][4 * q]), byte_of(acc[i][j][4 * q + 1]),
                                     byte_of(acc[i][j][4 * q + 2]), byte_of(acc[i][j][4 * q + 3]));
           *reinterpret_cast<uint32_t*>(tile + (grp * 128 + i * 32 + (lane & 31)) * kOutPitch +
-                                       wq * 64 + j * 32 + 8 * q + 4 * (lane >> 5)) = w;
+                                       wq * WL::WN + j * 32 + 8 * q + 4 * (lane >> 5)) = w;
         }
   };
   if (mod == 256) {
@@ -297,8 +308,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
   wg_barrier();  // the whole tile is staged
   int8_t* o = reinterpret_cast<int8_t*>(out) + l * stride_o;
 #pragma unroll 4
-  for (int s4 = 0; s4 < 8; ++s4) {
-    const int rl = wave * 32 + s4 * 4 + (lane >> 4), cl = 16 * (lane & 15);
+  for (int s4 = 0; s4 < 64 / NW; ++s4) {
+    const int rl = wave * (BM / NW) + s4 * 4 + (lane >> 4), cl = 16 * (lane & 15);
     const int64_t row = row0 + rl, col = col0 + cl;
     const int8_t* srcp = tile + rl * kOutPitch + cl;
     const uint2 lo = *reinterpret_cast<const uint2*>(srcp);
@@ -335,13 +346,14 @@ int launch_gemm_i8(int64_t m, int64_t n, int64_t kp, int r, const int8_t* pa, in
   const int64_t vbytes = 16;
   const int vec_out = (reinterpret_cast<uintptr_t>(out) % vbytes) == 0 &&
                       (ldo * elem) % vbytes == 0 && (stride_o * elem) % vbytes == 0;
+  constexpr int NW = kWavesDefault;
   if (epilogue == kEpiProducts)
-    hipLaunchKernelGGL(gemm_i8_kernel<kEpiProducts>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       s, m, n, kp, pa, stride_a, pb, stride_b, out, ldo, stride_o, tiles_m,
+    hipLaunchKernelGGL((gemm_i8_kernel<kEpiProducts, NW>), dim3((unsigned)blocks), dim3(64 * NW),
+                       0, s, m, n, kp, pa, stride_a, pb, stride_b, out, ldo, stride_o, tiles_m,
                        tiles_n, E, vec_out);
   else
-    hipLaunchKernelGGL(gemm_i8_kernel<kEpiResidues>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       s, m, n, kp, pa, stride_a, pb, stride_b, out, ldo, stride_o, tiles_m,
+    hipLaunchKernelGGL((gemm_i8_kernel<kEpiResidues, NW>), dim3((unsigned)blocks), dim3(64 * NW),
+                       0, s, m, n, kp, pa, stride_a, pb, stride_b, out, ldo, stride_o, tiles_m,
                        tiles_n, E, vec_out);
   return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
 }
