@@ -12,6 +12,13 @@ Readings of what the pages leave open (see also ``oracle.rns``):
   set by the max rule e_i = P_A - 1 - ilogb(max_h |a_ih|) (0 for an all-zero row),
   so that 2^(P_A-1) <= max_h |a_ih| 2^e_i < 2^P_A.  A row or column holding Inf or NaN
   gets the exponent NONFINITE and its residues are 0; the outputs it touches are NaN.
+* Norm rule (optional, ``scaling="norm"``): e_i = alpha_A - 1 - E_i with E_i an upper
+  bound of floor(log2 ||a_i||_2): T = ilogb(max_h |a_ih|), s = sum_h (a_ih 2^-T)^2 in
+  float64 (any order: its relative error is below 2^-35 for k <= 2^17), u = ilogb(RN(s
+  (1 + 2^-32))), E_i = T + floor(u/2).  Then 2^e_i ||a_i||_2 < 2^alpha_A, and with the
+  norm budget of ``rns.scaling_bits_norm`` the CRT lift stays exact (Cauchy-Schwarz).
+  The bound follows each line's 2-norm instead of k times its largest entry, so lines
+  with a few large entries keep more bits of the rest.
 * Rounding: a'_ih = RNE(a_ih 2^e_i), round half to even, held as an exact integer
   (it may be wider than 53 bits).
 * Output: C_ij = RN(X_ij 2^-(e_i + f_j)), one round-to-nearest-even of the exact value,
@@ -49,6 +56,57 @@ def scale_exponents(x: np.ndarray, p: int, axis: int) -> np.ndarray:
     _, ex = np.frexp(np.where(finite, t, 0.0))  # t = frac * 2^ex, ilogb(t) = ex - 1
     e = np.where(t > 0, p - ex.astype(np.int64), 0)
     return np.where(finite, e, NONFINITE).astype(np.int64)
+
+
+def scale_exponents_norm(x: np.ndarray, alpha: int, axis: int) -> np.ndarray:
+    """Per-row (axis 0) or per-column (axis 1) exponents by the norm rule: int64 e with
+    2^e ||x_line||_2 < 2^alpha; 0 for an all-zero line, NONFINITE for a line holding Inf
+    or NaN."""
+    x = np.asarray(x, dtype=np.float64)
+    lines = x if axis == 0 else x.T
+    out = np.empty(lines.shape[0], dtype=np.int64)
+    for i, row in enumerate(lines):
+        if not np.all(np.isfinite(row)):
+            out[i] = NONFINITE
+            continue
+        t = float(np.max(np.abs(row))) if row.size else 0.0
+        if t == 0.0:
+            out[i] = 0
+            continue
+        big_t = math.frexp(t)[1] - 1                      # ilogb(max |x|)
+        scaled = np.ldexp(row, -big_t)
+        s = float(np.sum(scaled * scaled))
+        u = math.frexp(s * (1.0 + 2.0**-32))[1] - 1        # ilogb
+        out[i] = alpha - 1 - (big_t + u // 2)
+    return out
+
+
+def exponents(x: np.ndarray, r: int, k: int, axis: int, operand: str,
+              scaling: str = "max") -> np.ndarray:
+    """Exponents of A's rows (operand "a") or B's columns (operand "b") by the given
+    scaling rule, with the matching bit budget for r moduli and dot length k."""
+    if scaling == "max":
+        pa, pb = rns.scaling_bits(r, k)
+        return scale_exponents(x, pa if operand == "a" else pb, axis)
+    if scaling == "norm":
+        aa, ab = rns.scaling_bits_norm(r, k)
+        return scale_exponents_norm(x, aa if operand == "a" else ab, axis)
+    raise ValueError(f"unknown scaling {scaling!r}")
+
+
+def exact_sum_bound_ok(a: np.ndarray, b: np.ndarray, e, f, r: int) -> bool:
+    """Whether sum_h |a'_ih| |b'_hj| <= (M-1)/2 for every output, in exact integers (the
+    condition for the CRT lift to recover every dot product); small inputs only."""
+    big_m, _ = rns.crt_basis(r)
+    half = (big_m - 1) // 2
+    m, k = a.shape
+    n = b.shape[1]
+    ai = [[abs(scaled_integer(float(a[i, h]), int(e[i]))) if e[i] != NONFINITE else 0
+           for h in range(k)] for i in range(m)]
+    bj = [[abs(scaled_integer(float(b[h, j]), int(f[j]))) if f[j] != NONFINITE else 0
+           for h in range(k)] for j in range(n)]
+    return all(sum(x * y for x, y in zip(ai[i], bj[j])) <= half
+               for i in range(m) for j in range(n))
 
 
 # --------------------------------------------------------------------------- step 2
@@ -160,19 +218,24 @@ def reconstruct(products: np.ndarray, r: int, e: np.ndarray, f: np.ndarray) -> n
 
 
 # --------------------------------------------------------------------------- pipelines
-def dgemm(a: np.ndarray, b: np.ndarray, r: int, rows=None, cols=None) -> np.ndarray:
+def dgemm(a: np.ndarray, b: np.ndarray, r: int, rows=None, cols=None,
+          scaling: str = "max", exps=None) -> np.ndarray:
     """Emulated C = A B (A m x k, B k x n), optionally only rows x cols of C.
 
     Exponents always come from the full rows of A and full columns of B, so a sampled
-    block equals the same block of the full product."""
+    block equals the same block of the full product.  ``exps`` = (e, f) supplies the
+    exponents of the selected rows and columns instead (they must satisfy the bound of
+    the rule; ``exact_sum_bound_ok`` checks it)."""
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
     k = a.shape[1]
-    pa, pb = rns.scaling_bits(r, k)
     rows = np.arange(a.shape[0]) if rows is None else np.asarray(rows)
     cols = np.arange(b.shape[1]) if cols is None else np.asarray(cols)
-    e = scale_exponents(a[rows], pa, axis=0)
-    f = scale_exponents(b[:, cols], pb, axis=1)
+    if exps is None:
+        e = exponents(a[rows], r, k, 0, "a", scaling)
+        f = exponents(b[:, cols], r, k, 1, "b", scaling)
+    else:
+        e, f = (np.asarray(v, dtype=np.int64) for v in exps)
     pla = residue_planes(a[rows], e, r, axis=0)
     plb = residue_planes(b[:, cols], f, r, axis=1)
     prods = modular_products(pla, plb)
@@ -185,16 +248,16 @@ def dgemv(a: np.ndarray, x: np.ndarray, r: int, rows=None) -> np.ndarray:
     return dgemm(a, x, r, rows=rows)
 
 
-def exact_scaled_product(a: np.ndarray, b: np.ndarray, r: int) -> np.ndarray:
+def exact_scaled_product(a: np.ndarray, b: np.ndarray, r: int,
+                         scaling: str = "max") -> np.ndarray:
     """The plain definition without residues, for tiny inputs: RN(2^-(e_i+f_j)
     sum_h a'_ih b'_hj) with the sum taken in Python integers."""
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
     m, k = a.shape
     n = b.shape[1]
-    pa, pb = rns.scaling_bits(r, k)
-    e = scale_exponents(a, pa, axis=0)
-    f = scale_exponents(b, pb, axis=1)
+    e = exponents(a, r, k, 0, "a", scaling)
+    f = exponents(b, r, k, 1, "b", scaling)
     ai = [[scaled_integer(float(a[i, h]), int(e[i])) for h in range(k)] for i in range(m)]
     bi = [[scaled_integer(float(b[h, j]), int(f[j])) for h in range(k)] for j in range(n)]
     out = np.empty((m, n))

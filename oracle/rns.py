@@ -16,6 +16,13 @@ name neither the moduli nor the reconstruction formula.  Readings taken here:
 * Bit budget: Q = floor(log2((M-1)/2)), beta = Q - ceil(log2 k), P_A = floor(beta/2),
   P_B = beta - P_A.  With |a'| <= 2^P_A and |b'| <= 2^P_B every exact dot product of
   length k satisfies sum |a'||b'| <= 2^Q <= (M-1)/2, so the CRT lift recovers it exactly.
+* Norm budget (the tighter row/column scaling): widths (alpha_A, alpha_B) for scaled
+  rows and columns whose 2-norms stay below 2^alpha_A and 2^alpha_B; rounding each of
+  the k entries moves a 2-norm by at most sqrt(k)/2, so by Cauchy-Schwarz
+  sum |a'||b'| < (2^alpha_A + sqrt(k)/2)(2^alpha_B + sqrt(k)/2), which is kept at or
+  below (M-1)/2.  alpha_A + alpha_B starts at Q - 1, each at most 76 (scaled integers
+  then stay below 2^77, as they do under the max rule for r = 20 and k = 1), and the
+  larger is lowered until the inequality holds exactly.
 """
 from __future__ import annotations
 
@@ -83,6 +90,35 @@ def scaling_bits(r: int, k: int) -> tuple[int, int]:
         raise ValueError(f"r={r} gives no bit budget for k={k}")
     pa = beta // 2
     return pa, beta - pa
+
+
+NORM_ALPHA_CAP = 76
+
+
+def norm_bound_holds(alpha_a: int, alpha_b: int, k: int, big_m: int) -> bool:
+    """(2^alpha_a + sqrt(k)/2)(2^alpha_b + sqrt(k)/2) <= (M-1)/2, exactly: with
+    t = isqrt(k - 1) + 1 >= sqrt(k), check (2^(alpha_a+1) + t)(2^(alpha_b+1) + t)
+    <= 2 (M - 1)."""
+    t = math.isqrt(k - 1) + 1
+    return ((1 << (alpha_a + 1)) + t) * ((1 << (alpha_b + 1)) + t) <= 2 * (big_m - 1)
+
+
+def scaling_bits_norm(r: int, k: int) -> tuple[int, int]:
+    """(alpha_A, alpha_B) of the norm rule (see the module docstring)."""
+    if k < 1:
+        raise ValueError("k must be >= 1")
+    big_m, _ = crt_basis(r)
+    q = budget_q(r)
+    aa = min((q - 1) // 2, NORM_ALPHA_CAP)
+    ab = min(q - 1 - (q - 1) // 2, NORM_ALPHA_CAP)
+    while not norm_bound_holds(aa, ab, k, big_m):
+        if aa >= ab:
+            aa -= 1
+        else:
+            ab -= 1
+        if aa < 1 or ab < 1:
+            raise ValueError(f"r={r} gives no norm budget for k={k}")
+    return aa, ab
 
 
 def smod(x: int, m: int) -> int:

@@ -4,6 +4,7 @@ Each check is against a closed form or brute force, never against the oracle's o
 formula retyped."""
 import math
 import random
+from fractions import Fraction
 
 import pytest
 
@@ -104,3 +105,54 @@ def test_smod_exhaustive(m):
         seen.add(s)
     assert seen == set(range(lo, hi + 1))
     assert rns.smod(128, 256) == -128 and rns.smod(127, 256) == 127
+
+
+@pytest.mark.parametrize("r", [1, 2, 3, 5, 8, 12, 14, 16, 18, 19, 20])
+@pytest.mark.parametrize("k", [1, 2, 63, 64, 4096, 32768, 131071])
+def test_norm_budget_exact_and_maximal(r, k):
+    """(alpha_A, alpha_B) satisfy (2^aA + sqrt(k)/2)(2^aB + sqrt(k)/2) <= (M-1)/2 checked
+    with exact rationals, and raising either width (within the cap and Q - 1) breaks it."""
+    big_m, _ = rns.crt_basis(r)
+    q = rns.budget_q(r)
+    try:
+        aa, ab = rns.scaling_bits_norm(r, k)
+    except ValueError:
+        # no budget: even (1, 1) fails the exact inequality
+        assert not rns.norm_bound_holds(1, 1, k, big_m)
+        return
+    root_k = Fraction(math.isqrt(k)) if math.isqrt(k) ** 2 == k else None
+
+    def exact_ok(x, y):
+        # compare (2^x + s)(2^y + s) with (M-1)/2 for s = sqrt(k)/2, exactly: expand the
+        # product; the sqrt(k) term is bounded by rationals from above when k is not a square
+        s2 = Fraction(k, 4)
+        lhs_rational = Fraction(2) ** (x + y) + s2
+        coef = Fraction(2) ** x + Fraction(2) ** y          # multiplies sqrt(k)/2
+        rhs = Fraction(big_m - 1, 2)
+        if root_k is not None:
+            return lhs_rational + coef * root_k / 2 <= rhs
+        upper = Fraction(math.isqrt(k) + 1)                  # > sqrt(k)
+        lower = Fraction(math.isqrt(k))                      # < sqrt(k)
+        if lhs_rational + coef * upper / 2 <= rhs:
+            return True
+        if lhs_rational + coef * lower / 2 > rhs:
+            return False
+        return (rhs - lhs_rational) ** 2 * 4 >= coef ** 2 * k  # exact squared comparison
+    assert exact_ok(aa, ab)
+    assert aa + ab <= q - 1 and aa <= rns.NORM_ALPHA_CAP and ab <= rns.NORM_ALPHA_CAP
+    for x, y in ((aa + 1, ab), (aa, ab + 1)):
+        if x + y <= q - 1 and max(x, y) <= rns.NORM_ALPHA_CAP:
+            assert not rns.norm_bound_holds(x, y, k, big_m)
+
+
+def test_norm_budget_never_below_max_rule():
+    for r in range(2, 21):
+        for k in (64, 4096, 8192, 32768):
+            try:
+                pa, pb = rns.scaling_bits(r, k)
+            except ValueError:
+                continue
+            aa, ab = rns.scaling_bits_norm(r, k)
+            # a row with every |entry| equal makes ||a'||_2 = sqrt(k) max|a'|: the norm rule
+            # then keeps floor(aA - log2 sqrt k) bits, no fewer than the max rule's P_A - 1
+            assert aa + ab >= pa + pb
