@@ -58,6 +58,17 @@ def scale_exponents(x: np.ndarray, p: int, axis: int) -> np.ndarray:
     return np.where(finite, e, NONFINITE).astype(np.int64)
 
 
+def norm_bracket(row: np.ndarray) -> tuple[int, float]:
+    """(T, s_up) for a finite, nonzero line: T = ilogb(max |x|) and s_up =
+    RN(s (1 + 2^-32)) with s = sum (x 2^-T)^2 in float64, an upper bound of the exact
+    sum of squares of x 2^-T whatever order s is summed in."""
+    t = float(np.max(np.abs(row)))
+    big_t = math.frexp(t)[1] - 1
+    scaled = np.ldexp(row, -big_t)
+    s = float(np.sum(scaled * scaled))
+    return big_t, s * (1.0 + 2.0**-32)
+
+
 def scale_exponents_norm(x: np.ndarray, alpha: int, axis: int) -> np.ndarray:
     """Per-row (axis 0) or per-column (axis 1) exponents by the norm rule: int64 e with
     2^e ||x_line||_2 < 2^alpha; 0 for an all-zero line, NONFINITE for a line holding Inf
@@ -69,14 +80,11 @@ def scale_exponents_norm(x: np.ndarray, alpha: int, axis: int) -> np.ndarray:
         if not np.all(np.isfinite(row)):
             out[i] = NONFINITE
             continue
-        t = float(np.max(np.abs(row))) if row.size else 0.0
-        if t == 0.0:
+        if not row.size or float(np.max(np.abs(row))) == 0.0:
             out[i] = 0
             continue
-        big_t = math.frexp(t)[1] - 1                      # ilogb(max |x|)
-        scaled = np.ldexp(row, -big_t)
-        s = float(np.sum(scaled * scaled))
-        u = math.frexp(s * (1.0 + 2.0**-32))[1] - 1        # ilogb
+        big_t, s_up = norm_bracket(row)
+        u = math.frexp(s_up)[1] - 1                        # ilogb(s_up)
         out[i] = alpha - 1 - (big_t + u // 2)
     return out
 

@@ -191,9 +191,28 @@ def _exact_norm2(row):
     return sum(Fraction(float(v)) ** 2 for v in row)
 
 
+def test_norm_bracket_bounds_the_exact_sum():
+    """s_up >= the exact sum of squares of x 2^-T on rows mixing large and tiny entries
+    (float summation alone falls below the exact sum on about half of them)."""
+    rng = np.random.default_rng(21)
+    below = 0
+    for trial in range(300):
+        k = int(rng.integers(2, 400))
+        row = ozk_inputs.phi_matrix(rng, (1, k), float(rng.uniform(0.1, 6.0)))[0]
+        if trial % 3 == 0:
+            row[rng.integers(k)] = 2.0 - 2.0**-52     # square just below 4
+        big_t, s_up = ozaki2.norm_bracket(row)
+        exact = sum((Fraction(float(v)) * Fraction(2) ** -big_t) ** 2 for v in row)
+        assert Fraction(s_up) >= exact
+        scaled = np.ldexp(row, -big_t)
+        below += Fraction(float(np.sum(scaled * scaled))) < exact
+    assert below > 30    # the safety factor is doing work on this data
+
+
 def test_norm_exponents_invariant():
-    """2^(aA-2) <= 2^e ||a||_2 < 2^aA with exact rationals (the rule never overshoots and
-    loses at most two bits to its power-of-two bracket)."""
+    """2^(aA-1) <= 2^e ||a||_2 < 2^aA with exact rationals (the rule never overshoots and
+    loses at most one bit to its power-of-two bracket), except that a sum of squares
+    within 2^-30 below a power of two may lose one more."""
     rng = np.random.default_rng(12)
     x = ozk_inputs.phi_matrix(rng, (40, 33), 4.0)
     x[3] = 0.0
@@ -212,6 +231,12 @@ def test_norm_exponents_invariant():
             scaled2 = n2 * Fraction(4) ** int(e[i])
             assert scaled2 < Fraction(4) ** alpha
             assert scaled2 >= Fraction(4) ** (alpha - 2)
+            big_t = math.frexp(float(np.max(np.abs(x[i]))))[1] - 1
+            s_exact = n2 * Fraction(4) ** -big_t
+            j = s_exact.numerator.bit_length() - s_exact.denominator.bit_length() + 1
+            near = Fraction(2) ** j * (1 - Fraction(2) ** -30) <= s_exact < Fraction(2) ** j
+            if not near:
+                assert scaled2 >= Fraction(4) ** (alpha - 1)
         f = ozaki2.scale_exponents_norm(x.T, alpha, axis=1)
         np.testing.assert_array_equal(e, f)
 
