@@ -15,8 +15,9 @@ Also reported on the same JSON line:
                 (made by `--counters` under two `rocprofv3 --pmc` passes, then
                 `--traffic-summary FETCH_DIR WRITE_DIR`).
   cpu_baseline  the CPU oracle (numpy, one BLAS thread) on 8 full output rows.
-  extras        native fp64 DGEMM (torch.matmul), the r sweep 12..18, deconstruction HBM
-                GB/s, the GEMV and FP4-limb engines when built.
+  extras        native fp64 DGEMM (torch.matmul), the r sweep 12..18, the norm scaling
+                rule against the max rule (time and distance to native fp64 at r = 12, 14,
+                16), deconstruction HBM GB/s, the GEMV and FP4-limb engines when built.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--r 16] [--no-cpu-baseline]
        python bench.py --counters            (launches only, for rocprofv3 --pmc)
@@ -639,6 +640,24 @@ def main() -> int:
                           "tflops": round(2.0 * M * N * K / ms / 1e9, 2)})
             del wsr
         extras["r_sweep"] = sweep
+        # Norm (Cauchy-Schwarz) scaling rule against the max rule on the same operands:
+        # step time and normwise distance to the native fp64 product.
+        norm_rows = []
+        ref_n = torch.linalg.norm(ref)
+        wsn = torch.empty(ozk.ozk_dgemm_workspace_size(M, N, K, 16), dtype=torch.uint8,
+                          device=dev)
+        for rr in (12, 14, 16):
+            row = {"r": rr}
+            for rule in ("max", "norm"):
+                f = lambda: ozk.ozk_dgemm_ex(da, db, rr, rule, out=out, workspace=wsn)
+                f()
+                row[f"ms_{rule}"] = round(_time_events(f, reps, stream), 4)
+                row[f"rel_vs_native_{rule}"] = float(torch.linalg.norm(out - ref) / ref_n)
+            row["widths_max"] = ozk.ozk_scaling_bits_ex(rr, K, "max")
+            row["widths_norm"] = ozk.ozk_scaling_bits_ex(rr, K, "norm")
+            norm_rows.append(row)
+        extras["norm_rule"] = norm_rows
+        del wsn
         dec = lambda: ozk.ozk_deconstruct(da, 0, r, planes=planes_a, exps=exps_a)
         dec()
         dec_ms = _time_events(dec, reps, stream)

@@ -16,8 +16,10 @@ import torch
 
 __all__ = [
     "LIB_PATH", "OzkError", "library",
-    "ozk_version", "ozk_moduli", "ozk_scaling_bits", "ozk_planes_ld",
-    "ozk_deconstruct", "ozk_modular_products", "ozk_modular_residues", "ozk_reconstruct", "ozk_dgemm", "ozk_dgemv",
+    "ozk_version", "ozk_moduli", "ozk_scaling_bits", "ozk_scaling_bits_ex", "ozk_planes_ld",
+    "ozk_deconstruct", "ozk_deconstruct_ex", "ozk_modular_products", "ozk_modular_residues",
+    "ozk_reconstruct", "ozk_dgemm", "ozk_dgemm_ex", "ozk_dgemv",
+    "OZK_SCALING_MAX", "OZK_SCALING_NORM",
     "ozk_fp4limb_pack", "ozk_fp4limb_products", "ozk_int8gemm_fp4limb",
     "ozk_dgemm_workspace_size", "ozk_dgemv_workspace_size",
     "ozk_int8gemm_fp4limb_workspace_size", "ozk_deconstruct_workspace_size",
@@ -38,6 +40,7 @@ _SIGNATURES = {
     "ozk_status_string": (ctypes.c_char_p, [_int]),
     "ozk_moduli": (_int, [_int, _ptr]),
     "ozk_scaling_bits": (_int, [_int, _i64, _ptr, _ptr]),
+    "ozk_scaling_bits_ex": (_int, [_int, _i64, _int, _ptr, _ptr]),
     "ozk_planes_ld": (_i64, [_i64]),
     "ozk_deconstruct_workspace_size": (_int, [_i64, _i64, _int, _ptr]),
     "ozk_deconstruct": (_int, [_ptr, _i64, _i64, _i64, _int, _int, _i64, _ptr, _i64, _i64, _ptr,
@@ -47,6 +50,10 @@ _SIGNATURES = {
     "ozk_modular_residues": (_int, [_i64, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64,
                                     _i64, _ptr]),
     "ozk_reconstruct": (_int, [_i64, _i64, _int, _ptr, _i64, _i64, _ptr, _ptr, _ptr, _i64, _ptr]),
+    "ozk_deconstruct_ex": (_int, [_ptr, _i64, _i64, _i64, _int, _int, _i64, _int, _ptr, _i64,
+                                  _i64, _ptr, _ptr, _size, _ptr]),
+    "ozk_dgemm_ex": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
+                            _ptr, _size, _ptr]),
     "ozk_dgemm_workspace_size": (_int, [_i64, _i64, _i64, _int, _ptr]),
     "ozk_dgemm": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _ptr, _size,
                          _ptr]),
@@ -63,6 +70,18 @@ _SIGNATURES = {
 }
 
 _LIB = None
+
+OZK_SCALING_MAX = 0   # per-line maximum (the default of every entry point)
+OZK_SCALING_NORM = 1  # per-line 2-norm (Cauchy-Schwarz)
+
+
+def _scaling(scaling) -> int:
+    names = {"max": OZK_SCALING_MAX, "norm": OZK_SCALING_NORM}
+    if isinstance(scaling, str):
+        if scaling not in names:
+            raise ValueError(f"unknown scaling rule {scaling!r}")
+        return names[scaling]
+    return int(scaling)
 
 
 class OzkError(RuntimeError):
@@ -141,6 +160,13 @@ def ozk_scaling_bits(r: int, k: int) -> tuple[int, int]:
     return pa.value, pb.value
 
 
+def ozk_scaling_bits_ex(r: int, k: int, scaling) -> tuple[int, int]:
+    """(P_A, P_B) for the max rule, (alpha_A, alpha_B) for the norm rule."""
+    pa, pb = ctypes.c_int32(), ctypes.c_int32()
+    _call("ozk_scaling_bits_ex", r, k, _scaling(scaling), ctypes.byref(pa), ctypes.byref(pb))
+    return pa.value, pb.value
+
+
 def ozk_planes_ld(k: int) -> int:
     return library().ozk_planes_ld(k)
 
@@ -168,10 +194,8 @@ def ozk_int8gemm_fp4limb_workspace_size(m: int, n: int, k: int) -> int:
 
 
 # ----------------------------------------------------------------------------- operations
-def ozk_deconstruct(x: torch.Tensor, axis: int, r: int, k_budget: int | None = None,
-                    planes: torch.Tensor | None = None, exps: torch.Tensor | None = None,
-                    workspace: torch.Tensor | None = None, stream=None):
-    """Residue planes [r][lines][ldp] (int8) and exponents [lines] (int32) of x."""
+def _deconstruct(name: str, extra: tuple, x: torch.Tensor, axis: int, r: int,
+                 k_budget, planes, exps, workspace, stream):
     _check(x, torch.float64, "x")
     rows, cols = x.shape
     kdim = cols if axis == 0 else rows
@@ -184,11 +208,28 @@ def ozk_deconstruct(x: torch.Tensor, axis: int, r: int, k_budget: int | None = N
     ws_bytes = ozk_deconstruct_workspace_size(rows, cols, axis)
     if workspace is None and ws_bytes > 0:
         workspace = _workspace(ws_bytes, x.device)
-    _call("ozk_deconstruct", _dev_ptr(x), rows, cols, _ld(x), axis, r,
-          k_budget if k_budget is not None else kdim, _dev_ptr(planes), planes.shape[-1],
-          planes.stride(0), _dev_ptr(exps), _dev_ptr(workspace),
+    _call(name, _dev_ptr(x), rows, cols, _ld(x), axis, r,
+          k_budget if k_budget is not None else kdim, *extra, _dev_ptr(planes),
+          planes.shape[-1], planes.stride(0), _dev_ptr(exps), _dev_ptr(workspace),
           0 if workspace is None else workspace.numel(), _stream(stream))
     return planes, exps
+
+
+def ozk_deconstruct(x: torch.Tensor, axis: int, r: int, k_budget: int | None = None,
+                    planes: torch.Tensor | None = None, exps: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None, stream=None):
+    """Residue planes [r][lines][ldp] (int8) and exponents [lines] (int32) of x."""
+    return _deconstruct("ozk_deconstruct", (), x, axis, r, k_budget, planes, exps, workspace,
+                        stream)
+
+
+def ozk_deconstruct_ex(x: torch.Tensor, axis: int, r: int, scaling="max",
+                       k_budget: int | None = None, planes: torch.Tensor | None = None,
+                       exps: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                       stream=None):
+    """ozk_deconstruct with a scaling rule ("max"/"norm" or OZK_SCALING_*)."""
+    return _deconstruct("ozk_deconstruct_ex", (_scaling(scaling),), x, axis, r, k_budget,
+                        planes, exps, workspace, stream)
 
 
 def ozk_modular_products(planes_a: torch.Tensor, planes_b: torch.Tensor, r: int | None = None,
@@ -239,9 +280,7 @@ def ozk_reconstruct(products: torch.Tensor, exps_a: torch.Tensor, exps_b: torch.
     return out
 
 
-def ozk_dgemm(a: torch.Tensor, b: torch.Tensor, r: int, out: torch.Tensor | None = None,
-              workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Emulated fp64 C = A B through r moduli."""
+def _dgemm_args(a, b, r, out, workspace):
     _check(a, torch.float64, "A")
     _check(b, torch.float64, "B")
     m, k = a.shape
@@ -252,8 +291,26 @@ def ozk_dgemm(a: torch.Tensor, b: torch.Tensor, r: int, out: torch.Tensor | None
         out = torch.empty((m, n), dtype=torch.float64, device=a.device)
     if workspace is None:
         workspace = _workspace(ozk_dgemm_workspace_size(m, n, k, r), a.device)
+    return m, n, k, out, workspace
+
+
+def ozk_dgemm(a: torch.Tensor, b: torch.Tensor, r: int, out: torch.Tensor | None = None,
+              workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Emulated fp64 C = A B through r moduli."""
+    m, n, k, out, workspace = _dgemm_args(a, b, r, out, workspace)
     _call("ozk_dgemm", m, n, k, _dev_ptr(a), _ld(a), _dev_ptr(b), _ld(b), _dev_ptr(out), _ld(out),
           r, _dev_ptr(workspace), workspace.numel(), _stream(stream))
+    return out
+
+
+def ozk_dgemm_ex(a: torch.Tensor, b: torch.Tensor, r: int, scaling="max",
+                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """ozk_dgemm with a scaling rule ("max"/"norm" or OZK_SCALING_*)."""
+    m, n, k, out, workspace = _dgemm_args(a, b, r, out, workspace)
+    _call("ozk_dgemm_ex", m, n, k, _dev_ptr(a), _ld(a), _dev_ptr(b), _ld(b), _dev_ptr(out),
+          _ld(out), r, _scaling(scaling), _dev_ptr(workspace), workspace.numel(),
+          _stream(stream))
     return out
 
 

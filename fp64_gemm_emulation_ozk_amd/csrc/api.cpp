@@ -23,12 +23,23 @@ struct Carver {
   }
 };
 
+// Scratch of one operand's deconstruction beyond its planes and exponents: the line
+// maxima of the max rule, or the chunk partials of the norm rule; the larger of the two,
+// so that one workspace query serves both rules.  None for rows the fused kernel takes.
+size_t deconstruct_scratch(int64_t rows, int64_t cols, int axis) {
+  if (axis == 0 && rows_fused_supported(cols)) return 0;
+  const int64_t lines = axis == 0 ? rows : cols;
+  const size_t maxb = align256((size_t)lines * 8);
+  const size_t part = 2 * align256((size_t)lines * norm_chunks(rows, cols, axis) * 8);
+  return maxb > part ? maxb : part;
+}
+
 struct DgemmLayout {
   int64_t kp;
-  size_t planes_a, planes_b, residues, exps_a, exps_b, max_a, max_b;
+  size_t planes_a, planes_b, residues, exps_a, exps_b, scr_a, scr_b;
   size_t total() const {
     return align256(planes_a) + align256(planes_b) + align256(residues) + align256(exps_a) +
-           align256(exps_b) + align256(max_a) + align256(max_b);
+           align256(exps_b) + align256(scr_a) + align256(scr_b);
   }
 };
 
@@ -40,26 +51,39 @@ DgemmLayout dgemm_layout(int64_t m, int64_t n, int64_t k, int r) {
   L.residues = (size_t)r * m * n;
   L.exps_a = (size_t)m * 4;
   L.exps_b = (size_t)n * 4;
-  L.max_a = rows_fused_supported(k) ? 0 : (size_t)m * 8;
-  L.max_b = (size_t)n * 8;
+  L.scr_a = deconstruct_scratch(m, k, 0);
+  L.scr_b = deconstruct_scratch(k, n, 1);
   return L;
 }
 
 int check_r(int r) { return (r >= 1 && r <= kMaxModuli) ? OZK_OK : OZK_EINVAL; }
 
-// Deconstruct one operand (axis 0: per-row, axis 1: per-column) into planes.
+// Deconstruct one operand (axis 0: per-row, axis 1: per-column) into planes by either
+// scaling rule; width is P (max rule) or alpha (norm rule) of this operand and scratch
+// holds deconstruct_scratch(rows, cols, axis) bytes.
 int deconstruct_impl(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis, int r,
-                     int p_bits, int8_t* planes, int64_t ldp, int64_t plane_stride,
-                     int32_t* exps, uint64_t* maxbits, hipStream_t s) {
+                     int scaling, int width, int8_t* planes, int64_t ldp, int64_t plane_stride,
+                     int32_t* exps, void* scratch, hipStream_t s) {
   int st;
   if (axis == 0 && rows_fused_supported(cols))
-    return launch_residues_rows_fused(x, rows, cols, ldx, r, p_bits, planes, ldp, plane_stride,
-                                      exps, s);
+    return launch_residues_rows_fused(x, rows, cols, ldx, r, scaling, width, planes, ldp,
+                                      plane_stride, exps, s);
   const int64_t lines = axis == 0 ? rows : cols;
+  if (scaling == OZK_SCALING_NORM) {
+    Carver cv(scratch);
+    const size_t n = (size_t)lines * norm_chunks(rows, cols, axis) * 8;
+    uint64_t* pmax = static_cast<uint64_t*>(cv.take(n));
+    double* ps = static_cast<double*>(cv.take(n));
+    if ((st = launch_norm_exps(x, rows, cols, ldx, axis, width, pmax, ps, exps, s)) != OZK_OK)
+      return st;
+    return launch_residues(x, rows, cols, ldx, axis, r, width, nullptr, planes, ldp,
+                           plane_stride, exps, 1, s);
+  }
+  uint64_t* maxbits = static_cast<uint64_t*>(scratch);
   if ((st = launch_fill_u64(maxbits, lines, 0, s)) != OZK_OK) return st;
   if ((st = launch_absmax(x, rows, cols, ldx, axis, maxbits, s)) != OZK_OK) return st;
-  return launch_residues(x, rows, cols, ldx, axis, r, p_bits, maxbits, planes, ldp, plane_stride,
-                         exps, s);
+  return launch_residues(x, rows, cols, ldx, axis, r, width, maxbits, planes, ldp, plane_stride,
+                         exps, 0, s);
 }
 
 }  // namespace
@@ -91,39 +115,53 @@ int ozk_scaling_bits(int r, int64_t k, int32_t* pa, int32_t* pb) {
   return OZK_OK;
 }
 
+int ozk_scaling_bits_ex(int r, int64_t k, int scaling, int32_t* pa, int32_t* pb) {
+  int a = 0, b = 0;
+  int st = scaling_widths(scaling, r, k, &a, &b);
+  if (st != OZK_OK) return st;
+  if (pa) *pa = a;
+  if (pb) *pb = b;
+  return OZK_OK;
+}
+
 int64_t ozk_planes_ld(int64_t k) { return k <= 0 ? 0 : round_up(k, kPlaneK); }
 
 int ozk_deconstruct_workspace_size(int64_t rows, int64_t cols, int axis, size_t* bytes) {
   if (!bytes || rows < 0 || cols < 0 || (axis != 0 && axis != 1)) return OZK_EINVAL;
-  if (axis == 0)
-    *bytes = rows_fused_supported(cols) ? 0 : align256((size_t)rows * 8);
-  else
-    *bytes = align256((size_t)cols * 8);
+  *bytes = deconstruct_scratch(rows, cols, axis);
   return OZK_OK;
 }
 
-int ozk_deconstruct(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis, int r,
-                    int64_t k_budget, int8_t* planes, int64_t ldp, int64_t plane_stride,
-                    int32_t* exps, void* workspace, size_t workspace_bytes, void* stream) {
+int ozk_deconstruct_ex(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                       int r, int64_t k_budget, int scaling, int8_t* planes, int64_t ldp,
+                       int64_t plane_stride, int32_t* exps, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   if (axis != 0 && axis != 1) return OZK_EINVAL;
+  if (scaling != OZK_SCALING_MAX && scaling != OZK_SCALING_NORM) return OZK_EINVAL;
   if (check_r(r) != OZK_OK) return OZK_EINVAL;
   if (rows < 0 || cols < 0 || ldx < (cols > 0 ? cols : 1)) return OZK_EINVAL;
   const int64_t K = axis == 0 ? cols : rows;
   const int64_t lines = axis == 0 ? rows : cols;
   if (ldp < K || ldp % kPlaneK != 0 || ldp <= 0) return OZK_EINVAL;
   if (plane_stride < lines * ldp || plane_stride % kPlaneK != 0) return OZK_EINVAL;
-  int pa = 0, pb = 0;
-  int st = scaling_bits(r, k_budget, &pa, &pb);
+  int wa = 0, wb = 0;
+  int st = scaling_widths(scaling, r, k_budget, &wa, &wb);
   if (st != OZK_OK) return st;
   if (lines == 0) return OZK_OK;
   if (!planes || !exps || (K > 0 && !x)) return OZK_EINVAL;
   if (!aligned(planes, 16)) return OZK_EINVAL;
-  size_t need = 0;
-  ozk_deconstruct_workspace_size(rows, cols, axis, &need);
+  const size_t need = deconstruct_scratch(rows, cols, axis);
   if (need > workspace_bytes || (need > 0 && !workspace)) return OZK_EWORKSPACE;
-  return deconstruct_impl(x, rows, cols, ldx, axis, r, axis == 0 ? pa : pb, planes, ldp,
-                          plane_stride, exps, static_cast<uint64_t*>(workspace),
-                          as_stream(stream));
+  if (need > 0 && !aligned(workspace, 8)) return OZK_EINVAL;
+  return deconstruct_impl(x, rows, cols, ldx, axis, r, scaling, axis == 0 ? wa : wb, planes,
+                          ldp, plane_stride, exps, workspace, as_stream(stream));
+}
+
+int ozk_deconstruct(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis, int r,
+                    int64_t k_budget, int8_t* planes, int64_t ldp, int64_t plane_stride,
+                    int32_t* exps, void* workspace, size_t workspace_bytes, void* stream) {
+  return ozk_deconstruct_ex(x, rows, cols, ldx, axis, r, k_budget, OZK_SCALING_MAX, planes, ldp,
+                            plane_stride, exps, workspace, workspace_bytes, stream);
 }
 
 int ozk_modular_products(int64_t m, int64_t n, int64_t kp, int r, const int8_t* pa,
@@ -176,15 +214,16 @@ int ozk_dgemm_workspace_size(int64_t m, int64_t n, int64_t k, int r, size_t* byt
   return OZK_OK;
 }
 
-int ozk_dgemm(int64_t m, int64_t n, int64_t k, const double* A, int64_t lda, const double* B,
-              int64_t ldb, double* C, int64_t ldc, int r, void* workspace,
-              size_t workspace_bytes, void* stream) {
+int ozk_dgemm_ex(int64_t m, int64_t n, int64_t k, const double* A, int64_t lda,
+                 const double* B, int64_t ldb, double* C, int64_t ldc, int r, int scaling,
+                 void* workspace, size_t workspace_bytes, void* stream) {
   if (check_r(r) != OZK_OK) return OZK_EINVAL;
+  if (scaling != OZK_SCALING_MAX && scaling != OZK_SCALING_NORM) return OZK_EINVAL;
   if (m < 0 || n < 0 || k < 1) return OZK_EINVAL;
   if (k > OZK_MAX_K) return OZK_ERANGE;
   if (lda < k || ldb < (n > 0 ? n : 1) || ldc < (n > 0 ? n : 1)) return OZK_EINVAL;
-  int pa = 0, pb = 0;
-  int st = scaling_bits(r, k, &pa, &pb);
+  int wa = 0, wb = 0;
+  int st = scaling_widths(scaling, r, k, &wa, &wb);
   if (st != OZK_OK) return st;
   if (m == 0 || n == 0) return OZK_OK;
   if (!A || !B || !C) return OZK_EINVAL;
@@ -198,18 +237,27 @@ int ozk_dgemm(int64_t m, int64_t n, int64_t k, const double* A, int64_t lda, con
   int8_t* residues = static_cast<int8_t*>(cv.take(L.residues));
   int32_t* exps_a = static_cast<int32_t*>(cv.take(L.exps_a));
   int32_t* exps_b = static_cast<int32_t*>(cv.take(L.exps_b));
-  uint64_t* max_a = static_cast<uint64_t*>(cv.take(L.max_a));
-  uint64_t* max_b = static_cast<uint64_t*>(cv.take(L.max_b));
+  void* scr_a = cv.take(L.scr_a);
+  void* scr_b = cv.take(L.scr_b);
   hipStream_t s = as_stream(stream);
   const int64_t kp = L.kp;
-  if ((st = deconstruct_impl(A, m, k, lda, 0, r, pa, planes_a, kp, m * kp, exps_a, max_a, s)))
+  if ((st = deconstruct_impl(A, m, k, lda, 0, r, scaling, wa, planes_a, kp, m * kp, exps_a,
+                             scr_a, s)))
     return st;
-  if ((st = deconstruct_impl(B, k, n, ldb, 1, r, pb, planes_b, kp, n * kp, exps_b, max_b, s)))
+  if ((st = deconstruct_impl(B, k, n, ldb, 1, r, scaling, wb, planes_b, kp, n * kp, exps_b,
+                             scr_b, s)))
     return st;
   if ((st = launch_gemm_i8(m, n, kp, r, planes_a, m * kp, planes_b, n * kp, residues, n, m * n,
                            kEpiResidues, s)))
     return st;
   return launch_crt(m, n, r, residues, 0, n, m * n, exps_a, exps_b, C, ldc, s);
+}
+
+int ozk_dgemm(int64_t m, int64_t n, int64_t k, const double* A, int64_t lda, const double* B,
+              int64_t ldb, double* C, int64_t ldc, int r, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  return ozk_dgemm_ex(m, n, k, A, lda, B, ldb, C, ldc, r, OZK_SCALING_MAX, workspace,
+                      workspace_bytes, stream);
 }
 
 }  // extern "C"
@@ -294,8 +342,8 @@ int ozk_dgemv(int64_t m, int64_t k, int64_t nrhs, const double* A, int64_t lda,
   int8_t* part = static_cast<int8_t*>(cv.take(L.part));
   hipStream_t s = as_stream(stream);
   const int64_t kp = L.kp;
-  if ((st = deconstruct_impl(X, k, nrhs, ldx, 1, r, pb, x_planes, kp, nrhs * kp, x_exps, x_max,
-                             s)))
+  if ((st = deconstruct_impl(X, k, nrhs, ldx, 1, r, OZK_SCALING_MAX, pb, x_planes, kp, nrhs * kp,
+                             x_exps, x_max, s)))
     return st;
   const int32_t* ea = A_exps;
   if (mode == 0) {

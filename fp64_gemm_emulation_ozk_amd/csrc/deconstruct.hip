@@ -11,7 +11,11 @@
 //                       per plane, 8 threads per 128-byte plane line (the transpose
 //                       happens in the store address)
 //   residues_rows_fused one workgroup per row: the row is held in registers, reduced
-//                       for its maximum, then turned into residues (one HBM read)
+//                       for its maximum (and, by the norm rule, for its scaled sum of
+//                       squares), then turned into residues (one HBM read)
+//   norm_partials_rows/cols  norm rule: per chunk of a line, its maximum and its sum of
+//                       squares scaled by that maximum's power of two
+//   exps_norm           norm rule: chunk partials combined in order, exponent per line
 #include "ozk_internal.h"
 #include "residue_math.h"
 
@@ -31,6 +35,12 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     uint64_t o = __shfl_xor(v, off, 64);
     v = umax64(v, o);
   }
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
 
@@ -131,14 +141,15 @@ __device__ __forceinline__ void load8(const double* __restrict__ xr, int64_t h0,
 }
 
 // Row residues with exponents from maxbits: grid (ldp / 2048 chunks, rows).
-template <bool kWide, bool kVec>
+// kGiven: the exponents are already in exps (norm rule); else the max rule from maxbits.
+template <bool kWide, bool kVec, bool kGiven>
 __global__ __launch_bounds__(256) void residues_rows_kernel(
     const double* __restrict__ x, int64_t cols, int64_t ldx, ResidueConsts K, int p_bits,
     const uint64_t* __restrict__ maxbits, int8_t* __restrict__ planes, int64_t ldp,
     int64_t plane_stride, int32_t* __restrict__ exps) {
   const int64_t row = blockIdx.y;
-  const int e = line_exponent(maxbits[row], p_bits);
-  if (blockIdx.x == 0 && threadIdx.x == 0) exps[row] = e;
+  const int e = kGiven ? exps[row] : line_exponent(maxbits[row], p_bits);
+  if (!kGiven && blockIdx.x == 0 && threadIdx.x == 0) exps[row] = e;
   const int64_t h0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
   if (h0 >= ldp) return;
   const double* xr = x + row * ldx;
@@ -153,7 +164,7 @@ __global__ __launch_bounds__(256) void residues_rows_kernel(
 // one whole 128-byte line of each plane row (16 bytes each), and each load instruction
 // reads 8 rows x 8 columns (the four waves of a block read the 32 columns of a row, so
 // every line is fetched once).
-template <bool kWide>
+template <bool kWide, bool kGiven>
 __global__ __launch_bounds__(256) void residues_cols_kernel(
     const double* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, ResidueConsts K,
     int p_bits, const uint64_t* __restrict__ maxbits, int8_t* __restrict__ planes,
@@ -162,8 +173,8 @@ __global__ __launch_bounds__(256) void residues_cols_kernel(
   if (col >= cols) return;
   const int64_t h0 = (int64_t)blockIdx.y * 128 + (threadIdx.x & 7) * 16;
   if (h0 >= ldp) return;  // ldp is a multiple of 64: the last block row may be half full
-  const int e = line_exponent(maxbits[col], p_bits);
-  if (blockIdx.y == 0 && (threadIdx.x & 7) == 0) exps[col] = e;
+  const int e = kGiven ? exps[col] : line_exponent(maxbits[col], p_bits);
+  if (!kGiven && blockIdx.y == 0 && (threadIdx.x & 7) == 0) exps[col] = e;
   double a[16];
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
@@ -174,9 +185,10 @@ __global__ __launch_bounds__(256) void residues_cols_kernel(
 }
 
 // One workgroup per row, the row in registers: kNT threads x kG groups of 8 elements.
-template <bool kWide, bool kVec, int kNT, int kG>
+// `width` is P of the max rule, or alpha of the norm rule (kNorm).
+template <bool kWide, bool kVec, int kNT, int kG, bool kNorm>
 __global__ __launch_bounds__(kNT) void residues_rows_fused_kernel(
-    const double* __restrict__ x, int64_t cols, int64_t ldx, ResidueConsts K, int p_bits,
+    const double* __restrict__ x, int64_t cols, int64_t ldx, ResidueConsts K, int width,
     int8_t* __restrict__ planes, int64_t ldp, int64_t plane_stride,
     int32_t* __restrict__ exps) {
   const int64_t row = blockIdx.x;
@@ -192,17 +204,48 @@ __global__ __launch_bounds__(kNT) void residues_rows_fused_kernel(
   }
   v = wave_max_u64(v);
   __shared__ uint64_t part[kNT / 64];
+  __shared__ double psum[kNT / 64];
   __shared__ int exp_shared;
+  __shared__ uint64_t max_shared;
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint64_t mx = 0;
     for (int w = 0; w < kNT / 64; ++w) mx = umax64(mx, part[w]);
-    int e = line_exponent(mx, p_bits);
-    exp_shared = e;
-    exps[row] = e;
+    if (kNorm) {
+      max_shared = mx;
+    } else {
+      int e = line_exponent(mx, width);
+      exp_shared = e;
+      exps[row] = e;
+    }
   }
   __syncthreads();
+  if (kNorm) {
+    // Sum of (x 2^-T)^2: per thread in element order, lanes by a fixed butterfly, waves
+    // in order (deterministic).
+    const uint64_t mx = max_shared;
+    const int t = line_ilogb(mx);
+    double ss = 0.0;
+#pragma unroll
+    for (int g = 0; g < kG; ++g)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const double y = __builtin_ldexp(a[g][u], -t);
+        ss = __builtin_fma(y, y, ss);
+      }
+    ss = wave_sum_f64(ss);
+    if ((threadIdx.x & 63) == 0) psum[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double s = 0.0;
+      for (int w = 0; w < kNT / 64; ++w) s += psum[w];
+      const int e = norm_exponent(mx, s, width);
+      exp_shared = e;
+      exps[row] = e;
+    }
+    __syncthreads();
+  }
   int e = exp_shared;
   const bool bad = e == INT32_MIN;
   if (bad) e = 0;
@@ -224,6 +267,99 @@ __global__ __launch_bounds__(kNT) void residues_rows_fused_kernel(
   }
 }
 
+// Norm rule outside the fused kernel.  The line is cut into chunks; each chunk writes
+// its own largest |x| (bit pattern) pmax and ps = sum of (x 2^-Tc)^2 with Tc = ilogb of
+// that maximum, in a fixed order.  exps_norm_kernel then takes T = ilogb of the line's
+// maximum and s = sum over chunks, in chunk order, of ps 2^(2 (Tc - T)): scaling by a
+// power of two is exact, so s is the line's scaled sum of squares in a fixed order
+// (terms that underflow are below 2^-1000 of s >= 1, far inside the bound's slack).
+// The line is read once for its exponent, as by the max rule.
+
+// Rows: grid (chunks of 2048 columns, rows); 256 threads x 8 elements,
+// written to pmax/ps[row * gridDim.x + chunk].
+__global__ __launch_bounds__(256) void norm_partials_rows_kernel(
+    const double* __restrict__ x, int64_t cols, int64_t ldx, uint64_t* __restrict__ pmax,
+    double* __restrict__ ps) {
+  const int64_t row = blockIdx.y;
+  const int64_t base = (int64_t)blockIdx.x * 2048;
+  const double* xr = x + row * ldx;
+  double a[8];
+  uint64_t v = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int64_t h = base + u * 256 + threadIdx.x;
+    a[u] = h < cols ? xr[h] : 0.0;
+    v = umax64(v, abs_bits(a[u]));
+  }
+  v = wave_max_u64(v);
+  __shared__ uint64_t wm[4];
+  __shared__ double ws[4];
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const uint64_t mx = umax64(umax64(wm[0], wm[1]), umax64(wm[2], wm[3]));
+  const int t = line_ilogb(mx);
+  double ss = 0.0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const double y = __builtin_ldexp(a[u], -t);
+    ss = __builtin_fma(y, y, ss);
+  }
+  ss = wave_sum_f64(ss);
+  if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int64_t i = row * gridDim.x + blockIdx.x;
+    pmax[i] = mx;
+    ps[i] = ((ws[0] + ws[1]) + ws[2]) + ws[3];
+  }
+}
+
+// Columns: grid (column blocks of 256, chunks of 32 rows); thread = column, its chunk
+// held in registers, written to pmax/ps[chunk * cols + col].
+__global__ __launch_bounds__(256) void norm_partials_cols_kernel(
+    const double* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+    uint64_t* __restrict__ pmax, double* __restrict__ ps) {
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (col >= cols) return;
+  const int64_t r0 = (int64_t)blockIdx.y * 32;
+  double a[32];
+  uint64_t v = 0;
+#pragma unroll
+  for (int u = 0; u < 32; ++u) {
+    a[u] = r0 + u < rows ? x[(r0 + u) * ldx + col] : 0.0;
+    v = umax64(v, abs_bits(a[u]));
+  }
+  const int t = line_ilogb(v);
+  double ss = 0.0;
+#pragma unroll
+  for (int u = 0; u < 32; ++u) {
+    const double y = __builtin_ldexp(a[u], -t);
+    ss = __builtin_fma(y, y, ss);
+  }
+  const int64_t i = (int64_t)blockIdx.y * cols + col;
+  pmax[i] = v;
+  ps[i] = ss;
+}
+
+// Per line: combine the chunk partials (maximum, then the rescaled sums in chunk order)
+// and write the norm-rule exponent.
+__global__ void exps_norm_kernel(const uint64_t* __restrict__ pmax,
+                                 const double* __restrict__ ps, int64_t lines, int64_t chunks,
+                                 int64_t stride_line, int64_t stride_chunk, int alpha,
+                                 int32_t* __restrict__ exps) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= lines) return;
+  uint64_t mx = 0;
+  for (int64_t c = 0; c < chunks; ++c) mx = umax64(mx, pmax[i * stride_line + c * stride_chunk]);
+  const int t = line_ilogb(mx);
+  double s = 0.0;
+  for (int64_t c = 0; c < chunks; ++c) {
+    const int64_t q = i * stride_line + c * stride_chunk;
+    s += __builtin_ldexp(ps[q], 2 * (line_ilogb(pmax[q]) - t));
+  }
+  exps[i] = norm_exponent(mx, s, alpha);
+}
+
 __global__ void exps_from_maxbits_kernel(const uint64_t* __restrict__ maxbits, int64_t n,
                                          int p_bits, int32_t* __restrict__ exps) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -232,16 +368,17 @@ __global__ void exps_from_maxbits_kernel(const uint64_t* __restrict__ maxbits, i
 
 template <bool kWide, int kNT, int kG>
 int launch_fused(const double* x, int64_t rows, int64_t cols, int64_t ldx,
-                 const ResidueConsts& K, int p_bits, int8_t* planes, int64_t ldp,
+                 const ResidueConsts& K, int norm, int width, int8_t* planes, int64_t ldp,
                  int64_t plane_stride, int32_t* exps, hipStream_t s) {
   const bool vec = (reinterpret_cast<uintptr_t>(x) & 15) == 0 && (ldx & 1) == 0;
-  if (vec)
-    hipLaunchKernelGGL((residues_rows_fused_kernel<kWide, true, kNT, kG>), dim3((unsigned)rows),
-                       dim3(kNT), 0, s, x, cols, ldx, K, p_bits, planes, ldp, plane_stride, exps);
-  else
-    hipLaunchKernelGGL((residues_rows_fused_kernel<kWide, false, kNT, kG>),
-                       dim3((unsigned)rows), dim3(kNT), 0, s, x, cols, ldx, K, p_bits, planes,
-                       ldp, plane_stride, exps);
+#define OZK_FUSED_LAUNCH(V, N)                                                              \
+  hipLaunchKernelGGL((residues_rows_fused_kernel<kWide, V, kNT, kG, N>), dim3((unsigned)rows), \
+                     dim3(kNT), 0, s, x, cols, ldx, K, width, planes, ldp, plane_stride, exps)
+  if (vec && norm) OZK_FUSED_LAUNCH(true, true);
+  else if (vec) OZK_FUSED_LAUNCH(true, false);
+  else if (norm) OZK_FUSED_LAUNCH(false, true);
+  else OZK_FUSED_LAUNCH(false, false);
+#undef OZK_FUSED_LAUNCH
   return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
 }
 
@@ -270,7 +407,7 @@ int launch_absmax(const double* x, int64_t rows, int64_t cols, int64_t ldx, int 
 
 int launch_residues(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis, int r,
                     int p_bits, const uint64_t* maxbits, int8_t* planes, int64_t ldp,
-                    int64_t plane_stride, int32_t* exps, hipStream_t s) {
+                    int64_t plane_stride, int32_t* exps, int given_exps, hipStream_t s) {
   const ResidueConsts& K = *residue_consts(r, p_bits);
   const bool wide = K.wide != 0;
   if (axis == 0) {
@@ -278,28 +415,60 @@ int launch_residues(const double* x, int64_t rows, int64_t cols, int64_t ldx, in
     if (rows > 65535) return OZK_EUNSUPPORTED;
     dim3 grid((unsigned)((ldp + 2047) / 2048), (unsigned)rows);
     const bool vec = (reinterpret_cast<uintptr_t>(x) & 15) == 0 && (ldx & 1) == 0;
-#define OZK_ROWS(W, V)                                                                     \
-  hipLaunchKernelGGL((residues_rows_kernel<W, V>), grid, dim3(256), 0, s, x, cols, ldx, K, \
+#define OZK_ROWS(W, V, G)                                                                     \
+  hipLaunchKernelGGL((residues_rows_kernel<W, V, G>), grid, dim3(256), 0, s, x, cols, ldx, K, \
                      p_bits, maxbits, planes, ldp, plane_stride, exps)
-    if (wide && vec) OZK_ROWS(true, true);
-    else if (wide) OZK_ROWS(true, false);
-    else if (vec) OZK_ROWS(false, true);
-    else OZK_ROWS(false, false);
+#define OZK_ROWS_G(W, V) \
+  if (given_exps) OZK_ROWS(W, V, true); else OZK_ROWS(W, V, false)
+    if (wide && vec) { OZK_ROWS_G(true, true); }
+    else if (wide) { OZK_ROWS_G(true, false); }
+    else if (vec) { OZK_ROWS_G(false, true); }
+    else { OZK_ROWS_G(false, false); }
+#undef OZK_ROWS_G
 #undef OZK_ROWS
   } else {
     if (cols <= 0) return OZK_OK;
     dim3 grid((unsigned)((cols + 31) / 32), (unsigned)((ldp + 127) / 128));
-    if (wide)
-      hipLaunchKernelGGL(residues_cols_kernel<true>, grid, dim3(256), 0, s, x, rows, cols, ldx,
-                         K, p_bits, maxbits, planes, ldp, plane_stride, exps);
-    else
-      hipLaunchKernelGGL(residues_cols_kernel<false>, grid, dim3(256), 0, s, x, rows, cols, ldx,
-                         K, p_bits, maxbits, planes, ldp, plane_stride, exps);
+#define OZK_COLS(W, G)                                                                      \
+  hipLaunchKernelGGL((residues_cols_kernel<W, G>), grid, dim3(256), 0, s, x, rows, cols, ldx, \
+                     K, p_bits, maxbits, planes, ldp, plane_stride, exps)
+    if (wide && given_exps) OZK_COLS(true, true);
+    else if (wide) OZK_COLS(true, false);
+    else if (given_exps) OZK_COLS(false, true);
+    else OZK_COLS(false, false);
+#undef OZK_COLS
   }
   return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
 }
 
 bool rows_fused_supported(int64_t cols) { return cols <= 32768; }
+
+int64_t norm_chunks(int64_t rows, int64_t cols, int axis) {
+  return axis == 0 ? (cols + 2047) / 2048 : (rows + 31) / 32;
+}
+
+int launch_norm_exps(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                     int alpha, uint64_t* pmax, double* ps, int32_t* exps, hipStream_t s) {
+  const int64_t lines = axis == 0 ? rows : cols;
+  if (lines <= 0) return OZK_OK;
+  const int64_t chunks = norm_chunks(rows, cols, axis);
+  if (chunks > 0) {
+    if (axis == 0) {
+      if (rows > 65535) return OZK_EUNSUPPORTED;
+      hipLaunchKernelGGL(norm_partials_rows_kernel, dim3((unsigned)chunks, (unsigned)rows),
+                         dim3(256), 0, s, x, cols, ldx, pmax, ps);
+    } else {
+      hipLaunchKernelGGL(norm_partials_cols_kernel,
+                         dim3((unsigned)((cols + 255) / 256), (unsigned)chunks), dim3(256), 0, s,
+                         x, rows, cols, ldx, pmax, ps);
+    }
+    if (hipGetLastError() != hipSuccess) return OZK_EHIP;
+  }
+  const int64_t sl = axis == 0 ? chunks : 1, sc = axis == 0 ? 1 : cols;
+  hipLaunchKernelGGL(exps_norm_kernel, dim3((unsigned)((lines + 255) / 256)), dim3(256), 0, s,
+                     pmax, ps, lines, chunks, sl, sc, alpha, exps);
+  return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
+}
 
 int launch_line_exps(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
                      int p_bits, uint64_t* maxbits, int32_t* exps, hipStream_t s) {
@@ -314,15 +483,16 @@ int launch_line_exps(const double* x, int64_t rows, int64_t cols, int64_t ldx, i
 }
 
 int launch_residues_rows_fused(const double* x, int64_t rows, int64_t cols, int64_t ldx, int r,
-                               int p_bits, int8_t* planes, int64_t ldp, int64_t plane_stride,
-                               int32_t* exps, hipStream_t s) {
+                               int scaling, int width, int8_t* planes, int64_t ldp,
+                               int64_t plane_stride, int32_t* exps, hipStream_t s) {
   if (rows <= 0) return OZK_OK;
-  const ResidueConsts& K = *residue_consts(r, p_bits);
+  const ResidueConsts& K = *residue_consts(r, width);
   const bool wide = K.wide != 0;
-#define OZK_FUSED(NT, G)                                                                     \
-  return wide ? launch_fused<true, NT, G>(x, rows, cols, ldx, K, p_bits, planes, ldp,        \
-                                          plane_stride, exps, s)                             \
-              : launch_fused<false, NT, G>(x, rows, cols, ldx, K, p_bits, planes, ldp,       \
+  const int norm = scaling == OZK_SCALING_NORM;
+#define OZK_FUSED(NT, G)                                                                      \
+  return wide ? launch_fused<true, NT, G>(x, rows, cols, ldx, K, norm, width, planes, ldp,    \
+                                          plane_stride, exps, s)                              \
+              : launch_fused<false, NT, G>(x, rows, cols, ldx, K, norm, width, planes, ldp,   \
                                            plane_stride, exps, s)
   if (cols <= 2048) { OZK_FUSED(256, 1); }
   if (cols <= 4096) { OZK_FUSED(256, 2); }

@@ -43,8 +43,16 @@ struct CrtConsts {
 };
 
 // Host side (rns_host.cpp)
+constexpr int kNormAlphaCap = 76;  // norm rule: scaled integers stay below 2^77
 int moduli_list(int r, int32_t* out);
 int scaling_bits(int r, int64_t k, int* pa, int* pb);
+// Norm rule widths (alpha_A, alpha_B): (2^aA + sqrt(k)/2)(2^aB + sqrt(k)/2) <= (M-1)/2.
+int scaling_bits_norm(int r, int64_t k, int* pa, int* pb);
+// Widths of either rule (OZK_SCALING_MAX: P_A, P_B; OZK_SCALING_NORM: alpha_A, alpha_B).
+int scaling_widths(int scaling, int r, int64_t k, int* wa, int* wb);
+// Either rule bounds every scaled integer by 2^width (max rule: |x| 2^e < 2^P; norm rule:
+// |x| 2^e <= ||x||_2 2^e < 2^alpha; round-to-nearest reaches at most the power of two),
+// so `width` alone picks the narrow or wide residue arithmetic.
 const ResidueConsts* residue_consts(int r, int p_bits);
 const CrtConsts* crt_consts(int r);
 
@@ -55,13 +63,20 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int launch_fill_u64(uint64_t* p, int64_t n, uint64_t v, hipStream_t s);
 int launch_absmax(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
                   uint64_t* maxbits, hipStream_t s);
+// given_exps: exps already holds the exponents (norm rule, width = alpha); else the max
+// rule with width = P from maxbits, written to exps.
 int launch_residues(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
-                    int r, int p_bits, const uint64_t* maxbits, int8_t* planes, int64_t ldp,
-                    int64_t plane_stride, int32_t* exps, hipStream_t s);
+                    int r, int width, const uint64_t* maxbits, int8_t* planes, int64_t ldp,
+                    int64_t plane_stride, int32_t* exps, int given_exps, hipStream_t s);
 int launch_residues_rows_fused(const double* x, int64_t rows, int64_t cols, int64_t ldx,
-                               int r, int p_bits, int8_t* planes, int64_t ldp,
+                               int r, int scaling, int width, int8_t* planes, int64_t ldp,
                                int64_t plane_stride, int32_t* exps, hipStream_t s);
 bool rows_fused_supported(int64_t cols);
+// Norm rule, unfused paths: per-chunk maxima and scaled sums of squares into pmax/ps
+// (norm_chunks(...) entries per line each), then the exponents from them.
+int64_t norm_chunks(int64_t rows, int64_t cols, int axis);
+int launch_norm_exps(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                     int alpha, uint64_t* pmax, double* ps, int32_t* exps, hipStream_t s);
 // Row (axis 0) or column (axis 1) exponents only, through maxbits scratch.
 int launch_line_exps(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
                      int p_bits, uint64_t* maxbits, int32_t* exps, hipStream_t s);

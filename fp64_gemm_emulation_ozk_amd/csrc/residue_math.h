@@ -84,6 +84,27 @@ __device__ __forceinline__ int line_exponent(uint64_t maxbits, int p_bits) {
   return p_bits - __builtin_amdgcn_frexp_exp(t);               // p - 1 - ilogb(t)
 }
 
+// Norm rule (tighter row/column scaling): the exponent of a line from the bit pattern of
+// its largest |x| and s = sum over the line of (x 2^-T)^2, T = ilogb(max |x|), summed in
+// fp64 in a fixed order.  s >= 1 (the largest term is in [1, 4)) and its relative error
+// is below 2^-35 for lines of at most 2^17 entries, so RN(s (1 + 2^-32)) bounds the exact
+// sum from above and, with u = its ilogb, ||x||_2 < 2^(T + floor(u/2) + 1):
+// e = alpha - 1 - (T + floor(u/2)) keeps 2^e ||x||_2 < 2^alpha.
+__device__ __forceinline__ int norm_exponent(uint64_t maxbits, double s, int alpha) {
+  if (maxbits >= 0x7ff0000000000000ull) return INT32_MIN;     // Inf or NaN in the line
+  if (maxbits == 0) return 0;
+  const int t = __builtin_amdgcn_frexp_exp(__longlong_as_double((long long)maxbits)) - 1;
+  const int u = __builtin_amdgcn_frexp_exp(s * (1.0 + 0x1p-32)) - 1;
+  return alpha - 1 - (t + (u >> 1));
+}
+
+// (x 2^-T)^2 added to acc, T = ilogb of the line's maximum (0 when that is 0 or not
+// finite: the sum is then unused).
+__device__ __forceinline__ int line_ilogb(uint64_t maxbits) {
+  if (maxbits == 0 || maxbits >= 0x7ff0000000000000ull) return 0;
+  return __builtin_amdgcn_frexp_exp(__longlong_as_double((long long)maxbits)) - 1;
+}
+
 __device__ __forceinline__ uint64_t abs_bits(double x) {
   return (uint64_t)__double_as_longlong(x) & 0x7fffffffffffffffull;
 }

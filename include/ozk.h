@@ -54,6 +54,9 @@ extern "C" {
 #define OZK_EHIP (-4)         /* a HIP launch failed */
 #define OZK_EUNSUPPORTED (-5) /* valid request this build does not handle */
 
+#define OZK_SCALING_MAX 0     /* scaling rule: per-line max (default of every entry point) */
+#define OZK_SCALING_NORM 1    /* scaling rule: per-line 2-norm (Cauchy-Schwarz), *_ex only */
+
 #define OZK_MAX_MODULI 20
 #define OZK_MAX_K 131071      /* |residue product| <= 2^14: int32 sums stay exact */
 #define OZK_PLANE_K 64        /* residue and limb planes pad K to a multiple of this */
@@ -71,6 +74,12 @@ int ozk_moduli(int r, int32_t* out);
 /* Bit budgets (P_A, P_B) of the scaling for r moduli and inner dimension k (host
  * outputs).  OZK_ERANGE when beta < 2 or k > OZK_MAX_K. */
 int ozk_scaling_bits(int r, int64_t k, int32_t* pa, int32_t* pb);
+
+/* Widths of either scaling rule (host outputs): OZK_SCALING_MAX gives (P_A, P_B) as
+ * above; OZK_SCALING_NORM gives (alpha_A, alpha_B), the largest widths (alpha_A +
+ * alpha_B <= Q - 1, each <= 76) with (2^aA + sqrt(k)/2)(2^aB + sqrt(k)/2) <= (M-1)/2,
+ * checked in exact integer arithmetic.  OZK_EINVAL for an unknown rule. */
+int ozk_scaling_bits_ex(int r, int64_t k, int scaling, int32_t* pa, int32_t* pb);
 
 /* Leading dimension used for planes over an inner dimension k: round_up(k, 64). */
 int64_t ozk_planes_ld(int64_t k);
@@ -95,6 +104,18 @@ int ozk_deconstruct(const double* x, int64_t rows, int64_t cols, int64_t ldx, in
                     int r, int64_t k_budget, int8_t* planes, int64_t ldp,
                     int64_t plane_stride, int32_t* exps, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/* The same with a choice of scaling rule (ozk_deconstruct is OZK_SCALING_MAX).
+ * OZK_SCALING_NORM: exps[line] = alpha - 1 - (T + floor(u/2)) with alpha the width of
+ * this operand (ozk_scaling_bits_ex), T = ilogb(max |x|) over the line, u = ilogb(RN(s
+ * (1 + 2^-32))) and s = sum over the line of (x 2^-T)^2 in fp64, summed in a fixed
+ * order (deterministic; the factor keeps RN(s (1 + 2^-32)) above the exact sum), so
+ * that 2^e ||line||_2 < 2^alpha; 0 for an all-zero line, INT32_MIN for a line with
+ * Inf/NaN.  The workspace of ozk_deconstruct_workspace_size covers both rules. */
+int ozk_deconstruct_ex(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                       int r, int64_t k_budget, int scaling, int8_t* planes, int64_t ldp,
+                       int64_t plane_stride, int32_t* exps, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- modular products
  * [TME4] abstract, the tensor term; [AWE] abstract, each product is an error-free
@@ -134,6 +155,14 @@ int ozk_dgemm_workspace_size(int64_t m, int64_t n, int64_t k, int r, size_t* byt
 int ozk_dgemm(int64_t m, int64_t n, int64_t k, const double* A, int64_t lda,
               const double* B, int64_t ldb, double* C, int64_t ldc, int r,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same with a choice of scaling rule (ozk_dgemm is OZK_SCALING_MAX); the workspace
+ * of ozk_dgemm_workspace_size covers both.  OZK_SCALING_NORM scales rows of A and
+ * columns of B by their 2-norms (see ozk_deconstruct_ex), which keeps more bits of
+ * lines whose entries differ widely in magnitude for the same r. */
+int ozk_dgemm_ex(int64_t m, int64_t n, int64_t k, const double* A, int64_t lda,
+                 const double* B, int64_t ldb, double* C, int64_t ldc, int r, int scaling,
+                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- emulated DGEMV
  * Y = A X for A m x k and X k x nrhs (1 <= nrhs <= 32): the memory-bound GEMV and

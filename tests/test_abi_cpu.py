@@ -70,6 +70,25 @@ def test_scaling_bits_errors(lib):
     assert lib.ozk_scaling_bits(5, 0, ctypes.byref(pa), ctypes.byref(pb)) == EINVAL
 
 
+@pytest.mark.parametrize("r,k", [(2, 1), (3, 64), (8, 4096), (12, 4096), (16, 4096),
+                                 (18, 4096), (20, 8192), (14, 32768), (16, 131071)])
+def test_scaling_bits_ex_match_oracle(lib, r, k):
+    assert ozk.ozk_scaling_bits_ex(r, k, "max") == rns.scaling_bits(r, k)
+    assert ozk.ozk_scaling_bits_ex(r, k, "norm") == rns.scaling_bits_norm(r, k)
+
+
+def test_scaling_bits_ex_errors(lib):
+    pa, pb = ctypes.c_int32(), ctypes.c_int32()
+    f = lib.ozk_scaling_bits_ex
+    assert f(16, 4096, 2, ctypes.byref(pa), ctypes.byref(pb)) == EINVAL       # unknown rule
+    assert f(16, 4096, -1, ctypes.byref(pa), ctypes.byref(pb)) == EINVAL
+    assert f(16, 131072, 1, ctypes.byref(pa), ctypes.byref(pb)) == ERANGE     # k too large
+    assert f(0, 64, 1, ctypes.byref(pa), ctypes.byref(pb)) == EINVAL
+    with pytest.raises(ValueError):
+        rns.scaling_bits_norm(1, 1 << 16)
+    assert f(1, 1 << 16, 1, ctypes.byref(pa), ctypes.byref(pb)) == ERANGE     # no budget
+
+
 def test_planes_ld(lib):
     assert [lib.ozk_planes_ld(k) for k in (1, 63, 64, 65, 4096, 4097)] == [64, 64, 64, 128, 4096,
                                                                           4160]
@@ -81,6 +100,12 @@ def test_workspace_sizes(lib):
     out = ctypes.c_size_t()
     assert lib.ozk_dgemm_workspace_size(4, 4, 200000, 16, ctypes.byref(out)) == ERANGE
     assert lib.ozk_dgemm_workspace_size(4, 4, 4, 0, ctypes.byref(out)) == EINVAL
+    # one query serves both rules: the norm rule's chunk partials (a maximum and a sum per
+    # 32 rows of a column; per 2048 columns of a row the fused kernel cannot hold)
+    assert ozk.ozk_deconstruct_workspace_size(4096, 4096, 1) >= 2 * 128 * 4096 * 8
+    assert ozk.ozk_deconstruct_workspace_size(4096, 4096, 0) == 0
+    assert ozk.ozk_deconstruct_workspace_size(8, 40000, 0) >= 2 * 8 * 20 * 8
+    assert ws >= 16 * 4096 * 4096 * 3 + 2 * 128 * 4096 * 8
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
@@ -113,6 +138,25 @@ def test_deconstruct_validation(lib):
     assert f(FAKE, 4, 100, 100, 0, 14, 100, None, 128, 512, FAKE, FAKE, 0, None) == EINVAL
     # axis 1 needs a column-maximum workspace
     assert f(FAKE, 100, 4, 4, 1, 14, 100, FAKE, 128, 512, FAKE, None, 0, None) == EWORKSPACE
+
+
+def test_ex_validation(lib):
+    f = lib.ozk_dgemm_ex
+    assert f(4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 14, 2, FAKE, 1 << 20, None) == EINVAL  # rule
+    assert f(4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 14, -1, FAKE, 1 << 20, None) == EINVAL
+    assert f(4, 4, 4, FAKE, 3, FAKE, 4, FAKE, 4, 14, 1, FAKE, 1 << 20, None) == EINVAL   # lda
+    assert f(4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 14, 1, None, 0, None) == EWORKSPACE
+    assert f(4, 4, 1 << 16, FAKE, 1 << 16, FAKE, 4, FAKE, 4, 1, 1, FAKE, 1 << 30,
+             None) == ERANGE                                                          # budget
+    assert f(0, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 14, 1, None, 0, None) == OK           # empty
+    g = lib.ozk_deconstruct_ex
+    assert g(FAKE, 4, 100, 100, 0, 14, 100, 5, FAKE, 128, 512, FAKE, FAKE, 0, None) == EINVAL
+    assert g(FAKE, 4, 100, 100, 0, 14, 100, 1, FAKE, 64, 256, FAKE, FAKE, 0, None) == EINVAL
+    # axis 1 by the norm rule needs the chunk partials: missing, too small, misaligned
+    assert g(FAKE, 100, 4, 4, 1, 14, 100, 1, FAKE, 128, 512, FAKE, None, 0, None) == EWORKSPACE
+    assert g(FAKE, 100, 4, 4, 1, 14, 100, 1, FAKE, 128, 512, FAKE, FAKE, 8, None) == EWORKSPACE
+    assert g(FAKE, 100, 4, 4, 1, 14, 100, 1, FAKE, 128, 512, FAKE, ctypes.c_void_p(0x1004),
+             1 << 20, None) == EINVAL
 
 
 def test_products_and_reconstruct_validation(lib):
