@@ -19,7 +19,8 @@ Also reported on the same JSON line:
                 rule against the max rule (time and distance to native fp64 at r = 12, 14,
                 16), deconstruction HBM GB/s, the GEMV and FP4-limb engines when built.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--r 16] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--r 16] [--scaling max|norm]
+                       [--no-cpu-baseline]
        python bench.py --counters            (launches only, for rocprofv3 --pmc)
        python bench.py --traffic-summary FETCH_DIR WRITE_DIR
 """
@@ -500,7 +501,7 @@ def measure_practical_peaks(stream) -> dict:
     return out
 
 
-def cpu_baseline(a, b, r: int) -> dict:
+def cpu_baseline(a, b, r: int, rule: str = "max") -> dict:
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -509,13 +510,13 @@ def cpu_baseline(a, b, r: int) -> dict:
     rows = np.arange(8)
     with threadpool_limits(1):
         t0 = time.perf_counter()
-        ozaki2.dgemm(a, b, r, rows=rows)
+        ozaki2.dgemm(a, b, r, rows=rows, scaling=rule)
         dt = time.perf_counter() - t0
     flops = 2.0 * len(rows) * N * K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
             "seconds": round(dt, 3),
             "sample": f"8 full rows of C (8 x {N} outputs; all of A's 8 rows and all of B "
-                      f"deconstructed), r={r}, numpy with 1 BLAS thread"}
+                      f"deconstructed), r={r}, {rule} scaling, numpy with 1 BLAS thread"}
 
 
 def main() -> int:
@@ -524,6 +525,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--r", type=int, default=16)
+    ap.add_argument("--scaling", choices=("max", "norm"), default="max",
+                    help="scaling rule of the timed step (max: per-line maximum, the "
+                         "headline; norm: per-line 2-norm)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-gemv", action="store_true")
@@ -569,7 +573,8 @@ def main() -> int:
     db = torch.from_numpy(b).to(dev)
     out = torch.empty((M, N), dtype=torch.float64, device=dev)
     ws = torch.empty(ozk.ozk_dgemm_workspace_size(M, N, K, r), dtype=torch.uint8, device=dev)
-    step = lambda: ozk.ozk_dgemm(da, db, r, out=out, workspace=ws)
+    rule = args.scaling
+    step = lambda: ozk.ozk_dgemm_ex(da, db, r, rule, out=out, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -586,8 +591,8 @@ def main() -> int:
     rel = float(torch.linalg.norm(out - ref) / torch.linalg.norm(ref))
 
     # Dominant kernel alone: batched int8 MFMA products with the residue epilogue.
-    planes_a, exps_a = ozk.ozk_deconstruct(da, 0, r)
-    planes_b, exps_b = ozk.ozk_deconstruct(db, 1, r, k_budget=K)
+    planes_a, exps_a = ozk.ozk_deconstruct_ex(da, 0, r, rule)
+    planes_b, exps_b = ozk.ozk_deconstruct_ex(db, 1, r, rule, k_budget=K)
     res = torch.empty((r, M, N), dtype=torch.int8, device=dev)
     gemm = lambda: ozk.ozk_modular_residues(planes_a, planes_b, out=res)
     for _ in range(2):
@@ -658,14 +663,15 @@ def main() -> int:
             norm_rows.append(row)
         extras["norm_rule"] = norm_rows
         del wsn
-        dec = lambda: ozk.ozk_deconstruct(da, 0, r, planes=planes_a, exps=exps_a)
+        dec = lambda: ozk.ozk_deconstruct_ex(da, 0, r, rule, planes=planes_a, exps=exps_a)
         dec()
         dec_ms = _time_events(dec, reps, stream)
         extras["deconstruct_rows"] = {
             "ms": round(dec_ms, 4), "bytes": (8 + r) * M * K,
             "gbs": round((8 + r) * M * K / dec_ms / 1e6, 1),
             "frac_hbm": round((8 + r) * M * K / dec_ms / 1e6 / PEAK_HBM_GBS, 4)}
-        decb = lambda: ozk.ozk_deconstruct(db, 1, r, k_budget=K, planes=planes_b, exps=exps_b)
+        decb = lambda: ozk.ozk_deconstruct_ex(db, 1, r, rule, k_budget=K, planes=planes_b,
+                                              exps=exps_b)
         decb()
         decb_ms = _time_events(decb, reps, stream)
         extras["deconstruct_cols"] = {
@@ -701,12 +707,13 @@ def main() -> int:
         "dtype": "f64",
         "data": "synthetic",
         "config": {"workload": f"emulated DGEMM {M}x{N}x{K}, entries (U-0.5)*exp({PHI}*N(0,1)), "
-                               f"seed {SEED}, r={r} moduli",
-                   "m": M, "n": N, "k": K, "r": r, "compute": "int8 MFMA + fp64 VALU"},
+                               f"seed {SEED}, r={r} moduli, {rule} scaling",
+                   "m": M, "n": N, "k": K, "r": r, "scaling": rule,
+                   "compute": "int8 MFMA + fp64 VALU"},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(a, b, r)
+        line["cpu_baseline"] = cpu_baseline(a, b, r, rule)
     line["extras"] = extras
     print(json.dumps(line), flush=True)
     return 0

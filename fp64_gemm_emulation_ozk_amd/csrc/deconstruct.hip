@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kNT) void residues_rows_fused_kernel(
 // Norm rule outside the fused kernel.  The line is cut into chunks; each chunk writes
 // its own largest |x| (bit pattern) pmax and ps = sum of (x 2^-Tc)^2 with Tc = ilogb of
 // that maximum, in a fixed order.  exps_norm_kernel then takes T = ilogb of the line's
-// maximum and s = sum over chunks, in chunk order, of ps 2^(2 (Tc - T)): scaling by a
+// maximum and s = the chunks' ps 2^(2 (Tc - T)) added in a fixed order: scaling by a
 // power of two is exact, so s is the line's scaled sum of squares in a fixed order
 // (terms that underflow are below 2^-1000 of s >= 1, far inside the bound's slack).
 // The line is read once for its exponent, as by the max rule.
@@ -314,50 +314,77 @@ __global__ __launch_bounds__(256) void norm_partials_rows_kernel(
   }
 }
 
-// Columns: grid (column blocks of 256, chunks of 32 rows); thread = column, its chunk
-// held in registers, written to pmax/ps[chunk * cols + col].
+// Adds a piece (maximum mc, sum sc scaled by 2^-2Tc, Tc = ilogb mc) into a running
+// (maximum m, sum s scaled by 2^-2T): both sums are brought to the larger maximum's
+// exponent by exact power-of-two scalings, then added.
+__device__ __forceinline__ void norm_combine(uint64_t& m, double& s, uint64_t mc, double sc) {
+  const uint64_t mn = umax64(m, mc);
+  const int t = line_ilogb(mn);
+  s = __builtin_ldexp(s, 2 * (line_ilogb(m) - t)) + __builtin_ldexp(sc, 2 * (line_ilogb(mc) - t));
+  m = mn;
+}
+
+// Columns: grid (column blocks of 256, chunks of 128 rows); thread = column.  The chunk
+// is taken as 4 pieces of 32 rows held in registers (maximum, then scaled squares), the
+// pieces combined in order; written to pmax/ps[chunk * cols + col].
 __global__ __launch_bounds__(256) void norm_partials_cols_kernel(
     const double* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
     uint64_t* __restrict__ pmax, double* __restrict__ ps) {
   const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (col >= cols) return;
-  const int64_t r0 = (int64_t)blockIdx.y * 32;
-  double a[32];
-  uint64_t v = 0;
+  uint64_t m = 0;
+  double s = 0.0;
+  for (int piece = 0; piece < 4; ++piece) {
+    const int64_t r0 = (int64_t)blockIdx.y * 128 + piece * 32;
+    if (r0 >= rows) break;
+    double a[32];
+    uint64_t v = 0;
 #pragma unroll
-  for (int u = 0; u < 32; ++u) {
-    a[u] = r0 + u < rows ? x[(r0 + u) * ldx + col] : 0.0;
-    v = umax64(v, abs_bits(a[u]));
-  }
-  const int t = line_ilogb(v);
-  double ss = 0.0;
+    for (int u = 0; u < 32; ++u) {
+      a[u] = r0 + u < rows ? x[(r0 + u) * ldx + col] : 0.0;
+      v = umax64(v, abs_bits(a[u]));
+    }
+    const int t = line_ilogb(v);
+    double ss = 0.0;
 #pragma unroll
-  for (int u = 0; u < 32; ++u) {
-    const double y = __builtin_ldexp(a[u], -t);
-    ss = __builtin_fma(y, y, ss);
+    for (int u = 0; u < 32; ++u) {
+      const double y = __builtin_ldexp(a[u], -t);
+      ss = __builtin_fma(y, y, ss);
+    }
+    norm_combine(m, s, v, ss);
   }
   const int64_t i = (int64_t)blockIdx.y * cols + col;
-  pmax[i] = v;
-  ps[i] = ss;
+  pmax[i] = m;
+  ps[i] = s;
 }
 
-// Per line: combine the chunk partials (maximum, then the rescaled sums in chunk order)
-// and write the norm-rule exponent.
-__global__ void exps_norm_kernel(const uint64_t* __restrict__ pmax,
-                                 const double* __restrict__ ps, int64_t lines, int64_t chunks,
-                                 int64_t stride_line, int64_t stride_chunk, int alpha,
-                                 int32_t* __restrict__ exps) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= lines) return;
-  uint64_t mx = 0;
-  for (int64_t c = 0; c < chunks; ++c) mx = umax64(mx, pmax[i * stride_line + c * stride_chunk]);
-  const int t = line_ilogb(mx);
+// Per line: combine the chunk partials and write the norm-rule exponent.  Block of 256
+// threads = 16 lines x 16 parts; part p combines chunks p, p + 16, ... in order, then
+// the 16 parts are combined in order (deterministic).
+__global__ __launch_bounds__(256) void exps_norm_kernel(
+    const uint64_t* __restrict__ pmax, const double* __restrict__ ps, int64_t lines,
+    int64_t chunks, int64_t stride_line, int64_t stride_chunk, int alpha,
+    int32_t* __restrict__ exps) {
+  const int j = threadIdx.x & 15, part = threadIdx.x >> 4;
+  const int64_t i = (int64_t)blockIdx.x * 16 + j;
+  uint64_t m = 0;
   double s = 0.0;
-  for (int64_t c = 0; c < chunks; ++c) {
-    const int64_t q = i * stride_line + c * stride_chunk;
-    s += __builtin_ldexp(ps[q], 2 * (line_ilogb(pmax[q]) - t));
+  if (i < lines)
+    for (int64_t c = part; c < chunks; c += 16) {
+      const int64_t q = i * stride_line + c * stride_chunk;
+      norm_combine(m, s, pmax[q], ps[q]);
+    }
+  __shared__ uint64_t lm[16][17];
+  __shared__ double ls[16][17];
+  lm[j][part] = m;
+  ls[j][part] = s;
+  __syncthreads();
+  if (part == 0 && i < lines) {
+    uint64_t mm = 0;
+    double sum = 0.0;
+    for (int p = 0; p < 16; ++p) norm_combine(mm, sum, lm[j][p], ls[j][p]);
+    exps[i] = norm_exponent(mm, sum, alpha);
   }
-  exps[i] = norm_exponent(mx, s, alpha);
 }
 
 __global__ void exps_from_maxbits_kernel(const uint64_t* __restrict__ maxbits, int64_t n,
@@ -444,7 +471,7 @@ int launch_residues(const double* x, int64_t rows, int64_t cols, int64_t ldx, in
 bool rows_fused_supported(int64_t cols) { return cols <= 32768; }
 
 int64_t norm_chunks(int64_t rows, int64_t cols, int axis) {
-  return axis == 0 ? (cols + 2047) / 2048 : (rows + 31) / 32;
+  return axis == 0 ? (cols + 2047) / 2048 : (rows + 127) / 128;
 }
 
 int launch_norm_exps(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
@@ -465,7 +492,7 @@ int launch_norm_exps(const double* x, int64_t rows, int64_t cols, int64_t ldx, i
     if (hipGetLastError() != hipSuccess) return OZK_EHIP;
   }
   const int64_t sl = axis == 0 ? chunks : 1, sc = axis == 0 ? 1 : cols;
-  hipLaunchKernelGGL(exps_norm_kernel, dim3((unsigned)((lines + 255) / 256)), dim3(256), 0, s,
+  hipLaunchKernelGGL(exps_norm_kernel, dim3((unsigned)((lines + 15) / 16)), dim3(256), 0, s,
                      pmax, ps, lines, chunks, sl, sc, alpha, exps);
   return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
 }

@@ -101,11 +101,11 @@ def test_workspace_sizes(lib):
     assert lib.ozk_dgemm_workspace_size(4, 4, 200000, 16, ctypes.byref(out)) == ERANGE
     assert lib.ozk_dgemm_workspace_size(4, 4, 4, 0, ctypes.byref(out)) == EINVAL
     # one query serves both rules: the norm rule's chunk partials (a maximum and a sum per
-    # 32 rows of a column; per 2048 columns of a row the fused kernel cannot hold)
-    assert ozk.ozk_deconstruct_workspace_size(4096, 4096, 1) >= 2 * 128 * 4096 * 8
+    # 128 rows of a column; per 2048 columns of a row the fused kernel cannot hold)
+    assert ozk.ozk_deconstruct_workspace_size(4096, 4096, 1) >= 2 * 32 * 4096 * 8
     assert ozk.ozk_deconstruct_workspace_size(4096, 4096, 0) == 0
     assert ozk.ozk_deconstruct_workspace_size(8, 40000, 0) >= 2 * 8 * 20 * 8
-    assert ws >= 16 * 4096 * 4096 * 3 + 2 * 128 * 4096 * 8
+    assert ws >= 16 * 4096 * 4096 * 3 + 2 * 32 * 4096 * 8
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation

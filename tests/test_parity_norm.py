@@ -34,8 +34,9 @@ def _special_lines(x: np.ndarray, axis: int) -> np.ndarray:
         v = x[sel(3)] * 1e-200
         v[-1] = 2.0**900
         x[sel(3)] = v
-        n = x[sel(4)].shape[0]
-        x[sel(4)] = np.ldexp(np.sign(x[sel(4)]) + (x[sel(4)] == 0), np.linspace(-1070, 1020, n).astype(int))
+        v = x[sel(4)]
+        sign = np.where(v < 0, -1.0, 1.0)
+        x[sel(4)] = np.ldexp(sign, np.linspace(-1070, 1020, v.shape[0]).astype(int))
     return x
 
 
@@ -71,9 +72,11 @@ NORM_DECON_CASES = [
     (6, 40000, 0, 14, "phi"),        # long rows: chunk partials of 2048 columns
     (100, 37, 1, 14, "uniform"),
     (257, 300, 1, 16, "phi"),
-    (4100, 70, 1, 20, "phi"),        # 129 chunks of 32 rows, ragged last chunk
+    (4100, 70, 1, 20, "phi"),        # 33 chunks of 128 rows, ragged last chunk and piece
+    (600, 300, 1, 14, "phi"),        # 5 chunks: the last one has 2 pieces of 32 rows, ragged
     (64, 64, 1, 8, "uniform"),
     (33, 5, 1, 12, "phi"),           # a single ragged chunk
+    (5000, 20, 1, 16, "phi"),        # 40 chunks: more than the 16 parts of the combine
 ]
 
 
