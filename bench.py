@@ -195,11 +195,12 @@ TME_PATH = os.path.join(ROOT, "profiles", "tme_counters.json")
 # Kernels whose instruction counts calibrate the time model: key -> (kernel-name
 # substring, unit the counts are divided by, number of units per dispatch, moduli).
 TME_KERNELS = {
-    "decon_rows_wide_4096_r16": ("residues_rows_fused_kernel<true, true, 256, 2>",
+    "decon_rows_wide_4096_r16": ("residues_rows_fused_kernel<true, true, 256, 2, false>",
                                  "element", 4096 * 4096, 16),
-    "decon_rows_narrow_32768_r14": ("residues_rows_fused_kernel<false, true, 1024, 4>",
+    "decon_rows_narrow_32768_r14": ("residues_rows_fused_kernel<false, true, 1024, 4, false>",
                                     "element", 32768 * 32768, 14),
-    "decon_cols_wide_4096_r16": ("residues_cols_kernel<true>", "element", 4096 * 4096, 16),
+    "decon_cols_wide_4096_r16": ("residues_cols_kernel<true, false>", "element", 4096 * 4096,
+                                 16),
     "gemv_fly_32768_r14_32cols": ("gemv_fly_kernel<false, 14>", "element of A",
                                   32768 * 32768, 14),
     "gemv_digits_32768_r14_1col": ("gemv_digits_kernel<1>", "element of A", 32768 * 32768, 14),
