@@ -17,7 +17,8 @@ Also reported on the same JSON line:
   cpu_baseline  the CPU oracle (numpy, one BLAS thread) on 8 full output rows.
   extras        native fp64 DGEMM (torch.matmul), the r sweep 12..18, the norm scaling
                 rule against the max rule (time and distance to native fp64 at r = 12, 14,
-                16), deconstruction HBM GB/s, the GEMV and FP4-limb engines when built.
+                16), deconstruction HBM GB/s, the GEMV and FP4-limb engines, and the
+                8192^3 wide-dynamic-range workload at r = 16..20 under both rules.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--r 16] [--scaling max|norm]
                        [--no-cpu-baseline]
@@ -417,6 +418,50 @@ def measure_gemv(reps: int, stream) -> dict:
     return out
 
 
+def measure_wide_range(reps: int, stream) -> dict:
+    """The wide-dynamic-range workload: 8192^3 with entries (U(0,1) - 0.5) exp(4 N(0,1))
+    (seed 3), r = 16..20 under both scaling rules, next to native fp64 DGEMM.  rel is the
+    normwise distance to the native product (its own rounding error is far below the
+    emulation's at small r).  The GPU tests fix the accuracy against the exact product:
+    1e-15 normwise needs r = 18 under the max rule and r = 16 under the norm rule."""
+    import torch
+
+    import fp64_gemm_emulation_ozk_amd as ozk
+    import ozk_inputs
+
+    n = 8192
+    dev = torch.device("cuda:0")
+    a, b = ozk_inputs.gemm_operands(n, n, n, seed=3, dist="phi", phi=4.0)
+    da, db = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    del a, b
+    flops = 2.0 * n * n * n
+    ref = torch.matmul(da, db)
+    nat = lambda: torch.matmul(da, db, out=ref)
+    t_nat = _time_events(nat, reps, stream)
+    ref_n = torch.linalg.norm(ref)
+    out = torch.empty_like(ref)
+    ws = torch.empty(ozk.ozk_dgemm_workspace_size(n, n, n, 20), dtype=torch.uint8, device=dev)
+    res = {"workload": f"DGEMM {n}^3, entries (U-0.5)*exp(4*N(0,1)), seed 3",
+           "native_fp64": {"ms": round(t_nat, 4), "tflops": round(flops / t_nat / 1e9, 2)},
+           "runs": []}
+    for rr in range(16, 21):
+        row = {"r": rr}
+        for rule in ("max", "norm"):
+            f = lambda: ozk.ozk_dgemm_ex(da, db, rr, rule, out=out, workspace=ws)
+            f()
+            t = _time_events(f, reps, stream)
+            row[rule] = {"ms": round(t, 4), "tflops": round(flops / t / 1e9, 2),
+                         "rel_vs_native": float(torch.linalg.norm(out - ref) / ref_n)}
+        res["runs"].append(row)
+    by_r = {row["r"]: row for row in res["runs"]}
+    res["same_accuracy_1e-15"] = {
+        "max_rule_r18_ms": by_r[18]["max"]["ms"], "norm_rule_r16_ms": by_r[16]["norm"]["ms"],
+        "speedup": round(by_r[18]["max"]["ms"] / by_r[16]["norm"]["ms"], 3)}
+    del da, db, ref, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def measure_fp4(reps: int, stream) -> dict:
     """The exact INT8 x INT8 product of 8192^3 int8 operands (uniform in [-128, 127],
     seed 5) through 9 FP4 GEMMs, against the 10.1 PFLOP/s dense FP4 MFMA peak."""
@@ -533,6 +578,8 @@ def main() -> int:
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--no-fp4", action="store_true")
+    ap.add_argument("--no-wide", action="store_true",
+                    help="skip the 8192^3 wide-dynamic-range extra")
     ap.add_argument("--counters", action="store_true",
                     help="only launch the kernels the counter passes profile")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -690,6 +737,8 @@ def main() -> int:
             extras["gemv_32768"] = measure_gemv(reps, stream)
         if not args.no_fp4:
             extras["fp4limb_int8gemm_8192"] = measure_fp4(reps, stream)
+        if not args.no_wide:
+            extras["wide_range_8192"] = measure_wide_range(reps, stream)
         model = tme_model(extras, peaks, ms_per_step)
         if model is not None:
             extras["tme_model"] = model
