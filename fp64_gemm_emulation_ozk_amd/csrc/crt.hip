@@ -1,19 +1,20 @@
 // CRT reconstruction and inverse scaling: the per-output reconstruction term of Ozaki
-// scheme II ([TME4] abstract).  Each thread reconstructs 4 consecutive outputs of a row.
+// scheme II ([TME4] abstract).
 //
-// Given symmetric residues c_l (|c_l| <= 128) of the exact integer X modulo m_l:
-//   1. q = round(sum_l c_l * RN(E_l / M)).  The exact value of the sum is q + X/M with
-//      |X| <= 2^Q <= (M-1)/2, and 1/2 - 2^Q/M >= 0.0142 for every r <= 20, far above
-//      the < 2^-30 error of the fp64 sum, so q is exact.
-//   2. X = sum_l c_l E_l - q M, in 2^40 limbs held in fp64: every limb sum stays below
-//      2^53 (at most 20 * 2^47 + 2^51.4), so all fp64 operations are exact.
-//   3. Limbs are normalised to digits in [0, 2^40) and the sign split off; RN(|X| 2^-s)
+// Given symmetric residues c_l (|c_l| <= 128) of the exact integer X modulo m_l, with
+// |X| <= 2^Q <= (M-1)/2:
+//   1. the digit sums S_b = sum_l c_l e_lb of the basis E_l in balanced base 256, and the
+//      same for the 24-bit fractions F_l ~ 2^24 E_l / M, come from one int8 matrix-core
+//      product per 32 outputs (crt_kernel below);
+//   2. q = rint(2^-24 sum_l c_l F_l) is exact (the distance of sum_l c_l E_l / M to the
+//      integer q is at most 1/2 - 2^Q/M, and 1/2 - 2^Q/M >= 0.0142 for every r <= 20);
+//   3. X = sum_b S_b 256^b - q M in 2^40 limbs held in fp64: every limb sum stays below
+//      2^52, so all fp64 operations are exact;
+//   4. limbs are normalised to digits in [0, 2^40) and the sign split off; RN(|X| 2^-s)
 //      is formed with one fp64 rounding of the top digits plus an exact tie correction
 //      (round_digits), or, for a subnormal result, by integer rounding at the reduced
 //      precision, so the output is rounded exactly once.
-// The constants come from the compile-time table in __constant__ memory; each block
-// stages the r(L+1)+L values it needs in LDS (compile-time r), and every constant is
-// read once per 4 outputs, so none of them has to live in scalar registers.
+// The constants come from compile-time tables in __constant__ memory.
 #include "ozk_internal.h"
 #include "rns_table.h"
 
@@ -22,6 +23,9 @@ namespace ozk {
 __constant__ RnsTable d_rns = make_rns_table();
 
 namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ uint64_t u64_of(double d) {  // d integer in [0, 2^53)
   const double hi = __builtin_floor(d * 0x1p-32);
@@ -125,144 +129,299 @@ __device__ __forceinline__ double round_digits(const double (&d)[4], int s) {
   return round_scaled_words(w0, w1, w2, s);
 }
 
-// Exact integer X of 4 outputs from their residues and the RNS constants in LDS,
-// rounded to fp64 with the shift s[u].
-template <int R>
-__device__ __forceinline__ void reconstruct4(const int32_t (&word)[R], const double* __restrict__ sc,
-                                             const int (&s)[4], const bool (&nan)[4],
-                                             double (&out)[4]) {
-  constexpr int L = R <= 15 ? 3 : 4;
-  // sc layout: frac[R], e[R][L], m[L]
-  double qf[4] = {0.0, 0.0, 0.0, 0.0};
+// Sign split, carries and the single rounding of X = sum_p x[p] 2^(40 p) (|x[p]| < 2^52,
+// L limbs): digits 0..L-2 are brought into [0, 2^40) with the sign carried into digit
+// L-1, the magnitude is taken, and RN(|X| 2^-s) is formed by round_digits.
+template <int L>
+__device__ __forceinline__ double finish(double (&x)[4], int s, bool nan) {
 #pragma unroll
-  for (int l = 0; l < R; ++l) {
-    const double fr = sc[l];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      qf[u] = __builtin_fma((double)(int)(int8_t)(word[l] >> (8 * u)), fr, qf[u]);
+  for (int p = 0; p < L - 1; ++p) {
+    const double carry = __builtin_floor(x[p] * 0x1p-40);
+    x[p] = __builtin_fma(-carry, 0x1p40, x[p]);
+    x[p + 1] += carry;
   }
-  double x[4][4];
+  const bool neg = x[L - 1] < 0.0;
+  if (neg) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const double q = __builtin_rint(qf[u]);
+    for (int p = 0; p < L; ++p) x[p] = -x[p];
 #pragma unroll
-    for (int p = 0; p < L; ++p) x[u][p] = -q * sc[R + R * L + p];  // |q| < 2^11.4: exact
-#pragma unroll
-    for (int p = L; p < 4; ++p) x[u][p] = 0.0;
-  }
-#pragma unroll
-  for (int l = 0; l < R; ++l) {
-    double cd[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) cd[u] = (double)(int)(int8_t)(word[l] >> (8 * u));
-#pragma unroll
-    for (int p = 0; p < L; ++p) {
-      const double e = sc[R + l * L + p];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) x[u][p] = __builtin_fma(cd[u], e, x[u][p]);
+    for (int p = 0; p < L - 1; ++p) {
+      const double carry = __builtin_floor(x[p] * 0x1p-40);
+      x[p] = __builtin_fma(-carry, 0x1p40, x[p]);
+      x[p + 1] += carry;
     }
   }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    double* xu = x[u];
-#pragma unroll
-    for (int p = 0; p < L - 1; ++p) {  // digits 0..L-2 in [0, 2^40); sign in digit L-1
-      const double carry = __builtin_floor(xu[p] * 0x1p-40);
-      xu[p] = __builtin_fma(-carry, 0x1p40, xu[p]);
-      xu[p + 1] += carry;
-    }
-    const bool neg = xu[L - 1] < 0.0;
-    if (neg) {
-#pragma unroll
-      for (int p = 0; p < L; ++p) xu[p] = -xu[p];
-#pragma unroll
-      for (int p = 0; p < L - 1; ++p) {
-        const double carry = __builtin_floor(xu[p] * 0x1p-40);
-        xu[p] = __builtin_fma(-carry, 0x1p40, xu[p]);
-        xu[p + 1] += carry;
-      }
-    }
-    double o = round_digits<L>(x[u], s[u]);
-    o = neg ? -o : o;
-    out[u] = nan[u] ? __builtin_nan("") : o;
-  }
+  double o = round_digits<L>(x, s);
+  o = neg ? -o : o;
+  return nan ? __builtin_nan("") : o;
 }
 
+// ---------------------------------------------------------------- CRT on the matrix cores
+// The lift sum_l c_l E_l is a product of the residue matrix (outputs x r) with the basis
+// (r x digits): E_l is written in balanced base-256 digits e_lb in [-128, 127] (the bytes
+// of E_l + 0x80..80, minus 128), so
+//   S_b = sum_l c_l e_lb   (|S_b| <= 20 * 2^14, exact in int32)
+// is one v_mfma_i32_32x32x32_i8 per 32 outputs with the digits as the A operand (row b)
+// and the residues as the B operand (column = output).  Four more rows hold the balanced
+// digits of F_l = RN(2^24 w_l / m_l) (E_l / M = w_l / m_l), from which
+//   q = rint(2^-24 sum_l c_l F_l)
+// is exact: the rows' rounding adds at most 20 * 128 * 2^-25 < 1e-4 to the exact
+// sum_l c_l E_l / M = q + X / M, whose distance to q is at most 1/2 - 0.0142.  Then
+//   X = sum_b S_b 256^b - q M
+// in 2^40 limbs (five digits per limb: every limb sum stays below 2^52, exact in fp64).
+//
+// Output layout of the MFMA: lane i holds column i % 32 and, in register v, row
+// 8 (v / 4) + 4 (i / 32) + v % 4.  Two MFMAs (outputs j0 .. j0+31 and j0+32 .. j0+63)
+// followed by v_permlane32_swap on each register pair leave lane i with every row of
+// output j0 + i.  The K slots of A and B pair up by (lane half, register, byte); residue
+// of modulus l sits in half l / H, byte l % H (H = ceil(r / 2)), the rest are zero.
+struct CrtDigitTable {
+  int8_t a[kTableModuli + 1][64][16];  // A operand per r and lane
+  int32_t ne[kTableModuli + 1];        // balanced E digits per r
+};
+
+constexpr CrtDigitTable make_crt_digit_table() {
+  using namespace rns_detail;
+  CrtDigitTable t{};
+  const RnsTable base = make_rns_table();
+  for (int r = 1; r <= kTableModuli; ++r) {
+    U192 big_m = u192(1);
+    for (int l = 0; l < r; ++l) big_m = mul_small(big_m, (uint32_t)base.moduli[l]);
+    const int ne = (bit_length(big_m) + 1 + 7) / 8;   // E_l + 0x80..80 < 256^ne
+    t.ne[r] = ne;
+    const int h_per = (r + 1) / 2;
+    for (int l = 0; l < r; ++l) {
+      const uint32_t m = (uint32_t)base.moduli[l];
+      const U192 cof = div_small(big_m, m);
+      const uint32_t w = inverse_mod(mod_small(cof, m), m);
+      U192 e = mul_small(cof, w);
+      // + 0x80 in each of the ne bytes
+      uint64_t carry = 0;
+      for (int i = 0; i < 6; ++i) {
+        uint32_t add = 0;
+        for (int by = 0; by < 4; ++by)
+          if (4 * i + by < ne) add |= 0x80u << (8 * by);
+        const uint64_t v = (uint64_t)e.w[i] + add + carry;
+        e.w[i] = (uint32_t)v;
+        carry = v >> 32;
+      }
+      // F_l = RN(2^24 w / m) (m = 256: exact), + 0x80808080
+      const uint64_t f = (((uint64_t)w << 25) / m + 1) >> 1;
+      const uint64_t fb = f + 0x80808080ull;
+      const int half = l / h_per, slot = l % h_per;
+      for (int row = 0; row < 32; ++row) {
+        int digit = 0;
+        if (row < ne)
+          digit = (int)((e.w[row / 4] >> (8 * (row % 4))) & 0xffu) - 128;
+        else if (row < ne + 4)
+          digit = (int)((fb >> (8 * (row - ne))) & 0xffu) - 128;
+        t.a[r][row + 32 * half][slot] = (int8_t)digit;
+      }
+    }
+  }
+  return t;
+}
+
+__constant__ CrtDigitTable d_crt = make_crt_digit_table();
+constexpr CrtDigitTable kCrtDigits = make_crt_digit_table();
+
+template <int R>
+struct CrtShape {
+  static constexpr int kH = (R + 1) / 2;             // moduli per lane half
+  static constexpr int kNE = kCrtDigits.ne[R];       // E digit rows
+  static constexpr int kRows = kNE + 4;              // + F digit rows
+  static constexpr int kL = (kNE + 4) / 5;           // 2^40 limbs of X
+  static constexpr int kSwaps = ((kRows + 7) / 8) * 4;  // registers holding used rows
+};
+
+// Symmetric residue of one input value of modulus l (int8 residues pass through).
 template <typename T>
-__device__ __forceinline__ int symmetric(T v, int l, int mod) {
-  if (sizeof(T) == 1) return (int)v;
-  // raw int32 products: reduce to the symmetric residue first
-  if (mod == 256) return (int)(int8_t)(v & 0xff);
+__device__ __forceinline__ uint32_t residue_byte(T v, int l) {
+  if (sizeof(T) == 1) return (uint32_t)(uint8_t)v;
+  const int mod = d_rns.moduli[l];
+  if (mod == 256) return (uint32_t)(v & 0xff);
   constexpr double kMagicD = 6755399441055744.0;
   const double d = (double)v;
   const double q = __builtin_fma(d, d_rns.inv[l], kMagicD) - kMagicD;
-  return (int)__builtin_fma(-q, (double)mod, d);
+  return (uint32_t)((int)__builtin_fma(-q, (double)mod, d) & 0xff);
 }
 
+// B operands of a group from byte loads (any alignment, ragged tails, int32 inputs):
+// lane (half, col) gathers the residues of outputs j0 + col and j0 + 32 + col for the
+// moduli of its half.  Every lane loads from a valid address (column clamped to n - 1,
+// modulus to r - 1) and zeroes what lies outside, so the loads need no branches.
+template <int R, typename T>
+__device__ __forceinline__ void load_b_bytes(const T* __restrict__ src, int64_t stride_r,
+                                             int64_t j0, int64_t n, int half, int col,
+                                             v4i& b1v, v4i& b2v) {
+  using S = CrtShape<R>;
+  const int64_t ja = j0 + col < n ? j0 + col : n - 1;
+  const int64_t jb = j0 + 32 + col < n ? j0 + 32 + col : n - 1;
+  const bool va = j0 + col < n, vb = j0 + 32 + col < n;
+  uint32_t w1[4] = {0u, 0u, 0u, 0u}, w2[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int slot = 0; slot < S::kH; ++slot) {
+    const int l0 = half * S::kH + slot;
+    const bool vl = l0 < R;
+    const int l = vl ? l0 : R - 1;
+    const T* p = src + l * stride_r;
+    const uint32_t b1 = residue_byte<T>(p[ja], l);
+    const uint32_t b2 = residue_byte<T>(p[jb], l);
+    w1[slot / 4] |= (vl && va ? b1 : 0u) << (8 * (slot % 4));
+    w2[slot / 4] |= (vl && vb ? b2 : 0u) << (8 * (slot % 4));
+  }
+  b1v = v4i{(int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
+  b2v = v4i{(int)w2[0], (int)w2[1], (int)w2[2], (int)w2[3]};
+}
+
+// B operands of a whole group of 64 int8 residues from dword loads (4-byte aligned
+// rows and planes): in each quad of lanes (col = 4t + u), lane u loads the four outputs
+// 4t .. 4t+3 of modulus (half H + 4d + u) for the first and second 32 outputs (k), and a
+// 4 x 4 byte transpose across the quad (two DPP exchanges, two byte permutes) leaves
+// lane u with the four moduli of output 4t + u, which is dword d of its B operand.  The
+// loads and the transposes are separate steps so that several groups' loads can be in
+// flight before the first transpose waits for its data.
+template <int R>
+struct WordLoads {
+  static constexpr int kND = (CrtShape<R>::kH + 3) / 4;
+  uint32_t w[2][kND];
+};
+
+template <int R>
+__device__ __forceinline__ void load_words(const int8_t* __restrict__ src, int64_t stride_r,
+                                           int half, int t, int u, WordLoads<R>& raw) {
+  using S = CrtShape<R>;
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int d = 0; d < WordLoads<R>::kND; ++d) {
+      const int slot = 4 * d + u;
+      const int l0 = half * S::kH + slot;
+      const bool ok = slot < S::kH && l0 < R;
+      const int l = ok ? l0 : R - 1;
+      const uint32_t x = *reinterpret_cast<const uint32_t*>(src + l * stride_r + 32 * k + 4 * t);
+      raw.w[k][d] = ok ? x : 0u;
+    }
+}
+
+template <int R>
+__device__ __forceinline__ void transpose_words(const WordLoads<R>& raw, uint32_t sel1,
+                                                uint32_t sel2, v4i& b1v, v4i& b2v) {
+  uint32_t w[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int d = 0; d < WordLoads<R>::kND; ++d) {
+      const uint32_t x = raw.w[k][d];
+      const uint32_t z = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4e, 0xf, 0xf, true);
+      const uint32_t s1 = __builtin_amdgcn_perm(z, x, sel1);
+      const uint32_t z2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s1, 0xb1, 0xf, 0xf, true);
+      w[k][d] = __builtin_amdgcn_perm(z2, s1, sel2);
+    }
+  b1v = v4i{(int)w[0][0], (int)w[0][1], (int)w[0][2], (int)w[0][3]};
+  b2v = v4i{(int)w[1][0], (int)w[1][1], (int)w[1][2], (int)w[1][3]};
+}
+
+// Persistent waves: each takes groups of 64 consecutive outputs of one row, four groups
+// per iteration (their loads in flight together), lane i finishing output j0 + i.
+// Columns past n read as residue 0 and are not stored.
 template <int R, typename T>
 __global__ __launch_bounds__(256) void crt_kernel(int64_t m, int64_t n, const T* __restrict__ res,
                                                   int64_t ldr, int64_t stride_r,
                                                   const int32_t* __restrict__ ea,
                                                   const int32_t* __restrict__ eb,
                                                   double* __restrict__ c, int64_t ldc) {
-  constexpr int L = R <= 15 ? 3 : 4;
-  constexpr int kConsts = R + R * L + L;
-  __shared__ double sc[kConsts];
-  for (int t = threadIdx.x; t < kConsts; t += blockDim.x) {
-    double v;
-    if (t < R)
-      v = d_rns.frac[R][t];
-    else if (t < R + R * L)
-      v = d_rns.e_limb[R][(t - R) / L][(t - R) % L];
-    else
-      v = d_rns.m_limb[R][t - R - R * L];
-    sc[t] = v;
-  }
-  __syncthreads();
-  // Flat index over (row, quad of 4 columns).
-  const int64_t nq = (n + 3) / 4;
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (g >= m * nq) return;
-  const int64_t i = g / nq;
-  const int64_t j0 = (g - i * nq) * 4;
-  const int cnt = n - j0 >= 4 ? 4 : (int)(n - j0);
-  int f[4];
+  using S = CrtShape<R>;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5, col = lane & 31, t = col >> 2, u = col & 3;
+  // byte selectors of the quad transpose (see load_b_words)
+  const uint32_t sel1 = u < 2 ? 0x05040100u : 0x03020706u;
+  const uint32_t sel2 = (u & 1) ? 0x03070105u : 0x06020400u;
+  const v4i a_op = *reinterpret_cast<const v4i*>(&d_crt.a[R][lane][0]);
+  const int64_t ngroups_row = (n + 63) / 64;
+  const int64_t groups = m * ngroups_row;
+  const int64_t waves = (int64_t)gridDim.x * 4;
+  const bool words = sizeof(T) == 1 &&
+                     ((ldr | stride_r | (int64_t)reinterpret_cast<uintptr_t>(res)) & 3) == 0;
+  double m_limb[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) f[u] = u < cnt ? eb[j0 + u] : 0;
-  const bool vec = cnt == 4 && sizeof(T) == 1 && ((ldr | stride_r | j0) & 3) == 0;
-  {
-    const int32_t e_i = ea[i];
-    const T* src = res + i * ldr + j0;
-    // Symmetric residues of the 4 outputs, one byte each, packed per modulus.
-    int32_t word[R];
-    if (vec) {
+  for (int p = 0; p < 4; ++p) m_limb[p] = d_rns.m_limb[R][p];
+
+  // A group covers outputs j0 .. j0+63 of row i; (i, j0) are wave-uniform and advance
+  // without divisions.
+  auto word_path = [&](int64_t j0) { return words && j0 + 64 <= n; };
+  auto finish_group = [&](int64_t i, int64_t j0, const v4i& b1v, const v4i& b2v) {
+    const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    const v16i d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_op, b1v, zero, 0, 0, 0);
+    const v16i d2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_op, b2v, zero, 0, 0, 0);
+    int sum[S::kRows];
 #pragma unroll
-      for (int l = 0; l < R; ++l) word[l] = *reinterpret_cast<const int32_t*>(src + l * stride_r);
-    } else {
-#pragma unroll
-      for (int l = 0; l < R; ++l) {
-        uint32_t w = 0;
-        for (int u = 0; u < cnt; ++u)
-          w |= ((uint32_t)symmetric<T>(src[l * stride_r + u], l, d_rns.moduli[l]) & 0xffu)
-               << (8 * u);
-        word[l] = (int32_t)w;
-      }
+    for (int v = 0; v < S::kSwaps; ++v) {
+      const auto sw = __builtin_amdgcn_permlane32_swap((unsigned)d1[v], (unsigned)d2[v], false,
+                                                       false);
+      const int row_a = 8 * (v / 4) + v % 4;      // rows of the first register
+      if (row_a < S::kRows) sum[row_a] = (int)sw[0];
+      if (row_a + 4 < S::kRows) sum[row_a + 4] = (int)sw[1];
     }
-    int s[4];
-    bool nan[4];
+    // q from the F rows, then X in 2^40 limbs.
+    const double tq = __builtin_fma(
+        (double)sum[S::kNE + 3], 0x1p24,
+        __builtin_fma((double)sum[S::kNE + 2], 0x1p16,
+                      __builtin_fma((double)sum[S::kNE + 1], 0x1p8, (double)sum[S::kNE])));
+    const double q = __builtin_rint(tq * 0x1p-24);
+    double x[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      s[u] = e_i + f[u];
-      nan[u] = e_i == INT32_MIN || f[u] == INT32_MIN;
+    for (int p = 0; p < S::kL; ++p) x[p] = -q * m_limb[p];   // |q| < 2^11.4: exact
+#pragma unroll
+    for (int b = 0; b < S::kNE; ++b)
+      x[b / 5] = __builtin_fma((double)sum[b], (double)(1ll << (8 * (b % 5))), x[b / 5]);
+    const int64_t j = j0 + lane;
+    if (j < n) {
+      const int32_t e_i = ea[i], f_j = eb[j];
+      const bool nan = e_i == INT32_MIN || f_j == INT32_MIN;
+      c[i * ldc + j] = finish<S::kL>(x, e_i + f_j, nan);
     }
-    double out[4];
-    reconstruct4<R>(word, sc, s, nan, out);
-    double* dst = c + i * ldc + j0;
-    if (cnt == 4 && ((ldc | j0) & 1) == 0) {
-      *reinterpret_cast<double2*>(dst) = make_double2(out[0], out[1]);
-      *reinterpret_cast<double2*>(dst + 2) = make_double2(out[2], out[3]);
-    } else {
-      for (int u = 0; u < cnt; ++u) dst[u] = out[u];
+  };
+  // Position (row, group within the row) of a group, advanced by `waves` groups.
+  struct Pos {
+    int64_t i, jg;
+  };
+  const int64_t g0 = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int64_t adv_i = waves / ngroups_row, adv_j = waves - adv_i * ngroups_row;
+  auto advance = [&](Pos p) {
+    p.i += adv_i;
+    p.jg += adv_j;
+    if (p.jg >= ngroups_row) {
+      p.jg -= ngroups_row;
+      ++p.i;
+    }
+    return p;
+  };
+  constexpr int kG = 4;                           // groups per iteration
+  Pos p{g0 / ngroups_row, g0 - (g0 / ngroups_row) * ngroups_row};
+  for (int64_t g = g0; g < groups; g += kG * waves) {
+    Pos pos[kG];
+    WordLoads<R> raw[kG];
+    pos[0] = p;
+#pragma unroll
+    for (int q = 1; q < kG; ++q) pos[q] = advance(pos[q - 1]);
+    p = advance(pos[kG - 1]);
+    // issue every word load of the iteration first
+#pragma unroll
+    for (int q = 0; q < kG; ++q)
+      if (g + q * waves < groups && word_path(pos[q].jg * 64))
+        load_words<R>(reinterpret_cast<const int8_t*>(res + pos[q].i * ldr) + pos[q].jg * 64,
+                      stride_r, half, t, u, raw[q]);
+#pragma unroll
+    for (int q = 0; q < kG; ++q) {
+      if (g + q * waves >= groups) break;           // wave-uniform
+      const int64_t i = pos[q].i, j0 = pos[q].jg * 64;
+      v4i b1v, b2v;
+      if (word_path(j0))
+        transpose_words<R>(raw[q], sel1, sel2, b1v, b2v);
+      else
+        load_b_bytes<R, T>(res + i * ldr, stride_r, j0, n, half, col, b1v, b2v);
+      finish_group(i, j0, b1v, b2v);
     }
   }
 }
@@ -307,8 +466,11 @@ int launch_crt(int64_t m, int64_t n, int r, const void* res, int res_is_i32, int
                hipStream_t s) {
   if (m <= 0 || n <= 0) return OZK_OK;
   if (r < 1 || r > kMaxModuli) return OZK_EINVAL;
-  const int64_t blocks = (m * ((n + 3) / 4) + 255) / 256;
-  if (blocks > 0x7fffffff) return OZK_EUNSUPPORTED;
+  // Persistent waves (4 per block), each over groups of 64 outputs of a row: enough
+  // blocks to fill the chip a few times over, fewer when there is less work.
+  const int64_t groups = m * ((n + 63) / 64);
+  const int64_t want = (groups + 3) / 4;
+  const int64_t blocks = want < 4096 ? want : 4096;
   dim3 grid((unsigned)blocks);
   Dispatch<1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20>::go(
       r, grid, s, m, n, res, res_is_i32, ldr, stride_r, ea, eb, c, ldc);

@@ -138,9 +138,11 @@ int ozk_modular_residues(int64_t m, int64_t n, int64_t kp, int r, const int8_t* 
 /* ---------------------------------------------------------------- reconstruction
  * [TME4] abstract, the per-output reconstruction term.  For each output, the r
  * int32 products are reduced modulo their moduli, lifted exactly by the Chinese
- * Remainder Theorem to the integer X in [-M/2, M/2), and
+ * Remainder Theorem to the integer X with |X| <= 2^Q (Q = floor(log2((M-1)/2)), the
+ * range the bit budget keeps every emulated dot product in), and
  *     C[i][j] = RN(X * 2^-(exps_a[i] + exps_b[j]))
  * rounded once to nearest even (subnormal results included; overflow gives +-Inf).
+ * Residues of an integer outside that range give an unspecified finite value.
  * A NONFINITE (INT32_MIN) exponent gives NaN.  ldp_in >= n, ldc >= n. */
 int ozk_reconstruct(int64_t m, int64_t n, int r, const int32_t* products, int64_t ldp_in,
                     int64_t stride_p, const int32_t* exps_a, const int32_t* exps_b,

@@ -129,14 +129,14 @@ def test_reconstruct_bit_exact(m, n, k, r, dist):
     assert assert_within_ulps(got.cpu().numpy(), want, 2) == 0
 
 
-def test_reconstruct_extremes():
+@pytest.mark.parametrize("r", [14, 16, 20, 5, 1])
+def test_reconstruct_extremes(r):
     """Subnormal, overflowing and cancelling outputs, NaN exponents, raw int32 inputs
-    (not reduced) and residues of an X near +-(M-1)/2."""
-    announce("reconstruct extremes")
-    r = 14
-    big_m, _ = rns.crt_basis(r)
+    (not reduced) and residues of X = +-2^Q, the end of the range the bit budget keeps
+    every emulated dot product in."""
+    announce(f"reconstruct extremes r={r}")
     ms = rns.moduli(r)
-    half = (big_m - 1) // 2
+    half = 2 ** rns.budget_q(r)
     rng = np.random.default_rng(0)
     xs = [0, 1, -1, half, -half, half - 12345, 2**60 + 1, -(2**53 + 1), 2**53 + 3, 3, 5, 7]
     xs += [int(v) for v in rng.integers(-2**62, 2**62, size=20)]
@@ -144,6 +144,8 @@ def test_reconstruct_extremes():
     ties = [2**93 + 2**40, 2**93 + 2**40 + 1, -(2**93 + 2**40 + 1), 2**53 + 1, 2**53 + 3,
             (2**53 + 1) * 2**40 + 7, 2**80 + 2**27, 2**80 + 2**27 + 5, 2**101 + 2**48 + 3]
     xs += ties
+    # every X must lie in [-2^Q, 2^Q]: fold the ones a small r cannot hold
+    xs = [((x + half) % (2 * half + 1)) - half for x in xs]
     shifts = [0, 1075, 1076, 1074, 1100, -970, -1000, 60, -10, 1075, 1075, 1075]
     shifts += [int(v) for v in rng.integers(-900, 1200, size=20)]
     shifts += [0, 0, 0, 0, 0, 40, 0, 3, 1100]
