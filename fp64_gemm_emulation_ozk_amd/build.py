@@ -27,6 +27,9 @@ COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
 # Packed fp32 instructions are disabled for all device code.
 DEVICE_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
                 "-packed-fp32-ops"]
+# Per-source additions.  The CRT reads every MFMA result straight into VALU work
+# (cross-lane swaps, conversions): results in VGPRs save a copy out of the AGPRs each.
+EXTRA_FLAGS = {"crt.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:
@@ -40,6 +43,7 @@ def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     cmd = [_hipcc(), *COMMON_FLAGS]
     cmd += DEVICE_FLAGS
+    cmd += EXTRA_FLAGS.get(src, [])
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
