@@ -690,7 +690,9 @@ def main() -> int:
             f()
             ms = _time_events(f, reps, stream)
             sweep.append({"r": rr, "ms": round(ms, 4),
-                          "tflops": round(2.0 * M * N * K / ms / 1e9, 2)})
+                          "tflops": round(2.0 * M * N * K / ms / 1e9, 2),
+                          "rel_vs_native": float(torch.linalg.norm(out - ref) /
+                                                 torch.linalg.norm(ref))})
             del wsr
         extras["r_sweep"] = sweep
         # Norm (Cauchy-Schwarz) scaling rule against the max rule on the same operands:

@@ -58,6 +58,23 @@ DgemmLayout dgemm_layout(int64_t m, int64_t n, int64_t k, int r) {
 
 int check_r(int r) { return (r >= 1 && r <= kMaxModuli) ? OZK_OK : OZK_EINVAL; }
 
+// First pass of a column deconstruction: the column maxima (max rule, into scratch as
+// maxbits) or the norm-rule exponents (chunk partials in scratch, exponents into exps).
+int cols_prep(const double* x, int64_t rows, int64_t cols, int64_t ldx, int scaling, int width,
+              void* scratch, int32_t* exps, hipStream_t s) {
+  int st;
+  if (scaling == OZK_SCALING_NORM) {
+    Carver cv(scratch);
+    const size_t n = (size_t)cols * norm_chunks(rows, cols, 1) * 8;
+    uint64_t* pmax = static_cast<uint64_t*>(cv.take(n));
+    double* ps = static_cast<double*>(cv.take(n));
+    return launch_norm_exps(x, rows, cols, ldx, 1, width, pmax, ps, exps, s);
+  }
+  uint64_t* maxbits = static_cast<uint64_t*>(scratch);
+  if ((st = launch_fill_u64(maxbits, cols, 0, s)) != OZK_OK) return st;
+  return launch_absmax(x, rows, cols, ldx, 1, maxbits, s);
+}
+
 // Deconstruct one operand (axis 0: per-row, axis 1: per-column) into planes by either
 // scaling rule; width is P (max rule) or alpha (norm rule) of this operand and scratch
 // holds deconstruct_scratch(rows, cols, axis) bytes.
@@ -68,22 +85,55 @@ int deconstruct_impl(const double* x, int64_t rows, int64_t cols, int64_t ldx, i
   if (axis == 0 && rows_fused_supported(cols))
     return launch_residues_rows_fused(x, rows, cols, ldx, r, scaling, width, planes, ldp,
                                       plane_stride, exps, s);
-  const int64_t lines = axis == 0 ? rows : cols;
-  if (scaling == OZK_SCALING_NORM) {
+  const int norm = scaling == OZK_SCALING_NORM;
+  if (axis == 1) {
+    if ((st = cols_prep(x, rows, cols, ldx, scaling, width, scratch, exps, s)) != OZK_OK)
+      return st;
+    return launch_residues(x, rows, cols, ldx, 1, r, width,
+                           static_cast<const uint64_t*>(scratch), planes, ldp, plane_stride,
+                           exps, norm, s);
+  }
+  if (norm) {
     Carver cv(scratch);
-    const size_t n = (size_t)lines * norm_chunks(rows, cols, axis) * 8;
+    const size_t n = (size_t)rows * norm_chunks(rows, cols, 0) * 8;
     uint64_t* pmax = static_cast<uint64_t*>(cv.take(n));
     double* ps = static_cast<double*>(cv.take(n));
-    if ((st = launch_norm_exps(x, rows, cols, ldx, axis, width, pmax, ps, exps, s)) != OZK_OK)
+    if ((st = launch_norm_exps(x, rows, cols, ldx, 0, width, pmax, ps, exps, s)) != OZK_OK)
       return st;
-    return launch_residues(x, rows, cols, ldx, axis, r, width, nullptr, planes, ldp,
+    return launch_residues(x, rows, cols, ldx, 0, r, width, nullptr, planes, ldp,
                            plane_stride, exps, 1, s);
   }
   uint64_t* maxbits = static_cast<uint64_t*>(scratch);
-  if ((st = launch_fill_u64(maxbits, lines, 0, s)) != OZK_OK) return st;
-  if ((st = launch_absmax(x, rows, cols, ldx, axis, maxbits, s)) != OZK_OK) return st;
-  return launch_residues(x, rows, cols, ldx, axis, r, width, maxbits, planes, ldp, plane_stride,
+  if ((st = launch_fill_u64(maxbits, rows, 0, s)) != OZK_OK) return st;
+  if ((st = launch_absmax(x, rows, cols, ldx, 0, maxbits, s)) != OZK_OK) return st;
+  return launch_residues(x, rows, cols, ldx, 0, r, width, maxbits, planes, ldp, plane_stride,
                          exps, 0, s);
+}
+
+// Both operands of a product: B's first pass, then A's rows and B's residues in one
+// launch where that applies, else one operand after the other.
+int deconstruct_operands(const double* A, int64_t m, int64_t k, int64_t lda, const double* B,
+                         int64_t n, int64_t ldb, int r, int scaling, int wa, int wb,
+                         int8_t* planes_a, int8_t* planes_b, int64_t kp, int32_t* exps_a,
+                         int32_t* exps_b, void* scr_a, void* scr_b, hipStream_t s) {
+  int st;
+  if (!rows_fused_supported(k) || k > 8192) {
+    if ((st = deconstruct_impl(A, m, k, lda, 0, r, scaling, wa, planes_a, kp, m * kp, exps_a,
+                               scr_a, s)))
+      return st;
+    return deconstruct_impl(B, k, n, ldb, 1, r, scaling, wb, planes_b, kp, n * kp, exps_b,
+                            scr_b, s);
+  }
+  if ((st = cols_prep(B, k, n, ldb, scaling, wb, scr_b, exps_b, s)) != OZK_OK) return st;
+  st = launch_deconstruct_pair(A, m, k, lda, B, n, ldb, r, scaling, wa, wb,
+                               static_cast<const uint64_t*>(scr_b), planes_a, planes_b, kp,
+                               exps_a, exps_b, s);
+  if (st != OZK_EUNSUPPORTED) return st;
+  if ((st = launch_residues_rows_fused(A, m, k, lda, r, scaling, wa, planes_a, kp, m * kp,
+                                       exps_a, s)))
+    return st;
+  return launch_residues(B, k, n, ldb, 1, r, wb, static_cast<const uint64_t*>(scr_b), planes_b,
+                         kp, n * kp, exps_b, scaling == OZK_SCALING_NORM, s);
 }
 
 }  // namespace
@@ -241,11 +291,8 @@ int ozk_dgemm_ex(int64_t m, int64_t n, int64_t k, const double* A, int64_t lda,
   void* scr_b = cv.take(L.scr_b);
   hipStream_t s = as_stream(stream);
   const int64_t kp = L.kp;
-  if ((st = deconstruct_impl(A, m, k, lda, 0, r, scaling, wa, planes_a, kp, m * kp, exps_a,
-                             scr_a, s)))
-    return st;
-  if ((st = deconstruct_impl(B, k, n, ldb, 1, r, scaling, wb, planes_b, kp, n * kp, exps_b,
-                             scr_b, s)))
+  if ((st = deconstruct_operands(A, m, k, lda, B, n, ldb, r, scaling, wa, wb, planes_a,
+                                 planes_b, kp, exps_a, exps_b, scr_a, scr_b, s)))
     return st;
   if ((st = launch_gemm_i8(m, n, kp, r, planes_a, m * kp, planes_b, n * kp, residues, n, m * n,
                            kEpiResidues, s)))

@@ -164,17 +164,19 @@ __global__ __launch_bounds__(256) void residues_rows_kernel(
 // one whole 128-byte line of each plane row (16 bytes each), and each load instruction
 // reads 8 rows x 8 columns (the four waves of a block read the 32 columns of a row, so
 // every line is fetched once).
+// Block (bx, by) of the column residues: 32 columns x 128 K positions.
 template <bool kWide, bool kGiven>
-__global__ __launch_bounds__(256) void residues_cols_kernel(
-    const double* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, ResidueConsts K,
-    int p_bits, const uint64_t* __restrict__ maxbits, int8_t* __restrict__ planes,
-    int64_t ldp, int64_t plane_stride, int32_t* __restrict__ exps) {
-  const int64_t col = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+__device__ __forceinline__ void cols_block(
+    int64_t bx, int64_t by, const double* __restrict__ x, int64_t rows, int64_t cols,
+    int64_t ldx, const ResidueConsts& K, int p_bits, const uint64_t* __restrict__ maxbits,
+    int8_t* __restrict__ planes, int64_t ldp, int64_t plane_stride,
+    int32_t* __restrict__ exps) {
+  const int64_t col = bx * 32 + (threadIdx.x >> 3);
   if (col >= cols) return;
-  const int64_t h0 = (int64_t)blockIdx.y * 128 + (threadIdx.x & 7) * 16;
+  const int64_t h0 = by * 128 + (threadIdx.x & 7) * 16;
   if (h0 >= ldp) return;  // ldp is a multiple of 64: the last block row may be half full
   const int e = kGiven ? exps[col] : line_exponent(maxbits[col], p_bits);
-  if (!kGiven && blockIdx.y == 0 && (threadIdx.x & 7) == 0) exps[col] = e;
+  if (!kGiven && by == 0 && (threadIdx.x & 7) == 0) exps[col] = e;
   double a[16];
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
@@ -184,14 +186,22 @@ __global__ __launch_bounds__(256) void residues_cols_kernel(
   store_residues<kWide, 16>(a, e == INT32_MIN ? 0 : e, K, planes + col * ldp + h0, plane_stride);
 }
 
+template <bool kWide, bool kGiven>
+__global__ __launch_bounds__(256) void residues_cols_kernel(
+    const double* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, ResidueConsts K,
+    int p_bits, const uint64_t* __restrict__ maxbits, int8_t* __restrict__ planes,
+    int64_t ldp, int64_t plane_stride, int32_t* __restrict__ exps) {
+  cols_block<kWide, kGiven>(blockIdx.x, blockIdx.y, x, rows, cols, ldx, K, p_bits, maxbits,
+                            planes, ldp, plane_stride, exps);
+}
+
 // One workgroup per row, the row in registers: kNT threads x kG groups of 8 elements.
 // `width` is P of the max rule, or alpha of the norm rule (kNorm).
 template <bool kWide, bool kVec, int kNT, int kG, bool kNorm>
-__global__ __launch_bounds__(kNT) void residues_rows_fused_kernel(
-    const double* __restrict__ x, int64_t cols, int64_t ldx, ResidueConsts K, int width,
-    int8_t* __restrict__ planes, int64_t ldp, int64_t plane_stride,
-    int32_t* __restrict__ exps) {
-  const int64_t row = blockIdx.x;
+__device__ __forceinline__ void rows_fused_block(
+    int64_t row, const double* __restrict__ x, int64_t cols, int64_t ldx,
+    const ResidueConsts& K, int width, int8_t* __restrict__ planes, int64_t ldp,
+    int64_t plane_stride, int32_t* __restrict__ exps) {
   const double* xr = x + row * ldx;
   double a[kG][8];
   uint64_t v = 0;
@@ -265,6 +275,58 @@ __global__ __launch_bounds__(kNT) void residues_rows_fused_kernel(
     for (int l = 0; l < K.r; ++l)
       *reinterpret_cast<uint2*>(prow + l * plane_stride + h0) = make_uint2(0u, 0u);
   }
+}
+
+template <bool kWide, bool kVec, int kNT, int kG, bool kNorm>
+__global__ __launch_bounds__(kNT) void residues_rows_fused_kernel(
+    const double* __restrict__ x, int64_t cols, int64_t ldx, ResidueConsts K, int width,
+    int8_t* __restrict__ planes, int64_t ldp, int64_t plane_stride,
+    int32_t* __restrict__ exps) {
+  rows_fused_block<kWide, kVec, kNT, kG, kNorm>(blockIdx.x, x, cols, ldx, K, width, planes,
+                                                ldp, plane_stride, exps);
+}
+
+// Both operands of a product in one launch: the rows of A (fused, one block per row)
+// and the column residues of B (exponents or maxima of B already computed), their
+// blocks interleaved so that the VALU-heavier row blocks and the store-heavier column
+// blocks share the chip.  Block b < 2 min(nA, nB) takes A row b / 2 (even b) or B block
+// b / 2 (odd b); the rest go to whichever operand has more.
+struct PairArgs {
+  const double* a;
+  int64_t m, k, lda;
+  ResidueConsts ka;
+  int width_a;
+  int8_t* planes_a;
+  int32_t* exps_a;
+  const double* b;
+  int64_t n, ldb;
+  ResidueConsts kb;
+  int width_b;
+  const uint64_t* maxbits_b;
+  int8_t* planes_b;
+  int32_t* exps_b;
+  int64_t kp, gx_b, blocks_b;
+};
+
+template <bool kWide, bool kVec, int kG, bool kNorm>
+__global__ __launch_bounds__(256) void deconstruct_pair_kernel(PairArgs p) {
+  const int64_t b = blockIdx.x;
+  const int64_t both = p.m < p.blocks_b ? p.m : p.blocks_b;
+  bool is_a;
+  int64_t idx;
+  if (b < 2 * both) {
+    is_a = (b & 1) == 0;
+    idx = b >> 1;
+  } else {
+    is_a = p.m > p.blocks_b;
+    idx = both + (b - 2 * both);
+  }
+  if (is_a)
+    rows_fused_block<kWide, kVec, 256, kG, kNorm>(idx, p.a, p.k, p.lda, p.ka, p.width_a,
+                                                  p.planes_a, p.kp, p.m * p.kp, p.exps_a);
+  else
+    cols_block<kWide, kNorm>(idx % p.gx_b, idx / p.gx_b, p.b, p.k, p.n, p.ldb, p.kb, p.width_b,
+                             p.maxbits_b, p.planes_b, p.kp, p.n * p.kp, p.exps_b);
 }
 
 // Norm rule outside the fused kernel.  The line is cut into chunks; each chunk writes
@@ -469,6 +531,45 @@ int launch_residues(const double* x, int64_t rows, int64_t cols, int64_t ldx, in
 }
 
 bool rows_fused_supported(int64_t cols) { return cols <= 32768; }
+
+int launch_deconstruct_pair(const double* a, int64_t m, int64_t k, int64_t lda, const double* b,
+                            int64_t n, int64_t ldb, int r, int scaling, int width_a, int width_b,
+                            const uint64_t* maxbits_b, int8_t* planes_a, int8_t* planes_b,
+                            int64_t kp, int32_t* exps_a, int32_t* exps_b, hipStream_t s) {
+  const ResidueConsts& ka = *residue_consts(r, width_a);
+  const ResidueConsts& kb = *residue_consts(r, width_b);
+  if (ka.wide != kb.wide || k > 8192 || m <= 0 || n <= 0) return OZK_EUNSUPPORTED;
+  PairArgs p;
+  p.a = a; p.m = m; p.k = k; p.lda = lda; p.ka = ka; p.width_a = width_a;
+  p.planes_a = planes_a; p.exps_a = exps_a;
+  p.b = b; p.n = n; p.ldb = ldb; p.kb = kb; p.width_b = width_b; p.maxbits_b = maxbits_b;
+  p.planes_b = planes_b; p.exps_b = exps_b; p.kp = kp;
+  p.gx_b = (n + 31) / 32;
+  p.blocks_b = p.gx_b * ((kp + 127) / 128);
+  const int64_t blocks = m + p.blocks_b;
+  if (blocks > 0x7fffffff) return OZK_EUNSUPPORTED;
+  const bool vec = (reinterpret_cast<uintptr_t>(a) & 15) == 0 && (lda & 1) == 0;
+  const bool norm = scaling == OZK_SCALING_NORM;
+  const int g = k <= 2048 ? 1 : (k <= 4096 ? 2 : 4);
+  const dim3 grid((unsigned)blocks);
+#define OZK_PAIR(W, V, G, N) \
+  hipLaunchKernelGGL((deconstruct_pair_kernel<W, V, G, N>), grid, dim3(256), 0, s, p)
+#define OZK_PAIR_G(W, V, N)              \
+  if (g == 1) OZK_PAIR(W, V, 1, N);      \
+  else if (g == 2) OZK_PAIR(W, V, 2, N); \
+  else OZK_PAIR(W, V, 4, N)
+#define OZK_PAIR_N(W, V)                        \
+  if (norm) { OZK_PAIR_G(W, V, true); }         \
+  else { OZK_PAIR_G(W, V, false); }
+  if (ka.wide && vec) { OZK_PAIR_N(true, true) }
+  else if (ka.wide) { OZK_PAIR_N(true, false) }
+  else if (vec) { OZK_PAIR_N(false, true) }
+  else { OZK_PAIR_N(false, false) }
+#undef OZK_PAIR_N
+#undef OZK_PAIR_G
+#undef OZK_PAIR
+  return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
+}
 
 int64_t norm_chunks(int64_t rows, int64_t cols, int axis) {
   return axis == 0 ? (cols + 2047) / 2048 : (rows + 127) / 128;

@@ -72,6 +72,14 @@ int launch_residues_rows_fused(const double* x, int64_t rows, int64_t cols, int6
                                int r, int scaling, int width, int8_t* planes, int64_t ldp,
                                int64_t plane_stride, int32_t* exps, hipStream_t s);
 bool rows_fused_supported(int64_t cols);
+// A (rows, fused) and B (column residues) of one product in a single launch, for k <=
+// 8192 and equal residue arithmetic on both sides; B's exponents (norm rule) or maxima
+// (max rule, maxbits_b) must already be in place.  OZK_EUNSUPPORTED when not
+// applicable (the caller then deconstructs the operands one after the other).
+int launch_deconstruct_pair(const double* a, int64_t m, int64_t k, int64_t lda, const double* b,
+                            int64_t n, int64_t ldb, int r, int scaling, int width_a, int width_b,
+                            const uint64_t* maxbits_b, int8_t* planes_a, int8_t* planes_b,
+                            int64_t kp, int32_t* exps_a, int32_t* exps_b, hipStream_t s);
 // Norm rule, unfused paths: per-chunk maxima and scaled sums of squares into pmax/ps
 // (norm_chunks(...) entries per line each), then the exponents from them.
 int64_t norm_chunks(int64_t rows, int64_t cols, int axis);

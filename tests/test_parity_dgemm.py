@@ -247,3 +247,27 @@ def test_dgemm_square_4096_sampled(r):
     want = ozaki2.dgemm(a, b, r, rows=rows, cols=cols)
     sub = got[torch.as_tensor(rows, device=got.device)][:, torch.as_tensor(cols, device=got.device)]
     assert assert_within_ulps(sub.cpu().numpy(), want, 2) == 0
+
+
+def test_dgemm_4096_error_vs_r():
+    """The 4096^3 workload's output error against the exact product, on a sampled block,
+    as r sweeps 12..18: it falls with every added modulus and reaches normwise 1e-15 at
+    r = 16 (the configuration the benchmark times)."""
+    announce("dgemm 4096^3 error vs r")
+    a, b = ozk_inputs.gemm_operands(4096, 4096, 4096, seed=2, dist="phi", phi=0.5)
+    da, db = to_dev(a), to_dev(b)
+    rng = np.random.default_rng(11)
+    rows = np.sort(rng.choice(4096, 6, replace=False))
+    cols = np.sort(rng.choice(4096, 48, replace=False))
+    exact = reference.exact_matmul(a[rows], b[:, cols])
+    r_i = torch.as_tensor(rows, device=da.device)
+    c_i = torch.as_tensor(cols, device=da.device)
+    errs = {}
+    for r in range(12, 19):
+        got = ozk.ozk_dgemm(da, db, r)[r_i][:, c_i].cpu().numpy()
+        errs[r] = float(np.linalg.norm(got - exact) / np.linalg.norm(exact))
+    announce(f"errors {errs}")
+    assert errs[16] <= 1e-15
+    assert errs[12] > 1e-13
+    for r in range(12, 16):
+        assert errs[r + 1] < errs[r] / 4
