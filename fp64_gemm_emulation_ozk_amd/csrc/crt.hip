@@ -364,17 +364,22 @@ __global__ __launch_bounds__(256) void crt_kernel(int64_t m, int64_t n, const T*
       if (row_a + 4 < S::kRows) sum[row_a + 4] = (int)sw[1];
     }
     // q from the F rows, then X in 2^40 limbs.
-    const double tq = __builtin_fma(
-        (double)sum[S::kNE + 3], 0x1p24,
-        __builtin_fma((double)sum[S::kNE + 2], 0x1p16,
-                      __builtin_fma((double)sum[S::kNE + 1], 0x1p8, (double)sum[S::kNE])));
+    // Adjacent digit sums are first combined in int32 (|S_b + 256 S_b+1| < 2^27), which
+    // halves the conversions to fp64.
+    const int f01 = sum[S::kNE] + 256 * sum[S::kNE + 1];
+    const int f23 = sum[S::kNE + 2] + 256 * sum[S::kNE + 3];
+    const double tq = __builtin_fma((double)f23, 0x1p16, (double)f01);
     const double q = __builtin_rint(tq * 0x1p-24);
     double x[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int p = 0; p < S::kL; ++p) x[p] = -q * m_limb[p];   // |q| < 2^11.4: exact
 #pragma unroll
-    for (int b = 0; b < S::kNE; ++b)
-      x[b / 5] = __builtin_fma((double)sum[b], (double)(1ll << (8 * (b % 5))), x[b / 5]);
+    for (int b = 0; b < S::kNE; ++b) {
+      const int pos = b % 5;           // digit position inside its 2^40 limb
+      if (pos == 1 || pos == 3) continue;  // folded into the digit below
+      const int v = (pos != 4 && b + 1 < S::kNE) ? sum[b] + 256 * sum[b + 1] : sum[b];
+      x[b / 5] = __builtin_fma((double)v, (double)(1ll << (8 * pos)), x[b / 5]);
+    }
     const int64_t j = j0 + lane;
     if (j < n) {
       const int32_t e_i = ea[i], f_j = eb[j];
