@@ -103,7 +103,8 @@ def _traffic(kernel: str, digest: str):
 
 # Kernels summarised from the counter passes: key -> (kernel-name substring, sources).
 COUNTER_KERNELS = {
-    "gemm_i8_residues": ("gemm_i8_kernel<1>", ["gemm_i8.hip"]),
+    "gemm_i8_residues": ("gemm_i8_kernel<1", ["gemm_i8.hip"]),
+    "deconstruct_pair": ("deconstruct_pair_kernel", ["deconstruct.hip"]),
     "residues_rows_fused": ("residues_rows_fused_kernel", ["deconstruct.hip"]),
     "absmax_cols": ("absmax_cols_kernel", ["deconstruct.hip"]),
     "residues_cols": ("residues_cols_kernel", ["deconstruct.hip"]),
@@ -114,7 +115,8 @@ COUNTER_KERNELS = {
 def run_counter_workload() -> int:
     """Launches profiled by the rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE): a
     plain device copy of COPY_BYTES (calibration), then two default steps (their kernels:
-    deconstruction of A and B, the residue GEMM, CRT).  Nothing is timed."""
+    deconstruction of A and B, the residue GEMM, CRT) and each operand's deconstruction
+    on its own.  Nothing is timed."""
     import torch
 
     import fp64_gemm_emulation_ozk_amd as ozk
@@ -133,6 +135,9 @@ def run_counter_workload() -> int:
     ws = torch.empty(ozk.ozk_dgemm_workspace_size(M, N, K, 16), dtype=torch.uint8, device=dev)
     for _ in range(2):
         ozk.ozk_dgemm(da, db, 16, out=out, workspace=ws)
+    # each operand's deconstruction on its own (the step runs them in one launch)
+    ozk.ozk_deconstruct(da, 0, 16)
+    ozk.ozk_deconstruct(db, 1, 16, k_budget=K)
     torch.cuda.synchronize()
     print("counter workload done", flush=True)
     return 0
@@ -208,13 +213,14 @@ TME_KERNELS = {
     "gemv_digits_32768_r14_8cols": ("gemv_digits_kernel<4>", "element of A", 32768 * 32768, 14),
     "gemv_stored_32768_r14_1col": ("gemv_stored_kernel", "element of A", 32768 * 32768, 14),
     "crt_4096_r16": ("crt_kernel<16", "output", 4096 * 4096, 16),
-    "gemm_i8_4096_r16": ("gemm_i8_kernel<1>", "output x modulus", 4096 * 4096 * 16, 16),
+    "gemm_i8_4096_r16": ("gemm_i8_kernel<1,", "output x modulus", 4096 * 4096 * 16, 16),
 }
 
 
 def run_tme_workload() -> int:
     """Launches profiled by the time-model counter pass (instruction counts only; nothing
-    is timed): two DGEMM steps of the 4096^3 r=16 workload, then the 32768^2 r=14 GEMV
+    is timed): two DGEMM steps of the 4096^3 r=16 workload and each operand's
+    deconstruction on its own, then the 32768^2 r=14 GEMV
     workload's deconstruction and one on-the-fly call for 1, 8 and 32 columns and one
     stored-plane call for 1 column."""
     import numpy as np
@@ -230,6 +236,8 @@ def run_tme_workload() -> int:
     ws = torch.empty(ozk.ozk_dgemm_workspace_size(M, N, K, 16), dtype=torch.uint8, device=dev)
     for _ in range(2):
         ozk.ozk_dgemm(da, db, 16, out=out, workspace=ws)
+    ozk.ozk_deconstruct(da, 0, 16)
+    ozk.ozk_deconstruct(db, 1, 16, k_budget=K)
     torch.cuda.synchronize()
     del da, db, out, ws
     mg, r = 32768, 14
