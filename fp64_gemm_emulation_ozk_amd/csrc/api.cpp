@@ -45,7 +45,8 @@ struct DgemmLayout {
 
 DgemmLayout dgemm_layout(int64_t m, int64_t n, int64_t k, int r) {
   DgemmLayout L;
-  L.kp = round_up(k, kPlaneK);
+  // K padded to whole 128-byte rows: the products then stream whole cache lines.
+  L.kp = round_up(k, 2 * kPlaneK);
   L.planes_a = (size_t)r * m * L.kp;
   L.planes_b = (size_t)r * n * L.kp;
   L.residues = (size_t)r * m * n;

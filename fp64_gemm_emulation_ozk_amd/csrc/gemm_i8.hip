@@ -97,6 +97,95 @@ struct WaveLayout {
 };
 static_assert(BM * kOutPitch <= kStages * kStageBytes, "residue staging must fit the ring");
 
+// Epilogue of a 256 x 256 tile: the int32 products, or their residues modulo m_l staged
+// through LDS (the ring is free: every wave has passed its last read and load wait).
+template <int kEpi, int NW>
+__device__ __forceinline__ void tile_epilogue(
+    const v16i (&acc)[WaveLayout<NW>::TI][WaveLayout<NW>::TJ], int8_t* lds, int64_t m,
+    int64_t n, int l, int64_t row0, int64_t col0, int grp, int wq, int wave, int lane,
+    const EpiModuli& E, void* __restrict__ out, int64_t ldo, int64_t stride_o, int vec_out) {
+  using WL = WaveLayout<NW>;
+  constexpr int TI = WL::TI, TJ = WL::TJ;
+
+  // The MFMA runs with the B fragment as its first operand, so each accumulator tile is
+  // C^T: lane -> row (lane & 31) of the 32 x 32 block of C, register v -> column
+  // 8*(v/4) + 4*(lane/32) + (v%4); registers 4q..4q+3 hold 4 consecutive columns.
+  const int mod = E.mod[l];
+  const double inv = E.inv[l];
+  const int64_t wrow0 = row0 + grp * 128, wcol0 = col0 + wq * WL::WN;
+  if (kEpi == kEpiProducts) {
+    int32_t* o = reinterpret_cast<int32_t*>(out) + l * stride_o;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int64_t row = wrow0 + i * 32 + (lane & 31);
+      if (row >= m) continue;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = wcol0 + j * 32 + 8 * q + 4 * (lane >> 5);
+          int32_t* dst = o + row * ldo + col;
+          if (vec_out && col + 4 <= n) {
+            *reinterpret_cast<v4i*>(dst) = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                               acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (col + u < n) dst[u] = acc[i][j][4 * q + u];
+          }
+        }
+    }
+    return;
+  }
+  // Residues: stage the 256 x 256 byte tile in LDS (row pitch 264: the dword writes of
+  // 64 lanes hit distinct banks), then each wave stores 32 rows, 16 lanes x 16 bytes per
+  // 256-byte row.
+  wg_barrier();  // every wave is past its reads and loads of the ring
+  int8_t* tile = lds;
+  // m = 256 keeps the low byte of the product; odd moduli reduce (uniform branch, taken
+  // once per tile rather than per element).
+  auto stage = [&](auto byte_of) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t w = pack4b(byte_of(acc[i][j][4 * q]), byte_of(acc[i][j][4 * q + 1]),
+                                    byte_of(acc[i][j][4 * q + 2]), byte_of(acc[i][j][4 * q + 3]));
+          *reinterpret_cast<uint32_t*>(tile + (grp * 128 + i * 32 + (lane & 31)) * kOutPitch +
+                                       wq * WL::WN + j * 32 + 8 * q + 4 * (lane >> 5)) = w;
+        }
+  };
+  if (mod == 256) {
+    stage([](int v) { return (uint32_t)v; });
+  } else {
+    const uint32_t um = (uint32_t)mod;
+    stage([=](int v) { return residue_byte_odd(v, um, inv); });
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  wg_barrier();  // the whole tile is staged
+  int8_t* o = reinterpret_cast<int8_t*>(out) + l * stride_o;
+#pragma unroll 4
+  for (int s4 = 0; s4 < 64 / NW; ++s4) {
+    const int rl = wave * (BM / NW) + s4 * 4 + (lane >> 4), cl = 16 * (lane & 15);
+    const int64_t row = row0 + rl, col = col0 + cl;
+    const int8_t* srcp = tile + rl * kOutPitch + cl;
+    const uint2 lo = *reinterpret_cast<const uint2*>(srcp);
+    const uint2 hi = *reinterpret_cast<const uint2*>(srcp + 8);
+    if (row >= m) continue;
+    int8_t* dst = o + row * ldo + col;
+    if (vec_out && col + 16 <= n) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    } else {
+      const uint32_t wv[4] = {lo.x, lo.y, hi.x, hi.y};
+      for (int u = 0; u < 16; ++u)
+        if (col + u < n) dst[u] = (int8_t)(wv[u >> 2] >> (8 * (u & 3)));
+    }
+  }
+}
+
+
 template <int kEpi, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_kernel(
     int64_t m, int64_t n, int64_t kp, const int8_t* __restrict__ pa, int64_t stride_a,
@@ -247,83 +336,171 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_kernel(
   }
   // The clamped loads past the last K step are still landing in the ring.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  tile_epilogue<kEpi, NW>(acc, lds, m, n, l, row0, col0, grp, wq, wave, lane, E, out, ldo,
+                          stride_o, vec_out);
+}
 
-  // The MFMA runs with the B fragment as its first operand, so each accumulator tile is
-  // C^T: lane -> row (lane & 31) of the 32 x 32 block of C, register v -> column
-  // 8*(v/4) + 4*(lane/32) + (v%4); registers 4q..4q+3 hold 4 consecutive columns.
-  const int mod = E.mod[l];
-  const double inv = E.inv[l];
-  const int64_t wrow0 = row0 + grp * 128, wcol0 = col0 + wq * WL::WN;
-  if (kEpi == kEpiProducts) {
-    int32_t* o = reinterpret_cast<int32_t*>(out) + l * stride_o;
+
+// Pair-stage variant for kp a multiple of 128: the LDS ring holds two stages of two K
+// steps each (64 KiB: A rows 0..255, then B rows 0..255, 128 bytes per row), so every
+// direct load moves 8 rows x 128 bytes (whole cache lines) instead of 16 rows x 64 bytes
+// (half lines), which is what limits the L2 -> LDS stream of the 64-byte ring.  The
+// eight 16-byte chunks of a row are XOR-swizzled by (row >> 1) & 7: the 16 lanes of a
+// fragment read (rows r .. r+15, one logical chunk) then cover all 64 banks.
+//
+// Per pair p (K bytes 128 p .. 128 p + 127, buffer p % 2) every wave runs four quarters
+// of 8 MFMAs (K sub-chunks of 32), reading the next quarter's fragments between them.
+// After quarter 2 the wave waits for its loads of pair p+1 and for its reads, and the
+// workgroup barrier makes pair p+1 complete and pair p fully read; quarter 3 then reads
+// pair p+1's first fragments and issues this wave's 8 loads of pair p+2 into buffer
+// p % 2, one after each MFMA.  Loads thus have four quarters before their wait.
+constexpr int kPairRow = 128;                       // bytes per row of a pair stage
+constexpr int kPairBytes = (BM + BN) * kPairRow;    // 64 KiB
+static_assert(2 * kPairBytes <= kStages * kStageBytes, "pair ring within the LDS array");
+static_assert(BM * kOutPitch <= 2 * kPairBytes, "residue staging within the pair ring");
+
+__device__ __forceinline__ int swz_pair(int row, int chunk) {
+  return row * kPairRow + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+
+template <int kEpi, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
+    int64_t m, int64_t n, int64_t kp, const int8_t* __restrict__ pa, int64_t stride_a,
+    const int8_t* __restrict__ pb, int64_t stride_b, void* __restrict__ out, int64_t ldo,
+    int64_t stride_o, int tiles_m, int tiles_n, EpiModuli E, int vec_out) {
+  __shared__ __attribute__((aligned(1024))) int8_t lds[kStages * kStageBytes];
+
+  // Block -> (modulus, tile row, tile column): XCD-contiguous, then grouped by kGroupM.
+  const int total = gridDim.x;
+  int bid = blockIdx.x;
+  if (total % kXcds == 0) bid = (bid % kXcds) * (total / kXcds) + bid / kXcds;
+  const int per_mod = tiles_m * tiles_n;
+  const int l = bid / per_mod;
+  const int rem = bid - l * per_mod;
+  const int per_group = kGroupM * tiles_n;
+  const int first_m = (rem / per_group) * kGroupM;
+  const int gsize = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+  const int in_group = rem % per_group;
+  const int tm = first_m + in_group % gsize;
+  const int tn = in_group / gsize;
+  const int8_t* A = pa + l * stride_a;
+  const int8_t* B = pb + l * stride_b;
+  const int64_t row0 = (int64_t)tm * BM;
+  const int64_t col0 = (int64_t)tn * BN;
+
+  using WL = WaveLayout<NW>;
+  constexpr int TI = WL::TI, TJ = WL::TJ, kWaves = NW;
+  constexpr int kRegions = kPairBytes / 1024;          // 64 regions of 8 rows x 128 B
+  constexpr int kLoadsPerWave = kRegions / NW;         // 8 (NW = 8)
+  static_assert(WL::kMfmaHalf == kLoadsPerWave, "one load per MFMA of quarter 3");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int grp = __builtin_amdgcn_readfirstlane(wave / (NW / 2));
+  const int wq = __builtin_amdgcn_readfirstlane(wave % (NW / 2));
+
+  // Region rg = wave + NW q: rows 8 (rg % 32) .. +7 of A (rg < 32) or B; lane i lands at
+  // row 8 (rg % 32) + i / 8, physical chunk i % 8, which holds logical chunk
+  // (i % 8) ^ ((row >> 1) & 7).
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint64_t sbase_a = (uint64_t)(A + row0 * kp), sbase_b = (uint64_t)(B + col0 * kp);
+  uint32_t voff[kLoadsPerWave];
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int64_t row = wrow0 + i * 32 + (lane & 31);
-      if (row >= m) continue;
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t col = wcol0 + j * 32 + 8 * q + 4 * (lane >> 5);
-          int32_t* dst = o + row * ldo + col;
-          if (vec_out && col + 4 <= n) {
-            *reinterpret_cast<v4i*>(dst) = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                                               acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          } else {
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              if (col + u < n) dst[u] = acc[i][j][4 * q + u];
-          }
-        }
-    }
-    return;
+  for (int q = 0; q < kLoadsPerWave; ++q) {
+    const int rg = wave + kWaves * q;
+    const bool is_b = rg >= 32;
+    const int row = 8 * (rg & 31) + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+    const int64_t origin = is_b ? col0 : row0;
+    const int64_t last = (is_b ? n : m) - 1;
+    const int64_t gr = origin + row < last ? origin + row : last;
+    voff[q] = (uint32_t)((gr - origin) * kp + 16 * chunk);
   }
-  // Residues: stage the 256 x 256 byte tile in LDS (row pitch 264: the dword writes of
-  // 64 lanes hit distinct banks), then each wave stores 32 rows, 16 lanes x 16 bytes per
-  // 256-byte row.
-  wg_barrier();  // every wave is past its reads and loads of the ring
-  int8_t* tile = lds;
-  // m = 256 keeps the low byte of the product; odd moduli reduce (uniform branch, taken
-  // once per tile rather than per element).
-  auto stage = [&](auto byte_of) {
+  auto region_base = [&](int q) { return wave_u + kWaves * q >= 32 ? sbase_b : sbase_a; };
+  const uint32_t lds0 = lds_address(lds);
+  const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(lds0 + wave * 1024);
+  const int np = (int)(kp / kPairRow);
+  auto issue_pair = [&](int p) {  // pair p (clamped to the last) into buffer p % 2
+    const int pc = p < np ? p : np - 1;
+    const uint32_t base = wave_lds + (uint32_t)(p & 1) * kPairBytes;
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t w = pack4b(byte_of(acc[i][j][4 * q]), byte_of(acc[i][j][4 * q + 1]),
-                                    byte_of(acc[i][j][4 * q + 2]), byte_of(acc[i][j][4 * q + 3]));
-          *reinterpret_cast<uint32_t*>(tile + (grp * 128 + i * 32 + (lane & 31)) * kOutPitch +
-                                       wq * WL::WN + j * 32 + 8 * q + 4 * (lane >> 5)) = w;
-        }
+    for (int q = 0; q < kLoadsPerWave; ++q)
+      dma16_sbase(voff[q], region_base(q) + (uint64_t)pc * kPairRow, base + q * (kWaves * 1024));
   };
-  if (mod == 256) {
-    stage([](int v) { return (uint32_t)v; });
-  } else {
-    const uint32_t um = (uint32_t)mod;
-    stage([=](int v) { return residue_byte_odd(v, um, inv); });
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  wg_barrier();  // the whole tile is staged
-  int8_t* o = reinterpret_cast<int8_t*>(out) + l * stride_o;
-#pragma unroll 4
-  for (int s4 = 0; s4 < 64 / NW; ++s4) {
-    const int rl = wave * (BM / NW) + s4 * 4 + (lane >> 4), cl = 16 * (lane & 15);
-    const int64_t row = row0 + rl, col = col0 + cl;
-    const int8_t* srcp = tile + rl * kOutPitch + cl;
-    const uint2 lo = *reinterpret_cast<const uint2*>(srcp);
-    const uint2 hi = *reinterpret_cast<const uint2*>(srcp + 8);
-    if (row >= m) continue;
-    int8_t* dst = o + row * ldo + col;
-    if (vec_out && col + 16 <= n) {
-      *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-    } else {
-      const uint32_t wv[4] = {lo.x, lo.y, hi.x, hi.y};
-      for (int u = 0; u < 16; ++u)
-        if (col + u < n) dst[u] = (int8_t)(wv[u >> 2] >> (8 * (u & 3)));
+
+  v16i acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+
+  // Fragments of quarter qq: lane holds row (lane & 31) of a 32-row block and the 16
+  // bytes of logical chunk 2 qq + (lane >> 5); A and B use the same K map.
+  const int frow = lane & 31;
+  const int fchunk = lane >> 5;
+  int offa[TI], offb[TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i) offa[i] = (grp * 128 + i * 32 + frow) * kPairRow;
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) offb[j] = BM * kPairRow + (wq * WL::WN + j * 32 + frow) * kPairRow;
+  const int sw = (frow >> 1) & 7;  // row swizzle (the same for every block: 16 | block rows)
+  v4i fa[2][TI], fb[2][TJ];
+  auto read_frags = [&](const int8_t* st, int qq, v4i (&xa)[TI], v4i (&xb)[TJ]) {
+    const int c = ((2 * qq + fchunk) ^ sw) << 4;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) xa[i] = *reinterpret_cast<const v4i*>(st + offa[i] + c);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) xb[j] = *reinterpret_cast<const v4i*>(st + offb[j] + c);
+  };
+  // 8 MFMAs on fragment set `cur`, the reads of quarter qq of stage st into set `nxt`
+  // between them (qq < 0: no reads), and optionally this wave's loads of pair `lp`.
+  auto quarter = [&](int cur, const int8_t* st, int qq, int lp, bool loads) {
+    const int c = qq >= 0 ? ((2 * qq + fchunk) ^ sw) << 4 : 0;
+    const uint32_t lbase = wave_lds + (uint32_t)(lp & 1) * kPairBytes;
+    const int lpc = lp < np ? lp : np - 1;
+#pragma unroll
+    for (int idx = 0; idx < WL::kMfmaHalf; ++idx) {
+      const int i = idx / TJ, j = idx % TJ;
+      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
+      if (qq >= 0) {
+        if (idx < TI)
+          fa[cur ^ 1][idx] = *reinterpret_cast<const v4i*>(st + offa[idx] + c);
+        else if (idx < TI + TJ)
+          fb[cur ^ 1][idx - TI] = *reinterpret_cast<const v4i*>(st + offb[idx - TI] + c);
+      }
+      if (loads)
+        dma16_sbase(voff[idx], region_base(idx) + (uint64_t)lpc * kPairRow,
+                    lbase + idx * (kWaves * 1024));
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  issue_pair(0);
+  issue_pair(1);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerWave) : "memory");
+  wg_barrier();
+  read_frags(lds, 0, fa[0], fb[0]);
+  for (int p = 0; p < np; ++p) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int8_t* st = lds + (p & 1) * kPairBytes;
+    quarter(0, st, 1, 0, false);
+    quarter(1, st, 2, 0, false);
+    quarter(0, st, 3, 0, false);
+    // pair p+1 has landed (this wave's loads; the barrier covers the others) and every
+    // wave holds its quarter-3 fragments of pair p
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    wg_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const int pn = p + 1 < np ? p + 1 : p;  // past the last pair: a harmless re-read
+    quarter(1, lds + (pn & 1) * kPairBytes, 0, p + 2, true);
   }
+  // The clamped loads past the last pair are still landing in the ring.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  tile_epilogue<kEpi, NW>(acc, lds, m, n, l, row0, col0, grp, wq, wave, lane, E, out, ldo,
+                          stride_o, vec_out);
 }
 
 }  // namespace
@@ -347,14 +524,19 @@ int launch_gemm_i8(int64_t m, int64_t n, int64_t kp, int r, const int8_t* pa, in
   const int vec_out = (reinterpret_cast<uintptr_t>(out) % vbytes) == 0 &&
                       (ldo * elem) % vbytes == 0 && (stride_o * elem) % vbytes == 0;
   constexpr int NW = kWavesDefault;
-  if (epilogue == kEpiProducts)
-    hipLaunchKernelGGL((gemm_i8_kernel<kEpiProducts, NW>), dim3((unsigned)blocks), dim3(64 * NW),
-                       0, s, m, n, kp, pa, stride_a, pb, stride_b, out, ldo, stride_o, tiles_m,
-                       tiles_n, E, vec_out);
-  else
-    hipLaunchKernelGGL((gemm_i8_kernel<kEpiResidues, NW>), dim3((unsigned)blocks), dim3(64 * NW),
-                       0, s, m, n, kp, pa, stride_a, pb, stride_b, out, ldo, stride_o, tiles_m,
-                       tiles_n, E, vec_out);
+  const dim3 grid((unsigned)blocks), block(64 * NW);
+#define OZK_GEMM(K, EPI)                                                                   \
+  hipLaunchKernelGGL((K<EPI, NW>), grid, block, 0, s, m, n, kp, pa, stride_a, pb, stride_b, \
+                     out, ldo, stride_o, tiles_m, tiles_n, E, vec_out)
+  const bool pairs = kp % kPairRow == 0;   // whole-line loads need K in steps of 128
+  if (epilogue == kEpiProducts) {
+    if (pairs) OZK_GEMM(gemm_i8_pairs_kernel, kEpiProducts);
+    else OZK_GEMM(gemm_i8_kernel, kEpiProducts);
+  } else {
+    if (pairs) OZK_GEMM(gemm_i8_pairs_kernel, kEpiResidues);
+    else OZK_GEMM(gemm_i8_kernel, kEpiResidues);
+  }
+#undef OZK_GEMM
   return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
 }
 
