@@ -103,7 +103,7 @@ def _traffic(kernel: str, digest: str):
 
 # Kernels summarised from the counter passes: key -> (kernel-name substring, sources).
 COUNTER_KERNELS = {
-    "gemm_i8_residues": ("gemm_i8_kernel<1", ["gemm_i8.hip"]),
+    "gemm_i8_residues": ("gemm_i8_pairs_kernel<1", ["gemm_i8.hip"]),
     "deconstruct_pair": ("deconstruct_pair_kernel", ["deconstruct.hip"]),
     "residues_rows_fused": ("residues_rows_fused_kernel", ["deconstruct.hip"]),
     "absmax_cols": ("absmax_cols_kernel", ["deconstruct.hip"]),
@@ -213,7 +213,8 @@ TME_KERNELS = {
     "gemv_digits_32768_r14_8cols": ("gemv_digits_kernel<4>", "element of A", 32768 * 32768, 14),
     "gemv_stored_32768_r14_1col": ("gemv_stored_kernel", "element of A", 32768 * 32768, 14),
     "crt_4096_r16": ("crt_kernel<16", "output", 4096 * 4096, 16),
-    "gemm_i8_4096_r16": ("gemm_i8_kernel<1,", "output x modulus", 4096 * 4096 * 16, 16),
+    "gemm_i8_4096_r16": ("gemm_i8_pairs_kernel<1,", "output x modulus", 4096 * 4096 * 16,
+                         16),
 }
 
 
@@ -661,7 +662,7 @@ def main() -> int:
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
                 "traffic": _traffic("gemm_i8_residues", digest),
-                "kernel": "gemm_i8_kernel<residues> (v_mfma_i32_32x32x32_i8)",
+                "kernel": "gemm_i8_pairs_kernel<residues> (v_mfma_i32_32x32x32_i8)",
                 "kernel_ms": round(gemm_ms, 4), "ops_per_launch": ops,
                 "source_digest": digest}
 

@@ -352,8 +352,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_kernel(
 // of 8 MFMAs (K sub-chunks of 32), reading the next quarter's fragments between them.
 // After quarter 2 the wave waits for its loads of pair p+1 and for its reads, and the
 // workgroup barrier makes pair p+1 complete and pair p fully read; quarter 3 then reads
-// pair p+1's first fragments and issues this wave's 8 loads of pair p+2 into buffer
-// p % 2, one after each MFMA.  Loads thus have four quarters before their wait.
+// pair p+1's first fragments and issues half of this wave's 8 loads of pair p+2 into
+// buffer p % 2 (one after every second MFMA), quarter 0 of pair p+1 the other half.
+// Loads thus have three to four quarters before their wait.
 constexpr int kPairRow = 128;                       // bytes per row of a pair stage
 constexpr int kPairBytes = (BM + BN) * kPairRow;    // 64 KiB
 static_assert(2 * kPairBytes <= kStages * kStageBytes, "pair ring within the LDS array");
@@ -454,9 +455,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
 #pragma unroll
     for (int j = 0; j < TJ; ++j) xb[j] = *reinterpret_cast<const v4i*>(st + offb[j] + c);
   };
-  // 8 MFMAs on fragment set `cur`, the reads of quarter qq of stage st into set `nxt`
-  // between them (qq < 0: no reads), and optionally this wave's loads of pair `lp`.
-  auto quarter = [&](int cur, const int8_t* st, int qq, int lp, bool loads) {
+  // 8 MFMAs on fragment set `cur`, the reads of quarter qq of stage st into the other set
+  // between them (qq < 0: no reads), and this wave's loads l0 .. l1-1 of pair `lp` after
+  // every second MFMA.
+  auto quarter = [&](int cur, const int8_t* st, int qq, int lp, int l0, int l1) {
+    const bool loads = l1 > l0;
     const int c = qq >= 0 ? ((2 * qq + fchunk) ^ sw) << 4 : 0;
     const uint32_t lbase = wave_lds + (uint32_t)(lp & 1) * kPairBytes;
     const int lpc = lp < np ? lp : np - 1;
@@ -470,9 +473,12 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
         else if (idx < TI + TJ)
           fb[cur ^ 1][idx - TI] = *reinterpret_cast<const v4i*>(st + offb[idx - TI] + c);
       }
-      if (loads)
-        dma16_sbase(voff[idx], region_base(idx) + (uint64_t)lpc * kPairRow,
-                    lbase + idx * (kWaves * 1024));
+      if (loads && (idx & 1) == 1) {
+        const int q = l0 + (idx >> 1);
+        if (q < l1)
+          dma16_sbase(voff[q], region_base(q) + (uint64_t)lpc * kPairRow,
+                      lbase + q * (kWaves * 1024));
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -485,9 +491,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
   for (int p = 0; p < np; ++p) {
     __builtin_amdgcn_sched_barrier(0);
     const int8_t* st = lds + (p & 1) * kPairBytes;
-    quarter(0, st, 1, 0, false);
-    quarter(1, st, 2, 0, false);
-    quarter(0, st, 3, 0, false);
+    if (p > 0) quarter(0, st, 1, p + 1, 4, 8);
+    else quarter(0, st, 1, 0, 0, 0);
+    quarter(1, st, 2, 0, 0, 0);
+    quarter(0, st, 3, 0, 0, 0);
     // pair p+1 has landed (this wave's loads; the barrier covers the others) and every
     // wave holds its quarter-3 fragments of pair p
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -495,7 +502,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
     wg_barrier();
     __builtin_amdgcn_sched_barrier(0);
     const int pn = p + 1 < np ? p + 1 : p;  // past the last pair: a harmless re-read
-    quarter(1, lds + (pn & 1) * kPairBytes, 0, p + 2, true);
+    quarter(1, lds + (pn & 1) * kPairBytes, 0, p + 2, 0, 4);
   }
   // The clamped loads past the last pair are still landing in the ring.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
