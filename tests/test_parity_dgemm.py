@@ -271,3 +271,40 @@ def test_dgemm_4096_error_vs_r():
     assert errs[12] > 1e-13
     for r in range(12, 16):
         assert errs[r + 1] < errs[r] / 4
+
+
+def test_modular_products_at_the_int32_bound():
+    """kp = 131072 (the largest K the planes allow) with every term (-128)(-128) except
+    one zero K column: the sum 131071 * 2^14 = 2^31 - 2^14 is the largest an int32 must
+    hold exactly, through the whole-line (pair-stage) product kernel."""
+    announce("modular products at the int32 bound")
+    kp, m, n = 131072, 64, 96
+    pa = np.full((1, m, kp), -128, dtype=np.int8)
+    pb = np.full((1, n, kp), -128, dtype=np.int8)
+    pa[:, :, -1] = 0
+    pb[:, 5, :] = 127                     # a column with the other sign
+    pb[:, 5, -1] = 0
+    got = ozk.ozk_modular_products(to_dev(pa), to_dev(pb)).cpu().numpy().astype(np.int64)
+    want = ozaki2.modular_products(pa, pb)
+    np.testing.assert_array_equal(got, want)
+    assert want[0, 0, 0] == 131071 * 2**14 and want[0, 0, 5] == -131071 * 128 * 127
+    got_r = ozk.ozk_modular_residues(to_dev(pa), to_dev(pb), r=1).cpu().numpy()
+    np.testing.assert_array_equal(got_r.astype(np.int64), ((want + 128) % 256) - 128)
+
+
+@pytest.mark.parametrize("scaling", ["max", "norm"])
+def test_dgemm_largest_k(scaling):
+    """k = 131071, the largest inner dimension: row deconstruction by the two-pass path,
+    K padded to 131072, against the oracle (norm rule: fed the GPU exponents)."""
+    announce(f"dgemm k=131071 {scaling}")
+    m, n, k, r = 24, 40, 131071, 16
+    a, b = ozk_inputs.gemm_operands(m, n, k, seed=17, dist="phi", phi=1.0)
+    got = ozk.ozk_dgemm_ex(to_dev(a), to_dev(b), r, scaling).cpu().numpy()
+    if scaling == "max":
+        want = ozaki2.dgemm(a, b, r)
+    else:
+        _, e = ozk.ozk_deconstruct_ex(to_dev(a), 0, r, "norm", k_budget=k)
+        _, f = ozk.ozk_deconstruct_ex(to_dev(b), 1, r, "norm", k_budget=k)
+        want = ozaki2.dgemm(a, b, r, exps=(e.cpu().numpy().astype(np.int64),
+                                          f.cpu().numpy().astype(np.int64)))
+    assert assert_within_ulps(got, want, 2) == 0
