@@ -88,3 +88,33 @@ def uniform_matrix_device(shape, seed: int, device):
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
     return torch.rand(shape, generator=gen, dtype=torch.float64, device=device) * 2.0 - 1.0
+
+
+def poisson_7pt_csr(n: int):
+    """The 7-point operator 6 u_p - (sum of the grid neighbours of p) on an n x n x n
+    grid with neighbours outside the grid dropped, rows in lexicographic order (i, j, k)
+    and columns ascending within each row: (row_ptr int32, col_idx int32, vals float64)."""
+    N = n ** 3
+    p = np.arange(N, dtype=np.int64)
+    i, j, k = p // (n * n), (p // n) % n, p % n
+    # offsets in ascending column order
+    offs = [(-n * n, i > 0), (-n, j > 0), (-1, k > 0), (0, np.ones(N, dtype=bool)),
+            (1, k < n - 1), (n, j < n - 1), (n * n, i < n - 1)]
+    cols = np.stack([p + d for d, _ in offs], axis=1)
+    valid = np.stack([m for _, m in offs], axis=1)
+    vals = np.where(np.arange(7)[None, :] == 3, 6.0, -1.0) * np.ones((N, 1))
+    row_ptr = np.concatenate([[0], np.cumsum(valid.sum(axis=1))]).astype(np.int32)
+    return row_ptr, cols[valid].astype(np.int32), vals[valid].astype(np.float64)
+
+
+def random_csr(rows: int, cols: int, max_len: int, seed: int, phi: float = 0.0):
+    """A CSR matrix with row lengths uniform in [0, max_len] (some rows empty), distinct
+    ascending column indices per row, values U(-1,1) (phi = 0) or (U - 0.5) exp(phi N)."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, max_len + 1, size=rows)
+    row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    col_idx = np.concatenate([np.sort(rng.choice(cols, size=L, replace=False)) for L in lens]
+                             ) if rows else np.zeros(0)
+    nnz = int(row_ptr[-1])
+    vals = (phi_matrix(rng, (1, nnz), phi)[0] if phi > 0 else uniform_matrix(rng, (1, nnz))[0])
+    return row_ptr, col_idx.astype(np.int32), vals
