@@ -18,7 +18,8 @@ __all__ = [
     "LIB_PATH", "OzkError", "library",
     "ozk_version", "ozk_moduli", "ozk_scaling_bits", "ozk_scaling_bits_ex", "ozk_planes_ld",
     "ozk_deconstruct", "ozk_deconstruct_ex", "ozk_modular_products", "ozk_modular_residues",
-    "ozk_reconstruct", "ozk_dgemm", "ozk_dgemm_ex", "ozk_dgemv",
+    "ozk_reconstruct", "ozk_dgemm", "ozk_dgemm_ex", "ozk_dgemv", "ozk_spmv_csr",
+    "ozk_spmv_csr_workspace_size",
     "OZK_SCALING_MAX", "OZK_SCALING_NORM",
     "ozk_fp4limb_pack", "ozk_fp4limb_products", "ozk_int8gemm_fp4limb",
     "ozk_dgemm_workspace_size", "ozk_dgemv_workspace_size",
@@ -55,6 +56,9 @@ _SIGNATURES = {
     "ozk_dgemm_ex": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
                             _ptr, _size, _ptr]),
     "ozk_dgemm_workspace_size": (_int, [_i64, _i64, _i64, _int, _ptr]),
+    "ozk_spmv_csr_workspace_size": (_int, [_i64, _i64, _int, _ptr]),
+    "ozk_spmv_csr": (_int, [_i64, _i64, _i64, _ptr, _ptr, _ptr, _i64, _ptr, _ptr, _int, _ptr,
+                            _size, _ptr]),
     "ozk_dgemm": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _ptr, _size,
                          _ptr]),
     "ozk_dgemv_workspace_size": (_int, [_i64, _i64, _i64, _int, _int, _ptr]),
@@ -133,6 +137,8 @@ def _check(t: torch.Tensor, dtype, name: str, ndim: int = 2):
         raise ValueError(f"{name} must be {ndim}-D")
     if ndim == 2 and t.numel() > 0 and t.stride(1) != 1:
         raise ValueError(f"{name} must be row-major with unit column stride")
+    if ndim == 1 and t.numel() > 1 and t.stride(0) != 1:
+        raise ValueError(f"{name} must be contiguous")
 
 
 def _ld(t: torch.Tensor) -> int:
@@ -337,6 +343,36 @@ def ozk_dgemv(a: torch.Tensor | None, x: torch.Tensor, r: int, mode: int = 0,
     _call("ozk_dgemv", m, k, nrhs, _dev_ptr(a), _ld(a) if a is not None else k,
           _dev_ptr(a_planes), ldp, pstride, _dev_ptr(a_exps), _dev_ptr(x), _ld(x),
           _dev_ptr(out), _ld(out), r, mode, _dev_ptr(workspace), workspace.numel(),
+          _stream(stream))
+    return out
+
+
+def ozk_spmv_csr_workspace_size(rows: int, cols: int, r: int) -> int:
+    return _size_query("ozk_spmv_csr_workspace_size", rows, cols, r)
+
+
+def ozk_spmv_csr(row_ptr: torch.Tensor, col_idx: torch.Tensor, vals: torch.Tensor,
+                 x: torch.Tensor, r: int, max_row_nnz: int | None = None,
+                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """Emulated fp64 y = A x for A in CSR (int32 row_ptr / col_idx, float64 vals).
+    max_row_nnz bounds the entries of a row (it sets the bit budget); when omitted it
+    is read from row_ptr, which synchronises with the device."""
+    _check(row_ptr, torch.int32, "row_ptr", 1)
+    _check(col_idx, torch.int32, "col_idx", 1)
+    _check(vals, torch.float64, "vals", 1)
+    _check(x, torch.float64, "x", 1)
+    rows, cols, nnz = row_ptr.shape[0] - 1, x.shape[0], vals.shape[0]
+    if col_idx.shape[0] != nnz:
+        raise ValueError("col_idx and vals differ in length")
+    if max_row_nnz is None:
+        max_row_nnz = max(int(torch.diff(row_ptr).max().item()) if rows > 0 else 1, 1)
+    if out is None:
+        out = torch.empty(rows, dtype=torch.float64, device=x.device)
+    if workspace is None:
+        workspace = _workspace(ozk_spmv_csr_workspace_size(rows, cols, r), x.device)
+    _call("ozk_spmv_csr", rows, cols, nnz, _dev_ptr(row_ptr), _dev_ptr(col_idx), _dev_ptr(vals),
+          max_row_nnz, _dev_ptr(x), _dev_ptr(out), r, _dev_ptr(workspace), workspace.numel(),
           _stream(stream))
     return out
 

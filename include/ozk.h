@@ -183,6 +183,24 @@ int ozk_dgemv(int64_t m, int64_t k, int64_t nrhs, const double* A, int64_t lda,
               const int32_t* A_exps, const double* X, int64_t ldx, double* Y, int64_t ldy,
               int r, int mode, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- emulated SpMV
+ * y = A x for A rows x cols in CSR (row_ptr: rows + 1 int32 offsets into col_idx and
+ * vals, nnz entries; column indices need not be sorted), x of cols entries, through r
+ * moduli: the sparse matrix-vector product [TME4] abstract lists among the memory-bound
+ * kernels of emulation.  Rows of A are scaled by the max rule over their nonzeros with
+ * the budget of dot products of max_row_nnz terms (ozk_scaling_bits(r, max_row_nnz)),
+ * x by one exponent; exact int32 row sums per modulus; CRT lift and one rounding, as
+ * ozk_dgemm.  An empty row gives +0.  A row whose row_ptr extent is not inside
+ * [0, nnz], that has more than max_row_nnz entries, holds a column index outside
+ * [0, cols) or holds Inf/NaN gives NaN (nothing is read through a bad index); Inf/NaN
+ * in x makes every y NaN.  All pointers are device pointers; 1 <= max_row_nnz <=
+ * OZK_MAX_K; nnz, rows and cols below 2^31. */
+int ozk_spmv_csr_workspace_size(int64_t rows, int64_t cols, int r, size_t* bytes);
+int ozk_spmv_csr(int64_t rows, int64_t cols, int64_t nnz, const int32_t* row_ptr,
+                 const int32_t* col_idx, const double* vals, int64_t max_row_nnz,
+                 const double* x, double* y, int r, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
 /* ---------------------------------------------------------------- FP4-limb INT8 GEMM
  * [AWE] abstract: x = d0 + 13 d1 + 169 d2 with every digit in
  * S = {0, +-1, +-2, +-3, +-4, +-6, +-8, +-12}; the digit of residue rho (mod 13) is

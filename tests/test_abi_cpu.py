@@ -159,6 +159,28 @@ def test_ex_validation(lib):
              1 << 20, None) == EINVAL
 
 
+def test_spmv_validation(lib):
+    f = lib.ozk_spmv_csr
+    out = ctypes.c_size_t()
+    assert lib.ozk_spmv_csr_workspace_size(10, 0, 14, ctypes.byref(out)) == EINVAL
+    assert lib.ozk_spmv_csr_workspace_size(10, 10, 14, ctypes.byref(out)) == OK
+    assert out.value >= 14 * 10 + 10 * 4 + 14 * 64
+    args = lambda **kw: dict(dict(rows=10, cols=10, nnz=30, kmax=7, r=14, ws=FAKE, wsb=1 << 20),
+                             **kw)
+    call = lambda a: f(a["rows"], a["cols"], a["nnz"], FAKE, FAKE, FAKE, a["kmax"], FAKE, FAKE,
+                       a["r"], a["ws"], a["wsb"], None)
+    assert call(args(r=0)) == EINVAL
+    assert call(args(cols=0)) == EINVAL
+    assert call(args(kmax=0)) == EINVAL
+    assert call(args(nnz=-1)) == EINVAL
+    assert call(args(kmax=131072)) == ERANGE
+    assert call(args(r=1, kmax=1000)) == ERANGE          # no bit budget
+    assert call(args(ws=None, wsb=0)) == EWORKSPACE
+    assert call(args(wsb=16)) == EWORKSPACE
+    assert call(args(nnz=1 << 31)) == EUNSUPPORTED
+    assert call(args(rows=0, ws=None, wsb=0)) == OK      # nothing to do
+
+
 def test_products_and_reconstruct_validation(lib):
     f = lib.ozk_modular_products
     assert f(4, 4, 100, 3, FAKE, 400, FAKE, 400, FAKE, 4, 16, None) == EINVAL       # kp % 64
