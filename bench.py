@@ -17,8 +17,9 @@ Also reported on the same JSON line:
   cpu_baseline  the CPU oracle (numpy, one BLAS thread) on 8 full output rows.
   extras        native fp64 DGEMM (torch.matmul), the r sweep 12..18, the norm scaling
                 rule against the max rule (time and distance to native fp64 at r = 12, 14,
-                16), deconstruction HBM GB/s, the GEMV and FP4-limb engines, and the
-                8192^3 wide-dynamic-range workload at r = 16..20 under both rules.
+                16), deconstruction HBM GB/s, the GEMV and FP4-limb engines, the
+                8192^3 wide-dynamic-range workload at r = 16..20 under both rules, and
+                the emulated SpMV of the 7-point Poisson operator on a 256^3 grid.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--r 16] [--scaling max|norm]
                        [--no-cpu-baseline]
@@ -471,6 +472,63 @@ def measure_wide_range(reps: int, stream) -> dict:
     return res
 
 
+def measure_spmv(reps: int, stream) -> dict:
+    """Emulated SpMV on the 7-point Poisson operator of a 256^3 grid (16.8 M rows, 117 M
+    entries, x U(-1,1) seed 7) at r = 14 and 16, next to the vendor fp64 CSR product
+    (torch.sparse.mm of the CSR tensor and x as one column).  GB/s counts the bytes a single pass over the
+    operator needs (8 B value + 4 B column per entry, 4 B row offset and 8 B each of x
+    and y per row), the same numerator for both."""
+    import numpy as np
+    import torch
+
+    import fp64_gemm_emulation_ozk_amd as ozk
+    import ozk_inputs
+
+    n = 256
+    dev = torch.device("cuda:0")
+    rp, ci, v = ozk_inputs.poisson_7pt_csr(n)
+    rows = n ** 3
+    nnz = int(rp[-1])
+    drp, dci, dv = (torch.from_numpy(t).to(dev) for t in (rp, ci, v))
+    del rp, ci, v
+    x = torch.from_numpy(ozk_inputs.uniform_matrix(np.random.default_rng(7), (rows, 1))[:, 0]
+                         ).to(dev)
+    y = torch.empty(rows, dtype=torch.float64, device=dev)
+    algo = 12.0 * nnz + 20.0 * rows
+    res = {"workload": f"7-point Poisson operator, {n}^3 grid ({rows} rows, {nnz} entries), "
+                       "x U(-1,1)", "bytes_per_call": algo}
+    try:
+        a_csr = torch.sparse_csr_tensor(drp, dci, dv, size=(rows, rows))
+        x2 = x[:, None].contiguous()
+        # the vendor sparse library's CSR product (torch.mv on a CSR tensor takes a far
+        # slower generic path on this build)
+        nat = lambda: torch.sparse.mm(a_csr, x2)
+        yn = nat()[:, 0]
+        t = _time_events(nat, reps, stream)
+        res["native_fp64"] = {"ms": round(t, 4), "gbs": round(algo / t / 1e6, 1),
+                              "what": "torch.sparse.mm (vendor CSR SpMM, one column)"}
+    except RuntimeError as exc:   # not every build ships the sparse path
+        res["native_fp64"] = {"error": str(exc)[:200]}
+        yn = None
+    for r in (14, 16):
+        ws = torch.empty(ozk.ozk_spmv_csr_workspace_size(rows, rows, r), dtype=torch.uint8,
+                         device=dev)
+        f = lambda: ozk.ozk_spmv_csr(drp, dci, dv, x, r, 7, out=y, workspace=ws)
+        f()
+        t = _time_events(f, reps, stream)
+        ent = {"ms": round(t, 4), "gbs": round(algo / t / 1e6, 1),
+               "frac_hbm": round(algo / t / 1e6 / PEAK_HBM_GBS, 4)}
+        if yn is not None:
+            ent["rel_vs_native"] = float(torch.linalg.norm(y - yn) / torch.linalg.norm(yn))
+            if "ms" in res["native_fp64"]:
+                ent["speed_vs_native"] = round(res["native_fp64"]["ms"] / t, 3)
+        res[f"emulated_r{r}"] = ent
+        del ws
+    del drp, dci, dv, x, y
+    torch.cuda.empty_cache()
+    return res
+
+
 def measure_fp4(reps: int, stream) -> dict:
     """The exact INT8 x INT8 product of 8192^3 int8 operands (uniform in [-128, 127],
     seed 5) through 9 FP4 GEMMs, against the 10.1 PFLOP/s dense FP4 MFMA peak."""
@@ -589,6 +647,8 @@ def main() -> int:
     ap.add_argument("--no-fp4", action="store_true")
     ap.add_argument("--no-wide", action="store_true",
                     help="skip the 8192^3 wide-dynamic-range extra")
+    ap.add_argument("--no-spmv", action="store_true",
+                    help="skip the emulated SpMV (Poisson 256^3) extra")
     ap.add_argument("--counters", action="store_true",
                     help="only launch the kernels the counter passes profile")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -752,6 +812,8 @@ def main() -> int:
             extras["fp4limb_int8gemm_8192"] = measure_fp4(reps, stream)
         if not args.no_wide:
             extras["wide_range_8192"] = measure_wide_range(reps, stream)
+        if not args.no_spmv:
+            extras["spmv_poisson_256"] = measure_spmv(reps, stream)
         model = tme_model(extras, peaks, ms_per_step)
         if model is not None:
             extras["tme_model"] = model

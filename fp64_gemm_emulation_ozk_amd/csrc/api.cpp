@@ -479,20 +479,18 @@ int ozk_int8gemm_fp4limb(int64_t m, int64_t n, int64_t k, const int8_t* A, int64
 namespace {
 
 struct SpmvLayout {
-  int64_t ldx;
-  size_t x_planes, x_exps, x_scr, res, row_exps;
+  size_t x_res, x_exp, x_partial, res, row_exps;
   size_t total() const {
-    return align256(x_planes) + align256(x_exps) + align256(x_scr) + align256(res) +
+    return align256(x_res) + align256(x_exp) + align256(x_partial) + align256(res) +
            align256(row_exps);
   }
 };
 
 SpmvLayout spmv_layout(int64_t rows, int64_t cols, int r) {
   SpmvLayout L;
-  L.ldx = round_up(cols, kPlaneK);
-  L.x_planes = (size_t)r * L.ldx;
-  L.x_exps = 4;
-  L.x_scr = deconstruct_scratch(1, cols, 0);  // x as a 1 x cols row
+  L.x_res = (size_t)cols * (r <= 16 ? 16 : 32);
+  L.x_exp = 4;
+  L.x_partial = (size_t)((cols + 2047) / 2048) * 8;
   L.res = (size_t)r * rows;
   L.row_exps = (size_t)rows * 4;
   return L;
@@ -525,18 +523,14 @@ int ozk_spmv_csr(int64_t rows, int64_t cols, int64_t nnz, const int32_t* row_ptr
   if (!workspace || workspace_bytes < L.total()) return OZK_EWORKSPACE;
   if (!aligned(workspace, 256)) return OZK_EINVAL;
   Carver cv(workspace);
-  int8_t* x_planes = static_cast<int8_t*>(cv.take(L.x_planes));
-  int32_t* x_exp = static_cast<int32_t*>(cv.take(L.x_exps));
-  void* x_scr = cv.take(L.x_scr);
+  int8_t* x_res = static_cast<int8_t*>(cv.take(L.x_res));
+  int32_t* x_exp = static_cast<int32_t*>(cv.take(L.x_exp));
+  uint64_t* x_partial = static_cast<uint64_t*>(cv.take(L.x_partial));
   int8_t* res = static_cast<int8_t*>(cv.take(L.res));
   int32_t* row_exps = static_cast<int32_t*>(cv.take(L.row_exps));
   hipStream_t s = as_stream(stream);
-  // x's residues: x as a 1 x cols row, one exponent, the width of the second operand
-  if ((st = deconstruct_impl(x, 1, cols, cols, 0, r, OZK_SCALING_MAX, pb, x_planes, L.ldx,
-                             L.ldx, x_exp, x_scr, s)))
-    return st;
-  if ((st = launch_spmv_residues(rows, cols, nnz, row_ptr, col_idx, vals, max_row_nnz, r, pa,
-                                 x_planes, L.ldx, res, row_exps, s)))
+  if ((st = launch_spmv(rows, cols, nnz, row_ptr, col_idx, vals, max_row_nnz, x, r, pa, pb,
+                        x_partial, x_exp, x_res, res, row_exps, s)))
     return st;
   // y as a 1 x rows matrix: output j scaled by x's exponent plus row j's
   return launch_crt(1, rows, r, res, 0, rows, rows, x_exp, row_exps, y, rows, s);

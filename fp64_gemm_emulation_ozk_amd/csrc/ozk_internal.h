@@ -85,14 +85,15 @@ int launch_deconstruct_pair(const double* a, int64_t m, int64_t k, int64_t lda, 
 int64_t norm_chunks(int64_t rows, int64_t cols, int axis);
 int launch_norm_exps(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
                      int alpha, uint64_t* pmax, double* ps, int32_t* exps, hipStream_t s);
-// Emulated SpMV, one thread per CSR row: row exponents (max rule, width p_bits) and the
-// symmetric residues of the row sums against x's residue planes xres ([r][x_stride]),
-// written as res[l * rows + i]; rows with a bad extent, more than kmax entries or a
-// column index outside [0, cols) get the exponent INT32_MIN.
-int launch_spmv_residues(int64_t rows, int64_t cols, int64_t nnz, const int32_t* row_ptr,
-                         const int32_t* col_idx, const double* vals, int64_t kmax, int r,
-                         int p_bits, const int8_t* xres, int64_t x_stride, int8_t* res,
-                         int32_t* exps, hipStream_t s);
+// Emulated SpMV: x's exponent (chunk maxima in x_partial, ceil(cols / 2048) entries) and
+// residues xres[cols][16 or 32] (r <= 16 or not), then one thread per CSR row: row
+// exponents (max rule, width p_a) and the symmetric residues of the row sums, written as
+// res[l * rows + i]; rows with a bad extent, more than kmax entries or a column index
+// outside [0, cols) get the exponent INT32_MIN.
+int launch_spmv(int64_t rows, int64_t cols, int64_t nnz, const int32_t* row_ptr,
+                const int32_t* col_idx, const double* vals, int64_t kmax, const double* x,
+                int r, int p_a, int p_b, uint64_t* x_partial, int32_t* x_exp, int8_t* xres,
+                int8_t* res, int32_t* exps, hipStream_t s);
 // Row (axis 0) or column (axis 1) exponents only, through maxbits scratch.
 int launch_line_exps(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
                      int p_bits, uint64_t* maxbits, int32_t* exps, hipStream_t s);

@@ -2,10 +2,12 @@
 // matrix-vector products among the memory-bound kernels whose emulation pays the
 // per-input deconstruction term.  The arithmetic is the dense path's: rows of A scaled
 // by the max rule over their nonzeros with the budget of dot products of at most kmax
-// terms, x by one exponent (its residue planes come from the row deconstruction of x
-// as a 1 x n matrix), exact int32 row sums per modulus, CRT lift and one rounding (the
-// CRT kernel of the dense path, on y as a 1 x rows matrix).
+// terms, x by one exponent, exact int32 row sums per modulus, CRT lift and one rounding
+// (the CRT kernel of the dense path, on y as a 1 x rows matrix).
 //
+// x: its exponent from chunk maxima (no atomics) and one combining block, then its r
+// residues per entry interleaved as xres[j][kXS] (16 bytes for r <= 16, else 32), so
+// that a row entry gathers all of them with one or two 16-byte loads.
 // spmv_residues_kernel: one thread per row.  The row's values are read twice (maximum,
 // then residues; the second read hits the cache), their residues are formed in
 // registers, multiplied by the gathered residues of x and summed per modulus; the sums'
@@ -27,12 +29,87 @@ __device__ __forceinline__ uint32_t sum_residue_byte(int v, uint32_t m, double i
   return (uint32_t)v - __umul24(q, m);
 }
 
-template <bool kWide>
+// Largest |x| (bit pattern) of each chunk of 2048 entries.
+__global__ __launch_bounds__(256) void vec_absmax_kernel(const double* __restrict__ x, int64_t n,
+                                                         uint64_t* __restrict__ partial) {
+  const int64_t base = (int64_t)blockIdx.x * 2048;
+  uint64_t v = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int64_t j = base + u * 256 + threadIdx.x;
+    if (j < n) {
+      const uint64_t b = abs_bits(x[j]);
+      v = v > b ? v : b;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint64_t o = __shfl_xor(v, off, 64);
+    v = v > o ? v : o;
+  }
+  __shared__ uint64_t w[4];
+  if ((threadIdx.x & 63) == 0) w[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t m = w[0];
+    for (int q = 1; q < 4; ++q) m = m > w[q] ? m : w[q];
+    partial[blockIdx.x] = m;
+  }
+}
+
+// One block: the maximum over the chunk maxima, then x's max-rule exponent.
+__global__ __launch_bounds__(256) void vec_exp_kernel(const uint64_t* __restrict__ partial,
+                                                      int64_t chunks, int p_bits,
+                                                      int32_t* __restrict__ exp) {
+  uint64_t v = 0;
+  for (int64_t c = threadIdx.x; c < chunks; c += 256) v = v > partial[c] ? v : partial[c];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint64_t o = __shfl_xor(v, off, 64);
+    v = v > o ? v : o;
+  }
+  __shared__ uint64_t w[4];
+  if ((threadIdx.x & 63) == 0) w[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t m = w[0];
+    for (int q = 1; q < 4; ++q) m = m > w[q] ? m : w[q];
+    exp[0] = line_exponent(m, p_bits);
+  }
+}
+
+// xres[j][0 .. kXS) = the r residues of x_j (zero past r, all zero if x's exponent marks
+// Inf/NaN).
+template <bool kWide, int kXS>
+__global__ __launch_bounds__(256) void x_residues_kernel(const double* __restrict__ x, int64_t n,
+                                                         const int32_t* __restrict__ exp,
+                                                         ResidueConsts K,
+                                                         int8_t* __restrict__ xres) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  const int e0 = exp[0];
+  const bool bad = e0 == INT32_MIN;
+  const Prepared pr = prepare_element<kWide>(bad ? 0.0 : x[j], bad ? 0 : e0);
+  uint32_t w[kXS / 4];
+#pragma unroll
+  for (int q = 0; q < kXS / 4; ++q) w[q] = 0;
+  w[0] = residue_byte_256(pr) & 0xffu;
+#pragma unroll
+  for (int l = 1; l < kXS; ++l)
+    if (l < K.r)
+      w[l / 4] |= (residue_byte<kWide>(pr, K.m[l], K.inv[l], K.c32[l]) & 0xffu) << (8 * (l % 4));
+  uint4* dst = reinterpret_cast<uint4*>(xres + j * kXS);
+#pragma unroll
+  for (int q = 0; q < kXS / 16; ++q)
+    dst[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+}
+
+template <bool kWide, int kXS>
 __global__ __launch_bounds__(256) void spmv_residues_kernel(
     int64_t rows, int64_t cols, int64_t nnz, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const double* __restrict__ vals, int64_t kmax,
-    ResidueConsts K, int p_bits, const int8_t* __restrict__ xres, int64_t x_stride,
-    int8_t* __restrict__ res, int32_t* __restrict__ exps) {
+    ResidueConsts K, int p_bits, const int8_t* __restrict__ xres, int8_t* __restrict__ res,
+    int32_t* __restrict__ exps) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= rows) return;
   const int64_t s = row_ptr[i], t = row_ptr[i + 1];
@@ -45,45 +122,67 @@ __global__ __launch_bounds__(256) void spmv_residues_kernel(
       mx = mx > abs_bits(vals[p]) ? mx : abs_bits(vals[p]);
     }
   }
-  int e = ok ? line_exponent(mx, p_bits) : INT32_MIN;
+  const int e = ok ? line_exponent(mx, p_bits) : INT32_MIN;
   exps[i] = e;
-  int acc[kMaxModuli];
+  int acc[kXS];
 #pragma unroll
-  for (int l = 0; l < kMaxModuli; ++l) acc[l] = 0;
+  for (int l = 0; l < kXS; ++l) acc[l] = 0;
   if (e != INT32_MIN) {
     for (int64_t p = s; p < t; ++p) {
-      const int64_t c = col_idx[p];
-      const Prepared pr = prepare_element<kWide>(vals[p], e);
-      acc[0] += (int)(int8_t)residue_byte_256(pr) * (int)xres[c];
+      const uint4* xs = reinterpret_cast<const uint4*>(xres + (int64_t)col_idx[p] * kXS);
+      uint32_t xw[kXS / 4];
 #pragma unroll
-      for (int l = 1; l < kMaxModuli; ++l)
+      for (int q = 0; q < kXS / 16; ++q) {
+        const uint4 v = xs[q];
+        xw[4 * q] = v.x;
+        xw[4 * q + 1] = v.y;
+        xw[4 * q + 2] = v.z;
+        xw[4 * q + 3] = v.w;
+      }
+      const Prepared pr = prepare_element<kWide>(vals[p], e);
+      acc[0] += (int)(int8_t)residue_byte_256(pr) * (int)(int8_t)(xw[0] & 0xffu);
+#pragma unroll
+      for (int l = 1; l < kXS; ++l)
         if (l < K.r)
           acc[l] += (int)(int8_t)residue_byte<kWide>(pr, K.m[l], K.inv[l], K.c32[l]) *
-                    (int)xres[l * x_stride + c];
+                    (int)(int8_t)((xw[l / 4] >> (8 * (l % 4))) & 0xffu);
     }
   }
   res[i] = (int8_t)(acc[0] & 0xff);
 #pragma unroll
-  for (int l = 1; l < kMaxModuli; ++l)
+  for (int l = 1; l < kXS; ++l)
     if (l < K.r)
       res[l * rows + i] = (int8_t)sum_residue_byte(acc[l], (uint32_t)K.m[l], K.inv[l]);
 }
 
 }  // namespace
 
-int launch_spmv_residues(int64_t rows, int64_t cols, int64_t nnz, const int32_t* row_ptr,
-                         const int32_t* col_idx, const double* vals, int64_t kmax, int r,
-                         int p_bits, const int8_t* xres, int64_t x_stride, int8_t* res,
-                         int32_t* exps, hipStream_t s) {
+int launch_spmv(int64_t rows, int64_t cols, int64_t nnz, const int32_t* row_ptr,
+                const int32_t* col_idx, const double* vals, int64_t kmax, const double* x,
+                int r, int p_a, int p_b, uint64_t* x_partial, int32_t* x_exp, int8_t* xres,
+                int8_t* res, int32_t* exps, hipStream_t s) {
   if (rows <= 0) return OZK_OK;
-  const ResidueConsts& K = *residue_consts(r, p_bits);
-  const dim3 grid((unsigned)((rows + 255) / 256));
-  if (K.wide)
-    hipLaunchKernelGGL(spmv_residues_kernel<true>, grid, dim3(256), 0, s, rows, cols, nnz,
-                       row_ptr, col_idx, vals, kmax, K, p_bits, xres, x_stride, res, exps);
-  else
-    hipLaunchKernelGGL(spmv_residues_kernel<false>, grid, dim3(256), 0, s, rows, cols, nnz,
-                       row_ptr, col_idx, vals, kmax, K, p_bits, xres, x_stride, res, exps);
+  const int64_t chunks = (cols + 2047) / 2048;
+  hipLaunchKernelGGL(vec_absmax_kernel, dim3((unsigned)chunks), dim3(256), 0, s, x, cols,
+                     x_partial);
+  hipLaunchKernelGGL(vec_exp_kernel, dim3(1), dim3(256), 0, s, x_partial, chunks, p_b, x_exp);
+  if (hipGetLastError() != hipSuccess) return OZK_EHIP;
+  const ResidueConsts& KB = *residue_consts(r, p_b);
+  const ResidueConsts& KA = *residue_consts(r, p_a);
+  const dim3 gx((unsigned)((cols + 255) / 256)), gr((unsigned)((rows + 255) / 256));
+#define OZK_SPMV(W, XS)                                                                      \
+  hipLaunchKernelGGL((x_residues_kernel<W, XS>), gx, dim3(256), 0, s, x, cols, x_exp, KB,   \
+                     xres);                                                                  \
+  hipLaunchKernelGGL((spmv_residues_kernel<W, XS>), gr, dim3(256), 0, s, rows, cols, nnz,  \
+                     row_ptr, col_idx, vals, kmax, KA, p_a, xres, res, exps)
+  // one residue arithmetic for both sides: the wide one if either side needs it
+  const bool wide = KA.wide || KB.wide;
+  if (r <= 16) {
+    if (wide) { OZK_SPMV(true, 16); } else { OZK_SPMV(false, 16); }
+  } else {
+    if (wide) { OZK_SPMV(true, 32); } else { OZK_SPMV(false, 32); }
+  }
+#undef OZK_SPMV
   return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
 }
 
