@@ -393,7 +393,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
   constexpr int TI = WL::TI, TJ = WL::TJ, kWaves = NW;
   constexpr int kRegions = kPairBytes / 1024;          // 64 regions of 8 rows x 128 B
   constexpr int kLoadsPerWave = kRegions / NW;         // 8 (NW = 8)
-  static_assert(WL::kMfmaHalf == kLoadsPerWave, "one load per MFMA of quarter 3");
+  static_assert(WL::kMfmaHalf == kLoadsPerWave, "half the loads in each of two quarters");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -491,7 +491,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
   for (int p = 0; p < np; ++p) {
     __builtin_amdgcn_sched_barrier(0);
     const int8_t* st = lds + (p & 1) * kPairBytes;
-    if (p > 0) quarter(0, st, 1, p + 1, 4, 8);
+    if (p > 0) quarter(0, st, 1, p + 1, kLoadsPerWave / 2, kLoadsPerWave);
     else quarter(0, st, 1, 0, 0, 0);
     quarter(1, st, 2, 0, 0, 0);
     quarter(0, st, 3, 0, 0, 0);
@@ -502,7 +502,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
     wg_barrier();
     __builtin_amdgcn_sched_barrier(0);
     const int pn = p + 1 < np ? p + 1 : p;  // past the last pair: a harmless re-read
-    quarter(1, lds + (pn & 1) * kPairBytes, 0, p + 2, 0, 4);
+    quarter(1, lds + (pn & 1) * kPairBytes, 0, p + 2, 0, kLoadsPerWave / 2);
   }
   // The clamped loads past the last pair are still landing in the ring.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
