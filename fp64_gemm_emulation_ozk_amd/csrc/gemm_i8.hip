@@ -23,6 +23,7 @@
 // Epilogues: the int32 products themselves, or their symmetric residues modulo m_l as
 // int8 (what the CRT reconstruction consumes: 1 byte instead of 4 per output), staged
 // through LDS as one 256 x 256 byte tile so that every global store writes 256-byte rows.
+#include <atomic>
 #include <type_traits>
 
 #include "lds_dma.h"
@@ -341,92 +342,166 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_kernel(
 }
 
 
-// Pair-stage variant for kp a multiple of 128: the LDS ring holds two stages of two K
-// steps each (64 KiB: A rows 0..255, then B rows 0..255, 128 bytes per row), so every
-// direct load moves 8 rows x 128 bytes (whole cache lines) instead of 16 rows x 64 bytes
-// (half lines), which is what limits the L2 -> LDS stream of the 64-byte ring.  The
-// eight 16-byte chunks of a row are XOR-swizzled by (row >> 1) & 7: the 16 lanes of a
-// fragment read (rows r .. r+15, one logical chunk) then cover all 64 banks.
+// Residues of one 256 x 256 tile stored straight from the accumulators (no LDS: the ring
+// already holds the next tile's first K steps).  Lane (row lane & 31, half h = lane >> 5)
+// of an MFMA block holds columns 8 q + 4 h .. +3 in registers 4 q .. 4 q + 3; after the
+// bytes are packed one word per q, two v_permlane32_swap exchanges (words 0 <-> 2 and
+// 1 <-> 3 across the halves) leave lane h with columns 16 h .. 16 h + 15 of its row, one
+// 16-byte store.  A full tile issues exactly TI * TJ stores per wave.
+template <int NW>
+__device__ __forceinline__ void store_residues_direct(
+    const v16i (&acc)[WaveLayout<NW>::TI][WaveLayout<NW>::TJ], int64_t m, int64_t n,
+    int64_t row0, int64_t col0, int grp, int wq, int lane, int mod, double inv,
+    int8_t* __restrict__ o, int64_t ldo, bool full, int vec_out) {
+  using WL = WaveLayout<NW>;
+  auto emit = [&](auto byte_of) {
+#pragma unroll
+    for (int i = 0; i < WL::TI; ++i)
+#pragma unroll
+      for (int j = 0; j < WL::TJ; ++j) {
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          w[q] = pack4b(byte_of(acc[i][j][4 * q]), byte_of(acc[i][j][4 * q + 1]),
+                        byte_of(acc[i][j][4 * q + 2]), byte_of(acc[i][j][4 * q + 3]));
+        const auto s02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+        const auto s13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+        const uint4 v = make_uint4(s02[0], s02[1], s13[0], s13[1]);
+        const int64_t row = row0 + grp * 128 + i * 32 + (lane & 31);
+        const int64_t col = col0 + wq * WL::WN + j * 32 + 16 * (lane >> 5);
+        int8_t* dst = o + row * ldo + col;
+        if (full) {
+          *reinterpret_cast<uint4*>(dst) = v;
+        } else if (row < m) {
+          if (vec_out && col + 16 <= n) {
+            *reinterpret_cast<uint4*>(dst) = v;
+          } else {
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+            for (int u = 0; u < 16; ++u)
+              if (col + u < n) dst[u] = (int8_t)(wv[u >> 2] >> (8 * (u & 3)));
+          }
+        }
+      }
+  };
+  if (mod == 256) {
+    emit([](int v) { return (uint32_t)v; });
+  } else {
+    const uint32_t um = (uint32_t)mod;
+    emit([=](int v) { return residue_byte_odd(v, um, inv); });
+  }
+}
+
+// Pair-stage persistent variant for kp a multiple of 128 with at least two pairs: the LDS
+// ring holds two stages of two K steps each (64 KiB: A rows 0..255, then B rows 0..255,
+// 128 bytes per row), so every direct load moves 8 rows x 128 bytes (whole cache lines)
+// instead of 16 rows x 64 bytes (half lines), which is what limits the L2 -> LDS stream of
+// the 64-byte ring.  The eight 16-byte chunks of a row are XOR-swizzled by (row >> 1) & 7:
+// the 16 lanes of a fragment read (rows r .. r+15, one logical chunk) then cover all 64
+// banks.
 //
-// Per pair p (K bytes 128 p .. 128 p + 127, buffer p % 2) every wave runs four quarters
-// of 8 MFMAs (K sub-chunks of 32), reading the next quarter's fragments between them.
-// After quarter 2 the wave waits for its loads of pair p+1 and for its reads, and the
-// workgroup barrier makes pair p+1 complete and pair p fully read; quarter 3 then reads
-// pair p+1's first fragments and issues half of this wave's 8 loads of pair p+2 into
-// buffer p % 2 (one after every second MFMA), quarter 0 of pair p+1 the other half.
-// Loads thus have three to four quarters before their wait.
+// Per pair p (K bytes 128 p .. 128 p + 127) every wave runs four quarters of 8 MFMAs (K
+// sub-chunks of 32), reading the next quarter's fragments between them.  After quarter 2
+// the wave waits for its loads of pair p+1 and for its reads, and the workgroup barrier
+// makes pair p+1 complete and pair p fully read; quarter 3 then reads pair p+1's first
+// fragments and issues half of this wave's 8 loads of pair p+2 into pair p's buffer (one
+// after every second MFMA), quarter 0 of pair p+1 the other half.
+//
+// One workgroup per CU walks a fixed list of tiles.  Pair numbers run on across tiles:
+// the last two pairs of a tile load the next tile's pairs 0 and 1 (all of pair 1 before
+// the epilogue), and its last quarter reads the next tile's first fragments, so the
+// epilogue (residues stored from registers) overlaps those loads, and the wait for pair
+// 1 after the next tile's first three quarters lets the epilogue's stores stay in flight.
+// Tiles are dealt XCD by XCD (the hardware deals workgroups out round-robin over the 8
+// XCDs): the workgroups of one XCD take consecutive tiles of one contiguous share, in
+// groups of kGroupM tile rows, so the tiles in flight on an XCD share A rows and B columns
+// in its L2.
 constexpr int kPairRow = 128;                       // bytes per row of a pair stage
 constexpr int kPairBytes = (BM + BN) * kPairRow;    // 64 KiB
-static_assert(2 * kPairBytes <= kStages * kStageBytes, "pair ring within the LDS array");
 static_assert(BM * kOutPitch <= 2 * kPairBytes, "residue staging within the pair ring");
-
-__device__ __forceinline__ int swz_pair(int row, int chunk) {
-  return row * kPairRow + ((chunk ^ ((row >> 1) & 7)) << 4);
-}
 
 template <int kEpi, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
     int64_t m, int64_t n, int64_t kp, const int8_t* __restrict__ pa, int64_t stride_a,
     const int8_t* __restrict__ pb, int64_t stride_b, void* __restrict__ out, int64_t ldo,
-    int64_t stride_o, int tiles_m, int tiles_n, EpiModuli E, int vec_out) {
-  __shared__ __attribute__((aligned(1024))) int8_t lds[kStages * kStageBytes];
-
-  // Block -> (modulus, tile row, tile column): XCD-contiguous, then grouped by kGroupM.
-  const int total = gridDim.x;
-  int bid = blockIdx.x;
-  if (total % kXcds == 0) bid = (bid % kXcds) * (total / kXcds) + bid / kXcds;
-  const int per_mod = tiles_m * tiles_n;
-  const int l = bid / per_mod;
-  const int rem = bid - l * per_mod;
-  const int per_group = kGroupM * tiles_n;
-  const int first_m = (rem / per_group) * kGroupM;
-  const int gsize = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
-  const int in_group = rem % per_group;
-  const int tm = first_m + in_group % gsize;
-  const int tn = in_group / gsize;
-  const int8_t* A = pa + l * stride_a;
-  const int8_t* B = pb + l * stride_b;
-  const int64_t row0 = (int64_t)tm * BM;
-  const int64_t col0 = (int64_t)tn * BN;
+    int64_t stride_o, int tiles_m, int tiles_n, int tiles, EpiModuli E, int vec_out) {
+  __shared__ __attribute__((aligned(1024))) int8_t lds[2 * kPairBytes];
 
   using WL = WaveLayout<NW>;
   constexpr int TI = WL::TI, TJ = WL::TJ, kWaves = NW;
   constexpr int kRegions = kPairBytes / 1024;          // 64 regions of 8 rows x 128 B
   constexpr int kLoadsPerWave = kRegions / NW;         // 8 (NW = 8)
+  constexpr int kHalf = kLoadsPerWave / 2;
+  constexpr int kStores = kEpi == kEpiProducts ? 4 * TI * TJ : TI * TJ;  // per full tile
   static_assert(WL::kMfmaHalf == kLoadsPerWave, "half the loads in each of two quarters");
+  static_assert(NW == 8 && kStores <= 63, "regions 0..31 are A; the store count fits vmcnt");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int grp = __builtin_amdgcn_readfirstlane(wave / (NW / 2));
   const int wq = __builtin_amdgcn_readfirstlane(wave % (NW / 2));
 
-  // Region rg = wave + NW q: rows 8 (rg % 32) .. +7 of A (rg < 32) or B; lane i lands at
-  // row 8 (rg % 32) + i / 8, physical chunk i % 8, which holds logical chunk
-  // (i % 8) ^ ((row >> 1) & 7).
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const uint64_t sbase_a = (uint64_t)(A + row0 * kp), sbase_b = (uint64_t)(B + col0 * kp);
-  uint32_t voff[kLoadsPerWave];
-#pragma unroll
-  for (int q = 0; q < kLoadsPerWave; ++q) {
-    const int rg = wave + kWaves * q;
-    const bool is_b = rg >= 32;
-    const int row = 8 * (rg & 31) + (lane >> 3);
-    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-    const int64_t origin = is_b ? col0 : row0;
-    const int64_t last = (is_b ? n : m) - 1;
-    const int64_t gr = origin + row < last ? origin + row : last;
-    voff[q] = (uint32_t)((gr - origin) * kp + 16 * chunk);
+  // This workgroup's tiles: first, first + step, ... below last (all uniform).
+  const int G = gridDim.x;
+  int t, t_end, step;
+  if (G % kXcds == 0) {
+    const int share = (tiles + kXcds - 1) / kXcds;
+    const int lo = (int)(blockIdx.x % kXcds) * share;
+    t = lo + (int)(blockIdx.x / kXcds);
+    t_end = lo + share < tiles ? lo + share : tiles;
+    step = G / kXcds;
+  } else {
+    t = blockIdx.x;
+    t_end = tiles;
+    step = G;
   }
-  auto region_base = [&](int q) { return wave_u + kWaves * q >= 32 ? sbase_b : sbase_a; };
+  if (t >= t_end) return;
+
+  // Tile -> (modulus, tile row, tile column), tile rows grouped by kGroupM.
+  struct Tile {
+    int l;
+    int64_t row0, col0;
+    uint64_t base_a, base_b;            // tile origins of A_l and B_l (uniform)
+    uint32_t voff[kLoadsPerWave];       // per-lane source offsets of the loads
+  };
+  const int per_mod = tiles_m * tiles_n;
+  const int per_group = kGroupM * tiles_n;
+  // Region rg = wave + NW q: rows 8 (rg % 32) .. +7 of A (q < 4) or B; lane i lands at
+  // row 8 (rg % 32) + i / 8, physical chunk i % 8, which holds logical chunk
+  // (i % 8) ^ ((row >> 1) & 7); rows past the matrix re-read its last row.
+  auto make_tile = [&](int tt, Tile& d) {
+    d.l = tt / per_mod;
+    const int rem = tt - d.l * per_mod;
+    const int first_m = (rem / per_group) * kGroupM;
+    const int gsize = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+    const int in_group = rem % per_group;
+    d.row0 = (int64_t)(first_m + in_group % gsize) * BM;
+    d.col0 = (int64_t)(in_group / gsize) * BN;
+    d.base_a = (uint64_t)(pa + d.l * stride_a + d.row0 * kp);
+    d.base_b = (uint64_t)(pb + d.l * stride_b + d.col0 * kp);
+#pragma unroll
+    for (int q = 0; q < kLoadsPerWave; ++q) {
+      const bool is_b = q >= kLoadsPerWave / 2;
+      const int row = 8 * ((wave + kWaves * q) & 31) + (lane >> 3);
+      const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+      const int64_t origin = is_b ? d.col0 : d.row0;
+      const int64_t last = (is_b ? n : m) - 1;
+      const int64_t gr = origin + row < last ? origin + row : last;
+      d.voff[q] = (uint32_t)((gr - origin) * kp + 16 * chunk);
+    }
+  };
+
   const uint32_t lds0 = lds_address(lds);
   const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(lds0 + wave * 1024);
   const int np = (int)(kp / kPairRow);
-  auto issue_pair = [&](int p) {  // pair p (clamped to the last) into buffer p % 2
-    const int pc = p < np ? p : np - 1;
-    const uint32_t base = wave_lds + (uint32_t)(p & 1) * kPairBytes;
-#pragma unroll
-    for (int q = 0; q < kLoadsPerWave; ++q)
-      dma16_sbase(voff[q], region_base(q) + (uint64_t)pc * kPairRow, base + q * (kWaves * 1024));
+  // Load q of pair `pair` of the current tile (next: of the next tile) into LDS buffer
+  // `buf`.
+  Tile cur, nxt;
+  auto load = [&](bool next, int pair, int buf, int q) {
+    const uint32_t vo = next ? nxt.voff[q] : cur.voff[q];
+    const uint64_t base = q < kLoadsPerWave / 2 ? (next ? nxt.base_a : cur.base_a)
+                                                : (next ? nxt.base_b : cur.base_b);
+    dma16_sbase(vo, base + (uint64_t)pair * kPairRow,
+                wave_lds + (uint32_t)buf * kPairBytes + q * (kWaves * 1024));
   };
 
   v16i acc[TI][TJ];
@@ -448,66 +523,147 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
   for (int j = 0; j < TJ; ++j) offb[j] = BM * kPairRow + (wq * WL::WN + j * 32 + frow) * kPairRow;
   const int sw = (frow >> 1) & 7;  // row swizzle (the same for every block: 16 | block rows)
   v4i fa[2][TI], fb[2][TJ];
-  auto read_frags = [&](const int8_t* st, int qq, v4i (&xa)[TI], v4i (&xb)[TJ]) {
-    const int c = ((2 * qq + fchunk) ^ sw) << 4;
-#pragma unroll
-    for (int i = 0; i < TI; ++i) xa[i] = *reinterpret_cast<const v4i*>(st + offa[i] + c);
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) xb[j] = *reinterpret_cast<const v4i*>(st + offb[j] + c);
-  };
   // 8 MFMAs on fragment set `cur`, the reads of quarter qq of stage st into the other set
-  // between them (qq < 0: no reads), and this wave's loads l0 .. l1-1 of pair `lp` after
-  // every second MFMA.
-  auto quarter = [&](int cur, const int8_t* st, int qq, int lp, int l0, int l1) {
-    const bool loads = l1 > l0;
-    const int c = qq >= 0 ? ((2 * qq + fchunk) ^ sw) << 4 : 0;
-    const uint32_t lbase = wave_lds + (uint32_t)(lp & 1) * kPairBytes;
-    const int lpc = lp < np ? lp : np - 1;
+  // between them, and loads l0 .. l1-1 of pair `lp` (of the next tile if `next`) into
+  // buffer `lb` after every second MFMA.
+  auto quarter = [&](int cur_set, const int8_t* st, int qq, bool next, int lp, int lb, int l0,
+                     int l1) {
+    const int c = ((2 * qq + fchunk) ^ sw) << 4;
 #pragma unroll
     for (int idx = 0; idx < WL::kMfmaHalf; ++idx) {
       const int i = idx / TJ, j = idx % TJ;
-      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
-      if (qq >= 0) {
-        if (idx < TI)
-          fa[cur ^ 1][idx] = *reinterpret_cast<const v4i*>(st + offa[idx] + c);
-        else if (idx < TI + TJ)
-          fb[cur ^ 1][idx - TI] = *reinterpret_cast<const v4i*>(st + offb[idx - TI] + c);
-      }
-      if (loads && (idx & 1) == 1) {
+      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[cur_set][j], fa[cur_set][i],
+                                                        acc[i][j], 0, 0, 0);
+      if (idx < TI)
+        fa[cur_set ^ 1][idx] = *reinterpret_cast<const v4i*>(st + offa[idx] + c);
+      else if (idx < TI + TJ)
+        fb[cur_set ^ 1][idx - TI] = *reinterpret_cast<const v4i*>(st + offb[idx - TI] + c);
+      if ((idx & 1) == 1) {
         const int q = l0 + (idx >> 1);
-        if (q < l1)
-          dma16_sbase(voff[q], region_base(q) + (uint64_t)lpc * kPairRow,
-                      lbase + q * (kWaves * 1024));
+        if (q < l1) load(next, lp, lb, q);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  issue_pair(0);
-  issue_pair(1);
+  make_tile(t, cur);
+#pragma unroll
+  for (int q = 0; q < kLoadsPerWave; ++q) load(false, 0, 0, q);
+#pragma unroll
+  for (int q = 0; q < kLoadsPerWave; ++q) load(false, 1, 1, q);
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerWave) : "memory");
   wg_barrier();
-  read_frags(lds, 0, fa[0], fb[0]);
-  for (int p = 0; p < np; ++p) {
-    __builtin_amdgcn_sched_barrier(0);
-    const int8_t* st = lds + (p & 1) * kPairBytes;
-    if (p > 0) quarter(0, st, 1, p + 1, kLoadsPerWave / 2, kLoadsPerWave);
-    else quarter(0, st, 1, 0, 0, 0);
-    quarter(1, st, 2, 0, 0, 0);
-    quarter(0, st, 3, 0, 0, 0);
-    // pair p+1 has landed (this wave's loads; the barrier covers the others) and every
-    // wave holds its quarter-3 fragments of pair p
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    wg_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    const int pn = p + 1 < np ? p + 1 : p;  // past the last pair: a harmless re-read
-    quarter(1, lds + (pn & 1) * kPairBytes, 0, p + 2, 0, kLoadsPerWave / 2);
+  {
+    const int c = ((0 + fchunk) ^ sw) << 4;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) fa[0][i] = *reinterpret_cast<const v4i*>(lds + offa[i] + c);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) fb[0][j] = *reinterpret_cast<const v4i*>(lds + offb[j] + c);
   }
-  // The clamped loads past the last pair are still landing in the ring.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  tile_epilogue<kEpi, NW>(acc, lds, m, n, l, row0, col0, grp, wq, wave, lane, E, out, ldo,
-                          stride_o, vec_out);
+  int par = 0;                 // LDS buffer of the current tile's pair 0
+  bool stores_pending = false; // the previous tile's epilogue issued exactly kStores stores
+  for (;;) {
+    const int t_next = t + step;
+    const bool has_next = t_next < t_end;
+    if (has_next) make_tile(t_next, nxt);
+    for (int p = 0; p < np; ++p) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int b0 = (par + p) & 1;      // pair p's buffer (and pair p+2's)
+      const int b1 = b0 ^ 1;             // pair p+1's buffer
+      const int8_t* st = lds + b0 * kPairBytes;
+      const bool last = p + 1 == np;
+      // quarter 0: the second half of pair p+1, the next tile's pair 0 in the last pair
+      // (pair 1 of every tile is issued whole before its pair 0 is used)
+      const bool q0_loads = p > 0 && (!last || has_next);
+      quarter(0, st, 1, last, last ? 0 : p + 1, b1, kHalf, q0_loads ? kLoadsPerWave : kHalf);
+      quarter(1, st, 2, false, 0, 0, 0, 0);
+      quarter(0, st, 3, false, 0, 0, 0, 0);
+      // pair p+1 has landed (this wave's loads; the barrier covers the others) and every
+      // wave holds its quarter-3 fragments of pair p.  In pair 0 only the previous
+      // epilogue's stores may be issued after pair 1's loads.
+      if (p == 0 && stores_pending)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStores) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      wg_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // quarter 3: the first fragments of pair p+1 (the next tile's pair 0 after the last
+      // pair; a harmless re-read of pair p after the last tile's), and the first half of
+      // pair p+2 into pair p's buffer, now free
+      const bool wrap = p + 2 >= np;     // pair p+2 belongs to the next tile
+      const bool q3_loads = !wrap || has_next;
+      const int8_t* sn = last && !has_next ? st : lds + b1 * kPairBytes;
+      quarter(1, sn, 0, wrap, wrap ? p + 2 - np : p + 2, b0, 0, q3_loads ? kHalf : 0);
+      if (last && has_next) {
+#pragma unroll
+        for (int q = kHalf; q < kLoadsPerWave; ++q) load(true, 1, b0, q);
+      }
+    }
+  // Epilogue of tile `cur`: exactly kStores stores per wave when the tile is full.
+    const bool full = vec_out && cur.row0 + BM <= m && cur.col0 + BN <= n;
+    if (kEpi == kEpiProducts) {
+      int32_t* o = reinterpret_cast<int32_t*>(out) + cur.l * stride_o;
+      const int64_t wrow0 = cur.row0 + grp * 128, wcol0 = cur.col0 + wq * WL::WN;
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int64_t row = wrow0 + i * 32 + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t col = wcol0 + j * 32 + 8 * q + 4 * (lane >> 5);
+            int32_t* dst = o + row * ldo + col;
+            const v4i v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                           acc[i][j][4 * q + 3]};
+            if (full) {
+              *reinterpret_cast<v4i*>(dst) = v;
+            } else if (row < m) {
+              if (vec_out && col + 4 <= n) {
+                *reinterpret_cast<v4i*>(dst) = v;
+              } else {
+                for (int u = 0; u < 4; ++u)
+                  if (col + u < n) dst[u] = v[u];
+              }
+            }
+          }
+      }
+    } else {
+      store_residues_direct<NW>(acc, m, n, cur.row0, cur.col0, grp, wq, lane, E.mod[cur.l],
+                                E.inv[cur.l], reinterpret_cast<int8_t*>(out) + cur.l * stride_o,
+                                ldo, full, vec_out);
+    }
+    if (!has_next) break;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+    stores_pending = full;
+    par = (par + np) & 1;
+    t = t_next;
+    cur = nxt;
+  }
+  // Every load this wave issued has been waited for (the last tile issues none past its
+  // last pair); the stores drain on their own.
+}
+
+// Compute units of the current device, cached per device.
+int compute_units() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (dev >= 0 && dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return -1;
+  if (dev >= 0 && dev < 64) cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 }  // namespace
@@ -531,17 +687,26 @@ int launch_gemm_i8(int64_t m, int64_t n, int64_t kp, int r, const int8_t* pa, in
   const int vec_out = (reinterpret_cast<uintptr_t>(out) % vbytes) == 0 &&
                       (ldo * elem) % vbytes == 0 && (stride_o * elem) % vbytes == 0;
   constexpr int NW = kWavesDefault;
-  const dim3 grid((unsigned)blocks), block(64 * NW);
-#define OZK_GEMM(K, EPI)                                                                   \
-  hipLaunchKernelGGL((K<EPI, NW>), grid, block, 0, s, m, n, kp, pa, stride_a, pb, stride_b, \
-                     out, ldo, stride_o, tiles_m, tiles_n, E, vec_out)
-  const bool pairs = kp % kPairRow == 0;   // whole-line loads need K in steps of 128
+  const dim3 block(64 * NW);
+  // whole-line loads need K in steps of 128; the tile pipeline needs two of them
+  const bool pairs = kp % kPairRow == 0 && kp >= 2 * kPairRow;
+  const int cus = compute_units();
+  if (cus <= 0) return OZK_EHIP;
+  const dim3 grid((unsigned)blocks);
+  const dim3 grid_p((unsigned)(blocks < cus ? blocks : cus));  // one workgroup per CU
+  const int tiles = (int)blocks;
+#define OZK_GEMM(EPI)                                                                        \
+  if (pairs)                                                                                 \
+    hipLaunchKernelGGL((gemm_i8_pairs_kernel<EPI, NW>), grid_p, block, 0, s, m, n, kp, pa,   \
+                       stride_a, pb, stride_b, out, ldo, stride_o, tiles_m, tiles_n, tiles, E, \
+                       vec_out);                                                             \
+  else                                                                                       \
+    hipLaunchKernelGGL((gemm_i8_kernel<EPI, NW>), grid, block, 0, s, m, n, kp, pa, stride_a,  \
+                       pb, stride_b, out, ldo, stride_o, tiles_m, tiles_n, E, vec_out)
   if (epilogue == kEpiProducts) {
-    if (pairs) OZK_GEMM(gemm_i8_pairs_kernel, kEpiProducts);
-    else OZK_GEMM(gemm_i8_kernel, kEpiProducts);
+    OZK_GEMM(kEpiProducts);
   } else {
-    if (pairs) OZK_GEMM(gemm_i8_pairs_kernel, kEpiResidues);
-    else OZK_GEMM(gemm_i8_kernel, kEpiResidues);
+    OZK_GEMM(kEpiResidues);
   }
 #undef OZK_GEMM
   return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;

@@ -79,8 +79,10 @@ def test_deconstruct_nonfinite_lines():
     np.testing.assert_array_equal(planes_t.cpu().numpy(), planes.cpu().numpy())
 
 
+# The last two have more tiles (r * tiles_m * tiles_n) than the device has compute
+# units, so workgroups walk several tiles: ragged and full tiles, 3 and 4 K pairs.
 PRODUCT_CASES = [(1, 1, 64, 1), (300, 200, 256, 3), (257, 129, 64, 2), (512, 384, 640, 2),
-                 (33, 700, 192, 4)]
+                 (33, 700, 192, 4), (1030, 1030, 512, 11), (1024, 1280, 384, 13)]
 
 
 @pytest.mark.parametrize("m,n,kp,r", PRODUCT_CASES)
@@ -98,7 +100,12 @@ def test_modular_products_bit_exact(m, n, kp, r):
     assert want[0, 0, 0] == kp * 2**14
 
 
-@pytest.mark.parametrize("m,n,kp,r", [(300, 200, 256, 20), (1, 1, 64, 1), (257, 130, 128, 16)])
+RESIDUE_CASES = [(300, 200, 256, 20), (1, 1, 64, 1), (257, 130, 128, 16),
+                 # several tiles per workgroup: ragged (3 pairs), full (2 and 8 pairs)
+                 (1100, 900, 384, 16), (1536, 1280, 256, 12), (2048, 2048, 1024, 16)]
+
+
+@pytest.mark.parametrize("m,n,kp,r", RESIDUE_CASES)
 def test_modular_residues_bit_exact(m, n, kp, r):
     announce(f"modular_residues m={m} n={n} kp={kp} r={r}")
     rng = np.random.default_rng(m * n + kp)
