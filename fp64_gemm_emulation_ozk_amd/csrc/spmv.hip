@@ -8,10 +8,10 @@
 // x: its exponent from chunk maxima (no atomics) and one combining block, then its r
 // residues per entry interleaved as xres[j][kXS] (16 bytes for r <= 16, else 32), so
 // that a row entry gathers all of them with one or two 16-byte loads.
-// spmv_residues_kernel: one thread per row.  The row's values are read twice (maximum,
-// then residues; the second read hits the cache), their residues are formed in
-// registers, multiplied by the gathered residues of x and summed per modulus; the sums'
-// symmetric residues go out as bytes [r][rows].  A row whose extent in row_ptr is not
+// spmv_residues_kernel: one thread per row, the workgroup's entries staged in LDS by
+// coalesced loads.  The row's values are read twice (maximum, then residues), their
+// residues are formed in registers, multiplied by the gathered residues of x and summed
+// per modulus; the sums' symmetric residues go out as bytes [r][rows].  A row whose extent in row_ptr is not
 // inside [0, nnz], that is longer than kmax or that holds a column index outside
 // [0, cols) reads nothing through it and gets the exponent INT32_MIN (its y is NaN).
 #include "ozk_internal.h"
@@ -104,55 +104,85 @@ __global__ __launch_bounds__(256) void x_residues_kernel(const double* __restric
     dst[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
 }
 
+constexpr int kSpmvRows = 256;    // rows (one per thread) per workgroup
+constexpr int kSpmvCap = 2048;    // entries of a workgroup's rows staged in LDS
+
+// One thread per row.  The workgroup first copies the values and column indices of its
+// 256 rows (one contiguous range of the CSR arrays) into LDS with coalesced loads, when
+// the range is well formed and holds at most kSpmvCap entries; a row then reads its
+// entries from LDS if its extent lies inside that range, else from global memory (the
+// result is the same either way).
 template <bool kWide, int kXS>
-__global__ __launch_bounds__(256) void spmv_residues_kernel(
+__global__ __launch_bounds__(kSpmvRows) void spmv_residues_kernel(
     int64_t rows, int64_t cols, int64_t nnz, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const double* __restrict__ vals, int64_t kmax,
     ResidueConsts K, int p_bits, const int8_t* __restrict__ xres, int8_t* __restrict__ res,
     int32_t* __restrict__ exps) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  __shared__ double s_val[kSpmvCap];
+  __shared__ int32_t s_col[kSpmvCap];
+  const int64_t b0 = (int64_t)blockIdx.x * kSpmvRows;
+  const int64_t bend = b0 + kSpmvRows < rows ? b0 + kSpmvRows : rows;
+  const int64_t s0 = row_ptr[b0], s1 = row_ptr[bend];
+  const bool staged = s0 >= 0 && s1 >= s0 && s1 <= nnz && s1 - s0 <= kSpmvCap;
+  if (staged) {
+    const int cnt = (int)(s1 - s0);
+    for (int e = threadIdx.x; e < cnt; e += kSpmvRows) {
+      s_val[e] = vals[s0 + e];
+      s_col[e] = col_idx[s0 + e];
+    }
+  }
+  __syncthreads();
+  const int64_t i = b0 + threadIdx.x;
   if (i >= rows) return;
   const int64_t s = row_ptr[i], t = row_ptr[i + 1];
-  bool ok = s >= 0 && t >= s && t <= nnz && t - s <= kmax;
-  uint64_t mx = 0;
-  if (ok) {
-    for (int64_t p = s; p < t; ++p) {
-      const int64_t c = col_idx[p];
-      ok = ok && c >= 0 && c < cols;
-      mx = mx > abs_bits(vals[p]) ? mx : abs_bits(vals[p]);
-    }
-  }
-  const int e = ok ? line_exponent(mx, p_bits) : INT32_MIN;
-  exps[i] = e;
-  int acc[kXS];
-#pragma unroll
-  for (int l = 0; l < kXS; ++l) acc[l] = 0;
-  if (e != INT32_MIN) {
-    for (int64_t p = s; p < t; ++p) {
-      const uint4* xs = reinterpret_cast<const uint4*>(xres + (int64_t)col_idx[p] * kXS);
-      uint32_t xw[kXS / 4];
-#pragma unroll
-      for (int q = 0; q < kXS / 16; ++q) {
-        const uint4 v = xs[q];
-        xw[4 * q] = v.x;
-        xw[4 * q + 1] = v.y;
-        xw[4 * q + 2] = v.z;
-        xw[4 * q + 3] = v.w;
+
+  auto row = [&](auto val_at, auto col_at) {
+    bool ok = s >= 0 && t >= s && t <= nnz && t - s <= kmax;
+    uint64_t mx = 0;
+    if (ok) {
+      for (int64_t p = s; p < t; ++p) {
+        const int64_t c = col_at(p);
+        ok = ok && c >= 0 && c < cols;
+        const uint64_t b = abs_bits(val_at(p));
+        mx = mx > b ? mx : b;
       }
-      const Prepared pr = prepare_element<kWide>(vals[p], e);
-      acc[0] += (int)(int8_t)residue_byte_256(pr) * (int)(int8_t)(xw[0] & 0xffu);
-#pragma unroll
-      for (int l = 1; l < kXS; ++l)
-        if (l < K.r)
-          acc[l] += (int)(int8_t)residue_byte<kWide>(pr, K.m[l], K.inv[l], K.c32[l]) *
-                    (int)(int8_t)((xw[l / 4] >> (8 * (l % 4))) & 0xffu);
     }
-  }
-  res[i] = (int8_t)(acc[0] & 0xff);
+    const int e = ok ? line_exponent(mx, p_bits) : INT32_MIN;
+    exps[i] = e;
+    int acc[kXS];
 #pragma unroll
-  for (int l = 1; l < kXS; ++l)
-    if (l < K.r)
-      res[l * rows + i] = (int8_t)sum_residue_byte(acc[l], (uint32_t)K.m[l], K.inv[l]);
+    for (int l = 0; l < kXS; ++l) acc[l] = 0;
+    if (e != INT32_MIN) {
+      for (int64_t p = s; p < t; ++p) {
+        const uint4* xs = reinterpret_cast<const uint4*>(xres + col_at(p) * kXS);
+        uint32_t xw[kXS / 4];
+#pragma unroll
+        for (int q = 0; q < kXS / 16; ++q) {
+          const uint4 v = xs[q];
+          xw[4 * q] = v.x;
+          xw[4 * q + 1] = v.y;
+          xw[4 * q + 2] = v.z;
+          xw[4 * q + 3] = v.w;
+        }
+        const Prepared pr = prepare_element<kWide>(val_at(p), e);
+        acc[0] += (int)(int8_t)residue_byte_256(pr) * (int)(int8_t)(xw[0] & 0xffu);
+#pragma unroll
+        for (int l = 1; l < kXS; ++l)
+          if (l < K.r)
+            acc[l] += (int)(int8_t)residue_byte<kWide>(pr, K.m[l], K.inv[l], K.c32[l]) *
+                      (int)(int8_t)((xw[l / 4] >> (8 * (l % 4))) & 0xffu);
+      }
+    }
+    res[i] = (int8_t)(acc[0] & 0xff);
+#pragma unroll
+    for (int l = 1; l < kXS; ++l)
+      if (l < K.r)
+        res[l * rows + i] = (int8_t)sum_residue_byte(acc[l], (uint32_t)K.m[l], K.inv[l]);
+  };
+  if (staged && s >= s0 && t >= s && t <= s1)
+    row([&](int64_t p) { return s_val[p - s0]; }, [&](int64_t p) { return (int64_t)s_col[p - s0]; });
+  else
+    row([&](int64_t p) { return vals[p]; }, [&](int64_t p) { return (int64_t)col_idx[p]; });
 }
 
 }  // namespace
@@ -169,11 +199,11 @@ int launch_spmv(int64_t rows, int64_t cols, int64_t nnz, const int32_t* row_ptr,
   if (hipGetLastError() != hipSuccess) return OZK_EHIP;
   const ResidueConsts& KB = *residue_consts(r, p_b);
   const ResidueConsts& KA = *residue_consts(r, p_a);
-  const dim3 gx((unsigned)((cols + 255) / 256)), gr((unsigned)((rows + 255) / 256));
+  const dim3 gx((unsigned)((cols + 255) / 256)), gr((unsigned)((rows + kSpmvRows - 1) / kSpmvRows));
 #define OZK_SPMV(W, XS)                                                                      \
   hipLaunchKernelGGL((x_residues_kernel<W, XS>), gx, dim3(256), 0, s, x, cols, x_exp, KB,   \
                      xres);                                                                  \
-  hipLaunchKernelGGL((spmv_residues_kernel<W, XS>), gr, dim3(256), 0, s, rows, cols, nnz,  \
+  hipLaunchKernelGGL((spmv_residues_kernel<W, XS>), gr, dim3(kSpmvRows), 0, s, rows, cols, nnz, \
                      row_ptr, col_idx, vals, kmax, KA, p_a, xres, res, exps)
   // one residue arithmetic for both sides: the wide one if either side needs it
   const bool wide = KA.wide || KB.wide;
