@@ -14,8 +14,11 @@
 // per modulus; the sums' symmetric residues go out as bytes [r][rows].  A row whose extent in row_ptr is not
 // inside [0, nnz], that is longer than kmax or that holds a column index outside
 // [0, cols) reads nothing through it and gets the exponent INT32_MIN (its y is NaN).
+#include <type_traits>
+
 #include "ozk_internal.h"
 #include "residue_math.h"
+#include "rns_table.h"
 
 namespace ozk {
 namespace {
@@ -104,6 +107,19 @@ __global__ __launch_bounds__(256) void x_residues_kernel(const double* __restric
     dst[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
 }
 
+// Moduli and their residue constants at compile time: the row pass is instantiated per r,
+// so every modulus's constants are immediates or scalar moves and no per-modulus branch
+// remains.
+constexpr RnsTable kRns = make_rns_table();
+
+template <int L, int N, typename F>
+__device__ __forceinline__ void for_moduli(F&& f) {
+  if constexpr (L < N) {
+    f(std::integral_constant<int, L>{});
+    for_moduli<L + 1, N>(f);
+  }
+}
+
 constexpr int kSpmvRows = 256;    // rows (one per thread) per workgroup
 constexpr int kSpmvCap = 2048;    // entries of a workgroup's rows staged in LDS
 
@@ -112,12 +128,13 @@ constexpr int kSpmvCap = 2048;    // entries of a workgroup's rows staged in LDS
 // the range is well formed and holds at most kSpmvCap entries; a row then reads its
 // entries from LDS if its extent lies inside that range, else from global memory (the
 // result is the same either way).
-template <bool kWide, int kXS>
+template <bool kWide, int R>
 __global__ __launch_bounds__(kSpmvRows) void spmv_residues_kernel(
     int64_t rows, int64_t cols, int64_t nnz, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const double* __restrict__ vals, int64_t kmax,
-    ResidueConsts K, int p_bits, const int8_t* __restrict__ xres, int8_t* __restrict__ res,
+    int p_bits, const int8_t* __restrict__ xres, int8_t* __restrict__ res,
     int32_t* __restrict__ exps) {
+  constexpr int kXS = R <= 16 ? 16 : 32;     // bytes of x's residues per entry
   __shared__ double s_val[kSpmvCap];
   __shared__ int32_t s_col[kSpmvCap];
   const int64_t b0 = (int64_t)blockIdx.x * kSpmvRows;
@@ -149,9 +166,9 @@ __global__ __launch_bounds__(kSpmvRows) void spmv_residues_kernel(
     }
     const int e = ok ? line_exponent(mx, p_bits) : INT32_MIN;
     exps[i] = e;
-    int acc[kXS];
+    int acc[R];
 #pragma unroll
-    for (int l = 0; l < kXS; ++l) acc[l] = 0;
+    for (int l = 0; l < R; ++l) acc[l] = 0;
     if (e != INT32_MIN) {
       for (int64_t p = s; p < t; ++p) {
         const uint4* xs = reinterpret_cast<const uint4*>(xres + col_at(p) * kXS);
@@ -166,24 +183,51 @@ __global__ __launch_bounds__(kSpmvRows) void spmv_residues_kernel(
         }
         const Prepared pr = prepare_element<kWide>(val_at(p), e);
         acc[0] += (int)(int8_t)residue_byte_256(pr) * (int)(int8_t)(xw[0] & 0xffu);
-#pragma unroll
-        for (int l = 1; l < kXS; ++l)
-          if (l < K.r)
-            acc[l] += (int)(int8_t)residue_byte<kWide>(pr, K.m[l], K.inv[l], K.c32[l]) *
-                      (int)(int8_t)((xw[l / 4] >> (8 * (l % 4))) & 0xffu);
+        for_moduli<1, R>([&](auto lc) {
+          constexpr int l = decltype(lc)::value;
+          constexpr double m = (double)kRns.moduli[l], inv = kRns.inv[l], c32 = kRns.c32[l];
+          acc[l] += (int)(int8_t)residue_byte<kWide>(pr, m, inv, c32) *
+                    (int)(int8_t)((xw[l / 4] >> (8 * (l % 4))) & 0xffu);
+        });
       }
     }
     res[i] = (int8_t)(acc[0] & 0xff);
-#pragma unroll
-    for (int l = 1; l < kXS; ++l)
-      if (l < K.r)
-        res[l * rows + i] = (int8_t)sum_residue_byte(acc[l], (uint32_t)K.m[l], K.inv[l]);
+    for_moduli<1, R>([&](auto lc) {
+      constexpr int l = decltype(lc)::value;
+      constexpr uint32_t m = (uint32_t)kRns.moduli[l];
+      constexpr double inv = kRns.inv[l];
+      res[l * rows + i] = (int8_t)sum_residue_byte(acc[l], m, inv);
+    });
   };
   if (staged && s >= s0 && t >= s && t <= s1)
     row([&](int64_t p) { return s_val[p - s0]; }, [&](int64_t p) { return (int64_t)s_col[p - s0]; });
   else
     row([&](int64_t p) { return vals[p]; }, [&](int64_t p) { return (int64_t)col_idx[p]; });
 }
+
+template <int... Rs>
+struct SpmvDispatch {
+  static void go(int, bool, dim3, hipStream_t, int64_t, int64_t, int64_t, const int32_t*,
+                 const int32_t*, const double*, int64_t, int, const int8_t*, int8_t*, int32_t*) {}
+};
+
+template <int R0, int... Rs>
+struct SpmvDispatch<R0, Rs...> {
+  static void go(int r, bool wide, dim3 g, hipStream_t s, int64_t rows, int64_t cols,
+                 int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx, const double* vals,
+                 int64_t kmax, int p_a, const int8_t* xres, int8_t* res, int32_t* exps) {
+    if (r != R0) {
+      SpmvDispatch<Rs...>::go(r, wide, g, s, rows, cols, nnz, row_ptr, col_idx, vals, kmax, p_a,
+                              xres, res, exps);
+    } else if (wide) {
+      hipLaunchKernelGGL((spmv_residues_kernel<true, R0>), g, dim3(kSpmvRows), 0, s, rows, cols,
+                         nnz, row_ptr, col_idx, vals, kmax, p_a, xres, res, exps);
+    } else {
+      hipLaunchKernelGGL((spmv_residues_kernel<false, R0>), g, dim3(kSpmvRows), 0, s, rows, cols,
+                         nnz, row_ptr, col_idx, vals, kmax, p_a, xres, res, exps);
+    }
+  }
+};
 
 }  // namespace
 
@@ -200,19 +244,25 @@ int launch_spmv(int64_t rows, int64_t cols, int64_t nnz, const int32_t* row_ptr,
   const ResidueConsts& KB = *residue_consts(r, p_b);
   const ResidueConsts& KA = *residue_consts(r, p_a);
   const dim3 gx((unsigned)((cols + 255) / 256)), gr((unsigned)((rows + kSpmvRows - 1) / kSpmvRows));
-#define OZK_SPMV(W, XS)                                                                      \
-  hipLaunchKernelGGL((x_residues_kernel<W, XS>), gx, dim3(256), 0, s, x, cols, x_exp, KB,   \
-                     xres);                                                                  \
-  hipLaunchKernelGGL((spmv_residues_kernel<W, XS>), gr, dim3(kSpmvRows), 0, s, rows, cols, nnz, \
-                     row_ptr, col_idx, vals, kmax, KA, p_a, xres, res, exps)
   // one residue arithmetic for both sides: the wide one if either side needs it
   const bool wide = KA.wide || KB.wide;
   if (r <= 16) {
-    if (wide) { OZK_SPMV(true, 16); } else { OZK_SPMV(false, 16); }
+    if (wide)
+      hipLaunchKernelGGL((x_residues_kernel<true, 16>), gx, dim3(256), 0, s, x, cols, x_exp, KB,
+                         xres);
+    else
+      hipLaunchKernelGGL((x_residues_kernel<false, 16>), gx, dim3(256), 0, s, x, cols, x_exp,
+                         KB, xres);
   } else {
-    if (wide) { OZK_SPMV(true, 32); } else { OZK_SPMV(false, 32); }
+    if (wide)
+      hipLaunchKernelGGL((x_residues_kernel<true, 32>), gx, dim3(256), 0, s, x, cols, x_exp, KB,
+                         xres);
+    else
+      hipLaunchKernelGGL((x_residues_kernel<false, 32>), gx, dim3(256), 0, s, x, cols, x_exp,
+                         KB, xres);
   }
-#undef OZK_SPMV
+  SpmvDispatch<1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20>::go(
+      r, wide, gr, s, rows, cols, nnz, row_ptr, col_idx, vals, kmax, p_a, xres, res, exps);
   return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
 }
 
