@@ -150,16 +150,30 @@ __global__ __launch_bounds__(256, 1) void gemv_fly_kernel(
     for (int v = 0; v < 16; ++v) acc[q][v] = 0;
 
   const int64_t nc = ldp / 32;
-  // X staging: NR moduli x 32 columns x 32 bytes = NR * 64 chunks of 16 bytes.
-  auto stage_x = [&](int buf, int64_t c) {
-    for (int idx = tid; idx < NR * 64; idx += 256) {
-      const int q = idx >> 6;
-      int col = (idx >> 1) & 31;
-      const int hh = idx & 1;
-      col = col < nrhs ? col : nrhs - 1;
-      const v4i v = *reinterpret_cast<const v4i*>(xp + (int64_t)(l0 + q) * x_stride + col * ldp +
-                                                  c * 32 + 16 * hh);
-      *reinterpret_cast<v4i*>(&xs[buf][q][(idx >> 1) & 31][16 * hh]) = v;
+  // X staging: NR moduli x 32 columns x 32 bytes = NR * 64 chunks of 16 bytes, fetched
+  // into registers together with the next chunk of A and written to LDS only after the
+  // current chunk's arithmetic, so that no wait for them stalls the A prefetch.
+  constexpr int kXL = (NR * 64 + 255) / 256;      // chunks per thread
+  auto fetch_x = [&](v4i (&xr)[kXL], int64_t c) {
+#pragma unroll
+    for (int u = 0; u < kXL; ++u) {
+      const int idx = tid + 256 * u;
+      if (idx < NR * 64) {
+        const int q = idx >> 6;
+        int col = (idx >> 1) & 31;
+        const int hh = idx & 1;
+        col = col < nrhs ? col : nrhs - 1;
+        xr[u] = *reinterpret_cast<const v4i*>(xp + (int64_t)(l0 + q) * x_stride + col * ldp +
+                                              c * 32 + 16 * hh);
+      }
+    }
+  };
+  auto store_x = [&](const v4i (&xr)[kXL], int buf) {
+#pragma unroll
+    for (int u = 0; u < kXL; ++u) {
+      const int idx = tid + 256 * u;
+      if (idx < NR * 64)
+        *reinterpret_cast<v4i*>(&xs[buf][idx >> 6][(idx >> 1) & 31][16 * (idx & 1)]) = xr[u];
     }
   };
   auto load_a = [&](double (&v)[16], int64_t c) {
@@ -178,14 +192,16 @@ __global__ __launch_bounds__(256, 1) void gemv_fly_kernel(
   };
 
   double cur[16], nxt[16];
+  v4i xr[kXL];
   load_a(cur, 0);
-  stage_x(0, 0);
+  fetch_x(xr, 0);
+  store_x(xr, 0);
   __syncthreads();
   for (int64_t c = 0; c < nc; ++c) {
     const int buf = (int)(c & 1);
     if (c + 1 < nc) {
       load_a(nxt, c + 1);
-      stage_x(buf ^ 1, c + 1);
+      fetch_x(xr, c + 1);
     }
     Prepared p[16];
 #pragma unroll
@@ -211,6 +227,7 @@ __global__ __launch_bounds__(256, 1) void gemv_fly_kernel(
       const v4i xf = *reinterpret_cast<const v4i*>(&xs[buf][q][lane & 31][16 * half]);
       acc[q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(frag, xf, acc[q], 0, 0, 0);
     }
+    if (c + 1 < nc) store_x(xr, buf ^ 1);  // buffer buf ^ 1 was last read before the barrier
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < 16; ++u) cur[u] = nxt[u];
