@@ -5,13 +5,13 @@
 //   on the fly  A arrives as fp64 (8 bytes per element) and every element is scaled,
 //               rounded and reduced modulo each modulus in registers before the products:
 //               the per-input deconstruction term sits on the VALU.
-// Both feed v_mfma_i32_32x32x32_i8 with the 1..32 right-hand sides padded to 32 columns
-// (the MFMA time stays far below the HBM time) and write the symmetric residues of the
-// exact int32 products; the CRT kernel then reconstructs Y.
-//
-// MFMA operand layout used here: for K chunk k0 of 32, lane (row or column = lane & 31,
-// half = lane >> 5) supplies the 16 bytes at K = k0 + 16*half .. +15, identically for A
-// (rows) and X (columns), so the K order inside the instruction does not matter.
+// Both write the symmetric residues of the exact int32 products; the CRT kernel then
+// reconstructs Y.  The stored path feeds v_mfma_i32_32x32x32_i8 with the 1..32
+// right-hand sides padded to 32 columns (the MFMA time stays far below the HBM time):
+// for K chunk k0 of 32, lane (row or column = lane & 31, half = lane >> 5) supplies the
+// 16 bytes at K = k0 + 16*half .. +15, identically for A (rows) and X (columns), so the
+// K order inside the instruction does not matter.  The on-the-fly path uses 16-row tiles
+// (v_mfma_i32_16x16x32_i8, see there) to keep its accumulators small.
 #include "ozk_internal.h"
 #include "residue_math.h"
 
@@ -120,78 +120,89 @@ __global__ __launch_bounds__(256) void gemv_stored_kernel(
 }
 
 // ------------------------------------------------------------------ on the fly
-// grid ceil(m / 128); 4 waves, each 32 rows and the moduli l0 .. l0+NR-1 (NR accumulator
-// tiles in AGPRs).  Per K chunk of 32: each lane loads its row's 16 fp64 values, scales
-// and rounds them (row exponent from exps), turns them into 16 residue bytes per modulus
-// and issues one MFMA per modulus against the X residues staged in LDS.
-template <bool kWide, int NR>
-__global__ __launch_bounds__(256, 1) void gemv_fly_kernel(
+// grid ceil(m / 128); 8 waves, each 16 rows and the moduli l0 .. l0+NR-1 against CT tiles
+// of 16 right-hand sides (v_mfma_i32_16x16x32_i8: NR x CT accumulators of 4 AGPRs, so the
+// kernel fits two waves per SIMD).  Per K step of 32: lane (row = lane & 15, quarter
+// kq = lane >> 4) loads the 8 fp64 values K = 32 c + 8 kq .. +7 of its row, scales and
+// rounds them (row exponent from exps), turns them into 8 residue bytes per modulus and
+// issues one MFMA per modulus and column tile against the X residues staged in LDS.  The
+// next step's A values and X residues are loaded into registers before this step's
+// arithmetic; the X residues go to LDS after it.
+//
+// Operand layout of the 16 x 16 x 32 instruction: lane supplies K = 8 (lane >> 4) .. +7 of
+// row (A) or column (B) lane & 15; the accumulator holds rows 4 (lane >> 4) .. +3 of
+// column lane & 15.
+typedef long v1l;
+constexpr int kFlyWaves = 8;
+constexpr int kFlyThreads = 64 * kFlyWaves;
+constexpr int kFlyRows = 16 * kFlyWaves;     // rows per workgroup
+constexpr int kXsPitch = 48;                 // bytes per staged X column (32 used)
+
+template <bool kWide, int NR, int CT>
+__global__ __launch_bounds__(kFlyThreads, 1) void gemv_fly_kernel(
     const double* __restrict__ a, int64_t m, int64_t k, int64_t lda,
     const int32_t* __restrict__ exps, ResidueConsts K, int l0, const int8_t* __restrict__ xp,
     int64_t ldp, int64_t x_stride, int nrhs, int8_t* __restrict__ res, int64_t res_stride,
     GemvModuli E, int vec) {
-  __shared__ __attribute__((aligned(16))) int8_t xs[2][NR][32][32];
+  __shared__ __attribute__((aligned(16))) int8_t xs[2][NR][32][kXsPitch];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (tid >> 6)) * 32;
-  int64_t row = row0 + (lane & 31);
+  const int64_t row0 = ((int64_t)blockIdx.x * kFlyWaves + (tid >> 6)) * 16;
+  int64_t row = row0 + (lane & 15);
   row = row < m ? row : m - 1;
-  const int half = lane >> 5;
+  const int kq = lane >> 4;
   int e = exps[row];
   const bool bad = e == INT32_MIN;
   if (bad) e = 0;
   const int64_t klim = bad ? 0 : k;  // a row with Inf/NaN contributes residues 0
   const double* pa = a + row * lda;
 
-  v16i acc[NR];
+  v4i acc[NR][CT];
 #pragma unroll
   for (int q = 0; q < NR; ++q)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[q][v] = 0;
+    for (int t = 0; t < CT; ++t) acc[q][t] = v4i{0, 0, 0, 0};
 
   const int64_t nc = ldp / 32;
-  // X staging: NR moduli x 32 columns x 32 bytes = NR * 64 chunks of 16 bytes, fetched
-  // into registers together with the next chunk of A and written to LDS only after the
-  // current chunk's arithmetic, so that no wait for them stalls the A prefetch.
-  constexpr int kXL = (NR * 64 + 255) / 256;      // chunks per thread
+  // X staging: NR moduli x 32 columns x 32 bytes = NR * 64 chunks of 16 bytes.
+  constexpr int kXL = (NR * 64 + kFlyThreads - 1) / kFlyThreads;   // chunks per thread
   auto fetch_x = [&](v4i (&xr)[kXL], int64_t c) {
 #pragma unroll
     for (int u = 0; u < kXL; ++u) {
-      const int idx = tid + 256 * u;
+      const int idx = tid + kFlyThreads * u;
       if (idx < NR * 64) {
         const int q = idx >> 6;
         int col = (idx >> 1) & 31;
-        const int hh = idx & 1;
         col = col < nrhs ? col : nrhs - 1;
         xr[u] = *reinterpret_cast<const v4i*>(xp + (int64_t)(l0 + q) * x_stride + col * ldp +
-                                              c * 32 + 16 * hh);
+                                              c * 32 + 16 * (idx & 1));
       }
     }
   };
   auto store_x = [&](const v4i (&xr)[kXL], int buf) {
 #pragma unroll
     for (int u = 0; u < kXL; ++u) {
-      const int idx = tid + 256 * u;
+      const int idx = tid + kFlyThreads * u;
       if (idx < NR * 64)
         *reinterpret_cast<v4i*>(&xs[buf][idx >> 6][(idx >> 1) & 31][16 * (idx & 1)]) = xr[u];
     }
   };
-  auto load_a = [&](double (&v)[16], int64_t c) {
-    const int64_t h0 = c * 32 + 16 * half;
-    if (vec && h0 + 16 <= klim) {
+  auto load_a = [&](double (&v)[8], int64_t c) {
+    const int64_t h0 = c * 32 + 8 * kq;
+    if (vec && h0 + 8 <= klim) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 4; ++u) {
         const double2 d = *reinterpret_cast<const double2*>(pa + h0 + 2 * u);
         v[2 * u] = d.x;
         v[2 * u + 1] = d.y;
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = h0 + u < klim ? pa[h0 + u] : 0.0;
+      for (int u = 0; u < 8; ++u) v[u] = h0 + u < klim ? pa[h0 + u] : 0.0;
     }
   };
 
-  double cur[16], nxt[16];
+  double cur[8], nxt[8];
   v4i xr[kXL];
   load_a(cur, 0);
   fetch_x(xr, 0);
@@ -203,40 +214,54 @@ __global__ __launch_bounds__(256, 1) void gemv_fly_kernel(
       load_a(nxt, c + 1);
       fetch_x(xr, c + 1);
     }
-    Prepared p[16];
+    Prepared p[8];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) p[u] = prepare_element<kWide>(cur[u], e);
+    for (int u = 0; u < 8; ++u) p[u] = prepare_element<kWide>(cur[u], e);
 #pragma unroll
     for (int q = 0; q < NR; ++q) {
       const int l = l0 + q;
-      v4i frag;
+      uint32_t w0, w1;
       if (l == 0) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          frag[w] = (int)pack4(residue_byte_256(p[4 * w]), residue_byte_256(p[4 * w + 1]),
-                               residue_byte_256(p[4 * w + 2]), residue_byte_256(p[4 * w + 3]));
+        w0 = pack4(residue_byte_256(p[0]), residue_byte_256(p[1]), residue_byte_256(p[2]),
+                   residue_byte_256(p[3]));
+        w1 = pack4(residue_byte_256(p[4]), residue_byte_256(p[5]), residue_byte_256(p[6]),
+                   residue_byte_256(p[7]));
       } else {
         const double md = K.m[l], inv = K.inv[l], c32 = K.c32[l];
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          frag[w] = (int)pack4(residue_byte<kWide>(p[4 * w], md, inv, c32),
-                               residue_byte<kWide>(p[4 * w + 1], md, inv, c32),
-                               residue_byte<kWide>(p[4 * w + 2], md, inv, c32),
-                               residue_byte<kWide>(p[4 * w + 3], md, inv, c32));
+        w0 = pack4(residue_byte<kWide>(p[0], md, inv, c32), residue_byte<kWide>(p[1], md, inv, c32),
+                   residue_byte<kWide>(p[2], md, inv, c32), residue_byte<kWide>(p[3], md, inv, c32));
+        w1 = pack4(residue_byte<kWide>(p[4], md, inv, c32), residue_byte<kWide>(p[5], md, inv, c32),
+                   residue_byte<kWide>(p[6], md, inv, c32), residue_byte<kWide>(p[7], md, inv, c32));
       }
-      const v4i xf = *reinterpret_cast<const v4i*>(&xs[buf][q][lane & 31][16 * half]);
-      acc[q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(frag, xf, acc[q], 0, 0, 0);
+      const v1l frag = (v1l)(((uint64_t)w1 << 32) | w0);
+#pragma unroll
+      for (int t = 0; t < CT; ++t) {
+        const v1l xf = *reinterpret_cast<const v1l*>(&xs[buf][q][16 * t + (lane & 15)][8 * kq]);
+        acc[q][t] = __builtin_amdgcn_mfma_i32_16x16x32_i8(frag, xf, acc[q][t], 0, 0, 0);
+      }
     }
     if (c + 1 < nc) store_x(xr, buf ^ 1);  // buffer buf ^ 1 was last read before the barrier
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < 16; ++u) cur[u] = nxt[u];
+    for (int u = 0; u < 8; ++u) cur[u] = nxt[u];
   }
   if (row0 >= m) return;
 #pragma unroll
-  for (int q = 0; q < NR; ++q)
-    store_tile(acc[q], lane, row0, m, nrhs, E.mod[l0 + q], E.inv[l0 + q],
-               res + (int64_t)(l0 + q) * res_stride);
+  for (int q = 0; q < NR; ++q) {
+    const int mod = E.mod[l0 + q];
+    const double inv = E.inv[l0 + q];
+    int8_t* out = res + (int64_t)(l0 + q) * res_stride;
+#pragma unroll
+    for (int t = 0; t < CT; ++t) {
+      const int col = 16 * t + (lane & 15);
+      if (col >= nrhs) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t rr = row0 + 4 * kq + v;
+        if (rr < m) out[rr * nrhs + col] = (int8_t)sym_residue32(acc[q][t][v], mod, inv);
+      }
+    }
+  }
 }
 
 GemvModuli gemv_moduli(int r) {
@@ -255,8 +280,12 @@ void launch_fly(dim3 grid, hipStream_t s, const double* a, int64_t m, int64_t k,
                 int64_t ldp, int64_t x_stride, int nrhs, int8_t* res, int64_t res_stride,
                 const GemvModuli& E) {
   const int vec = (reinterpret_cast<uintptr_t>(a) & 15) == 0 && (lda & 1) == 0;
-  hipLaunchKernelGGL((gemv_fly_kernel<kWide, NR>), grid, dim3(256), 0, s, a, m, k, lda, exps, K,
-                     l0, xp, ldp, x_stride, nrhs, res, res_stride, E, vec);
+  if (nrhs <= 16)
+    hipLaunchKernelGGL((gemv_fly_kernel<kWide, NR, 1>), grid, dim3(kFlyThreads), 0, s, a, m, k,
+                       lda, exps, K, l0, xp, ldp, x_stride, nrhs, res, res_stride, E, vec);
+  else
+    hipLaunchKernelGGL((gemv_fly_kernel<kWide, NR, 2>), grid, dim3(kFlyThreads), 0, s, a, m, k,
+                       lda, exps, K, l0, xp, ldp, x_stride, nrhs, res, res_stride, E, vec);
 }
 
 template <bool kWide>
@@ -299,8 +328,8 @@ int launch_gemv_fly(const double* a, int64_t m, int64_t k, int64_t lda, const in
   if (m <= 0) return OZK_OK;
   const ResidueConsts& K = *residue_consts(r, p_bits);
   const GemvModuli E = gemv_moduli(r);
-  dim3 grid((unsigned)((m + 127) / 128));
-  // At most 16 moduli per pass (16 accumulator tiles = 256 AGPRs); r > 16 takes two.
+  dim3 grid((unsigned)((m + kFlyRows - 1) / kFlyRows));
+  // At most 16 moduli per pass (16 x 2 accumulator tiles = 128 AGPRs); r > 16 takes two.
   for (int l0 = 0; l0 < r; l0 += 16) {
     const int nr = r - l0 < 16 ? r - l0 : 16;
     if (K.wide)
