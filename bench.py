@@ -208,7 +208,7 @@ TME_KERNELS = {
                                     "element", 32768 * 32768, 14),
     "decon_cols_wide_4096_r16": ("residues_cols_kernel<true, false>", "element", 4096 * 4096,
                                  16),
-    "gemv_fly_32768_r14_32cols": ("gemv_fly_kernel<false, 14, 2>", "element of A",
+    "gemv_fly_32768_r14_32cols": ("gemv_fly_kernel<false, 0, 14, 2>", "element of A",
                                   32768 * 32768, 14),
     "gemv_digits_32768_r14_1col": ("gemv_digits_kernel<1>", "element of A", 32768 * 32768, 14),
     "gemv_digits_32768_r14_8cols": ("gemv_digits_kernel<4>", "element of A", 32768 * 32768, 14),

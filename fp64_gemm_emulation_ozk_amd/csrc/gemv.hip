@@ -12,8 +12,11 @@
 // 16 bytes at K = k0 + 16*half .. +15, identically for A (rows) and X (columns), so the
 // K order inside the instruction does not matter.  The on-the-fly path uses 16-row tiles
 // (v_mfma_i32_16x16x32_i8, see there) to keep its accumulators small.
+#include <type_traits>
+
 #include "ozk_internal.h"
 #include "residue_math.h"
+#include "rns_table.h"
 
 namespace ozk {
 namespace {
@@ -133,17 +136,29 @@ __global__ __launch_bounds__(256) void gemv_stored_kernel(
 // row (A) or column (B) lane & 15; the accumulator holds rows 4 (lane >> 4) .. +3 of
 // column lane & 15.
 typedef long v1l;
+// Moduli and their residue constants at compile time (the kernel is instantiated per pass
+// of moduli L0 .. L0+NR-1), so no constant is loaded inside the loop.
+constexpr RnsTable kRns = make_rns_table();
+
+template <int L, int N, typename F>
+__device__ __forceinline__ void for_moduli(F&& f) {
+  if constexpr (L < N) {
+    f(std::integral_constant<int, L>{});
+    for_moduli<L + 1, N>(f);
+  }
+}
+
 constexpr int kFlyWaves = 8;
 constexpr int kFlyThreads = 64 * kFlyWaves;
 constexpr int kFlyRows = 16 * kFlyWaves;     // rows per workgroup
 constexpr int kXsPitch = 48;                 // bytes per staged X column (32 used)
 
-template <bool kWide, int NR, int CT>
+template <bool kWide, int L0, int NR, int CT>
 __global__ __launch_bounds__(kFlyThreads, 1) void gemv_fly_kernel(
     const double* __restrict__ a, int64_t m, int64_t k, int64_t lda,
-    const int32_t* __restrict__ exps, ResidueConsts K, int l0, const int8_t* __restrict__ xp,
-    int64_t ldp, int64_t x_stride, int nrhs, int8_t* __restrict__ res, int64_t res_stride,
-    GemvModuli E, int vec) {
+    const int32_t* __restrict__ exps, const int8_t* __restrict__ xp, int64_t ldp,
+    int64_t x_stride, int nrhs, int8_t* __restrict__ res, int64_t res_stride, int vec) {
+  constexpr int l0 = L0;
   __shared__ __attribute__((aligned(16))) int8_t xs[2][NR][32][kXsPitch];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -217,17 +232,17 @@ __global__ __launch_bounds__(kFlyThreads, 1) void gemv_fly_kernel(
     Prepared p[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) p[u] = prepare_element<kWide>(cur[u], e);
-#pragma unroll
-    for (int q = 0; q < NR; ++q) {
-      const int l = l0 + q;
+    for_moduli<0, NR>([&](auto qc) {
+      constexpr int q = decltype(qc)::value;
+      constexpr int l = l0 + q;
       uint32_t w0, w1;
-      if (l == 0) {
+      if constexpr (l == 0) {
         w0 = pack4(residue_byte_256(p[0]), residue_byte_256(p[1]), residue_byte_256(p[2]),
                    residue_byte_256(p[3]));
         w1 = pack4(residue_byte_256(p[4]), residue_byte_256(p[5]), residue_byte_256(p[6]),
                    residue_byte_256(p[7]));
       } else {
-        const double md = K.m[l], inv = K.inv[l], c32 = K.c32[l];
+        constexpr double md = (double)kRns.moduli[l], inv = kRns.inv[l], c32 = kRns.c32[l];
         w0 = pack4(residue_byte<kWide>(p[0], md, inv, c32), residue_byte<kWide>(p[1], md, inv, c32),
                    residue_byte<kWide>(p[2], md, inv, c32), residue_byte<kWide>(p[3], md, inv, c32));
         w1 = pack4(residue_byte<kWide>(p[4], md, inv, c32), residue_byte<kWide>(p[5], md, inv, c32),
@@ -239,7 +254,7 @@ __global__ __launch_bounds__(kFlyThreads, 1) void gemv_fly_kernel(
         const v1l xf = *reinterpret_cast<const v1l*>(&xs[buf][q][16 * t + (lane & 15)][8 * kq]);
         acc[q][t] = __builtin_amdgcn_mfma_i32_16x16x32_i8(frag, xf, acc[q][t], 0, 0, 0);
       }
-    }
+    });
     if (c + 1 < nc) store_x(xr, buf ^ 1);  // buffer buf ^ 1 was last read before the barrier
     __syncthreads();
 #pragma unroll
@@ -248,8 +263,8 @@ __global__ __launch_bounds__(kFlyThreads, 1) void gemv_fly_kernel(
   if (row0 >= m) return;
 #pragma unroll
   for (int q = 0; q < NR; ++q) {
-    const int mod = E.mod[l0 + q];
-    const double inv = E.inv[l0 + q];
+    const int mod = kRns.moduli[l0 + q];
+    const double inv = kRns.inv[l0 + q];
     int8_t* out = res + (int64_t)(l0 + q) * res_stride;
 #pragma unroll
     for (int t = 0; t < CT; ++t) {
@@ -274,37 +289,32 @@ GemvModuli gemv_moduli(int r) {
   return E;
 }
 
-template <bool kWide, int NR>
+template <bool kWide, int L0, int NR>
 void launch_fly(dim3 grid, hipStream_t s, const double* a, int64_t m, int64_t k, int64_t lda,
-                const int32_t* exps, const ResidueConsts& K, int l0, const int8_t* xp,
-                int64_t ldp, int64_t x_stride, int nrhs, int8_t* res, int64_t res_stride,
-                const GemvModuli& E) {
+                const int32_t* exps, const int8_t* xp, int64_t ldp, int64_t x_stride, int nrhs,
+                int8_t* res, int64_t res_stride) {
   const int vec = (reinterpret_cast<uintptr_t>(a) & 15) == 0 && (lda & 1) == 0;
   if (nrhs <= 16)
-    hipLaunchKernelGGL((gemv_fly_kernel<kWide, NR, 1>), grid, dim3(kFlyThreads), 0, s, a, m, k,
-                       lda, exps, K, l0, xp, ldp, x_stride, nrhs, res, res_stride, E, vec);
+    hipLaunchKernelGGL((gemv_fly_kernel<kWide, L0, NR, 1>), grid, dim3(kFlyThreads), 0, s, a, m,
+                       k, lda, exps, xp, ldp, x_stride, nrhs, res, res_stride, vec);
   else
-    hipLaunchKernelGGL((gemv_fly_kernel<kWide, NR, 2>), grid, dim3(kFlyThreads), 0, s, a, m, k,
-                       lda, exps, K, l0, xp, ldp, x_stride, nrhs, res, res_stride, E, vec);
+    hipLaunchKernelGGL((gemv_fly_kernel<kWide, L0, NR, 2>), grid, dim3(kFlyThreads), 0, s, a, m,
+                       k, lda, exps, xp, ldp, x_stride, nrhs, res, res_stride, vec);
 }
 
-template <bool kWide>
+// Passes of moduli: 0 .. min(r, 16) - 1, then 16 .. r - 1.
+template <bool kWide, int L0, int NR, int NMax>
 void dispatch_fly(int nr, dim3 grid, hipStream_t s, const double* a, int64_t m, int64_t k,
-                  int64_t lda, const int32_t* exps, const ResidueConsts& K, int l0,
-                  const int8_t* xp, int64_t ldp, int64_t x_stride, int nrhs, int8_t* res,
-                  int64_t res_stride, const GemvModuli& E) {
-#define OZK_FLY(N)                                                                            \
-  case N:                                                                                     \
-    launch_fly<kWide, N>(grid, s, a, m, k, lda, exps, K, l0, xp, ldp, x_stride, nrhs, res,    \
-                         res_stride, E);                                                      \
-    break
-  switch (nr) {
-    OZK_FLY(1); OZK_FLY(2); OZK_FLY(3); OZK_FLY(4); OZK_FLY(5); OZK_FLY(6); OZK_FLY(7);
-    OZK_FLY(8); OZK_FLY(9); OZK_FLY(10); OZK_FLY(11); OZK_FLY(12); OZK_FLY(13); OZK_FLY(14);
-    OZK_FLY(15); OZK_FLY(16);
-    default: break;
+                  int64_t lda, const int32_t* exps, const int8_t* xp, int64_t ldp,
+                  int64_t x_stride, int nrhs, int8_t* res, int64_t res_stride) {
+  if constexpr (NR <= NMax) {
+    if (nr == NR)
+      launch_fly<kWide, L0, NR>(grid, s, a, m, k, lda, exps, xp, ldp, x_stride, nrhs, res,
+                                res_stride);
+    else
+      dispatch_fly<kWide, L0, NR + 1, NMax>(nr, grid, s, a, m, k, lda, exps, xp, ldp, x_stride,
+                                            nrhs, res, res_stride);
   }
-#undef OZK_FLY
 }
 
 }  // namespace
@@ -326,18 +336,24 @@ int launch_gemv_fly(const double* a, int64_t m, int64_t k, int64_t lda, const in
                     int r, int p_bits, const int8_t* xp, int64_t ldp, int64_t x_stride, int nrhs,
                     int8_t* res, hipStream_t s) {
   if (m <= 0) return OZK_OK;
-  const ResidueConsts& K = *residue_consts(r, p_bits);
-  const GemvModuli E = gemv_moduli(r);
+  const bool wide = residue_consts(r, p_bits)->wide;
   dim3 grid((unsigned)((m + kFlyRows - 1) / kFlyRows));
-  // At most 16 moduli per pass (16 x 2 accumulator tiles = 128 AGPRs); r > 16 takes two.
-  for (int l0 = 0; l0 < r; l0 += 16) {
-    const int nr = r - l0 < 16 ? r - l0 : 16;
-    if (K.wide)
-      dispatch_fly<true>(nr, grid, s, a, m, k, lda, exps, K, l0, xp, ldp, x_stride, nrhs, res,
-                         m * nrhs, E);
+  // At most 16 moduli per pass (16 x 2 accumulator tiles = 128 registers); r > 16 takes two.
+  const int n0 = r < 16 ? r : 16;
+  if (wide)
+    dispatch_fly<true, 0, 1, 16>(n0, grid, s, a, m, k, lda, exps, xp, ldp, x_stride, nrhs, res,
+                                 m * nrhs);
+  else
+    dispatch_fly<false, 0, 1, 16>(n0, grid, s, a, m, k, lda, exps, xp, ldp, x_stride, nrhs, res,
+                                  m * nrhs);
+  if (hipGetLastError() != hipSuccess) return OZK_EHIP;
+  if (r > 16) {
+    if (wide)
+      dispatch_fly<true, 16, 1, kMaxModuli - 16>(r - 16, grid, s, a, m, k, lda, exps, xp, ldp,
+                                                 x_stride, nrhs, res, m * nrhs);
     else
-      dispatch_fly<false>(nr, grid, s, a, m, k, lda, exps, K, l0, xp, ldp, x_stride, nrhs, res,
-                          m * nrhs, E);
+      dispatch_fly<false, 16, 1, kMaxModuli - 16>(r - 16, grid, s, a, m, k, lda, exps, xp, ldp,
+                                                  x_stride, nrhs, res, m * nrhs);
     if (hipGetLastError() != hipSuccess) return OZK_EHIP;
   }
   return OZK_OK;
