@@ -180,6 +180,12 @@ def traffic_summary(fetch_dir: str, write_dir: str) -> int:
     data = {"what": "L2-to-fabric bytes per launch (HBM or MALL) from rocprofv3 FETCH_SIZE and "
                     "WRITE_SIZE (KiB per dispatch), each scaled by the factor that maps the "
                     "same counter on a plain 1 GiB device copy to 1 GiB",
+            "commands": [
+                "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv "
+                "-d <out>/fetch -o out -- python3 <repo>/bench.py --counters",
+                "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv "
+                "-d <out>/write -o out -- python3 <repo>/bench.py --counters",
+                "python3 bench.py --traffic-summary <out>/fetch <out>/write"],
             "calibration": {"copy_bytes": COPY_BYTES, "fetch_kib": copy_f, "write_kib": copy_w,
                             "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},
             "kernels": {}}
@@ -262,6 +268,10 @@ def tme_summary(run_dir: str) -> int:
     means = {c: _counter_means(run_dir, c) for c in TME_COUNTERS}
     data = {"what": "rocprofv3 --pmc " + " ".join(TME_COUNTERS) + " over `bench.py "
                     "--tme-counters`; instruction counts are per wave (64 lanes)",
+            "commands": [
+                "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + " ".join(TME_COUNTERS) +
+                " --output-format csv -d <out> -o out -- python3 <repo>/bench.py --tme-counters",
+                "python3 bench.py --tme-summary <out>"],
             "kernels": {}}
     for key, (sub, unit, units, r) in TME_KERNELS.items():
         ent = {"kernel": sub, "unit": unit, "units_per_dispatch": units, "r": r}
