@@ -6,6 +6,10 @@
 // transposed by the deconstruction), kp a multiple of 64 and zero-padded, so the K loop
 // has no tail.  |residue| <= 128 and kp <= 131072 keep every int32 sum exact.
 //
+// Two kernels share the tiling below: gemm_i8_pairs_kernel (K in steps of 128, at least two
+// of them: persistent, whole-cache-line loads, described above it) and gemm_i8_kernel (any
+// K that is a multiple of 64: one workgroup per tile, described here).
+//
 // Tiling: workgroup tile 256 x 256 x 64, 512 threads = 8 waves, two per SIMD.  Waves
 // 0..3 own rows 0..127 of the tile, waves 4..7 rows 128..255; each wave a 128 x 64 block
 // of 4 x 2 MFMA tiles of 32 x 32 (128 accumulator registers).  Each K step is two halves
