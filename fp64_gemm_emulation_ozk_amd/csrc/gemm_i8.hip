@@ -62,12 +62,13 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 // q = round(v / m) is read from the low word of v * RN(1/m) + 1.5 * 2^52: the product is
 // within 2^-30 of v / m, whose distance to a half-integer is at least 1 / (2m), so the
 // rounding is exact.  The residue v - q m lies in [-(m-1)/2, (m-1)/2]; its low byte is
-// (v - q m) mod 2^8, for which the low 24 bits of q suffice (v_mul_u32_u24).
+// (v - q m) mod 2^8, for which the low 24 bits of q suffice: one signed 24-bit
+// multiply-add q * (-m) + v (v_mad_i32_i24).
 __device__ __forceinline__ uint32_t residue_byte_odd(int v, uint32_t m, double inv) {
   constexpr double kMagicD = 6755399441055744.0;
   const double t = __builtin_fma((double)v, inv, kMagicD);
-  const uint32_t q = (uint32_t)__double_as_longlong(t);
-  return (uint32_t)v - __umul24(q, m);
+  const int q = (int)(uint32_t)__double_as_longlong(t);
+  return (uint32_t)(__mul24(q, -(int)m) + v);
 }
 
 // Bytes 0 of four words into one word (b0 lowest).

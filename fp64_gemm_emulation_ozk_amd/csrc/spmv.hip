@@ -28,8 +28,8 @@ namespace {
 // a half-integer is at least 1 / (2m), so the rounding is exact).
 __device__ __forceinline__ uint32_t sum_residue_byte(int v, uint32_t m, double inv) {
   constexpr double kMagicD = 6755399441055744.0;
-  const uint32_t q = (uint32_t)__double_as_longlong(__builtin_fma((double)v, inv, kMagicD));
-  return (uint32_t)v - __umul24(q, m);
+  const int q = (int)(uint32_t)__double_as_longlong(__builtin_fma((double)v, inv, kMagicD));
+  return (uint32_t)(__mul24(q, -(int)m) + v);   // low byte: the low 24 bits of q suffice
 }
 
 // Largest |x| (bit pattern) of each chunk of 2048 entries.
