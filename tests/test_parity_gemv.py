@@ -38,6 +38,9 @@ CASES = [
     (1, 1, 1, 5),
     (200, 300, 5, 20),
     (257, 4100, 32, 18),
+    # on-the-fly residue path (r * nrhs > 256) with a partly filled second 16-column tile
+    (130, 700, 20, 14),
+    (97, 333, 17, 16),
 ]
 
 

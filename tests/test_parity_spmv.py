@@ -88,3 +88,41 @@ def test_spmv_poisson_128_sampled():
     rows = np.sort(np.concatenate([rng.choice(n ** 3, 300, replace=False), [0, n ** 3 - 1]]))
     want = spmv.spmv_csr(rp, ci, v, x, 16, 7, rows=rows)
     assert assert_within_ulps(got[rows], want, 2) == 0
+
+
+def test_spmv_blocks_staged_and_direct():
+    """Row blocks of 256 whose entries fit the workgroup's LDS staging (short rows) next to
+    blocks that do not (long rows), in one matrix, against the oracle."""
+    announce("spmv staged and direct blocks")
+    r, kmax, cols = 14, 40, 3000
+    rp1, ci1, v1 = ozk_inputs.random_csr(600, cols, 6, seed=31, phi=1.0)
+    rp2, ci2, v2 = ozk_inputs.random_csr(500, cols, kmax, seed=32, phi=1.0)
+    rp = np.concatenate([rp1, rp2[1:] + rp1[-1]]).astype(np.int32)
+    ci = np.concatenate([ci1, ci2]).astype(np.int32)
+    v = np.concatenate([v1, v2])
+    x = ozk_inputs.phi_matrix(np.random.default_rng(33), (cols, 1), 2.0)[:, 0]
+    got = _run(rp, ci, v, x, r, kmax)
+    want = spmv.spmv_csr(rp, ci, v, x, r, kmax)
+    assert assert_within_ulps(got, want, 2) == 0
+
+
+def test_spmv_non_monotone_row_ptr():
+    """Rows whose extents leave the range their workgroup staged (row_ptr not monotone)
+    read their entries from global memory; a row with end < start is malformed (NaN).
+    Each well-formed row must equal the oracle on the same entries laid out in order."""
+    announce("spmv non-monotone row_ptr")
+    r, kmax = 12, 16
+    rng = np.random.default_rng(41)
+    nnz, cols = 40, 30
+    ci = rng.integers(0, cols, size=nnz).astype(np.int32)
+    v = ozk_inputs.uniform_matrix(rng, (1, nnz))[0]
+    # the workgroup stages entries [2, 20): rows 0 and 3 lie inside, row 2 starts before
+    # it (read from global memory), row 1 is reversed
+    rp = np.array([2, 9, 1, 6, 20], dtype=np.int32)
+    x = ozk_inputs.uniform_matrix(rng, (cols, 1))[:, 0]
+    got = _run(rp, ci, v, x, r, kmax)
+    assert np.isnan(got[1])
+    for i in (0, 2, 3):
+        s, t = int(rp[i]), int(rp[i + 1])
+        want = spmv.spmv_csr(np.array([0, t - s]), ci[s:t], v[s:t], x, r, kmax)
+        assert assert_within_ulps(got[i:i + 1], want, 2) == 0
