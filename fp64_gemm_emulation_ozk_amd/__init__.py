@@ -18,7 +18,8 @@ __all__ = [
     "LIB_PATH", "OzkError", "library",
     "ozk_version", "ozk_moduli", "ozk_scaling_bits", "ozk_scaling_bits_ex", "ozk_planes_ld",
     "ozk_deconstruct", "ozk_deconstruct_ex", "ozk_modular_products", "ozk_modular_residues",
-    "ozk_reconstruct", "ozk_dgemm", "ozk_dgemm_ex", "ozk_dgemv", "ozk_spmv_csr",
+    "ozk_reconstruct", "ozk_dgemm", "ozk_dgemm_ex", "ozk_dgemm_ex_timed", "ozk_dgemv",
+    "ozk_spmv_csr",
     "ozk_spmv_csr_workspace_size",
     "OZK_SCALING_MAX", "OZK_SCALING_NORM",
     "ozk_fp4limb_pack", "ozk_fp4limb_products", "ozk_int8gemm_fp4limb",
@@ -55,6 +56,8 @@ _SIGNATURES = {
                                   _i64, _ptr, _ptr, _size, _ptr]),
     "ozk_dgemm_ex": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
                             _ptr, _size, _ptr]),
+    "ozk_dgemm_ex_timed": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int,
+                                  _int, _ptr, _size, _ptr, _ptr, _ptr]),
     "ozk_dgemm_workspace_size": (_int, [_i64, _i64, _i64, _int, _ptr]),
     "ozk_spmv_csr_workspace_size": (_int, [_i64, _i64, _int, _ptr]),
     "ozk_spmv_csr": (_int, [_i64, _i64, _i64, _ptr, _ptr, _ptr, _i64, _ptr, _ptr, _int, _ptr,
@@ -317,6 +320,18 @@ def ozk_dgemm_ex(a: torch.Tensor, b: torch.Tensor, r: int, scaling="max",
     _call("ozk_dgemm_ex", m, n, k, _dev_ptr(a), _ld(a), _dev_ptr(b), _ld(b), _dev_ptr(out),
           _ld(out), r, _scaling(scaling), _dev_ptr(workspace), workspace.numel(),
           _stream(stream))
+    return out
+
+
+def ozk_dgemm_ex_timed(a: torch.Tensor, b: torch.Tensor, r: int, gemm_start, gemm_stop,
+                       scaling="max", out: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """ozk_dgemm_ex that records two torch.cuda.Event objects (enable_timing=True, already
+    recorded once so that they exist) around the launch of the residue products."""
+    m, n, k, out, workspace = _dgemm_args(a, b, r, out, workspace)
+    _call("ozk_dgemm_ex_timed", m, n, k, _dev_ptr(a), _ld(a), _dev_ptr(b), _ld(b),
+          _dev_ptr(out), _ld(out), r, _scaling(scaling), _dev_ptr(workspace), workspace.numel(),
+          _stream(stream), gemm_start.cuda_event, gemm_stop.cuda_event)
     return out
 
 

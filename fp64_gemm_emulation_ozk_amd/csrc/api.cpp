@@ -268,6 +268,15 @@ int ozk_dgemm_workspace_size(int64_t m, int64_t n, int64_t k, int r, size_t* byt
 int ozk_dgemm_ex(int64_t m, int64_t n, int64_t k, const double* A, int64_t lda,
                  const double* B, int64_t ldb, double* C, int64_t ldc, int r, int scaling,
                  void* workspace, size_t workspace_bytes, void* stream) {
+  return ozk_dgemm_ex_timed(m, n, k, A, lda, B, ldb, C, ldc, r, scaling, workspace,
+                            workspace_bytes, stream, nullptr, nullptr);
+}
+
+int ozk_dgemm_ex_timed(int64_t m, int64_t n, int64_t k, const double* A, int64_t lda,
+                       const double* B, int64_t ldb, double* C, int64_t ldc, int r, int scaling,
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       void* gemm_start, void* gemm_stop) {
+  if ((gemm_start == nullptr) != (gemm_stop == nullptr)) return OZK_EINVAL;
   if (check_r(r) != OZK_OK) return OZK_EINVAL;
   if (scaling != OZK_SCALING_MAX && scaling != OZK_SCALING_NORM) return OZK_EINVAL;
   if (m < 0 || n < 0 || k < 1) return OZK_EINVAL;
@@ -295,9 +304,13 @@ int ozk_dgemm_ex(int64_t m, int64_t n, int64_t k, const double* A, int64_t lda,
   if ((st = deconstruct_operands(A, m, k, lda, B, n, ldb, r, scaling, wa, wb, planes_a,
                                  planes_b, kp, exps_a, exps_b, scr_a, scr_b, s)))
     return st;
+  if (gemm_start && hipEventRecord(static_cast<hipEvent_t>(gemm_start), s) != hipSuccess)
+    return OZK_EHIP;
   if ((st = launch_gemm_i8(m, n, kp, r, planes_a, m * kp, planes_b, n * kp, residues, n, m * n,
                            kEpiResidues, s)))
     return st;
+  if (gemm_stop && hipEventRecord(static_cast<hipEvent_t>(gemm_stop), s) != hipSuccess)
+    return OZK_EHIP;
   return launch_crt(m, n, r, residues, 0, n, m * n, exps_a, exps_b, C, ldc, s);
 }
 

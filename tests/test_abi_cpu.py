@@ -159,6 +159,19 @@ def test_ex_validation(lib):
              1 << 20, None) == EINVAL
 
 
+def test_dgemm_timed_validation(lib):
+    f = lib.ozk_dgemm_ex_timed
+    # one event without the other
+    assert f(4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 14, 1, FAKE, 1 << 20, None, FAKE,
+             None) == EINVAL
+    assert f(4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 14, 1, FAKE, 1 << 20, None, None,
+             FAKE) == EINVAL
+    # otherwise the checks of ozk_dgemm_ex
+    assert f(4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 14, 2, FAKE, 1 << 20, None, None,
+             None) == EINVAL
+    assert f(0, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 14, 1, None, 0, None, None, None) == OK
+
+
 def test_spmv_validation(lib):
     f = lib.ozk_spmv_csr
     out = ctypes.c_size_t()
