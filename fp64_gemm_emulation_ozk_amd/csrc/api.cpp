@@ -304,13 +304,10 @@ int ozk_dgemm_ex_timed(int64_t m, int64_t n, int64_t k, const double* A, int64_t
   if ((st = deconstruct_operands(A, m, k, lda, B, n, ldb, r, scaling, wa, wb, planes_a,
                                  planes_b, kp, exps_a, exps_b, scr_a, scr_b, s)))
     return st;
-  if (gemm_start && hipEventRecord(static_cast<hipEvent_t>(gemm_start), s) != hipSuccess)
-    return OZK_EHIP;
   if ((st = launch_gemm_i8(m, n, kp, r, planes_a, m * kp, planes_b, n * kp, residues, n, m * n,
-                           kEpiResidues, s)))
+                           kEpiResidues, s, static_cast<hipEvent_t>(gemm_start),
+                           static_cast<hipEvent_t>(gemm_stop))))
     return st;
-  if (gemm_stop && hipEventRecord(static_cast<hipEvent_t>(gemm_stop), s) != hipSuccess)
-    return OZK_EHIP;
   return launch_crt(m, n, r, residues, 0, n, m * n, exps_a, exps_b, C, ldc, s);
 }
 

@@ -30,6 +30,8 @@
 #include <atomic>
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "lds_dma.h"
 #include "ozk_internal.h"
 
@@ -675,7 +677,7 @@ int compute_units() {
 
 int launch_gemm_i8(int64_t m, int64_t n, int64_t kp, int r, const int8_t* pa, int64_t stride_a,
                    const int8_t* pb, int64_t stride_b, void* out, int64_t ldo, int64_t stride_o,
-                   int epilogue, hipStream_t s) {
+                   int epilogue, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (m <= 0 || n <= 0) return OZK_OK;
   const int tiles_m = (int)((m + BM - 1) / BM);
   const int tiles_n = (int)((n + BN - 1) / BN);
@@ -702,12 +704,13 @@ int launch_gemm_i8(int64_t m, int64_t n, int64_t kp, int r, const int8_t* pa, in
   const int tiles = (int)blocks;
 #define OZK_GEMM(EPI)                                                                        \
   if (pairs)                                                                                 \
-    hipLaunchKernelGGL((gemm_i8_pairs_kernel<EPI, NW>), grid_p, block, 0, s, m, n, kp, pa,   \
-                       stride_a, pb, stride_b, out, ldo, stride_o, tiles_m, tiles_n, tiles, E, \
-                       vec_out);                                                             \
+    hipExtLaunchKernelGGL((gemm_i8_pairs_kernel<EPI, NW>), grid_p, block, 0, s, ev_start,    \
+                          ev_stop, 0, m, n, kp, pa, stride_a, pb, stride_b, out, ldo,         \
+                          stride_o, tiles_m, tiles_n, tiles, E, vec_out);                     \
   else                                                                                       \
-    hipLaunchKernelGGL((gemm_i8_kernel<EPI, NW>), grid, block, 0, s, m, n, kp, pa, stride_a,  \
-                       pb, stride_b, out, ldo, stride_o, tiles_m, tiles_n, E, vec_out)
+    hipExtLaunchKernelGGL((gemm_i8_kernel<EPI, NW>), grid, block, 0, s, ev_start, ev_stop, 0, \
+                          m, n, kp, pa, stride_a, pb, stride_b, out, ldo, stride_o, tiles_m,  \
+                          tiles_n, E, vec_out)
   if (epilogue == kEpiProducts) {
     OZK_GEMM(kEpiProducts);
   } else {

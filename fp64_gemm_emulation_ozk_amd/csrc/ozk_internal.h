@@ -123,9 +123,12 @@ int launch_fp4_gemm(int64_t m, int64_t n, int64_t ldpb, const uint8_t* pa, int64
                     const uint8_t* pb, int64_t stride_b, int32_t* c, int64_t ldc, hipStream_t s);
 
 enum GemmEpilogue { kEpiProducts = 0, kEpiResidues = 1 };
+// ev_start / ev_stop (optional, both or neither): caller events the launch records its
+// start and end in (hipExtLaunchKernel), for timing the products inside a step.
 int launch_gemm_i8(int64_t m, int64_t n, int64_t kp, int r, const int8_t* pa, int64_t stride_a,
                    const int8_t* pb, int64_t stride_b, void* out, int64_t ldo, int64_t stride_o,
-                   int epilogue, hipStream_t s);
+                   int epilogue, hipStream_t s, hipEvent_t ev_start = nullptr,
+                   hipEvent_t ev_stop = nullptr);
 
 int launch_crt(int64_t m, int64_t n, int r, const void* res, int res_is_i32, int64_t ldr,
                int64_t stride_r, const int32_t* ea, const int32_t* eb, double* c, int64_t ldc,

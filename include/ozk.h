@@ -242,12 +242,13 @@ int ozk_int8gemm_fp4limb(int64_t m, int64_t n, int64_t k, const int8_t* A, int64
 int ozk_probe_mfma(int kind, const void* operands, int64_t operand_bytes, int64_t iters,
                    int workgroups, int32_t* sink, double* ops, void* stream);
 
-/* ozk_dgemm_ex_timed: ozk_dgemm_ex that also records the caller's two hipEvent_t handles
- *   (gemm_start, gemm_stop; both NULL or both valid events of the stream's device) on the
- *   stream immediately before and after the launch of the r residue products, so that a
- *   benchmark can time that kernel inside the steps it times.  Same arguments, result and
- *   errors as ozk_dgemm_ex; one of the two events NULL without the other: OZK_EINVAL; a
- *   failing hipEventRecord: OZK_EHIP.  The events stay owned by the caller. */
+/* ozk_dgemm_ex_timed: ozk_dgemm_ex that also has the launch of the r residue products
+ *   record its start and end in the caller's two hipEvent_t handles (gemm_start,
+ *   gemm_stop: both NULL or both events created with timing on the stream's device; the
+ *   launch records them itself, hipExtLaunchKernel, so no extra stream commands are
+ *   added), so that a benchmark can time that kernel inside the steps it times.  Same
+ *   arguments, result and errors as ozk_dgemm_ex; one of the two events NULL without the
+ *   other: OZK_EINVAL.  The events stay owned by the caller. */
 int ozk_dgemm_ex_timed(int64_t m, int64_t n, int64_t k, const double* A, int64_t lda,
                        const double* B, int64_t ldb, double* C, int64_t ldc, int r, int scaling,
                        void* workspace, size_t workspace_bytes, void* stream,
