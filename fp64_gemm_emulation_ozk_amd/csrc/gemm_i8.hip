@@ -417,14 +417,15 @@ __device__ __forceinline__ void store_residues_direct(
 // the last two pairs of a tile load the next tile's pairs 0 and 1 (all of pair 1 before
 // the epilogue), and its last quarter reads the next tile's first fragments, so the
 // epilogue (residues stored from registers) overlaps those loads, and the wait for pair
-// 1 after the next tile's first three quarters lets the epilogue's stores stay in flight.
+// 1 after the next tile's first three quarters lets the epilogue's stores stay in flight
+// (vector memory operations count down in issue order, so vmcnt(number of stores) covers
+// every load issued before them).
 // Tiles are dealt XCD by XCD (the hardware deals workgroups out round-robin over the 8
 // XCDs): the workgroups of one XCD take consecutive tiles of one contiguous share, in
 // groups of kGroupM tile rows, so the tiles in flight on an XCD share A rows and B columns
 // in its L2.
 constexpr int kPairRow = 128;                       // bytes per row of a pair stage
 constexpr int kPairBytes = (BM + BN) * kPairRow;    // 64 KiB
-static_assert(BM * kOutPitch <= 2 * kPairBytes, "residue staging within the pair ring");
 
 template <int kEpi, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
