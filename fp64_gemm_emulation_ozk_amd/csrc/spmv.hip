@@ -11,9 +11,11 @@
 // spmv_residues_kernel: one thread per row, the workgroup's entries staged in LDS by
 // coalesced loads.  The row's values are read twice (maximum, then residues), their
 // residues are formed in registers, multiplied by the gathered residues of x and summed
-// per modulus; the sums' symmetric residues go out as bytes [r][rows].  A row whose extent in row_ptr is not
-// inside [0, nnz], that is longer than kmax or that holds a column index outside
-// [0, cols) reads nothing through it and gets the exponent INT32_MIN (its y is NaN).
+// per modulus; the sums' symmetric residues go out as bytes [r][rows].  The row pass is
+// instantiated per r, its moduli's constants compile-time values.  A row whose extent in
+// row_ptr is not inside [0, nnz], that is longer than kmax or that holds a column index
+// outside [0, cols) reads nothing through it and gets the exponent INT32_MIN (its y is
+// NaN).
 #include <type_traits>
 
 #include "ozk_internal.h"
