@@ -315,3 +315,24 @@ def test_dgemm_largest_k(scaling):
         want = ozaki2.dgemm(a, b, r, exps=(e.cpu().numpy().astype(np.int64),
                                           f.cpu().numpy().astype(np.int64)))
     assert assert_within_ulps(got, want, 2) == 0
+
+
+def test_dgemm_timed_equals_untimed():
+    """ozk_dgemm_ex_timed: the same result as ozk_dgemm_ex, bit for bit, and its events
+    bracket the residue products (a positive time below the whole call's)."""
+    announce("dgemm timed entry point")
+    a, b = ozk_inputs.gemm_operands(600, 520, 700, seed=17, dist="phi", phi=2.0)
+    da, db = to_dev(a), to_dev(b)
+    plain = ozk.ozk_dgemm_ex(da, db, 16, "max")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record()
+    ev[0].record()
+    timed = ozk.ozk_dgemm_ex_timed(da, db, 16, ev[1], ev[2], "max")
+    ev[3].record()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(timed.cpu().numpy(), plain.cpu().numpy())
+    inner, outer = ev[1].elapsed_time(ev[2]), ev[0].elapsed_time(ev[3])
+    assert 0.0 < inner <= outer
+    want = ozaki2.dgemm(a, b, 16)
+    assert assert_within_ulps(timed.cpu().numpy(), want, 2) == 0
