@@ -88,10 +88,12 @@ __device__ __forceinline__ void pack32(const int8_t (&v)[32], const uint16_t* lu
 }
 
 // axis 0: x rows x cols (K = cols); thread -> (row, 32-value chunk).
+// vec: x and ldx are 16-byte aligned, so a whole 32-value chunk is two 16-byte loads.
 __global__ __launch_bounds__(256) void pack_rows_kernel(const int8_t* __restrict__ x,
                                                         int64_t rows, int64_t cols, int64_t ldx,
                                                         uint8_t* __restrict__ planes,
-                                                        int64_t ldpb, int64_t plane_stride) {
+                                                        int64_t ldpb, int64_t plane_stride,
+                                                        int vec) {
   __shared__ uint16_t lut[256];
   lut[threadIdx.x] = d_limbs.codes[threadIdx.x];
   __syncthreads();
@@ -102,8 +104,16 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const int8_t* __restrict
   const int64_t h0 = (g - row * chunks) * 32;
   const int8_t* src = x + row * ldx;
   int8_t v[32];
+  if (vec && h0 + 32 <= cols) {
+    const uint4 w0 = *reinterpret_cast<const uint4*>(src + h0);
+    const uint4 w1 = *reinterpret_cast<const uint4*>(src + h0 + 16);
+    const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-  for (int u = 0; u < 32; ++u) v[u] = h0 + u < cols ? src[h0 + u] : (int8_t)0;
+    for (int u = 0; u < 32; ++u) v[u] = (int8_t)(w[u >> 2] >> (8 * (u & 3)));
+  } else {
+#pragma unroll
+    for (int u = 0; u < 32; ++u) v[u] = h0 + u < cols ? src[h0 + u] : (int8_t)0;
+  }
   uint4 out[3];
   pack32(v, lut, out);
 #pragma unroll
@@ -374,8 +384,9 @@ int launch_fp4_pack(const int8_t* x, int64_t rows, int64_t cols, int64_t ldx, in
   if (axis == 0) {
     if (rows <= 0) return OZK_OK;
     const int64_t threads = rows * (ldpb / 16);
+    const int vec = (reinterpret_cast<uintptr_t>(x) % 16) == 0 && ldx % 16 == 0;
     hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                       x, rows, cols, ldx, planes, ldpb, plane_stride);
+                       x, rows, cols, ldx, planes, ldpb, plane_stride, vec);
   } else {
     if (cols <= 0) return OZK_OK;
     dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((2 * ldpb / 32 + 3) / 4));

@@ -20,7 +20,10 @@ def _kpad(k):
 
 
 @pytest.mark.parametrize("rows,cols,axis", [(37, 100, 0), (5, 64, 0), (100, 37, 1), (300, 130, 1),
-                                            (1, 1, 0), (1, 1, 1)])
+                                            (1, 1, 0), (1, 1, 1),
+                                            # 16-byte rows: whole chunks by vector loads,
+                                            # a ragged last chunk byte by byte
+                                            (9, 208, 0), (33, 512, 0)])
 def test_pack_bit_exact(rows, cols, axis):
     announce(f"fp4 pack rows={rows} cols={cols} axis={axis}")
     rng = np.random.default_rng(rows * 3 + cols)
