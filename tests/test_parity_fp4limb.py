@@ -23,7 +23,9 @@ def _kpad(k):
                                             (1, 1, 0), (1, 1, 1),
                                             # 16-byte rows: whole chunks by vector loads,
                                             # a ragged last chunk byte by byte
-                                            (9, 208, 0), (33, 512, 0)])
+                                            (9, 208, 0), (33, 512, 0),
+                                            # columns by 4-byte loads (rows a multiple of 4)
+                                            (70, 64, 1), (45, 260, 1)])
 def test_pack_bit_exact(rows, cols, axis):
     announce(f"fp4 pack rows={rows} cols={cols} axis={axis}")
     rng = np.random.default_rng(rows * 3 + cols)
