@@ -8,10 +8,12 @@
 //   a' = RNE(a 2^e)                    ldexp is exact here; rint rounds half to even
 //   narrow (|a'| <= 2^51):
 //     q   = RN(a' * RN(1/m) + 1.5*2^52) - 1.5*2^52     = round(a'/m)  (exact, below)
-//     rho = RN(-q*m + (a' + 1.5*2^52))                 = 1.5*2^52 + smod(a', m)
+//     rho = a' - q m                                   = smod(a', m)
 //   wide (|a'| <= 2^71):  a' = hi*2^32 + lo, lo in [0, 2^32)
 //     t   = hi * smod(2^32, m) + lo     (|t| < 2^47, congruent to a' mod m)
 //     then q and rho as above with t in place of a'.
+//   rho is wanted as a byte only, so it is formed modulo 2^32 from the low words of the
+//   magic-offset doubles (residue_byte).
 //
 // Exactness of q: for odd m <= 255 the true quotient t/m is never closer than 1/(2m)
 // >= 1/510 to a half-integer, while |t * RN(1/m) - t/m| <= |t|/m * 2^-53 <= 1/692 for
@@ -53,17 +55,24 @@ __device__ __forceinline__ Prepared prepare_element(double a, int e) {
 }
 
 // Low byte of smod(a', m) for an odd modulus m (inv = RN(1/m), c32 = smod(2^32, m)).
+// Only the byte is needed, so the residue is formed modulo 2^32 in integer arithmetic:
+// with q = round(t / m) (t = a' narrow, t = hi c32 + lo wide, |t| <= 2^51), the low words
+// of q + 1.5*2^52 and t + 1.5*2^52 are q and t modulo 2^32, and the low byte of
+// t - q m is that of their combination by one signed 24-bit multiply-add (only the low 24
+// bits of q matter modulo 2^8).  Narrow: one fp64 FMA and one integer operation per
+// modulus; wide: three fp64 operations (t + 1.5*2^52 exact by FMA, then t, then q).
 template <bool kWide>
 __device__ __forceinline__ uint32_t residue_byte(const Prepared& p, double m, double inv,
                                                  double c32) {
   constexpr double kMagicD = 6755399441055744.0;
+  const int neg_m = -(int)m;
   if (kWide) {
-    double t = __builtin_fma(p.hi, c32, p.v);
-    double q = __builtin_fma(t, inv, kMagicD) - kMagicD;
-    return lo32(__builtin_fma(-q, m, t) + kMagicD);
+    const double tm = __builtin_fma(p.hi, c32, p.vm);   // t + 1.5*2^52, exact
+    const double qm = __builtin_fma(tm - kMagicD, inv, kMagicD);
+    return (uint32_t)(__mul24((int)lo32(qm), neg_m) + (int)lo32(tm));
   } else {
-    double q = __builtin_fma(p.v, inv, kMagicD) - kMagicD;
-    return lo32(__builtin_fma(-q, m, p.vm));
+    const double qm = __builtin_fma(p.v, inv, kMagicD);
+    return (uint32_t)(__mul24((int)lo32(qm), neg_m) + (int)lo32(p.vm));
   }
 }
 
