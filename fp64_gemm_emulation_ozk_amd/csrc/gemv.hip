@@ -136,6 +136,7 @@ __global__ __launch_bounds__(256) void gemv_stored_kernel(
 // row (A) or column (B) lane & 15; the accumulator holds rows 4 (lane >> 4) .. +3 of
 // column lane & 15.
 typedef long v1l;
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 // Moduli and their residue constants at compile time (the kernel is instantiated per pass
 // of moduli L0 .. L0+NR-1), so no constant is loaded inside the loop.
 constexpr RnsTable kRns = make_rns_table();
@@ -232,6 +233,14 @@ __global__ __launch_bounds__(kFlyThreads, 1) void gemv_fly_kernel(
     Prepared p[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) p[u] = prepare_element<kWide>(cur[u], e);
+    // Narrow residues two elements at a time: the low 16 bits of a' (the same for every
+    // modulus) and of q = round(a' / m) of elements 2i, 2i+1 side by side, then one packed
+    // 16-bit multiply-add q (-m) + a' gives both residues modulo 2^16 (their low bytes are
+    // the residue bytes, as in residue_byte).
+    uint32_t vpair[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      vpair[i] = __builtin_amdgcn_perm(lo32(p[2 * i + 1].vm), lo32(p[2 * i].vm), 0x05040100u);
     for_moduli<0, NR>([&](auto qc) {
       constexpr int q = decltype(qc)::value;
       constexpr int l = l0 + q;
@@ -241,6 +250,21 @@ __global__ __launch_bounds__(kFlyThreads, 1) void gemv_fly_kernel(
                    residue_byte_256(p[3]));
         w1 = pack4(residue_byte_256(p[4]), residue_byte_256(p[5]), residue_byte_256(p[6]),
                    residue_byte_256(p[7]));
+      } else if constexpr (!kWide) {
+        constexpr double inv = kRns.inv[l];
+        constexpr uint16_t neg_m = (uint16_t)(0x10000 - kRns.moduli[l]);
+        constexpr double kMagicD = 6755399441055744.0;
+        uint32_t r2[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t qa = lo32(__builtin_fma(p[2 * i].v, inv, kMagicD));
+          const uint32_t qb = lo32(__builtin_fma(p[2 * i + 1].v, inv, kMagicD));
+          const u16x2 qp = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(qb, qa, 0x05040100u));
+          const u16x2 vp = __builtin_bit_cast(u16x2, vpair[i]);
+          r2[i] = __builtin_bit_cast(uint32_t, qp * u16x2{neg_m, neg_m} + vp);
+        }
+        w0 = __builtin_amdgcn_perm(r2[1], r2[0], 0x06040200u);
+        w1 = __builtin_amdgcn_perm(r2[3], r2[2], 0x06040200u);
       } else {
         constexpr double md = (double)kRns.moduli[l], inv = kRns.inv[l], c32 = kRns.c32[l];
         w0 = pack4(residue_byte<kWide>(p[0], md, inv, c32), residue_byte<kWide>(p[1], md, inv, c32),
