@@ -497,6 +497,7 @@ int launch_absmax(const double* x, int64_t rows, int64_t cols, int64_t ldx, int 
 int launch_residues(const double* x, int64_t rows, int64_t cols, int64_t ldx, int axis, int r,
                     int p_bits, const uint64_t* maxbits, int8_t* planes, int64_t ldp,
                     int64_t plane_stride, int32_t* exps, int given_exps, hipStream_t s) {
+  if (!residue_consts(r, p_bits)) return OZK_EINVAL;
   const ResidueConsts& K = *residue_consts(r, p_bits);
   const bool wide = K.wide != 0;
   if (axis == 0) {
@@ -536,6 +537,7 @@ int launch_deconstruct_pair(const double* a, int64_t m, int64_t k, int64_t lda, 
                             int64_t n, int64_t ldb, int r, int scaling, int width_a, int width_b,
                             const uint64_t* maxbits_b, int8_t* planes_a, int8_t* planes_b,
                             int64_t kp, int32_t* exps_a, int32_t* exps_b, hipStream_t s) {
+  if (!residue_consts(r, width_a) || !residue_consts(r, width_b)) return OZK_EINVAL;
   const ResidueConsts& ka = *residue_consts(r, width_a);
   const ResidueConsts& kb = *residue_consts(r, width_b);
   if (ka.wide != kb.wide || k > 8192 || m <= 0 || n <= 0) return OZK_EUNSUPPORTED;
@@ -614,6 +616,7 @@ int launch_residues_rows_fused(const double* x, int64_t rows, int64_t cols, int6
                                int scaling, int width, int8_t* planes, int64_t ldp,
                                int64_t plane_stride, int32_t* exps, hipStream_t s) {
   if (rows <= 0) return OZK_OK;
+  if (!residue_consts(r, width)) return OZK_EINVAL;
   const ResidueConsts& K = *residue_consts(r, width);
   const bool wide = K.wide != 0;
   const int norm = scaling == OZK_SCALING_NORM;

@@ -360,6 +360,7 @@ int launch_gemv_fly(const double* a, int64_t m, int64_t k, int64_t lda, const in
                     int r, int p_bits, const int8_t* xp, int64_t ldp, int64_t x_stride, int nrhs,
                     int8_t* res, hipStream_t s) {
   if (m <= 0) return OZK_OK;
+  if (!residue_consts(r, p_bits)) return OZK_EINVAL;
   const bool wide = residue_consts(r, p_bits)->wide;
   dim3 grid((unsigned)((m + kFlyRows - 1) / kFlyRows));
   // At most 16 moduli per pass (16 x 2 accumulator tiles = 128 registers); r > 16 takes two.

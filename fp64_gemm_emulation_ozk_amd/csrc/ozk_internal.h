@@ -43,7 +43,9 @@ struct CrtConsts {
 };
 
 // Host side (rns_host.cpp)
-constexpr int kNormAlphaCap = 76;  // norm rule: scaled integers stay below 2^77
+// Largest width of a scaled integer under either rule: |a'| <= 2^76 keeps the wide residue
+// arithmetic exact (|hi smod(2^32, m) + lo| <= 2^44 * 127 + 2^32 < 2^51).
+constexpr int kWidthCap = 76;
 int moduli_list(int r, int32_t* out);
 int scaling_bits(int r, int64_t k, int* pa, int* pb);
 // Norm rule widths (alpha_A, alpha_B): (2^aA + sqrt(k)/2)(2^aB + sqrt(k)/2) <= (M-1)/2.

@@ -9,14 +9,15 @@
 //   narrow (|a'| <= 2^51):
 //     q   = RN(a' * RN(1/m) + 1.5*2^52) - 1.5*2^52     = round(a'/m)  (exact, below)
 //     rho = a' - q m                                   = smod(a', m)
-//   wide (|a'| <= 2^71):  a' = hi*2^32 + lo, lo in [0, 2^32)
-//     t   = hi * smod(2^32, m) + lo     (|t| < 2^47, congruent to a' mod m)
+//   wide (|a'| <= 2^76):  a' = hi*2^32 + lo, lo in [0, 2^32), |hi| <= 2^44
+//     t   = hi * smod(2^32, m) + lo     (|t| <= 2^44 * 127 + 2^32 < 2^51, congruent to
+//                                        a' mod m; beyond 2^76 this bound fails)
 //     then q and rho as above with t in place of a'.
 //   rho is wanted as a byte only, so it is formed modulo 2^32 from the low words of the
 //   magic-offset doubles (residue_byte).
 //
 // Exactness of q: for odd m <= 255 the true quotient t/m is never closer than 1/(2m)
-// >= 1/510 to a half-integer, while |t * RN(1/m) - t/m| <= |t|/m * 2^-53 <= 1/692 for
+// to a half-integer, while |t * RN(1/m) - t/m| <= |t|/m * 2^-53 <= 1/(4m) < 1/(2m) for
 // |t| <= 2^51; so the rounding picks round(t/m) and rho = t - m round(t/m) is the
 // symmetric residue in [-(m-1)/2, (m-1)/2].  For m = 256 the residue is the low byte
 // of a' in two's complement, i.e. smod(a', 256) in [-128, 127].  Adding 1.5*2^52 to an

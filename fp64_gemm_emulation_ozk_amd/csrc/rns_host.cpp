@@ -27,8 +27,10 @@ int scaling_bits(int r, int64_t k, int* pa, int* pb) {
   while ((int64_t(1) << ceil_log2) < k) ++ceil_log2;
   const int beta = kRns.q[r] - ceil_log2;
   if (beta < 2) return OZK_ERANGE;
-  if (pa) *pa = beta / 2;
-  if (pb) *pb = beta - beta / 2;
+  // Each width is capped at kWidthCap: it binds only for r = 20 with k <= 2.
+  const int a = beta / 2, b = beta - beta / 2;
+  if (pa) *pa = a < kWidthCap ? a : kWidthCap;
+  if (pb) *pb = b < kWidthCap ? b : kWidthCap;
   return OZK_OK;
 }
 
@@ -104,8 +106,8 @@ int scaling_bits_norm(int r, int64_t k, int* pa, int* pb) {
   const W192 two_m1 = w192_mul_small(m, 2);
   const uint64_t t = isqrt_u64((uint64_t)k - 1) + 1;
   const int q = kRns.q[r];
-  int aa = (q - 1) / 2 < kNormAlphaCap ? (q - 1) / 2 : kNormAlphaCap;
-  int ab = q - 1 - (q - 1) / 2 < kNormAlphaCap ? q - 1 - (q - 1) / 2 : kNormAlphaCap;
+  int aa = (q - 1) / 2 < kWidthCap ? (q - 1) / 2 : kWidthCap;
+  int ab = q - 1 - (q - 1) / 2 < kWidthCap ? q - 1 - (q - 1) / 2 : kWidthCap;
   while (!w192_le(w192_mul(w192_pow2_plus(aa + 1, t), w192_pow2_plus(ab + 1, t)), two_m1)) {
     if (aa >= ab)
       --aa;
@@ -126,7 +128,9 @@ int scaling_widths(int scaling, int r, int64_t k, int* wa, int* wb) {
 
 const ResidueConsts* residue_consts(int r, int p_bits) {
   // p_bits selects whether scaled integers may exceed 2^51, the range where the
-  // x + 1.5*2^52 rounding and the fp64 quotient are exact (the "wide" split path).
+  // x + 1.5*2^52 rounding and the fp64 quotient are exact (the "wide" split path, exact
+  // up to 2^76 = kWidthCap bits).  Widths come from scaling_widths, which never exceeds
+  // the cap; a larger p_bits is refused.
   static ResidueConsts table[kMaxModuli + 1][2];
   static std::once_flag once;
   std::call_once(once, [] {
@@ -144,7 +148,7 @@ const ResidueConsts* residue_consts(int r, int p_bits) {
       }
     }
   });
-  if (r < 1 || r > kMaxModuli) return nullptr;
+  if (r < 1 || r > kMaxModuli || p_bits > kWidthCap) return nullptr;
   return &table[r][p_bits > 51 ? 1 : 0];
 }
 

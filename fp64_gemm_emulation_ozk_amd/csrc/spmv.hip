@@ -238,6 +238,7 @@ int launch_spmv(int64_t rows, int64_t cols, int64_t nnz, const int32_t* row_ptr,
                 int r, int p_a, int p_b, uint64_t* x_partial, int32_t* x_exp, int8_t* xres,
                 int8_t* res, int32_t* exps, hipStream_t s) {
   if (rows <= 0) return OZK_OK;
+  if (!residue_consts(r, p_b) || !residue_consts(r, p_a)) return OZK_EINVAL;
   const int64_t chunks = (cols + 2047) / 2048;
   hipLaunchKernelGGL(vec_absmax_kernel, dim3((unsigned)chunks), dim3(256), 0, s, x, cols,
                      x_partial);

@@ -196,18 +196,14 @@ def round_scaled(x: int, s: int) -> float:
 
 
 def crt_integers(products: np.ndarray, r: int) -> np.ndarray:
-    """CRT lift of each output's r modular products: object array of Python ints."""
-    big_m, basis = rns.crt_basis(r)
-    ms = rns.moduli(r)
-    acc = np.zeros(products.shape[1:], dtype=object)
-    for l, m in enumerate(ms):
-        acc = acc + basis[l] * (np.asarray(products[l]) % m).astype(object)
-    half = (big_m - 1) // 2
-    flat = acc.reshape(-1)
-    for idx in range(flat.size):
-        v = flat[idx] % big_m
-        flat[idx] = v - big_m if v > half else v
-    return flat.reshape(acc.shape)
+    """CRT lift of each output's r modular products (``rns.crt_lift`` per output): object
+    array of Python ints."""
+    prods = np.asarray(products)
+    flat = prods.reshape(r, -1)
+    out = np.empty(flat.shape[1], dtype=object)
+    for idx in range(flat.shape[1]):
+        out[idx] = rns.crt_lift([int(v) for v in flat[:, idx]], r)
+    return out.reshape(prods.shape[1:])
 
 
 def reconstruct(products: np.ndarray, r: int, e: np.ndarray, f: np.ndarray) -> np.ndarray:

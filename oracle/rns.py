@@ -14,15 +14,19 @@ name neither the moduli nor the reconstruction formula.  Readings taken here:
 * Reconstruction: the Chinese Remainder Theorem, X = sum_l E_l c_l mod M with
   E_l = (M/m_l) * ((M/m_l)^-1 mod m_l), lifted to the symmetric range.
 * Bit budget: Q = floor(log2((M-1)/2)), beta = Q - ceil(log2 k), P_A = floor(beta/2),
-  P_B = beta - P_A.  With |a'| <= 2^P_A and |b'| <= 2^P_B every exact dot product of
-  length k satisfies sum |a'||b'| <= 2^Q <= (M-1)/2, so the CRT lift recovers it exactly.
+  P_B = beta - P_A, each capped at WIDTH_CAP = 76.  With |a'| <= 2^P_A and |b'| <= 2^P_B
+  every exact dot product of length k satisfies sum |a'||b'| <= 2^Q <= (M-1)/2, so the
+  CRT lift recovers it exactly.  The cap only binds at r = 20 with k <= 2 (beta 153 or
+  154); there a dot product of one or two terms still carries 76 bits per operand, far
+  more than the 53 its fp64 result keeps, and every scaled integer stays at or below
+  2^76, the range the norm rule already keeps to.
 * Norm budget (the tighter row/column scaling): widths (alpha_A, alpha_B) for scaled
   rows and columns whose 2-norms stay below 2^alpha_A and 2^alpha_B; rounding each of
   the k entries moves a 2-norm by at most sqrt(k)/2, so by Cauchy-Schwarz
   sum |a'||b'| < (2^alpha_A + sqrt(k)/2)(2^alpha_B + sqrt(k)/2), which is kept at or
-  below (M-1)/2.  alpha_A + alpha_B starts at Q - 1, each at most 76 (scaled integers
-  then stay below 2^77, as they do under the max rule for r = 20 and k = 1), and the
-  larger is lowered until the inequality holds exactly.
+  below (M-1)/2.  alpha_A + alpha_B starts at Q - 1, each at most WIDTH_CAP = 76 (scaled
+  integers then stay at or below 2^76, as under the max rule), and the larger is lowered
+  until the inequality holds exactly.
 """
 from __future__ import annotations
 
@@ -83,16 +87,17 @@ def ceil_log2(k: int) -> int:
     return (k - 1).bit_length()
 
 
+WIDTH_CAP = 76
+NORM_ALPHA_CAP = WIDTH_CAP
+
+
 def scaling_bits(r: int, k: int) -> tuple[int, int]:
     """(P_A, P_B): the integer widths the scaled operands of A and B may use."""
     beta = budget_q(r) - ceil_log2(k)
     if beta < 2:
         raise ValueError(f"r={r} gives no bit budget for k={k}")
     pa = beta // 2
-    return pa, beta - pa
-
-
-NORM_ALPHA_CAP = 76
+    return min(pa, WIDTH_CAP), min(beta - pa, WIDTH_CAP)
 
 
 def norm_bound_holds(alpha_a: int, alpha_b: int, k: int, big_m: int) -> bool:

@@ -86,7 +86,26 @@ def test_scaling_bits_guarantee_exact_crt(r, k):
     assert k * 2 ** (pa + pb) <= (big_m - 1) // 2
     kk = 1 << rns.ceil_log2(k)
     assert kk >= k and (kk == 1 or kk // 2 < k)
-    assert kk * 2 ** (pa + pb + 1) > 2 ** rns.budget_q(r)
+    if pb < rns.WIDTH_CAP:
+        assert kk * 2 ** (pa + pb + 1) > 2 ** rns.budget_q(r)
+
+
+@pytest.mark.parametrize("r", range(1, 21))
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 64])
+def test_scaling_bits_capped_at_76(r, k):
+    """Every width stays at or below 76 bits; the cap binds only at r = 20 with k <= 2,
+    where beta = Q - ceil(log2 k) is 154 or 153 (widths (76, 76) instead of (77, 77) and
+    (76, 77)); everywhere else the widths are floor(beta/2) and beta - floor(beta/2)."""
+    try:
+        pa, pb = rns.scaling_bits(r, k)
+    except ValueError:
+        return
+    beta = rns.budget_q(r) - rns.ceil_log2(k)
+    assert max(pa, pb) <= 76
+    if r == 20 and k <= 2:
+        assert (pa, pb) == (76, 76) and beta in (153, 154)
+    else:
+        assert (pa, pb) == (beta // 2, beta - beta // 2)
 
 
 def test_scaling_bits_no_budget():

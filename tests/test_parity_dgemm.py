@@ -240,7 +240,7 @@ def test_dgemm_deterministic():
     assert torch.equal(c1.view(torch.int64), c2.view(torch.int64))
 
 
-@pytest.mark.parametrize("r", [12, 16, 18])
+@pytest.mark.parametrize("r", list(range(12, 19)))
 def test_dgemm_square_4096_sampled(r):
     """The 4096^3 configuration, entries (U-0.5) exp(0.5 N), sampled outputs vs oracle."""
     announce(f"dgemm 4096^3 r={r} sampled")

@@ -51,7 +51,7 @@ def _run(cfg, r: int, rule: str) -> np.ndarray:
     return _sample(cfg, cfg["out"])
 
 
-@pytest.mark.parametrize("r", [16, 18, 20])
+@pytest.mark.parametrize("r", [16, 17, 18, 19, 20])
 def test_wide_range_max_rule_matches_oracle(cfg, r):
     announce(f"wide range 8192^3 max rule r={r}")
     got = _run(cfg, r, "max")
@@ -59,7 +59,7 @@ def test_wide_range_max_rule_matches_oracle(cfg, r):
     assert assert_within_ulps(got, want, 2) == 0
 
 
-@pytest.mark.parametrize("r", [16, 20])
+@pytest.mark.parametrize("r", [16, 17, 18, 19, 20])
 def test_wide_range_norm_rule_matches_oracle(cfg, r):
     announce(f"wide range 8192^3 norm rule r={r}")
     got = _run(cfg, r, "norm")
