@@ -3,7 +3,8 @@ GEMM for MI355X).
 
 Argument marshalling only: each ``ozk_*`` function here checks tensor devices, dtypes and
 strides, allocates outputs and workspace with torch (device memory), and calls the C
-entry point of the same name on torch's current HIP stream.  Every step of the
+entry point of the same name on the given stream (torch's current HIP stream by
+default).  Every step of the
 computation runs in the library's HIP kernels; there is no other code path.  If the
 library is not built, loading fails with an error.
 """
@@ -25,7 +26,6 @@ __all__ = [
     "ozk_fp4limb_pack", "ozk_fp4limb_products", "ozk_int8gemm_fp4limb",
     "ozk_dgemm_workspace_size", "ozk_dgemv_workspace_size",
     "ozk_int8gemm_fp4limb_workspace_size", "ozk_deconstruct_workspace_size",
-    "ozk_probe_mfma",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libozk.so")
@@ -73,7 +73,6 @@ _SIGNATURES = {
     "ozk_int8gemm_fp4limb_workspace_size": (_int, [_i64, _i64, _i64, _ptr]),
     "ozk_int8gemm_fp4limb": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr,
                                     _size, _ptr]),
-    "ozk_probe_mfma": (_int, [_int, _ptr, _i64, _i64, _int, _ptr, _ptr, _ptr]),
 }
 
 _LIB = None
@@ -121,9 +120,17 @@ def _call(name: str, *args) -> int:
     return st
 
 
-def _stream(stream=None):
+def _stream(stream=None, *tensors):
+    """The hipStream_t handle of `stream` (torch's current stream when None).  Tensors this
+    binding allocated (outputs, workspace) come from torch's caching allocator on the
+    current stream; when the work goes to another stream they are marked as used there,
+    so that their memory is not handed out again before that stream's work ends."""
     if stream is None:
         stream = torch.cuda.current_stream()
+    elif stream != torch.cuda.current_stream():
+        for t in tensors:
+            if t is not None:
+                t.record_stream(stream)
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -220,7 +227,8 @@ def _deconstruct(name: str, extra: tuple, x: torch.Tensor, axis: int, r: int,
     _call(name, _dev_ptr(x), rows, cols, _ld(x), axis, r,
           k_budget if k_budget is not None else kdim, *extra, _dev_ptr(planes),
           planes.shape[-1], planes.stride(0), _dev_ptr(exps), _dev_ptr(workspace),
-          0 if workspace is None else workspace.numel(), _stream(stream))
+          0 if workspace is None else workspace.numel(),
+          _stream(stream, planes, exps, workspace))
     return planes, exps
 
 
@@ -253,7 +261,7 @@ def ozk_modular_products(planes_a: torch.Tensor, planes_b: torch.Tensor, r: int 
         out = torch.empty((r, m, n), dtype=torch.int32, device=planes_a.device)
     _call("ozk_modular_products", m, n, kp, r, _dev_ptr(planes_a), planes_a.stride(0),
           _dev_ptr(planes_b), planes_b.stride(0), _dev_ptr(out), out.stride(1), out.stride(0),
-          _stream(stream))
+          _stream(stream, out))
     return out
 
 
@@ -269,7 +277,7 @@ def ozk_modular_residues(planes_a: torch.Tensor, planes_b: torch.Tensor, r: int 
         out = torch.empty((r, m, n), dtype=torch.int8, device=planes_a.device)
     _call("ozk_modular_residues", m, n, kp, r, _dev_ptr(planes_a), planes_a.stride(0),
           _dev_ptr(planes_b), planes_b.stride(0), _dev_ptr(out), out.stride(1), out.stride(0),
-          _stream(stream))
+          _stream(stream, out))
     return out
 
 
@@ -285,7 +293,7 @@ def ozk_reconstruct(products: torch.Tensor, exps_a: torch.Tensor, exps_b: torch.
     if out is None:
         out = torch.empty((m, n), dtype=torch.float64, device=products.device)
     _call("ozk_reconstruct", m, n, r, _dev_ptr(products), products.stride(1), products.stride(0),
-          _dev_ptr(exps_a), _dev_ptr(exps_b), _dev_ptr(out), _ld(out), _stream(stream))
+          _dev_ptr(exps_a), _dev_ptr(exps_b), _dev_ptr(out), _ld(out), _stream(stream, out))
     return out
 
 
@@ -308,7 +316,7 @@ def ozk_dgemm(a: torch.Tensor, b: torch.Tensor, r: int, out: torch.Tensor | None
     """Emulated fp64 C = A B through r moduli."""
     m, n, k, out, workspace = _dgemm_args(a, b, r, out, workspace)
     _call("ozk_dgemm", m, n, k, _dev_ptr(a), _ld(a), _dev_ptr(b), _ld(b), _dev_ptr(out), _ld(out),
-          r, _dev_ptr(workspace), workspace.numel(), _stream(stream))
+          r, _dev_ptr(workspace), workspace.numel(), _stream(stream, out, workspace))
     return out
 
 
@@ -319,7 +327,7 @@ def ozk_dgemm_ex(a: torch.Tensor, b: torch.Tensor, r: int, scaling="max",
     m, n, k, out, workspace = _dgemm_args(a, b, r, out, workspace)
     _call("ozk_dgemm_ex", m, n, k, _dev_ptr(a), _ld(a), _dev_ptr(b), _ld(b), _dev_ptr(out),
           _ld(out), r, _scaling(scaling), _dev_ptr(workspace), workspace.numel(),
-          _stream(stream))
+          _stream(stream, out, workspace))
     return out
 
 
@@ -331,7 +339,7 @@ def ozk_dgemm_ex_timed(a: torch.Tensor, b: torch.Tensor, r: int, gemm_start, gem
     m, n, k, out, workspace = _dgemm_args(a, b, r, out, workspace)
     _call("ozk_dgemm_ex_timed", m, n, k, _dev_ptr(a), _ld(a), _dev_ptr(b), _ld(b),
           _dev_ptr(out), _ld(out), r, _scaling(scaling), _dev_ptr(workspace), workspace.numel(),
-          _stream(stream), gemm_start.cuda_event, gemm_stop.cuda_event)
+          _stream(stream, out, workspace), gemm_start.cuda_event, gemm_stop.cuda_event)
     return out
 
 
@@ -358,7 +366,7 @@ def ozk_dgemv(a: torch.Tensor | None, x: torch.Tensor, r: int, mode: int = 0,
     _call("ozk_dgemv", m, k, nrhs, _dev_ptr(a), _ld(a) if a is not None else k,
           _dev_ptr(a_planes), ldp, pstride, _dev_ptr(a_exps), _dev_ptr(x), _ld(x),
           _dev_ptr(out), _ld(out), r, mode, _dev_ptr(workspace), workspace.numel(),
-          _stream(stream))
+          _stream(stream, out, workspace))
     return out
 
 
@@ -388,7 +396,7 @@ def ozk_spmv_csr(row_ptr: torch.Tensor, col_idx: torch.Tensor, vals: torch.Tenso
         workspace = _workspace(ozk_spmv_csr_workspace_size(rows, cols, r), x.device)
     _call("ozk_spmv_csr", rows, cols, nnz, _dev_ptr(row_ptr), _dev_ptr(col_idx), _dev_ptr(vals),
           max_row_nnz, _dev_ptr(x), _dev_ptr(out), r, _dev_ptr(workspace), workspace.numel(),
-          _stream(stream))
+          _stream(stream, out, workspace))
     return out
 
 
@@ -403,7 +411,7 @@ def ozk_fp4limb_pack(x: torch.Tensor, axis: int, planes: torch.Tensor | None = N
     if planes is None:
         planes = torch.empty((3, lines, ldpb), dtype=torch.uint8, device=x.device)
     _call("ozk_fp4limb_pack", _dev_ptr(x), rows, cols, _ld(x), axis, _dev_ptr(planes),
-          planes.shape[-1], planes.stride(0), _stream(stream))
+          planes.shape[-1], planes.stride(0), _stream(stream, planes))
     return planes
 
 
@@ -418,7 +426,7 @@ def ozk_fp4limb_products(planes_a: torch.Tensor, planes_b: torch.Tensor,
         out = torch.empty((9, m, n), dtype=torch.int32, device=planes_a.device)
     _call("ozk_fp4limb_products", m, n, ldpb, _dev_ptr(planes_a), planes_a.stride(0),
           _dev_ptr(planes_b), planes_b.stride(0), _dev_ptr(out), out.stride(1), out.stride(0),
-          _stream(stream))
+          _stream(stream, out))
     return out
 
 
@@ -434,22 +442,6 @@ def ozk_int8gemm_fp4limb(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | N
     if workspace is None:
         workspace = _workspace(ozk_int8gemm_fp4limb_workspace_size(m, n, k), a.device)
     _call("ozk_int8gemm_fp4limb", m, n, k, _dev_ptr(a), _ld(a), _dev_ptr(b), _ld(b),
-          _dev_ptr(out), _ld(out), _dev_ptr(workspace), workspace.numel(), _stream(stream))
+          _dev_ptr(out), _ld(out), _dev_ptr(workspace), workspace.numel(),
+          _stream(stream, out, workspace))
     return out
-
-
-# ----------------------------------------------------------------------- measurement
-def ozk_probe_mfma(kind: int, operands: torch.Tensor, iters: int, workgroups: int,
-                   sink: torch.Tensor | None = None, stream=None) -> float:
-    """Enqueue the register-only matrix-core loop (kind 0: int8 32x32x32, kind 1: e2m1
-    32x32x64) over the bytes of `operands`; returns the operation count of the launch."""
-    if not isinstance(operands, torch.Tensor) or not operands.is_cuda or not operands.is_contiguous():
-        raise TypeError("operands must be a contiguous CUDA/HIP tensor")
-    if sink is None:
-        sink = torch.empty(workgroups * 512, dtype=torch.int32, device=operands.device)
-    if sink.dtype != torch.int32 or sink.numel() < workgroups * 512:
-        raise ValueError("sink must hold workgroups * 512 int32 values")
-    ops = ctypes.c_double(0.0)
-    _call("ozk_probe_mfma", kind, _dev_ptr(operands), operands.numel() * operands.element_size(),
-          iters, workgroups, _dev_ptr(sink), ctypes.byref(ops), _stream(stream))
-    return ops.value

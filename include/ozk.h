@@ -31,8 +31,9 @@
  *    199, 197, 193, 191, 181, 179, 173); 1 <= r <= 20.
  *  - Scaling: a power of two per row of A and per column of B/X by the max rule
  *    e = P - 1 - ilogb(max |x|) (0 for an all-zero line), with bit budgets
- *    P_A = floor(beta/2), P_B = beta - P_A, beta = floor(log2((M-1)/2)) - ceil(log2 k),
- *    M the product of the moduli.  Scaled integers are rounded half to even.
+ *    P_A = min(floor(beta/2), 76), P_B = min(beta - floor(beta/2), 76),
+ *    beta = floor(log2((M-1)/2)) - ceil(log2 k), M the product of the moduli.  Scaled
+ *    integers are rounded half to even and stay within 2^76 in magnitude.
  *  - Residues are symmetric: smod(x, m) in [-floor(m/2), ceil(m/2) - 1] (int8).
  *  - A line (row or column) holding Inf or NaN gets the exponent INT32_MIN, all-zero
  *    residues, and NaN in every output it touches.
@@ -72,13 +73,18 @@ const char* ozk_status_string(int status);
 int ozk_moduli(int r, int32_t* out);
 
 /* Bit budgets (P_A, P_B) of the scaling for r moduli and inner dimension k (host
- * outputs).  OZK_ERANGE when beta < 2 or k > OZK_MAX_K. */
+ * outputs): the widths of the scaled, rounded integers of [TME4] abstract ("scaled,
+ * rounded, and reduced modulo each of the r moduli"), chosen so that every dot product
+ * of length k stays inside the range the r moduli determine exactly.  The pages fix no
+ * rule; this is the max rule of the conventions above.  pa/pb may be NULL.  OZK_EINVAL
+ * for r outside [1, 20] or k < 1; OZK_ERANGE when beta < 2 or k > OZK_MAX_K. */
 int ozk_scaling_bits(int r, int64_t k, int32_t* pa, int32_t* pb);
 
-/* Widths of either scaling rule (host outputs): OZK_SCALING_MAX gives (P_A, P_B) as
- * above; OZK_SCALING_NORM gives (alpha_A, alpha_B), the largest widths (alpha_A +
- * alpha_B <= Q - 1, each <= 76) with (2^aA + sqrt(k)/2)(2^aB + sqrt(k)/2) <= (M-1)/2,
- * checked in exact integer arithmetic.  OZK_EINVAL for an unknown rule. */
+/* Widths of either scaling rule (host outputs), the budget of the scaling step of
+ * [TME4] abstract: OZK_SCALING_MAX gives (P_A, P_B) as above; OZK_SCALING_NORM gives
+ * (alpha_A, alpha_B), the largest widths (alpha_A + alpha_B <= Q - 1, each <= 76) with
+ * (2^aA + sqrt(k)/2)(2^aB + sqrt(k)/2) <= (M-1)/2, checked in exact integer arithmetic.
+ * OZK_EINVAL for an unknown rule; otherwise the errors of ozk_scaling_bits. */
 int ozk_scaling_bits_ex(int r, int64_t k, int scaling, int32_t* pa, int32_t* pb);
 
 /* Leading dimension used for planes over an inner dimension k: round_up(k, 64). */
@@ -123,7 +129,11 @@ int ozk_deconstruct_ex(const double* x, int64_t rows, int64_t cols, int64_t ldx,
  *     products[l*stride_p + i*ldp_out + j] = sum_{h < kp} pa[l*stride_a + i*kp + h]
  *                                                       * pb[l*stride_b + j*kp + h]
  * exactly in int32 (int8 planes as written by ozk_deconstruct; kp a multiple of 64,
- * kp <= OZK_MAX_K rounded up).  m x n outputs per modulus; ldp_out >= n. */
+ * kp <= OZK_MAX_K rounded up, i.e. at most 131072).  Exact while every sum fits int32,
+ * which planes from ozk_deconstruct (at most 131071 live K positions, the padding zero)
+ * always do; caller-made planes with kp = 131072 must keep one K position zero in A or
+ * B, or a line of 131072 terms (-128)(-128) = 2^31 wraps.  m x n outputs per modulus;
+ * ldp_out >= n. */
 int ozk_modular_products(int64_t m, int64_t n, int64_t kp, int r, const int8_t* pa,
                          int64_t stride_a, const int8_t* pb, int64_t stride_b,
                          int32_t* products, int64_t ldp_out, int64_t stride_p, void* stream);
@@ -149,10 +159,17 @@ int ozk_reconstruct(int64_t m, int64_t n, int r, const int32_t* products, int64_
                     double* C, int64_t ldc, void* stream);
 
 /* ---------------------------------------------------------------- emulated DGEMM
+ * [TME4] abstract (Ozaki scheme II: deconstruction, one integer product per modulus,
+ * per-output reconstruction); [AWE] abstract (each product an error-free integer matrix
+ * product times a scale factor).
  * C = A B (m x n, A m x k, B k x n, no alpha/beta) through r moduli: deconstruction
  * of A (rows) and B (columns), r int8 MFMA products with the residue epilogue, CRT
  * reconstruction.  The result equals RN(2^-(e_i+f_j) sum_h a'_ih b'_hj) with the
- * sum exact.  m, n >= 0; 1 <= k <= OZK_MAX_K; lda >= k, ldb >= n, ldc >= n. */
+ * sum exact.  m, n >= 0; 1 <= k <= OZK_MAX_K; lda >= k, ldb >= n, ldc >= n.  The
+ * workspace (device, 256-byte aligned, at least ozk_dgemm_workspace_size bytes) holds
+ * the residue planes of A and B, the product residues and the exponents; its contents
+ * are scratch on return.  OZK_EWORKSPACE when it is missing or short; nothing is
+ * enqueued on any error. */
 int ozk_dgemm_workspace_size(int64_t m, int64_t n, int64_t k, int r, size_t* bytes);
 int ozk_dgemm(int64_t m, int64_t n, int64_t k, const double* A, int64_t lda,
               const double* B, int64_t ldb, double* C, int64_t ldc, int r,
@@ -227,22 +244,7 @@ int ozk_int8gemm_fp4limb(int64_t m, int64_t n, int64_t k, const int8_t* A, int64
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- measurement support
- * ozk_probe_mfma: enqueue a register-only loop of matrix-core instructions with the
- *   caller's operand bytes, to measure the sustained rate this GPU reaches on data like
- *   the products' (the matrix cores draw data-dependent power; random operands hold
- *   the board at its power cap below the datasheet clock).  kind 0: int8
- *   v_mfma_i32_32x32x32_i8 (65536 ops each); kind 1: e2m1 x e2m1
- *   v_mfma_scale_f32_32x32x64_f8f6f4 (131072 ops each).  `operands`: device memory,
- *   16-byte aligned, operand_bytes >= 16 (random bytes give the representative rate;
- *   each wave reads 16 KiB of it, wrapping around).  `sink`: device int32 array of
- *   workgroups * 512 entries, overwritten.  `ops` (host, may be NULL) receives the
- *   operation count of the launch, to be divided by the caller's measured time.
- *   Launches `workgroups` workgroups of 512 threads, each running `iters` iterations of
- *   32 instructions per wave. */
-int ozk_probe_mfma(int kind, const void* operands, int64_t operand_bytes, int64_t iters,
-                   int workgroups, int32_t* sink, double* ops, void* stream);
-
-/* ozk_dgemm_ex_timed: ozk_dgemm_ex that also has the launch of the r residue products
+ * ozk_dgemm_ex_timed: ozk_dgemm_ex that also has the launch of the r residue products
  *   record its start and end in the caller's two hipEvent_t handles (gemm_start,
  *   gemm_stop: both NULL or both events created with timing on the stream's device; the
  *   launch records them itself, hipExtLaunchKernel, so no extra stream commands are
