@@ -20,6 +20,7 @@ __all__ = [
     "ozk_version", "ozk_moduli", "ozk_scaling_bits", "ozk_scaling_bits_ex", "ozk_planes_ld",
     "ozk_deconstruct", "ozk_deconstruct_ex", "ozk_modular_products", "ozk_modular_residues",
     "ozk_reconstruct", "ozk_dgemm", "ozk_dgemm_ex", "ozk_dgemm_ex_timed", "ozk_dgemv",
+    "ozk_dgemv_noalloc", "OZK_NOALLOC_SCRATCH_BYTES",
     "ozk_spmv_csr",
     "ozk_spmv_csr_workspace_size",
     "OZK_SCALING_MAX", "OZK_SCALING_NORM",
@@ -30,6 +31,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libozk.so")
 OZK_PLANE_K = 64
+OZK_NOALLOC_SCRATCH_BYTES = 64 << 20   # scratch array of ozk_dgemv_noalloc, per GPU
 
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -67,6 +69,8 @@ _SIGNATURES = {
     "ozk_dgemv_workspace_size": (_int, [_i64, _i64, _i64, _int, _int, _ptr]),
     "ozk_dgemv": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _ptr, _ptr, _i64, _ptr,
                          _i64, _int, _int, _ptr, _size, _ptr]),
+    "ozk_dgemv_noalloc": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _ptr, _ptr, _i64,
+                                 _ptr, _i64, _int, _int, _ptr]),
     "ozk_fp4limb_pack": (_int, [_ptr, _i64, _i64, _i64, _int, _ptr, _i64, _i64, _ptr]),
     "ozk_fp4limb_products": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _i64,
                                     _ptr]),
@@ -367,6 +371,32 @@ def ozk_dgemv(a: torch.Tensor | None, x: torch.Tensor, r: int, mode: int = 0,
           _dev_ptr(a_planes), ldp, pstride, _dev_ptr(a_exps), _dev_ptr(x), _ld(x),
           _dev_ptr(out), _ld(out), r, mode, _dev_ptr(workspace), workspace.numel(),
           _stream(stream, out, workspace))
+    return out
+
+
+def ozk_dgemv_noalloc(a: torch.Tensor | None, x: torch.Tensor, r: int, mode: int = 0,
+                      a_planes: torch.Tensor | None = None, a_exps: torch.Tensor | None = None,
+                      out: torch.Tensor | None = None, m: int | None = None,
+                      stream=None) -> torch.Tensor:
+    """ozk_dgemv through the allocation-free entry point: the library's fixed scratch
+    array (OZK_NOALLOC_SCRATCH_BYTES per GPU) instead of a workspace.  With `out` given
+    nothing is allocated at all; calls that overlap in time on one GPU race."""
+    _check(x, torch.float64, "X")
+    k, nrhs = x.shape
+    if a is not None:
+        _check(a, torch.float64, "A")
+        m = a.shape[0]
+    elif a_planes is not None:
+        m = a_planes.shape[1]
+    if m is None:
+        raise ValueError("m unknown")
+    if out is None:
+        out = torch.empty((m, nrhs), dtype=torch.float64, device=x.device)
+    ldp = a_planes.shape[-1] if a_planes is not None else 0
+    pstride = a_planes.stride(0) if a_planes is not None else 0
+    _call("ozk_dgemv_noalloc", m, k, nrhs, _dev_ptr(a), _ld(a) if a is not None else k,
+          _dev_ptr(a_planes), ldp, pstride, _dev_ptr(a_exps), _dev_ptr(x), _ld(x),
+          _dev_ptr(out), _ld(out), r, mode, _stream(stream, out))
     return out
 
 

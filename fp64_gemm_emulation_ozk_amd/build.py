@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libozk.so")
 
 ARCH = "gfx950"
 DEVICE_SOURCES = ["deconstruct.hip", "gemm_i8.hip", "crt.hip", "gemv.hip", "gemv_digits.hip",
-                  "fp4limb.hip", "spmv.hip"]
+                  "fp4limb.hip", "spmv.hip", "noalloc.hip"]
 HOST_SOURCES = ["rns_host.cpp", "api.cpp"]
 
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

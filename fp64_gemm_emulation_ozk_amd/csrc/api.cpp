@@ -151,6 +151,8 @@ const char* ozk_status_string(int status) {
     case OZK_ERANGE: return "inner dimension out of range for exact products or the bit budget";
     case OZK_EHIP: return "HIP launch failed";
     case OZK_EUNSUPPORTED: return "unsupported request";
+    case OZK_ENOSCRATCH:
+      return "request needs more scratch than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }
@@ -364,10 +366,14 @@ int ozk_dgemv_workspace_size(int64_t m, int64_t k, int64_t nrhs, int r, int mode
   return OZK_OK;
 }
 
-int ozk_dgemv(int64_t m, int64_t k, int64_t nrhs, const double* A, int64_t lda,
-              const int8_t* A_planes, int64_t ldp, int64_t plane_stride, const int32_t* A_exps,
-              const double* X, int64_t ldx, double* Y, int64_t ldy, int r, int mode,
-              void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace ozk {
+
+int dgemv_validate(int64_t m, int64_t k, int64_t nrhs, const double* A, int64_t lda,
+                   const int8_t* A_planes, int64_t ldp, int64_t plane_stride,
+                   const int32_t* A_exps, const double* X, int64_t ldx, const double* Y,
+                   int64_t ldy, int r, int mode) {
   if (check_r(r) != OZK_OK || (mode != 0 && mode != 1)) return OZK_EINVAL;
   if (m < 0 || k < 1 || nrhs < 1 || nrhs > 32) return OZK_EINVAL;
   if (k > OZK_MAX_K) return OZK_ERANGE;
@@ -375,17 +381,34 @@ int ozk_dgemv(int64_t m, int64_t k, int64_t nrhs, const double* A, int64_t lda,
   int pa = 0, pb = 0;
   int st = scaling_bits(r, k, &pa, &pb);
   if (st != OZK_OK) return st;
-  const GemvLayout L = gemv_layout(m, k, nrhs, r, mode);
+  const int64_t kp = round_up(k, kPlaneK);
   if (mode == 0) {
     if (lda < k) return OZK_EINVAL;
   } else {
-    if (ldp < L.kp || ldp % kPlaneK != 0 || plane_stride < m * ldp || plane_stride % 16 != 0)
+    if (ldp < kp || ldp % kPlaneK != 0 || plane_stride < m * ldp || plane_stride % 16 != 0)
       return OZK_EINVAL;
   }
   if (m == 0) return OZK_OK;
   if (!X || !Y) return OZK_EINVAL;
   if (mode == 0 && !A) return OZK_EINVAL;
   if (mode == 1 && (!A_planes || !A_exps || !aligned(A_planes, 16))) return OZK_EINVAL;
+  return OZK_OK;
+}
+
+}  // namespace ozk
+
+extern "C" {
+
+int ozk_dgemv(int64_t m, int64_t k, int64_t nrhs, const double* A, int64_t lda,
+              const int8_t* A_planes, int64_t ldp, int64_t plane_stride, const int32_t* A_exps,
+              const double* X, int64_t ldx, double* Y, int64_t ldy, int r, int mode,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  int st = dgemv_validate(m, k, nrhs, A, lda, A_planes, ldp, plane_stride, A_exps, X, ldx, Y,
+                          ldy, r, mode);
+  if (st != OZK_OK || m == 0) return st;
+  int pa = 0, pb = 0;
+  scaling_bits(r, k, &pa, &pb);
+  const GemvLayout L = gemv_layout(m, k, nrhs, r, mode);
   if (!workspace || workspace_bytes < L.total()) return OZK_EWORKSPACE;
   if (!aligned(workspace, 256)) return OZK_EINVAL;
   Carver cv(workspace);

@@ -59,6 +59,13 @@ const ResidueConsts* residue_consts(int r, int p_bits);
 const CrtConsts* crt_consts(int r);
 
 inline int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Every argument check of ozk_dgemv except the workspace's (no HIP call): OZK_OK or the
+// status ozk_dgemv would return.
+int dgemv_validate(int64_t m, int64_t k, int64_t nrhs, const double* A, int64_t lda,
+                   const int8_t* A_planes, int64_t ldp, int64_t plane_stride,
+                   const int32_t* A_exps, const double* X, int64_t ldx, const double* Y,
+                   int64_t ldy, int r, int mode);
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Launchers (each defined next to its kernels).  All return OZK_OK or OZK_EHIP.

@@ -54,6 +54,8 @@ extern "C" {
 #define OZK_ERANGE (-3)       /* k too large: int32 products or the bit budget would fail */
 #define OZK_EHIP (-4)         /* a HIP launch failed */
 #define OZK_EUNSUPPORTED (-5) /* valid request this build does not handle */
+#define OZK_ENOSCRATCH (-6)   /* request needs more scratch than the allocation-free entry
+                                 point's fixed array holds (OZK_NOALLOC_SCRATCH_BYTES) */
 
 #define OZK_SCALING_MAX 0     /* scaling rule: per-line max (default of every entry point) */
 #define OZK_SCALING_NORM 1    /* scaling rule: per-line 2-norm (Cauchy-Schwarz), *_ex only */
@@ -61,6 +63,7 @@ extern "C" {
 #define OZK_MAX_MODULI 20
 #define OZK_MAX_K 131071      /* |residue product| <= 2^14: int32 sums stay exact */
 #define OZK_PLANE_K 64        /* residue and limb planes pad K to a multiple of this */
+#define OZK_NOALLOC_SCRATCH_BYTES (64ull << 20)  /* scratch of ozk_dgemv_noalloc, per GPU */
 
 /* Library version (major * 10000 + minor * 100 + patch). */
 int ozk_version(void);
@@ -199,6 +202,22 @@ int ozk_dgemv(int64_t m, int64_t k, int64_t nrhs, const double* A, int64_t lda,
               const int8_t* A_planes, int64_t ldp, int64_t plane_stride,
               const int32_t* A_exps, const double* X, int64_t ldx, double* Y, int64_t ldy,
               int r, int mode, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ozk_dgemv_noalloc: for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  ozk_dgemv with
+ * the same arguments, result and errors, except that there is no workspace: the
+ * scratch lives in a fixed device array of the library, OZK_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) per GPU, held by each GPU the library runs on until the process ends.  A
+ * request whose ozk_dgemv_workspace_size exceeds it returns OZK_ENOSCRATCH (nothing is
+ * enqueued); 64 MiB covers the 32768 x 32768 GEMV at r = 14 with 1, 8 or 32 columns in
+ * both modes.  The call uses the scratch of the current device, so `stream` must belong
+ * to the current device.  It allocates nothing and calls no allocating routine.  Every
+ * call on one GPU shares that GPU's array: calls ordered on one stream are safe, calls
+ * that may overlap in time on one GPU (other streams, other threads) race. */
+int ozk_dgemv_noalloc(int64_t m, int64_t k, int64_t nrhs, const double* A, int64_t lda,
+                      const int8_t* A_planes, int64_t ldp, int64_t plane_stride,
+                      const int32_t* A_exps, const double* X, int64_t ldx, double* Y,
+                      int64_t ldy, int r, int mode, void* stream);
 
 /* ---------------------------------------------------------------- emulated SpMV
  * y = A x for A rows x cols in CSR (row_ptr: rows + 1 int32 offsets into col_idx and

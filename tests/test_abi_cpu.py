@@ -210,3 +210,21 @@ def test_products_and_reconstruct_validation(lib):
 def test_no_measurement_probe_exported(lib):
     """The library exports the method's entry points only (no matrix-core rate probe)."""
     assert not hasattr(lib, "ozk_probe_mfma")
+
+
+def test_noalloc_gemv_validation(lib):
+    """ozk_dgemv_noalloc checks its arguments like ozk_dgemv and refuses a request whose
+    scratch exceeds its fixed array (OZK_ENOSCRATCH = -6), all before any HIP call."""
+    f = lib.ozk_dgemv_noalloc
+    assert f(64, 64, 33, FAKE, 64, None, 0, 0, None, FAKE, 33, FAKE, 33, 14, 0, None) == EINVAL
+    assert f(64, 64, 2, FAKE, 64, None, 0, 0, None, FAKE, 2, FAKE, 2, 21, 0, None) == EINVAL
+    assert f(64, 64, 2, None, 64, None, 0, 0, None, FAKE, 2, FAKE, 2, 14, 0, None) == EINVAL
+    assert f(64, 1 << 17, 2, FAKE, 1 << 17, None, 0, 0, None, FAKE, 2, FAKE, 2, 14, 0,
+             None) == ERANGE
+    assert f(0, 64, 2, None, 64, None, 0, 0, None, None, 2, None, 2, 14, 0, None) == OK
+    need = ozk.ozk_dgemv_workspace_size(32768, 32768, 16, 14, 0)
+    assert need > ozk.OZK_NOALLOC_SCRATCH_BYTES
+    assert f(32768, 32768, 16, FAKE, 32768, None, 0, 0, None, FAKE, 16, FAKE, 16, 14, 0,
+             None) == -6
+    assert ozk.ozk_dgemv_workspace_size(32768, 32768, 32, 14, 0) <= ozk.OZK_NOALLOC_SCRATCH_BYTES
+    assert b"scratch" in lib.ozk_status_string(-6)
