@@ -1,28 +1,33 @@
 #!/usr/bin/env python
 """Benchmark of the emulated fp64 GEMM (Ozaki scheme II through int8 MFMA) on one MI355X.
 
-One step = one ozk_dgemm call on the 4096 x 4096 x 4096 workload with entries
-(U(0,1) - 0.5) exp(0.5 N(0,1)) (seed 2) at r = 16 moduli: deconstruction of A and B,
-16 int8 MFMA products with the residue epilogue, CRT reconstruction.  Inputs are
-resident in HBM before timing starts.  `value` is emulated fp64 TFLOP/s = 2 m n k / t.
+One step = one ozk_dgemm_ex call on the largest single-GPU fp64 GEMM workload: 8192 x 8192
+x 8192 with entries (U(0,1) - 0.5) exp(4 N(0,1)) (seed 3, the wide-dynamic-range case),
+r = 16 moduli and the norm (Cauchy-Schwarz) row/column scaling, the configuration that
+reaches normwise 1e-15 against the exact product with the fewest moduli (the max rule
+needs r = 18 there: `--scaling max --r 18`).  A step is the whole hot path: column
+scaling of B, deconstruction of A and B, 16 int8 MFMA products with the residue epilogue,
+CRT reconstruction.  Inputs are resident in HBM before timing starts.  `value` is
+emulated fp64 TFLOP/s = 2 m n k / t.
 
 Also reported on the same JSON line:
-  roofline      the dominant kernel (batched int8 MFMA products, residue epilogue) timed
-                alone, one HIP event pair per launch on its stream: r * 2 * m * n * kp int8
-                ops per launch
+  roofline      the dominant kernel (batched int8 MFMA products with the residue
+                epilogue) timed inside the timed steps, one HIP event pair per launch
+                recorded by the launch itself: r * 2 * m * n * kp int8 ops per launch
                 against the 5.0 POP/s dense int8 MFMA peak; HBM traffic per launch from
                 the committed rocprofv3 counter summary when it matches the kernel source
                 (made by `--counters` under two `rocprofv3 --pmc` passes, then
                 `--traffic-summary FETCH_DIR WRITE_DIR`).
-  cpu_baseline  the CPU oracle (numpy, one BLAS thread) on 8 full output rows.
-  extras        native fp64 DGEMM (torch.matmul), the r sweep 12..18, the norm scaling
-                rule against the max rule (time and distance to native fp64 at r = 12, 14,
-                16), deconstruction HBM GB/s, the GEMV and FP4-limb engines, the
-                8192^3 wide-dynamic-range workload at r = 16..20 under both rules, and
+  cpu_baseline  the CPU oracle (numpy; its matrix products on every BLAS thread) on a
+                sampled block of 256 x 1024 outputs of the same workload, with the time of
+                each phase (scaling, residues, modular products, CRT).
+  extras        native fp64 DGEMM (torch.matmul), the 4096^3 square workload (r sweep
+                12..18 under both scaling rules, deconstruction HBM GB/s), the wide-range
+                workload at r = 16..20 under both rules, the GEMV and FP4-limb engines, and
                 the emulated SpMV of the 7-point Poisson operator on a 256^3 grid.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--r 16] [--scaling max|norm]
-                       [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--r 16] [--scaling norm|max]
+                       [--no-cpu-baseline] [--no-extras]
        python bench.py --counters            (launches only, for rocprofv3 --pmc)
        python bench.py --traffic-summary FETCH_DIR WRITE_DIR
 """
@@ -42,9 +47,16 @@ METRIC = ("emulated FP64 GEMM TFLOP/s and % int8-MFMA peak; deconstruction/GEMV 
 PEAK_INT8_TOPS = 5000.0     # dense int8 MFMA, TOP/s
 PEAK_FP4_TFLOPS = 10100.0   # dense FP4 MFMA
 PEAK_HBM_GBS = 8000.0
-M = N = K = 4096
-SEED = 2
-PHI = 0.5
+# The timed workload: the wide-dynamic-range fp64 GEMM.
+M = N = K = 8192
+SEED = 3
+PHI = 4.0
+DEFAULT_R = 16
+DEFAULT_SCALING = "norm"
+# The square workload reported among the extras.
+SQ = 4096
+SQ_SEED = 2
+SQ_PHI = 0.5
 
 
 def _source_digest(names) -> str:
@@ -84,7 +96,7 @@ def _time_each(fn, reps: int, stream) -> float:
     return sum(a.elapsed_time(b) for a, b in ev) / reps
 
 
-TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic_dgemm_4096_r16.json")
+TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic_dgemm_8192_r16_norm.json")
 COPY_BYTES = 1 << 30   # calibration copy (elementwise negation): 1 GiB read + 1 GiB written
 
 
@@ -106,8 +118,9 @@ def _traffic(kernel: str, digest: str):
 COUNTER_KERNELS = {
     "gemm_i8_residues": ("gemm_i8_pairs_kernel<1", ["gemm_i8.hip"]),
     "deconstruct_pair": ("deconstruct_pair_kernel", ["deconstruct.hip"]),
+    "norm_partials_cols": ("norm_partials_cols_kernel", ["deconstruct.hip"]),
+    "exps_norm": ("exps_norm_kernel", ["deconstruct.hip"]),
     "residues_rows_fused": ("residues_rows_fused_kernel", ["deconstruct.hip"]),
-    "absmax_cols": ("absmax_cols_kernel", ["deconstruct.hip"]),
     "residues_cols": ("residues_cols_kernel", ["deconstruct.hip"]),
     "crt": ("crt_kernel<16", ["crt.hip"]),
 }
@@ -116,8 +129,8 @@ COUNTER_KERNELS = {
 def run_counter_workload() -> int:
     """Launches profiled by the rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE): a
     plain device copy of COPY_BYTES (calibration), then two default steps (their kernels:
-    deconstruction of A and B, the residue GEMM, CRT) and each operand's deconstruction
-    on its own.  Nothing is timed."""
+    column norms of B, the paired deconstruction of A and B, the residue GEMM, CRT) and
+    each operand's deconstruction on its own.  Nothing is timed."""
     import torch
 
     import fp64_gemm_emulation_ozk_amd as ozk
@@ -132,13 +145,15 @@ def run_counter_workload() -> int:
     del src, dst
     a, b = ozk_inputs.gemm_operands(M, N, K, seed=SEED, dist="phi", phi=PHI)
     da, db = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    del a, b
+    r, rule = DEFAULT_R, DEFAULT_SCALING
     out = torch.empty((M, N), dtype=torch.float64, device=dev)
-    ws = torch.empty(ozk.ozk_dgemm_workspace_size(M, N, K, 16), dtype=torch.uint8, device=dev)
+    ws = torch.empty(ozk.ozk_dgemm_workspace_size(M, N, K, r), dtype=torch.uint8, device=dev)
     for _ in range(2):
-        ozk.ozk_dgemm(da, db, 16, out=out, workspace=ws)
+        ozk.ozk_dgemm_ex(da, db, r, rule, out=out, workspace=ws)
     # each operand's deconstruction on its own (the step runs them in one launch)
-    ozk.ozk_deconstruct(da, 0, 16)
-    ozk.ozk_deconstruct(db, 1, 16, k_budget=K)
+    ozk.ozk_deconstruct_ex(da, 0, r, rule)
+    ozk.ozk_deconstruct_ex(db, 1, r, rule, k_budget=K)
     torch.cuda.synchronize()
     print("counter workload done", flush=True)
     return 0
@@ -238,14 +253,14 @@ def run_tme_workload() -> int:
     import ozk_inputs
 
     dev = torch.device("cuda:0")
-    a, b = ozk_inputs.gemm_operands(M, N, K, seed=SEED, dist="phi", phi=PHI)
+    a, b = ozk_inputs.gemm_operands(SQ, SQ, SQ, seed=SQ_SEED, dist="phi", phi=SQ_PHI)
     da, db = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
-    out = torch.empty((M, N), dtype=torch.float64, device=dev)
-    ws = torch.empty(ozk.ozk_dgemm_workspace_size(M, N, K, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((SQ, SQ), dtype=torch.float64, device=dev)
+    ws = torch.empty(ozk.ozk_dgemm_workspace_size(SQ, SQ, SQ, 16), dtype=torch.uint8, device=dev)
     for _ in range(2):
         ozk.ozk_dgemm(da, db, 16, out=out, workspace=ws)
     ozk.ozk_deconstruct(da, 0, 16)
-    ozk.ozk_deconstruct(db, 1, 16, k_budget=K)
+    ozk.ozk_deconstruct(db, 1, 16, k_budget=SQ)
     torch.cuda.synchronize()
     del da, db, out, ws
     mg, r = 32768, 14
@@ -296,22 +311,22 @@ P_FP64 = 78.6e12          # fp64 FLOP/s (datasheet, vector and matrix)
 P_VALU = 256 * 4 * 16 * 2.4e9   # vector lane-operations per second: 256 CUs x 4 SIMDs x 16 lanes
 
 
-def tme_model(extras: dict, peaks: dict, dgemm_ms: float) -> dict | None:
+def tme_model(extras: dict, hbm: dict) -> dict | None:
     """Page 1's four-term time model instantiated on this GPU: T = max(T_tensor, T_HBM) +
     T_recon + T_decon, with T_decon = c_q r N / P_int the per-input deconstruction term.
     Instruction counts come from the committed counter pass (profiles/tme_counters.json:
     vector lane-operations and MFMA instructions per element, per kernel); rates are the
-    measured random-operand MFMA ceiling and read bandwidth of this run, and the datasheet
-    vector rate.  Returns the threshold OI* = c_q r P_fp64 / (8 P_int), the per-element
-    instruction budget below which an on-the-fly GEMV can stream at memory speed, and
-    model-versus-measured times of the GEMV paths and the DGEMM step."""
+    datasheet ones (int8 MFMA 5.0 POP/s, HBM 8 TB/s, vector lane-operations 39.3 T/s).
+    Returns the threshold OI* = c_q r P_fp64 / (8 P_int), the per-element instruction
+    budget below which an on-the-fly GEMV can stream at memory speed, and
+    model-versus-measured times of the GEMV paths and the 4096^3 DGEMM step."""
     try:
         with open(TME_PATH) as fh:
             cal = json.load(fh)["kernels"]
     except (OSError, ValueError, KeyError):
         return None
-    p_i8 = peaks["int8_mfma_random_operands_tops"] * 1e12
-    bw = peaks["hbm_read_gbs"] * 1e9
+    p_i8 = PEAK_INT8_TOPS * 1e12
+    bw = PEAK_HBM_GBS * 1e9
 
     def k(key, field):
         return cal[key][field]
@@ -326,7 +341,7 @@ def tme_model(extras: dict, peaks: dict, dgemm_ms: float) -> dict | None:
            "fp64_ridge_flop_per_byte": round(P_FP64 / 8e12, 2),
            "max_lane_ops_per_element_for_memory_speed": {
                "at_8_TBs": round(8 * P_VALU / 8e12, 1),
-               "at_measured_read_bw": round(8 * P_VALU / bw, 1)},
+               "at_measured_read_bw": round(8 * P_VALU / (hbm["hbm_read_gbs"] * 1e9), 1)},
            "digits_path_lane_ops_per_element": k("gemv_digits_32768_r14_1col",
                                                  "vector_lane_ops_per_unit")}
     n_a = 32768.0 * 32768.0
@@ -363,20 +378,21 @@ def tme_model(extras: dict, peaks: dict, dgemm_ms: float) -> dict | None:
                              "measured_ms": by[nrhs]["native_fp64"]["ms"]})
     # DGEMM step: products on the matrix cores, deconstruction of A (rows) and B
     # (columns), CRT per output; HBM bytes are small next to the tensor term.
-    t_t = 16 * 2.0 * M * N * K / p_i8
-    t_d = (k("decon_rows_wide_4096_r16", "vector_lane_ops_per_unit") +
-           k("decon_cols_wide_4096_r16", "vector_lane_ops_per_unit")) * M * K / P_VALU
-    t_r = k("crt_4096_r16", "vector_lane_ops_per_unit") * M * N / P_VALU
-    case = {"case": "DGEMM 4096^3 r=16", "T_tensor_ms": round(t_t * 1e3, 3),
-            "T_decon_ms": round(t_d * 1e3, 3), "T_recon_ms": round(t_r * 1e3, 3),
-            "model_ms": round((t_t + t_d + t_r) * 1e3, 3), "measured_ms": round(dgemm_ms, 4)}
-    if "deconstruct_cols" in extras and "reconstruct_and_gaps" in extras:
-        case["measured_phases_ms"] = {
-            "products": extras.get("products_ms"),
-            "deconstruct_rows": extras["deconstruct_rows"]["ms"],
-            "deconstruct_cols": extras["deconstruct_cols"]["ms"],
-            "reconstruct_and_gaps": extras["reconstruct_and_gaps"]["ms"]}
-    rows.append(case)
+    sq = extras.get("square_4096")
+    if sq:
+        t_t = 16 * 2.0 * SQ * SQ * SQ / p_i8
+        t_d = (k("decon_rows_wide_4096_r16", "vector_lane_ops_per_unit") +
+               k("decon_cols_wide_4096_r16", "vector_lane_ops_per_unit")) * SQ * SQ / P_VALU
+        t_r = k("crt_4096_r16", "vector_lane_ops_per_unit") * SQ * SQ / P_VALU
+        case = {"case": "DGEMM 4096^3 r=16 (max rule)", "T_tensor_ms": round(t_t * 1e3, 3),
+                "T_decon_ms": round(t_d * 1e3, 3), "T_recon_ms": round(t_r * 1e3, 3),
+                "model_ms": round((t_t + t_d + t_r) * 1e3, 3),
+                "measured_ms": sq["step_r16_max"]["ms"],
+                "measured_phases_ms": {
+                    "products": sq["step_r16_max"]["products_ms"],
+                    "deconstruct_rows": sq["deconstruct_rows"]["ms"],
+                    "deconstruct_cols": sq["deconstruct_cols"]["ms"]}}
+        rows.append(case)
     out["cases"] = rows
     return out
 
@@ -438,7 +454,7 @@ def measure_gemv(reps: int, stream) -> dict:
     return out
 
 
-def measure_wide_range(reps: int, stream) -> dict:
+def measure_wide_range(reps: int, stream, da, db) -> dict:
     """The wide-dynamic-range workload: 8192^3 with entries (U(0,1) - 0.5) exp(4 N(0,1))
     (seed 3), r = 16..20 under both scaling rules, next to native fp64 DGEMM.  rel is the
     normwise distance to the native product (its own rounding error is far below the
@@ -447,13 +463,9 @@ def measure_wide_range(reps: int, stream) -> dict:
     import torch
 
     import fp64_gemm_emulation_ozk_amd as ozk
-    import ozk_inputs
 
-    n = 8192
-    dev = torch.device("cuda:0")
-    a, b = ozk_inputs.gemm_operands(n, n, n, seed=3, dist="phi", phi=4.0)
-    da, db = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
-    del a, b
+    n = da.shape[0]
+    dev = da.device
     flops = 2.0 * n * n * n
     ref = torch.matmul(da, db)
     nat = lambda: torch.matmul(da, db, out=ref)
@@ -477,7 +489,7 @@ def measure_wide_range(reps: int, stream) -> dict:
     res["same_accuracy_1e-15"] = {
         "max_rule_r18_ms": by_r[18]["max"]["ms"], "norm_rule_r16_ms": by_r[16]["norm"]["ms"],
         "speedup": round(by_r[18]["max"]["ms"] / by_r[16]["norm"]["ms"], 3)}
-    del da, db, ref, out, ws
+    del ref, out, ws
     torch.cuda.empty_cache()
     return res
 
@@ -583,28 +595,14 @@ def measure_fp4(reps: int, stream) -> dict:
     return out
 
 
-def measure_practical_peaks(stream) -> dict:
-    """Rates this GPU sustains on data like the products': the register-only int8 and e2m1
-    matrix-core loops of ozk_probe_mfma over random operand bytes (about 0.2 s per launch,
-    the last of three back-to-back launches timed, so the board sits at its power limit),
-    a plain device copy of 2 GiB (torch, read + write bytes) and a 2 GiB reduction (torch
-    sum, read bytes)."""
+def measure_hbm_rates(stream) -> dict:
+    """What plain streaming reaches on this GPU, as context for the HBM rooflines: a device
+    copy of 2 GiB (torch, read + write bytes) and a read-only reduction of 2 GiB (torch sum,
+    read bytes)."""
     import torch
 
-    import fp64_gemm_emulation_ozk_amd as ozk
-
     dev = torch.device("cuda:0")
-    g = torch.Generator(device=dev)
-    g.manual_seed(11)
-    operands = torch.randint(-128, 128, (1 << 20,), dtype=torch.int8, device=dev, generator=g)
     out = {}
-    for kind, key in ((0, "int8_mfma_random_operands_tops"), (1, "fp4_mfma_random_operands_tflops")):
-        iters = 150000 if kind == 0 else 80000
-        ops = 0.0
-        for _ in range(2):
-            ops = ozk.ozk_probe_mfma(kind, operands, iters, 256)
-        t = _time_events(lambda: ozk.ozk_probe_mfma(kind, operands, iters, 256), 1, stream)
-        out[key] = round(ops / (t * 1e-3) / 1e12, 1)
     src = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -616,33 +614,154 @@ def measure_practical_peaks(stream) -> dict:
     torch.sum(x, dim=0, out=acc)
     t = _time_events(lambda: torch.sum(x, dim=0, out=acc), 5, stream)
     out["hbm_read_gbs"] = round(src.numel() / t / 1e6, 1)
-    del src, x, operands
+    del src, x
     torch.cuda.empty_cache()
-    out["what"] = ("sustained rates with random operands (matrix cores draw data-dependent "
-                   "power; the board holds its power limit below the datasheet clock) and "
-                   "a 2 GiB device copy and a 2 GiB read-only reduction")
+    out["what"] = "a 2 GiB device copy and a 2 GiB read-only reduction (torch)"
     return out
 
 
-def cpu_baseline(a, b, r: int, rule: str = "max") -> dict:
+def measure_square_4096(reps: int, stream) -> dict:
+    """The square workload: 4096^3 with entries (U(0,1) - 0.5) exp(0.5 N(0,1)) (seed 2).
+    The step at r = 16 (max rule) with its residue products timed inside it, native fp64
+    DGEMM and the vendor int8 GEMM on the same sizes, the r sweep 12..18 under both
+    scaling rules (time and normwise distance to the native product), and each
+    operand's deconstruction alone in HBM GB/s (algorithmic bytes: 8 B read + r B
+    written per element, + 8 B for the column maxima pass of B)."""
+    import torch
+
+    import fp64_gemm_emulation_ozk_amd as ozk
+    import ozk_inputs
+
+    n = SQ
+    dev = torch.device("cuda:0")
+    a, b = ozk_inputs.gemm_operands(n, n, n, seed=SQ_SEED, dist="phi", phi=SQ_PHI)
+    da, db = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    del a, b
+    flops = 2.0 * n * n * n
+    out = torch.empty((n, n), dtype=torch.float64, device=dev)
+    ws = torch.empty(ozk.ozk_dgemm_workspace_size(n, n, n, 18), dtype=torch.uint8, device=dev)
+    res = {"workload": f"DGEMM {n}^3, entries (U-0.5)*exp({SQ_PHI}*N(0,1)), seed {SQ_SEED}"}
+    for _ in range(20):
+        ozk.ozk_dgemm(da, db, 16, out=out, workspace=ws)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        e1.record(stream)
+    it = iter(ev)
+
+    def timed():
+        e0, e1 = next(it)
+        ozk.ozk_dgemm_ex_timed(da, db, 16, e0, e1, "max", out=out, workspace=ws)
+
+    t = _time_events(timed, reps, stream)
+    prod_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
+    ops = 16 * 2.0 * n * n * n
+    res["step_r16_max"] = {"ms": round(t, 4), "tflops": round(flops / t / 1e9, 2),
+                           "products_ms": round(prod_ms, 4),
+                           "products_frac_int8_peak": round(ops / prod_ms / 1e9 /
+                                                            PEAK_INT8_TOPS, 4)}
+    ref = torch.matmul(da, db)
+    t = _time_events(lambda: torch.matmul(da, db, out=ref), reps, stream)
+    res["native_fp64"] = {"ms": round(t, 4), "tflops": round(flops / t / 1e9, 2)}
+    try:
+        ia = torch.randint(-128, 128, (n, n), dtype=torch.int8, device=dev)
+        ib = torch.randint(-128, 128, (n, n), dtype=torch.int8, device=dev)
+        torch._int_mm(ia, ib)
+        t = _time_events(lambda: torch._int_mm(ia, ib), reps, stream)
+        res["vendor_int8_gemm"] = {"what": "torch._int_mm on one 4096^3 int8 product",
+                                   "ms": round(t, 4), "tops": round(flops / t / 1e9, 1),
+                                   "ours_per_modulus_ms": round(prod_ms / 16, 4)}
+        del ia, ib
+    except RuntimeError as exc:  # not every build ships the int8 path
+        res["vendor_int8_gemm"] = {"error": str(exc)[:200]}
+    ref_n = torch.linalg.norm(ref)
+    sweep = []
+    for rr in range(12, 19):
+        row = {"r": rr}
+        for rule in ("max", "norm"):
+            f = lambda: ozk.ozk_dgemm_ex(da, db, rr, rule, out=out, workspace=ws)
+            f()
+            t = _time_events(f, reps, stream)
+            row[rule] = {"ms": round(t, 4), "tflops": round(flops / t / 1e9, 2),
+                         "rel_vs_native": float(torch.linalg.norm(out - ref) / ref_n)}
+        sweep.append(row)
+    res["r_sweep"] = sweep
+    del ws, out, ref
+    r = 16
+    planes_a, exps_a = ozk.ozk_deconstruct(da, 0, r)
+    planes_b, exps_b = ozk.ozk_deconstruct(db, 1, r, k_budget=n)
+    dec = lambda: ozk.ozk_deconstruct(da, 0, r, planes=planes_a, exps=exps_a)
+    dec()
+    t = _time_events(dec, reps, stream)
+    res["deconstruct_rows"] = {"ms": round(t, 4), "bytes": (8 + r) * n * n,
+                               "gbs": round((8 + r) * n * n / t / 1e6, 1),
+                               "frac_hbm": round((8 + r) * n * n / t / 1e6 / PEAK_HBM_GBS, 4)}
+    decb = lambda: ozk.ozk_deconstruct(db, 1, r, k_budget=n, planes=planes_b, exps=exps_b)
+    decb()
+    t = _time_events(decb, reps, stream)
+    res["deconstruct_cols"] = {"ms": round(t, 4), "bytes": (16 + r) * n * n,
+                               "gbs": round((16 + r) * n * n / t / 1e6, 1),
+                               "note": "column maxima pass (8 B per element) + residues "
+                                       "(8 + r B per element)"}
+    del da, db, planes_a, planes_b
+    torch.cuda.empty_cache()
+    return res
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(a, b, r: int, rule: str) -> dict:
+    """The oracle, as it stands, on a sampled block of the timed workload: rows 0, 32, 64,
+    ... of C (256 rows) by columns 0, 8, 16, ... (1024 columns), 262144 outputs, each phase
+    timed.  Exponents come from the full rows of A and columns of B, so the block equals
+    the same block of the whole product.  The modular products run in float64 BLAS on all
+    of its threads; the other phases are numpy and Python integers on one thread."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
+    from threadpoolctl import threadpool_info
 
     from oracle import ozaki2
 
-    # 256 rows: about 10 s on a current server core, most of it the deconstruction of
-    # all of B, which any number of rows needs.
-    rows = np.arange(256)
-    with threadpool_limits(1):
-        t0 = time.perf_counter()
-        ozaki2.dgemm(a, b, r, rows=rows, scaling=rule)
-        dt = time.perf_counter() - t0
-    flops = 2.0 * len(rows) * N * K
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"{len(rows)} full rows of C ({len(rows)} x {N} outputs; those rows of A "
-                      f"and all of B "
-                      f"deconstructed), r={r}, {rule} scaling, numpy with 1 BLAS thread"}
+    k = a.shape[1]
+    rows = np.arange(0, a.shape[0], 32)
+    cols = np.arange(0, b.shape[1], 8)
+    phases = {}
+    t0 = time.perf_counter()
+    ar, bc = a[rows], b[:, cols]
+    e = ozaki2.exponents(ar, r, k, 0, "a", rule)
+    f = ozaki2.exponents(bc, r, k, 1, "b", rule)
+    t1 = time.perf_counter()
+    pla = ozaki2.residue_planes(ar, e, r, 0)
+    plb = ozaki2.residue_planes(bc, f, r, 1)
+    t2 = time.perf_counter()
+    prods = ozaki2.modular_products(pla, plb)
+    t3 = time.perf_counter()
+    ozaki2.reconstruct(prods, r, e, f)
+    t4 = time.perf_counter()
+    phases = {"scaling_s": round(t1 - t0, 3), "residues_s": round(t2 - t1, 3),
+              "modular_products_s": round(t3 - t2, 3), "crt_s": round(t4 - t3, 3)}
+    dt = t4 - t0
+    flops = 2.0 * len(rows) * len(cols) * k
+    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max(blas) if blas else 1
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 3), "phases": phases, "cpu_model": _cpu_model(),
+            "host_logical_cpus": os.cpu_count(),
+            "sample": f"{len(rows)} x {len(cols)} block of C (every 32nd row, every 8th "
+                      f"column) of the {M}x{N}x{K} workload, r={r}, {rule} scaling; rate = "
+                      f"2 * outputs * k / time, i.e. the whole product's rate at this "
+                      f"per-output cost; numpy, modular products on {threads} BLAS threads, "
+                      f"other phases on one thread"}
 
 
 def main() -> int:
@@ -650,21 +769,22 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     # Untimed warm-up: after an idle spell the board needs some 50-65 ms of this load before
-    # its clocks settle (4096^3 r=16: 1.33 ms per step after 3 warm-up steps, 1.24 ms after
-    # 50, 200 or 400), so the default covers that.
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--r", type=int, default=16)
-    ap.add_argument("--scaling", choices=("max", "norm"), default="max",
-                    help="scaling rule of the timed step (max: per-line maximum, the "
-                         "headline; norm: per-line 2-norm)")
+    # its clocks settle, so the default covers that.
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--r", type=int, default=DEFAULT_R)
+    ap.add_argument("--scaling", choices=("max", "norm"), default=DEFAULT_SCALING,
+                    help="scaling rule of the timed step (norm: per-line 2-norm, the "
+                         "headline; max: per-line maximum, needs r = 18 for 1e-15 here)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--no-fp4", action="store_true")
     ap.add_argument("--no-wide", action="store_true",
-                    help="skip the 8192^3 wide-dynamic-range extra")
+                    help="skip the wide-range r = 16..20 sweep under both rules")
     ap.add_argument("--no-spmv", action="store_true",
                     help="skip the emulated SpMV (Poisson 256^3) extra")
+    ap.add_argument("--no-square", action="store_true",
+                    help="skip the 4096^3 square workload extra")
     ap.add_argument("--counters", action="store_true",
                     help="only launch the kernels the counter passes profile")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -684,7 +804,6 @@ def main() -> int:
               "supported.", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import fp64_gemm_emulation_ozk_amd as ozk
@@ -700,13 +819,13 @@ def main() -> int:
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     r = args.r
+    rule = args.scaling
 
     a, b = ozk_inputs.gemm_operands(M, N, K, seed=SEED, dist="phi", phi=PHI)
     da = torch.from_numpy(a).to(dev)
     db = torch.from_numpy(b).to(dev)
     out = torch.empty((M, N), dtype=torch.float64, device=dev)
     ws = torch.empty(ozk.ozk_dgemm_workspace_size(M, N, K, r), dtype=torch.uint8, device=dev)
-    rule = args.scaling
     step = lambda: ozk.ozk_dgemm_ex(da, db, r, rule, out=out, workspace=ws)
 
     for _ in range(args.warmup):
@@ -738,17 +857,8 @@ def main() -> int:
     # Sanity: normwise distance to native fp64 (not a parity check; tests do that).
     ref = torch.matmul(da, db)
     rel = float(torch.linalg.norm(out - ref) / torch.linalg.norm(ref))
-
-    # Context: the same product launched alone, back to back (no memory-bound kernels
-    # between launches, so it runs at the lower clock of a sustained matrix-core load).
-    planes_a, exps_a = ozk.ozk_deconstruct_ex(da, 0, r, rule)
-    planes_b, exps_b = ozk.ozk_deconstruct_ex(db, 1, r, rule, k_budget=K)
-    res = torch.empty((r, M, N), dtype=torch.int8, device=dev)
-    gemm = lambda: ozk.ozk_modular_residues(planes_a, planes_b, out=res)
-    for _ in range(2):
-        gemm()
-    alone_ms = _time_each(gemm, args.steps, stream)
-    kp = planes_a.shape[-1]
+    kp = ozk.ozk_planes_ld(K)
+    kp = (kp + 127) // 128 * 128          # the step pads K to whole 128-byte rows
     ops = r * 2.0 * M * N * kp
     achieved = ops / (gemm_ms * 1e-3) / 1e12
     digest = _source_digest(["gemm_i8.hip"])
@@ -757,66 +867,25 @@ def main() -> int:
                 "traffic": _traffic("gemm_i8_residues", digest),
                 "kernel": "gemm_i8_pairs_kernel<residues> (v_mfma_i32_32x32x32_i8)",
                 "kernel_ms": round(gemm_ms, 4), "ops_per_launch": ops,
+                "ops_unit": "int8 multiply-adds x 2 (TOP/s reported in the TFLOP/s slot)",
                 "timed": "inside the timed steps, one HIP event pair per launch",
                 "source_digest": digest}
 
     extras = {"wall_ms_per_step": round(wall_ms, 4), "normwise_vs_native_fp64": rel,
               "ms_per_step_without_gemm_events": round(plain_ms, 4),
               "emulated_pct_int8_peak": round(r * value / PEAK_INT8_TOPS * 100, 2),
-              "products_ms": round(gemm_ms, 4), "products_alone_ms": round(alone_ms, 4)}
+              "products_ms": round(gemm_ms, 4),
+              "step_phases": "column scaling of B, paired deconstruction of A and B, "
+                             "residue products, CRT"}
+    reps = max(args.steps // 2, 5)
+    nat_ms = _time_events(lambda: torch.matmul(da, db, out=ref), reps, stream)
+    extras["native_fp64_dgemm"] = {"ms": round(nat_ms, 4),
+                                   "tflops": round(2.0 * M * N * K / nat_ms / 1e9, 2),
+                                   "emulated_speedup": round(nat_ms / ms_per_step, 3)}
+    del ref
     if not args.no_extras:
-        peaks = measure_practical_peaks(stream)
-        extras["practical_peaks"] = peaks
-        ceil = peaks["int8_mfma_random_operands_tops"]
-        roofline["measured_ceiling"] = ceil
-        roofline["frac_of_measured_ceiling"] = round(achieved / ceil, 4)
-        reps = max(args.steps // 2, 5)
-        nat_ms = _time_events(lambda: torch.matmul(da, db, out=ref), reps, stream)
-        extras["native_fp64_dgemm"] = {"ms": round(nat_ms, 4),
-                                       "tflops": round(2.0 * M * N * K / nat_ms / 1e9, 2)}
-        try:
-            ia = torch.randint(-128, 128, (M, K), dtype=torch.int8, device=dev)
-            ib = torch.randint(-128, 128, (K, N), dtype=torch.int8, device=dev)
-            torch._int_mm(ia, ib)
-            i8_ms = _time_events(lambda: torch._int_mm(ia, ib), reps, stream)
-            extras["library_int8_gemm"] = {
-                "what": "torch._int_mm (vendor int8 GEMM) on one 4096^3 int8 product",
-                "ms": round(i8_ms, 4), "tops": round(2.0 * M * N * K / i8_ms / 1e9, 1),
-                "ours_per_modulus_ms": round(gemm_ms / r, 4)}
-            del ia, ib
-        except RuntimeError as exc:  # not every build ships the int8 path
-            extras["library_int8_gemm"] = {"error": str(exc)[:200]}
-        sweep = []
-        for rr in range(12, 19):
-            wsr = torch.empty(ozk.ozk_dgemm_workspace_size(M, N, K, rr), dtype=torch.uint8,
-                              device=dev)
-            f = lambda: ozk.ozk_dgemm(da, db, rr, out=out, workspace=wsr)
-            f()
-            ms = _time_events(f, reps, stream)
-            sweep.append({"r": rr, "ms": round(ms, 4),
-                          "tflops": round(2.0 * M * N * K / ms / 1e9, 2),
-                          "rel_vs_native": float(torch.linalg.norm(out - ref) /
-                                                 torch.linalg.norm(ref))})
-            del wsr
-        extras["r_sweep"] = sweep
-        # Norm (Cauchy-Schwarz) scaling rule against the max rule on the same operands:
-        # step time and normwise distance to the native fp64 product.
-        norm_rows = []
-        ref_n = torch.linalg.norm(ref)
-        wsn = torch.empty(ozk.ozk_dgemm_workspace_size(M, N, K, 16), dtype=torch.uint8,
-                          device=dev)
-        for rr in (12, 14, 16):
-            row = {"r": rr}
-            for rl in ("max", "norm"):
-                f = lambda: ozk.ozk_dgemm_ex(da, db, rr, rl, out=out, workspace=wsn)
-                f()
-                row[f"ms_{rl}"] = round(_time_events(f, reps, stream), 4)
-                row[f"rel_vs_native_{rl}"] = float(torch.linalg.norm(out - ref) / ref_n)
-            row["widths_max"] = ozk.ozk_scaling_bits_ex(rr, K, "max")
-            row["widths_norm"] = ozk.ozk_scaling_bits_ex(rr, K, "norm")
-            norm_rows.append(row)
-        extras["norm_rule"] = norm_rows
-        del wsn
+        planes_a, exps_a = ozk.ozk_deconstruct_ex(da, 0, r, rule)
+        planes_b, exps_b = ozk.ozk_deconstruct_ex(db, 1, r, rule, k_budget=K)
         dec = lambda: ozk.ozk_deconstruct_ex(da, 0, r, rule, planes=planes_a, exps=exps_a)
         dec()
         dec_ms = _time_events(dec, reps, stream)
@@ -831,25 +900,23 @@ def main() -> int:
         extras["deconstruct_cols"] = {
             "ms": round(decb_ms, 4), "bytes": (8 + 8 + r) * K * N,
             "gbs": round((8 + 8 + r) * K * N / decb_ms / 1e6, 1),
-            "note": "column maxima pass (8 B per element) + residues (8 + r B per element)"}
-        # The CRT of the step runs on int8 residues inside ozk_dgemm; its share is what the
-        # step leaves after the products and both deconstructions.
-        extras["reconstruct_and_gaps"] = {
-            "ms": round(ms_per_step - gemm_ms - dec_ms - decb_ms, 4),
-            "note": "step time minus the products and both deconstructions timed on their "
-                    "own (inside the step A's rows and B's residues share one launch, which "
-                    "is faster than the two calls, so this understates the CRT)"}
+            "note": "norm (or maxima) pass over B (8 B per element) + residues "
+                    "(8 + r B per element)"}
+        del planes_a, planes_b, ws, out
+        torch.cuda.empty_cache()
+        hbm = measure_hbm_rates(stream)
+        extras["hbm_rates"] = hbm
+        if not args.no_wide:
+            extras["wide_range_8192"] = measure_wide_range(reps, stream, da, db)
+        if not args.no_square:
+            extras["square_4096"] = measure_square_4096(reps, stream)
         if not args.no_gemv:
-            del planes_a, planes_b, res, ws
-            torch.cuda.empty_cache()
             extras["gemv_32768"] = measure_gemv(reps, stream)
         if not args.no_fp4:
             extras["fp4limb_int8gemm_8192"] = measure_fp4(reps, stream)
-        if not args.no_wide:
-            extras["wide_range_8192"] = measure_wide_range(reps, stream)
         if not args.no_spmv:
             extras["spmv_poisson_256"] = measure_spmv(reps, stream)
-        model = tme_model(extras, peaks, ms_per_step)
+        model = tme_model(extras, hbm)
         if model is not None:
             extras["tme_model"] = model
 
@@ -867,7 +934,7 @@ def main() -> int:
         "dtype": "f64",
         "data": "synthetic",
         "config": {"workload": f"emulated DGEMM {M}x{N}x{K}, entries (U-0.5)*exp({PHI}*N(0,1)), "
-                               f"seed {SEED}, r={r} moduli, {rule} scaling",
+                               f"seed {SEED}, r={r} moduli, {rule} row/column scaling",
                    "m": M, "n": N, "k": K, "r": r, "scaling": rule,
                    "compute": "int8 MFMA + fp64 VALU"},
         "roofline": roofline,
