@@ -126,11 +126,29 @@ COUNTER_KERNELS = {
 }
 
 
-def run_counter_workload() -> int:
-    """Launches profiled by the rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE): a
-    plain device copy of COPY_BYTES (calibration), then two default steps (their kernels:
-    column norms of B, the paired deconstruction of A and B, the residue GEMM, CRT) and
-    each operand's deconstruction on its own.  Nothing is timed."""
+# Kernels of the other engines, summarised when the counter workload ran them
+# (`--counters all`): key -> (kernel-name substring, sources, algorithmic bytes per launch).
+COUNTER_KERNELS_EXTRA = {
+    "gemv_digits_1col": ("gemv_digits_kernel<1>", ["gemv_digits.hip"], 8 * 32768 * 32768),
+    "gemv_digits_8cols": ("gemv_digits_kernel<4>", ["gemv_digits.hip"], 8 * 32768 * 32768),
+    "gemv_fly_32cols": ("gemv_fly_kernel<false, 0, 14, 2>", ["gemv.hip"], 8 * 32768 * 32768),
+    "gemv_stored_1col": ("gemv_stored_kernel", ["gemv.hip"], 14 * 32768 * 32768),
+    "fp4_gemm": ("fp4_gemm_kernel", ["fp4limb.hip"], None),
+    "fp4_pack_rows": ("pack_rows_kernel", ["fp4limb.hip"], 8192 * 8192 * (1 + 1.5)),
+    "fp4_pack_cols": ("pack_cols_kernel", ["fp4limb.hip"], 8192 * 8192 * (1 + 1.5)),
+    "spmv_rows_r16": ("spmv_residues_kernel<true, 16>", ["spmv.hip"], None),
+}
+
+
+def run_counter_workload(extra: bool = False) -> int:
+    """Launches profiled by the rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE, or
+    instruction and utilisation counters): a plain device copy of COPY_BYTES
+    (calibration), then two default steps (their kernels: column norms of B, the paired
+    deconstruction of A and B, the residue GEMM, CRT) and each operand's deconstruction on
+    its own.  With `extra`, also one call of each other engine at its workload size: the
+    32768^2 GEMV at r = 14 (digits path at 1 and 8 columns, residue path at 32, stored
+    planes at 1), the 8192^3 INT8 product through FP4 limbs and the emulated SpMV of the
+    256^3 Poisson operator at r = 16.  Nothing is timed."""
     import torch
 
     import fp64_gemm_emulation_ozk_amd as ozk
@@ -155,6 +173,33 @@ def run_counter_workload() -> int:
     ozk.ozk_deconstruct_ex(da, 0, r, rule)
     ozk.ozk_deconstruct_ex(db, 1, r, rule, k_budget=K)
     torch.cuda.synchronize()
+    del da, db, out, ws
+    torch.cuda.empty_cache()
+    if extra:
+        import numpy as np
+
+        mg = 32768
+        ga = ozk_inputs.uniform_matrix_device((mg, mg), 4, dev)
+        x_all = torch.from_numpy(ozk_inputs.uniform_matrix(np.random.default_rng(4),
+                                                           (mg, 32))).to(dev)
+        planes, exps = ozk.ozk_deconstruct(ga, 0, 14, k_budget=mg)
+        for nrhs in (1, 8, 32):
+            ozk.ozk_dgemv(ga, x_all[:, :nrhs].contiguous(), 14, mode=0, a_exps=exps)
+        ozk.ozk_dgemv(None, x_all[:, :1].contiguous(), 14, mode=1, a_planes=planes, a_exps=exps)
+        torch.cuda.synchronize()
+        del ga, planes, x_all
+        torch.cuda.empty_cache()
+        ia, ib = (torch.from_numpy(t).to(dev) for t in ozk_inputs.int8_operands(8192, 8192, 8192,
+                                                                                 seed=5))
+        ozk.ozk_int8gemm_fp4limb(ia, ib)
+        torch.cuda.synchronize()
+        del ia, ib
+        rp, ci, v = ozk_inputs.poisson_7pt_csr(256)
+        drp, dci, dv = (torch.from_numpy(t).to(dev) for t in (rp, ci, v))
+        xs = torch.from_numpy(ozk_inputs.uniform_matrix(np.random.default_rng(7),
+                                                        (256 ** 3, 1))[:, 0]).to(dev)
+        ozk.ozk_spmv_csr(drp, dci, dv, xs, 16, 7)
+        torch.cuda.synchronize()
     print("counter workload done", flush=True)
     return 0
 
@@ -177,9 +222,10 @@ def _counter_means(run_dir: str, counter: str) -> dict:
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
-def traffic_summary(fetch_dir: str, write_dir: str) -> int:
+def traffic_summary(fetch_dir: str, write_dir: str, out_path: str | None = None) -> int:
     """Turn the two counter passes into per-launch HBM bytes, scaled by what the same
-    counters read for the calibration copy, and write TRAFFIC_PATH."""
+    counters read for the calibration copy, and write out_path (default TRAFFIC_PATH)."""
+    out_path = out_path or TRAFFIC_PATH
     fetch = _counter_means(fetch_dir, "FETCH_SIZE")
     write = _counter_means(write_dir, "WRITE_SIZE")
 
@@ -210,10 +256,55 @@ def traffic_summary(fetch_dir: str, write_dir: str) -> int:
         data["kernels"][key] = {"kernel": sub, "fetch_bytes": round(fb), "write_bytes": round(wb),
                                 "hbm_bytes_per_launch": round(fb + wb),
                                 "source_digest": _source_digest(srcs)}
-    with open(TRAFFIC_PATH, "w") as fh:
+    for key, (sub, srcs, algo) in COUNTER_KERNELS_EXTRA.items():
+        if not any(sub in k for k in fetch) or not any(sub in k for k in write):
+            continue
+        fb = pick(fetch, sub) * 1024.0 * f_fac
+        wb = pick(write, sub) * 1024.0 * w_fac
+        ent = {"kernel": sub, "fetch_bytes": round(fb), "write_bytes": round(wb),
+               "hbm_bytes_per_launch": round(fb + wb), "source_digest": _source_digest(srcs)}
+        if algo:
+            ent["algorithmic_bytes"] = algo
+            ent["traffic_over_algorithmic"] = round((fb + wb) / algo, 3)
+        data["kernels"][key] = ent
+    with open(out_path, "w") as fh:
         json.dump(data, fh, indent=1)
         fh.write("\n")
     print(json.dumps(data, indent=1))
+    return 0
+
+
+def pmc_summary(run_dir: str, out_json: str) -> int:
+    """Per-kernel mean per dispatch of every counter found in a rocprofv3 --pmc csv run
+    (kernel names shortened to their template head), written to out_json."""
+    import csv
+    import glob
+    import re
+
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    acc = {}
+    for f in files:
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                name = re.sub(r"\(.*$", "", re.sub(r"ozk::\(anonymous namespace\)::|^void ", "",
+                                                  row["Kernel_Name"]))[:80]
+                ent = acc.setdefault(name, {})
+                ent.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+                ent.setdefault("_ns", {})[row["Dispatch_Id"]] = (
+                    int(row["End_Timestamp"]) - int(row["Start_Timestamp"]))
+    out = {"what": "per-dispatch means of rocprofv3 --pmc counters, per kernel", "kernels": {}}
+    for name, ent in acc.items():
+        ns = ent.pop("_ns")
+        row = {c: round(sum(v) / len(v), 1) for c, v in ent.items()}
+        row["dispatches"] = len(ns)
+        row["mean_duration_us"] = round(sum(ns.values()) / len(ns) / 1e3, 1)
+        out["kernels"][name] = row
+    with open(out_json, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out, indent=1))
     return 0
 
 
@@ -785,19 +876,27 @@ def main() -> int:
                     help="skip the emulated SpMV (Poisson 256^3) extra")
     ap.add_argument("--no-square", action="store_true",
                     help="skip the 4096^3 square workload extra")
-    ap.add_argument("--counters", action="store_true",
-                    help="only launch the kernels the counter passes profile")
-    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write the HBM traffic summary from two rocprofv3 --pmc csv runs")
+    ap.add_argument("--counters", nargs="?", const="dgemm", choices=("dgemm", "all"),
+                    help="only launch the kernels the counter passes profile (all: also the "
+                         "GEMV, FP4-limb and SpMV engines)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("DIR", "OUT_JSON"),
+                    help="per-kernel means of every counter of a rocprofv3 --pmc csv run")
+    ap.add_argument("--traffic-summary", nargs="+", metavar="DIR",
+                    help="FETCH_DIR WRITE_DIR [OUT_JSON]: write the HBM traffic summary from "
+                         "two rocprofv3 --pmc csv runs")
     ap.add_argument("--tme-counters", action="store_true",
                     help="only launch the kernels the time-model counter pass profiles")
     ap.add_argument("--tme-summary", metavar="DIR",
                     help="write the time-model instruction counts from a rocprofv3 --pmc run")
     args = ap.parse_args()
     if args.traffic_summary:
+        if len(args.traffic_summary) not in (2, 3):
+            ap.error("--traffic-summary takes FETCH_DIR WRITE_DIR [OUT_JSON]")
         return traffic_summary(*args.traffic_summary)
     if args.tme_summary:
         return tme_summary(args.tme_summary)
+    if args.pmc_summary:
+        return pmc_summary(*args.pmc_summary)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the emulation "
               "path is built and measured on a single MI355X; multi-GPU runs are not "
@@ -813,7 +912,7 @@ def main() -> int:
         from fp64_gemm_emulation_ozk_amd.build import build_library
         build_library()
     if args.counters:
-        return run_counter_workload()
+        return run_counter_workload(extra=args.counters == "all")
     if args.tme_counters:
         return run_tme_workload()
     dev = torch.device("cuda:0")
