@@ -15,7 +15,8 @@ Sources it follows (cited by page title and part):
 * [AWE] arXiv 2609.24519 listing (Nagoya University), English abstract: each Ozaki
   product is an exact integer matrix product times a scale; the set S of FP4 values
   times 2 holds every residue modulo 13, so integers split into base-13 digits with
-  weights (1, 13, 169), and an INT8 x INT8 product takes 9 pairwise FP4 GEMMs.
+  weights (1, 13, 169), and an INT8 x INT8 product takes 9 pairwise FP4 GEMMs; with
+  free limb weights and planes that combine limbs it takes 6.
 
 Where the pages leave a step open, the module that implements it states the reading it
 takes (moduli, scaling rule, symmetric range, digit choice, e2m1 nibble order).
@@ -25,5 +26,7 @@ Modules:
     ozaki2     exponents, scaled integers, residue planes, modular products, reconstruction
     reference  Dot2 double-double dot products and exact rational products (accuracy pins)
     fp4limb    base-13 digit split, e2m1 codes, 9-product limb GEMM
+    fp4awe     weights (1, 29, 37), limb and pairwise-sum planes, 6-product limb GEMM
+    spmv       emulated CSR sparse matrix-vector product
 """
-from . import rns, ozaki2, reference, fp4limb  # noqa: F401
+from . import rns, ozaki2, reference, fp4limb, fp4awe, spmv  # noqa: F401
