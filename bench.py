@@ -134,6 +134,7 @@ COUNTER_KERNELS_EXTRA = {
     "gemv_fly_32cols": ("gemv_fly_kernel<false, 0, 14, 2>", ["gemv.hip"], 8 * 32768 * 32768),
     "gemv_stored_1col": ("gemv_stored_kernel", ["gemv.hip"], 14 * 32768 * 32768),
     "fp4_gemm": ("fp4_gemm_kernel", ["fp4limb.hip"], None),
+    "fp4awe_gemm": ("awe_gemm_kernel", ["fp4awe.hip"], None),
     "fp4_pack_rows": ("pack_rows_kernel", ["fp4limb.hip"], 8192 * 8192 * (1 + 1.5)),
     "fp4_pack_cols": ("pack_cols_kernel", ["fp4limb.hip"], 8192 * 8192 * (1 + 1.5)),
     "spmv_rows_r16": ("spmv_residues_kernel<true, 16>", ["spmv.hip"], None),
@@ -192,6 +193,7 @@ def run_counter_workload(extra: bool = False) -> int:
         ia, ib = (torch.from_numpy(t).to(dev) for t in ozk_inputs.int8_operands(8192, 8192, 8192,
                                                                                  seed=5))
         ozk.ozk_int8gemm_fp4limb(ia, ib)
+        ozk.ozk_int8gemm_fp4awe(ia, ib)
         torch.cuda.synchronize()
         del ia, ib
         rp, ci, v = ozk_inputs.poisson_7pt_csr(256)
@@ -675,13 +677,32 @@ def measure_fp4(reps: int, stream) -> dict:
            "fp4_tflops_gemm": round(fp4_flops / (t - tp) / 1e9, 1),
            "frac_fp4_peak_gemm": round(fp4_flops / (t - tp) / 1e9 / PEAK_FP4_TFLOPS, 4),
            "int8_equiv_tops": round(2.0 * n ** 3 / t / 1e9, 1)}
+    # the 6-product engine (weights 1, 29, 37; limb and pairwise-sum planes)
+    ws6 = torch.empty(ozk.ozk_int8gemm_fp4awe_workspace_size(n, n, n), dtype=torch.uint8,
+                      device=dev)
+    f6 = lambda: ozk.ozk_int8gemm_fp4awe(ia, ib, out=c, workspace=ws6)
+    f6()
+    t6 = _time_events(f6, reps, stream)
+    qa = ozk.ozk_fp4awe_pack(ia, 0)
+    qb = ozk.ozk_fp4awe_pack(ib, 1)
+    pack6 = lambda: (ozk.ozk_fp4awe_pack(ia, 0, planes=qa), ozk.ozk_fp4awe_pack(ib, 1, planes=qb))
+    pack6()
+    tp6 = _time_events(pack6, reps, stream)
+    fl6 = 6 * 2.0 * n * n * n
+    out["six_products"] = {
+        "what": "6 FP4 plane products (weights 1, 29, 37; limb and pairwise-sum planes)",
+        "ms": round(t6, 4), "pack_ms": round(tp6, 4), "gemm_ms_excl_pack": round(t6 - tp6, 4),
+        "fp4_tflops_gemm": round(fl6 / (t6 - tp6) / 1e9, 1),
+        "frac_fp4_peak_gemm": round(fl6 / (t6 - tp6) / 1e9 / PEAK_FP4_TFLOPS, 4),
+        "int8_equiv_tops": round(2.0 * n ** 3 / t6 / 1e9, 1),
+        "speedup_vs_nine": round(t / t6, 3)}
     try:
         torch._int_mm(ia, ib)
         ti = _time_events(lambda: torch._int_mm(ia, ib), reps, stream)
         out["vendor_int8_gemm"] = {"ms": round(ti, 4), "tops": round(2.0 * n ** 3 / ti / 1e9, 1)}
     except RuntimeError as exc:
         out["vendor_int8_gemm"] = {"error": str(exc)[:200]}
-    del ia, ib, c, ws, pa, pb
+    del ia, ib, c, ws, pa, pb, ws6, qa, qb
     torch.cuda.empty_cache()
     return out
 

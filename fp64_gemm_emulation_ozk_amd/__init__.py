@@ -25,6 +25,8 @@ __all__ = [
     "ozk_spmv_csr_workspace_size",
     "OZK_SCALING_MAX", "OZK_SCALING_NORM",
     "ozk_fp4limb_pack", "ozk_fp4limb_products", "ozk_int8gemm_fp4limb",
+    "ozk_fp4awe_line_bytes", "ozk_fp4awe_pack", "ozk_fp4awe_products", "ozk_int8gemm_fp4awe",
+    "ozk_int8gemm_fp4awe_workspace_size",
     "ozk_dgemm_workspace_size", "ozk_dgemv_workspace_size",
     "ozk_int8gemm_fp4limb_workspace_size", "ozk_deconstruct_workspace_size",
 ]
@@ -75,6 +77,13 @@ _SIGNATURES = {
     "ozk_fp4limb_products": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _i64,
                                     _ptr]),
     "ozk_int8gemm_fp4limb_workspace_size": (_int, [_i64, _i64, _i64, _ptr]),
+    "ozk_fp4awe_line_bytes": (_i64, [_i64]),
+    "ozk_fp4awe_pack": (_int, [_ptr, _i64, _i64, _i64, _int, _ptr, _i64, _ptr]),
+    "ozk_fp4awe_products": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _i64,
+                                   _ptr]),
+    "ozk_int8gemm_fp4awe_workspace_size": (_int, [_i64, _i64, _i64, _ptr]),
+    "ozk_int8gemm_fp4awe": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr,
+                                   _size, _ptr]),
     "ozk_int8gemm_fp4limb": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr,
                                     _size, _ptr]),
 }
@@ -472,6 +481,62 @@ def ozk_int8gemm_fp4limb(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | N
     if workspace is None:
         workspace = _workspace(ozk_int8gemm_fp4limb_workspace_size(m, n, k), a.device)
     _call("ozk_int8gemm_fp4limb", m, n, k, _dev_ptr(a), _ld(a), _dev_ptr(b), _ld(b),
+          _dev_ptr(out), _ld(out), _dev_ptr(workspace), workspace.numel(),
+          _stream(stream, out, workspace))
+    return out
+
+
+# ------------------------------------------------------------ 6-product FP4 INT8 GEMM
+def ozk_fp4awe_line_bytes(k: int) -> int:
+    return library().ozk_fp4awe_line_bytes(k)
+
+
+def ozk_int8gemm_fp4awe_workspace_size(m: int, n: int, k: int) -> int:
+    return _size_query("ozk_int8gemm_fp4awe_workspace_size", m, n, k)
+
+
+def ozk_fp4awe_pack(x: torch.Tensor, axis: int, planes: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """Packed 6-product planes uint8 [lines][line_bytes] of an int8 matrix (axis 0: rows
+    are lines, K = columns; axis 1: columns are lines, K = rows)."""
+    _check(x, torch.int8, "x")
+    rows, cols = x.shape
+    kdim = cols if axis == 0 else rows
+    lines = rows if axis == 0 else cols
+    if planes is None:
+        planes = torch.empty((lines, ozk_fp4awe_line_bytes(max(kdim, 1))), dtype=torch.uint8,
+                             device=x.device)
+    _call("ozk_fp4awe_pack", _dev_ptr(x), rows, cols, _ld(x), axis, _dev_ptr(planes),
+          planes.stride(0), _stream(stream, planes))
+    return planes
+
+
+def ozk_fp4awe_products(planes_a: torch.Tensor, planes_b: torch.Tensor, k: int,
+                        out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The 6 exact plane products int32 [6][m][n] from packed lines of A and B."""
+    _check(planes_a, torch.uint8, "planes_a")
+    _check(planes_b, torch.uint8, "planes_b")
+    m, n = planes_a.shape[0], planes_b.shape[0]
+    if out is None:
+        out = torch.empty((6, m, n), dtype=torch.int32, device=planes_a.device)
+    _call("ozk_fp4awe_products", m, n, k, _dev_ptr(planes_a), planes_a.stride(0),
+          _dev_ptr(planes_b), planes_b.stride(0), _dev_ptr(out), out.stride(1), out.stride(0),
+          _stream(stream, out))
+    return out
+
+
+def ozk_int8gemm_fp4awe(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Exact int32 C = A B for int8 A, B through 6 FP4 plane products."""
+    _check(a, torch.int8, "A")
+    _check(b, torch.int8, "B")
+    m, k = a.shape
+    n = b.shape[1]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.int32, device=a.device)
+    if workspace is None:
+        workspace = _workspace(ozk_int8gemm_fp4awe_workspace_size(m, n, k), a.device)
+    _call("ozk_int8gemm_fp4awe", m, n, k, _dev_ptr(a), _ld(a), _dev_ptr(b), _ld(b),
           _dev_ptr(out), _ld(out), _dev_ptr(workspace), workspace.numel(),
           _stream(stream, out, workspace))
     return out

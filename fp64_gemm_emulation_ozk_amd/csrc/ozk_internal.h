@@ -131,6 +131,18 @@ int launch_fp4_products(int64_t m, int64_t n, int64_t ldpb, const uint8_t* pa, i
 int launch_fp4_gemm(int64_t m, int64_t n, int64_t ldpb, const uint8_t* pa, int64_t stride_a,
                     const uint8_t* pb, int64_t stride_b, int32_t* c, int64_t ldc, hipStream_t s);
 
+// The 6-product FP4 engine (fp4awe.hip): bytes of one packed line over inner dimension k
+// (192 per K step of 64 codes), packer (axis 0: lines are rows of x, K = cols; axis 1:
+// lines are columns, K = rows), the 6 plane products (test path) and the fused GEMM.
+int64_t awe_line_bytes(int64_t k);
+int launch_awe_pack(const int8_t* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                    uint8_t* out, int64_t ld_line, hipStream_t s);
+int launch_awe_products(int64_t m, int64_t n, int64_t steps, const uint8_t* pa, int64_t lda,
+                        const uint8_t* pb, int64_t ldb, int32_t* out, int64_t ldo,
+                        int64_t stride_o, hipStream_t s);
+int launch_awe_gemm(int64_t m, int64_t n, int64_t steps, const uint8_t* pa, int64_t lda,
+                    const uint8_t* pb, int64_t ldb, int32_t* c, int64_t ldc, hipStream_t s);
+
 enum GemmEpilogue { kEpiProducts = 0, kEpiResidues = 1 };
 // ev_start / ev_stop (optional, both or neither): caller events the launch records its
 // start and end in (hipExtLaunchKernel), for timing the products inside a step.

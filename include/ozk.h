@@ -262,6 +262,41 @@ int ozk_int8gemm_fp4limb(int64_t m, int64_t n, int64_t k, const int8_t* A, int64
                          const int8_t* B, int64_t ldb, int32_t* C, int64_t ldc,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- 6-product FP4 INT8 GEMM
+ * [AWE] abstract: with free integer limb weights and stored planes that combine limbs, an
+ * INT8 x INT8 product takes 6 FP4 matrix products instead of 9.  Encoding used here: x =
+ * a0 + 29 a1 + 37 a2 with the limbs a_i and their pairwise sums a0+a1, a0+a2, a1+a2 all in
+ * S (each at most 6 in magnitude); of the triples that encode x, the one whose six plane
+ * values have the smallest largest magnitude, then sum of squares, then (a0, a1, a2)
+ * lexicographically.  C = A B = sum_t coef_t P_t over the 6 plane products, coef = (-65,
+ * -261, 259, 29, 37, 1073) (the three-term Karatsuba identity).
+ *
+ * Packed layout: one line per row of A (axis 0, K = cols) or column of B (axis 1, K =
+ * rows); K in steps of 64 codes, step s of a line at bytes 192 s .. 192 s + 191, plane t
+ * (a0, a1, a2, a0+a1, a0+a2, a1+a2) at byte 32 t of the step, value d stored as the e2m1
+ * code of d/2, two codes per byte with the even K index in the low nibble; codes past K
+ * are 0.  ozk_fp4awe_line_bytes(k) = 192 ceil(k / 64) is the smallest line stride.
+ *
+ * ozk_fp4awe_pack: planes[line * ld_line + ...] (device, 16-byte aligned), ld_line >=
+ *   ozk_fp4awe_line_bytes(K) and a multiple of 16; K <= OZK_MAX_K.
+ * ozk_fp4awe_products: the 6 exact plane products, products[t*stride_p + i*ldp_out + j] =
+ *   sum_h U_t(A)[i][h] V_t(B)[h][j] (int32), from packed lines of A (m lines, stride lda)
+ *   and B (n lines, stride ldb) over inner dimension k <= OZK_MAX_K.
+ * ozk_int8gemm_fp4awe: C = A B exactly in int32 (A m x k, B k x n int8 row-major), packing
+ *   both operands into the workspace (ozk_int8gemm_fp4awe_workspace_size bytes, 256-byte
+ *   aligned) and summing the 6 weighted plane products.  k <= OZK_MAX_K (fp32 partial
+ *   sums stay exact: each elementary product is at most 36). */
+int64_t ozk_fp4awe_line_bytes(int64_t k);
+int ozk_fp4awe_pack(const int8_t* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                    uint8_t* planes, int64_t ld_line, void* stream);
+int ozk_fp4awe_products(int64_t m, int64_t n, int64_t k, const uint8_t* planes_a, int64_t lda,
+                        const uint8_t* planes_b, int64_t ldb, int32_t* products,
+                        int64_t ldp_out, int64_t stride_p, void* stream);
+int ozk_int8gemm_fp4awe_workspace_size(int64_t m, int64_t n, int64_t k, size_t* bytes);
+int ozk_int8gemm_fp4awe(int64_t m, int64_t n, int64_t k, const int8_t* A, int64_t lda,
+                        const int8_t* B, int64_t ldb, int32_t* C, int64_t ldc, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------- measurement support
  * ozk_dgemm_ex_timed: ozk_dgemm_ex that also has the launch of the r residue products
  *   record its start and end in the caller's two hipEvent_t handles (gemm_start,
