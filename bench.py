@@ -985,7 +985,7 @@ def main() -> int:
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
                 "traffic": _traffic("gemm_i8_residues", digest),
-                "kernel": "gemm_i8_pairs_kernel<residues> (v_mfma_i32_32x32x32_i8)",
+                "kernel": "gemm_i8_pairs_kernel<residues> (v_mfma_i32_16x16x64_i8)",
                 "kernel_ms": round(gemm_ms, 4), "ops_per_launch": ops,
                 "ops_unit": "int8 multiply-adds x 2 (TOP/s reported in the TFLOP/s slot)",
                 "timed": "inside the timed steps, one HIP event pair per launch",

@@ -1,14 +1,16 @@
 // Exact int8 x int8 -> int32 matrix products, one per modulus, on the gfx950 MFMA
-// units (v_mfma_i32_32x32x32_i8).  [TME4] abstract: the tensor term of Ozaki scheme II;
+// units (v_mfma_i32_16x16x64_i8 in the persistent kernel, v_mfma_i32_32x32x32_i8 in the
+// one-tile-per-workgroup kernel).  [TME4] abstract: the tensor term of Ozaki scheme II;
 // [AWE] abstract: each product is an error-free integer matrix product.
 //
 // Operands are residue planes with K contiguous: A_l [m][kp], B_l [n][kp] (B already
 // transposed by the deconstruction), kp a multiple of 64 and zero-padded, so the K loop
 // has no tail.  |residue| <= 128 and kp <= 131072 keep every int32 sum exact.
 //
-// Two kernels share the tiling below: gemm_i8_pairs_kernel (K in steps of 128, at least two
-// of them: persistent, whole-cache-line loads, described above it) and gemm_i8_kernel (any
-// K that is a multiple of 64: one workgroup per tile, described here).
+// Two kernels share the workgroup tiling below: gemm_i8_pairs_kernel (K in steps of 128,
+// at least two of them: persistent, whole-cache-line loads, 16 x 16 x 64 MFMAs, described
+// above it) and gemm_i8_kernel (any K that is a multiple of 64: one workgroup per tile,
+// 32 x 32 x 32 MFMAs, described here).
 //
 // Tiling: workgroup tile 256 x 256 x 64, 512 threads = 8 waves, two per SIMD.  Waves
 // 0..3 own rows 0..127 of the tile, waves 4..7 rows 128..255; each wave a 128 x 64 block
@@ -406,12 +408,17 @@ __device__ __forceinline__ void store_residues_direct(
 // the 16 lanes of a fragment read (rows r .. r+15, one logical chunk) then cover all 64
 // banks.
 //
-// Per pair p (K bytes 128 p .. 128 p + 127) every wave runs four quarters of 8 MFMAs (K
-// sub-chunks of 32), reading the next quarter's fragments between them.  After quarter 2
-// the wave waits for its loads of pair p+1 and for its reads, and the workgroup barrier
-// makes pair p+1 complete and pair p fully read; quarter 3 then reads pair p+1's first
-// fragments and issues half of this wave's 8 loads of pair p+2 into pair p's buffer (one
-// after every second MFMA), quarter 0 of pair p+1 the other half.
+// Every wave's 128 x 64 outputs are 8 x 4 blocks of 16 x 16 on v_mfma_i32_16x16x64_i8
+// (32 accumulators of 4 registers; on random operands this shape sustains about 17 % more
+// operations per second under the board's power limit than 32 x 32 x 32).  Per pair p
+// (K bytes 128 p .. 128 p + 127) every wave runs four quarters of 16 MFMAs, (K half, row
+// half) = (0, 0), (0, 1), (1, 0), (1, 1), reading the next quarter's fragments between
+// them (a fragment: 16 rows x 64 K bytes, lane -> row lane % 16, 16-byte chunk lane / 16
+// of the K half; A and B the same).  After quarter 2 the wave waits for its loads of pair
+// p+1 and for its reads, and the workgroup barrier makes pair p+1 complete and pair p
+// fully read; quarter 3 then reads pair p+1's first fragments and issues half of this
+// wave's 8 loads of pair p+2 into pair p's buffer (one after every fourth MFMA), quarter
+// 0 of pair p+1 the other half.
 //
 // One workgroup per CU walks a fixed list of tiles.  Pair numbers run on across tiles:
 // the last two pairs of a tile load the next tile's pairs 0 and 1 (all of pair 1 before
@@ -427,6 +434,56 @@ __device__ __forceinline__ void store_residues_direct(
 constexpr int kPairRow = 128;                       // bytes per row of a pair stage
 constexpr int kPairBytes = (BM + BN) * kPairRow;    // 64 KiB
 
+// Residues of one 256 x 256 tile stored straight from the 16 x 16 accumulators.  The MFMA
+// runs with the B fragment first, so lane l of block (i, j) holds row 16 i + l % 16 and the
+// four consecutive columns 16 j + 4 (l / 16) + 0..3 in its 4 registers (one word once
+// packed to bytes).  For one row block the four lanes l % 16 + {0, 16, 32, 48} hold a
+// 4 x 4 matrix of words M[lane group][j]; a v_permlane32_swap and a v_permlane16_swap on
+// each of two word pairs transpose it, leaving lane group g with M[0..3][g], i.e. the 16
+// consecutive columns 16 g .. 16 g + 15: one 16-byte store per row block and lane.
+template <int NW>
+__device__ __forceinline__ void store_residues16(const v4i (&acc)[8][4], int64_t m, int64_t n,
+                                                 int64_t row0, int64_t col0, int grp, int wq,
+                                                 int lane, int mod, double inv,
+                                                 int8_t* __restrict__ o, int64_t ldo, bool full,
+                                                 int vec_out) {
+  auto emit = [&](auto byte_of) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = pack4b(byte_of(acc[i][j][0]), byte_of(acc[i][j][1]), byte_of(acc[i][j][2]),
+                      byte_of(acc[i][j][3]));
+      const auto r02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+      const auto r13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+      const auto x = __builtin_amdgcn_permlane16_swap(r02[0], r13[0], false, false);
+      const auto y = __builtin_amdgcn_permlane16_swap(r02[1], r13[1], false, false);
+      const uint4 v = make_uint4(x[0], x[1], y[0], y[1]);
+      const int64_t row = row0 + grp * 128 + 16 * i + (lane & 15);
+      const int64_t col = col0 + wq * 64 + 16 * (lane >> 4);
+      int8_t* dst = o + row * ldo + col;
+      if (full) {
+        *reinterpret_cast<uint4*>(dst) = v;
+      } else if (row < m) {
+        if (vec_out && col + 16 <= n) {
+          *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+          for (int u = 0; u < 16; ++u)
+            if (col + u < n) dst[u] = (int8_t)(wv[u >> 2] >> (8 * (u & 3)));
+        }
+      }
+    }
+  };
+  if (mod == 256) {
+    emit([](int v) { return (uint32_t)v; });
+  } else {
+    const uint32_t um = (uint32_t)mod;
+    emit([=](int v) { return residue_byte_odd(v, um, inv); });
+  }
+}
+
 template <int kEpi, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
     int64_t m, int64_t n, int64_t kp, const int8_t* __restrict__ pa, int64_t stride_a,
@@ -434,19 +491,19 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
     int64_t stride_o, int tiles_m, int tiles_n, int tiles, EpiModuli E, int vec_out) {
   __shared__ __attribute__((aligned(1024))) int8_t lds[2 * kPairBytes];
 
-  using WL = WaveLayout<NW>;
-  constexpr int TI = WL::TI, TJ = WL::TJ, kWaves = NW;
+  constexpr int kWaves = NW;
   constexpr int kRegions = kPairBytes / 1024;          // 64 regions of 8 rows x 128 B
   constexpr int kLoadsPerWave = kRegions / NW;         // 8 (NW = 8)
   constexpr int kHalf = kLoadsPerWave / 2;
-  constexpr int kStores = kEpi == kEpiProducts ? 4 * TI * TJ : TI * TJ;  // per full tile
-  static_assert(WL::kMfmaHalf == kLoadsPerWave, "half the loads in each of two quarters");
+  constexpr int TI = 8, TJ = 4;                        // 16 x 16 blocks of a wave
+  constexpr int kStores = kEpi == kEpiProducts ? TI * TJ : TI;  // per full tile
   static_assert(NW == 8 && kStores <= 63, "regions 0..31 are A; the store count fits vmcnt");
+  static_assert(kLoadsPerWave == 8, "4 loads in each of two quarters of 16 MFMAs");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int grp = __builtin_amdgcn_readfirstlane(wave / (NW / 2));
-  const int wq = __builtin_amdgcn_readfirstlane(wave % (NW / 2));
+  const int grp = __builtin_amdgcn_readfirstlane(wave / (NW / 2));   // rows grp * 128
+  const int wq = __builtin_amdgcn_readfirstlane(wave % (NW / 2));    // columns wq * 64
 
   // This workgroup's tiles: first, first + step, ... below last (all uniform).
   const int G = gridDim.x;
@@ -512,42 +569,57 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
                 wave_lds + (uint32_t)buf * kPairBytes + q * (kWaves * 1024));
   };
 
-  v16i acc[TI][TJ];
+  v4i acc[TI][TJ];
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = 0;
 
-  // Fragments of quarter qq: lane holds row (lane & 31) of a 32-row block and the 16
-  // bytes of logical chunk 2 qq + (lane >> 5); A and B use the same K map.
-  const int frow = lane & 31;
-  const int fchunk = lane >> 5;
-  int offa[TI], offb[TJ];
+  // Fragment rows: A block i at tile row grp * 128 + 16 i + lane % 16, B block j at tile
+  // column wq * 64 + 16 j + lane % 16; K half kh holds logical chunks 4 kh .. 4 kh + 3.
+  // Blocks start at multiples of 16 rows, so the row swizzle is (lane % 16) / 2 for all.
+  const int frow = lane & 15;
+  const int fchunk = lane >> 4;
+  const int sw = frow >> 1;
+  // per K half: this lane's row of A block 0 and of B block 0 plus its swizzled chunk;
+  // other blocks are 16 rows (2 KiB) further, a constant offset
+  const int oa0 = (grp * 128 + frow) * kPairRow + (((0 + fchunk) ^ sw) << 4);
+  const int oa1 = (grp * 128 + frow) * kPairRow + (((4 + fchunk) ^ sw) << 4);
+  const int ob0 = BM * kPairRow + (wq * 64 + frow) * kPairRow + (((0 + fchunk) ^ sw) << 4);
+  const int ob1 = BM * kPairRow + (wq * 64 + frow) * kPairRow + (((4 + fchunk) ^ sw) << 4);
+  v4i fa[2][4], fb[2][4];
+  auto read_a = [&](int set, const int8_t* st, int kh, int rh, int idx) {
+    fa[set][idx] = *reinterpret_cast<const v4i*>(st + (kh ? oa1 : oa0) +
+                                                 (4 * rh + idx) * 16 * kPairRow);
+  };
+  auto read_b = [&](int set, const int8_t* st, int kh, int idx) {
+    fb[set][idx] = *reinterpret_cast<const v4i*>(st + (kh ? ob1 : ob0) + idx * 16 * kPairRow);
+  };
+  // 16 MFMAs of row half rh on A set `as` and B set `bs`; between them the reads of the
+  // next quarter (mode 0: A (kh, rh 1) into set 1; mode 1: A (1, 0) into set 0 and B (1)
+  // into set 1; mode 2: A (1, 1) into set 1; mode 3: A (0, 0) and B (0) of stage `rs` into
+  // sets 0), and loads l0 .. l1-1 of pair lp (next tile if `next`) into buffer lb after
+  // every fourth MFMA.
+  auto quarter = [&](int as, int bs, int rh, int mode, const int8_t* rs, bool next, int lp,
+                     int lb, int l0, int l1) {
 #pragma unroll
-  for (int i = 0; i < TI; ++i) offa[i] = (grp * 128 + i * 32 + frow) * kPairRow;
-#pragma unroll
-  for (int j = 0; j < TJ; ++j) offb[j] = BM * kPairRow + (wq * WL::WN + j * 32 + frow) * kPairRow;
-  const int sw = (frow >> 1) & 7;  // row swizzle (the same for every block: 16 | block rows)
-  v4i fa[2][TI], fb[2][TJ];
-  // 8 MFMAs on fragment set `cur`, the reads of quarter qq of stage st into the other set
-  // between them, and loads l0 .. l1-1 of pair `lp` (of the next tile if `next`) into
-  // buffer `lb` after every second MFMA.
-  auto quarter = [&](int cur_set, const int8_t* st, int qq, bool next, int lp, int lb, int l0,
-                     int l1) {
-    const int c = ((2 * qq + fchunk) ^ sw) << 4;
-#pragma unroll
-    for (int idx = 0; idx < WL::kMfmaHalf; ++idx) {
-      const int i = idx / TJ, j = idx % TJ;
-      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[cur_set][j], fa[cur_set][i],
-                                                        acc[i][j], 0, 0, 0);
-      if (idx < TI)
-        fa[cur_set ^ 1][idx] = *reinterpret_cast<const v4i*>(st + offa[idx] + c);
-      else if (idx < TI + TJ)
-        fb[cur_set ^ 1][idx - TI] = *reinterpret_cast<const v4i*>(st + offb[idx - TI] + c);
-      if ((idx & 1) == 1) {
-        const int q = l0 + (idx >> 1);
+    for (int idx = 0; idx < 16; ++idx) {
+      const int i = idx >> 2, j = idx & 3;
+      acc[4 * rh + i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb[bs][j], fa[as][i],
+                                                                 acc[4 * rh + i][j], 0, 0, 0);
+      if (idx < 4) {
+        if (mode == 0) read_a(1, rs, 0, 1, idx);
+        else if (mode == 1) read_a(0, rs, 1, 0, idx);
+        else if (mode == 2) read_a(1, rs, 1, 1, idx);
+        else read_a(0, rs, 0, 0, idx);
+      } else if (idx < 8) {
+        if (mode == 1) read_b(1, rs, 1, idx - 4);
+        else if (mode == 3) read_b(0, rs, 0, idx - 4);
+      }
+      if ((idx & 3) == 3) {
+        const int q = l0 + (idx >> 2);
         if (q < l1) load(next, lp, lb, q);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -561,12 +633,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
   for (int q = 0; q < kLoadsPerWave; ++q) load(false, 1, 1, q);
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerWave) : "memory");
   wg_barrier();
-  {
-    const int c = ((0 + fchunk) ^ sw) << 4;
 #pragma unroll
-    for (int i = 0; i < TI; ++i) fa[0][i] = *reinterpret_cast<const v4i*>(lds + offa[i] + c);
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) fb[0][j] = *reinterpret_cast<const v4i*>(lds + offb[j] + c);
+  for (int idx = 0; idx < 4; ++idx) {
+    read_a(0, lds, 0, 0, idx);
+    read_b(0, lds, 0, idx);
   }
   int par = 0;                 // LDS buffer of the current tile's pair 0
   bool stores_pending = false; // the previous tile's epilogue issued exactly kStores stores
@@ -583,9 +653,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
       // quarter 0: the second half of pair p+1, the next tile's pair 0 in the last pair
       // (pair 1 of every tile is issued whole before its pair 0 is used)
       const bool q0_loads = p > 0 && (!last || has_next);
-      quarter(0, st, 1, last, last ? 0 : p + 1, b1, kHalf, q0_loads ? kLoadsPerWave : kHalf);
-      quarter(1, st, 2, false, 0, 0, 0, 0);
-      quarter(0, st, 3, false, 0, 0, 0, 0);
+      quarter(0, 0, 0, 0, st, last, last ? 0 : p + 1, b1, kHalf,
+              q0_loads ? kLoadsPerWave : kHalf);
+      quarter(1, 0, 1, 1, st, false, 0, 0, 0, 0);
+      quarter(0, 1, 0, 2, st, false, 0, 0, 0, 0);
       // pair p+1 has landed (this wave's loads; the barrier covers the others) and every
       // wave holds its quarter-3 fragments of pair p.  In pair 0 only the previous
       // epilogue's stores may be issued after pair 1's loads.
@@ -602,44 +673,41 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
       const bool wrap = p + 2 >= np;     // pair p+2 belongs to the next tile
       const bool q3_loads = !wrap || has_next;
       const int8_t* sn = last && !has_next ? st : lds + b1 * kPairBytes;
-      quarter(1, sn, 0, wrap, wrap ? p + 2 - np : p + 2, b0, 0, q3_loads ? kHalf : 0);
+      quarter(1, 1, 1, 3, sn, wrap, wrap ? p + 2 - np : p + 2, b0, 0, q3_loads ? kHalf : 0);
       if (last && has_next) {
 #pragma unroll
         for (int q = kHalf; q < kLoadsPerWave; ++q) load(true, 1, b0, q);
       }
     }
-  // Epilogue of tile `cur`: exactly kStores stores per wave when the tile is full.
+    // Epilogue of tile `cur`: exactly kStores stores per wave when the tile is full.
     const bool full = vec_out && cur.row0 + BM <= m && cur.col0 + BN <= n;
     if (kEpi == kEpiProducts) {
+      // lane l of block (i, j): row 16 i + l % 16, columns 16 j + 4 (l / 16) + 0..3
       int32_t* o = reinterpret_cast<int32_t*>(out) + cur.l * stride_o;
-      const int64_t wrow0 = cur.row0 + grp * 128, wcol0 = cur.col0 + wq * WL::WN;
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const int64_t row = wrow0 + i * 32 + (lane & 31);
+        const int64_t row = cur.row0 + grp * 128 + 16 * i + (lane & 15);
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int64_t col = wcol0 + j * 32 + 8 * q + 4 * (lane >> 5);
-            int32_t* dst = o + row * ldo + col;
-            const v4i v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                           acc[i][j][4 * q + 3]};
-            if (full) {
+        for (int j = 0; j < TJ; ++j) {
+          const int64_t col = cur.col0 + wq * 64 + 16 * j + 4 * (lane >> 4);
+          int32_t* dst = o + row * ldo + col;
+          const v4i v = acc[i][j];
+          if (full) {
+            *reinterpret_cast<v4i*>(dst) = v;
+          } else if (row < m) {
+            if (vec_out && col + 4 <= n) {
               *reinterpret_cast<v4i*>(dst) = v;
-            } else if (row < m) {
-              if (vec_out && col + 4 <= n) {
-                *reinterpret_cast<v4i*>(dst) = v;
-              } else {
-                for (int u = 0; u < 4; ++u)
-                  if (col + u < n) dst[u] = v[u];
-              }
+            } else {
+              for (int u = 0; u < 4; ++u)
+                if (col + u < n) dst[u] = v[u];
             }
           }
+        }
       }
     } else {
-      store_residues_direct<NW>(acc, m, n, cur.row0, cur.col0, grp, wq, lane, E.mod[cur.l],
-                                E.inv[cur.l], reinterpret_cast<int8_t*>(out) + cur.l * stride_o,
-                                ldo, full, vec_out);
+      store_residues16<NW>(acc, m, n, cur.row0, cur.col0, grp, wq, lane, E.mod[cur.l],
+                           E.inv[cur.l], reinterpret_cast<int8_t*>(out) + cur.l * stride_o, ldo,
+                           full, vec_out);
     }
     if (!has_next) break;
 #pragma unroll
@@ -647,7 +715,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+        for (int v = 0; v < 4; ++v) acc[i][j][v] = 0;
     stores_pending = full;
     par = (par + np) & 1;
     t = t_next;
