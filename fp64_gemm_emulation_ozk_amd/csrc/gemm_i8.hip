@@ -416,22 +416,28 @@ __device__ __forceinline__ void store_residues_direct(
 // them (a fragment: 16 rows x 64 K bytes, lane -> row lane % 16, 16-byte chunk lane / 16
 // of the K half; A and B the same).  After quarter 2 the wave waits for its loads of pair
 // p+1 and for its reads, and the workgroup barrier makes pair p+1 complete and pair p
-// fully read; quarter 3 then reads pair p+1's first fragments and issues half of this
-// wave's 8 loads of pair p+2 into pair p's buffer (one after every fourth MFMA), quarter
-// 0 of pair p+1 the other half.
+// fully read; quarter 3 then reads pair p+1's first fragments and issues all 8 of this
+// wave's loads of pair p+2 into pair p's buffer (one after every second MFMA), so every
+// load has three quarters to land before its wait.
 //
 // One workgroup per CU walks a fixed list of tiles.  Pair numbers run on across tiles:
-// the last two pairs of a tile load the next tile's pairs 0 and 1 (all of pair 1 before
-// the epilogue), and its last quarter reads the next tile's first fragments, so the
-// epilogue (residues stored from registers) overlaps those loads, and the wait for pair
-// 1 after the next tile's first three quarters lets the epilogue's stores stay in flight
-// (vector memory operations count down in issue order, so vmcnt(number of stores) covers
-// every load issued before them).
-// Tiles are dealt XCD by XCD (the hardware deals workgroups out round-robin over the 8
-// XCDs): the workgroups of one XCD take consecutive tiles of one contiguous share, in
-// groups of kGroupM tile rows, so the tiles in flight on an XCD share A rows and B columns
-// in its L2.
+// the last two pairs of a tile load the next tile's pairs 0 and 1 (both before the
+// epilogue), and its last quarter reads the next tile's first fragments, so the epilogue
+// (residues stored from registers) overlaps those loads, and the wait for pair 1 after
+// the next tile's first three quarters lets the epilogue's stores stay in flight (vector
+// memory operations count down in issue order, so vmcnt(number of stores) covers every
+// load issued before them).
+// Tile order and placement: the kernel runs under the board's power limit, so fewer bytes
+// fetched from HBM per product is time saved.  The launch has G workgroups (one per CU,
+// G a multiple of 8); round j is the G consecutive tiles G j .. G j + G - 1 of the order
+// (modulus, groups of kPairGroupM = 8 tile rows, column, row in group), and the G / 8
+// workgroups of one XCD (the hardware deals workgroups out round-robin over the 8 XCDs)
+// take one contiguous run of it: 8 tile rows x 4 tile columns at the 8192 x 8192 shape,
+// 12 panels of A and B for 32 tiles in that XCD's L2.  All XCDs work on the same modulus
+// and the same 8 tile rows at once, so the A panels and (from one group of rows to the
+// next) the B panels they share come from the 256 MB last-level cache rather than HBM.
 constexpr int kPairRow = 128;                       // bytes per row of a pair stage
+constexpr int kPairGroupM = 8;                      // tile rows per group of the tile order
 constexpr int kPairBytes = (BM + BN) * kPairRow;    // 64 KiB
 
 // Residues of one 256 x 256 tile stored straight from the 16 x 16 accumulators.  The MFMA
@@ -494,34 +500,25 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
   constexpr int kWaves = NW;
   constexpr int kRegions = kPairBytes / 1024;          // 64 regions of 8 rows x 128 B
   constexpr int kLoadsPerWave = kRegions / NW;         // 8 (NW = 8)
-  constexpr int kHalf = kLoadsPerWave / 2;
   constexpr int TI = 8, TJ = 4;                        // 16 x 16 blocks of a wave
   constexpr int kStores = kEpi == kEpiProducts ? TI * TJ : TI;  // per full tile
   static_assert(NW == 8 && kStores <= 63, "regions 0..31 are A; the store count fits vmcnt");
-  static_assert(kLoadsPerWave == 8, "4 loads in each of two quarters of 16 MFMAs");
+  static_assert(kLoadsPerWave == 8, "8 loads in one quarter of 16 MFMAs");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int grp = __builtin_amdgcn_readfirstlane(wave / (NW / 2));   // rows grp * 128
   const int wq = __builtin_amdgcn_readfirstlane(wave % (NW / 2));    // columns wq * 64
 
-  // This workgroup's tiles: first, first + step, ... below last (all uniform).
+  // This workgroup's tiles: first, first + G, ... below tiles (all uniform).
   const int G = gridDim.x;
-  int t, t_end, step;
-  if (G % kXcds == 0) {
-    const int share = (tiles + kXcds - 1) / kXcds;
-    const int lo = (int)(blockIdx.x % kXcds) * share;
-    t = lo + (int)(blockIdx.x / kXcds);
-    t_end = lo + share < tiles ? lo + share : tiles;
-    step = G / kXcds;
-  } else {
-    t = blockIdx.x;
-    t_end = tiles;
-    step = G;
-  }
+  const int t_end = tiles;
+  const int step = G;
+  int t = G % kXcds == 0 ? (int)(blockIdx.x % kXcds) * (G / kXcds) + (int)(blockIdx.x / kXcds)
+                         : (int)blockIdx.x;
   if (t >= t_end) return;
 
-  // Tile -> (modulus, tile row, tile column), tile rows grouped by kGroupM.
+  // Tile -> (modulus, tile row, tile column), tile rows grouped by kPairGroupM.
   struct Tile {
     int l;
     int64_t row0, col0;
@@ -529,15 +526,15 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
     uint32_t voff[kLoadsPerWave];       // per-lane source offsets of the loads
   };
   const int per_mod = tiles_m * tiles_n;
-  const int per_group = kGroupM * tiles_n;
+  const int per_group = kPairGroupM * tiles_n;
   // Region rg = wave + NW q: rows 8 (rg % 32) .. +7 of A (q < 4) or B; lane i lands at
   // row 8 (rg % 32) + i / 8, physical chunk i % 8, which holds logical chunk
   // (i % 8) ^ ((row >> 1) & 7); rows past the matrix re-read its last row.
   auto make_tile = [&](int tt, Tile& d) {
     d.l = tt / per_mod;
     const int rem = tt - d.l * per_mod;
-    const int first_m = (rem / per_group) * kGroupM;
-    const int gsize = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+    const int first_m = (rem / per_group) * kPairGroupM;
+    const int gsize = tiles_m - first_m < kPairGroupM ? tiles_m - first_m : kPairGroupM;
     const int in_group = rem % per_group;
     d.row0 = (int64_t)(first_m + in_group % gsize) * BM;
     d.col0 = (int64_t)(in_group / gsize) * BN;
@@ -600,10 +597,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
   // 16 MFMAs of row half rh on A set `as` and B set `bs`; between them the reads of the
   // next quarter (mode 0: A (kh, rh 1) into set 1; mode 1: A (1, 0) into set 0 and B (1)
   // into set 1; mode 2: A (1, 1) into set 1; mode 3: A (0, 0) and B (0) of stage `rs` into
-  // sets 0), and loads l0 .. l1-1 of pair lp (next tile if `next`) into buffer lb after
-  // every fourth MFMA.
+  // sets 0), and loads 0 .. nl-1 of pair lp (next tile if `next`) into buffer lb, one
+  // after every second MFMA.
   auto quarter = [&](int as, int bs, int rh, int mode, const int8_t* rs, bool next, int lp,
-                     int lb, int l0, int l1) {
+                     int lb, int nl) {
 #pragma unroll
     for (int idx = 0; idx < 16; ++idx) {
       const int i = idx >> 2, j = idx & 3;
@@ -618,10 +615,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
         if (mode == 1) read_b(1, rs, 1, idx - 4);
         else if (mode == 3) read_b(0, rs, 0, idx - 4);
       }
-      if ((idx & 3) == 3) {
-        const int q = l0 + (idx >> 2);
-        if (q < l1) load(next, lp, lb, q);
-      }
+      if ((idx & 1) == 1 && (idx >> 1) < nl) load(next, lp, lb, idx >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -650,13 +644,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
       const int b1 = b0 ^ 1;             // pair p+1's buffer
       const int8_t* st = lds + b0 * kPairBytes;
       const bool last = p + 1 == np;
-      // quarter 0: the second half of pair p+1, the next tile's pair 0 in the last pair
-      // (pair 1 of every tile is issued whole before its pair 0 is used)
-      const bool q0_loads = p > 0 && (!last || has_next);
-      quarter(0, 0, 0, 0, st, last, last ? 0 : p + 1, b1, kHalf,
-              q0_loads ? kLoadsPerWave : kHalf);
-      quarter(1, 0, 1, 1, st, false, 0, 0, 0, 0);
-      quarter(0, 1, 0, 2, st, false, 0, 0, 0, 0);
+      quarter(0, 0, 0, 0, st, false, 0, 0, 0);
+      quarter(1, 0, 1, 1, st, false, 0, 0, 0);
+      quarter(0, 1, 0, 2, st, false, 0, 0, 0);
       // pair p+1 has landed (this wave's loads; the barrier covers the others) and every
       // wave holds its quarter-3 fragments of pair p.  In pair 0 only the previous
       // epilogue's stores may be issued after pair 1's loads.
@@ -668,16 +658,12 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
       wg_barrier();
       __builtin_amdgcn_sched_barrier(0);
       // quarter 3: the first fragments of pair p+1 (the next tile's pair 0 after the last
-      // pair; a harmless re-read of pair p after the last tile's), and the first half of
-      // pair p+2 into pair p's buffer, now free
+      // pair; a harmless re-read of pair p after the last tile's), and pair p+2 into pair
+      // p's buffer, now free
       const bool wrap = p + 2 >= np;     // pair p+2 belongs to the next tile
       const bool q3_loads = !wrap || has_next;
       const int8_t* sn = last && !has_next ? st : lds + b1 * kPairBytes;
-      quarter(1, 1, 1, 3, sn, wrap, wrap ? p + 2 - np : p + 2, b0, 0, q3_loads ? kHalf : 0);
-      if (last && has_next) {
-#pragma unroll
-        for (int q = kHalf; q < kLoadsPerWave; ++q) load(true, 1, b0, q);
-      }
+      quarter(1, 1, 1, 3, sn, wrap, wrap ? p + 2 - np : p + 2, b0, q3_loads ? kLoadsPerWave : 0);
     }
     // Epilogue of tile `cur`: exactly kStores stores per wave when the tile is full.
     const bool full = vec_out && cur.row0 + BM <= m && cur.col0 + BN <= n;
