@@ -907,6 +907,9 @@ def main() -> int:
                          "two rocprofv3 --pmc csv runs")
     ap.add_argument("--tme-counters", action="store_true",
                     help="only launch the kernels the time-model counter pass profiles")
+    ap.add_argument("--hold", type=float, metavar="SECONDS",
+                    help="run the timed step back to back for SECONDS and print its mean time "
+                         "(a steady load for reading the board's power and clocks with amd-smi)")
     ap.add_argument("--tme-summary", metavar="DIR",
                     help="write the time-model instruction counts from a rocprofv3 --pmc run")
     args = ap.parse_args()
@@ -947,6 +950,20 @@ def main() -> int:
     out = torch.empty((M, N), dtype=torch.float64, device=dev)
     ws = torch.empty(ozk.ozk_dgemm_workspace_size(M, N, K, r), dtype=torch.uint8, device=dev)
     step = lambda: ozk.ozk_dgemm_ex(da, db, r, rule, out=out, workspace=ws)
+
+    if args.hold:
+        step()
+        torch.cuda.synchronize()
+        print(f"hold start: {M}^3 r={r} {rule} rule", flush=True)
+        t0, done = time.perf_counter(), 0
+        while time.perf_counter() - t0 < args.hold:
+            for _ in range(25):
+                step()
+            torch.cuda.synchronize()
+            done += 25
+        dt = time.perf_counter() - t0
+        print(f"hold done: {done} steps, {dt / done * 1e3:.3f} ms each", flush=True)
+        return 0
 
     for _ in range(args.warmup):
         step()
