@@ -9,13 +9,15 @@
 // rho mod 13 (so |d0|, |d1| <= 8 and d2 in {-1, 0, 1}); a digit d is stored as the e2m1
 // code of d/2, two codes per byte with the even K index in the low nibble.
 //
-// Products: v_mfma_scale_f32_32x32x64_f8f6f4 with both operands in e2m1 and both E8M0
+// Products: v_mfma_scale_f32 f8f6f4 MFMAs with both operands in e2m1 and both E8M0
 // block scales equal to 2^1, so every elementary product is the integer d_a d_b.  The 9
 // digit products are summed per weight class w = da + db (5 fp32 accumulators).  Each
 // K element adds at most 128 in magnitude to any class (class 1: |d0 d1| + |d1 d0|), so
 // for K <= 131071 every partial sum is an integer below 2^24 and fp32 holds it exactly;
 // the classes are then converted to integers and combined with weights 1, 13, 169, 2197,
 // 28561 in wrap-around 32-bit arithmetic (the exact result fits int32: |C| <= 2^14 K).
+#include <type_traits>
+
 #include "lds_dma.h"
 #include "ozk_internal.h"
 
@@ -149,6 +151,17 @@ __device__ __forceinline__ v16f mfma_fp4(const v4i& a, const v4i& b, const v16f&
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, 0x80, 0, 0x80);
 }
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// The same on v_mfma_scale_f32_16x16x128_f8f6f4: lane (row lane % 16, chunk lane / 16)
+// holds 32 codes of its row, A and B alike; lane l of the result holds column l % 16,
+// rows 4 (l / 16) + 0..3.
+__device__ __forceinline__ v4f mfma_fp4_16(const v4i& a, const v4i& b, const v4f& c) {
+  const v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  const v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 4, 0, 0x80, 0, 0x80);
+}
+
 // ------------------------------------------------------------------ 9 products (test path)
 // One wave per 32 x 32 output block; fragments straight from global memory.  Lane
 // (row = lane & 31, half = lane >> 5) supplies the 16 bytes (32 codes) at byte offset
@@ -193,21 +206,24 @@ __global__ __launch_bounds__(64) void limb_products_kernel(
 
 // ------------------------------------------------------------------ fused weighted GEMM
 // Workgroup tile 128 x 128, K step 128 codes (64 bytes per row per digit plane), 512
-// threads = 8 waves in 2 x 4, each wave 64 x 32 = 2 MFMA row blocks x 5 weight classes
-// (160 accumulator registers).  The three digit planes of A and of B (48 KiB per K step)
-// are loaded straight into a 3-stage LDS ring by global_load_lds_dwordx4, two K steps
-// ahead; every load instruction covers 16 rows x 64 bytes (16 lines, where 32-byte row
-// pieces would touch 32 lines for the same kilobyte).  LDS rows are 64 bytes with the
-// four 16-byte chunks XOR-swizzled by (row >> 2) & 3, so the 16 lanes of a fragment read
-// cover all 64 banks.  A K step runs as four quarters of 9 MFMAs, (kk, row block) =
-// (0,0), (0,1), (1,0), (1,1), each reading the fragments of the next quarter between its
-// MFMAs; one barrier per step sits between quarters 1 and 2 and follows a wait for all of
-// this wave's loads (those of step t+1).  After it the loads of step t+2 (into the stage
-// of step t-1, whose last reads were in quarter 2 of step t-1; past the last step the last
-// step is loaded again) are issued between the MFMAs of quarter 2, from wave-uniform SGPR
-// bases plus a fixed lane offset; quarter 3 reads step t+1's first fragments.  Workgroups are dealt out XCD by XCD onto
-// contiguous runs of tiles grouped by 4 tile rows, so the tiles in flight on one XCD share
-// A rows and B columns in its L2.
+// threads = 8 waves in 2 x 4, each wave 64 x 32 outputs = 4 x 2 blocks of 16 x 16 on
+// v_mfma_scale_f32_16x16x128_f8f6f4 (one MFMA takes the whole K step; on random codes
+// this shape sustains about 10 % more operations under the board's power limit than
+// 32 x 32 x 64), each block with 5 weight-class accumulators (160 registers).  The three
+// digit planes of A and of B (48 KiB per K step) are loaded straight into a 3-stage LDS
+// ring by global_load_lds_dwordx4, two K steps ahead; every load instruction covers 16
+// rows x 64 bytes (16 lines, where 32-byte row pieces would touch 32 lines for the same
+// kilobyte).  LDS rows are 64 bytes with the four 16-byte chunks XOR-swizzled by
+// (row >> 2) & 3, so the 16 lanes of a fragment read (16 rows, one chunk) cover all 64
+// banks.  A K step runs as four quarters of 18 MFMAs, one per row block (both column
+// blocks, the 9 digit pairs, the column blocks alternating so that the MFMAs chaining on
+// one class accumulator stand four apart); quarters 0..2 read the next row block's A
+// fragments between their MFMAs.  After quarter 2 the wave waits for its loads (those of
+// step t+1) and its reads, and one barrier makes step t+1 complete and step t fully read;
+// quarter 3 then issues the 6 loads of step t+2 into the stage of step t-1 (past the last
+// step the last step is loaded again) and reads step t+1's first A row block and both B
+// blocks.  Workgroups are dealt out XCD by XCD onto contiguous runs of tiles grouped by 4
+// tile rows, so the tiles in flight on one XCD share A rows and B columns in its L2.
 constexpr int FBM = 128, FBN = 128, FROW = 64;  // bytes per row per plane per K step
 constexpr int kFThreads = 512;
 constexpr int kFPlane = 128 * FROW;              // 8 KiB: one digit plane of A or B
@@ -267,27 +283,29 @@ __global__ __launch_bounds__(kFThreads, 1) void fp4_gemm_kernel(
       dma16_sbase(voff_b, base_b + (uint64_t)((q - 3) * stride_b) + kb, dst);
   };
 
-  v16f acc[2][5];
+  v4f acc[4][2][5];   // [row block][column block][weight class]
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int w = 0; w < 5; ++w)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][w][v] = 0.0f;
+      for (int w = 0; w < 5; ++w)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[i][j][w][v] = 0.0f;
 
-  // Fragments: lane (row = lane & 31, half = lane >> 5) of a 32-row block; 16 bytes =
-  // 32 codes at K offset 64 kk + 32 half within the step, the same map for A and B.
-  const int frow = lane & 31, fhalf = lane >> 5;
-  auto read_a = [&](v4i& x, int t, int rbk, int d, int kk) {
+  // Fragments of a 16-row block: lane (row lane & 15, chunk lane >> 4) = 32 codes of the
+  // step's 128, the same map for A and B.
+  const int frow = lane & 15, fch = lane >> 4;
+  auto read_a = [&](v4i& x, int t, int rbk, int d) {
     x = *reinterpret_cast<const v4i*>(lds + (t % kFStages) * kStage + d * kFPlane +
-                                      fswz(wr * 64 + rbk * 32 + frow, 2 * kk + fhalf));
+                                      fswz(wr * 64 + rbk * 16 + frow, fch));
   };
-  auto read_b = [&](v4i& x, int t, int d, int kk) {
+  auto read_b = [&](v4i& x, int t, int cbk, int d) {
     x = *reinterpret_cast<const v4i*>(lds + (t % kFStages) * kStage + (3 + d) * kFPlane +
-                                      fswz(wc * 32 + frow, 2 * kk + fhalf));
+                                      fswz(wc * 32 + cbk * 16 + frow, fch));
   };
 
-  v4i fa[2][3], fb[2][3];
+  v4i fa[2][3], fb[2][2][3];   // fa[set][digit]; fb[set][col block][digit]
 #pragma unroll
   for (int q = 0; q < 6; ++q) issue_one(q, 0, 0);
   if (nk > 1) {
@@ -300,81 +318,73 @@ __global__ __launch_bounds__(kFThreads, 1) void fp4_gemm_kernel(
   __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int d = 0; d < 3; ++d) {
-    read_a(fa[0][d], 0, 0, d, 0);
-    read_b(fb[0][d], 0, d, 0);
+    read_a(fa[0][d], 0, 0, d);
+    read_b(fb[0][0][d], 0, 0, d);
+    read_b(fb[0][1][d], 0, 1, d);
   }
-  for (int t = 0; t < nk; ++t) {
+  // 18 MFMAs of row block i (A set as, B set bs); after MFMA idx, optional reads and loads.
+  auto quarter = [&](int i, int as, int bs, auto&& after) {
+#pragma unroll
+    for (int idx = 0; idx < 18; ++idx) {
+      const int j = idx & 1, da = (idx >> 1) / 3, db = (idx >> 1) % 3;
+      acc[i][j][da + db] = mfma_fp4_16(fa[as][da], fb[bs][j][db], acc[i][j][da + db]);
+      after(idx);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // One K step; `s` (the B set of step t, t & 1) is a compile-time constant.  Quarters
+  // 0..2 (row blocks 0..2) read the next row block's A fragments into the other A set.
+  auto kstep = [&](int t, auto s_tag) {
+    constexpr int s = decltype(s_tag)::value;
     __builtin_amdgcn_sched_barrier(0);
-    // Quarter 0 (kk 0, row block 0); reads A (kk 0, row block 1).
-#pragma unroll
-    for (int idx = 0; idx < 9; ++idx) {
-      const int da = idx / 3, db = idx % 3;
-      acc[0][da + db] = mfma_fp4(fa[0][da], fb[0][db], acc[0][da + db]);
-      if (idx % 3 == 0) read_a(fa[1][idx / 3], t, 1, idx / 3, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // Quarter 1 (kk 0, row block 1); reads A (kk 1, row block 0) and B (kk 1).
-#pragma unroll
-    for (int idx = 0; idx < 9; ++idx) {
-      const int da = idx / 3, db = idx % 3;
-      acc[1][da + db] = mfma_fp4(fa[1][da], fb[0][db], acc[1][da + db]);
-      if (idx < 3)
-        read_a(fa[0][idx], t, 0, idx, 1);
-      else if (idx < 6)
-        read_b(fb[1][idx - 3], t, idx - 3, 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // Every load of this wave (those of step t+1) complete; after the barrier step t+1
-    // is complete in LDS and every wave is past its reads of step t-1.
+    quarter(0, 0, s, [&](int idx) { if (idx % 6 == 0) read_a(fa[1][idx / 6], t, 1, idx / 6); });
+    quarter(1, 1, s, [&](int idx) { if (idx % 6 == 0) read_a(fa[0][idx / 6], t, 2, idx / 6); });
+    quarter(2, 0, s, [&](int idx) { if (idx % 6 == 0) read_a(fa[1][idx / 6], t, 3, idx / 6); });
+    // Every load of this wave (those of step t+1) and every read complete; after the
+    // barrier step t+1 is complete in LDS and every wave is done with step t's stage.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    const int tl = t + 2 < nk ? t + 2 : nk - 1;  // past the end: reload the last step
-    // Quarter 2 (kk 1, row block 0); reads A (kk 1, row block 1); the 6 loads of step t+2,
-    // after MFMAs 0, 1, 3, 4, 6, 7 (as early as the stage is free: the latency they must
-    // hide runs to the barrier of step t+1).
-#pragma unroll
-    for (int idx = 0; idx < 9; ++idx) {
-      const int da = idx / 3, db = idx % 3;
-      acc[0][da + db] = mfma_fp4(fa[0][da], fb[1][db], acc[0][da + db]);
-      if (idx % 3 == 0) {
-        read_a(fa[1][idx / 3], t, 1, idx / 3, 1);
-        issue_one(idx / 3, tl, t + 2);
-      } else if (idx % 3 == 1) {
-        issue_one(3 + idx / 3, tl, t + 2);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // Quarter 3 (kk 1, row block 1); reads step t+1's A (kk 0, row block 0) and B (kk 0).
+    const int tl = t + 2 < nk ? t + 2 : nk - 1;
     const int tn1 = t + 1 < nk ? t + 1 : t;  // past the last step: harmless re-read
-#pragma unroll
-    for (int idx = 0; idx < 9; ++idx) {
-      const int da = idx / 3, db = idx % 3;
-      acc[1][da + db] = mfma_fp4(fa[1][da], fb[1][db], acc[1][da + db]);
-      if (idx % 3 == 0) {
-        read_a(fa[0][idx / 3], tn1, 0, idx / 3, 0);
-      } else if (idx % 3 == 1) {
-        read_b(fb[0][idx / 3], tn1, idx / 3, 0);
+    // Quarter 3 (row block 3): the 6 loads of step t+2 after the even MFMAs, and step
+    // t+1's A row block 0 and both B blocks after the odd ones.
+    quarter(3, 1, s, [&](int idx) {
+      if (idx % 2 == 0 && idx < 12) issue_one(idx / 2, tl, t + 2);
+      if (idx % 2 == 1) {
+        const int r = idx / 2;
+        if (r < 3) read_a(fa[0][r], tn1, 0, r);
+        else if (r < 6) read_b(fb[s ^ 1][0][r - 3], tn1, 0, r - 3);
+        else read_b(fb[s ^ 1][1][r - 6], tn1, 1, r - 6);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    });
+  };
+  for (int t = 0; t < nk; t += 2) {
+    kstep(t, std::integral_constant<int, 0>{});
+    if (t + 1 < nk) kstep(t + 1, std::integral_constant<int, 1>{});
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  const int64_t col = col0 + wc * 32 + (lane & 31);
-  if (col >= n) return;
+  // lane l of block (i, j): column 16 j + l % 16, rows 16 i + 4 (l / 16) + 0..3; the
+  // classes are exact integers, combined in wrap-around 32-bit arithmetic.
   constexpr uint32_t kW[5] = {1u, 13u, 169u, 2197u, 28561u};
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < 2; ++j) {
+    const int64_t col = col0 + wc * 32 + j * 16 + (lane & 15);
+    if (col >= n) continue;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t row = row0 + wr * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (row >= m) continue;
-      uint32_t sum = 0;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int w = 0; w < 5; ++w) sum += kW[w] * (uint32_t)(int32_t)acc[i][w][v];
-      c[row * ldc + col] = (int32_t)sum;
-    }
+      for (int v = 0; v < 4; ++v) {
+        const int64_t row = row0 + wr * 64 + i * 16 + 4 * (lane >> 4) + v;
+        if (row >= m) continue;
+        uint32_t sum = 0;
+#pragma unroll
+        for (int w = 0; w < 5; ++w) sum += kW[w] * (uint32_t)(int32_t)acc[i][j][w][v];
+        c[row * ldc + col] = (int32_t)sum;
+      }
+  }
 }
 
 }  // namespace
