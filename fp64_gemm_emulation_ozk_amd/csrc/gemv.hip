@@ -129,8 +129,13 @@ __global__ __launch_bounds__(256) void gemv_stored_kernel(
 // kq = lane >> 4) loads the 8 fp64 values K = 32 c + 8 kq .. +7 of its row, scales and
 // rounds them (row exponent from exps), turns them into 8 residue bytes per modulus and
 // issues one MFMA per modulus and column tile against the X residues staged in LDS.  The
-// next step's A values and X residues are loaded into registers before this step's
-// arithmetic; the X residues go to LDS after it.
+// next step's X residues are loaded into registers before this step's arithmetic and go
+// to LDS after it.  A is loaded kPF steps ahead into a ring of registers.  When the rows
+// are 16-byte aligned and k is a multiple of 32 (every K step below k is whole), every
+// load of the loop is issued unconditionally from addresses clamped into A and X, in one
+// fixed order per step, so the compiler's waits count exactly the loads a step needs;
+// steps past k and rows holding Inf/NaN feed zeros.  Otherwise the loads are guarded and
+// the waits drain every load in flight (same results, slower).
 //
 // Operand layout of the 16 x 16 x 32 instruction: lane supplies K = 8 (lane >> 4) .. +7 of
 // row (A) or column (B) lane & 15; the accumulator holds rows 4 (lane >> 4) .. +3 of
@@ -154,12 +159,13 @@ constexpr int kFlyThreads = 64 * kFlyWaves;
 constexpr int kFlyRows = 16 * kFlyWaves;     // rows per workgroup
 constexpr int kXsPitch = 48;                 // bytes per staged X column (32 used)
 
-template <bool kWide, int L0, int NR, int CT>
+template <bool kWide, int L0, int NR, int CT, bool kFast>
 __global__ __launch_bounds__(kFlyThreads, 1) void gemv_fly_kernel(
     const double* __restrict__ a, int64_t m, int64_t k, int64_t lda,
     const int32_t* __restrict__ exps, const int8_t* __restrict__ xp, int64_t ldp,
     int64_t x_stride, int nrhs, int8_t* __restrict__ res, int64_t res_stride, int vec) {
   constexpr int l0 = L0;
+  constexpr int kPF = !kFast ? 2 : NR * CT >= 30 ? 3 : 4;   // A steps in flight (registers)
   __shared__ __attribute__((aligned(16))) int8_t xs[2][NR][32][kXsPitch];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -180,27 +186,40 @@ __global__ __launch_bounds__(kFlyThreads, 1) void gemv_fly_kernel(
     for (int t = 0; t < CT; ++t) acc[q][t] = v4i{0, 0, 0, 0};
 
   const int64_t nc = ldp / 32;
+  const int64_t nc_k = (k + 31) / 32;   // K steps holding elements of A
+  const bool any_bad = __ballot(bad) != 0;
   // X staging: NR moduli x 32 columns x 32 bytes = NR * 64 chunks of 16 bytes.
   constexpr int kXL = (NR * 64 + kFlyThreads - 1) / kFlyThreads;   // chunks per thread
+  // Every thread loads its chunks (indexes past the last chunk re-read it); only the
+  // owners store them.
   auto fetch_x = [&](v4i (&xr)[kXL], int64_t c) {
 #pragma unroll
     for (int u = 0; u < kXL; ++u) {
-      const int idx = tid + kFlyThreads * u;
-      if (idx < NR * 64) {
-        const int q = idx >> 6;
-        int col = (idx >> 1) & 31;
-        col = col < nrhs ? col : nrhs - 1;
-        xr[u] = *reinterpret_cast<const v4i*>(xp + (int64_t)(l0 + q) * x_stride + col * ldp +
-                                              c * 32 + 16 * (idx & 1));
-      }
+      int idx = tid + kFlyThreads * u;
+      idx = idx < NR * 64 ? idx : NR * 64 - 1;
+      const int q = idx >> 6;
+      int col = (idx >> 1) & 31;
+      col = col < nrhs ? col : nrhs - 1;
+      xr[u] = *reinterpret_cast<const v4i*>(xp + (int64_t)(l0 + q) * x_stride + col * ldp +
+                                            c * 32 + 16 * (idx & 1));
     }
   };
-  auto store_x = [&](const v4i (&xr)[kXL], int buf) {
+  auto store_x = [&](const v4i(&xr)[kXL], int buf) {
 #pragma unroll
     for (int u = 0; u < kXL; ++u) {
       const int idx = tid + kFlyThreads * u;
       if (idx < NR * 64)
         *reinterpret_cast<v4i*>(&xs[buf][idx >> 6][(idx >> 1) & 31][16 * (idx & 1)]) = xr[u];
+    }
+  };
+  // Fast path: step c clamped into the steps below k, no condition per lane.
+  auto load_a_fast = [&](double (&v)[8], int64_t c) {
+    const int64_t h0 = (c < nc_k ? c : nc_k - 1) * 32 + 8 * kq;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const double2 d = *reinterpret_cast<const double2*>(pa + h0 + 2 * u);
+      v[2 * u] = d.x;
+      v[2 * u + 1] = d.y;
     }
   };
   auto load_a = [&](double (&v)[8], int64_t c) {
@@ -218,71 +237,92 @@ __global__ __launch_bounds__(kFlyThreads, 1) void gemv_fly_kernel(
     }
   };
 
-  double cur[8], nxt[8];
   v4i xr[kXL];
-  load_a(cur, 0);
-  fetch_x(xr, 0);
-  store_x(xr, 0);
-  __syncthreads();
-  for (int64_t c = 0; c < nc; ++c) {
-    const int buf = (int)(c & 1);
-    if (c + 1 < nc) {
-      load_a(nxt, c + 1);
-      fetch_x(xr, c + 1);
+  // A ring of kPF steps: step c lives in va[c % kPF]; each step issues its X loads for step
+  // c + 1 first, then its arithmetic, then A's loads for step c + kPF.  kFast (chosen by the
+  // host): rows 16-byte aligned and k a multiple of 32.
+  {
+    double va[kPF][8];
+#pragma unroll
+    for (int i = 0; i < kPF; ++i) {
+      if (kFast)
+        load_a_fast(va[i], i);
+      else
+        load_a(va[i], i);
     }
-    Prepared p[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) p[u] = prepare_element<kWide>(cur[u], e);
-    // Narrow residues two elements at a time: the low 16 bits of a' (the same for every
-    // modulus) and of q = round(a' / m) of elements 2i, 2i+1 side by side, then one packed
-    // 16-bit multiply-add q (-m) + a' gives both residues modulo 2^16 (their low bytes are
-    // the residue bytes, as in residue_byte).
-    uint32_t vpair[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      vpair[i] = __builtin_amdgcn_perm(lo32(p[2 * i + 1].vm), lo32(p[2 * i].vm), 0x05040100u);
-    for_moduli<0, NR>([&](auto qc) {
-      constexpr int q = decltype(qc)::value;
-      constexpr int l = l0 + q;
-      uint32_t w0, w1;
-      if constexpr (l == 0) {
-        w0 = pack4(residue_byte_256(p[0]), residue_byte_256(p[1]), residue_byte_256(p[2]),
-                   residue_byte_256(p[3]));
-        w1 = pack4(residue_byte_256(p[4]), residue_byte_256(p[5]), residue_byte_256(p[6]),
-                   residue_byte_256(p[7]));
-      } else if constexpr (!kWide) {
-        constexpr double inv = kRns.inv[l];
-        constexpr uint16_t neg_m = (uint16_t)(0x10000 - kRns.moduli[l]);
-        constexpr double kMagicD = 6755399441055744.0;
-        uint32_t r2[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t qa = lo32(__builtin_fma(p[2 * i].v, inv, kMagicD));
-          const uint32_t qb = lo32(__builtin_fma(p[2 * i + 1].v, inv, kMagicD));
-          const u16x2 qp = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(qb, qa, 0x05040100u));
-          const u16x2 vp = __builtin_bit_cast(u16x2, vpair[i]);
-          r2[i] = __builtin_bit_cast(uint32_t, qp * u16x2{neg_m, neg_m} + vp);
-        }
-        w0 = __builtin_amdgcn_perm(r2[1], r2[0], 0x06040200u);
-        w1 = __builtin_amdgcn_perm(r2[3], r2[2], 0x06040200u);
-      } else {
-        constexpr double md = (double)kRns.moduli[l], inv = kRns.inv[l], c32 = kRns.c32[l];
-        w0 = pack4(residue_byte<kWide>(p[0], md, inv, c32), residue_byte<kWide>(p[1], md, inv, c32),
-                   residue_byte<kWide>(p[2], md, inv, c32), residue_byte<kWide>(p[3], md, inv, c32));
-        w1 = pack4(residue_byte<kWide>(p[4], md, inv, c32), residue_byte<kWide>(p[5], md, inv, c32),
-                   residue_byte<kWide>(p[6], md, inv, c32), residue_byte<kWide>(p[7], md, inv, c32));
-      }
-      const v1l frag = (v1l)(((uint64_t)w1 << 32) | w0);
-#pragma unroll
-      for (int t = 0; t < CT; ++t) {
-        const v1l xf = *reinterpret_cast<const v1l*>(&xs[buf][q][16 * t + (lane & 15)][8 * kq]);
-        acc[q][t] = __builtin_amdgcn_mfma_i32_16x16x32_i8(frag, xf, acc[q][t], 0, 0, 0);
-      }
-    });
-    if (c + 1 < nc) store_x(xr, buf ^ 1);  // buffer buf ^ 1 was last read before the barrier
+    fetch_x(xr, 0);
+    store_x(xr, 0);
     __syncthreads();
+    const int64_t ncr = (nc + kPF - 1) / kPF * kPF;
+    for (int64_t c0 = 0; c0 < ncr; c0 += kPF) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) cur[u] = nxt[u];
+      for (int ii = 0; ii < kPF; ++ii) {
+        const int64_t c = c0 + ii;
+        double(&cur)[8] = va[ii];
+        const int buf = (int)(c & 1);
+        if (c + 1 < nc) fetch_x(xr, c + 1);
+        if (c < nc) {
+          Prepared p[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            p[u] = prepare_element<kWide>(
+                kFast && (c >= nc_k || (any_bad && bad)) ? 0.0 : cur[u], e);
+          // Narrow residues two elements at a time: the low 16 bits of a' (the same for every
+          // modulus) and of q = round(a' / m) of elements 2i, 2i+1 side by side, then one packed
+          // 16-bit multiply-add q (-m) + a' gives both residues modulo 2^16 (their low bytes are
+          // the residue bytes, as in residue_byte).
+          uint32_t vpair[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            vpair[i] = __builtin_amdgcn_perm(lo32(p[2 * i + 1].vm), lo32(p[2 * i].vm), 0x05040100u);
+          for_moduli<0, NR>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            constexpr int l = l0 + q;
+            uint32_t w0, w1;
+            if constexpr (l == 0) {
+              w0 = pack4(residue_byte_256(p[0]), residue_byte_256(p[1]), residue_byte_256(p[2]),
+                         residue_byte_256(p[3]));
+              w1 = pack4(residue_byte_256(p[4]), residue_byte_256(p[5]), residue_byte_256(p[6]),
+                         residue_byte_256(p[7]));
+            } else if constexpr (!kWide) {
+              constexpr double inv = kRns.inv[l];
+              constexpr uint16_t neg_m = (uint16_t)(0x10000 - kRns.moduli[l]);
+              constexpr double kMagicD = 6755399441055744.0;
+              uint32_t r2[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const uint32_t qa = lo32(__builtin_fma(p[2 * i].v, inv, kMagicD));
+                const uint32_t qb = lo32(__builtin_fma(p[2 * i + 1].v, inv, kMagicD));
+                const u16x2 qp =
+                  __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(qb, qa, 0x05040100u));
+                const u16x2 vp = __builtin_bit_cast(u16x2, vpair[i]);
+                r2[i] = __builtin_bit_cast(uint32_t, qp * u16x2{neg_m, neg_m} + vp);
+              }
+              w0 = __builtin_amdgcn_perm(r2[1], r2[0], 0x06040200u);
+              w1 = __builtin_amdgcn_perm(r2[3], r2[2], 0x06040200u);
+            } else {
+              constexpr double md = (double)kRns.moduli[l], inv = kRns.inv[l], c32 = kRns.c32[l];
+              auto rb = [&](int u) { return residue_byte<kWide>(p[u], md, inv, c32); };
+              w0 = pack4(rb(0), rb(1), rb(2), rb(3));
+              w1 = pack4(rb(4), rb(5), rb(6), rb(7));
+            }
+            const v1l frag = (v1l)(((uint64_t)w1 << 32) | w0);
+#pragma unroll
+            for (int t = 0; t < CT; ++t) {
+              const v1l xf =
+                  *reinterpret_cast<const v1l*>(&xs[buf][q][16 * t + (lane & 15)][8 * kq]);
+              acc[q][t] = __builtin_amdgcn_mfma_i32_16x16x32_i8(frag, xf, acc[q][t], 0, 0, 0);
+            }
+          });
+        }
+        if (kFast)
+          load_a_fast(cur, c + kPF);
+        else
+          load_a(cur, c + kPF);
+        if (c + 1 < nc) store_x(xr, buf ^ 1);  // buffer buf ^ 1 was last read before the barrier
+        __syncthreads();
+      }
+    }
   }
   if (row0 >= m) return;
 #pragma unroll
@@ -313,17 +353,29 @@ GemvModuli gemv_moduli(int r) {
   return E;
 }
 
+template <bool kWide, int L0, int NR, int CT>
+void launch_fly_ct(dim3 grid, hipStream_t s, const double* a, int64_t m, int64_t k, int64_t lda,
+                   const int32_t* exps, const int8_t* xp, int64_t ldp, int64_t x_stride, int nrhs,
+                   int8_t* res, int64_t res_stride) {
+  const int vec = (reinterpret_cast<uintptr_t>(a) & 15) == 0 && (lda & 1) == 0;
+  if (vec && k % 32 == 0 && k > 0)
+    hipLaunchKernelGGL((gemv_fly_kernel<kWide, L0, NR, CT, true>), grid, dim3(kFlyThreads), 0, s,
+                       a, m, k, lda, exps, xp, ldp, x_stride, nrhs, res, res_stride, vec);
+  else
+    hipLaunchKernelGGL((gemv_fly_kernel<kWide, L0, NR, CT, false>), grid, dim3(kFlyThreads), 0, s,
+                       a, m, k, lda, exps, xp, ldp, x_stride, nrhs, res, res_stride, vec);
+}
+
 template <bool kWide, int L0, int NR>
 void launch_fly(dim3 grid, hipStream_t s, const double* a, int64_t m, int64_t k, int64_t lda,
                 const int32_t* exps, const int8_t* xp, int64_t ldp, int64_t x_stride, int nrhs,
                 int8_t* res, int64_t res_stride) {
-  const int vec = (reinterpret_cast<uintptr_t>(a) & 15) == 0 && (lda & 1) == 0;
   if (nrhs <= 16)
-    hipLaunchKernelGGL((gemv_fly_kernel<kWide, L0, NR, 1>), grid, dim3(kFlyThreads), 0, s, a, m,
-                       k, lda, exps, xp, ldp, x_stride, nrhs, res, res_stride, vec);
+    launch_fly_ct<kWide, L0, NR, 1>(grid, s, a, m, k, lda, exps, xp, ldp, x_stride, nrhs, res,
+                                    res_stride);
   else
-    hipLaunchKernelGGL((gemv_fly_kernel<kWide, L0, NR, 2>), grid, dim3(kFlyThreads), 0, s, a, m,
-                       k, lda, exps, xp, ldp, x_stride, nrhs, res, res_stride, vec);
+    launch_fly_ct<kWide, L0, NR, 2>(grid, s, a, m, k, lda, exps, xp, ldp, x_stride, nrhs, res,
+                                    res_stride);
 }
 
 // Passes of moduli: 0 .. min(r, 16) - 1, then 16 .. r - 1.

@@ -205,6 +205,42 @@ def test_dgemv_fly_kernel_matches_oracle(r, k, nrhs):
     assert assert_within_ulps(got.cpu().numpy(), want, 2) == 0
 
 
+def _fast_k(r, k, nrhs):
+    """A multiple of 32 near k that reaches the same on-the-fly kernels (the kernels take an
+    unconditional-load path when k is a multiple of 32 and the rows are 16-byte aligned)."""
+    want = gemv_fly_kernels(r, k, nrhs)
+    for kk in (k // 32 * 32, (k + 31) // 32 * 32, (k // 32 + 2) * 32, (k // 32 - 1) * 32):
+        if kk > 0 and gemv_fly_kernels(r, kk, nrhs) == want:
+            return kk
+    raise AssertionError((r, k, nrhs))
+
+
+# The same 23 kernels on their unconditional-load path (k a multiple of 32).
+FLY_FAST_CASES = [(r, _fast_k(r, k, nrhs), nrhs) for r, k, nrhs in FLY_CASES]
+
+
+def test_fly_fast_cases_cover_every_reachable_kernel():
+    reached = set()
+    for r, k, nrhs in FLY_FAST_CASES:
+        assert k % 32 == 0
+        reached.update(gemv_fly_kernels(r, k, nrhs))
+    assert len(reached) == 23
+
+
+@pytest.mark.parametrize("r,k,nrhs", FLY_FAST_CASES)
+def test_dgemv_fly_fast_path_matches_oracle(r, k, nrhs):
+    """Rows of 16-byte aligned fp64 and k % 32 == 0; a row holding a NaN, a row scaled far
+    down, and K padded past k when k is an odd multiple of 32."""
+    announce(f"dgemv fly fast r={r} k={k} nrhs={nrhs} kernels={gemv_fly_kernels(r, k, nrhs)}")
+    a, x = ozk_inputs.gemv_operands(140, k, nrhs, seed=r * 1000 + nrhs + 7)
+    a[5] *= 2.0 ** -40
+    a[9, k // 2] = np.nan
+    got = ozk.ozk_dgemv(to_dev(a), to_dev(x), r, mode=0)
+    torch.cuda.synchronize()
+    want = ozaki2.dgemv(a, x, r)
+    assert assert_within_ulps(got.cpu().numpy(), want, 2) == 0
+
+
 # Base-256 digits path for every r that takes it (1..15), every count of 32-column tiles.
 DIGIT_CASES = [(1, 10, 32), (2, 700, 32), (3, 700, 32), (4, 700, 32), (5, 700, 32),
                (6, 700, 32), (7, 700, 32), (8, 700, 32), (9, 700, 3), (10, 700, 6),
