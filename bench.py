@@ -131,7 +131,8 @@ COUNTER_KERNELS = {
 COUNTER_KERNELS_EXTRA = {
     "gemv_digits_1col": ("gemv_digits_kernel<1>", ["gemv_digits.hip"], 8 * 32768 * 32768),
     "gemv_digits_8cols": ("gemv_digits_kernel<4>", ["gemv_digits.hip"], 8 * 32768 * 32768),
-    "gemv_fly_32cols": ("gemv_fly_kernel<false, 0, 14, 2>", ["gemv.hip"], 8 * 32768 * 32768),
+    "gemv_fly_32cols": ("gemv_fly_kernel<false, 0, 14, 2, true>", ["gemv.hip"],
+                        8 * 32768 * 32768),
     "gemv_stored_1col": ("gemv_stored_kernel", ["gemv.hip"], 14 * 32768 * 32768),
     "fp4_gemm": ("fp4_gemm_kernel", ["fp4limb.hip"], None),
     "fp4awe_gemm": ("awe_gemm_kernel", ["fp4awe.hip"], None),
@@ -322,7 +323,7 @@ TME_KERNELS = {
                                     "element", 32768 * 32768, 14),
     "decon_cols_wide_4096_r16": ("residues_cols_kernel<true, false>", "element", 4096 * 4096,
                                  16),
-    "gemv_fly_32768_r14_32cols": ("gemv_fly_kernel<false, 0, 14, 2>", "element of A",
+    "gemv_fly_32768_r14_32cols": ("gemv_fly_kernel<false, 0, 14, 2, true>", "element of A",
                                   32768 * 32768, 14),
     "gemv_digits_32768_r14_1col": ("gemv_digits_kernel<1>", "element of A", 32768 * 32768, 14),
     "gemv_digits_32768_r14_8cols": ("gemv_digits_kernel<4>", "element of A", 32768 * 32768, 14),
@@ -876,6 +877,53 @@ def cpu_baseline(a, b, r: int, rule: str) -> dict:
                       f"other phases on one thread"}
 
 
+def hold(seconds: float, what: str, step, da, db, r: int, rule: str) -> int:
+    """Run one workload back to back for `seconds` (for external power and clock readings)
+    and print the mean time per call."""
+    import numpy as np
+    import torch
+
+    import fp64_gemm_emulation_ozk_amd as ozk
+    import ozk_inputs
+
+    dev = da.device
+    if what == "dgemm":
+        call, name = step, f"DGEMM step {M}^3 r={r} {rule} rule"
+    elif what == "products":
+        pa = ozk.ozk_deconstruct_ex(da, 0, r, scaling=rule)[0]
+        pb = ozk.ozk_deconstruct_ex(db, 1, r, scaling=rule)[0]
+        res = ozk.ozk_modular_residues(pa, pb, r)
+        call = lambda: ozk.ozk_modular_residues(pa, pb, r, out=res)
+        name = f"residue products {M}^3 r={r}"
+    else:
+        del da, db
+        torch.cuda.empty_cache()
+        nrhs, mg, rg = int(what[4:]), 32768, 14
+        ga = ozk_inputs.uniform_matrix_device((mg, mg), 4, dev)
+        x = torch.from_numpy(ozk_inputs.uniform_matrix(np.random.default_rng(4), (mg, 32)))
+        x = x.to(dev)[:, :nrhs].contiguous()
+        planes, exps = ozk.ozk_deconstruct(ga, 0, rg, k_budget=mg)[:2]
+        del planes
+        torch.cuda.empty_cache()
+        ws = torch.empty(ozk.ozk_dgemv_workspace_size(mg, mg, nrhs, rg, 0), dtype=torch.uint8,
+                         device=dev)
+        y = torch.empty((mg, nrhs), dtype=torch.float64, device=dev)
+        call = lambda: ozk.ozk_dgemv(ga, x, rg, mode=0, a_exps=exps, out=y, workspace=ws)
+        name = f"GEMV {mg}^2 r={rg} on the fly, {nrhs} columns"
+    call()
+    torch.cuda.synchronize()
+    print(f"hold start: {name}", flush=True)
+    t0, done = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(25):
+            call()
+        torch.cuda.synchronize()
+        done += 25
+    dt = time.perf_counter() - t0
+    print(f"hold done: {done} calls, {dt / done * 1e3:.3f} ms each", flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -908,8 +956,12 @@ def main() -> int:
     ap.add_argument("--tme-counters", action="store_true",
                     help="only launch the kernels the time-model counter pass profiles")
     ap.add_argument("--hold", type=float, metavar="SECONDS",
-                    help="run the timed step back to back for SECONDS and print its mean time "
+                    help="run one workload back to back for SECONDS and print its mean time "
                          "(a steady load for reading the board's power and clocks with amd-smi)")
+    ap.add_argument("--hold-workload", default="dgemm",
+                    choices=("dgemm", "products", "gemv1", "gemv8", "gemv32"),
+                    help="what --hold runs: the timed step, its residue products alone, or the "
+                         "32768^2 GEMV on the fly (r = 14, cached exponents) with 1/8/32 columns")
     ap.add_argument("--tme-summary", metavar="DIR",
                     help="write the time-model instruction counts from a rocprofv3 --pmc run")
     args = ap.parse_args()
@@ -952,18 +1004,7 @@ def main() -> int:
     step = lambda: ozk.ozk_dgemm_ex(da, db, r, rule, out=out, workspace=ws)
 
     if args.hold:
-        step()
-        torch.cuda.synchronize()
-        print(f"hold start: {M}^3 r={r} {rule} rule", flush=True)
-        t0, done = time.perf_counter(), 0
-        while time.perf_counter() - t0 < args.hold:
-            for _ in range(25):
-                step()
-            torch.cuda.synchronize()
-            done += 25
-        dt = time.perf_counter() - t0
-        print(f"hold done: {done} steps, {dt / done * 1e3:.3f} ms each", flush=True)
-        return 0
+        return hold(args.hold, args.hold_workload, step, da, db, r, rule)
 
     for _ in range(args.warmup):
         step()
