@@ -591,9 +591,9 @@ def measure_wide_range(reps: int, stream, da, db) -> dict:
 def measure_spmv(reps: int, stream) -> dict:
     """Emulated SpMV on the 7-point Poisson operator of a 256^3 grid (16.8 M rows, 117 M
     entries, x U(-1,1) seed 7) at r = 14 and 16, next to the vendor fp64 CSR product
-    (torch.sparse.mm of the CSR tensor and x as one column).  GB/s counts the bytes a single pass over the
-    operator needs (8 B value + 4 B column per entry, 4 B row offset and 8 B each of x
-    and y per row), the same numerator for both."""
+    (torch.sparse.mm of the CSR tensor and x as one column).  GB/s counts the bytes a
+    single pass over the operator needs (8 B value + 4 B column per entry, 4 B row offset
+    and 8 B each of x and y per row), the same numerator for both."""
     import numpy as np
     import torch
 
@@ -877,6 +877,15 @@ def cpu_baseline(a, b, r: int, rule: str) -> dict:
                       f"other phases on one thread"}
 
 
+def _percentiles(ms: list) -> dict:
+    """Median, 10th and 90th percentile of a list of times (ms), and their count."""
+    import numpy as np
+
+    v = np.asarray(ms, dtype=np.float64)
+    return {"median": round(float(np.median(v)), 4), "p10": round(float(np.percentile(v, 10)), 4),
+            "p90": round(float(np.percentile(v, 90)), 4), "n": int(v.size)}
+
+
 def hold(seconds: float, what: str, step, da, db, r: int, rule: str) -> int:
     """Run one workload back to back for `seconds` (for external power and clock readings)
     and print the mean time per call."""
@@ -1031,6 +1040,17 @@ def main() -> int:
     gemm_ms = sum(ga.elapsed_time(gb) for ga, gb in gev) / args.steps
     # the same steps without the two event records, for comparison
     plain_ms = _time_events(step, args.steps, stream)
+    # distribution of single steps (one event pair each, after the timed region) and of
+    # the residue-product launches inside the timed steps
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for ea, eb in sev:
+        ea.record(stream)
+        step()
+        eb.record(stream)
+    torch.cuda.synchronize()
+    step_dist = _percentiles([ea.elapsed_time(eb) for ea, eb in sev])
+    gemm_dist = _percentiles([ga.elapsed_time(gb) for ga, gb in gev])
 
     # Sanity: normwise distance to native fp64 (not a parity check; tests do that).
     ref = torch.matmul(da, db)
@@ -1054,7 +1074,8 @@ def main() -> int:
               "emulated_pct_int8_peak": round(r * value / PEAK_INT8_TOPS * 100, 2),
               "products_ms": round(gemm_ms, 4),
               "step_phases": "column scaling of B, paired deconstruction of A and B, "
-                             "residue products, CRT"}
+                             "residue products, CRT",
+              "step_ms_distribution": step_dist, "products_ms_distribution": gemm_dist}
     reps = max(args.steps // 2, 5)
     nat_ms = _time_events(lambda: torch.matmul(da, db, out=ref), reps, stream)
     extras["native_fp64_dgemm"] = {"ms": round(nat_ms, 4),
