@@ -67,10 +67,18 @@ def _source_digest(names) -> str:
     return h.hexdigest()[:16]
 
 
-def _time_events(fn, reps: int, stream) -> float:
-    """Average milliseconds per call of fn over reps calls, HIP events on `stream`."""
+def _time_events(fn, reps: int, stream, warm_ms: float = 80.0) -> float:
+    """Average milliseconds per call of fn over reps calls, HIP events on `stream`, after
+    calling fn back to back for at least warm_ms (the board's clocks take some 50-65 ms
+    of load to settle after a change of workload)."""
     import torch
 
+    if warm_ms > 0:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < warm_ms:
+            fn()
+            torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -79,21 +87,6 @@ def _time_events(fn, reps: int, stream) -> float:
     end.record(stream)
     end.synchronize()
     return start.elapsed_time(end) / reps
-
-
-def _time_each(fn, reps: int, stream) -> float:
-    """Average milliseconds per launch of fn, one HIP event pair around each of reps
-    back-to-back launches on `stream` (launch gaps between calls are not counted)."""
-    import torch
-
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
-    for a, b in ev:
-        a.record(stream)
-        fn()
-        b.record(stream)
-    ev[-1][1].synchronize()
-    return sum(a.elapsed_time(b) for a, b in ev) / reps
 
 
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic_dgemm_8192_r16_norm.json")
@@ -1032,7 +1025,7 @@ def main() -> int:
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms_events = _time_events(timed_step, args.steps, stream)
+    ms_events = _time_events(timed_step, args.steps, stream, warm_ms=0)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     ms_per_step = max(ms_events, 1e-9)
