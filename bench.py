@@ -703,8 +703,8 @@ def measure_fp4(reps: int, stream) -> dict:
 
 def measure_hbm_rates(stream) -> dict:
     """What plain streaming reaches on this GPU, as context for the HBM rooflines: a device
-    copy of 2 GiB (torch, read + write bytes) and a read-only reduction of 2 GiB (torch sum,
-    read bytes)."""
+    copy of 2 GiB (torch, read + write bytes), a read-only reduction of 2 GiB (torch sum,
+    read bytes) and a write-only fill of 2 GiB."""
     import torch
 
     dev = torch.device("cuda:0")
@@ -720,9 +720,12 @@ def measure_hbm_rates(stream) -> dict:
     torch.sum(x, dim=0, out=acc)
     t = _time_events(lambda: torch.sum(x, dim=0, out=acc), 5, stream)
     out["hbm_read_gbs"] = round(src.numel() / t / 1e6, 1)
+    t = _time_events(lambda: src.fill_(7), 5, stream)
+    out["hbm_write_gbs"] = round(src.numel() / t / 1e6, 1)
     del src, x
     torch.cuda.empty_cache()
-    out["what"] = "a 2 GiB device copy and a 2 GiB read-only reduction (torch)"
+    out["what"] = ("a 2 GiB device copy, a 2 GiB read-only reduction and a 2 GiB fill "
+                   "(write only), torch")
     return out
 
 
