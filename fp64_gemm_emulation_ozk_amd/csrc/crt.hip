@@ -10,10 +10,11 @@
 //      integer q is at most 1/2 - 2^Q/M, and 1/2 - 2^Q/M >= 0.0142 for every r <= 20);
 //   3. X = sum_b S_b 256^b - q M in 2^40 limbs held in fp64: every limb sum stays below
 //      2^52, so all fp64 operations are exact;
-//   4. limbs are normalised to digits in [0, 2^40) and the sign split off; RN(|X| 2^-s)
-//      is formed with one fp64 rounding of the top digits plus an exact tie correction
-//      (round_digits), or, for a subnormal result, by integer rounding at the reduced
-//      precision, so the output is rounded exactly once.
+//   4. limbs are normalised to digits in [0, 2^40), the sign left in the top digit;
+//      RN(X 2^-s) is formed with one fp64 rounding of the folded top digits plus an exact
+//      tie correction (round_fast), or, for a result below the normal range, by splitting
+//      off the sign and rounding the magnitude at the reduced precision (round_exact), so
+//      the output is rounded exactly once.
 // The constants come from compile-time tables in __constant__ memory.
 #include "ozk_internal.h"
 #include "rns_table.h"
@@ -129,30 +130,93 @@ __device__ __forceinline__ double round_digits(const double (&d)[4], int s) {
   return round_scaled_words(w0, w1, w2, s);
 }
 
-// Sign split, carries and the single rounding of X = sum_p x[p] 2^(40 p) (|x[p]| < 2^52,
-// L limbs): digits 0..L-2 are brought into [0, 2^40) with the sign carried into digit
-// L-1, the magnitude is taken, and RN(|X| 2^-s) is formed by round_digits.
+// The carry pass: digits 0..L-2 of X = sum_p x[p] 2^(40 p) (|x[p]| < 2^52) brought into
+// [0, 2^40), the sign carried into the top limb x[L-1].
 template <int L>
-__device__ __forceinline__ double finish(double (&x)[4], int s, bool nan) {
+__device__ __forceinline__ void carry_digits(double (&x)[4]) {
 #pragma unroll
   for (int p = 0; p < L - 1; ++p) {
     const double carry = __builtin_floor(x[p] * 0x1p-40);
     x[p] = __builtin_fma(-carry, 0x1p40, x[p]);
     x[p + 1] += carry;
   }
+}
+
+// RN(X 2^-s) exactly for any X in carried digits (the path of small results): the sign
+// is split off, the magnitude carried again and rounded by round_digits, which also
+// rounds subnormal results at their reduced precision.
+template <int L>
+__device__ __forceinline__ double round_exact(const double (&xin)[4], int s) {
+  double x[4] = {xin[0], xin[1], xin[2], xin[3]};
   const bool neg = x[L - 1] < 0.0;
   if (neg) {
 #pragma unroll
     for (int p = 0; p < L; ++p) x[p] = -x[p];
-#pragma unroll
-    for (int p = 0; p < L - 1; ++p) {
-      const double carry = __builtin_floor(x[p] * 0x1p-40);
-      x[p] = __builtin_fma(-carry, 0x1p40, x[p]);
-      x[p + 1] += carry;
-    }
+    carry_digits<L>(x);
   }
-  double o = round_digits<L>(x, s);
-  o = neg ? -o : o;
+  const double o = round_digits<L>(x, s);
+  return neg ? -o : o;
+}
+
+// The double next to v (finite, nonzero) in the direction of +Inf.
+__device__ __forceinline__ double next_up(double v) {
+  const int64_t b = __double_as_longlong(v);
+  return __longlong_as_double(b + (v > 0.0 ? 1 : -1));
+}
+
+// RN(X 2^-s) for X in carried digits, both signs at once, for results in the normal
+// range.  With B = 2^40 and the lower digits non-negative, the digits are folded from the
+// top, v <- v B + d, which stays exact while the folded value v lies in [-8192, 8192)
+// (then |v B + d| <= 2^53).  The first level whose v is outside that range gives
+// S = RN(v B + d) with |S| >= 2^53, so S has at least 54 bits and every rounding
+// midpoint is an integer; the digits below add 0 <= eps < 1 unit, which moves the true
+// value towards +Inf and decides only when v B + d lies exactly on the midpoint above S:
+// then the result is the next double above S.  If no level is outside the range the
+// fold reaches the last digit and S = RN(X) directly.  kBigTop: the top digit can leave
+// [-8192, 8192) at this r (the budget bounds |X| <= 2^(Q+1)).
+template <int L, bool kBigTop>
+__device__ __forceinline__ double round_fast(const double (&d)[4], int s) {
+  constexpr double B = 0x1p40;
+  double hv, lv;
+  bool below;
+  int base;
+  auto big = [](double v) { return v >= 8192.0 || v < -8192.0; };
+  if constexpr (L == 1) {
+    hv = 0.0; lv = d[0]; below = false; base = 0;
+  } else if constexpr (L == 2) {
+    hv = d[1]; lv = d[0]; below = false; base = 0;
+  } else if constexpr (L == 3) {
+    const bool ba = kBigTop && big(d[2]);
+    const double b = __builtin_fma(d[2], B, d[1]);
+    hv = ba ? d[2] : b;
+    lv = ba ? d[1] : d[0];
+    below = ba && d[0] != 0.0;
+    base = ba ? 40 : 0;
+  } else {
+    const bool ba = kBigTop && big(d[3]);
+    const double b = __builtin_fma(d[3], B, d[2]);
+    const bool bb = big(b);
+    const double c = __builtin_fma(b, B, d[1]);
+    hv = ba ? d[3] : (bb ? b : c);
+    lv = ba ? d[2] : (bb ? d[1] : d[0]);
+    below = ba ? (d[1] != 0.0 || d[0] != 0.0) : (bb && d[0] != 0.0);
+    base = ba ? 80 : (bb ? 40 : 0);
+  }
+  double S = __builtin_fma(hv, B, lv);
+  const double err = __builtin_fma(hv, B, -S) + lv;   // exact: an integer below 2^42
+  const double up = next_up(S);
+  if (below && err == 0.5 * (up - S)) S = up;
+  return __builtin_ldexp(S, base - s);
+}
+
+// Carries and the single rounding of X = sum_p x[p] 2^(40 p) (|x[p]| < 2^52, L limbs):
+// the fast signed rounding, and the exact path for results below 2^-1021 in magnitude
+// (subnormal, zero or underflowing), which only the lanes holding one take.
+template <int L, bool kBigTop>
+__device__ __forceinline__ double finish(double (&x)[4], int s, bool nan) {
+  carry_digits<L>(x);
+  double o = round_fast<L, kBigTop>(x, s);
+  if (__builtin_fabs(o) < 0x1p-1021) o = round_exact<L>(x, s);
   return nan ? __builtin_nan("") : o;
 }
 
@@ -232,6 +296,9 @@ struct CrtShape {
   static constexpr int kRows = kNE + 4;              // + F digit rows
   static constexpr int kL = (kNE + 4) / 5;           // 2^40 limbs of X
   static constexpr int kSwaps = ((kRows + 7) / 8) * 4;  // registers holding used rows
+  // |X| < 2^(Q+1): the top carried digit lies in [-8192, 8192) unless Q + 1 exceeds the
+  // top limb's position by more than 13 bits
+  static constexpr bool kBigTop = kL >= 3 && make_rns_table().q[R] + 1 - 40 * (kL - 1) > 13;
 };
 
 // Symmetric residue of one input value of modulus l (int8 residues pass through).
@@ -384,7 +451,7 @@ __global__ __launch_bounds__(256) void crt_kernel(int64_t m, int64_t n, const T*
     if (j < n) {
       const int32_t e_i = ea[i], f_j = eb[j];
       const bool nan = e_i == INT32_MIN || f_j == INT32_MIN;
-      c[i * ldc + j] = finish<S::kL>(x, e_i + f_j, nan);
+      c[i * ldc + j] = finish<S::kL, S::kBigTop>(x, e_i + f_j, nan);
     }
   };
   // Position (row, group within the row) of a group, advanced by `waves` groups.
