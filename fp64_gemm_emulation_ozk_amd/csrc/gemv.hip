@@ -157,7 +157,12 @@ __device__ __forceinline__ void for_moduli(F&& f) {
 constexpr int kFlyWaves = 8;
 constexpr int kFlyThreads = 64 * kFlyWaves;
 constexpr int kFlyRows = 16 * kFlyWaves;     // rows per workgroup
-constexpr int kXsPitch = 48;                 // bytes per staged X column (32 used)
+// Staged X residues: per buffer and modulus, four planes (one per K quarter kq) of 32
+// columns x 8 bytes, 288 bytes apart.  A fragment read (16 lanes of one kq, 16 columns)
+// is 128 contiguous bytes; the two 8-byte halves a thread writes land in planes 2h and
+// 2h + 1, whose 32-byte pad puts the writes of the two halves of 8 columns on disjoint
+// banks.
+constexpr int kXsPlane = 288;
 
 template <bool kWide, int L0, int NR, int CT, bool kFast>
 __global__ __launch_bounds__(kFlyThreads, 1) void gemv_fly_kernel(
@@ -166,7 +171,7 @@ __global__ __launch_bounds__(kFlyThreads, 1) void gemv_fly_kernel(
     int64_t x_stride, int nrhs, int8_t* __restrict__ res, int64_t res_stride, int vec) {
   constexpr int l0 = L0;
   constexpr int kPF = !kFast ? 2 : NR * CT >= 30 ? 3 : 4;   // A steps in flight (registers)
-  __shared__ __attribute__((aligned(16))) int8_t xs[2][NR][32][kXsPitch];
+  __shared__ __attribute__((aligned(16))) int8_t xs[2][NR][4][kXsPlane];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int64_t row0 = ((int64_t)blockIdx.x * kFlyWaves + (tid >> 6)) * 16;
@@ -208,8 +213,13 @@ __global__ __launch_bounds__(kFlyThreads, 1) void gemv_fly_kernel(
 #pragma unroll
     for (int u = 0; u < kXL; ++u) {
       const int idx = tid + kFlyThreads * u;
-      if (idx < NR * 64)
-        *reinterpret_cast<v4i*>(&xs[buf][idx >> 6][(idx >> 1) & 31][16 * (idx & 1)]) = xr[u];
+      if (idx < NR * 64) {
+        const int q = idx >> 6, col = (idx >> 1) & 31, h = idx & 1;
+        *reinterpret_cast<v1l*>(&xs[buf][q][2 * h][8 * col]) =
+            (v1l)(((uint64_t)(uint32_t)xr[u][1] << 32) | (uint32_t)xr[u][0]);
+        *reinterpret_cast<v1l*>(&xs[buf][q][2 * h + 1][8 * col]) =
+            (v1l)(((uint64_t)(uint32_t)xr[u][3] << 32) | (uint32_t)xr[u][2]);
+      }
     }
   };
   // Fast path: step c clamped into the steps below k, no condition per lane.
@@ -310,7 +320,7 @@ __global__ __launch_bounds__(kFlyThreads, 1) void gemv_fly_kernel(
 #pragma unroll
             for (int t = 0; t < CT; ++t) {
               const v1l xf =
-                  *reinterpret_cast<const v1l*>(&xs[buf][q][16 * t + (lane & 15)][8 * kq]);
+                  *reinterpret_cast<const v1l*>(&xs[buf][q][kq][8 * (16 * t + (lane & 15))]);
               acc[q][t] = __builtin_amdgcn_mfma_i32_16x16x32_i8(frag, xf, acc[q][t], 0, 0, 0);
             }
           });
