@@ -389,8 +389,8 @@ __device__ __forceinline__ void transpose_words(const WordLoads<R>& raw, uint32_
   b2v = v4i{(int)w[1][0], (int)w[1][1], (int)w[1][2], (int)w[1][3]};
 }
 
-// Persistent waves: each takes groups of 64 consecutive outputs of one row, four groups
-// per iteration (their loads in flight together), lane i finishing output j0 + i.
+// Persistent waves: each takes groups of 64 consecutive outputs of one row, lane i
+// finishing output j0 + i; consecutive waves take consecutive groups.
 // Columns past n read as residue 0 and are not stored.
 template <int R, typename T>
 __global__ __launch_bounds__(256) void crt_kernel(int64_t m, int64_t n, const T* __restrict__ res,
@@ -469,7 +469,11 @@ __global__ __launch_bounds__(256) void crt_kernel(int64_t m, int64_t n, const T*
     }
     return p;
   };
-  constexpr int kG = 4;                           // groups per iteration
+  // Groups per iteration.  One keeps the wave's loads next to its neighbours' (waves
+  // take consecutive groups), so the loads in flight chip-wide span few DRAM pages:
+  // 8192^2, r = 16, inside the DGEMM step: 449 us with 4 groups per iteration, 433 with
+  // 3, 423 with 2, 412 with 1.
+  constexpr int kG = 1;
   Pos p{g0 / ngroups_row, g0 - (g0 / ngroups_row) * ngroups_row};
   for (int64_t g = g0; g < groups; g += kG * waves) {
     Pos pos[kG];
@@ -538,13 +542,13 @@ int launch_crt(int64_t m, int64_t n, int r, const void* res, int res_is_i32, int
                hipStream_t s) {
   if (m <= 0 || n <= 0) return OZK_OK;
   if (r < 1 || r > kMaxModuli) return OZK_EINVAL;
-  // Persistent waves (4 per block), each over groups of 64 outputs of a row: enough
-  // blocks for about five rounds of the chip's resident waves (six per SIMD), which
-  // evens out the last round (4096^2, r = 16: 130 us with 4096 blocks, 125 us with 6144
-  // to 12288, 174 us with one block per 4 groups), fewer when there is less work.
+  // Persistent waves (4 per block), each over groups of 64 outputs of a row, at most
+  // 16384 blocks (about ten rounds of the chip's resident waves, six per SIMD): inside
+  // the DGEMM step at r = 16, 8192^2 takes 422 / 412 / 402 / 395 us with 4096 / 8192 /
+  // 16384 / 32768 blocks, 4096^2 106 / 106 / 106 / 113 us (its last round fills badly).
   const int64_t groups = m * ((n + 63) / 64);
   const int64_t want = (groups + 3) / 4;
-  const int64_t blocks = want < 8192 ? want : 8192;
+  const int64_t blocks = want < 16384 ? want : 16384;
   dim3 grid((unsigned)blocks);
   Dispatch<1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20>::go(
       r, grid, s, m, n, res, res_is_i32, ldr, stride_r, ea, eb, c, ldc);
