@@ -6,7 +6,8 @@ passes), so each r is its own code.  This file runs every such instantiation at 
 once, element by element against the oracle (<= 2 ulp, expected bit-exact):
 
 * the CRT reconstruction on extreme values (X = +-2^Q, rounding ties, subnormal and
-  overflowing results, NaN exponents) for r = 1..20;
+  overflowing results, NaN exponents) for r = 1..20, and on values next to the points
+  where its rounding of both signs changes level, for r with 2, 3 and 4 limbs;
 * the whole emulated DGEMM for r = 1..20 on wide-range operands;
 * the widest scaled integers the budget allows (r = 20 with k = 1 and 2: 76-bit widths)
   through ozk_deconstruct, ozk_dgemm (both scaling rules) and ozk_dgemv;
@@ -68,6 +69,55 @@ def test_reconstruct_extremes_every_r(r):
     e = np.array([0], dtype=np.int64)
     f = np.array(shifts, dtype=np.int64)
     f[-1] = ozaki2.NONFINITE
+    got = ozk.ozk_reconstruct(to_dev(prods.astype(np.int32)), to_dev(e.astype(np.int32)),
+                              to_dev(f.astype(np.int32)))
+    torch.cuda.synchronize()
+    want = ozaki2.reconstruct(prods, r, e, f)
+    assert assert_within_ulps(got.cpu().numpy(), want, 0) == 0
+
+
+def _fold_boundary_values(rng, q):
+    """Integers |X| <= 2^q that stress the CRT's rounding of both signs: X around v 2^80
+    and v 2^120 for v next to +-8192 (where the folded top digits leave 13 bits), with
+    lower digits that are zero, half a unit or random; midpoints above and below negative
+    powers of two with and without a nonzero tail; negative ties of odd and even
+    mantissas."""
+    xs = []
+    for shift in (40, 80, 120):
+        for v in (-8194, -8193, -8192, -8191, -8190, 8190, 8191, 8192, 8193):
+            for low in (0, 1, 1 << (shift - 1), (1 << shift) - 1,
+                        int.from_bytes(rng.bytes(16), "little") % (1 << shift)):
+                xs.append(v * (1 << shift) + low)
+    for k in (54, 60, 93, 100, 121, 133):
+        p2 = 1 << k
+        mid_up = -p2 + (1 << (k - 54))        # halfway to the next double towards zero
+        xs += [mid_up, mid_up + 1, mid_up - 1, -p2, -p2 + 1, -p2 - 1]
+        mid_dn = -p2 - (1 << (k - 53))        # halfway to the next double away from zero
+        xs += [mid_dn, mid_dn + 1, mid_dn - 1]
+        odd = -(p2 + (1 << (k - 52)) + (1 << (k - 53)))   # tie next to an odd mantissa
+        xs += [odd, odd + 1, odd - 1]
+    return [x for x in xs if abs(x) <= 1 << q]
+
+
+@pytest.mark.parametrize("r", [9, 10, 11, 12, 13, 15, 16, 17, 18, 20])
+def test_reconstruct_signed_rounding(r):
+    """The CRT rounds both signs from carried digits, folding the top digits until the
+    value has 54 bits; X on and next to the fold boundaries, negative ties and midpoints
+    next to negative powers of two must round exactly as the oracle's exact rounding, for
+    r with 2, 3 and 4 limbs, with and without a top digit beyond 13 bits.  Shifts keep
+    the results normal (other tests cover subnormal and overflowing ones)."""
+    announce(f"reconstruct signed rounding r={r}")
+    ms = rns.moduli(r)
+    rng = np.random.default_rng(700 + r)
+    xs = _fold_boundary_values(rng, rns.budget_q(r))
+    n = len(xs)
+    assert n > 20
+    prods = np.empty((r, 1, n), dtype=np.int64)
+    for j, x in enumerate(xs):
+        for l, m in enumerate(ms):
+            prods[l, 0, j] = (x % m) + m * int(rng.integers(-8000, 8000))
+    e = np.array([0], dtype=np.int64)
+    f = rng.integers(-200, 200, size=n).astype(np.int64)
     got = ozk.ozk_reconstruct(to_dev(prods.astype(np.int32)), to_dev(e.astype(np.int32)),
                               to_dev(f.astype(np.int32)))
     torch.cuda.synchronize()
