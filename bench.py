@@ -133,7 +133,7 @@ COUNTER_KERNELS_EXTRA = {
     "fp4awe_gemm": ("awe_gemm_kernel", ["fp4awe.hip"], None),
     "fp4_pack_rows": ("pack_rows_kernel", ["fp4limb.hip"], 8192 * 8192 * (1 + 1.5)),
     "fp4_pack_cols": ("pack_cols_kernel", ["fp4limb.hip"], 8192 * 8192 * (1 + 1.5)),
-    "spmv_rows_r16": ("spmv_residues_kernel<true, 16>", ["spmv.hip"], None),
+    "spmv_rows_r14": ("spmv_residues_kernel<true, 14>", ["spmv.hip"], None),
 }
 
 
@@ -145,7 +145,8 @@ def run_counter_workload(extra: bool = False) -> int:
     its own.  With `extra`, also one call of each other engine at its workload size: the
     32768^2 GEMV at r = 14 (digits path at 1 and 8 columns, residue path at 32, stored
     planes at 1), the 8192^3 INT8 product through FP4 limbs and the emulated SpMV of the
-    256^3 Poisson operator at r = 16.  Nothing is timed."""
+    256^3 Poisson operator at r = 14 (so that every crt_kernel<16> launch is a DGEMM
+    step's).  Nothing is timed."""
     import torch
 
     import fp64_gemm_emulation_ozk_amd as ozk
@@ -196,7 +197,7 @@ def run_counter_workload(extra: bool = False) -> int:
         drp, dci, dv = (torch.from_numpy(t).to(dev) for t in (rp, ci, v))
         xs = torch.from_numpy(ozk_inputs.uniform_matrix(np.random.default_rng(7),
                                                         (256 ** 3, 1))[:, 0]).to(dev)
-        ozk.ozk_spmv_csr(drp, dci, dv, xs, 16, 7)
+        ozk.ozk_spmv_csr(drp, dci, dv, xs, 14, 7)
         torch.cuda.synchronize()
     print("counter workload done", flush=True)
     return 0
