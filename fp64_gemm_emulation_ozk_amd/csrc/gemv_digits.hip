@@ -149,7 +149,10 @@ __global__ __launch_bounds__(256) void xdigits_kernel(const int8_t* __restrict__
 // next group are issued at the start of a group and written to LDS at its end.
 template <int NT>
 struct DigitsShape {
-  static constexpr int G = NT == 1 ? 4 : (NT <= 4 ? 2 : 1);   // super-chunks per stage
+  // Super-chunks per stage, measured at 32768^2, r = 14 (ms for G = 1 / 2 / 4 or 1 / 2):
+  // NT = 1 (1 column) 1.51 / 1.52 / 1.54, NT = 2 (4 columns) 1.58 / 1.75, NT = 3
+  // (6 columns) 2.24 / 1.99, NT = 4 (8 columns) 2.05 / 2.05.
+  static constexpr int G = NT <= 2 ? 1 : (NT <= 4 ? 2 : 1);
   static constexpr int kStageBytes = G * NT * 32 * 128;
   static constexpr int kLoads = G * NT;                        // 16-byte loads per thread
 };
