@@ -409,7 +409,14 @@ def tme_model(extras: dict, hbm: dict) -> dict | None:
     datasheet ones (int8 MFMA 5.0 POP/s, HBM 8 TB/s, vector lane-operations 39.3 T/s).
     Returns the threshold OI* = c_q r P_fp64 / (8 P_int), the per-element instruction
     budget below which an on-the-fly GEMV can stream at memory speed, and
-    model-versus-measured times of the GEMV paths and the 4096^3 DGEMM step."""
+    model-versus-measured times of the GEMV paths and the 4096^3 DGEMM step.
+
+    Each case also carries `model_calibrated_ms`: the same four terms with the ceilings
+    this GPU reaches in place of the datasheet rates: the tensor term at the rate the
+    4096^3 step's residue products reach (they run under the board's power limit), HBM
+    terms at the measured read-only (streams of A) or copy rate (the deconstruction and
+    the CRT, which read and write), each of those two terms the larger of its vector-issue
+    and its memory time."""
     try:
         with open(TME_PATH) as fh:
             cal = json.load(fh)["kernels"]
@@ -436,6 +443,12 @@ def tme_model(extras: dict, hbm: dict) -> dict | None:
                                                  "vector_lane_ops_per_unit")}
     n_a = 32768.0 * 32768.0
     rows = []
+    sq = extras.get("square_4096")
+    # measured ceilings (None where the run did not measure them)
+    p_i8_cal = (16 * 2.0 * SQ ** 3 / (sq["step_r16_max"]["products_ms"] * 1e-3)
+                if sq else None)
+    bw_read = hbm.get("hbm_read_gbs", 0.0) * 1e9 or None
+    bw_copy = hbm.get("hbm_copy_gbs", 0.0) * 1e9 or None
     g = extras.get("gemv_32768")
     if g:
         by = {run["nrhs"]: run for run in g["runs"]}
@@ -454,12 +467,17 @@ def tme_model(extras: dict, hbm: dict) -> dict | None:
                   by.get(32, {}).get("on_the_fly_cached_exps", {}).get("ms")),
                  ("stored planes, 1 col", "gemv_stored_32768_r14_1col", r14 * n_a,
                   by.get(1, {}).get("stored_planes", {}).get("ms"))]
-        for name, key, hbm, measured in cases:
-            t_t, t_h, t_d = model(key, hbm)
-            rows.append({"case": f"GEMV 32768^2 r=14, {name}", "T_tensor_ms": round(t_t * 1e3, 3),
-                         "T_hbm_ms": round(t_h * 1e3, 3), "T_decon_ms": round(t_d * 1e3, 3),
-                         "model_ms": round((max(t_t, t_h) + t_d) * 1e3, 3),
-                         "measured_ms": measured})
+        for name, key, hbm_bytes, measured in cases:
+            t_t, t_h, t_d = model(key, hbm_bytes)
+            row = {"case": f"GEMV 32768^2 r=14, {name}", "T_tensor_ms": round(t_t * 1e3, 3),
+                   "T_hbm_ms": round(t_h * 1e3, 3), "T_decon_ms": round(t_d * 1e3, 3),
+                   "model_ms": round((max(t_t, t_h) + t_d) * 1e3, 3),
+                   "measured_ms": measured}
+            if p_i8_cal and bw_read:
+                t_tc = t_t * p_i8 / p_i8_cal
+                t_hc = hbm_bytes / bw_read
+                row["model_calibrated_ms"] = round((max(t_tc, t_hc) + t_d) * 1e3, 3)
+            rows.append(row)
         for nrhs in (1, 8, 32):
             if nrhs in by:
                 rows.append({"case": f"GEMV 32768^2 native fp64, {nrhs} col",
@@ -468,7 +486,6 @@ def tme_model(extras: dict, hbm: dict) -> dict | None:
                              "measured_ms": by[nrhs]["native_fp64"]["ms"]})
     # DGEMM step: products on the matrix cores, deconstruction of A (rows) and B
     # (columns), CRT per output; HBM bytes are small next to the tensor term.
-    sq = extras.get("square_4096")
     if sq:
         t_t = 16 * 2.0 * SQ * SQ * SQ / p_i8
         t_d = (k("decon_rows_wide_4096_r16", "vector_lane_ops_per_unit") +
@@ -482,6 +499,13 @@ def tme_model(extras: dict, hbm: dict) -> dict | None:
                     "products": sq["step_r16_max"]["products_ms"],
                     "deconstruct_rows": sq["deconstruct_rows"]["ms"],
                     "deconstruct_cols": sq["deconstruct_cols"]["ms"]}}
+        if p_i8_cal and bw_copy:
+            nn = float(SQ * SQ)
+            # bytes: rows 8 + 16 per element; columns a maxima pass (8) + 8 + 16; CRT
+            # 16 residues in, 8 out per output
+            t_dc = max(t_d, (24 + 32) * nn / bw_copy)
+            t_rc = max(t_r, 24 * nn / bw_copy)
+            case["model_calibrated_ms"] = round((t_t * p_i8 / p_i8_cal + t_dc + t_rc) * 1e3, 3)
         rows.append(case)
     out["cases"] = rows
     return out

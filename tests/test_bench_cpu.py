@@ -67,3 +67,30 @@ def test_traffic_is_withheld_for_other_sources(tmp_path, monkeypatch):
     assert bench._traffic("crt", "0123456789abcdef") is None
     monkeypatch.setattr(bench, "TRAFFIC_PATH", str(tmp_path / "missing.json"))
     assert bench._traffic("gemm_i8_residues", "0123456789abcdef") is None
+
+
+def _fake_extras(products_ms):
+    runs = [{"nrhs": n, "native_fp64": {"ms": 3.0}, "on_the_fly_cached_exps": {"ms": 2.0},
+             "stored_planes": {"ms": 2.5}} for n in (1, 8, 32)]
+    return {"gemv_32768": {"runs": runs},
+            "square_4096": {"step_r16_max": {"ms": 1.2, "products_ms": products_ms},
+                            "deconstruct_rows": {"ms": 0.1}, "deconstruct_cols": {"ms": 0.12}}}
+
+
+def test_calibrated_time_model_reduces_to_the_datasheet_model():
+    """With measured ceilings equal to the datasheet rates (and an unbounded copy rate)
+    the calibrated model equals the datasheet one; with slower products and streams every
+    calibrated time is at least the datasheet one."""
+    peak_ms = 16 * 2.0 * bench.SQ ** 3 / (bench.PEAK_INT8_TOPS * 1e12) * 1e3
+    fast = bench.tme_model(_fake_extras(peak_ms),
+                           {"hbm_read_gbs": bench.PEAK_HBM_GBS, "hbm_copy_gbs": 1e12})
+    assert fast is not None
+    for case in fast["cases"]:
+        if "model_calibrated_ms" in case:
+            assert case["model_calibrated_ms"] == pytest.approx(case["model_ms"], abs=2e-3)
+    slow = bench.tme_model(_fake_extras(2 * peak_ms),
+                           {"hbm_read_gbs": 6000.0, "hbm_copy_gbs": 5000.0})
+    cal = [c for c in slow["cases"] if "model_calibrated_ms" in c]
+    assert len(cal) == 5   # four GEMV paths and the DGEMM step
+    for case in cal:
+        assert case["model_calibrated_ms"] >= case["model_ms"] - 1e-9
