@@ -36,12 +36,11 @@ namespace ozk {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kSliceElems = 8192;          // elements of K per int32 accumulation
 constexpr int kSuper = 16;                 // elements per super-chunk (128 digit bytes)
-constexpr int kRowsPerBlock = 128;         // 4 waves x 32 rows
-constexpr int kMaxTiles = 8;               // 32-column MFMA tiles per pass (r * nrhs <= 256)
+constexpr int kRowsPerBlock = 128;         // 4 waves x 2 row tiles of 16
+constexpr int kMaxTiles = 16;              // 16-column MFMA tiles per pass (r * nrhs <= 256)
 
 struct DigitModuli {
   int32_t m[kMaxModuli];
@@ -86,13 +85,14 @@ __device__ __forceinline__ int sym_mod(int v, int m, double inv) {
 }
 
 // Position of digit j of element h inside a column of the weighted digit planes, in the
-// order the main kernel feeds the MFMA: super-chunk s = h / 16 holds 4 K chunks of 32
-// bytes; in chunk q, lane half `half` supplies elements 16 s + 8 half + 2 q + {0, 1}.
+// order the main kernel feeds the MFMA: super-chunk s = h / 16 holds 2 K steps of 64
+// bytes; in K step ks, lane group g (lanes 16 g .. 16 g + 15) supplies elements
+// 16 s + 4 g + 2 ks + {0, 1}.
 __device__ __forceinline__ int64_t digit_pos(int64_t h) {
   const int64_t s = h >> 4;
   const int rem = (int)(h & 15);
-  const int half = rem >> 3, q = (rem >> 1) & 3, u = rem & 1;
-  return s * 128 + q * 32 + half * 16 + u * 8;
+  const int g = rem >> 2, ks = (rem >> 1) & 1, u = rem & 1;
+  return s * 128 + ks * 64 + g * 16 + u * 8;
 }
 
 // ------------------------------------------------------------------ weighted X digits
@@ -139,140 +139,181 @@ __global__ __launch_bounds__(256) void xdigits_kernel(const int8_t* __restrict__
 }
 
 // ------------------------------------------------------------------ main kernel
-// grid (ceil(m / 128), slices, passes); 4 waves, each 32 rows of A against NT tiles of
-// 32 output columns (columns n0 .. n0 + 32 NT - 1, n0 = 512 blockIdx.z), over the K slice
-// blockIdx.y.  The block stages the 128 digit bytes per column of G super-chunks (16
-// elements each) at a time in LDS, double-buffered, one barrier per group; the 16-byte
-// chunk index is XOR-swizzled by (column >> 1) & 7 so that the 16 lanes of a fragment
-// read hit distinct banks.  Each lane turns 8 fp64 of its row per super-chunk into four
-// 16-byte MFMA operands; A is prefetched two super-chunks ahead, and the X' loads of the
-// next group are issued at the start of a group and written to LDS at its end.
+// grid (ceil(m / 128), slices, passes); 4 waves, each 2 row tiles of 16 rows of A against
+// NT tiles of 16 output columns (columns n0 .. n0 + 16 NT - 1, n0 = 256 blockIdx.z) on
+// v_mfma_i32_16x16x64_i8, over the K slice blockIdx.y.  The block stages the 128 digit
+// bytes per column of G super-chunks (16 elements each) at a time in LDS,
+// double-buffered, one barrier per group; the 16-byte chunk index is XOR-swizzled by
+// (column >> 1) & 7 so that the 16 lanes of a fragment read hit distinct banks.  Lane
+// (row lane % 16, group g = lane / 16) turns the 4 fp64 of its row it holds per
+// super-chunk (elements 4 g .. 4 g + 3) into the MFMA operands of the super-chunk's two K
+// steps, for each of its two row tiles; the two K steps of an output tile go to the
+// matrix core back to back.  A is prefetched two super-chunks ahead, and the X' loads of
+// the next group are issued at the start of a group and written to LDS at its end.
+// G super-chunks per LDS stage, measured at 32768^2, r = 14 (ms for G = 1 / 2): 2 columns
+// (NT = 2) 1.50 / 1.56, 4 columns (NT = 4) 1.86-1.90 / 1.53, 6 columns (NT = 6) 1.77 /
+// 1.64-1.68, 8 columns (NT = 7) 1.80-1.84 / 1.82-1.87.  Three or four row tiles per wave
+// (fewer X' reads per MFMA) were slower at every column count: the accumulators leave
+// room for one wave per SIMD only.
 template <int NT>
+constexpr int digits_stage_group() {
+  return NT >= 3 && NT <= 6 ? 2 : 1;
+}
+
+template <int NT, int G>
 struct DigitsShape {
-  // Super-chunks per stage, measured at 32768^2, r = 14 (ms for G = 1 / 2 / 4 or 1 / 2):
-  // NT = 1 (1 column) 1.51 / 1.52 / 1.54, NT = 2 (4 columns) 1.58 / 1.75, NT = 3
-  // (6 columns) 2.24 / 1.99, NT = 4 (8 columns) 2.05 / 2.05.
-  static constexpr int G = NT <= 2 ? 1 : (NT <= 4 ? 2 : 1);
-  static constexpr int kStageBytes = G * NT * 32 * 128;
-  static constexpr int kLoads = G * NT;                        // 16-byte loads per thread
+  static constexpr int kStageBytes = G * NT * 16 * 128;
+  static constexpr int kChunks = kStageBytes / 16;
+  static constexpr int kLoads = (kChunks + 255) / 256;      // 16-byte loads per thread
 };
 
-template <int NT>
+template <int NT, int G>
 __global__ __launch_bounds__(256) void gemv_digits_kernel(
     const double* __restrict__ a, int64_t m, int64_t k, int64_t lda,
     const int32_t* __restrict__ exps, const int8_t* __restrict__ xd, int64_t kp, int nrhs,
     int ncols, int8_t* __restrict__ part, int vec) {
-  using S = DigitsShape<NT>;
-  constexpr int G = S::G;
+  using S = DigitsShape<NT, G>;
   __shared__ __attribute__((aligned(16))) int8_t xs[2][S::kStageBytes];
   constexpr double kDigitMagic = 0x1.8808080808080p+52;   // 2^52 + 0x8808080808080
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int half = lane >> 5;
+  const int grp = lane >> 4;
   const int64_t row0 = ((int64_t)blockIdx.x * 4 + (tid >> 6)) * 32;
-  int64_t row = row0 + (lane & 31);
-  row = row < m ? row : m - 1;
+  int64_t rows[2];
+  rows[0] = row0 + (lane & 15);
+  rows[1] = rows[0] + 16;
   const int slice = blockIdx.y;
-  const int n0 = blockIdx.z * kMaxTiles * 32;
+  const int n0 = blockIdx.z * kMaxTiles * 16;
   const int64_t h_begin = (int64_t)slice * kSliceElems;
   const int64_t h_end = h_begin + kSliceElems < kp ? h_begin + kSliceElems : kp;
   const int64_t nsc = (h_end - h_begin) / kSuper;
 
-  int e = exps[row];
-  const bool bad = e == INT32_MIN;
-  if (bad) e = 0;
-  const int64_t klim = bad ? 0 : k;   // a row holding Inf/NaN contributes residues 0
-  // 2^e as two normal factors (s0 = 1 unless the row is so small that e > 1023).
-  const double s1 = __builtin_ldexp(1.0, e < 1023 ? e : 1023);
-  const double s0 = __builtin_ldexp(1.0, e < 1023 ? 0 : e - 1023);
-  const bool tiny = __ballot(e > 1023) != 0;   // wave-uniform
-  const double* pa = a + row * lda;
-
-  v16i acc[NT];
+  // Per row tile: 2^e as two normal factors (s0 = 1 unless the row is so small that
+  // e > 1023); a row holding Inf/NaN contributes residues 0.
+  double s0[2], s1[2];
+  int64_t klim[2];
+  const double* pa[2];
+  bool tiny_any = false;
 #pragma unroll
-  for (int q = 0; q < NT; ++q)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[q][v] = 0;
+  for (int rt = 0; rt < 2; ++rt) {
+    const int64_t row = rows[rt] < m ? rows[rt] : m - 1;
+    int e = exps[row];
+    const bool bad = e == INT32_MIN;
+    if (bad) e = 0;
+    klim[rt] = bad ? 0 : k;
+    s1[rt] = __builtin_ldexp(1.0, e < 1023 ? e : 1023);
+    s0[rt] = __builtin_ldexp(1.0, e < 1023 ? 0 : e - 1023);
+    tiny_any |= e > 1023;
+    pa[rt] = a + row * lda;
+  }
+  const bool tiny = __ballot(tiny_any) != 0;   // wave-uniform
 
-  // Staging of group g: load i of a thread is chunk (tid & 7) of column 32 (i % NT) +
-  // (tid >> 3) in super-chunk G g + i / NT.  Columns past ncols are not loaded (their
-  // MFMA results are never stored).
+  v4i acc[2][NT];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int q = 0; q < NT; ++q)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[rt][q][v] = 0;
+
+  // Staging of group g: load i of a thread is chunk c = 256 i + tid of the stage, i.e.
+  // chunk c % 8 of column (c / 8) % (16 NT) in super-chunk G g + c / (128 NT).  Columns
+  // past ncols are not loaded (their MFMA results are never stored).
   auto x_load = [&](v4i (&xr)[S::kLoads], int64_t g) {
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
-      const int64_t sc = g * G + i / NT;
-      const int n = n0 + (i % NT) * 32 + (tid >> 3);
-      if (n < ncols && sc < nsc)
+      const int c = 256 * i + tid;
+      const int64_t sc = g * G + c / (128 * NT);
+      const int col = (c >> 3) % (16 * NT);
+      const int n = n0 + col;
+      if (c < S::kChunks && n < ncols && sc < nsc)
         xr[i] = *reinterpret_cast<const v4i*>(xd + (int64_t)n * 8 * kp +
-                                              (h_begin / kSuper + sc) * 128 + (tid & 7) * 16);
+                                              (h_begin / kSuper + sc) * 128 + (c & 7) * 16);
     }
   };
   auto x_store = [&](const v4i (&xr)[S::kLoads], int buf) {
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
-      const int col = (i % NT) * 32 + (tid >> 3), ch = tid & 7;
-      *reinterpret_cast<v4i*>(&xs[buf][(i / NT) * (NT * 4096) + col * 128 +
-                                       ((ch ^ ((col >> 1) & 7)) << 4)]) = xr[i];
+      const int c = 256 * i + tid;
+      if (c < S::kChunks) {
+        const int w = c / (128 * NT);
+        const int col = (c >> 3) % (16 * NT), ch = c & 7;
+        *reinterpret_cast<v4i*>(&xs[buf][w * (NT * 2048) + col * 128 +
+                                         ((ch ^ ((col >> 1) & 7)) << 4)]) = xr[i];
+      }
     }
   };
-  // The 8 fp64 this lane feeds in super-chunk sc (elements 16 sc + 8 half .. + 7).
-  auto load_a = [&](double (&v)[8], int64_t sc) {
-    const int64_t h0 = h_begin + sc * kSuper + 8 * half;
-    if (vec && h0 + 8 <= klim) {
+  // The 4 fp64 of each row tile this lane feeds in super-chunk sc (elements
+  // 16 sc + 4 grp .. + 3).
+  auto load_a = [&](double (&v)[2][4], int64_t sc) {
+    const int64_t h0 = h_begin + sc * kSuper + 4 * grp;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const double2 d = *reinterpret_cast<const double2*>(pa + h0 + 2 * u);
-        v[2 * u] = d.x;
-        v[2 * u + 1] = d.y;
+    for (int rt = 0; rt < 2; ++rt) {
+      if (vec && h0 + 4 <= klim[rt]) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const double2 d = *reinterpret_cast<const double2*>(pa[rt] + h0 + 2 * u);
+          v[rt][2 * u] = d.x;
+          v[rt][2 * u + 1] = d.y;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[rt][u] = h0 + u < klim[rt] ? pa[rt][h0 + u] : 0.0;
       }
-    } else {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = h0 + u < klim ? pa[h0 + u] : 0.0;
     }
   };
 
   v4i xr[S::kLoads];
   const int64_t ngroups = (nsc + G - 1) / G;
   // One super-chunk: MFMAs on v (then v is reloaded with super-chunk sc + 2).
-  auto step = [&](double (&v)[8], int64_t sc, auto tiny_tag) {
+  auto step = [&](double (&v)[2][4], int64_t sc, auto tiny_tag) {
     constexpr bool kTiny = decltype(tiny_tag)::value;
     const int64_t g = sc / G;
     const int within = (int)(sc - g * G);
     const int buf = (int)(g & 1);
     const bool more = g + 1 < ngroups;
     if (within == 0 && more) x_load(xr, g + 1);
-    const int8_t* xb = &xs[buf][within * (NT * 4096)];
+    const int8_t* xb = &xs[buf][within * (NT * 2048)];
+    v4i frag[2][2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      double x0 = v[2 * q], x1 = v[2 * q + 1];
-      if (kTiny) {
-        x0 *= s0;
-        x1 *= s0;
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        double x0 = v[rt][2 * ks], x1 = v[rt][2 * ks + 1];
+        if (kTiny) {
+          x0 *= s0[rt];
+          x1 *= s0[rt];
+        }
+        const uint64_t t0 =
+            (uint64_t)__double_as_longlong(__builtin_fma(x0, s1[rt], kDigitMagic));
+        const uint64_t t1 =
+            (uint64_t)__double_as_longlong(__builtin_fma(x1, s1[rt], kDigitMagic));
+        frag[rt][ks][0] = (int)((uint32_t)t0 ^ 0x80808080u);
+        frag[rt][ks][1] = (int)((uint32_t)(t0 >> 32) ^ 0x00008080u);
+        frag[rt][ks][2] = (int)((uint32_t)t1 ^ 0x80808080u);
+        frag[rt][ks][3] = (int)((uint32_t)(t1 >> 32) ^ 0x00008080u);
       }
-      const uint64_t t0 = (uint64_t)__double_as_longlong(__builtin_fma(x0, s1, kDigitMagic));
-      const uint64_t t1 = (uint64_t)__double_as_longlong(__builtin_fma(x1, s1, kDigitMagic));
-      v4i frag;
-      frag[0] = (int)((uint32_t)t0 ^ 0x80808080u);
-      frag[1] = (int)((uint32_t)(t0 >> 32) ^ 0x00008080u);
-      frag[2] = (int)((uint32_t)t1 ^ 0x80808080u);
-      frag[3] = (int)((uint32_t)(t1 >> 32) ^ 0x00008080u);
-      const int ch = 2 * q + half;
+    if (sc + 2 < nsc) load_a(v, sc + 2);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int col = nt * 32 + (lane & 31);
-        const v4i xf =
-            *reinterpret_cast<const v4i*>(xb + col * 128 + ((ch ^ ((col >> 1) & 7)) << 4));
-        acc[nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(frag, xf, acc[nt], 0, 0, 0);
+    for (int nt = 0; nt < NT; ++nt) {
+      const int col = nt * 16 + (lane & 15);
+      const v4i xf0 =
+          *reinterpret_cast<const v4i*>(xb + col * 128 + (((0 + grp) ^ ((col >> 1) & 7)) << 4));
+      const v4i xf1 =
+          *reinterpret_cast<const v4i*>(xb + col * 128 + (((4 + grp) ^ ((col >> 1) & 7)) << 4));
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        acc[rt][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(frag[rt][0], xf0, acc[rt][nt], 0, 0, 0);
+        acc[rt][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(frag[rt][1], xf1, acc[rt][nt], 0, 0, 0);
       }
     }
-    if (sc + 2 < nsc) load_a(v, sc + 2);
     if (within == G - 1 || sc == nsc - 1) {
       if (more) x_store(xr, buf ^ 1);
       __syncthreads();
     }
   };
   auto run = [&](auto tiny_tag) {
-    double va[8], vb[8];
+    double va[2][4], vb[2][4];
     load_a(va, 0);
     if (nsc > 1) load_a(vb, 1);
     x_load(xr, 0);
@@ -290,24 +331,24 @@ __global__ __launch_bounds__(256) void gemv_digits_kernel(
   if (row0 >= m) return;
 
   // Residues of the slice: lane -> column n (one modulus per lane), register v -> row
-  // 8 (v / 4) + 4 half + v % 4; four consecutive rows pack into one dword.
+  // 4 (lane / 16) + v of the row tile; four consecutive rows pack into one dword.
   int8_t* ps = part + (int64_t)slice * ncols * m;
   const bool vrows = (m & 3) == 0;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int n = n0 + nt * 32 + (lane & 31);
+    const int n = n0 + nt * 16 + (lane & 15);
     if (n >= ncols) continue;
     const int l = n / nrhs;
     const int md = d_dm.m[l];
     const double inv = d_dm.inv[l];
     int8_t* pn = ps + (int64_t)n * m;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int64_t r0 = row0 + 8 * g + 4 * half;
+    for (int rt = 0; rt < 2; ++rt) {
+      const int64_t r0 = row0 + 16 * rt + 4 * grp;
       uint32_t w = 0;
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        w |= ((uint32_t)sym_mod(acc[nt][4 * g + u], md, inv) & 0xffu) << (8 * u);
+        w |= ((uint32_t)sym_mod(acc[rt][nt][u], md, inv) & 0xffu) << (8 * u);
       if (vrows && r0 + 4 <= m) {
         *reinterpret_cast<uint32_t*>(pn + r0) = w;
       } else {
@@ -343,13 +384,14 @@ template <int NT>
 void launch_main(dim3 grid, hipStream_t s, const double* a, int64_t m, int64_t k, int64_t lda,
                  const int32_t* exps, const int8_t* xd, int64_t kp, int nrhs, int ncols,
                  int8_t* part, int vec) {
-  hipLaunchKernelGGL((gemv_digits_kernel<NT>), grid, dim3(256), 0, s, a, m, k, lda, exps, xd,
+  constexpr int G = digits_stage_group<NT>();
+  hipLaunchKernelGGL((gemv_digits_kernel<NT, G>), grid, dim3(256), 0, s, a, m, k, lda, exps, xd,
                      kp, nrhs, ncols, part, vec);
 }
 
 }  // namespace
 
-// Digits pay 8 MFMA K-bytes per element and output column; beyond 256 columns (8 tiles)
+// Digits pay 8 MFMA K-bytes per element and output column; beyond 256 columns (16 tiles)
 // the residue kernel, whose per-element cost does not grow with the columns, is faster.
 bool gemv_digits_supported(int p_bits, int64_t ncols) { return p_bits <= 50 && ncols <= 256; }
 
@@ -374,7 +416,7 @@ int launch_gemv_digits(const double* a, int64_t m, int64_t k, int64_t lda, const
                      xp, kp, x_stride, nrhs, xd, psum);
   if (hipGetLastError() != hipSuccess) return OZK_EHIP;
   const int slices = (int)((kp + kSliceElems - 1) / kSliceElems);
-  const int tiles = (ncols + 31) / 32;
+  const int tiles = (ncols + 15) / 16;
   const int passes = (tiles + kMaxTiles - 1) / kMaxTiles;
   const int nt = tiles < kMaxTiles ? tiles : kMaxTiles;
   const int vec = (reinterpret_cast<uintptr_t>(a) & 15) == 0 && (lda & 1) == 0;
@@ -386,7 +428,8 @@ int launch_gemv_digits(const double* a, int64_t m, int64_t k, int64_t lda, const
     break
   switch (nt) {
     OZK_DIG(1); OZK_DIG(2); OZK_DIG(3); OZK_DIG(4); OZK_DIG(5); OZK_DIG(6); OZK_DIG(7);
-    OZK_DIG(8);
+    OZK_DIG(8); OZK_DIG(9); OZK_DIG(10); OZK_DIG(11); OZK_DIG(12); OZK_DIG(13); OZK_DIG(14);
+    OZK_DIG(15); OZK_DIG(16);
     default: return OZK_EINVAL;
   }
 #undef OZK_DIG

@@ -291,16 +291,18 @@ def test_dgemv_fly_fast_path_matches_oracle(r, k, nrhs):
     assert assert_within_ulps(got.cpu().numpy(), want, 2) == 0
 
 
-# Base-256 digits path for every r that takes it (1..15), every count of 32-column tiles.
-DIGIT_CASES = [(1, 10, 32), (2, 700, 32), (3, 700, 32), (4, 700, 32), (5, 700, 32),
-               (6, 700, 32), (7, 700, 32), (8, 700, 32), (9, 700, 3), (10, 700, 6),
-               (11, 700, 8), (12, 700, 10), (13, 700, 12), (14, 700, 13), (15, 16385, 14)]
+# Base-256 digits path for every r that takes it (1..15), every count of 16-column tiles
+# (1..16, each instantiated with its own tile count), full and partial last tiles.
+DIGIT_CASES = [(1, 10, 16), (2, 700, 16), (3, 700, 16), (4, 700, 16), (5, 700, 16),
+               (6, 700, 16), (7, 700, 16), (8, 700, 16), (9, 700, 16), (10, 700, 16),
+               (11, 700, 16), (12, 700, 16), (13, 700, 16), (14, 700, 16), (15, 16385, 16),
+               (8, 700, 32), (3, 700, 5), (9, 700, 3), (13, 700, 12), (14, 700, 8)]
 
 
 @pytest.mark.parametrize("r,k,nrhs", DIGIT_CASES)
 def test_dgemv_digits_every_r(r, k, nrhs):
     assert gemv_fly_kernels(r, k, nrhs) == []
-    announce(f"dgemv digits r={r} k={k} nrhs={nrhs} tiles={(r * nrhs + 31) // 32}")
+    announce(f"dgemv digits r={r} k={k} nrhs={nrhs} tiles={(r * nrhs + 15) // 16}")
     a, x = ozk_inputs.gemv_operands(150, k, nrhs, seed=r * 77 + nrhs)
     got = ozk.ozk_dgemv(to_dev(a), to_dev(x), r, mode=0)
     planes, exps = ozk.ozk_deconstruct(to_dev(a), 0, r, k_budget=k)
@@ -312,8 +314,9 @@ def test_dgemv_digits_every_r(r, k, nrhs):
 
 
 def test_digit_cases_cover_every_tile_count():
-    tiles = {(r * nrhs + 31) // 32 for r, _, nrhs in DIGIT_CASES}
-    assert tiles == set(range(1, 9))
+    tiles = {(r * nrhs + 15) // 16 for r, _, nrhs in DIGIT_CASES}
+    assert tiles == set(range(1, 17))
+    assert any(r * nrhs % 16 for r, _, nrhs in DIGIT_CASES)
     assert {r for r, _, _ in DIGIT_CASES} == set(range(1, 16))
 
 
