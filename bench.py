@@ -124,8 +124,8 @@ COUNTER_KERNELS = {
 # Kernels of the other engines, summarised when the counter workload ran them
 # (`--counters all`): key -> (kernel-name substring, sources, algorithmic bytes per launch).
 COUNTER_KERNELS_EXTRA = {
-    "gemv_digits_1col": ("gemv_digits_kernel<1>", ["gemv_digits.hip"], 8 * 32768 * 32768),
-    "gemv_digits_8cols": ("gemv_digits_kernel<4>", ["gemv_digits.hip"], 8 * 32768 * 32768),
+    "gemv_digits_1col": ("gemv_digits_kernel<1, 1>", ["gemv_digits.hip"], 8 * 32768 * 32768),
+    "gemv_digits_8cols": ("gemv_digits_kernel<7, 1>", ["gemv_digits.hip"], 8 * 32768 * 32768),
     "gemv_fly_32cols": ("gemv_fly_kernel<false, 0, 14, 2, true>", ["gemv.hip"],
                         8 * 32768 * 32768),
     "gemv_stored_1col": ("gemv_stored_kernel", ["gemv.hip"], 14 * 32768 * 32768),
