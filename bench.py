@@ -321,8 +321,8 @@ TME_KERNELS = {
                                  16),
     "gemv_fly_32768_r14_32cols": ("gemv_fly_kernel<false, 0, 14, 2, true>", "element of A",
                                   32768 * 32768, 14),
-    "gemv_digits_32768_r14_1col": ("gemv_digits_kernel<1>", "element of A", 32768 * 32768, 14),
-    "gemv_digits_32768_r14_8cols": ("gemv_digits_kernel<4>", "element of A", 32768 * 32768, 14),
+    "gemv_digits_32768_r14_1col": ("gemv_digits_kernel<1, 1>", "element of A", 32768 * 32768, 14),
+    "gemv_digits_32768_r14_8cols": ("gemv_digits_kernel<7, 1>", "element of A", 32768 * 32768, 14),
     "gemv_stored_32768_r14_1col": ("gemv_stored_kernel", "element of A", 32768 * 32768, 14),
     "crt_4096_r16": ("crt_kernel<16", "output", 4096 * 4096, 16),
     "gemm_i8_4096_r16": ("gemm_i8_pairs_kernel<1,", "output x modulus", 4096 * 4096 * 16,

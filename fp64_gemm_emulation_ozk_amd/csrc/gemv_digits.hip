@@ -167,7 +167,7 @@ struct DigitsShape {
   static constexpr int kLoads = (kChunks + 255) / 256;      // 16-byte loads per thread
 };
 
-template <int NT, int G>
+template <int NT, int G, bool kFast>
 __global__ __launch_bounds__(256) void gemv_digits_kernel(
     const double* __restrict__ a, int64_t m, int64_t k, int64_t lda,
     const int32_t* __restrict__ exps, const int8_t* __restrict__ xd, int64_t kp, int nrhs,
@@ -189,7 +189,9 @@ __global__ __launch_bounds__(256) void gemv_digits_kernel(
   const int64_t nsc = (h_end - h_begin) / kSuper;
 
   // Per row tile: 2^e as two normal factors (s0 = 1 unless the row is so small that
-  // e > 1023); a row holding Inf/NaN contributes residues 0.
+  // e > 1023).  A row holding Inf/NaN (exponent INT32_MIN) contributes residues 0 on the
+  // general path; the fast path below feeds it as it is: its residues are then
+  // meaningless, and the reconstruction turns every output of the row into NaN either way.
   double s0[2], s1[2];
   int64_t klim[2];
   const double* pa[2];
@@ -263,23 +265,71 @@ __global__ __launch_bounds__(256) void gemv_digits_kernel(
     }
   };
 
+  // Fast path (chosen by the host: rows 16-byte aligned, k a multiple of 16, so every
+  // super-chunk below k is whole): every global load of the loop is issued without a
+  // condition, from addresses clamped into A and X' (super-chunks past k feed zeros), in
+  // one fixed order per super-chunk (staging loads, then A two super-chunks ahead, then
+  // the MFMAs), so the compiler's waits count exactly the loads a super-chunk needs and
+  // leave A's loads in flight (32768^2, r = 14, 8 columns: 1.835 -> 1.790 ms).
+  int64_t nsc_k = (k - h_begin) / kSuper;
+  nsc_k = nsc_k < nsc ? nsc_k : nsc;
+  auto load_a_fast = [&](double (&v)[2][4], int64_t sc) {
+    const int64_t h0 = (sc < nsc_k ? sc : nsc_k - 1) * kSuper + h_begin + 4 * grp;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const double2 d = *reinterpret_cast<const double2*>(pa[rt] + h0 + 2 * u);
+        v[rt][2 * u] = d.x;
+        v[rt][2 * u + 1] = d.y;
+      }
+  };
+  // A lane past the stage's last chunk loads and stores that chunk again (the same bytes
+  // to the same place), a column past ncols reads the last live column.
+  uint32_t x_src[S::kLoads], x_dst[S::kLoads];
+#pragma unroll
+  for (int i = 0; i < S::kLoads; ++i) {
+    int c = 256 * i + tid;
+    c = c < S::kChunks ? c : S::kChunks - 1;
+    const int w = c / (128 * NT);
+    const int col = (c >> 3) % (16 * NT), ch = c & 7;
+    const int n = n0 + col < ncols ? n0 + col : ncols - 1;
+    x_src[i] = (uint32_t)((int64_t)n * 8 * kp + (h_begin / kSuper + w) * 128 + ch * 16);
+    x_dst[i] = (uint32_t)(w * (NT * 2048) + col * 128 + ((ch ^ ((col >> 1) & 7)) << 4));
+  }
+  auto x_load_fast = [&](v4i (&xr)[S::kLoads], int64_t g) {
+    const int8_t* base = xd + g * G * 128;
+#pragma unroll
+    for (int i = 0; i < S::kLoads; ++i) xr[i] = *reinterpret_cast<const v4i*>(base + x_src[i]);
+  };
+  auto x_store_fast = [&](const v4i (&xr)[S::kLoads], int buf) {
+#pragma unroll
+    for (int i = 0; i < S::kLoads; ++i) *reinterpret_cast<v4i*>(&xs[buf][x_dst[i]]) = xr[i];
+  };
+
   v4i xr[S::kLoads];
   const int64_t ngroups = (nsc + G - 1) / G;
   // One super-chunk: MFMAs on v (then v is reloaded with super-chunk sc + 2).
-  auto step = [&](double (&v)[2][4], int64_t sc, auto tiny_tag) {
+  auto step = [&](double (&v)[2][4], int64_t sc, auto tiny_tag, auto within_tag) {
     constexpr bool kTiny = decltype(tiny_tag)::value;
+    constexpr int within = decltype(within_tag)::value;   // sc % G
     const int64_t g = sc / G;
-    const int within = (int)(sc - g * G);
     const int buf = (int)(g & 1);
     const bool more = g + 1 < ngroups;
-    if (within == 0 && more) x_load(xr, g + 1);
+    if (kFast) {
+      if (within == 0) x_load_fast(xr, more ? g + 1 : g);
+      __builtin_amdgcn_sched_barrier(0);   // the staging loads go out first
+    } else if (within == 0 && more) {
+      x_load(xr, g + 1);
+    }
     const int8_t* xb = &xs[buf][within * (NT * 2048)];
     v4i frag[2][2];
+    const bool past_k = kFast && sc >= nsc_k;   // wave-uniform
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        double x0 = v[rt][2 * ks], x1 = v[rt][2 * ks + 1];
+        double x0 = past_k ? 0.0 : v[rt][2 * ks], x1 = past_k ? 0.0 : v[rt][2 * ks + 1];
         if (kTiny) {
           x0 *= s0[rt];
           x1 *= s0[rt];
@@ -293,7 +343,12 @@ __global__ __launch_bounds__(256) void gemv_digits_kernel(
         frag[rt][ks][2] = (int)((uint32_t)t1 ^ 0x80808080u);
         frag[rt][ks][3] = (int)((uint32_t)(t1 >> 32) ^ 0x00008080u);
       }
-    if (sc + 2 < nsc) load_a(v, sc + 2);
+    if (kFast) {
+      load_a_fast(v, sc + 2);
+      __builtin_amdgcn_sched_barrier(0);   // then A two super-chunks ahead, then the MFMAs
+    } else if (sc + 2 < nsc) {
+      load_a(v, sc + 2);
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int col = nt * 16 + (lane & 15);
@@ -307,21 +362,35 @@ __global__ __launch_bounds__(256) void gemv_digits_kernel(
         acc[rt][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(frag[rt][1], xf1, acc[rt][nt], 0, 0, 0);
       }
     }
-    if (within == G - 1 || sc == nsc - 1) {
+    if (kFast) {
+      // the next group's stage (a harmless rewrite of the other buffer after the last)
+      __builtin_amdgcn_sched_barrier(0);
+      if (within == G - 1) {
+        x_store_fast(xr, buf ^ 1);
+        __syncthreads();
+      }
+    } else if (within == G - 1 || sc == nsc - 1) {
       if (more) x_store(xr, buf ^ 1);
       __syncthreads();
     }
   };
   auto run = [&](auto tiny_tag) {
     double va[2][4], vb[2][4];
-    load_a(va, 0);
-    if (nsc > 1) load_a(vb, 1);
-    x_load(xr, 0);
+    if (kFast) {
+      load_a_fast(va, 0);
+      load_a_fast(vb, 1);
+      x_load_fast(xr, 0);
+    } else {
+      load_a(va, 0);
+      if (nsc > 1) load_a(vb, 1);
+      x_load(xr, 0);
+    }
     x_store(xr, 0);
     __syncthreads();
+    // nsc is a multiple of 4 (kp a multiple of 64), so the pair loop has no tail
     for (int64_t sc = 0; sc < nsc; sc += 2) {
-      step(va, sc, tiny_tag);
-      if (sc + 1 < nsc) step(vb, sc + 1, tiny_tag);
+      step(va, sc, tiny_tag, std::integral_constant<int, 0>{});
+      step(vb, sc + 1, tiny_tag, std::integral_constant<int, 1 % G>{});
     }
   };
   if (tiny)
@@ -385,8 +454,12 @@ void launch_main(dim3 grid, hipStream_t s, const double* a, int64_t m, int64_t k
                  const int32_t* exps, const int8_t* xd, int64_t kp, int nrhs, int ncols,
                  int8_t* part, int vec) {
   constexpr int G = digits_stage_group<NT>();
-  hipLaunchKernelGGL((gemv_digits_kernel<NT, G>), grid, dim3(256), 0, s, a, m, k, lda, exps, xd,
-                     kp, nrhs, ncols, part, vec);
+  if (vec && k % kSuper == 0)
+    hipLaunchKernelGGL((gemv_digits_kernel<NT, G, true>), grid, dim3(256), 0, s, a, m, k, lda,
+                       exps, xd, kp, nrhs, ncols, part, vec);
+  else
+    hipLaunchKernelGGL((gemv_digits_kernel<NT, G, false>), grid, dim3(256), 0, s, a, m, k, lda,
+                       exps, xd, kp, nrhs, ncols, part, vec);
 }
 
 }  // namespace

@@ -140,6 +140,42 @@ def test_dgemv_digits_slices_and_tiles(m, k, nrhs, r):
     assert assert_within_ulps(got.cpu().numpy(), want, 2) == 0
 
 
+# The digits kernel's fast path (rows 16-byte aligned, k a multiple of 16): super-chunks
+# past k inside the padding to 64, several K slices, ragged rows, special rows fed as they
+# are (Inf/NaN rows must still give NaN), and several column-tile counts.
+@pytest.mark.parametrize("m,k,nrhs,r", [(130, 720, 8, 14), (65, 2 * 8192 + 48, 2, 12),
+                                        (200, 1024, 3, 14), (97, 656, 16, 14),
+                                        (33, 16, 1, 9)])
+def test_dgemv_digits_fast_path(m, k, nrhs, r):
+    announce(f"dgemv digits fast path m={m} k={k} nrhs={nrhs} r={r}")
+    assert _digit_path(k, r, nrhs) and k % 16 == 0
+    a, x = ozk_inputs.gemv_operands(m, k, nrhs, seed=m + k + nrhs)
+    got = _run(a, x, r, 0)
+    torch.cuda.synchronize()
+    want = ozaki2.dgemv(a, x, r)
+    assert assert_within_ulps(got.cpu().numpy(), want, 2) == 0
+
+
+def test_dgemv_digits_fast_path_special_rows():
+    announce("dgemv digits fast path special rows")
+    m, k, nrhs, r = 100, 320, 4, 14
+    assert _digit_path(k, r, nrhs)
+    rng = np.random.default_rng(28)
+    a = ozk_inputs.phi_matrix(rng, (m, k), 4.0)
+    x = ozk_inputs.uniform_matrix(rng, (k, nrhs))
+    a[3] = 0.0
+    a[7, 11] = np.nan
+    a[9] *= 1e-305          # e > 1023 for this row
+    a[10] = 1e-320 * np.sign(a[10])   # subnormal row
+    a[12, 5] = np.inf
+    a[13, 319] = -np.inf    # in the last super-chunk
+    got = _run(a, x, r, 0)
+    torch.cuda.synchronize()
+    want = ozaki2.dgemv(a, x, r)
+    assert np.isnan(want[[7, 12, 13]]).all()
+    assert assert_within_ulps(got.cpu().numpy(), want, 2) == 0
+
+
 def test_dgemv_strided():
     announce("dgemv strided")
     a, x = ozk_inputs.gemv_operands(70, 90, 3, seed=2)
