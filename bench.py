@@ -124,8 +124,8 @@ COUNTER_KERNELS = {
 # Kernels of the other engines, summarised when the counter workload ran them
 # (`--counters all`): key -> (kernel-name substring, sources, algorithmic bytes per launch).
 COUNTER_KERNELS_EXTRA = {
-    "gemv_digits_1col": ("gemv_digits_kernel<1, 1>", ["gemv_digits.hip"], 8 * 32768 * 32768),
-    "gemv_digits_8cols": ("gemv_digits_kernel<7, 1>", ["gemv_digits.hip"], 8 * 32768 * 32768),
+    "gemv_digits_1col": ("gemv_digits_kernel<1, 1, true>", ["gemv_digits.hip"], 8 * 32768 * 32768),
+    "gemv_digits_8cols": ("gemv_digits_kernel<7, 1, true>", ["gemv_digits.hip"], 8 * 32768 * 32768),
     "gemv_fly_32cols": ("gemv_fly_kernel<false, 0, 14, 2, true>", ["gemv.hip"],
                         8 * 32768 * 32768),
     "gemv_stored_1col": ("gemv_stored_kernel", ["gemv.hip"], 14 * 32768 * 32768),
@@ -321,8 +321,8 @@ TME_KERNELS = {
                                  16),
     "gemv_fly_32768_r14_32cols": ("gemv_fly_kernel<false, 0, 14, 2, true>", "element of A",
                                   32768 * 32768, 14),
-    "gemv_digits_32768_r14_1col": ("gemv_digits_kernel<1, 1>", "element of A", 32768 * 32768, 14),
-    "gemv_digits_32768_r14_8cols": ("gemv_digits_kernel<7, 1>", "element of A", 32768 * 32768, 14),
+    "gemv_digits_32768_r14_1col": ("gemv_digits_kernel<1, 1, true>", "element of A", 32768 * 32768, 14),
+    "gemv_digits_32768_r14_8cols": ("gemv_digits_kernel<7, 1, true>", "element of A", 32768 * 32768, 14),
     "gemv_stored_32768_r14_1col": ("gemv_stored_kernel", "element of A", 32768 * 32768, 14),
     "crt_4096_r16": ("crt_kernel<16", "output", 4096 * 4096, 16),
     "gemm_i8_4096_r16": ("gemm_i8_pairs_kernel<1,", "output x modulus", 4096 * 4096 * 16,
