@@ -453,22 +453,24 @@ def tme_model(extras: dict, hbm: dict) -> dict | None:
     if g:
         by = {run["nrhs"]: run for run in g["runs"]}
 
-        def model(key, hbm_bytes, mfma_ops_per_inst=65536.0):
+        def model(key, hbm_bytes, mfma_ops_per_inst):
             t_t = cal[key]["mfma_per_unit"] * n_a * mfma_ops_per_inst / p_i8
             t_h = hbm_bytes / bw
             t_d = cal[key]["vector_lane_ops_per_unit"] * n_a / P_VALU
             return t_t, t_h, t_d
 
+        # int8 operations per MFMA instruction of each kernel: 16 x 16 x 64 (digits),
+        # 16 x 16 x 32 (residues on the fly), 32 x 32 x 32 (stored planes), times 2
         cases = [("on the fly, digits, 1 col", "gemv_digits_32768_r14_1col", 8 * n_a,
-                  by.get(1, {}).get("on_the_fly_cached_exps", {}).get("ms")),
+                  by.get(1, {}).get("on_the_fly_cached_exps", {}).get("ms"), 32768.0),
                  ("on the fly, digits, 8 cols", "gemv_digits_32768_r14_8cols", 8 * n_a,
-                  by.get(8, {}).get("on_the_fly_cached_exps", {}).get("ms")),
+                  by.get(8, {}).get("on_the_fly_cached_exps", {}).get("ms"), 32768.0),
                  ("on the fly, residues, 32 cols", "gemv_fly_32768_r14_32cols", 8 * n_a,
-                  by.get(32, {}).get("on_the_fly_cached_exps", {}).get("ms")),
+                  by.get(32, {}).get("on_the_fly_cached_exps", {}).get("ms"), 16384.0),
                  ("stored planes, 1 col", "gemv_stored_32768_r14_1col", r14 * n_a,
-                  by.get(1, {}).get("stored_planes", {}).get("ms"))]
-        for name, key, hbm_bytes, measured in cases:
-            t_t, t_h, t_d = model(key, hbm_bytes)
+                  by.get(1, {}).get("stored_planes", {}).get("ms"), 65536.0)]
+        for name, key, hbm_bytes, measured, ops_inst in cases:
+            t_t, t_h, t_d = model(key, hbm_bytes, ops_inst)
             row = {"case": f"GEMV 32768^2 r=14, {name}", "T_tensor_ms": round(t_t * 1e3, 3),
                    "T_hbm_ms": round(t_h * 1e3, 3), "T_decon_ms": round(t_d * 1e3, 3),
                    "model_ms": round((max(t_t, t_h) + t_d) * 1e3, 3),
