@@ -16,7 +16,7 @@ Sources it follows (cited by page title and part):
   product is an exact integer matrix product times a scale; the set S of FP4 values
   times 2 holds every residue modulo 13, so integers split into base-13 digits with
   weights (1, 13, 169), and an INT8 x INT8 product takes 9 pairwise FP4 GEMMs; with
-  free limb weights and planes that combine limbs it takes 6.
+  free limb weights and planes that combine limbs it takes 6, and INT4 x INT8 takes 4.
 
 Where the pages leave a step open, the module that implements it states the reading it
 takes (moduli, scaling rule, symmetric range, digit choice, e2m1 nibble order).
@@ -27,6 +27,7 @@ Modules:
     reference  Dot2 double-double dot products and exact rational products (accuracy pins)
     fp4limb    base-13 digit split, e2m1 codes, 9-product limb GEMM
     fp4awe     weights (1, 29, 37), limb and pairwise-sum planes, 6-product limb GEMM
+    fp4awe4    INT4 x INT8 in 4 FP4 products (limb weight 5, planes at four points)
     spmv       emulated CSR sparse matrix-vector product
 """
 from . import rns, ozaki2, reference, fp4limb, fp4awe, spmv  # noqa: F401
