@@ -27,6 +27,8 @@ __all__ = [
     "ozk_fp4limb_pack", "ozk_fp4limb_products", "ozk_int8gemm_fp4limb",
     "ozk_fp4awe_line_bytes", "ozk_fp4awe_pack", "ozk_fp4awe_products", "ozk_int8gemm_fp4awe",
     "ozk_int8gemm_fp4awe_workspace_size",
+    "ozk_fp4awe4_line_bytes", "ozk_fp4awe4_pack", "ozk_fp4awe4_products",
+    "ozk_int4int8gemm_fp4awe", "ozk_int4int8gemm_fp4awe_workspace_size",
     "ozk_dgemm_workspace_size", "ozk_dgemv_workspace_size",
     "ozk_int8gemm_fp4limb_workspace_size", "ozk_deconstruct_workspace_size",
 ]
@@ -86,6 +88,13 @@ _SIGNATURES = {
                                    _size, _ptr]),
     "ozk_int8gemm_fp4limb": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr,
                                     _size, _ptr]),
+    "ozk_fp4awe4_line_bytes": (_i64, [_i64]),
+    "ozk_fp4awe4_pack": (_int, [_ptr, _i64, _i64, _i64, _int, _int, _ptr, _i64, _ptr]),
+    "ozk_fp4awe4_products": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _i64,
+                                    _ptr]),
+    "ozk_int4int8gemm_fp4awe_workspace_size": (_int, [_i64, _i64, _i64, _ptr]),
+    "ozk_int4int8gemm_fp4awe": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr,
+                                       _size, _ptr]),
 }
 
 _LIB = None
@@ -537,6 +546,63 @@ def ozk_int8gemm_fp4awe(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | No
     if workspace is None:
         workspace = _workspace(ozk_int8gemm_fp4awe_workspace_size(m, n, k), a.device)
     _call("ozk_int8gemm_fp4awe", m, n, k, _dev_ptr(a), _ld(a), _dev_ptr(b), _ld(b),
+          _dev_ptr(out), _ld(out), _dev_ptr(workspace), workspace.numel(),
+          _stream(stream, out, workspace))
+    return out
+
+
+# ------------------------------------------------------------ 4-product FP4 INT4 x INT8 GEMM
+def ozk_fp4awe4_line_bytes(k: int) -> int:
+    return library().ozk_fp4awe4_line_bytes(k)
+
+
+def ozk_int4int8gemm_fp4awe_workspace_size(m: int, n: int, k: int) -> int:
+    return _size_query("ozk_int4int8gemm_fp4awe_workspace_size", m, n, k)
+
+
+def ozk_fp4awe4_pack(x: torch.Tensor, axis: int, int4: bool,
+                     planes: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Packed 4-product planes uint8 [lines][line_bytes] of an int4 (low nibbles, int4=True)
+    or int8 matrix (axis 0: rows are lines, K = columns; axis 1: columns are lines)."""
+    _check(x, torch.int8, "x")
+    rows, cols = x.shape
+    kdim = cols if axis == 0 else rows
+    lines = rows if axis == 0 else cols
+    if planes is None:
+        planes = torch.empty((lines, ozk_fp4awe4_line_bytes(max(kdim, 1))), dtype=torch.uint8,
+                             device=x.device)
+    _call("ozk_fp4awe4_pack", _dev_ptr(x), rows, cols, _ld(x), axis, 1 if int4 else 0,
+          _dev_ptr(planes), planes.stride(0), _stream(stream, planes))
+    return planes
+
+
+def ozk_fp4awe4_products(planes_a: torch.Tensor, planes_b: torch.Tensor, k: int,
+                         out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The 4 exact plane products int32 [4][m][n] from packed lines of A and B."""
+    _check(planes_a, torch.uint8, "planes_a")
+    _check(planes_b, torch.uint8, "planes_b")
+    m, n = planes_a.shape[0], planes_b.shape[0]
+    if out is None:
+        out = torch.empty((4, m, n), dtype=torch.int32, device=planes_a.device)
+    _call("ozk_fp4awe4_products", m, n, k, _dev_ptr(planes_a), planes_a.stride(0),
+          _dev_ptr(planes_b), planes_b.stride(0), _dev_ptr(out), out.stride(1), out.stride(0),
+          _stream(stream, out))
+    return out
+
+
+def ozk_int4int8gemm_fp4awe(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Exact int32 C = A B for an int4 A (one value per byte, low nibble) and an int8 B
+    through 4 FP4 plane products."""
+    _check(a, torch.int8, "A")
+    _check(b, torch.int8, "B")
+    m, k = a.shape
+    n = b.shape[1]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.int32, device=a.device)
+    if workspace is None:
+        workspace = _workspace(ozk_int4int8gemm_fp4awe_workspace_size(m, n, k), a.device)
+    _call("ozk_int4int8gemm_fp4awe", m, n, k, _dev_ptr(a), _ld(a), _dev_ptr(b), _ld(b),
           _dev_ptr(out), _ld(out), _dev_ptr(workspace), workspace.numel(),
           _stream(stream, out, workspace))
     return out

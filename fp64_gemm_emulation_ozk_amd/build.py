@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libozk.so")
 
 ARCH = "gfx950"
 DEVICE_SOURCES = ["deconstruct.hip", "gemm_i8.hip", "crt.hip", "gemv.hip", "gemv_digits.hip",
-                  "fp4limb.hip", "fp4awe.hip", "spmv.hip", "noalloc.hip"]
+                  "fp4limb.hip", "fp4awe.hip", "fp4awe4.hip", "spmv.hip", "noalloc.hip"]
 HOST_SOURCES = ["rns_host.cpp", "api.cpp"]
 
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -32,7 +32,8 @@ DEVICE_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang
 # (cross-lane swaps, conversions): results in VGPRs save a copy out of the AGPRs each.
 EXTRA_FLAGS = {"crt.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                # the 6-product encoding table is searched at compile time
-               "fp4awe.hip": ["-fconstexpr-steps=16777216"]}
+               "fp4awe.hip": ["-fconstexpr-steps=16777216"],
+               "fp4awe4.hip": ["-fconstexpr-steps=16777216"]}
 
 
 def _hipcc() -> str:

@@ -568,6 +568,69 @@ int ozk_int8gemm_fp4awe(int64_t m, int64_t n, int64_t k, const int8_t* A, int64_
   return launch_awe_gemm(m, n, line / 192, pa, line, pb, line, C, ldc, s);
 }
 
+// ---------------------------------------------------------------- 4-product FP4 INT4 x INT8 GEMM
+int64_t ozk_fp4awe4_line_bytes(int64_t k) { return k <= 0 ? 0 : awe4_line_bytes(k); }
+
+int ozk_fp4awe4_pack(const int8_t* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                     int int4, uint8_t* planes, int64_t ld_line, void* stream) {
+  if (axis != 0 && axis != 1) return OZK_EINVAL;
+  if (int4 != 0 && int4 != 1) return OZK_EINVAL;
+  if (rows < 0 || cols < 0 || ldx < (cols > 0 ? cols : 1)) return OZK_EINVAL;
+  const int64_t K = axis == 0 ? cols : rows;
+  const int64_t lines = axis == 0 ? rows : cols;
+  if (K > OZK_MAX_K) return OZK_ERANGE;
+  if (ld_line < awe4_line_bytes(K > 0 ? K : 1) || ld_line % 16 != 0) return OZK_EINVAL;
+  if (lines == 0 || K == 0) return OZK_OK;
+  if (!planes || !x || !aligned(planes, 16)) return OZK_EINVAL;
+  return launch_awe4_pack(x, rows, cols, ldx, axis, int4, planes, ld_line, as_stream(stream));
+}
+
+int ozk_fp4awe4_products(int64_t m, int64_t n, int64_t k, const uint8_t* planes_a,
+                         int64_t lda, const uint8_t* planes_b, int64_t ldb, int32_t* products,
+                         int64_t ldp_out, int64_t stride_p, void* stream) {
+  if (m < 0 || n < 0 || k < 1) return OZK_EINVAL;
+  if (k > OZK_MAX_K) return OZK_ERANGE;
+  const int64_t line = awe4_line_bytes(k);
+  if (lda < line || ldb < line || lda % 16 || ldb % 16) return OZK_EINVAL;
+  if (ldp_out < (n > 0 ? n : 1) || stride_p < m * ldp_out) return OZK_EINVAL;
+  if (m == 0 || n == 0) return OZK_OK;
+  if (!planes_a || !planes_b || !products || !aligned(planes_a, 16) || !aligned(planes_b, 16))
+    return OZK_EINVAL;
+  return launch_awe4_products(m, n, line / 128, planes_a, lda, planes_b, ldb, products,
+                              ldp_out, stride_p, as_stream(stream));
+}
+
+int ozk_int4int8gemm_fp4awe_workspace_size(int64_t m, int64_t n, int64_t k, size_t* bytes) {
+  if (!bytes || m < 0 || n < 0 || k < 1) return OZK_EINVAL;
+  if (k > OZK_MAX_K) return OZK_ERANGE;
+  const int64_t line = awe4_line_bytes(k);
+  *bytes = align256((size_t)m * line) + align256((size_t)n * line);
+  return OZK_OK;
+}
+
+int ozk_int4int8gemm_fp4awe(int64_t m, int64_t n, int64_t k, const int8_t* A, int64_t lda,
+                            const int8_t* B, int64_t ldb, int32_t* C, int64_t ldc,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (m < 0 || n < 0 || k < 1) return OZK_EINVAL;
+  if (k > OZK_MAX_K) return OZK_ERANGE;
+  if (lda < k || ldb < (n > 0 ? n : 1) || ldc < (n > 0 ? n : 1)) return OZK_EINVAL;
+  if (m == 0 || n == 0) return OZK_OK;
+  if (!A || !B || !C) return OZK_EINVAL;
+  size_t need = 0;
+  ozk_int4int8gemm_fp4awe_workspace_size(m, n, k, &need);
+  if (!workspace || workspace_bytes < need) return OZK_EWORKSPACE;
+  if (!aligned(workspace, 256)) return OZK_EINVAL;
+  const int64_t line = awe4_line_bytes(k);
+  Carver cv(workspace);
+  uint8_t* pa = static_cast<uint8_t*>(cv.take((size_t)m * line));
+  uint8_t* pb = static_cast<uint8_t*>(cv.take((size_t)n * line));
+  hipStream_t s = as_stream(stream);
+  int st;
+  if ((st = launch_awe4_pack(A, m, k, lda, 0, 1, pa, line, s))) return st;
+  if ((st = launch_awe4_pack(B, k, n, ldb, 1, 0, pb, line, s))) return st;
+  return launch_awe4_gemm(m, n, line / 128, pa, line, pb, line, C, ldc, s);
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------- emulated SpMV (CSR)

@@ -142,6 +142,17 @@ int launch_awe_products(int64_t m, int64_t n, int64_t steps, const uint8_t* pa, 
                         int64_t stride_o, hipStream_t s);
 int launch_awe_gemm(int64_t m, int64_t n, int64_t steps, const uint8_t* pa, int64_t lda,
                     const uint8_t* pb, int64_t ldb, int32_t* c, int64_t ldc, hipStream_t s);
+// The 4-product INT4 x INT8 FP4 engine (fp4awe4.hip): bytes of one packed line over inner
+// dimension k, packers (int4: A-side planes of the low nibbles, else B-side planes of int8
+// values), plane products, fused GEMM.
+int64_t awe4_line_bytes(int64_t k);
+int launch_awe4_pack(const int8_t* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                     int int4, uint8_t* out, int64_t ld_line, hipStream_t s);
+int launch_awe4_products(int64_t m, int64_t n, int64_t steps, const uint8_t* pa, int64_t lda,
+                         const uint8_t* pb, int64_t ldb, int32_t* out, int64_t ldo,
+                         int64_t stride_o, hipStream_t s);
+int launch_awe4_gemm(int64_t m, int64_t n, int64_t steps, const uint8_t* pa, int64_t lda,
+                     const uint8_t* pb, int64_t ldb, int32_t* c, int64_t ldc, hipStream_t s);
 
 enum GemmEpilogue { kEpiProducts = 0, kEpiResidues = 1 };
 // ev_start / ev_stop (optional, both or neither): caller events the launch records its

@@ -297,6 +297,48 @@ int ozk_int8gemm_fp4awe(int64_t m, int64_t n, int64_t k, const int8_t* A, int64_
                         const int8_t* B, int64_t ldb, int32_t* C, int64_t ldc, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- 4-product FP4 INT4 x INT8 GEMM
+ * [AWE] abstract: with free integer limb weights and stored planes that combine limbs, an
+ * INT4 x INT8 product takes 4 FP4 matrix products.  Encoding used here: an int4 x = a0 +
+ * 5 a1 and an int8 y = b0 + 5 b1 + 25 b2 are the values at (5, 1) of the forms X(p, q) =
+ * q a0 + p a1 and Y(p, q) = q^2 b0 + p q b1 + p^2 b2; the stored planes are X and Y at the
+ * points (0, 1), (1, 0), (1, 1), (1, 2): U = (a0, a1, a0+a1, 2 a0+a1) for the int4 operand,
+ * V = (b0, b2, b0+b1+b2, 4 b0+2 b1+b2) for the int8 operand, all in S (U at most 4 and V
+ * at most 12 in magnitude); of the limb tuples that encode a value, the one whose planes
+ * have the smallest largest magnitude, then sum of squares, then the smallest limbs
+ * lexicographically.  C = A B = 36 P_0 + 90 P_1 + 45 P_2 - 10 P_3 over the plane products
+ * P_t = U_t(A) V_t(B) (interpolation of the cubic form X Y at the four points).  An int4
+ * value is the low four bits of its byte, two's complement: an int8 array of values in
+ * [-8, 7] is read as it is, any other byte by its low nibble.
+ *
+ * Packed layout: one line per row (axis 0, K = cols) or column (axis 1, K = rows) of x; K
+ * in steps of 64 codes, step s of a line at bytes 128 s .. 128 s + 127, plane t at byte
+ * 32 t of the step, value d stored as the e2m1 code of d/2, two codes per byte with the
+ * even K index in the low nibble; codes past K are 0.  ozk_fp4awe4_line_bytes(k) = 128
+ * ceil(k / 64) is the smallest line stride.
+ *
+ * ozk_fp4awe4_pack: the U planes of an int4 matrix (int4 = 1) or the V planes of an int8
+ *   matrix (int4 = 0); planes[line * ld_line + ...] (device, 16-byte aligned), ld_line >=
+ *   ozk_fp4awe4_line_bytes(K) and a multiple of 16; K <= OZK_MAX_K.
+ * ozk_fp4awe4_products: the 4 exact plane products, products[t*stride_p + i*ldp_out + j] =
+ *   sum_h U_t(A)[i][h] V_t(B)[h][j] (int32), from packed lines of A (m lines, stride lda)
+ *   and B (n lines, stride ldb) over inner dimension k <= OZK_MAX_K.
+ * ozk_int4int8gemm_fp4awe: C = A B exactly in int32 (A m x k int4 values one per byte, B
+ *   k x n int8, both row-major), packing both operands into the workspace
+ *   (ozk_int4int8gemm_fp4awe_workspace_size bytes, 256-byte aligned) and summing the 4
+ *   weighted plane products.  k <= OZK_MAX_K (fp32 partial sums stay exact: each
+ *   elementary product is at most 48). */
+int64_t ozk_fp4awe4_line_bytes(int64_t k);
+int ozk_fp4awe4_pack(const int8_t* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                     int int4, uint8_t* planes, int64_t ld_line, void* stream);
+int ozk_fp4awe4_products(int64_t m, int64_t n, int64_t k, const uint8_t* planes_a,
+                         int64_t lda, const uint8_t* planes_b, int64_t ldb, int32_t* products,
+                         int64_t ldp_out, int64_t stride_p, void* stream);
+int ozk_int4int8gemm_fp4awe_workspace_size(int64_t m, int64_t n, int64_t k, size_t* bytes);
+int ozk_int4int8gemm_fp4awe(int64_t m, int64_t n, int64_t k, const int8_t* A, int64_t lda,
+                            const int8_t* B, int64_t ldb, int32_t* C, int64_t ldc,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------- measurement support
  * ozk_dgemm_ex_timed: ozk_dgemm_ex that also has the launch of the r residue products
  *   record its start and end in the caller's two hipEvent_t handles (gemm_start,

@@ -80,6 +80,15 @@ def int8_operands(m: int, n: int, k: int, seed: int):
     return a, b
 
 
+def int4_int8_operands(m: int, n: int, k: int, seed: int):
+    """A (m x k) int4 uniform in [-8, 7], one value per int8 byte, and B (k x n) int8
+    uniform in [-128, 127], drawn A first then B."""
+    rng = np.random.default_rng(seed)
+    a = rng.integers(-8, 8, size=(m, k), dtype=np.int8)
+    b = int8_matrix(rng, (k, n))
+    return a, b
+
+
 def uniform_matrix_device(shape, seed: int, device):
     """Entries U(-1, 1) as float64 drawn on a GPU by torch's seeded generator (for
     operands too large to draw on the host); the same seed gives the same matrix."""
