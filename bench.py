@@ -131,6 +131,7 @@ COUNTER_KERNELS_EXTRA = {
     "gemv_stored_1col": ("gemv_stored_kernel", ["gemv.hip"], 14 * 32768 * 32768),
     "fp4_gemm": ("fp4_gemm_kernel", ["fp4limb.hip"], None),
     "fp4awe_gemm": ("awe_gemm_kernel", ["fp4awe.hip"], None),
+    "fp4awe4_gemm": ("awe4_gemm_kernel", ["fp4awe4.hip"], None),
     "fp4_pack_rows": ("pack_rows_kernel", ["fp4limb.hip"], 8192 * 8192 * (1 + 1.5)),
     "fp4_pack_cols": ("pack_cols_kernel", ["fp4limb.hip"], 8192 * 8192 * (1 + 1.5)),
     "spmv_rows_r14": ("spmv_residues_kernel<true, 14>", ["spmv.hip"], None),
@@ -191,6 +192,7 @@ def run_counter_workload(extra: bool = False) -> int:
                                                                                  seed=5))
         ozk.ozk_int8gemm_fp4limb(ia, ib)
         ozk.ozk_int8gemm_fp4awe(ia, ib)
+        ozk.ozk_int4int8gemm_fp4awe(ia, ib)     # A read as int4 (low nibbles)
         torch.cuda.synchronize()
         del ia, ib
         rp, ci, v = ozk_inputs.poisson_7pt_csr(256)
@@ -719,6 +721,34 @@ def measure_fp4(reps: int, stream) -> dict:
         "frac_fp4_peak_gemm": round(fl6 / (t6 - tp6) / 1e9 / PEAK_FP4_TFLOPS, 4),
         "int8_equiv_tops": round(2.0 * n ** 3 / t6 / 1e9, 1),
         "speedup_vs_nine": round(t / t6, 3)}
+    # the 4-product INT4 x INT8 engine (limb weight 5) on int4 A (uniform in [-8, 7])
+    a4, b4 = ozk_inputs.int4_int8_operands(n, n, n, seed=5)
+    ja, jb = torch.from_numpy(a4).to(dev), torch.from_numpy(b4).to(dev)
+    del a4, b4
+    ws4 = torch.empty(ozk.ozk_int4int8gemm_fp4awe_workspace_size(n, n, n), dtype=torch.uint8,
+                      device=dev)
+    f4 = lambda: ozk.ozk_int4int8gemm_fp4awe(ja, jb, out=c, workspace=ws4)
+    f4()
+    t4 = _time_events(f4, reps, stream)
+    ra = ozk.ozk_fp4awe4_pack(ja, 0, True)
+    rb = ozk.ozk_fp4awe4_pack(jb, 1, False)
+    pack4 = lambda: (ozk.ozk_fp4awe4_pack(ja, 0, True, planes=ra),
+                     ozk.ozk_fp4awe4_pack(jb, 1, False, planes=rb))
+    pack4()
+    tp4 = _time_events(pack4, reps, stream)
+    f6i4 = lambda: ozk.ozk_int8gemm_fp4awe(ja, jb, out=c, workspace=ws6)
+    t6i4 = _time_events(f6i4, reps, stream)
+    fl4 = 4 * 2.0 * n * n * n
+    out["int4_x_int8_four_products"] = {
+        "what": ("int4 A uniform in [-8, 7] x int8 B, seed 5: 4 FP4 plane products (limb "
+                 "weight 5, points 0, inf, 1, 1/2)"),
+        "ms": round(t4, 4), "pack_ms": round(tp4, 4), "gemm_ms_excl_pack": round(t4 - tp4, 4),
+        "fp4_tflops_gemm": round(fl4 / (t4 - tp4) / 1e9, 1),
+        "frac_fp4_peak_gemm": round(fl4 / (t4 - tp4) / 1e9 / PEAK_FP4_TFLOPS, 4),
+        "int8_equiv_tops": round(2.0 * n ** 3 / t4 / 1e9, 1),
+        "six_product_engine_same_operands_ms": round(t6i4, 4),
+        "speedup_vs_six": round(t6i4 / t4, 3)}
+    del ja, jb, ws4, ra, rb
     try:
         torch._int_mm(ia, ib)
         ti = _time_events(lambda: torch._int_mm(ia, ib), reps, stream)

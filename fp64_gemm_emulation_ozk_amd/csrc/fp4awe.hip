@@ -21,6 +21,7 @@
 // codes; step s of line i occupies bytes 192 s .. 192 s + 191 of the line, plane t at
 // byte 32 t of the step, two codes per byte with the even K index in the low nibble.  A
 // K step of a whole 128-line tile is then 128 contiguous 192-byte pieces.
+#include "fp4_pack.h"
 #include "lds_dma.h"
 #include "ozk_internal.h"
 
@@ -118,74 +119,139 @@ __constant__ AweTable d_awe = make_awe_table();
 static_assert(make_awe_table().codes[128] == 0, "0 encodes as six zero planes");
 
 // ------------------------------------------------------------------ packers
-// 64 consecutive K values of one line -> the 192 bytes of its K step.
-__device__ __forceinline__ void pack_step(const int8_t (&v)[64], const uint32_t* lut,
-                                          uint8_t* __restrict__ dst) {
+// A packer's table in LDS, indexed by the unsigned byte of the stored value: the spread
+// words (byte t = code of plane t) of planes 0..3 and of planes 4..5.
+__device__ __forceinline__ void load_awe_lut(uint2* lut) {
+  const uint32_t c = d_awe.codes[threadIdx.x ^ 0x80];   // 256 threads
+  lut[threadIdx.x] = make_uint2(spread_nibbles(c & 0xFFFFu), spread_nibbles(c >> 16));
+  __syncthreads();
+}
+
+// 64 consecutive K values of one line -> the 192 bytes of its K step as 12 pieces of 16
+// (piece 2 t + half: plane t, values 32 half .. 32 half + 31); at(h) is the unsigned byte
+// of value h.
+template <typename At>
+__device__ __forceinline__ void pack_step(At at, const uint2* lut, uint4 (&piece)[12]) {
+  uint32_t w[kPlanes][8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    uint32_t lo[8], hi[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint2 e = lut[at(8 * q + u)];
+      lo[u] = e.x;
+      hi[u] = e.y;
+    }
+    uint32_t o[4], o2[2];
+    pack8_planes<4>(lo, o);
+    pack8_planes<2>(hi, o2);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) w[t][q] = o[t];
+    w[4][q] = o2[0];
+    w[5][q] = o2[1];
+  }
 #pragma unroll
   for (int t = 0; t < kPlanes; ++t) {
-    uint32_t w[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      w[q] = 0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        w[q] |= ((lut[(int)v[8 * q + u] + 128] >> (4 * t)) & 15u) << (4 * u);
-    }
-    uint4* o = reinterpret_cast<uint4*>(dst + 32 * t);
-    o[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    piece[2 * t] = make_uint4(w[t][0], w[t][1], w[t][2], w[t][3]);
+    piece[2 * t + 1] = make_uint4(w[t][4], w[t][5], w[t][6], w[t][7]);
   }
 }
 
-// axis 0: x rows x cols (K = cols); thread -> (row, K step).  vec: x and ldx 16-byte
-// aligned, so a whole step of 64 values is four 16-byte loads.
+// Per-block LDS of the packers: the table and, per wave, 64 staged K steps and their
+// destinations.
+struct AwePackShared {
+  uint2 lut[256];
+  uint4 stage[4][64 * 12];
+  uint8_t* dsts[4][64];
+};
+
+// axis 0: x rows x cols (K = cols); thread -> (row, K step); consecutive threads take
+// consecutive steps of a row, so the staged stores of a wave write 12 KiB runs.  vec: x
+// and ldx 16-byte aligned, so a whole step of 64 values is four 16-byte loads.
 __global__ __launch_bounds__(256) void awe_pack_rows_kernel(const int8_t* __restrict__ x,
                                                             int64_t rows, int64_t cols,
                                                             int64_t ldx, uint8_t* __restrict__ out,
                                                             int64_t ld_line, int64_t steps,
                                                             int vec) {
-  __shared__ uint32_t lut[256];
-  lut[threadIdx.x] = d_awe.codes[threadIdx.x];
-  __syncthreads();
+  __shared__ AwePackShared sh;
+  load_awe_lut(sh.lut);
+  const int wave = threadIdx.x >> 6;
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (g >= rows * steps) return;
-  const int64_t row = g / steps;
-  const int64_t s = g - row * steps;
+  const int64_t wave_g0 = g - (threadIdx.x & 63);
+  if (wave_g0 >= rows * steps) return;            // the whole wave is past the end
+  const bool valid = g < rows * steps;
+  const int64_t gg = valid ? g : wave_g0;           // lanes past the end pack a copy
+  const int64_t row = gg / steps;
+  const int64_t s = gg - row * steps;
   const int64_t h0 = s * kStepCodes;
   const int8_t* src = x + row * ldx;
-  int8_t v[64];
+  uint32_t d[16];   // byte h & 3 of d[h >> 2] = value h0 + h
   if (vec && h0 + 64 <= cols) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint4 w = *reinterpret_cast<const uint4*>(src + h0 + 16 * q);
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int u = 0; u < 16; ++u) v[16 * q + u] = (int8_t)(ww[u >> 2] >> (8 * (u & 3)));
+      d[4 * q] = w.x;
+      d[4 * q + 1] = w.y;
+      d[4 * q + 2] = w.z;
+      d[4 * q + 3] = w.w;
     }
   } else {
 #pragma unroll
-    for (int u = 0; u < 64; ++u) v[u] = h0 + u < cols ? src[h0 + u] : (int8_t)0;
+    for (int q = 0; q < 16; ++q) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (h0 + 4 * q + c < cols) w |= (uint32_t)(uint8_t)src[h0 + 4 * q + c] << (8 * c);
+      d[q] = w;
+    }
   }
-  pack_step(v, lut, out + row * ld_line + s * kStepBytes);
+  uint4 piece[12];
+  pack_step([&](int h) { return byte_of(d[h >> 2], h & 3, 255u); }, sh.lut, piece);
+  wave_staged_store<12>(sh.stage[wave], sh.dsts[wave], piece,
+                        valid ? out + row * ld_line + s * kStepBytes : nullptr);
 }
 
-// axis 1: x rows x cols with K = rows; thread -> (column, K step).  The 64 threads of a
-// wave take 64 consecutive columns, so every load reads 64 consecutive bytes.
+// axis 1: x rows x cols with K = rows; thread -> (4 consecutive columns, K step).  The 64
+// threads of a wave take 256 consecutive columns, so with vec (x and ldx 4-byte aligned)
+// every load instruction reads 256 consecutive bytes of one row; each of the 4 column
+// rounds stores whole 192-byte steps through the staging area.
 __global__ __launch_bounds__(256) void awe_pack_cols_kernel(const int8_t* __restrict__ x,
                                                             int64_t rows, int64_t cols,
                                                             int64_t ldx, uint8_t* __restrict__ out,
-                                                            int64_t ld_line, int64_t steps) {
-  __shared__ uint32_t lut[256];
-  lut[threadIdx.x] = d_awe.codes[threadIdx.x];
-  __syncthreads();
-  const int64_t col = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
-  const int64_t s = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
-  if (col >= cols || s >= steps) return;
+                                                            int64_t ld_line, int64_t steps,
+                                                            int vec) {
+  __shared__ AwePackShared sh;
+  load_awe_lut(sh.lut);
+  const int wave = threadIdx.x >> 6;
+  const int64_t col0 = 4 * ((int64_t)blockIdx.x * 64 + (threadIdx.x & 63));
+  const int64_t s = (int64_t)blockIdx.y * 4 + wave;
+  if (s >= steps || 4 * (int64_t)blockIdx.x * 64 >= cols) return;   // wave-uniform
   const int64_t h0 = s * kStepCodes;
-  int8_t v[64];
+  const bool full = vec && col0 + 4 <= cols;
+  uint32_t r[64];   // byte c of r[h] = row h0 + h, column col0 + c (0 past the matrix)
 #pragma unroll
-  for (int u = 0; u < 64; ++u) v[u] = h0 + u < rows ? x[(h0 + u) * ldx + col] : (int8_t)0;
-  pack_step(v, lut, out + col * ld_line + s * kStepBytes);
+  for (int h = 0; h < 64; ++h) {
+    uint32_t w = 0;
+    if (h0 + h < rows) {
+      const int8_t* p = x + (h0 + h) * ldx + col0;
+      if (full) {
+        w = *reinterpret_cast<const uint32_t*>(p);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (col0 + c < cols) w |= (uint32_t)(uint8_t)p[c] << (8 * c);
+      }
+    }
+    r[h] = w;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint4 piece[12];
+    pack_step([&](int h) { return byte_of(r[h], c, 255u); }, sh.lut, piece);
+    wave_staged_store<12>(sh.stage[wave], sh.dsts[wave], piece,
+                          col0 + c < cols ? out + (col0 + c) * ld_line + s * kStepBytes
+                                          : nullptr);
+  }
 }
 
 __device__ __forceinline__ v16f mfma_fp4(const v4i& a, const v4i& b, const v16f& c) {
@@ -465,9 +531,10 @@ int launch_awe_pack(const int8_t* x, int64_t rows, int64_t cols, int64_t ldx, in
                        0, s, x, rows, cols, ldx, out, ld_line, steps, vec);
   } else {
     if (cols <= 0 || steps <= 0) return OZK_OK;
-    dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((steps + 3) / 4));
+    const int vec = (reinterpret_cast<uintptr_t>(x) % 4) == 0 && ldx % 4 == 0;
+    dim3 grid((unsigned)((cols + 255) / 256), (unsigned)((steps + 3) / 4));
     hipLaunchKernelGGL(awe_pack_cols_kernel, grid, dim3(256), 0, s, x, rows, cols, ldx, out,
-                       ld_line, steps);
+                       ld_line, steps, vec);
   }
   return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
 }

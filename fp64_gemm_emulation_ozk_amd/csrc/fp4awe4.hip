@@ -25,6 +25,7 @@
 // column of B): K in steps of 64 codes; step s of line i occupies bytes 128 s .. 128 s +
 // 127, plane t at byte 32 t of the step, two codes per byte with the even K index in the
 // low nibble.  A K step of a 128-line tile is then 128 contiguous cache lines.
+#include "fp4_pack.h"
 #include "lds_dma.h"
 #include "ozk_internal.h"
 
@@ -139,89 +140,142 @@ static_assert(make_awe4_tables().x_codes[8] == 0 && make_awe4_tables().y_codes[1
               "0 encodes as four zero planes");
 
 // ------------------------------------------------------------------ packers
-// 64 consecutive K values of one line -> the 128 bytes of its K step.  kInt4: the values
-// are int4 in the low nibble of each byte (A side), else int8 (B side).
+// A packer's table in LDS: the spread word (byte t = code of plane t) of every value,
+// indexed by the low nibble of the stored byte (int4, A side) or by the unsigned byte
+// (int8, B side).
 template <bool kInt4>
-__device__ __forceinline__ void pack_step4(const int8_t (&v)[64], const uint16_t* lut,
-                                           uint8_t* __restrict__ dst) {
-#pragma unroll
-  for (int t = 0; t < kPlanes4; ++t) {
-    uint32_t w[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      w[q] = 0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int idx = kInt4 ? ((int)v[8 * q + u] & 15) ^ 8 : (int)v[8 * q + u] + 128;
-        w[q] |= (((uint32_t)lut[idx] >> (4 * t)) & 15u) << (4 * u);
-      }
-    }
-    uint4* o = reinterpret_cast<uint4*>(dst + 32 * t);
-    o[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    o[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  }
-}
-
-// A line's table: 16 int4 entries (index (x & 15) ^ 8 = x + 8) or 256 int8 entries.
-template <bool kInt4>
-__device__ __forceinline__ void load_lut4(uint16_t* lut) {
+__device__ __forceinline__ void load_lut4(uint32_t* lut) {
+  const int b = threadIdx.x;   // 256 threads
   if (kInt4) {
-    if (threadIdx.x < 16) lut[threadIdx.x] = d_awe4.x_codes[threadIdx.x];
+    if (b < 16) lut[b] = spread_nibbles(d_awe4.x_codes[b ^ 8]);
   } else {
-    lut[threadIdx.x] = d_awe4.y_codes[threadIdx.x];
+    lut[b] = spread_nibbles(d_awe4.y_codes[b ^ 0x80]);
   }
   __syncthreads();
 }
 
-// axis 0: x rows x cols (K = cols); thread -> (row, K step).  vec: x and ldx 16-byte
-// aligned, so a whole step of 64 values is four 16-byte loads.
+// 64 consecutive K values of one line -> the 128 bytes of its K step as 8 pieces of 16
+// (piece 2 t + half: plane t, values 32 half .. 32 half + 31); at(h) is the table index
+// of value h.
+template <typename At>
+__device__ __forceinline__ void pack_step4(At at, const uint32_t* lut, uint4 (&piece)[8]) {
+  uint32_t w[kPlanes4][8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    uint32_t sw[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sw[u] = lut[at(8 * q + u)];
+    uint32_t o[kPlanes4];
+    pack8_planes<kPlanes4>(sw, o);
+#pragma unroll
+    for (int t = 0; t < kPlanes4; ++t) w[t][q] = o[t];
+  }
+#pragma unroll
+  for (int t = 0; t < kPlanes4; ++t) {
+    piece[2 * t] = make_uint4(w[t][0], w[t][1], w[t][2], w[t][3]);
+    piece[2 * t + 1] = make_uint4(w[t][4], w[t][5], w[t][6], w[t][7]);
+  }
+}
+
+// Per-block LDS of the packers: the table and, per wave, 64 staged K steps and their
+// destinations.
+struct Awe4PackShared {
+  uint32_t lut[256];
+  uint4 stage[4][64 * 8];
+  uint8_t* dsts[4][64];
+};
+
+// axis 0: x rows x cols (K = cols); thread -> (row, K step); consecutive threads take
+// consecutive steps of a row, so the staged stores of a wave write 8 KiB runs.  vec: x and
+// ldx 16-byte aligned, so a whole step of 64 values is four 16-byte loads.
 template <bool kInt4>
 __global__ __launch_bounds__(256) void awe4_pack_rows_kernel(const int8_t* __restrict__ x,
                                                              int64_t rows, int64_t cols,
                                                              int64_t ldx, uint8_t* __restrict__ out,
                                                              int64_t ld_line, int64_t steps,
                                                              int vec) {
-  __shared__ uint16_t lut[256];
-  load_lut4<kInt4>(lut);
+  __shared__ Awe4PackShared sh;
+  load_lut4<kInt4>(sh.lut);
+  const int wave = threadIdx.x >> 6;
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (g >= rows * steps) return;
-  const int64_t row = g / steps;
-  const int64_t s = g - row * steps;
+  const int64_t wave_g0 = g - (threadIdx.x & 63);
+  if (wave_g0 >= rows * steps) return;            // the whole wave is past the end
+  const bool valid = g < rows * steps;
+  const int64_t gg = valid ? g : wave_g0;           // lanes past the end pack a copy
+  const int64_t row = gg / steps;
+  const int64_t s = gg - row * steps;
   const int64_t h0 = s * kStepCodes4;
   const int8_t* src = x + row * ldx;
-  int8_t v[64];
+  uint32_t d[16];   // byte h & 3 of d[h >> 2] = value h0 + h
   if (vec && h0 + 64 <= cols) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint4 w = *reinterpret_cast<const uint4*>(src + h0 + 16 * q);
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int u = 0; u < 16; ++u) v[16 * q + u] = (int8_t)(ww[u >> 2] >> (8 * (u & 3)));
+      d[4 * q] = w.x;
+      d[4 * q + 1] = w.y;
+      d[4 * q + 2] = w.z;
+      d[4 * q + 3] = w.w;
     }
   } else {
 #pragma unroll
-    for (int u = 0; u < 64; ++u) v[u] = h0 + u < cols ? src[h0 + u] : (int8_t)0;
+    for (int q = 0; q < 16; ++q) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (h0 + 4 * q + c < cols) w |= (uint32_t)(uint8_t)src[h0 + 4 * q + c] << (8 * c);
+      d[q] = w;
+    }
   }
-  pack_step4<kInt4>(v, lut, out + row * ld_line + s * kStepBytes4);
+  constexpr uint32_t mask = kInt4 ? 15u : 255u;
+  uint4 piece[8];
+  pack_step4([&](int h) { return byte_of(d[h >> 2], h & 3, mask); }, sh.lut, piece);
+  wave_staged_store<8>(sh.stage[wave], sh.dsts[wave], piece,
+                       valid ? out + row * ld_line + s * kStepBytes4 : nullptr);
 }
 
-// axis 1: x rows x cols with K = rows; thread -> (column, K step).  The 64 threads of a
-// wave take 64 consecutive columns, so every load reads 64 consecutive bytes.
+// axis 1: x rows x cols with K = rows; thread -> (4 consecutive columns, K step).  The 64
+// threads of a wave take 256 consecutive columns, so with vec (x and ldx 4-byte aligned)
+// every load instruction reads 256 consecutive bytes of one row; each of the 4 column
+// rounds stores whole 128-byte steps through the staging area.
 template <bool kInt4>
 __global__ __launch_bounds__(256) void awe4_pack_cols_kernel(const int8_t* __restrict__ x,
                                                              int64_t rows, int64_t cols,
                                                              int64_t ldx, uint8_t* __restrict__ out,
-                                                             int64_t ld_line, int64_t steps) {
-  __shared__ uint16_t lut[256];
-  load_lut4<kInt4>(lut);
-  const int64_t col = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
-  const int64_t s = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
-  if (col >= cols || s >= steps) return;
+                                                             int64_t ld_line, int64_t steps,
+                                                             int vec) {
+  __shared__ Awe4PackShared sh;
+  load_lut4<kInt4>(sh.lut);
+  const int wave = threadIdx.x >> 6;
+  const int64_t col0 = 4 * ((int64_t)blockIdx.x * 64 + (threadIdx.x & 63));
+  const int64_t s = (int64_t)blockIdx.y * 4 + wave;
+  if (s >= steps || 4 * (int64_t)blockIdx.x * 64 >= cols) return;   // wave-uniform
   const int64_t h0 = s * kStepCodes4;
-  int8_t v[64];
+  const bool full = vec && col0 + 4 <= cols;
+  uint32_t r[64];   // byte c of r[h] = row h0 + h, column col0 + c (0 past the matrix)
 #pragma unroll
-  for (int u = 0; u < 64; ++u) v[u] = h0 + u < rows ? x[(h0 + u) * ldx + col] : (int8_t)0;
-  pack_step4<kInt4>(v, lut, out + col * ld_line + s * kStepBytes4);
+  for (int h = 0; h < 64; ++h) {
+    uint32_t w = 0;
+    if (h0 + h < rows) {
+      const int8_t* p = x + (h0 + h) * ldx + col0;
+      if (full) {
+        w = *reinterpret_cast<const uint32_t*>(p);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (col0 + c < cols) w |= (uint32_t)(uint8_t)p[c] << (8 * c);
+      }
+    }
+    r[h] = w;
+  }
+  constexpr uint32_t mask = kInt4 ? 15u : 255u;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint4 piece[8];
+    pack_step4([&](int h) { return byte_of(r[h], c, mask); }, sh.lut, piece);
+    wave_staged_store<8>(sh.stage[wave], sh.dsts[wave], piece,
+                         col0 + c < cols ? out + (col0 + c) * ld_line + s * kStepBytes4
+                                         : nullptr);
+  }
 }
 
 __device__ __forceinline__ v16f mfma_fp4_32(const v4i& a, const v4i& b, const v16f& c) {
@@ -275,7 +329,7 @@ __global__ __launch_bounds__(64) void awe4_products_kernel(
 // region g (rows 64 (g >> 1), columns 64 (g & 1)) and split the four products: wave 2g+h
 // takes products 2h and 2h+1, over 2 x 2 MFMA blocks of 32 x 32 (2 x 4 fp32 accumulators
 // of 16 registers).  Per K step (64 codes) the tile needs 128 A lines and 128 B lines of
-// 128 bytes (32 KiB), loaded straight into a 3-stage LDS ring by global_load_lds_dwordx4
+// 128 bytes (32 KiB), loaded straight into a 4-stage LDS ring by global_load_lds_dwordx4
 // from wave-uniform SGPR bases plus fixed lane offsets (4 loads of 1 KiB per wave and
 // step).  LDS rows are 128 bytes: 8 chunks of 16 bytes, XOR-swizzled by (row >> 1) & 7,
 // so that the 16 lanes of a fragment read (16 consecutive rows, one logical chunk) cover
@@ -284,7 +338,7 @@ __global__ __launch_bounds__(64) void awe4_products_kernel(
 // Step t of a wave: the 4 MFMAs of its first product, reading the second product's four
 // fragments between them; a wait for its loads of step t+1 and its reads; the workgroup
 // barrier (step t+1 complete in LDS, step t read by every wave); the second product's
-// MFMAs, reading step t+1's first fragments and issuing its 4 loads of step t+3 into the
+// MFMAs, reading step t+1's first fragments and issuing its 4 loads of step t+4 into the
 // stage of step t.  Past the last step the last step is loaded again.  Epilogue: each
 // wave sums coef_t x (int) acc_t over its products in wrap-around 32-bit integers; the odd
 // wave of each pair hands its partial sums to the even one through LDS, which adds them
@@ -293,7 +347,7 @@ constexpr int BM4 = 128, BN4 = 128;
 constexpr int kAwe4Threads = 512;
 constexpr int kRowBytes4 = kStepBytes4;                 // 128
 constexpr int kAwe4Stage = (BM4 + BN4) * kRowBytes4;    // 32 KiB
-constexpr int kAwe4Stages = 3;
+constexpr int kAwe4Stages = 4;
 constexpr int kAwe4Loads = kAwe4Stage / 1024 / 8;       // 4 per wave and step
 constexpr int kAwe4GroupM = 4;
 constexpr int kAwe4Xcds = 8;
@@ -399,10 +453,10 @@ __global__ __launch_bounds__(kAwe4Threads, 1) void awe4_gemm_kernel(
   };
 
 #pragma unroll
-  for (int s = 0; s < 3; ++s)
+  for (int s = 0; s < kAwe4Stages; ++s)
 #pragma unroll
     for (int q = 0; q < kAwe4Loads; ++q) issue(q, s < nk ? s : nk - 1, s);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kAwe4Loads) : "memory");  // step 0 landed
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAwe4Stages - 1) * kAwe4Loads) : "memory");  // step 0
   awe4_barrier();
 #pragma unroll
   for (int idx = 0; idx < 4; ++idx) read(0, 0, 0, idx);
@@ -411,14 +465,16 @@ __global__ __launch_bounds__(kAwe4Threads, 1) void awe4_gemm_kernel(
     const int st = t % kAwe4Stages;
     __builtin_amdgcn_sched_barrier(0);
     product(0, 0, 1, st, 0, 0, 0);
-    // step t+1 landed (this wave's loads; the barrier covers the others), step t+2's
-    // loads may still be in flight; every read of step t is done
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAwe4Loads) : "memory");
+    // step t+1 landed (this wave's loads; the barrier covers the others), the loads of
+    // steps t+2 and t+3 may still be in flight; every read of step t is done (a 3-stage
+    // ring, loads two steps ahead, measured 2 % slower at 8192^3)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAwe4Stages - 2) * kAwe4Loads) : "memory");
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     awe4_barrier();
     __builtin_amdgcn_sched_barrier(0);
     const int tn = t + 1 < nk ? t + 1 : t;       // past the last step: a harmless re-read
-    const int tl = t + 3 < nk ? t + 3 : nk - 1;  // past the last step: reload the last
+    // past the last step: reload the last
+    const int tl = t + kAwe4Stages < nk ? t + kAwe4Stages : nk - 1;
     product(1, 1, 0, tn % kAwe4Stages, kAwe4Loads, tl, st);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -488,13 +544,14 @@ int launch_awe4_pack(const int8_t* x, int64_t rows, int64_t cols, int64_t ldx, i
                          out, ld_line, steps, vec);
   } else {
     if (cols <= 0 || steps <= 0) return OZK_OK;
-    const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((steps + 3) / 4));
+    const int vec = (reinterpret_cast<uintptr_t>(x) % 4) == 0 && ldx % 4 == 0;
+    const dim3 grid((unsigned)((cols + 255) / 256), (unsigned)((steps + 3) / 4));
     if (int4)
       hipLaunchKernelGGL(awe4_pack_cols_kernel<true>, grid, dim3(256), 0, s, x, rows, cols, ldx,
-                         out, ld_line, steps);
+                         out, ld_line, steps, vec);
     else
       hipLaunchKernelGGL(awe4_pack_cols_kernel<false>, grid, dim3(256), 0, s, x, rows, cols, ldx,
-                         out, ld_line, steps);
+                         out, ld_line, steps, vec);
   }
   return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
 }

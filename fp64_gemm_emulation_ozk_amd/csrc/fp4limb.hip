@@ -18,6 +18,7 @@
 // 28561 in wrap-around 32-bit arithmetic (the exact result fits int32: |C| <= 2^14 K).
 #include <type_traits>
 
+#include "fp4_pack.h"
 #include "lds_dma.h"
 #include "ozk_internal.h"
 
@@ -71,19 +72,27 @@ __constant__ LimbTable d_limbs = make_limb_table();
 static_assert(make_limb_table().codes[128] == 0, "0 splits into three zero digits");
 
 // ------------------------------------------------------------------ packer
-// 32 consecutive K values -> 16 bytes per digit plane.
-__device__ __forceinline__ void pack32(const int8_t (&v)[32], const uint16_t* lut, uint4 (&out)[3]) {
+// A packer's table in LDS: the spread word (byte d = code of digit plane d) of every
+// value, indexed by the unsigned byte of the stored value.
+__device__ __forceinline__ void load_limb_lut(uint32_t* lut) {
+  lut[threadIdx.x] = spread_nibbles(d_limbs.codes[threadIdx.x ^ 0x80]);   // 256 threads
+  __syncthreads();
+}
+
+// 32 consecutive K values -> 16 bytes per digit plane; at(h) is the unsigned byte of
+// value h.
+template <typename At>
+__device__ __forceinline__ void pack32(At at, const uint32_t* lut, uint4 (&out)[3]) {
   uint32_t w[3][4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
+    uint32_t sw[8];
 #pragma unroll
-    for (int d = 0; d < 3; ++d) w[d][q] = 0;
+    for (int u = 0; u < 8; ++u) sw[u] = lut[at(8 * q + u)];
+    uint32_t o[3];
+    pack8_planes<3>(sw, o);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const uint32_t c = lut[(int)v[8 * q + u] + 128];
-#pragma unroll
-      for (int d = 0; d < 3; ++d) w[d][q] |= ((c >> (4 * d)) & 15u) << (4 * u);
-    }
+    for (int d = 0; d < 3; ++d) w[d][q] = o[d];
   }
 #pragma unroll
   for (int d = 0; d < 3; ++d) out[d] = make_uint4(w[d][0], w[d][1], w[d][2], w[d][3]);
@@ -96,52 +105,77 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const int8_t* __restrict
                                                         uint8_t* __restrict__ planes,
                                                         int64_t ldpb, int64_t plane_stride,
                                                         int vec) {
-  __shared__ uint16_t lut[256];
-  lut[threadIdx.x] = d_limbs.codes[threadIdx.x];
-  __syncthreads();
+  __shared__ uint32_t lut[256];
+  load_limb_lut(lut);
   const int64_t chunks = ldpb / 16;
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (g >= rows * chunks) return;
   const int64_t row = g / chunks;
   const int64_t h0 = (g - row * chunks) * 32;
   const int8_t* src = x + row * ldx;
-  int8_t v[32];
+  uint32_t d[8];   // byte h & 3 of d[h >> 2] = value h0 + h
   if (vec && h0 + 32 <= cols) {
     const uint4 w0 = *reinterpret_cast<const uint4*>(src + h0);
     const uint4 w1 = *reinterpret_cast<const uint4*>(src + h0 + 16);
-    const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-    for (int u = 0; u < 32; ++u) v[u] = (int8_t)(w[u >> 2] >> (8 * (u & 3)));
+    d[0] = w0.x; d[1] = w0.y; d[2] = w0.z; d[3] = w0.w;
+    d[4] = w1.x; d[5] = w1.y; d[6] = w1.z; d[7] = w1.w;
   } else {
 #pragma unroll
-    for (int u = 0; u < 32; ++u) v[u] = h0 + u < cols ? src[h0 + u] : (int8_t)0;
+    for (int q = 0; q < 8; ++q) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (h0 + 4 * q + c < cols) w |= (uint32_t)(uint8_t)src[h0 + 4 * q + c] << (8 * c);
+      d[q] = w;
+    }
   }
   uint4 out[3];
-  pack32(v, lut, out);
+  pack32([&](int h) { return byte_of(d[h >> 2], h & 3, 255u); }, lut, out);
 #pragma unroll
-  for (int d = 0; d < 3; ++d)
-    *reinterpret_cast<uint4*>(planes + d * plane_stride + row * ldpb + h0 / 2) = out[d];
+  for (int dd = 0; dd < 3; ++dd)
+    *reinterpret_cast<uint4*>(planes + dd * plane_stride + row * ldpb + h0 / 2) = out[dd];
 }
 
-// axis 1: x rows x cols with K = rows; thread -> (column, 32-value chunk of K).
+// axis 1: x rows x cols with K = rows; thread -> (4 consecutive columns, 32-value chunk of
+// K).  The 64 threads of a wave take 256 consecutive columns, so with vec (x and ldx 4-byte
+// aligned) every load instruction reads 256 consecutive bytes of one row.
 __global__ __launch_bounds__(256) void pack_cols_kernel(const int8_t* __restrict__ x,
                                                         int64_t rows, int64_t cols, int64_t ldx,
                                                         uint8_t* __restrict__ planes,
-                                                        int64_t ldpb, int64_t plane_stride) {
-  __shared__ uint16_t lut[256];
-  lut[threadIdx.x] = d_limbs.codes[threadIdx.x];
-  __syncthreads();
-  const int64_t col = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+                                                        int64_t ldpb, int64_t plane_stride,
+                                                        int vec) {
+  __shared__ uint32_t lut[256];
+  load_limb_lut(lut);
+  const int64_t col0 = 4 * ((int64_t)blockIdx.x * 64 + (threadIdx.x & 63));
   const int64_t h0 = ((int64_t)blockIdx.y * 4 + (threadIdx.x >> 6)) * 32;
-  if (col >= cols || h0 >= 2 * ldpb) return;
-  int8_t v[32];
+  if (col0 >= cols || h0 >= 2 * ldpb) return;
+  const bool full = vec && col0 + 4 <= cols;
+  uint32_t r[32];   // byte c of r[h] = row h0 + h, column col0 + c (0 past the matrix)
 #pragma unroll
-  for (int u = 0; u < 32; ++u) v[u] = h0 + u < rows ? x[(h0 + u) * ldx + col] : (int8_t)0;
-  uint4 out[3];
-  pack32(v, lut, out);
+  for (int h = 0; h < 32; ++h) {
+    uint32_t w = 0;
+    if (h0 + h < rows) {
+      const int8_t* p = x + (h0 + h) * ldx + col0;
+      if (full) {
+        w = *reinterpret_cast<const uint32_t*>(p);
+      } else {
 #pragma unroll
-  for (int d = 0; d < 3; ++d)
-    *reinterpret_cast<uint4*>(planes + d * plane_stride + col * ldpb + h0 / 2) = out[d];
+        for (int c = 0; c < 4; ++c)
+          if (col0 + c < cols) w |= (uint32_t)(uint8_t)p[c] << (8 * c);
+      }
+    }
+    r[h] = w;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (col0 + c >= cols) break;
+    uint4 out[3];
+    pack32([&](int h) { return byte_of(r[h], c, 255u); }, lut, out);
+#pragma unroll
+    for (int dd = 0; dd < 3; ++dd)
+      *reinterpret_cast<uint4*>(planes + dd * plane_stride + (col0 + c) * ldpb + h0 / 2) =
+          out[dd];
+  }
 }
 
 __device__ __forceinline__ v16f mfma_fp4(const v4i& a, const v4i& b, const v16f& c) {
@@ -411,9 +445,10 @@ int launch_fp4_pack(const int8_t* x, int64_t rows, int64_t cols, int64_t ldx, in
                        x, rows, cols, ldx, planes, ldpb, plane_stride, vec);
   } else {
     if (cols <= 0) return OZK_OK;
-    dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((2 * ldpb / 32 + 3) / 4));
+    const int vec = (reinterpret_cast<uintptr_t>(x) % 4) == 0 && ldx % 4 == 0;
+    dim3 grid((unsigned)((cols + 255) / 256), (unsigned)((2 * ldpb / 32 + 3) / 4));
     hipLaunchKernelGGL(pack_cols_kernel, grid, dim3(256), 0, s, x, rows, cols, ldx, planes, ldpb,
-                       plane_stride);
+                       plane_stride, vec);
   }
   return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
 }
