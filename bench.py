@@ -132,8 +132,19 @@ COUNTER_KERNELS_EXTRA = {
     "fp4_gemm": ("fp4_gemm_kernel", ["fp4limb.hip"], None),
     "fp4awe_gemm": ("awe_gemm_kernel", ["fp4awe.hip"], None),
     "fp4awe4_gemm": ("awe4_gemm_kernel", ["fp4awe4.hip"], None),
-    "fp4_pack_rows": ("pack_rows_kernel", ["fp4limb.hip"], 8192 * 8192 * (1 + 1.5)),
-    "fp4_pack_cols": ("pack_cols_kernel", ["fp4limb.hip"], 8192 * 8192 * (1 + 1.5)),
+    # full kernel names: "::pack_rows_kernel(" is the 9-product packer alone
+    "fp4_pack_rows": ("::pack_rows_kernel(", ["fp4limb.hip", "fp4_pack.h"],
+                      8192 * 8192 * (1 + 1.5)),
+    "fp4_pack_cols": ("::pack_cols_kernel(", ["fp4limb.hip", "fp4_pack.h"],
+                      8192 * 8192 * (1 + 1.5)),
+    "fp4awe_pack_rows": ("awe_pack_rows_kernel(", ["fp4awe.hip", "fp4_pack.h"],
+                         8192 * 8192 * (1 + 3)),
+    "fp4awe_pack_cols": ("awe_pack_cols_kernel(", ["fp4awe.hip", "fp4_pack.h"],
+                         8192 * 8192 * (1 + 3)),
+    "fp4awe4_pack_rows_int4": ("awe4_pack_rows_kernel<true>(", ["fp4awe4.hip", "fp4_pack.h"],
+                               8192 * 8192 * (1 + 2)),
+    "fp4awe4_pack_cols_int8": ("awe4_pack_cols_kernel<false>(", ["fp4awe4.hip", "fp4_pack.h"],
+                               8192 * 8192 * (1 + 2)),
     "spmv_rows_r14": ("spmv_residues_kernel<true, 14>", ["spmv.hip"], None),
 }
 
