@@ -25,6 +25,8 @@
 // column of B): K in steps of 64 codes; step s of line i occupies bytes 128 s .. 128 s +
 // 127, plane t at byte 32 t of the step, two codes per byte with the even K index in the
 // low nibble.  A K step of a 128-line tile is then 128 contiguous cache lines.
+#include <type_traits>
+
 #include "fp4_pack.h"
 #include "lds_dma.h"
 #include "ozk_internal.h"
@@ -325,39 +327,53 @@ __global__ __launch_bounds__(64) void awe4_products_kernel(
 }
 
 // ------------------------------------------------------------------ fused weighted GEMM
-// Workgroup tile 128 x 128, 512 threads = 8 waves.  Waves 2g and 2g+1 share the 64 x 64
-// region g (rows 64 (g >> 1), columns 64 (g & 1)) and split the four products: wave 2g+h
-// takes products 2h and 2h+1, over 2 x 2 MFMA blocks of 32 x 32 (2 x 4 fp32 accumulators
-// of 16 registers).  Per K step (64 codes) the tile needs 128 A lines and 128 B lines of
-// 128 bytes (32 KiB), loaded straight into a 4-stage LDS ring by global_load_lds_dwordx4
-// from wave-uniform SGPR bases plus fixed lane offsets (4 loads of 1 KiB per wave and
-// step).  LDS rows are 128 bytes: 8 chunks of 16 bytes, XOR-swizzled by (row >> 1) & 7,
-// so that the 16 lanes of a fragment read (16 consecutive rows, one logical chunk) cover
-// all 64 banks.
+// Products 1 and 2 share an accumulator: with block scales 2^2 x 2^1 on product 1 (twice
+// the 2^1 x 2^1 of the others) it adds 2 P1 + P2, and C = 36 P0 + 45 (2 P1 + P2) - 10 P3.
+// Per K value |2 u1 v1 + u2 v2| <= 27 over all int4 x int8 pairs (|u0 v0| <= 18,
+// |u3 v3| <= 48), so all three fp32 sums stay exact integers for K <= 349525.
 //
-// Step t of a wave: the 4 MFMAs of its first product, reading the second product's four
-// fragments between them; a wait for its loads of step t+1 and its reads; the workgroup
-// barrier (step t+1 complete in LDS, step t read by every wave); the second product's
-// MFMAs, reading step t+1's first fragments and issuing its 4 loads of step t+4 into the
+// Workgroup tile 128 x 256, 512 threads = 8 waves; wave w computes all four products of
+// the 64 x 64 region (rows 64 (w >> 2), columns 64 (w & 3)) as 2 x 2 blocks of 32 x 32 in
+// three accumulator sets (192 registers).  Three sets per output, instead of one per
+// product, are what let the tile grow from 128 x 128: per K step (64 codes) it needs 128
+// A lines and 256 B lines of 128 bytes (48 KiB) for 128 MFMAs, 384 bytes per MFMA instead
+// of 512.  The lines go straight into a 3-stage LDS ring by global_load_lds_dwordx4 from
+// wave-uniform SGPR bases plus fixed lane offsets (6 loads of 1 KiB per wave and step).
+// LDS rows are 128 bytes: 8 chunks of 16 bytes, XOR-swizzled by (row >> 1) & 7, so that
+// the 16 lanes of a fragment read (16 consecutive rows, one logical chunk) cover all 64
+// banks.
+//
+// Step t of a wave: products 0, 1 and 2 (4 MFMAs each), each reading the next product's
+// four fragments between its MFMAs; a wait for its loads of step t+1 and its reads; the
+// workgroup barrier (step t+1 complete in LDS, step t read by every wave); product 3,
+// reading step t+1's product-0 fragments and issuing its 6 loads of step t+3 into the
 // stage of step t.  Past the last step the last step is loaded again.  Epilogue: each
-// wave sums coef_t x (int) acc_t over its products in wrap-around 32-bit integers; the odd
-// wave of each pair hands its partial sums to the even one through LDS, which adds them
-// and stores C.
-constexpr int BM4 = 128, BN4 = 128;
+// lane combines its three sums in wrap-around 32-bit integers and stores C.
+constexpr int BM4 = 128, BN4 = 256;
 constexpr int kAwe4Threads = 512;
 constexpr int kRowBytes4 = kStepBytes4;                 // 128
-constexpr int kAwe4Stage = (BM4 + BN4) * kRowBytes4;    // 32 KiB
-constexpr int kAwe4Stages = 4;
-constexpr int kAwe4Loads = kAwe4Stage / 1024 / 8;       // 4 per wave and step
+constexpr int kAwe4Stage = (BM4 + BN4) * kRowBytes4;    // 48 KiB
+constexpr int kAwe4Stages = 3;
+constexpr int kAwe4Loads = kAwe4Stage / 1024 / 8;       // 6 per wave and step
 constexpr int kAwe4GroupM = 4;
 constexpr int kAwe4Xcds = 8;
 static_assert(kAwe4Stages * kAwe4Stage <= 160 * 1024, "ring fits the LDS");
-static_assert(4 * 64 * 64 * 4 <= kAwe4Stages * kAwe4Stage, "epilogue exchange fits the ring");
+static_assert(kAwe4Loads == 6 && BM4 * kRowBytes4 == 2 * 8192, "A rows are loads 0 and 1");
+static_assert(kCoef4[1] == 2 * kCoef4[2], "products 1 and 2 share a sum at scales 2 : 1");
 
 __device__ __forceinline__ void awe4_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// Product t's MFMA: block scales 2^1 on both operands (each code holds half its plane
+// value), 2^2 on A for product 1 (added twice into the shared sum).
+template <int kScaleA>
+__device__ __forceinline__ v16f mfma_fp4_32s(const v4i& a, const v4i& b, const v16f& c) {
+  const v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  const v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, kScaleA, 0, 0x80);
 }
 
 __global__ __launch_bounds__(kAwe4Threads, 1) void awe4_gemm_kernel(
@@ -379,25 +395,24 @@ __global__ __launch_bounds__(kAwe4Threads, 1) void awe4_gemm_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = wave >> 1;          // region
-  const int h = wave & 1;           // products 2h, 2h+1
-  const int r0 = (g >> 1) * 64;     // region rows within the tile
-  const int c0 = (g & 1) * 64;      // region columns
+  const int r0 = (wave >> 2) * 64;   // region rows within the tile
+  const int c0 = (wave & 3) * 64;    // region columns
 
   // Direct loads: load q of this wave covers stage bytes 1024 (wave + 8 q) .. +1023, i.e.
   // LDS rows 8 (wave + 8 q) .. +7; lane i writes row 8 (wave + 8 q) + i / 8 at physical
   // chunk i % 8, which holds logical chunk (i % 8) ^ ((row >> 1) & 7) of that row's K step.
-  // Rows 0..127 are A lines row0.. (q < 2), rows 128..255 B lines col0..; lines past the
+  // Rows 0..127 are A lines row0.. (q < 2), rows 128..383 B lines col0..; lines past the
   // matrix re-read its last line.
   uint32_t voff[kAwe4Loads];
 #pragma unroll
   for (int q = 0; q < kAwe4Loads; ++q) {
     const int row = 8 * (wave + 8 * q) + (lane >> 3);
     const int lc = (lane & 7) ^ ((row >> 1) & 7);
-    const bool is_b = q >= kAwe4Loads / 2;
+    const bool is_b = q >= 2;
     const int64_t origin = is_b ? col0 : row0;
     const int64_t last = (is_b ? n : m) - 1;
-    const int64_t line = origin + (row & 127) < last ? origin + (row & 127) : last;
+    const int rel = is_b ? row - BM4 : row;
+    const int64_t line = origin + rel < last ? origin + rel : last;
     voff[q] = (uint32_t)((line - origin) * (is_b ? ldb : lda) + 16 * lc);
   }
   const uint64_t base_a = (uint64_t)(pa + row0 * lda), base_b = (uint64_t)(pb + col0 * ldb);
@@ -406,12 +421,12 @@ __global__ __launch_bounds__(kAwe4Threads, 1) void awe4_gemm_kernel(
   auto issue = [&](int q, int tk, int stage) {
     const uint64_t kb = (uint64_t)tk * kStepBytes4;
     const uint32_t dst = wave_lds + (uint32_t)stage * kAwe4Stage + q * (8 * 1024);
-    dma16_sbase(voff[q], (q < kAwe4Loads / 2 ? base_a : base_b) + kb, dst);
+    dma16_sbase(voff[q], (q < 2 ? base_a : base_b) + kb, dst);
   };
 
-  v16f acc[2][2][2];
+  v16f acc[3][2][2];   // sums of P0, 2 P1 + P2, P3
 #pragma unroll
-  for (int p = 0; p < 2; ++p)
+  for (int p = 0; p < 3; ++p)
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -429,28 +444,33 @@ __global__ __launch_bounds__(kAwe4Threads, 1) void awe4_gemm_kernel(
   for (int i = 0; i < 2; ++i) offa[i] = (r0 + 32 * i + frow) * kRowBytes4;
 #pragma unroll
   for (int j = 0; j < 2; ++j) offb[j] = (BM4 + c0 + 32 * j + frow) * kRowBytes4;
-  int chunk_off[2];   // byte offset of this lane's chunk of each of its products
+  int chunk_off[kPlanes4];   // byte offset of this lane's chunk of each plane
 #pragma unroll
-  for (int p = 0; p < 2; ++p) chunk_off[p] = ((2 * (2 * h + p) + fhalf) ^ sw) << 4;
+  for (int t = 0; t < kPlanes4; ++t) chunk_off[t] = ((2 * t + fhalf) ^ sw) << 4;
   // frag[set][0..1] = A blocks, [2..3] = B blocks
   v4i frag[2][4];
-  auto read = [&](int set, int stage, int p, int idx) {
-    const uint8_t* st = lds + stage * kAwe4Stage + chunk_off[p];
+  auto read = [&](int set, int stage, int t, int idx) {
+    const uint8_t* st = lds + stage * kAwe4Stage + chunk_off[t];
     const int off = idx < 2 ? offa[idx] : offb[idx - 2];
     frag[set][idx] = *reinterpret_cast<const v4i*>(st + off);
   };
-  // the 4 MFMAs of product p from fragment set `set`, the reads of (rp, rstage) into the
-  // other set between them, and loads [0, nl) of step lt into stage ls, one per MFMA.
-  auto product = [&](int set, int p, int rp, int rstage, int nl, int lt, int ls) {
+  // the 4 MFMAs of product t (into sum a, A scale kScaleA) from fragment set `set`, the
+  // reads of plane rt of stage rstage into the other set between them, and loads [0, nl)
+  // of step lt into stage ls, two per MFMA.
+  auto product = [&](auto scale_a, int set, int a, int rt, int rstage, int nl, int lt, int ls) {
 #pragma unroll
     for (int idx = 0; idx < 4; ++idx) {
       const int i = idx >> 1, j = idx & 1;
-      acc[p][i][j] = mfma_fp4_32(frag[set][i], frag[set][2 + j], acc[p][i][j]);
-      read(set ^ 1, rstage, rp, idx);
-      if (idx < nl) issue(idx, lt, ls);
+      acc[a][i][j] = mfma_fp4_32s<decltype(scale_a)::value>(frag[set][i], frag[set][2 + j],
+                                                             acc[a][i][j]);
+      read(set ^ 1, rstage, rt, idx);
+      if (2 * idx < nl) issue(2 * idx, lt, ls);
+      if (2 * idx + 1 < nl) issue(2 * idx + 1, lt, ls);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  using S1 = std::integral_constant<int, 0x80>;
+  using S2 = std::integral_constant<int, 0x81>;
 
 #pragma unroll
   for (int s = 0; s < kAwe4Stages; ++s)
@@ -464,10 +484,11 @@ __global__ __launch_bounds__(kAwe4Threads, 1) void awe4_gemm_kernel(
   for (int t = 0; t < nk; ++t) {
     const int st = t % kAwe4Stages;
     __builtin_amdgcn_sched_barrier(0);
-    product(0, 0, 1, st, 0, 0, 0);
-    // step t+1 landed (this wave's loads; the barrier covers the others), the loads of
-    // steps t+2 and t+3 may still be in flight; every read of step t is done (a 3-stage
-    // ring, loads two steps ahead, measured 2 % slower at 8192^3)
+    product(S1{}, 0, 0, 1, st, 0, 0, 0);   // P0, reading P1
+    product(S2{}, 1, 1, 2, st, 0, 0, 0);   // 2 P1, reading P2
+    product(S1{}, 0, 1, 3, st, 0, 0, 0);   // P2, reading P3
+    // step t+1 landed (this wave's loads; the barrier covers the others), step t+2's
+    // loads may still be in flight; every read of step t is done
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAwe4Stages - 2) * kAwe4Loads) : "memory");
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     awe4_barrier();
@@ -475,38 +496,11 @@ __global__ __launch_bounds__(kAwe4Threads, 1) void awe4_gemm_kernel(
     const int tn = t + 1 < nk ? t + 1 : t;       // past the last step: a harmless re-read
     // past the last step: reload the last
     const int tl = t + kAwe4Stages < nk ? t + kAwe4Stages : nk - 1;
-    product(1, 1, 0, tn % kAwe4Stages, kAwe4Loads, tl, st);
+    product(S1{}, 1, 2, 0, tn % kAwe4Stages, kAwe4Loads, tl, st);   // P3, reading next P0
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  awe4_barrier();   // every wave is past its last load and LDS read of the ring
 
-  // Epilogue: weighted sum of this wave's products, the odd wave's through LDS.
-  uint32_t part[2][2][16];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        uint32_t sum = 0;
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-          sum += (uint32_t)kCoef4[2 * h + p] * (uint32_t)(int32_t)acc[p][i][j][v];
-        part[i][j][v] = sum;
-      }
-  uint32_t* xch = reinterpret_cast<uint32_t*>(lds) + g * (4 * 16 * 64);
-  if (h == 1) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) xch[((2 * i + j) * 16 + v) * 64 + lane] = part[i][j][v];
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  awe4_barrier();
-  if (h == 1) return;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -514,7 +508,9 @@ __global__ __launch_bounds__(kAwe4Threads, 1) void awe4_gemm_kernel(
       const int64_t col = col0 + c0 + 32 * j + (lane & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const uint32_t sum = part[i][j][v] + xch[((2 * i + j) * 16 + v) * 64 + lane];
+        const uint32_t sum = (uint32_t)kCoef4[0] * (uint32_t)(int32_t)acc[0][i][j][v] +
+                             (uint32_t)kCoef4[2] * (uint32_t)(int32_t)acc[1][i][j][v] +
+                             (uint32_t)kCoef4[3] * (uint32_t)(int32_t)acc[2][i][j][v];
         const int64_t row = row0 + r0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (row < m && col < n) c[row * ldc + col] = (int32_t)sum;
       }
@@ -569,9 +565,9 @@ int launch_awe4_products(int64_t m, int64_t n, int64_t steps, const uint8_t* pa,
 int launch_awe4_gemm(int64_t m, int64_t n, int64_t steps, const uint8_t* pa, int64_t lda,
                      const uint8_t* pb, int64_t ldb, int32_t* c, int64_t ldc, hipStream_t s) {
   if (m <= 0 || n <= 0) return OZK_OK;
-  // 32-bit lane offsets within a 128-line tile; line strides hold every step
+  // 32-bit lane offsets within a 256-line tile; line strides hold every step
   if (steps <= 0 || lda < steps * kStepBytes4 || ldb < steps * kStepBytes4 || lda % 16 ||
-      ldb % 16 || 128 * (lda > ldb ? lda : ldb) >= ((int64_t)1 << 31))
+      ldb % 16 || BN4 * (lda > ldb ? lda : ldb) >= ((int64_t)1 << 31))
     return OZK_EINVAL;
   const int64_t tiles_m = (m + BM4 - 1) / BM4, tiles_n = (n + BN4 - 1) / BN4;
   if (tiles_m * tiles_n > 0x7fffffff) return OZK_EUNSUPPORTED;
