@@ -326,8 +326,9 @@ int ozk_int8gemm_fp4awe(int64_t m, int64_t n, int64_t k, const int8_t* A, int64_
  * ozk_int4int8gemm_fp4awe: C = A B exactly in int32 (A m x k int4 values one per byte, B
  *   k x n int8, both row-major), packing both operands into the workspace
  *   (ozk_int4int8gemm_fp4awe_workspace_size bytes, 256-byte aligned) and summing the 4
- *   weighted plane products.  k <= OZK_MAX_K (fp32 partial sums stay exact: each
- *   elementary product is at most 48). */
+ *   weighted plane products (products 1 and 2, whose weights are 90 and 45, summed in one
+ *   fp32 accumulator).  k <= OZK_MAX_K (fp32 partial sums stay exact: per K value the
+ *   plane products are at most 48 in magnitude, and 2 P1 + P2 at most 27). */
 int64_t ozk_fp4awe4_line_bytes(int64_t k);
 int ozk_fp4awe4_pack(const int8_t* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
                      int int4, uint8_t* planes, int64_t ld_line, void* stream);
