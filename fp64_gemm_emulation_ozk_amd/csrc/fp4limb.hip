@@ -75,7 +75,7 @@ static_assert(make_limb_table().codes[128] == 0, "0 splits into three zero digit
 // A packer's table in LDS: the spread word (byte d = code of digit plane d) of every
 // value, indexed by the unsigned byte of the stored value.
 __device__ __forceinline__ void load_limb_lut(uint32_t* lut) {
-  lut[threadIdx.x] = spread_nibbles(d_limbs.codes[threadIdx.x ^ 0x80]);   // 256 threads
+  if (threadIdx.x < 256) lut[threadIdx.x] = spread_nibbles(d_limbs.codes[threadIdx.x ^ 0x80]);
   __syncthreads();
 }
 
@@ -138,8 +138,10 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const int8_t* __restrict
 
 // axis 1: x rows x cols with K = rows; thread -> (4 consecutive columns, 32-value chunk of
 // K).  The 64 threads of a wave take 256 consecutive columns, so with vec (x and ldx 4-byte
-// aligned) every load instruction reads 256 consecutive bytes of one row.
-__global__ __launch_bounds__(256) void pack_cols_kernel(const int8_t* __restrict__ x,
+// aligned) every load instruction reads 256 consecutive bytes of one row; the 8 waves of a
+// block take 8 consecutive chunks, so each 128-byte line of a plane is written whole by one
+// block (with 4 waves per block two blocks shared every line: 1.33x the algorithmic bytes).
+__global__ __launch_bounds__(512) void pack_cols_kernel(const int8_t* __restrict__ x,
                                                         int64_t rows, int64_t cols, int64_t ldx,
                                                         uint8_t* __restrict__ planes,
                                                         int64_t ldpb, int64_t plane_stride,
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(256) void pack_cols_kernel(const int8_t* __restrict
   __shared__ uint32_t lut[256];
   load_limb_lut(lut);
   const int64_t col0 = 4 * ((int64_t)blockIdx.x * 64 + (threadIdx.x & 63));
-  const int64_t h0 = ((int64_t)blockIdx.y * 4 + (threadIdx.x >> 6)) * 32;
+  const int64_t h0 = ((int64_t)blockIdx.y * 8 + (threadIdx.x >> 6)) * 32;
   if (col0 >= cols || h0 >= 2 * ldpb) return;
   const bool full = vec && col0 + 4 <= cols;
   uint32_t r[32];   // byte c of r[h] = row h0 + h, column col0 + c (0 past the matrix)
@@ -446,8 +448,8 @@ int launch_fp4_pack(const int8_t* x, int64_t rows, int64_t cols, int64_t ldx, in
   } else {
     if (cols <= 0) return OZK_OK;
     const int vec = (reinterpret_cast<uintptr_t>(x) % 4) == 0 && ldx % 4 == 0;
-    dim3 grid((unsigned)((cols + 255) / 256), (unsigned)((2 * ldpb / 32 + 3) / 4));
-    hipLaunchKernelGGL(pack_cols_kernel, grid, dim3(256), 0, s, x, rows, cols, ldx, planes, ldpb,
+    dim3 grid((unsigned)((cols + 255) / 256), (unsigned)((2 * ldpb / 32 + 7) / 8));
+    hipLaunchKernelGGL(pack_cols_kernel, grid, dim3(512), 0, s, x, rows, cols, ldx, planes, ldpb,
                        plane_stride, vec);
   }
   return hipGetLastError() == hipSuccess ? OZK_OK : OZK_EHIP;
