@@ -32,12 +32,12 @@ __device__ __forceinline__ void pack8_planes(const uint32_t (&s)[8], uint32_t (&
   const uint32_t x0 = __builtin_amdgcn_perm(p[1], p[0], 0x05010400u);  // p0.0 p1.0 p0.1 p1.1
   const uint32_t y0 = __builtin_amdgcn_perm(p[3], p[2], 0x05010400u);  // p2.0 p3.0 p2.1 p3.1
   w[0] = __builtin_amdgcn_perm(y0, x0, 0x05040100u);
-  if (NP > 1) w[NP > 1 ? 1 : 0] = __builtin_amdgcn_perm(y0, x0, 0x07060302u);
-  if (NP > 2) {
+  if constexpr (NP > 1) w[1] = __builtin_amdgcn_perm(y0, x0, 0x07060302u);
+  if constexpr (NP > 2) {
     const uint32_t x1 = __builtin_amdgcn_perm(p[1], p[0], 0x07030602u);  // p0.2 p1.2 p0.3 p1.3
     const uint32_t y1 = __builtin_amdgcn_perm(p[3], p[2], 0x07030602u);
-    w[NP > 2 ? 2 : 0] = __builtin_amdgcn_perm(y1, x1, 0x05040100u);
-    if (NP > 3) w[NP > 3 ? 3 : 0] = __builtin_amdgcn_perm(y1, x1, 0x07060302u);
+    w[2] = __builtin_amdgcn_perm(y1, x1, 0x05040100u);
+    if constexpr (NP > 3) w[3] = __builtin_amdgcn_perm(y1, x1, 0x07060302u);
   }
 }
 
@@ -46,10 +46,6 @@ __device__ __forceinline__ void pack8_planes(const uint32_t (&s)[8], uint32_t (&
 __device__ __forceinline__ uint32_t byte_of(uint32_t w, int c, uint32_t mask) {
   return (w >> (8 * c)) & mask;
 }
-
-}  // namespace ozk
-
-namespace ozk {
 
 // Coalesced store of one item of NP 16-byte pieces per lane (a line's K step) through this
 // wave's LDS area: `stage` holds 64 items of 16 NP bytes, `dsts` 64 destinations.  Lane i
