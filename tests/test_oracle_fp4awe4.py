@@ -138,3 +138,31 @@ def test_packed_layout_decodes_back():
                 code = (byte >> 4) if c % 2 else (byte & 15)
                 want = planes[t, line, h] if h < 100 else 0
                 assert lut[int(code)] == want
+
+
+def test_products_one_and_two_can_share_an_fp32_sum():
+    """The coefficients of products 1 and 2 stand in the ratio 2 : 1, so a block scale of 2
+    on product 1 lets both add into one fp32 sum 2 P1 + P2; per K value that sum is at most
+    27 in magnitude over all int4 x int8 pairs, so it stays an exact integer below 2^24 for
+    K up to 621378 (beyond the library's 131071).  The other pairs of coefficients are not
+    power-of-two multiples of each other."""
+    coef = fp4awe4.coefficients()
+    assert coef[1] == 2 * coef[2]
+    for i in range(4):
+        for j in range(i + 1, 4):
+            if (i, j) == (1, 2):
+                continue
+            ratio = abs(coef[i] / coef[j])
+            assert not any(ratio == 2.0 ** e for e in range(-8, 9))
+    us = [fp4awe4.x_planes(a) for a in fp4awe4.x_table().values()]
+    vs = [fp4awe4.y_planes(b) for b in fp4awe4.y_table().values()]
+    bound = max(abs(2 * u[1] * v[1] + u[2] * v[2]) for u in us for v in vs)
+    assert bound == 27
+    assert 27 * 621378 < 2**24 <= 27 * 621379
+    # and the combination reproduces x y for every pair
+    xs, ys = np.arange(-8, 8), np.arange(-128, 128)
+    u = fp4awe4.planes_x(xs[None, :])[:, 0, :].astype(np.int64)
+    v = fp4awe4.planes_y(ys[None, :])[:, 0, :].astype(np.int64)
+    shared = 2 * np.outer(u[1], v[1]) + np.outer(u[2], v[2])
+    got = coef[0] * np.outer(u[0], v[0]) + coef[2] * shared + coef[3] * np.outer(u[3], v[3])
+    np.testing.assert_array_equal(got, np.outer(xs, ys))
