@@ -91,10 +91,13 @@ def _largest_plane_value(table, planes):
     return max(table, key=lambda v: sum(abs(t) for t in planes(table[v])))
 
 
-@pytest.mark.parametrize("va,vb", [(-8, -128), (7, -128), (-8, 127), ("big", "big")])
+# (-7, -105): the pair whose shared sum 2 P1 + P2 is largest (27 per K value)
+@pytest.mark.parametrize("va,vb", [(-8, -128), (7, -128), (-8, 127), ("big", "big"),
+                                   (-7, -105)])
 def test_int4int8gemm_fp4awe_accumulator_bound(va, vb):
     """Constant operands with K = 131071 (the largest K): every plane product sums K equal
-    terms of up to 48 in magnitude, 6.3 M, still an integer below 2^24 in fp32."""
+    terms of up to 48 in magnitude, 6.3 M, and the shared sum 2 P1 + P2 terms of up to 27,
+    3.5 M, still integers below 2^24 in fp32."""
     if va == "big":
         va = _largest_plane_value(fp4awe4.x_table(), fp4awe4.x_planes)
         vb = _largest_plane_value(fp4awe4.y_table(), fp4awe4.y_planes)
