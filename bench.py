@@ -971,6 +971,22 @@ def hold(seconds: float, what: str, step, da, db, r: int, rule: str) -> int:
         res = ozk.ozk_modular_residues(pa, pb, r)
         call = lambda: ozk.ozk_modular_residues(pa, pb, r, out=res)
         name = f"residue products {M}^3 r={r}"
+    elif what in ("fp4limb", "fp4awe4"):
+        del da, db
+        torch.cuda.empty_cache()
+        gen = ozk_inputs.int8_operands if what == "fp4limb" else ozk_inputs.int4_int8_operands
+        ia, ib = (torch.from_numpy(t).to(dev) for t in gen(M, M, M, seed=5))
+        out = torch.empty((M, M), dtype=torch.int32, device=dev)
+        if what == "fp4limb":
+            ws = torch.empty(ozk.ozk_int8gemm_fp4limb_workspace_size(M, M, M), dtype=torch.uint8,
+                             device=dev)
+            call = lambda: ozk.ozk_int8gemm_fp4limb(ia, ib, out=out, workspace=ws)
+            name = f"INT8 {M}^3 through 9 FP4 products"
+        else:
+            ws = torch.empty(ozk.ozk_int4int8gemm_fp4awe_workspace_size(M, M, M),
+                             dtype=torch.uint8, device=dev)
+            call = lambda: ozk.ozk_int4int8gemm_fp4awe(ia, ib, out=out, workspace=ws)
+            name = f"INT4 x INT8 {M}^3 through 4 FP4 products"
     else:
         del da, db
         torch.cuda.empty_cache()
@@ -1035,9 +1051,11 @@ def main() -> int:
                     help="run one workload back to back for SECONDS and print its mean time "
                          "(a steady load for reading the board's power and clocks with amd-smi)")
     ap.add_argument("--hold-workload", default="dgemm",
-                    choices=("dgemm", "products", "gemv1", "gemv8", "gemv32"),
-                    help="what --hold runs: the timed step, its residue products alone, or the "
-                         "32768^2 GEMV on the fly (r = 14, cached exponents) with 1/8/32 columns")
+                    choices=("dgemm", "products", "gemv1", "gemv8", "gemv32", "fp4limb",
+                             "fp4awe4"),
+                    help="what --hold runs: the timed step, its residue products alone, the "
+                         "32768^2 GEMV on the fly (r = 14, cached exponents) with 1/8/32 columns, "
+                         "or the 8192^3 INT8 (9 FP4 products) or INT4 x INT8 (4) product")
     ap.add_argument("--tme-summary", metavar="DIR",
                     help="write the time-model instruction counts from a rocprofv3 --pmc run")
     args = ap.parse_args()
